@@ -1,0 +1,234 @@
+/*
+ * zero_mi355x.h - C ABI of the per-rank partitioned mixed-precision optimizer
+ * step (ZeRO / FSDP data parallelism) on AMD MI355X (gfx950).
+ *
+ * Cited page: "Zero Redundancy Optimizer (ZeRO) and Fully Sharded Data
+ * Parallelism (FSDP): Mathematical Foundations of Memory Partitioning,
+ * Communication Complexity, and Overlapped Execution" (llms.blog), written
+ * [ZF] below with the section name.
+ *
+ * One rank's step, as [ZF] "Execution Flow for ZeRO-1" (steps 2-4) and
+ * "ZeRO-Stage 2" lay it out, maps onto these calls:
+ *   zero_partition_plan     flat padded buffer cut into N_d equal shards
+ *   zero_grad_reduce_shard  the rank's averaged gradient slice (reduce-scatter,
+ *                           seen from the receiving rank)
+ *   zero_grad_sqnorm        squared-norm partial of a gradient shard
+ *   zero_clip_scale         global-norm clip coefficient from all partials
+ *   zero_shard_adamw_step   fp32 master/m/v update and bf16 parameter emit
+ *   zero_gather_params      bf16 shards back to per-tensor parameters
+ *                           (all-gather output layout, then un-flatten)
+ *
+ * Conventions, for every function below:
+ *   - bf16 values travel as raw uint16_t bit patterns; fp32 as float.
+ *   - "device" pointers address GPU memory of the current HIP device; the
+ *     caller allocates and owns them. The library never frees them and keeps
+ *     no reference to them after the call returns.
+ *   - "host" pointers are read during the call only.
+ *   - Device work is enqueued on `stream` (0 = the legacy default stream) and
+ *     runs asynchronously; the function returns once the work is enqueued.
+ *     Results are visible to later work on the same stream.
+ *   - Every function returns a zero_status; nothing aborts or throws across
+ *     the ABI. On failure nothing has been enqueued, unless the status is
+ *     ZERO_EHIP from a failed launch. zero_last_error() gives a readable
+ *     detail for the last failure on the calling thread.
+ *   - Element counts and offsets are int64_t; buffers beyond 2^32 elements
+ *     are supported everywhere.
+ *   - Any device pointer that is not 16-byte aligned is accepted; such calls
+ *     run a slower scalar path with identical results.
+ */
+#ifndef ZERO_MI355X_H
+#define ZERO_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum zero_status {
+    ZERO_OK = 0,
+    ZERO_EINVAL = 1,    /* an argument is invalid (null, negative, out of range) */
+    ZERO_ERANGE = 2,    /* a size overflows int64 or exceeds a documented maximum */
+    ZERO_ENOMEM = 3,    /* host memory allocation failed */
+    ZERO_EHIP = 4,      /* a HIP runtime call or kernel launch failed */
+    ZERO_ENOSPACE = 5   /* the caller's workspace is smaller than required */
+} zero_status;
+
+/* Largest number of gradient replicas one zero_grad_reduce_shard call reduces. */
+#define ZERO_MAX_REPLICAS 64
+
+/* Opaque partition plan: host memory owned by the library, immutable after
+ * zero_partition_plan returns, safe to read from several threads. */
+typedef struct zero_plan zero_plan;
+
+/* The part of tensor `tensor` that lies in rank `rank`'s shard:
+ * tensor elements [tensor_offset, tensor_offset + length) are shard elements
+ * [shard_offset, shard_offset + length). */
+typedef struct zero_segment {
+    int32_t tensor;
+    int32_t rank;
+    int64_t tensor_offset;
+    int64_t shard_offset;
+    int64_t length;
+} zero_segment;
+
+/* ------------------------------------------------------------------ plan (host only)
+ *
+ * [ZF] "FSDP-1: FlatParameter and Module-Level Wrapping": a unit's tensors are
+ * flattened into one contiguous 1-D buffer, padded to a length divisible by
+ * the world size, and cut into N_d equal chunks; [ZF] "ZeRO-Stage 1" gives
+ * each rank a Phi/N_d slice of the optimizer state.
+ *
+ * numels       host [n_tensors]: element count of each tensor, in flat order
+ *              (each >= 0; zero-sized tensors are allowed and own no elements).
+ * n_tensors    >= 0.
+ * n_ranks      N_d >= 1.
+ * align_elems  A >= 1: every shard length is a multiple of A, so the padded
+ *              length P = ceil(Phi / (N_d*A)) * N_d*A and the shard length
+ *              S = P / N_d. Tensor t starts at flat element sum(numels[<t]);
+ *              elements [Phi, P) are padding. Rank r owns [r*S, (r+1)*S).
+ * out          receives the new plan; free it with zero_plan_free.
+ * Errors: ZERO_EINVAL for a null pointer, a negative count, n_ranks < 1 or
+ * align_elems < 1; ZERO_ERANGE if P would overflow int64; ZERO_ENOMEM. */
+zero_status zero_partition_plan(const int64_t* numels, int32_t n_tensors, int32_t n_ranks,
+                                int32_t align_elems, zero_plan** out);
+void zero_plan_free(zero_plan* plan);                       /* accepts NULL */
+
+int64_t zero_plan_numel(const zero_plan* plan);             /* Phi, or -1 if plan is NULL */
+int64_t zero_plan_padded_numel(const zero_plan* plan);      /* P,   or -1 */
+int64_t zero_plan_shard_numel(const zero_plan* plan);       /* S,   or -1 */
+int32_t zero_plan_num_tensors(const zero_plan* plan);       /* T,   or -1 */
+int32_t zero_plan_num_ranks(const zero_plan* plan);         /* N_d, or -1 */
+int64_t zero_plan_tensor_offset(const zero_plan* plan, int32_t tensor);  /* -1 if out of range */
+int32_t zero_plan_num_segments(const zero_plan* plan, int32_t rank);     /* -1 if out of range */
+
+/* Copies rank's segments, in flat order, into host array out[capacity].
+ * *count receives the number of segments; ZERO_ENOSPACE (with *count set) if
+ * capacity is too small. */
+zero_status zero_plan_segments(const zero_plan* plan, int32_t rank, zero_segment* out,
+                               int32_t capacity, int32_t* count);
+
+/* Static training-state bytes per GPU. [ZF] "Static Memory Allocation"
+ * (16 bytes per parameter: 2 bf16 param, 2 bf16 grad, 12 fp32 master/m/v)
+ * and the stage formulas of [ZF] "ZeRO-Stage 1" (4 Phi + 12 Phi/N_d),
+ * "ZeRO-Stage 2" (2 Phi + 14 Phi/N_d) and "ZeRO-Stage 3 and Fully Sharded Data
+ * Parallelism" (16 Phi/N_d). stage: 0 = DDP, 1, 2, 3. padded != 0 counts the
+ * flat buffers at P and the shards at S (stage 0 stays 16 Phi). */
+zero_status zero_plan_memory_bytes(const zero_plan* plan, int32_t stage, int32_t padded,
+                                   double* bytes);
+
+/* ------------------------------------------------------------------ gradient reduction
+ *
+ * [ZF] "Execution Flow for ZeRO-1", step 2: rank i receives the gradient of
+ * its own partition averaged over the data-parallel ranks; [ZF] "ZeRO-Stage 2":
+ * gradients are reduced into their owners' slices bucket by bucket as backward
+ * produces them. On one GPU the R replicas sit in one HBM; this call is the
+ * receiving rank's arithmetic of that reduce-scatter.
+ *
+ * replicas     host [n_replicas] of device pointers; replicas[k] points at
+ *              replica k's bf16 gradient for global flat elements
+ *              [begin, begin + count) (a whole flat buffer, or one bucket).
+ * n_replicas   R, 1 <= R <= ZERO_MAX_REPLICAS.
+ * begin,count  the global flat window the replica buffers cover (count >= 0,
+ *              begin >= 0, begin + count <= P).
+ * shard_grad   device [S]: element i is global element rank*S + i. Only the
+ *              window's intersection with rank's shard is written:
+ *              out = bf16_rne( (sum over k = 0..R-1, in order, of fp32(rep_k)) / R ),
+ *              the sum and the division in IEEE fp32.
+ * sqnorm_out   device, nullable: receives the fp64 sum of squares of the bf16
+ *              values this call wrote (0 if it wrote nothing). Deterministic for a
+ *              given device.
+ * workspace    device, required when sqnorm_out is non-null; at least
+ *              zero_sqnorm_workspace_bytes() bytes, 8-byte aligned.
+ * Errors: ZERO_EINVAL (null plan/replicas/shard_grad, a null replica pointer,
+ * R out of range, rank out of range, bad window); ZERO_ENOSPACE; ZERO_EHIP. */
+zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
+                                   const uint16_t* const* replicas, int32_t n_replicas,
+                                   int64_t begin, int64_t count, uint16_t* shard_grad,
+                                   double* sqnorm_out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------ squared norm
+ *
+ * Sum of squares of n bf16 values (device [n]), accumulated in fp64 (each
+ * square is exact), written to device sqnorm_out[0]. Two fixed-order
+ * reduction levels, no floating-point atomics: the result is reproducible on
+ * a given device. The norm clip is not on the cited pages; the global norm it
+ * needs is the sum of these partials over every rank.
+ * Errors: ZERO_EINVAL (null pointers with n > 0, n < 0); ZERO_ENOSPACE; ZERO_EHIP. */
+zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double* sqnorm_out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes that zero_grad_sqnorm and zero_grad_reduce_shard need: a
+ * fixed bound, independent of n and of the device. */
+size_t zero_sqnorm_workspace_bytes(void);
+
+/* ------------------------------------------------------------------ clip coefficient
+ *
+ * partials     device [n_partials] fp64 squared-norm partials (one per rank, or
+ *              per bucket), summed in index order in fp64.
+ * max_norm     clip threshold; <= 0 disables clipping (coefficient 1).
+ * scale_out    device float: min(1, max_norm / (sqrt(total) + 1e-6)) rounded
+ *              once to fp32; NaN when the total is not finite, which makes
+ *              zero_shard_adamw_step skip its update.
+ * Errors: ZERO_EINVAL (null pointers, n_partials < 1 or > 65536); ZERO_EHIP. */
+zero_status zero_clip_scale(const double* partials, int32_t n_partials, double max_norm,
+                            float* scale_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------ AdamW shard update
+ *
+ * [ZF] "Static Memory Allocation": fp32 master weights, fp32 first moment m_t
+ * and fp32 second moment v_t, 16-bit parameters; [ZF] "Execution Flow for
+ * ZeRO-1", steps 3-4: the rank updates its own slice and emits 16-bit
+ * parameters for the all-gather; [ZF] "ZeRO-Offload Mechanics": O(1) work per
+ * parameter, so the update is bound by memory traffic (28 bytes per element).
+ *
+ * Per element, each operation one IEEE fp32 operation (no fused multiply-add),
+ * in this order, with the scalars computed in fp64 on the host and rounded
+ * once to fp32 (t = step):
+ *   g = fp32(grad) * clip
+ *   m = beta1*m + (1-beta1)*g
+ *   v = beta2*v + (1-beta2)*(g*g)
+ *   p = p * (1 - lr*weight_decay)
+ *   p = p - (lr/(1-beta1^t)) * (m / (sqrt(v)/sqrt(1-beta2^t) + eps))
+ *   param_out = bf16_rne(p)
+ * master, exp_avg, exp_avg_sq  device [n] fp32, updated in place.
+ * grad         device [n] bf16, read only.
+ * param_out    device [n] bf16, written; must not overlap the fp32 arrays.
+ * step         t >= 1 (1-based bias-correction step).
+ * clip_scale   device float, nullable (NULL means 1). A non-finite value skips
+ *              the update: nothing is read or written.
+ * Errors: ZERO_EINVAL (null pointers with n > 0, n < 0, step < 1, beta1 or
+ * beta2 outside [0, 1), eps <= 0, lr < 0, non-finite scalars); ZERO_EHIP. */
+zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
+                                  const uint16_t* grad, uint16_t* param_out, int64_t n,
+                                  int64_t step, double lr, double beta1, double beta2, double eps,
+                                  double weight_decay, const float* clip_scale,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------ gather
+ *
+ * [ZF] "Execution Flow for ZeRO-1", step 4 and "FSDP-1": the N_d bf16 shards,
+ * concatenated in rank order, are the flat parameter buffer; tensor t is its
+ * slice [offset_t, offset_t + numel_t). This copies every plan segment from
+ * its shard into its tensor (padding is not copied).
+ * shards       host [N_d] of device pointers, each to S bf16 values.
+ * tensors      host [T] of device pointers, tensor t to numel_t bf16 values
+ *              (may be NULL only for zero-sized tensors). Outputs must not
+ *              overlap the shards or each other.
+ * Errors: ZERO_EINVAL (null plan/arrays or a needed null pointer); ZERO_EHIP. */
+zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* shards,
+                               uint16_t* const* tensors, hipStream_t stream);
+
+/* ------------------------------------------------------------------ diagnostics */
+const char* zero_status_string(zero_status status);   /* static string */
+const char* zero_last_error(void);                    /* thread-local; "" if none */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_MI355X_H */

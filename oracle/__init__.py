@@ -32,5 +32,5 @@ from .clip import clip_scale  # noqa: F401
 from .gather import gather_params  # noqa: F401
 from .plan import Plan, memory_bytes, partition_plan  # noqa: F401
 from .reduce import reduce_shard  # noqa: F401
-from .sqnorm import sqnorm, sqnorm_fsum  # noqa: F401
+from .sqnorm import SqnormAccumulator, sqnorm, sqnorm_fsum  # noqa: F401
 from .step import rank_step  # noqa: F401

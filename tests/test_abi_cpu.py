@@ -1,0 +1,122 @@
+"""The C-ABI library on the host (no GPU calls): symbols, plan logic, argument checks."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def zm():
+    import zero_partitioned_mixed_partition_amd as m
+    return m
+
+
+def _declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function(zm):
+    names = _declared_functions()
+    assert len(names) >= 18, names
+    lib = ctypes.CDLL(zm.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_plan_matches_oracle_on_workloads(zm, name):
+    w = synth.WORKLOADS[name]
+    for n_ranks in sorted({w.n_ranks, 1, 3}):
+        ref = oracle.partition_plan(w.numels, n_ranks, w.align)
+        plan = zm.zero_partition_plan(w.numels, n_ranks, w.align)
+        assert (plan.numel, plan.padded_numel, plan.shard_numel, plan.num_tensors,
+                plan.num_ranks) == (ref.numel, ref.padded_numel, ref.shard_numel,
+                                    len(w.numels), n_ranks)
+        assert [plan.tensor_offset(t) for t in range(len(w.numels))] == ref.offsets
+        for r in range(n_ranks):
+            assert plan.segments(r) == ref.segments(r), (name, n_ranks, r)
+        for stage in range(4):
+            for padded in (False, True):
+                assert plan.memory_bytes(stage, padded) == oracle.memory_bytes(ref, stage, padded)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_plan_matches_oracle_random(zm, seed):
+    rng = np.random.default_rng(1000 + seed)
+    t = int(rng.integers(0, 12))
+    numels = [int(x) for x in rng.integers(0, 5000, t)]
+    if seed % 5 == 0 and t:
+        numels[int(rng.integers(0, t))] = 0
+    n_ranks = int(rng.choice([1, 2, 3, 5, 8, 64]))
+    align = int(rng.choice([1, 2, 8, 128, 1000]))
+    ref = oracle.partition_plan(numels, n_ranks, align)
+    plan = zm.zero_partition_plan(numels, n_ranks, align)
+    assert (plan.numel, plan.padded_numel, plan.shard_numel) == (
+        ref.numel, ref.padded_numel, ref.shard_numel)
+    for r in range(n_ranks):
+        assert plan.segments(r) == ref.segments(r)
+
+
+def test_plan_page_figures_through_the_abi(zm):
+    plan = zm.zero_partition_plan([70_000_000_000], 64, 1)
+    gb = [plan.memory_bytes(s) / 1e9 for s in range(4)]
+    assert gb == [1120.0, 280 + 840 / 64, 140 + 980 / 64, 1120 / 64]
+
+
+def test_plan_errors(zm):
+    with pytest.raises(zm.ZeroError):
+        zm.zero_partition_plan([5, -1], 2, 1)
+    with pytest.raises(zm.ZeroError):
+        zm.zero_partition_plan([5], 0, 1)
+    with pytest.raises(zm.ZeroError):
+        zm.zero_partition_plan([5], 1, 0)
+    with pytest.raises(zm.ZeroError):   # total overflows int64
+        zm.zero_partition_plan([2 ** 62, 2 ** 62], 1, 1)
+    with pytest.raises(zm.ZeroError):   # padding overflows int64
+        zm.zero_partition_plan([2 ** 63 - 2], 1, 1 << 20)
+    plan = zm.zero_partition_plan([], 4, 128)
+    assert (plan.numel, plan.padded_numel, plan.shard_numel, plan.num_segments(0)) == (0, 0, 0, 0)
+    plan = zm.zero_partition_plan([10], 2, 1)
+    with pytest.raises(ValueError):
+        plan.segments(2)
+    with pytest.raises(zm.ZeroError):
+        plan.memory_bytes(4)
+    assert plan.tensor_offset(1) == -1
+
+
+def test_device_calls_reject_bad_arguments_before_touching_the_gpu(zm):
+    lib = zm._binding
+    st = lib._adamw(None, None, None, None, None, 16, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, None, None)
+    assert st == zm._binding.ZERO_EINVAL            # step < 1
+    st = lib._adamw(None, None, None, None, None, -1, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None, None)
+    assert st == zm._binding.ZERO_EINVAL            # n < 0
+    st = lib._adamw(None, None, None, None, None, 0, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None, None)
+    assert st == zm._binding.ZERO_OK                # empty: nothing to do
+    st = lib._adamw(None, None, None, None, None, 4, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None, None)
+    assert st == zm._binding.ZERO_EINVAL            # NULL arrays
+    assert "NULL" in zm.zero_last_error()
+    st = lib._sqnorm(None, -1, None, None, 0, None)
+    assert st == zm._binding.ZERO_EINVAL
+    st = lib._clip(None, 1, 1.0, None, None)
+    assert st == zm._binding.ZERO_EINVAL
+    st = lib._gather(None, None, None, None)
+    assert st == zm._binding.ZERO_EINVAL
+    plan = zm.zero_partition_plan([100], 2, 1)
+    st = lib._reduce(plan.handle, 5, None, 1, 0, 100, None, None, None, 0, None)
+    assert st == zm._binding.ZERO_EINVAL
+    assert zm.zero_status_string(zm._binding.ZERO_ENOSPACE).startswith("workspace")
+    assert zm.zero_sqnorm_workspace_bytes() >= 8

@@ -1,0 +1,265 @@
+"""GPU parity of each entry point against the CPU oracle, through the C ABI.
+
+Sizes span several workgroups, a ragged tail, and unaligned (scalar-path)
+pointers; edge cases cover empty inputs, single replicas, the maximum replica
+count, a skipped step, and argument errors.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (assert_bf16_close, assert_bits_equal, assert_f32_close, dev, host_f32,
+                      host_u16, needs_gpu, note, to_dev_f32, to_dev_u16)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+@pytest.fixture(scope="module")
+def zm():
+    import zero_partitioned_mixed_partition_amd as m
+    torch.cuda.set_device(0)
+    return m
+
+
+# ----------------------------------------------------------------------------- AdamW
+
+def _adamw_inputs(n, seed):
+    p = synth.normal_f32(n, seed, synth.KIND_MASTER, 0, 0, sigma=0.02)
+    m = synth.normal_f32(n, seed, 10, 0, 0, sigma=1e-4)
+    v = np.abs(synth.normal_f32(n, seed, 11, 0, 0, sigma=1e-7))
+    g = synth.normal_bf16(n, seed, synth.KIND_GRAD, 1, 0, sigma=1e-3)
+    return p, m, v, g
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 4097, 256 * 8 * 37 + 5, (1 << 20) + 3])
+def test_adamw_matches_oracle(zm, n):
+    note(f"adamw n={n}")
+    p, m, v, g = _adamw_inputs(n, 100 + n % 97)
+    dp, dm, dv, dg = to_dev_f32(p), to_dev_f32(m), to_dev_f32(v), to_dev_u16(g)
+    dout = torch.zeros(n, dtype=torch.int16, device=dev())
+    scale = torch.tensor([0.37], dtype=torch.float32, device=dev())
+    for t in (1, 2, 3):
+        zm.zero_shard_adamw_step(dp, dm, dv, dg, dout, t, clip_scale=scale, **HP)
+        p, m, v, bits = oracle.adamw_step(p, m, v, g, t, clip=0.37, **HP)
+    torch.cuda.synchronize()
+    for got, want, what in ((dp, p, "master"), (dm, m, "exp_avg"), (dv, v, "exp_avg_sq")):
+        exact = assert_f32_close(host_f32(got), want, what)
+        assert exact == 1.0, f"{what}: expected bit-identical fp32 ({exact:.6f})"
+    assert_bits_equal(host_u16(dout), bits, "param bf16")
+
+
+@pytest.mark.parametrize("offset", [1, 3])
+def test_adamw_unaligned_pointers_take_the_scalar_path(zm, offset):
+    n = 5000
+    p, m, v, g = _adamw_inputs(n + offset, 7)
+    dp, dm, dv, dg = to_dev_f32(p), to_dev_f32(m), to_dev_f32(v), to_dev_u16(g)
+    dout = torch.zeros(n + offset, dtype=torch.int16, device=dev())
+    zm.zero_shard_adamw_step(dp[offset:], dm[offset:], dv[offset:], dg[offset:], dout[offset:], 4,
+                             **HP)
+    P, M, V, B = oracle.adamw_step(p[offset:], m[offset:], v[offset:], g[offset:], 4, **HP)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_f32(dp)[offset:].view(np.uint32), P.view(np.uint32), "master")
+    assert_bits_equal(host_f32(dm)[offset:].view(np.uint32), M.view(np.uint32), "exp_avg")
+    assert_bits_equal(host_f32(dv)[offset:].view(np.uint32), V.view(np.uint32), "exp_avg_sq")
+    assert_bits_equal(host_u16(dout)[offset:], B, "param")
+    assert_bits_equal(host_f32(dp)[:offset].view(np.uint32), p[:offset].view(np.uint32), "untouched")
+
+
+def test_adamw_special_values(zm):
+    n = 64
+    p = np.linspace(-3, 3, n).astype(np.float32)
+    p[0], p[1], p[2] = 0.0, -0.0, 1e-40
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    g32 = np.linspace(-1e-2, 1e-2, n).astype(np.float32)
+    g32[3], g32[4], g32[5], g32[6] = np.inf, -np.inf, np.nan, 0.0
+    g32[7], g32[8] = 1e-38, 3e38
+    g = oracle.f32_to_bf16(g32)
+    dp, dm, dv, dg = to_dev_f32(p), to_dev_f32(m), to_dev_f32(v), to_dev_u16(g)
+    dout = torch.zeros(n, dtype=torch.int16, device=dev())
+    zm.zero_shard_adamw_step(dp, dm, dv, dg, dout, 1, **HP)
+    P, M, V, B = oracle.adamw_step(p, m, v, g, 1, **HP)
+    torch.cuda.synchronize()
+    assert_f32_close(host_f32(dp), P, "master")
+    assert_f32_close(host_f32(dm), M, "exp_avg")
+    assert_f32_close(host_f32(dv), V, "exp_avg_sq")
+    assert_bf16_close(host_u16(dout), B, "param")
+
+
+def test_adamw_nonfinite_scale_skips_and_lr0_keeps(zm):
+    n = 3000
+    p, m, v, g = _adamw_inputs(n, 9)
+    dp, dm, dv, dg = to_dev_f32(p), to_dev_f32(m), to_dev_f32(v), to_dev_u16(g)
+    dout = torch.full((n,), 77, dtype=torch.int16, device=dev())
+    nan = torch.tensor([float("nan")], dtype=torch.float32, device=dev())
+    zm.zero_shard_adamw_step(dp, dm, dv, dg, dout, 1, clip_scale=nan, **HP)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_f32(dp).view(np.uint32), p.view(np.uint32), "skipped master")
+    assert_bits_equal(host_f32(dv).view(np.uint32), v.view(np.uint32), "skipped v")
+    assert (host_u16(dout) == 77).all()
+    zm.zero_shard_adamw_step(dp, dm, dv, dg, dout, 1, **dict(HP, lr=0.0))
+    torch.cuda.synchronize()
+    assert_bits_equal(host_f32(dp).view(np.uint32), p.view(np.uint32), "lr=0 master")
+    assert_bits_equal(host_u16(dout), oracle.f32_to_bf16(p), "lr=0 param")
+
+
+def test_adamw_argument_errors(zm):
+    x = torch.zeros(16, dtype=torch.float32, device=dev())
+    h = torch.zeros(16, dtype=torch.int16, device=dev())
+    for bad in (dict(HP, beta1=1.0), dict(HP, eps=0.0), dict(HP, lr=-1.0), dict(HP, beta2=-0.1)):
+        with pytest.raises(zm.ZeroError):
+            zm.zero_shard_adamw_step(x, x.clone(), x.clone(), h, h.clone(), 1, **bad)
+    with pytest.raises(zm.ZeroError):
+        zm.zero_shard_adamw_step(x, x.clone(), x.clone(), h, h.clone(), 0, **HP)
+    with pytest.raises(zm.ZeroError):   # param_out aliasing the master weights
+        zm.zero_shard_adamw_step(x, x.clone(), x.clone(), h, x.view(torch.int16)[:16], 1, **HP)
+    zm.zero_shard_adamw_step(x, x, x, h, h, 1, n=0, **HP)   # empty: a no-op
+
+
+# ----------------------------------------------------------------------------- reduce
+
+@pytest.mark.parametrize("numels,n_ranks,align,rank,R,window", [
+    ([1000, 37, 4096, 3], 4, 128, 2, 3, "full"),
+    ([1000, 37, 4096, 3], 4, 128, 0, 1, "full"),
+    ([100_000, 77_777], 8, 128, 7, 8, "full"),
+    ([100_000, 77_777], 8, 128, 3, 64, "full"),
+    ([100_000, 77_777], 8, 128, 5, 8, "bucket"),
+    ([100_000, 77_777], 8, 128, 5, 2, "odd"),
+    ([100_000, 77_777], 8, 128, 1, 8, "miss"),
+    ([(1 << 20) + 13], 2, 8, 1, 5, "full"),
+])
+def test_reduce_matches_oracle(zm, numels, n_ranks, align, rank, R, window):
+    note(f"reduce numels={numels} N_d={n_ranks} rank={rank} R={R} window={window}")
+    ref = oracle.partition_plan(numels, n_ranks, align)
+    plan = zm.zero_partition_plan(numels, n_ranks, align)
+    P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
+    begin, count = {
+        "full": (0, P),
+        "bucket": (rank * S - 1000, S // 3 + 1000),        # straddles the shard start
+        "odd": (rank * S + 3, S - 7),                      # unaligned: scalar path
+        "miss": ((rank + 2) * S, S // 2),                  # does not meet the shard
+    }[window]
+    reps = [synth.normal_bf16(count, 5, synth.KIND_REPLICA, 1, k, begin, phi, 1e-3) for k in range(R)]
+    want = np.full(S, 0x1234, np.uint16)
+    lo, hi = oracle.reduce_shard(ref, rank, reps, begin, want)
+    d_out = to_dev_u16(np.full(S, 0x1234, np.uint16))
+    d_sq = torch.full((1,), -1.0, dtype=torch.float64, device=dev())
+    zm.zero_grad_reduce_shard(plan, rank, [to_dev_u16(r) for r in reps], begin, count, d_out,
+                              sqnorm_out=d_sq)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u16(d_out), want, "reduced shard")
+    want_sq = oracle.sqnorm(want[lo - rank * S:hi - rank * S]) if hi > lo else 0.0
+    got_sq = float(d_sq.item())
+    assert abs(got_sq - want_sq) <= 1e-12 * abs(want_sq), (got_sq, want_sq)
+
+
+def test_reduce_argument_errors(zm):
+    plan = zm.zero_partition_plan([1000], 4, 8)
+    out = torch.zeros(plan.shard_numel, dtype=torch.int16, device=dev())
+    rep = torch.zeros(plan.padded_numel, dtype=torch.int16, device=dev())
+    with pytest.raises(zm.ZeroError):
+        zm.zero_grad_reduce_shard(plan, 4, [rep], 0, plan.padded_numel, out)
+    with pytest.raises(zm.ZeroError):
+        zm.zero_grad_reduce_shard(plan, 0, [rep] * 65, 0, plan.padded_numel, out)
+    with pytest.raises(zm.ZeroError):
+        zm.zero_grad_reduce_shard(plan, 0, [rep], 10, plan.padded_numel, out)
+    with pytest.raises(zm.ZeroError):   # workspace smaller than required
+        zm.zero_grad_reduce_shard(plan, 0, [rep], 0, plan.padded_numel, out,
+                                  sqnorm_out=torch.zeros(1, dtype=torch.float64, device=dev()),
+                                  workspace=torch.zeros(8, dtype=torch.uint8, device=dev()))
+
+
+# ----------------------------------------------------------------------------- sqnorm, clip
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 2049, (1 << 22) + 5])
+def test_sqnorm_matches_oracle(zm, n):
+    g = synth.normal_bf16(max(n, 1), 8, synth.KIND_GRAD, 2, 0, sigma=1e-3)[:n]
+    d = to_dev_u16(g) if n else torch.zeros(1, dtype=torch.int16, device=dev())
+    out = torch.full((1,), -1.0, dtype=torch.float64, device=dev())
+    zm.zero_grad_sqnorm(d, out, n=n)
+    torch.cuda.synchronize()
+    want = oracle.sqnorm(g)
+    assert abs(out.item() - want) <= 1e-12 * want, (out.item(), want)
+    zm.zero_grad_sqnorm(d, out, n=n)           # repeatable bit for bit
+    again = out.item()
+    zm.zero_grad_sqnorm(d, out, n=n)
+    torch.cuda.synchronize()
+    assert again == out.item()
+
+
+def test_sqnorm_constant_closed_form_and_unaligned(zm):
+    c = oracle.f32_to_bf16(np.array([3.0e-3], np.float32))[0]
+    cv = float(oracle.bf16_to_f32(np.array([c]))[0])
+    n = 50_000_001
+    d = torch.full((n + 1,), int(np.int16(np.uint16(c).view(np.int16))), dtype=torch.int16,
+                   device=dev())
+    out = torch.zeros(1, dtype=torch.float64, device=dev())
+    zm.zero_grad_sqnorm(d[:n], out)
+    torch.cuda.synchronize()
+    assert out.item() == n * cv * cv
+    zm.zero_grad_sqnorm(d[1:], out)          # 2-byte offset: scalar path
+    torch.cuda.synchronize()
+    assert out.item() == n * cv * cv
+
+
+@pytest.mark.parametrize("partials,max_norm", [
+    ([0.25, 0.75], 0.5), ([0.25, 0.75], 2.0), ([3.0], 0.0), ([1.0, math.inf], 1.0),
+    ([124.44096632917478], 1.0), ([1e-30] * 64, 1.0), ([0.0], 1.0)])
+def test_clip_scale_matches_oracle(zm, partials, max_norm):
+    d = torch.tensor(partials, dtype=torch.float64, device=dev())
+    out = torch.zeros(1, dtype=torch.float32, device=dev())
+    zm.zero_clip_scale(d, max_norm, out)
+    torch.cuda.synchronize()
+    want = oracle.clip_scale(partials, max_norm)
+    got = np.float32(out.item())
+    assert (np.isnan(want) and np.isnan(got)) or got == want, (got, want)
+
+
+# ----------------------------------------------------------------------------- gather
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gather_random_plans(zm, seed):
+    rng = np.random.default_rng(seed)
+    t = int(rng.integers(1, 9))
+    numels = [int(x) for x in rng.integers(0, 40_000, t)]
+    numels[0] += 1
+    n_ranks = int(rng.choice([1, 2, 3, 4, 8]))
+    align = int(rng.choice([1, 8, 128]))
+    note(f"gather numels={numels} N_d={n_ranks} A={align}")
+    ref = oracle.partition_plan(numels, n_ranks, align)
+    plan = zm.zero_partition_plan(numels, n_ranks, align)
+    S = ref.shard_numel
+    shards = [rng.integers(0, 1 << 16, S).astype(np.uint16) for _ in range(n_ranks)]
+    want = oracle.gather_params(ref, shards)
+    outs = [torch.full((max(n, 1),), 0x5555, dtype=torch.int16, device=dev()) for n in numels]
+    zm.zero_gather_params(plan, [to_dev_u16(s) for s in shards],
+                          [o[:n] for o, n in zip(outs, numels)])
+    torch.cuda.synchronize()
+    for i, (o, w) in enumerate(zip(outs, want)):
+        assert_bits_equal(host_u16(o)[:numels[i]], w, f"tensor {i}")
+
+
+def test_gather_workload_plans_and_misaligned_destinations(zm):
+    for name in ("tiny-a", "tiny-b", "gpt2-small"):
+        w = synth.WORKLOADS[name]
+        ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
+        plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
+        S = ref.shard_numel
+        note(f"gather {name} T={len(w.numels)} S={S}")
+        shards = [synth.normal_bf16(S, 30, synth.KIND_PARAM, 0, 0, r * S, ref.numel, 0.02)
+                  for r in range(w.n_ranks)]
+        d_shards = [to_dev_u16(s) for s in shards]
+        # destinations start 1 element into their buffers: bf16 pointers off by 2 bytes
+        bufs = [torch.zeros(n + 1, dtype=torch.int16, device=dev()) for n in w.numels]
+        zm.zero_gather_params(plan, d_shards, [b[1:] for b in bufs])
+        torch.cuda.synchronize()
+        flat = np.concatenate(shards)
+        for i, b in enumerate(bufs):
+            off = ref.offsets[i]
+            assert_bits_equal(host_u16(b)[1:], flat[off:off + w.numels[i]], f"{name} tensor {i}")

@@ -1,0 +1,179 @@
+"""GPU parity on the model-shaped workloads, in the launch configuration the
+benchmark times (the same RankStep call sequence and the same kernels).
+
+tiny-a / tiny-b  1M-parameter flat model, N_d = 4, every shard stepped in turn,
+                 gathered every step, 10 steps: full arrays against the oracle.
+gpt2-small       GPT-2-small tensor list, N_d = 8, rank 7 (15.6M elements),
+                 already-averaged gradients, global-norm clip 1.0, 100 steps:
+                 the oracle computes every step's global norm over all 8 ranks
+                 (124M values) and the AdamW state on sampled windows.
+bench pipeline   the benchmark's own step (8 replicas reduced for rank 7, fused
+                 norm, clip, AdamW, gather of 148 tensors): full arrays for 2 steps.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (assert_bf16_close, assert_bits_equal, assert_f32_close, dev, host_f32,
+                      host_u16, needs_gpu, note, to_dev_u16)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+@pytest.fixture(scope="module")
+def zm():
+    import zero_partitioned_mixed_partition_amd as m
+    torch.cuda.set_device(0)
+    return m
+
+
+@pytest.mark.parametrize("name", ["tiny-a", "tiny-b"])
+def test_tiny_all_shards_ten_steps(zm, name):
+    w = synth.WORKLOADS[name]
+    ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
+    plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
+    P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
+    note(f"{name}: Phi={phi} P={P} S={S} T={len(w.numels)}")
+    master = synth.normal_f32(P, w.seed, synth.KIND_MASTER, 0, 0, 0, phi, synth.MASTER_SIGMA)
+    states = [{"master": master[r * S:(r + 1) * S].copy(), "exp_avg": np.zeros(S, np.float32),
+               "exp_avg_sq": np.zeros(S, np.float32)} for r in range(w.n_ranks)]
+    shards = [np.zeros(S, np.uint16) for _ in range(w.n_ranks)]
+    d_master = torch.from_numpy(master).to(dev())
+    d_m = torch.zeros(P, dtype=torch.float32, device=dev())
+    d_v = torch.zeros(P, dtype=torch.float32, device=dev())
+    d_grad = torch.empty(P, dtype=torch.int16, device=dev())
+    d_param = torch.zeros(P, dtype=torch.int16, device=dev())
+    d_tensors = [torch.empty(n, dtype=torch.int16, device=dev()) for n in w.numels]
+    d_shards = [d_param[r * S:(r + 1) * S] for r in range(w.n_ranks)]
+    for t in range(1, w.steps + 1):
+        synth.device_normal_bf16(d_grad, w.seed, synth.KIND_GRAD, t, 0, 0, phi, synth.GRAD_SIGMA)
+        g = synth.normal_bf16(P, w.seed, synth.KIND_GRAD, t, 0, 0, phi, synth.GRAD_SIGMA)
+        for r in range(w.n_ranks):
+            sl = slice(r * S, (r + 1) * S)
+            zm.zero_shard_adamw_step(d_master[sl], d_m[sl], d_v[sl], d_grad[sl], d_shards[r], t,
+                                     lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                                     weight_decay=w.weight_decay)
+            st = states[r]
+            st["master"], st["exp_avg"], st["exp_avg_sq"], shards[r] = oracle.adamw_step(
+                st["master"], st["exp_avg"], st["exp_avg_sq"], g[sl], t, **HP)
+        zm.zero_gather_params(plan, d_shards, d_tensors)
+        want = oracle.gather_params(ref, shards)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_u16(d_grad), g, f"generated grad step {t}")
+        for i, (a, b) in enumerate(zip(d_tensors, want)):
+            assert_bits_equal(host_u16(a), b, f"step {t} tensor {i}")
+    full = {k: np.concatenate([s[k] for s in states]) for k in ("master", "exp_avg", "exp_avg_sq")}
+    for got, key in ((d_master, "master"), (d_m, "exp_avg"), (d_v, "exp_avg_sq")):
+        exact = assert_f32_close(host_f32(got), full[key], f"{name} {key}")
+        assert exact == 1.0, f"{key}: {exact:.6f} bit-identical"
+    assert (host_f32(d_master)[phi:] == 0).all(), "padding must stay zero"
+
+
+def test_gpt2_small_rank7_hundred_steps_clip(zm):
+    from oracle_workers import grad_sqnorms
+    w = synth.WORKLOADS["gpt2-small"]
+    ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
+    P, S, phi, rank = ref.padded_numel, ref.shard_numel, ref.numel, 7
+    steps = w.steps
+    note(f"gpt2-small: P={P} S={S}, {steps} steps on the GPU")
+    lo = rank * S
+    d_grad = torch.empty(P, dtype=torch.int16, device=dev())
+    d_master = torch.empty(S, dtype=torch.float32, device=dev())
+    synth.device_normal_f32(d_master, w.seed, synth.KIND_MASTER, 0, 0, lo, phi, synth.MASTER_SIGMA)
+    d_m = torch.zeros(S, dtype=torch.float32, device=dev())
+    d_v = torch.zeros(S, dtype=torch.float32, device=dev())
+    d_param = torch.zeros(S, dtype=torch.int16, device=dev())
+    d_parts = torch.zeros(w.n_ranks, dtype=torch.float64, device=dev())
+    d_scale = torch.zeros(1, dtype=torch.float32, device=dev())
+    d_scales = torch.zeros(steps, dtype=torch.float32, device=dev())
+    d_parts_all = torch.zeros(steps, w.n_ranks, dtype=torch.float64, device=dev())
+    for t in range(1, steps + 1):
+        synth.device_normal_bf16(d_grad, w.seed, synth.KIND_GRAD, t, 0, 0, phi, synth.GRAD_SIGMA)
+        for r in range(w.n_ranks):
+            zm.zero_grad_sqnorm(d_grad[r * S:(r + 1) * S], d_parts[r:r + 1])
+        zm.zero_clip_scale(d_parts, w.max_norm, d_scale)
+        zm.zero_shard_adamw_step(d_master, d_m, d_v, d_grad[lo:lo + S], d_param, t,
+                                 clip_scale=d_scale, **HP)
+        d_scales[t - 1:t].copy_(d_scale)
+        d_parts_all[t - 1].copy_(d_parts)
+    torch.cuda.synchronize()
+
+    note("gpt2-small: oracle norms over all ranks for every step (process pool)")
+    tasks = [(w.seed, synth.KIND_GRAD, t, 0, r * S, S, phi, synth.GRAD_SIGMA)
+             for t in range(1, steps + 1) for r in range(w.n_ranks)]
+    parts = np.array(grad_sqnorms(tasks)).reshape(steps, w.n_ranks)
+    got_parts = d_parts_all.cpu().numpy()
+    assert (np.abs(got_parts - parts) <= 1e-12 * parts).all(), "per-rank norm partials"
+    scales = np.array([oracle.clip_scale(list(parts[t]), w.max_norm) for t in range(steps)],
+                      dtype=np.float32)
+    got_scales = d_scales.cpu().numpy()
+    ulps = np.abs(got_scales.view(np.int32) - scales.view(np.int32))
+    assert ulps.max() <= 1, "clip coefficients"
+    note(f"gpt2-small: clip coefficients {scales.min():.6f}..{scales.max():.6f}, "
+         f"{int((ulps == 0).sum())}/{steps} bit-identical")
+
+    rng = np.random.default_rng(0)
+    starts = [0, S // 2 - 2048, S - 4096, int(rng.integers(0, S - 4096))]
+    for w0 in starts:
+        n = 4096
+        st = {"master": synth.normal_f32(n, w.seed, synth.KIND_MASTER, 0, 0, lo + w0, phi,
+                                         synth.MASTER_SIGMA),
+              "exp_avg": np.zeros(n, np.float32), "exp_avg_sq": np.zeros(n, np.float32)}
+        bits = None
+        for t in range(1, steps + 1):
+            g = synth.normal_bf16(n, w.seed, synth.KIND_GRAD, t, 0, lo + w0, phi, synth.GRAD_SIGMA)
+            st["master"], st["exp_avg"], st["exp_avg_sq"], bits = oracle.adamw_step(
+                st["master"], st["exp_avg"], st["exp_avg_sq"], g, t, clip=scales[t - 1], **HP)
+        sl = slice(w0, w0 + n)
+        assert_f32_close(host_f32(d_master[sl]), st["master"], f"master window {w0}")
+        assert_f32_close(host_f32(d_m[sl]), st["exp_avg"], f"exp_avg window {w0}")
+        assert_f32_close(host_f32(d_v[sl]), st["exp_avg_sq"], f"exp_avg_sq window {w0}")
+        assert_bf16_close(host_u16(d_param[sl]), bits, f"param window {w0}")
+
+
+def test_bench_pipeline_matches_oracle(zm):
+    import bench
+    setup = bench.Setup("gpt2-small", dev())
+    P, S, phi, rank, R = setup.P, setup.S, setup.phi, setup.rank, setup.replicas
+    ref = oracle.partition_plan(setup.workload.numels, setup.n_ranks, setup.workload.align)
+    note(f"bench pipeline: reduce of {R} replicas for rank {rank} of {setup.n_ranks}, S={S}")
+    steps = 2
+    for _ in range(steps):
+        setup.step()
+    torch.cuda.synchronize()
+
+    # oracle: every rank's reduced gradient (for the partials), then rank 7's steps
+    reps = [synth.normal_bf16(P, setup.seed, synth.KIND_REPLICA, 1, k, 0, phi, synth.GRAD_SIGMA)
+            for k in range(R)]
+    partials = []
+    for r in range(setup.n_ranks):
+        g = np.zeros(S, np.uint16)
+        oracle.reduce_shard(ref, r, reps, 0, g)
+        partials.append(oracle.sqnorm(g))
+    state = {"master": synth.normal_f32(S, setup.seed, synth.KIND_MASTER, 0, 0, rank * S, phi,
+                                        synth.MASTER_SIGMA),
+             "exp_avg": np.zeros(S, np.float32), "exp_avg_sq": np.zeros(S, np.float32)}
+    shards = [synth.normal_bf16(S, setup.seed, synth.KIND_PARAM, 0, 0, r * S, phi, synth.MASTER_SIGMA)
+              if r != rank else np.zeros(S, np.uint16) for r in range(setup.n_ranks)]
+    out = None
+    for t in range(1, steps + 1):
+        out = oracle.rank_step(ref, rank, reps, 0, state, shards, partials, t, setup.hyper.as_kwargs(),
+                               setup.max_norm)
+    assert_bits_equal(host_u16(setup.rs.grad), out["shard_grad"], "reduced shard grad")
+    got_parts = setup.rs.partials.cpu().numpy()
+    want_parts = np.array(out["partials"])
+    own = got_parts[setup.n_ranks]
+    assert abs(own - want_parts[rank]) <= 1e-12 * want_parts[rank]
+    others = np.delete(np.arange(setup.n_ranks), rank)
+    assert (np.abs(got_parts[others] - want_parts[others]) <= 1e-12 * want_parts[others]).all()
+    got_scale = np.float32(setup.rs.scale.item())
+    assert abs(int(got_scale.view(np.int32)) - int(np.float32(out["clip"]).view(np.int32))) <= 1
+    for got, key in ((setup.rs.master, "master"), (setup.rs.exp_avg, "exp_avg"),
+                     (setup.rs.exp_avg_sq, "exp_avg_sq")):
+        assert_f32_close(host_f32(got), state[key], key)
+    for i, (a, b) in enumerate(zip(setup.rs.tensors, out["tensors"])):
+        assert_bf16_close(host_u16(a), b, f"gathered tensor {i}")

@@ -377,3 +377,12 @@ def test_rank_step_composes_parts():
     assert out["partials"][2] == oracle.sqnorm(g)
     assert out["clip"] == oracle.clip_scale([0.1, 0.2, oracle.sqnorm(g), 0.3], 1.0)
     assert len(out["tensors"]) == 3
+
+
+def test_sqnorm_accumulator_chunks_equal_whole():
+    rng = np.random.default_rng(21)
+    b = _random_bf16(rng, 50_000, lo=-60, hi=60)
+    acc = oracle.SqnormAccumulator()
+    for i in range(0, len(b), 7_777):
+        acc.add(b[i:i + 7_777])
+    assert acc.value() == oracle.sqnorm_fsum(b)

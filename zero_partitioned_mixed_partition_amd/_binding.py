@@ -1,0 +1,249 @@
+"""ctypes binding of libzero_mi355x.so: the same entry points, argument marshalling only.
+
+Device buffers are torch tensors on a ROCm device (torch supplies memory and
+streams, nothing else); every computation runs in the library's HIP kernels.
+If the library is not built, importing this module raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_mi355x.so")
+
+ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_ENOMEM, ZERO_EHIP, ZERO_ENOSPACE = range(6)
+ZERO_MAX_REPLICAS = 64
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                      "(hipcc, gfx950); there is no CPU fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+c_i32, c_i64, c_dbl, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t, \
+    ctypes.c_void_p
+
+
+class zero_segment(ctypes.Structure):
+    _fields_ = [("tensor", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("tensor_offset", ctypes.c_int64), ("shard_offset", ctypes.c_int64),
+                ("length", ctypes.c_int64)]
+
+
+def _fn(name, restype, argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = argtypes
+    return f
+
+
+_partition_plan = _fn("zero_partition_plan", c_i32,
+                      [ctypes.POINTER(c_i64), c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)])
+_plan_free = _fn("zero_plan_free", None, [c_vp])
+_plan_numel = _fn("zero_plan_numel", c_i64, [c_vp])
+_plan_padded = _fn("zero_plan_padded_numel", c_i64, [c_vp])
+_plan_shard = _fn("zero_plan_shard_numel", c_i64, [c_vp])
+_plan_ntensors = _fn("zero_plan_num_tensors", c_i32, [c_vp])
+_plan_nranks = _fn("zero_plan_num_ranks", c_i32, [c_vp])
+_plan_offset = _fn("zero_plan_tensor_offset", c_i64, [c_vp, c_i32])
+_plan_nsegs = _fn("zero_plan_num_segments", c_i32, [c_vp, c_i32])
+_plan_segments = _fn("zero_plan_segments", c_i32,
+                     [c_vp, c_i32, ctypes.POINTER(zero_segment), c_i32, ctypes.POINTER(c_i32)])
+_plan_memory = _fn("zero_plan_memory_bytes", c_i32, [c_vp, c_i32, c_i32, ctypes.POINTER(c_dbl)])
+_reduce = _fn("zero_grad_reduce_shard", c_i32,
+              [c_vp, c_i32, ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp])
+_sqnorm = _fn("zero_grad_sqnorm", c_i32, [c_vp, c_i64, c_vp, c_vp, c_sz, c_vp])
+_ws_bytes = _fn("zero_sqnorm_workspace_bytes", c_sz, [])
+_clip = _fn("zero_clip_scale", c_i32, [c_vp, c_i32, c_dbl, c_vp, c_vp])
+_adamw = _fn("zero_shard_adamw_step", c_i32,
+             [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl, c_vp,
+              c_vp])
+_gather = _fn("zero_gather_params", c_i32, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp])
+_status_string = _fn("zero_status_string", ctypes.c_char_p, [c_i32])
+_last_error = _fn("zero_last_error", ctypes.c_char_p, [])
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = _last_error().decode()
+        super().__init__(f"{where}: {_status_string(status).decode()} ({detail})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != ZERO_OK:
+        raise ZeroError(status, where)
+
+
+# --------------------------------------------------------------------------- plan
+
+class Plan:
+    """Owner of a zero_plan handle."""
+
+    def __init__(self, handle: int):
+        self._h = c_vp(handle)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _plan_free(h)
+            self._h = c_vp(None)
+
+    @property
+    def handle(self) -> c_vp:
+        return self._h
+
+    @property
+    def numel(self) -> int:
+        return _plan_numel(self._h)
+
+    @property
+    def padded_numel(self) -> int:
+        return _plan_padded(self._h)
+
+    @property
+    def shard_numel(self) -> int:
+        return _plan_shard(self._h)
+
+    @property
+    def num_tensors(self) -> int:
+        return _plan_ntensors(self._h)
+
+    @property
+    def num_ranks(self) -> int:
+        return _plan_nranks(self._h)
+
+    def tensor_offset(self, t: int) -> int:
+        return _plan_offset(self._h, t)
+
+    def num_segments(self, rank: int) -> int:
+        return _plan_nsegs(self._h, rank)
+
+    def segments(self, rank: int) -> List[Tuple[int, int, int, int]]:
+        """(tensor, offset in tensor, offset in shard, length) in flat order."""
+        n = _plan_nsegs(self._h, rank)
+        if n < 0:
+            raise ValueError("rank out of range")
+        arr = (zero_segment * max(n, 1))()
+        count = c_i32(0)
+        _check(_plan_segments(self._h, rank, arr, n, ctypes.byref(count)), "zero_plan_segments")
+        return [(s.tensor, s.tensor_offset, s.shard_offset, s.length) for s in arr[:count.value]]
+
+    def memory_bytes(self, stage: int, padded: bool = False) -> float:
+        out = c_dbl(0.0)
+        _check(_plan_memory(self._h, stage, int(padded), ctypes.byref(out)),
+               "zero_plan_memory_bytes")
+        return out.value
+
+
+def zero_partition_plan(numels: Sequence[int], n_ranks: int, align_elems: int = 128) -> Plan:
+    arr = (c_i64 * max(len(numels), 1))(*[int(n) for n in numels])
+    h = c_vp(None)
+    _check(_partition_plan(arr, len(numels), n_ranks, align_elems, ctypes.byref(h)),
+           "zero_partition_plan")
+    return Plan(h.value)
+
+
+# --------------------------------------------------------------------------- device calls
+
+def _stream(stream, tensor) -> int:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream(tensor.device).cuda_stream
+
+
+def _ptr(t, elem_size: int, what: str) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if t.element_size() != elem_size:
+        raise ValueError(f"{what} must have {elem_size}-byte elements")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+_ws_cache = {}
+
+
+def sqnorm_workspace(device) -> "object":
+    """A cached device workspace of zero_sqnorm_workspace_bytes() bytes (torch-allocated)."""
+    import torch
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = torch.empty(_ws_bytes(), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def zero_sqnorm_workspace_bytes() -> int:
+    return _ws_bytes()
+
+
+def zero_grad_reduce_shard(plan: Plan, rank: int, replicas: Sequence, begin: int, count: int,
+                           shard_grad, sqnorm_out=None, workspace=None, stream=None) -> None:
+    """replicas: R device tensors (2-byte elements) covering flat window [begin, begin+count)."""
+    ptrs = (c_vp * max(len(replicas), 1))(*[_ptr(r, 2, "replica") for r in replicas])
+    out = _ptr(shard_grad, 2, "shard_grad")
+    sq = _ptr(sqnorm_out, 8, "sqnorm_out")
+    if sqnorm_out is not None and workspace is None:
+        workspace = sqnorm_workspace(shard_grad.device)
+    ws = workspace.data_ptr() if workspace is not None else 0
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_reduce(plan.handle, rank, ptrs, len(replicas), begin, count, out, sq, ws, wsb,
+                   _stream(stream, shard_grad)), "zero_grad_reduce_shard")
+
+
+def zero_grad_sqnorm(grad, sqnorm_out, n: Optional[int] = None, workspace=None, stream=None) -> None:
+    n = grad.numel() if n is None else n
+    if workspace is None:
+        workspace = sqnorm_workspace(grad.device)
+    _check(_sqnorm(_ptr(grad, 2, "grad"), n, _ptr(sqnorm_out, 8, "sqnorm_out"), workspace.data_ptr(),
+                   workspace.numel() * workspace.element_size(), _stream(stream, grad)),
+           "zero_grad_sqnorm")
+
+
+def zero_clip_scale(partials, max_norm: float, scale_out, n_partials: Optional[int] = None,
+                    stream=None) -> None:
+    n = partials.numel() if n_partials is None else n_partials
+    _check(_clip(_ptr(partials, 8, "partials"), n, float(max_norm), _ptr(scale_out, 4, "scale_out"),
+                 _stream(stream, partials)), "zero_clip_scale")
+
+
+def zero_shard_adamw_step(master, exp_avg, exp_avg_sq, grad, param_out, step: int, lr: float,
+                          beta1: float, beta2: float, eps: float, weight_decay: float,
+                          clip_scale=None, n: Optional[int] = None, stream=None) -> None:
+    n = master.numel() if n is None else n
+    for t, what in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad"),
+                    (param_out, "param_out")):
+        if t.numel() < n:
+            raise ValueError(f"{what} holds fewer than n elements")
+    _check(_adamw(_ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                  _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(grad, 2, "grad"),
+                  _ptr(param_out, 2, "param_out"), n, step, lr, beta1, beta2, eps, weight_decay,
+                  _ptr(clip_scale, 4, "clip_scale"), _stream(stream, master)),
+           "zero_shard_adamw_step")
+
+
+def zero_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, stream=None) -> None:
+    if len(shards) != plan.num_ranks or len(tensors) != plan.num_tensors:
+        raise ValueError("need N_d shards and T tensors")
+    sp = (c_vp * max(len(shards), 1))(*[_ptr(s, 2, "shard") for s in shards])
+    tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
+    ref = shards[0] if len(shards) else None
+    _check(_gather(plan.handle, sp, tp, _stream(stream, ref) if ref is not None else 0),
+           "zero_gather_params")
+
+
+def zero_status_string(status: int) -> str:
+    return _status_string(status).decode()
+
+
+def zero_last_error() -> str:
+    return _last_error().decode()

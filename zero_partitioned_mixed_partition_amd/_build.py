@@ -1,0 +1,64 @@
+"""Builds libzero_mi355x.so in-tree with hipcc for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from typing import List, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libzero_mi355x.so")
+
+SOURCES = ["status.cpp", "plan.cpp", "adamw.hip", "reduce.hip", "gather.hip"]
+
+# -ffp-contract=off: the AdamW and reduction arithmetic is specified operation
+# by operation; no multiply-add fusion. Packed fp32 instructions are disabled.
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-ffp-contract=off", f"-I{INCLUDE}", f"-I{CSRC}"]
+DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fno-gpu-rdc"]
+
+
+def _compile(src: str, obj: str, defines: List[str], save_temps: Optional[str]) -> List[str]:
+    cmd = ["hipcc", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + defines
+    if src.endswith(".hip"):
+        cmd += DEVICE
+        if save_temps:
+            cmd += [f"-save-temps={'obj'}"]
+    else:
+        pass
+    return cmd
+
+
+def build(out: str = LIB, defines: Optional[List[str]] = None, save_temps: Optional[str] = None,
+          verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    defines = list(defines or [])
+    objdir = save_temps or os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cmds = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append(_compile(src, obj, defines, save_temps))
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True, cwd=objdir)
+
+    with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
+        list(ex.map(run, cmds))
+    tmp = out + ".tmp"
+    link = ["hipcc", "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
+    run(link)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)

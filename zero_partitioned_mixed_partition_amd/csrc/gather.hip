@@ -1,0 +1,123 @@
+// Gather of bf16 parameter shards into per-tensor parameters (gfx950).
+//
+// "Zero Redundancy Optimizer (ZeRO) and Fully Sharded Data Parallelism (FSDP):
+// Mathematical Foundations ...", section "Execution Flow for ZeRO-1", step 4:
+// the all-gather rebuilds the complete 16-bit parameters from every rank's
+// shard; section "FSDP-1": the shards are equal chunks of one flat buffer, so
+// each tensor is a slice of the shards' concatenation. The plan lists that
+// slice as segments (tensor, offset in tensor, shard, offset in shard,
+// length); this kernel copies every segment.
+//
+// Memory: 2 bytes read and 2 written per parameter. The segment table travels
+// in the kernel arguments, kSegs segments per launch (no device-side table,
+// no host-to-device copy, nothing allocated): workgroup b finds its segment by
+// a binary search over the per-segment workgroup prefix, then copies a chunk
+// of kChunk elements with 16-byte non-temporal accesses when source and
+// destination are 16-byte co-aligned, element by element otherwise.
+#include <hip/hip_runtime.h>
+
+#include <string>
+#include <vector>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSegs = 40;                       // segments per launch (kernarg ~1.3 KB)
+#ifndef ZERO_GATHER_VECS_PER_THREAD
+#define ZERO_GATHER_VECS_PER_THREAD 4
+#endif
+constexpr int64_t kChunk = int64_t(kThreads) * 8 * ZERO_GATHER_VECS_PER_THREAD;   // elements
+
+struct SegBatch {
+    const uint16_t* src[kSegs];
+    uint16_t* dst[kSegs];
+    int64_t len[kSegs];
+    int64_t first_block[kSegs + 1];   // workgroups [first_block[s], first_block[s+1]) copy segment s
+    int32_t n;
+};
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
+    const int64_t blk = blockIdx.x;
+    int lo = 0, hi = b.n - 1;                         // find s with first_block[s] <= blk < first_block[s+1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
+    }
+    const int s = lo;
+    const int64_t start = (blk - b.first_block[s]) * kChunk;
+    const int64_t len = b.len[s] - start < kChunk ? b.len[s] - start : kChunk;
+    const uint16_t* src = b.src[s] + start;
+    uint16_t* dst = b.dst[s] + start;
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(src), da = reinterpret_cast<uintptr_t>(dst);
+    if (((sa ^ da) & 15u) == 0) {
+        // Co-aligned: scalar head up to the 16-byte boundary, vector body, scalar tail.
+        int64_t head = static_cast<int64_t>(((16u - (da & 15u)) & 15u) / 2u);
+        if (head > len) head = len;
+        if (threadIdx.x < head) dst[threadIdx.x] = src[threadIdx.x];
+        const int64_t body = (len - head) / 8;
+        const zero::dev::u32x4* s4 = reinterpret_cast<const zero::dev::u32x4*>(src + head);
+        zero::dev::u32x4* d4 = reinterpret_cast<zero::dev::u32x4*>(dst + head);
+#pragma unroll
+        for (int u = 0; u < ZERO_GATHER_VECS_PER_THREAD; ++u) {
+            const int64_t i = static_cast<int64_t>(u) * kThreads + threadIdx.x;
+            if (i < body) zero::dev::st_stream(d4 + i, zero::dev::ld_stream(s4 + i));
+        }
+        const int64_t done = head + body * 8;
+        const int64_t t = done + threadIdx.x;
+        if (t < len) dst[t] = src[t];
+    } else {
+        for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+    }
+}
+
+}  // namespace
+
+extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* shards,
+                                          uint16_t* const* tensors, hipStream_t stream) {
+    using zero::fail;
+    zero::clear_error();
+    if (plan == nullptr || shards == nullptr)
+        return fail(ZERO_EINVAL, "zero_gather_params: NULL plan or shards");
+    if (!plan->numels.empty() && tensors == nullptr)
+        return fail(ZERO_EINVAL, "zero_gather_params: NULL tensors");
+    for (int32_t r = 0; r < plan->n_ranks; ++r)
+        if (plan->shard > 0 && shards[r] == nullptr)
+            return fail(ZERO_EINVAL, "zero_gather_params: NULL shard " + std::to_string(r));
+    for (size_t t = 0; t < plan->numels.size(); ++t)
+        if (plan->numels[t] > 0 && tensors[t] == nullptr)
+            return fail(ZERO_EINVAL, "zero_gather_params: NULL tensor " + std::to_string(t));
+
+    SegBatch batch{};
+    auto flush = [&]() -> zero_status {
+        if (batch.n == 0) return ZERO_OK;
+        const int64_t blocks = batch.first_block[batch.n];
+        if (blocks > 0x7FFFFFFF) return fail(ZERO_ERANGE, "zero_gather_params: grid too large");
+        hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                           stream, batch);
+        batch.n = 0;
+        batch.first_block[0] = 0;
+        return zero::check_hip(hipGetLastError(), "zero_gather_params launch");
+    };
+    for (const zero_segment& seg : plan->all) {
+        const int64_t chunks = (seg.length + kChunk - 1) / kChunk;
+        const int64_t next = batch.first_block[batch.n] + chunks;
+        if (next > 0x7FFFFFFF) {   // keep one launch's grid within 2^31 workgroups
+            zero_status st = flush();
+            if (st != ZERO_OK) return st;
+        }
+        const int i = batch.n;
+        batch.src[i] = shards[seg.rank] + seg.shard_offset;
+        batch.dst[i] = tensors[seg.tensor] + seg.tensor_offset;
+        batch.len[i] = seg.length;
+        batch.first_block[i + 1] = batch.first_block[i] + chunks;
+        batch.n = i + 1;
+        if (batch.n == kSegs) {
+            zero_status st = flush();
+            if (st != ZERO_OK) return st;
+        }
+    }
+    return flush();
+}

@@ -1,0 +1,39 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "zero_mi355x.h"
+
+struct zero_plan {
+    int32_t n_ranks = 0;
+    int32_t align = 0;
+    int64_t numel = 0;    // Phi
+    int64_t padded = 0;   // P
+    int64_t shard = 0;    // S
+    std::vector<int64_t> numels;
+    std::vector<int64_t> offsets;
+    std::vector<std::vector<zero_segment>> by_rank;   // segments of each rank, flat order
+    std::vector<zero_segment> all;                    // every segment, flat order
+};
+
+namespace zero {
+
+// Records a readable detail for zero_last_error() and returns `st`.
+zero_status fail(zero_status st, const std::string& detail);
+// Maps a HIP error to ZERO_EHIP with its string, or returns ZERO_OK.
+zero_status check_hip(int hip_error, const char* what);
+// Clears the thread's last error (called on entry of each ABI function).
+void clear_error();
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// Workgroups of `kernel` (at `threads` per workgroup, no dynamic LDS) that fit on
+// the whole current device at once: CU count times the occupancy limit from
+// registers and LDS. Falls back to 4 per CU if the query fails.
+int device_resident_blocks(const void* kernel, int threads);
+
+}  // namespace zero

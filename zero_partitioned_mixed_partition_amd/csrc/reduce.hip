@@ -1,0 +1,324 @@
+// Shard-local gradient reduction, squared-norm partials and the clip
+// coefficient (gfx950).
+//
+// "Zero Redundancy Optimizer (ZeRO) and Fully Sharded Data Parallelism (FSDP):
+// Mathematical Foundations ...", section "Execution Flow for ZeRO-1", step 2:
+// each rank receives the gradient of its own partition averaged over the
+// ranks; section "ZeRO-Stage 2": the reduction happens bucket by bucket. The
+// kernel here is the receiving rank's arithmetic: R replica buffers in HBM,
+// summed in replica order in fp32, divided by R, rounded once to bf16.
+//
+// Memory: per shard element R bf16 reads and one bf16 write, (2R + 2) bytes.
+// Each thread handles 8 elements per 16-byte access and keeps up to 8 replica
+// loads in flight before it adds them, in order, into its accumulators.
+//
+// The squared norm (not on the pages; needed by the global-norm clip) sums
+// exact fp64 squares of bf16 values: per-thread fp64 partials, a butterfly in
+// each wavefront, waves in order through LDS, one partial per workgroup in the
+// caller's workspace, then a single-workgroup pass adds the workgroup partials
+// in a fixed order. No floating-point atomics: results repeat bit for bit.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+using zero::dev::u32x4;
+
+constexpr int kThreads = 256;
+constexpr int kMaxPartials = 4096;           // workgroup partials in the workspace
+constexpr int kReplicaBatch = 8;             // replica loads in flight per thread
+#ifndef ZERO_REDUCE_BLOCKS_PER_CU
+#define ZERO_REDUCE_BLOCKS_PER_CU 8
+#endif
+#ifndef ZERO_SQNORM_BLOCKS_PER_CU
+#define ZERO_SQNORM_BLOCKS_PER_CU 8
+#endif
+
+struct ReplicaTable {
+    const uint16_t* p[ZERO_MAX_REPLICAS];
+};
+
+__device__ __forceinline__ double sq8(const u32x4& w) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const double a = static_cast<double>(zero::dev::lo_bf16(ws[j]));
+        const double b = static_cast<double>(zero::dev::hi_bf16(ws[j]));
+        s += a * a;
+        s += b * b;
+    }
+    return s;
+}
+
+__device__ __forceinline__ double sq1(uint16_t h) {
+    const double a = static_cast<double>(zero::dev::bf16_to_f32(h));
+    return a * a;
+}
+
+__device__ __forceinline__ void store_partial(double sq, double* partials) {
+    __shared__ double lds[kThreads / zero::dev::kWave];
+    const double total = zero::dev::block_sum<kThreads>(sq, lds);
+    if (threadIdx.x == 0) partials[blockIdx.x] = total;
+}
+
+// Vector path. src_off: element offset into each replica buffer of the first
+// element to reduce; out: first output element; n: elements to reduce. The
+// caller guarantees every replica + src_off and out are 16-byte aligned.
+template <bool kNorm>
+__global__ __launch_bounds__(kThreads) void reduce_vec(ReplicaTable reps, int n_rep,
+                                                       int64_t src_off,
+                                                       uint16_t* __restrict__ out, int64_t n,
+                                                       double* __restrict__ partials) {
+    const float r = static_cast<float>(n_rep);
+    const int64_t groups = n / 8;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    double sq = 0.0;
+    for (int64_t i = tid; i < groups; i += stride) {
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int k0 = 0; k0 < n_rep; k0 += kReplicaBatch) {
+            u32x4 x[kReplicaBatch];
+            const int kn = n_rep - k0 < kReplicaBatch ? n_rep - k0 : kReplicaBatch;
+#pragma unroll
+            for (int k = 0; k < kReplicaBatch; ++k)
+                if (k < kn)
+                    x[k] = zero::dev::ld_stream(
+                        reinterpret_cast<const u32x4*>(reps.p[k0 + k] + src_off) + i);
+#pragma unroll
+            for (int k = 0; k < kReplicaBatch; ++k) {
+                if (k < kn) {
+                    const uint32_t w[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(w[j]);
+                        acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(w[j]);
+                    }
+                }
+            }
+        }
+        u32x4 o;
+        o.x = zero::dev::pack_bf16(acc[0] / r, acc[1] / r);
+        o.y = zero::dev::pack_bf16(acc[2] / r, acc[3] / r);
+        o.z = zero::dev::pack_bf16(acc[4] / r, acc[5] / r);
+        o.w = zero::dev::pack_bf16(acc[6] / r, acc[7] / r);
+        zero::dev::st_stream(reinterpret_cast<u32x4*>(out) + i, o);
+        if (kNorm) sq += sq8(o);
+    }
+    // Ragged tail (< 8 elements), one per thread of the first threads.
+    const int64_t tail = n - groups * 8;
+    if (tid < tail) {
+        const int64_t e = groups * 8 + tid;
+        float acc = 0.0f;
+        for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(reps.p[k][src_off + e]);
+        const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
+        out[e] = h;
+        if (kNorm) sq += sq1(h);
+    }
+    if (kNorm) store_partial(sq, partials);
+}
+
+// Any alignment: one element per thread.
+template <bool kNorm>
+__global__ __launch_bounds__(kThreads) void reduce_scalar(ReplicaTable reps, int n_rep,
+                                                          int64_t src_off,
+                                                          uint16_t* __restrict__ out, int64_t n,
+                                                          double* __restrict__ partials) {
+    const float r = static_cast<float>(n_rep);
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    double sq = 0.0;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < n; e += stride) {
+        float acc = 0.0f;
+        for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(reps.p[k][src_off + e]);
+        const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
+        out[e] = h;
+        if (kNorm) sq += sq1(h);
+    }
+    if (kNorm) store_partial(sq, partials);
+}
+
+__global__ __launch_bounds__(kThreads) void sqnorm_vec(const uint16_t* __restrict__ g, int64_t n,
+                                                       double* __restrict__ partials) {
+    const int64_t groups = n / 8;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    double sq = 0.0;
+    for (int64_t i = tid; i < groups; i += stride)
+        sq += sq8(zero::dev::ld_stream(reinterpret_cast<const u32x4*>(g) + i));
+    const int64_t tail = n - groups * 8;
+    if (tid < tail) sq += sq1(g[groups * 8 + tid]);
+    store_partial(sq, partials);
+}
+
+__global__ __launch_bounds__(kThreads) void sqnorm_scalar(const uint16_t* __restrict__ g, int64_t n,
+                                                          double* __restrict__ partials) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    double sq = 0.0;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < n; e += stride)
+        sq += sq1(g[e]);
+    store_partial(sq, partials);
+}
+
+// Adds partials[0..count) in a fixed order into out[0]: thread t sums
+// t, t+256, ... sequentially, then the fixed block tree.
+__global__ __launch_bounds__(kThreads) void finish_sum(const double* __restrict__ partials,
+                                                       int count, double* __restrict__ out) {
+    __shared__ double lds[kThreads / zero::dev::kWave];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < count; i += kThreads) s += partials[i];
+    const double total = zero::dev::block_sum<kThreads>(s, lds);
+    if (threadIdx.x == 0) out[0] = total;
+}
+
+__global__ void write_zero(double* out) {
+    if (threadIdx.x == 0) out[0] = 0.0;
+}
+
+// Global norm from per-rank partials, in index order; the coefficient of the
+// clip-by-total-norm convention, NaN when the norm is not finite.
+__global__ void clip_kernel(const double* __restrict__ partials, int n, double max_norm,
+                            float* __restrict__ scale) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    double total = 0.0;
+    for (int i = 0; i < n; ++i) total += partials[i];
+    float out;
+    if (!isfinite(total)) {
+        out = __builtin_nanf("");
+    } else if (!(max_norm > 0.0)) {
+        out = 1.0f;
+    } else {
+        const double coef = max_norm / (sqrt(total) + 1e-6);
+        out = static_cast<float>(coef < 1.0 ? coef : 1.0);
+    }
+    scale[0] = out;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int grid_for(int64_t work_items, int blocks_per_cu) {
+    int64_t blocks = (work_items + kThreads - 1) / kThreads;
+    const int64_t cap = static_cast<int64_t>(zero::device_cu_count()) * blocks_per_cu;
+    if (blocks > cap) blocks = cap;
+    if (blocks > kMaxPartials) blocks = kMaxPartials;
+    if (blocks < 1) blocks = 1;
+    return static_cast<int>(blocks);
+}
+
+}  // namespace
+
+extern "C" size_t zero_sqnorm_workspace_bytes(void) { return kMaxPartials * sizeof(double); }
+
+extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
+                                              const uint16_t* const* replicas, int32_t n_replicas,
+                                              int64_t begin, int64_t count, uint16_t* shard_grad,
+                                              double* sqnorm_out, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+    using zero::fail;
+    zero::clear_error();
+    if (plan == nullptr || replicas == nullptr || shard_grad == nullptr)
+        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: NULL plan, replicas or shard_grad");
+    if (rank < 0 || rank >= plan->n_ranks)
+        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: rank out of range");
+    if (n_replicas < 1 || n_replicas > ZERO_MAX_REPLICAS)
+        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: n_replicas must be 1.." +
+                                     std::to_string(ZERO_MAX_REPLICAS));
+    if (begin < 0 || count < 0 || begin > plan->padded || count > plan->padded - begin)
+        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: window outside [0, P)");
+    if (sqnorm_out != nullptr) {
+        if (workspace == nullptr) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: NULL workspace");
+        if (workspace_bytes < zero_sqnorm_workspace_bytes())
+            return fail(ZERO_ENOSPACE, "zero_grad_reduce_shard: workspace too small");
+    }
+    ReplicaTable table{};
+    for (int32_t k = 0; k < n_replicas; ++k) {
+        if (replicas[k] == nullptr) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: NULL replica");
+        table.p[k] = replicas[k];
+    }
+    const int64_t shard_lo = static_cast<int64_t>(rank) * plan->shard;
+    const int64_t lo = begin > shard_lo ? begin : shard_lo;
+    const int64_t end = begin + count, shard_hi = shard_lo + plan->shard;
+    const int64_t hi = end < shard_hi ? end : shard_hi;
+    double* partials = static_cast<double*>(workspace);
+    if (lo >= hi) {
+        if (sqnorm_out != nullptr) {
+            hipLaunchKernelGGL(write_zero, dim3(1), dim3(64), 0, stream, sqnorm_out);
+            return zero::check_hip(hipGetLastError(), "zero_grad_reduce_shard launch");
+        }
+        return ZERO_OK;
+    }
+    const int64_t n = hi - lo, src_off = lo - begin;
+    uint16_t* out = shard_grad + (lo - shard_lo);
+    bool vec = aligned16(out);
+    for (int32_t k = 0; k < n_replicas && vec; ++k) vec = aligned16(replicas[k] + src_off);
+    const bool norm = sqnorm_out != nullptr;
+    const int blocks = grid_for(vec ? n / 8 : n, ZERO_REDUCE_BLOCKS_PER_CU);
+    if (vec) {
+        if (norm)
+            hipLaunchKernelGGL(reduce_vec<true>, dim3(blocks), dim3(kThreads), 0, stream, table,
+                               n_replicas, src_off, out, n, partials);
+        else
+            hipLaunchKernelGGL(reduce_vec<false>, dim3(blocks), dim3(kThreads), 0, stream, table,
+                               n_replicas, src_off, out, n, partials);
+    } else {
+        if (norm)
+            hipLaunchKernelGGL(reduce_scalar<true>, dim3(blocks), dim3(kThreads), 0, stream, table,
+                               n_replicas, src_off, out, n, partials);
+        else
+            hipLaunchKernelGGL(reduce_scalar<false>, dim3(blocks), dim3(kThreads), 0, stream, table,
+                               n_replicas, src_off, out, n, partials);
+    }
+    zero_status st = zero::check_hip(hipGetLastError(), "zero_grad_reduce_shard launch");
+    if (st != ZERO_OK || !norm) return st;
+    hipLaunchKernelGGL(finish_sum, dim3(1), dim3(kThreads), 0, stream, partials, blocks, sqnorm_out);
+    return zero::check_hip(hipGetLastError(), "zero_grad_reduce_shard finish launch");
+}
+
+extern "C" zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double* sqnorm_out,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    using zero::fail;
+    zero::clear_error();
+    if (n < 0) return fail(ZERO_EINVAL, "zero_grad_sqnorm: n < 0");
+    if (sqnorm_out == nullptr || (n > 0 && grad == nullptr) || workspace == nullptr)
+        return fail(ZERO_EINVAL, "zero_grad_sqnorm: NULL pointer");
+    if (workspace_bytes < zero_sqnorm_workspace_bytes())
+        return fail(ZERO_ENOSPACE, "zero_grad_sqnorm: workspace too small");
+    double* partials = static_cast<double*>(workspace);
+    if (n == 0) {
+        hipLaunchKernelGGL(write_zero, dim3(1), dim3(64), 0, stream, sqnorm_out);
+        return zero::check_hip(hipGetLastError(), "zero_grad_sqnorm launch");
+    }
+    const bool vec = aligned16(grad);
+    const int blocks = grid_for(vec ? n / 8 : n, ZERO_SQNORM_BLOCKS_PER_CU);
+    if (vec)
+        hipLaunchKernelGGL(sqnorm_vec, dim3(blocks), dim3(kThreads), 0, stream, grad, n, partials);
+    else
+        hipLaunchKernelGGL(sqnorm_scalar, dim3(blocks), dim3(kThreads), 0, stream, grad, n, partials);
+    zero_status st = zero::check_hip(hipGetLastError(), "zero_grad_sqnorm launch");
+    if (st != ZERO_OK) return st;
+    hipLaunchKernelGGL(finish_sum, dim3(1), dim3(kThreads), 0, stream, partials, blocks, sqnorm_out);
+    return zero::check_hip(hipGetLastError(), "zero_grad_sqnorm finish launch");
+}
+
+extern "C" zero_status zero_clip_scale(const double* partials, int32_t n_partials, double max_norm,
+                                       float* scale_out, hipStream_t stream) {
+    using zero::fail;
+    zero::clear_error();
+    if (partials == nullptr || scale_out == nullptr)
+        return fail(ZERO_EINVAL, "zero_clip_scale: NULL pointer");
+    if (n_partials < 1 || n_partials > 65536)
+        return fail(ZERO_EINVAL, "zero_clip_scale: n_partials must be 1..65536");
+    if (std::isnan(max_norm)) return fail(ZERO_EINVAL, "zero_clip_scale: max_norm is NaN");
+    hipLaunchKernelGGL(clip_kernel, dim3(1), dim3(64), 0, stream, partials, n_partials, max_norm,
+                       scale_out);
+    return zero::check_hip(hipGetLastError(), "zero_clip_scale launch");
+}

@@ -1,0 +1,136 @@
+"""One data-parallel rank's optimizer step as a sequence of C-ABI calls.
+
+"Zero Redundancy Optimizer (ZeRO) and Fully Sharded Data Parallelism (FSDP):
+Mathematical Foundations ...", section "Execution Flow for ZeRO-1", steps 2-4,
+with section "ZeRO-Stage 2"'s bucketed reduction:
+
+  1. zero_grad_reduce_shard  per gradient window (whole flat buffer or bucket):
+                             the rank's averaged slice, plus its squared norm
+  2. zero_clip_scale         global-norm clip coefficient from every partial
+  3. zero_shard_adamw_step   fp32 master/m/v update, bf16 shard emitted into
+                             the rank's slot of the parameter shards
+  4. zero_gather_params      all shards -> per-tensor bf16 parameters
+
+Everything stays on the device and on one stream; nothing synchronises with
+the host inside a step. The other ranks' norm partials and parameter shards
+are inputs: on a cluster they arrive through a scalar all-reduce and the
+parameter all-gather.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _binding as zb
+
+
+@dataclass
+class Hyper:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+
+    def as_kwargs(self) -> dict:
+        return dict(lr=self.lr, beta1=self.beta1, beta2=self.beta2, eps=self.eps,
+                    weight_decay=self.weight_decay)
+
+
+class RankStep:
+    """Device state of one rank and the call sequence of its step.
+
+    plan         zero_partition_plan of the model's tensor list.
+    rank         this rank.
+    n_windows    gradient windows reduced per step (1 for a whole flat buffer,
+                 the number of buckets that meet the shard otherwise).
+    max_norm     clip threshold (<= 0: no clipping).
+    """
+
+    def __init__(self, plan: zb.Plan, rank: int, n_windows: int, hyper: Hyper, max_norm: float,
+                 device: torch.device, gather: bool = True):
+        self.plan, self.rank, self.hyper, self.max_norm = plan, rank, hyper, max_norm
+        self.device = device
+        s, nd = plan.shard_numel, plan.num_ranks
+        self.master = torch.zeros(s, dtype=torch.float32, device=device)
+        self.exp_avg = torch.zeros(s, dtype=torch.float32, device=device)
+        self.exp_avg_sq = torch.zeros(s, dtype=torch.float32, device=device)
+        self.grad = torch.zeros(s, dtype=torch.int16, device=device)
+        # per-rank partials [0, N_d) (own slot left 0), then one per own window
+        self.partials = torch.zeros(nd + n_windows, dtype=torch.float64, device=device)
+        self.scale = torch.ones(1, dtype=torch.float32, device=device)
+        self.param_shards = [torch.zeros(s, dtype=torch.int16, device=device) for _ in range(nd)]
+        self.tensors: List[torch.Tensor] = []
+        if gather:
+            self.tensors = [torch.empty(max(n, 0), dtype=torch.int16, device=device)
+                            for n in plan_numels(plan)]
+        self.workspace = torch.empty(zb.zero_sqnorm_workspace_bytes(), dtype=torch.uint8,
+                                     device=device)
+        self.n_windows = n_windows
+        self.t = 0
+
+    def set_remote_partials(self, partials: Sequence[float]) -> None:
+        p = torch.tensor(list(partials), dtype=torch.float64)
+        p[self.rank] = 0.0
+        self.partials[:self.plan.num_ranks].copy_(p.to(self.device))
+
+    def reduce(self, windows: Sequence[Tuple[int, int, Sequence[torch.Tensor]]], stream=None):
+        """windows: (begin, count, replica tensors) per window, in arrival order."""
+        if len(windows) != self.n_windows:
+            raise ValueError("window count differs from the one the step was built for")
+        nd = self.plan.num_ranks
+        for w, (begin, count, reps) in enumerate(windows):
+            zb.zero_grad_reduce_shard(self.plan, self.rank, reps, begin, count, self.grad,
+                                      sqnorm_out=self.partials[nd + w:nd + w + 1],
+                                      workspace=self.workspace, stream=stream)
+
+    def clip(self, stream=None):
+        if self.max_norm > 0:
+            zb.zero_clip_scale(self.partials, self.max_norm, self.scale, stream=stream)
+
+    def adamw(self, stream=None):
+        self.t += 1
+        zb.zero_shard_adamw_step(self.master, self.exp_avg, self.exp_avg_sq, self.grad,
+                                 self.param_shards[self.rank], self.t,
+                                 clip_scale=self.scale if self.max_norm > 0 else None,
+                                 stream=stream, **self.hyper.as_kwargs())
+
+    def gather(self, stream=None):
+        if self.tensors:
+            zb.zero_gather_params(self.plan, self.param_shards, self.tensors, stream=stream)
+
+    def step(self, windows, stream=None) -> None:
+        self.reduce(windows, stream)
+        self.clip(stream)
+        self.adamw(stream)
+        self.gather(stream)
+
+
+def plan_numels(plan: zb.Plan) -> List[int]:
+    t = plan.num_tensors
+    offs = [plan.tensor_offset(i) for i in range(t)] + [plan.numel]
+    return [offs[i + 1] - offs[i] for i in range(t)]
+
+
+def bucket_windows(padded_numel: int, bucket: int, lo: int, hi: int) -> List[Tuple[int, int]]:
+    """Fixed-size flat-index buckets [b*bucket, (b+1)*bucket) meeting [lo, hi), in
+    backward (descending) order, each clipped to the padded buffer."""
+    out = []
+    if bucket <= 0:
+        return [(0, padded_numel)]
+    first, last = lo // bucket, (hi - 1) // bucket
+    for b in range(last, first - 1, -1):
+        begin = b * bucket
+        out.append((begin, min(bucket, padded_numel - begin)))
+    return out
+
+
+def rank_step_plan_windows(plan: zb.Plan, rank: int, bucket: int) -> List[Tuple[int, int]]:
+    s = plan.shard_numel
+    return bucket_windows(plan.padded_numel, bucket, rank * s, (rank + 1) * s)
+
+
+def optional_stream(stream: Optional[torch.cuda.Stream]):
+    return None if stream is None else stream.cuda_stream
