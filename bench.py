@@ -44,6 +44,9 @@ def parse_args(argv=None):
                     help="rough budget for the oracle's host timing (0 disables it)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only this many steps, untimed, for a profiler (no JSON)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="with --profile-steps: first copy 1 GiB once (a plain copy kernel of known "
+                         "size, to scale hardware byte counters)")
     return ap.parse_args(argv)
 
 
@@ -127,6 +130,31 @@ def time_kernels(setup: "Setup", steps: int):
     return {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_traffic.json")
+ADAMW_SOURCES = [os.path.join(ROOT, "zero_partitioned_mixed_partition_amd", "csrc", f)
+                 for f in ("adamw.hip", "device_common.hpp")]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ADAMW_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(setup: "Setup"):
+    """HBM bytes per AdamW launch from the committed counter runs (FETCH_SIZE and
+    WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel sources have
+    changed since they were taken or they cover another shard size."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    d = json.load(open(TRAFFIC_FILE))
+    if d.get("source_sha256") != kernel_source_digest() or d.get("elems") != setup.S:
+        return None
+    return d["bytes_per_launch"]
+
+
 def cpu_baseline(setup: "Setup", budget_s: float):
     """The oracle's rank step on the host for the same workload, bounded in time."""
     import numpy as np
@@ -179,6 +207,13 @@ def main(argv=None):
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     setup = Setup(args.workload, device)
     if args.profile_steps:
+        if args.calibrate_copy:
+            src = torch.ones(1 << 28, dtype=torch.float32, device=device)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)                      # reads 1 GiB, writes 1 GiB
+            torch.cuda.synchronize()
+            del src, dst
         for _ in range(args.profile_steps):
             setup.step()
         torch.cuda.synchronize()
@@ -188,20 +223,33 @@ def main(argv=None):
     for _ in range(args.warmup):
         setup.step()
     torch.cuda.synchronize()
+    # Timed region: whole steps; AdamW is bracketed by events on the stream it is
+    # launched on (torch's current stream, which every call here uses).
+    adamw_ev = []
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
-        setup.step()
+        setup.rs.reduce(setup.windows)
+        setup.rs.clip()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        setup.rs.adamw()
+        b.record()
+        adamw_ev.append((a, b))
+        setup.rs.gather()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
-    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s)",
-          file=sys.stderr, flush=True)
+    adamw_ms = sum(a.elapsed_time(b) for a, b in adamw_ev) / len(adamw_ev)
+    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s), "
+          f"adamw {adamw_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     kernel_ms = time_kernels(setup, max(20, min(args.steps, 200)))
+    kernel_ms["adamw"] = adamw_ms
     bpk = setup.bytes_per_kernel()
     kernels = {n: {"ms": kernel_ms[n], "bytes": bpk[n],
                    "gbs": bpk[n] / (kernel_ms[n] * 1e-3) / 1e9,
@@ -210,6 +258,7 @@ def main(argv=None):
     step_bytes = sum(bpk.values())
     adamw_gbs = kernels["adamw"]["gbs"]
     value = setup.S / (ms_per_step * 1e-3)
+    traffic = measured_traffic(setup)
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
@@ -242,7 +291,7 @@ def main(argv=None):
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": "adamw_vec", "achieved": adamw_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": adamw_gbs / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

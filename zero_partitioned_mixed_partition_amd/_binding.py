@@ -247,3 +247,68 @@ def zero_status_string(status: int) -> str:
 
 def zero_last_error() -> str:
     return _last_error().decode()
+
+
+# --------------------------------------------------------------------------- prepared calls
+#
+# The same entry points with their arguments marshalled once, for loops that
+# call them with unchanged buffers every step: each call then costs one ctypes
+# dispatch instead of rebuilding pointer tables.
+
+class Prepared:
+    def __init__(self, fn, args, where: str, step_index: Optional[int] = None):
+        self._fn, self._args, self._where, self._step_index = fn, list(args), where, step_index
+
+    def __call__(self, step: Optional[int] = None) -> None:
+        args = self._args
+        if self._step_index is not None:
+            args = list(args)
+            args[self._step_index] = step
+        _check(self._fn(*args), self._where)
+
+
+def prepare_grad_reduce_shard(plan: Plan, rank: int, replicas: Sequence, begin: int, count: int,
+                              shard_grad, sqnorm_out, workspace, stream) -> Prepared:
+    ptrs = (c_vp * max(len(replicas), 1))(*[_ptr(r, 2, "replica") for r in replicas])
+    ws = workspace.data_ptr() if workspace is not None else 0
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    p = Prepared(_reduce, [plan.handle, rank, ptrs, len(replicas), begin, count,
+                           _ptr(shard_grad, 2, "shard_grad"), _ptr(sqnorm_out, 8, "sqnorm_out"), ws,
+                           wsb, _stream(stream, shard_grad)], "zero_grad_reduce_shard")
+    p._keep = (ptrs, replicas, shard_grad, sqnorm_out, workspace)
+    return p
+
+
+def prepare_clip_scale(partials, max_norm: float, scale_out, stream) -> Prepared:
+    p = Prepared(_clip, [_ptr(partials, 8, "partials"), partials.numel(), float(max_norm),
+                         _ptr(scale_out, 4, "scale_out"), _stream(stream, partials)],
+                 "zero_clip_scale")
+    p._keep = (partials, scale_out)
+    return p
+
+
+def prepare_shard_adamw_step(master, exp_avg, exp_avg_sq, grad, param_out, lr: float, beta1: float,
+                             beta2: float, eps: float, weight_decay: float, clip_scale, stream
+                             ) -> Prepared:
+    """Call the result with the 1-based step number."""
+    n = master.numel()
+    for t in (exp_avg, exp_avg_sq, grad, param_out):
+        if t.numel() < n:
+            raise ValueError("an array holds fewer elements than master")
+    p = Prepared(_adamw, [_ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                          _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(grad, 2, "grad"),
+                          _ptr(param_out, 2, "param_out"), n, 1, lr, beta1, beta2, eps,
+                          weight_decay, _ptr(clip_scale, 4, "clip_scale"),
+                          _stream(stream, master)], "zero_shard_adamw_step", step_index=6)
+    p._keep = (master, exp_avg, exp_avg_sq, grad, param_out, clip_scale)
+    return p
+
+
+def prepare_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, stream) -> Prepared:
+    if len(shards) != plan.num_ranks or len(tensors) != plan.num_tensors:
+        raise ValueError("need N_d shards and T tensors")
+    sp = (c_vp * max(len(shards), 1))(*[_ptr(s, 2, "shard") for s in shards])
+    tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
+    p = Prepared(_gather, [plan.handle, sp, tp, _stream(stream, shards[0])], "zero_gather_params")
+    p._keep = (sp, tp, shards, tensors)
+    return p

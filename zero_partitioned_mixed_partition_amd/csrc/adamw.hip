@@ -12,11 +12,13 @@
 //
 // Memory: 28 bytes per element (read 12 fp32 + 2 bf16, write 12 fp32 + 2
 // bf16), about 15 flops: HBM-bound by a factor of ~40 against the fp32
-// vector ridge point, so no matrix cores. Each thread moves groups of 8
-// elements with 16-byte non-temporal loads and stores: two dwordx4 per fp32
-// array, one for the bf16 gradient and one for the bf16 parameters. The grid
-// is persistent (a few workgroups per compute unit, sized from the device's
-// CU count) and grid-strides over the groups with 64-bit indices.
+// vector ridge point, so no matrix cores. Each thread updates four
+// consecutive elements with non-temporal accesses: one dwordx4 per fp32
+// array, one dwordx2 for the bf16 gradient and one for the bf16 parameters.
+// The grid covers the shard with one group per thread (up to 2^20
+// workgroups, then threads stride): measured on MI355X, short-lived waves
+// that the dispatcher keeps refilling sustain more HBM bandwidth than a
+// persistent few-workgroups-per-CU loop. Indices are 64-bit.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -30,15 +32,17 @@
 namespace {
 
 using zero::dev::f32x4;
-using zero::dev::u32x4;
+using zero::dev::u32x2;
 
-constexpr int kThreads = 256;
-#ifndef ZERO_ADAMW_OVERSUB
-#define ZERO_ADAMW_OVERSUB 1
+#ifndef ZERO_ADAMW_THREADS
+#define ZERO_ADAMW_THREADS 256
 #endif
-#ifndef ZERO_ADAMW_UNROLL
-#define ZERO_ADAMW_UNROLL 2
+// Upper bound on the grid; below it every thread updates exactly one group of
+// four elements (no loop), above it threads stride over the groups.
+#ifndef ZERO_ADAMW_MAX_BLOCKS
+#define ZERO_ADAMW_MAX_BLOCKS (1 << 20)
 #endif
+constexpr int kThreads = ZERO_ADAMW_THREADS;
 
 struct AdamScalars {
     float beta1, one_minus_beta1, beta2, one_minus_beta2, eps, step_size, sqrt_bc2, decay;
@@ -65,51 +69,31 @@ __device__ __forceinline__ float read_clip(const float* clip_scale) {
     return clip_scale != nullptr ? *clip_scale : 1.0f;
 }
 
-struct Group {   // 8 consecutive elements of every stream
-    f32x4 p[2], m[2], v[2];
-    u32x4 g;
-};
-
-__device__ __forceinline__ void load_group(Group& x, const f32x4* master, const f32x4* m,
-                                           const f32x4* v, const u32x4* grad, int64_t i) {
-    x.p[0] = zero::dev::ld_stream(master + 2 * i);
-    x.p[1] = zero::dev::ld_stream(master + 2 * i + 1);
-    x.m[0] = zero::dev::ld_stream(m + 2 * i);
-    x.m[1] = zero::dev::ld_stream(m + 2 * i + 1);
-    x.v[0] = zero::dev::ld_stream(v + 2 * i);
-    x.v[1] = zero::dev::ld_stream(v + 2 * i + 1);
-    x.g = zero::dev::ld_stream(grad + i);
-}
-
-__device__ __forceinline__ void update_group(Group& x, float clip, const AdamScalars& c,
-                                             u32x4& out) {
-    float pv[8];
+// Four consecutive elements: 16-byte accesses for each fp32 array, 8-byte
+// accesses for the bf16 gradient and parameters.
+__device__ __forceinline__ void update4(f32x4* __restrict__ p4, f32x4* __restrict__ m4,
+                                        f32x4* __restrict__ v4, const u32x2* __restrict__ g4,
+                                        u32x2* __restrict__ o4, int64_t i, float clip,
+                                        const AdamScalars& c) {
+    f32x4 p = zero::dev::ld_stream(p4 + i);
+    f32x4 m = zero::dev::ld_stream(m4 + i);
+    f32x4 v = zero::dev::ld_stream(v4 + i);
+    const u32x2 g = zero::dev::ld_stream(g4 + i);
+    const float gs[4] = {zero::dev::lo_bf16(g.x), zero::dev::hi_bf16(g.x), zero::dev::lo_bf16(g.y),
+                         zero::dev::hi_bf16(g.y)};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t w = x.g[j / 2];
-        const float gj = (j & 1) ? zero::dev::hi_bf16(w) : zero::dev::lo_bf16(w);
-        float p = x.p[j / 4][j % 4], m = x.m[j / 4][j % 4], v = x.v[j / 4][j % 4];
-        adam_elem(p, m, v, gj * clip, c);
-        x.p[j / 4][j % 4] = p;
-        x.m[j / 4][j % 4] = m;
-        x.v[j / 4][j % 4] = v;
-        pv[j] = p;
+    for (int j = 0; j < 4; ++j) {
+        float pj = p[j], mj = m[j], vj = v[j];
+        adam_elem(pj, mj, vj, gs[j] * clip, c);
+        p[j] = pj;
+        m[j] = mj;
+        v[j] = vj;
     }
-    out.x = zero::dev::pack_bf16(pv[0], pv[1]);
-    out.y = zero::dev::pack_bf16(pv[2], pv[3]);
-    out.z = zero::dev::pack_bf16(pv[4], pv[5]);
-    out.w = zero::dev::pack_bf16(pv[6], pv[7]);
-}
-
-__device__ __forceinline__ void store_group(const Group& x, const u32x4& out, f32x4* master,
-                                            f32x4* m, f32x4* v, u32x4* param, int64_t i) {
-    zero::dev::st_stream(master + 2 * i, x.p[0]);
-    zero::dev::st_stream(master + 2 * i + 1, x.p[1]);
-    zero::dev::st_stream(m + 2 * i, x.m[0]);
-    zero::dev::st_stream(m + 2 * i + 1, x.m[1]);
-    zero::dev::st_stream(v + 2 * i, x.v[0]);
-    zero::dev::st_stream(v + 2 * i + 1, x.v[1]);
-    zero::dev::st_stream(param + i, out);
+    zero::dev::st_stream(p4 + i, p);
+    zero::dev::st_stream(m4 + i, m);
+    zero::dev::st_stream(v4 + i, v);
+    const u32x2 out = {zero::dev::pack_bf16(p[0], p[1]), zero::dev::pack_bf16(p[2], p[3])};
+    zero::dev::st_stream(o4 + i, out);
 }
 
 __device__ __forceinline__ void scalar_elem(float* __restrict__ master, float* __restrict__ m,
@@ -125,9 +109,8 @@ __device__ __forceinline__ void scalar_elem(float* __restrict__ master, float* _
     param[i] = static_cast<uint16_t>(zero::dev::f32_to_bf16(p));
 }
 
-// Vector path: groups [0, n_groups) of 8 elements, then elements
-// [8*n_groups, n) one per thread. All five pointers are 16-byte aligned.
-template <int kUnroll>
+// Vector path: groups [0, n/4) of four elements, then the n % 4 tail elements
+// one per thread. master/m/v are 16-byte aligned, grad and param 8-byte.
 __global__ __launch_bounds__(kThreads) void adamw_vec(float* __restrict__ master,
                                                       float* __restrict__ m,
                                                       float* __restrict__ v,
@@ -137,40 +120,18 @@ __global__ __launch_bounds__(kThreads) void adamw_vec(float* __restrict__ master
                                                       const float* __restrict__ clip_scale) {
     const float clip = read_clip(clip_scale);
     if (!isfinite(clip)) return;
-    f32x4* m4 = reinterpret_cast<f32x4*>(m);
-    f32x4* v4 = reinterpret_cast<f32x4*>(v);
-    f32x4* p4 = reinterpret_cast<f32x4*>(master);
-    const u32x4* g8 = reinterpret_cast<const u32x4*>(grad);
-    u32x4* o8 = reinterpret_cast<u32x4*>(param);
-    const int64_t n_groups = n / 8;
+    const int64_t groups = n / 4;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-
-    int64_t i = tid;
-    // Main loop: kUnroll groups per thread in flight, all loads issued first.
-    for (; i + (kUnroll - 1) * stride < n_groups; i += kUnroll * stride) {
-        Group x[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) load_group(x[u], p4, m4, v4, g8, i + u * stride);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            u32x4 out;
-            update_group(x[u], clip, c, out);
-            store_group(x[u], out, p4, m4, v4, o8, i + u * stride);
-        }
-    }
-    for (; i < n_groups; i += stride) {
-        Group x;
-        load_group(x, p4, m4, v4, g8, i);
-        u32x4 out;
-        update_group(x, clip, c, out);
-        store_group(x, out, p4, m4, v4, o8, i);
-    }
-    const int64_t tail = n - n_groups * 8;
-    if (tid < tail) scalar_elem(master, m, v, grad, param, n_groups * 8 + tid, clip, c);
+    for (int64_t i = tid; i < groups; i += stride)
+        update4(reinterpret_cast<f32x4*>(master), reinterpret_cast<f32x4*>(m),
+                reinterpret_cast<f32x4*>(v), reinterpret_cast<const u32x2*>(grad),
+                reinterpret_cast<u32x2*>(param), i, clip, c);
+    const int64_t tail = n - groups * 4;
+    if (tid < tail) scalar_elem(master, m, v, grad, param, groups * 4 + tid, clip, c);
 }
 
-// Fallback for pointers that are not 16-byte aligned: one element per thread.
+// Fallback for pointers without that alignment: one element per thread.
 __global__ __launch_bounds__(kThreads) void adamw_scalar(float* __restrict__ master,
                                                          float* __restrict__ m,
                                                          float* __restrict__ v,
@@ -185,11 +146,17 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar(float* __restrict__ mas
         scalar_elem(master, m, v, grad, param, i, clip, c);
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool ranges_overlap(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
     return x < y + b_bytes && y < x + a_bytes;
+}
+
+int64_t blocks_for(int64_t items) {
+    int64_t blocks = (items + kThreads - 1) / kThreads;
+    if (blocks > ZERO_ADAMW_MAX_BLOCKS) blocks = ZERO_ADAMW_MAX_BLOCKS;
+    return blocks < 1 ? 1 : blocks;
 }
 
 }  // namespace
@@ -233,32 +200,14 @@ extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, floa
     c.sqrt_bc2 = static_cast<float>(std::sqrt(bc2));
     c.decay = static_cast<float>(1.0 - lr * weight_decay);
 
-    const bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
-                     aligned16(grad) && aligned16(param_out);
-    // Persistent grid: every workgroup resident at once (occupancy x CUs, times
-    // ZERO_ADAMW_OVERSUB), none idle when the work is small.
+    const bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
+                     aligned(grad, 8) && aligned(param_out, 8);
     if (vec) {
-        const void* kern = reinterpret_cast<const void*>(&adamw_vec<ZERO_ADAMW_UNROLL>);
-        static thread_local int cached_dev = -1, cached_blocks = 0;
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        if (dev != cached_dev) {
-            cached_blocks = zero::device_resident_blocks(kern, kThreads) * ZERO_ADAMW_OVERSUB;
-            cached_dev = dev;
-        }
-        const int64_t groups = n / 8;
-        int64_t blocks = (groups + kThreads - 1) / kThreads;
-        if (blocks > cached_blocks) blocks = cached_blocks;
-        if (blocks < 1) blocks = 1;
-        hipLaunchKernelGGL(adamw_vec<ZERO_ADAMW_UNROLL>, dim3(static_cast<unsigned>(blocks)),
-                           dim3(kThreads), 0, stream, master, exp_avg, exp_avg_sq, grad, param_out,
-                           n, c, clip_scale);
+        hipLaunchKernelGGL(adamw_vec, dim3(static_cast<unsigned>(blocks_for(n / 4))), dim3(kThreads),
+                           0, stream, master, exp_avg, exp_avg_sq, grad, param_out, n, c, clip_scale);
     } else {
-        int64_t blocks = (n + kThreads - 1) / kThreads;
-        const int64_t cap = static_cast<int64_t>(zero::device_cu_count()) * 8;
-        if (blocks > cap) blocks = cap;
-        hipLaunchKernelGGL(adamw_scalar, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                           stream, master, exp_avg, exp_avg_sq, grad, param_out, n, c, clip_scale);
+        hipLaunchKernelGGL(adamw_scalar, dim3(static_cast<unsigned>(blocks_for(n))), dim3(kThreads),
+                           0, stream, master, exp_avg, exp_avg_sq, grad, param_out, n, c, clip_scale);
     }
     return zero::check_hip(hipGetLastError(), "zero_shard_adamw_step launch");
 }

@@ -25,9 +25,9 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSegs = 40;                       // segments per launch (kernarg ~1.3 KB)
+constexpr int kSegs = 96;                       // segments per launch (kernarg ~3.1 KB of the 4 KB limit)
 #ifndef ZERO_GATHER_VECS_PER_THREAD
-#define ZERO_GATHER_VECS_PER_THREAD 4
+#define ZERO_GATHER_VECS_PER_THREAD 1
 #endif
 constexpr int64_t kChunk = int64_t(kThreads) * 8 * ZERO_GATHER_VECS_PER_THREAD;   // elements
 

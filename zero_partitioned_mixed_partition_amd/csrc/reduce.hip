@@ -16,7 +16,8 @@
 // exact fp64 squares of bf16 values: per-thread fp64 partials, a butterfly in
 // each wavefront, waves in order through LDS, one partial per workgroup in the
 // caller's workspace, then a single-workgroup pass adds the workgroup partials
-// in a fixed order. No floating-point atomics: results repeat bit for bit.
+// in a fixed order. No floating-point atomics, and a grid that depends on n
+// alone: results repeat bit for bit, on any device.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -32,14 +33,15 @@ namespace {
 using zero::dev::u32x4;
 
 constexpr int kThreads = 256;
-constexpr int kMaxPartials = 4096;           // workgroup partials in the workspace
+// Grid cap, and so the number of workgroup partials the workspace holds. Below
+// it each thread handles one group of 8 elements; above it threads stride.
+// The grid depends on n only, so the summation order (and the fp64 result)
+// is the same on every device.
+#ifndef ZERO_REDUCE_MAX_BLOCKS
+#define ZERO_REDUCE_MAX_BLOCKS 4096
+#endif
+constexpr int kMaxPartials = ZERO_REDUCE_MAX_BLOCKS;
 constexpr int kReplicaBatch = 8;             // replica loads in flight per thread
-#ifndef ZERO_REDUCE_BLOCKS_PER_CU
-#define ZERO_REDUCE_BLOCKS_PER_CU 8
-#endif
-#ifndef ZERO_SQNORM_BLOCKS_PER_CU
-#define ZERO_SQNORM_BLOCKS_PER_CU 8
-#endif
 
 struct ReplicaTable {
     const uint16_t* p[ZERO_MAX_REPLICAS];
@@ -204,10 +206,8 @@ __global__ void clip_kernel(const double* __restrict__ partials, int n, double m
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int grid_for(int64_t work_items, int blocks_per_cu) {
+int grid_for(int64_t work_items) {
     int64_t blocks = (work_items + kThreads - 1) / kThreads;
-    const int64_t cap = static_cast<int64_t>(zero::device_cu_count()) * blocks_per_cu;
-    if (blocks > cap) blocks = cap;
     if (blocks > kMaxPartials) blocks = kMaxPartials;
     if (blocks < 1) blocks = 1;
     return static_cast<int>(blocks);
@@ -260,7 +260,7 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
     bool vec = aligned16(out);
     for (int32_t k = 0; k < n_replicas && vec; ++k) vec = aligned16(replicas[k] + src_off);
     const bool norm = sqnorm_out != nullptr;
-    const int blocks = grid_for(vec ? n / 8 : n, ZERO_REDUCE_BLOCKS_PER_CU);
+    const int blocks = grid_for(vec ? n / 8 : n);
     if (vec) {
         if (norm)
             hipLaunchKernelGGL(reduce_vec<true>, dim3(blocks), dim3(kThreads), 0, stream, table,
@@ -298,7 +298,7 @@ extern "C" zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double*
         return zero::check_hip(hipGetLastError(), "zero_grad_sqnorm launch");
     }
     const bool vec = aligned16(grad);
-    const int blocks = grid_for(vec ? n / 8 : n, ZERO_SQNORM_BLOCKS_PER_CU);
+    const int blocks = grid_for(vec ? n / 8 : n);
     if (vec)
         hipLaunchKernelGGL(sqnorm_vec, dim3(blocks), dim3(kThreads), 0, stream, grad, n, partials);
     else

