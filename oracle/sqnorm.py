@@ -51,6 +51,15 @@ class SqnormAccumulator:
             raise OverflowError("too many values for exact per-exponent sums")
         return self
 
+    def merge(self, other: "SqnormAccumulator") -> "SqnormAccumulator":
+        """Adds another accumulator's values (exact: integer sums per exponent)."""
+        self.per_exp += other.per_exp
+        self.count += other.count
+        self.special += other.special
+        if self.count >= (1 << 53) // 65025:
+            raise OverflowError("too many values for exact per-exponent sums")
+        return self
+
     def value(self) -> float:
         if self.special != 0.0:
             return self.special

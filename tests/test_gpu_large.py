@@ -1,0 +1,301 @@
+"""GPU parity on the large model-shaped workloads at their full sizes.
+
+llama3-8b   Llama-3-8B tensor list, N_d = 64, rank 63 (125,472,896 elements):
+            the shard's gradient arrives as six 25M-element flat-index buckets,
+            each as 64 replica buffers, reduced into the shard in backward
+            (descending) order; global-norm clip 1.0; one AdamW step. Full
+            arrays against the oracle (the oracle reduces the shard in chunks
+            across a process pool).
+gpt-1.3b    1.3B GPT list, N_d = 8: 8 replicas reduced for every rank, AdamW on
+            every shard, gather to 292 tensors. Sampled windows against the
+            oracle (every rank boundary and every tensor start), exact norm
+            partials for two ranks, and a full-size gather of synthetic shards.
+llama3-70b  Llama-3-70B list, N_d = 8, rank 7 (8,819,213,312 elements, indices
+            past 2^33): 5 AdamW steps on windows at the shard ends, around 2^31,
+            2^32 and 2^33, at tensor boundaries and at random; exact norm partials
+            of the own and one other rank; the clip coefficient on device.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (assert_bf16_close, assert_bits_equal, assert_f32_close, dev, host_f32,
+                      host_u16, needs_gpu, note)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+@pytest.fixture(scope="module")
+def zm():
+    import zero_partitioned_mixed_partition_amd as m
+    torch.cuda.set_device(0)
+    return m
+
+
+def _free_gpu():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_llama3_8b_rank63_buckets_clip_one_step(zm):
+    from oracle_workers import grad_sqnorms, reduce_windows
+    from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep, bucket_windows
+    w = synth.WORKLOADS["llama3-8b"]
+    rank, R = 63, w.replicas
+    plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
+    P, S, phi = plan.padded_numel, plan.shard_numel, plan.numel
+    lo = rank * S
+    # the other ranks reduce on their own GPUs; their averaged gradients are drawn
+    # directly, with the standard deviation of a mean of R replicas
+    sigma_avg = synth.GRAD_SIGMA / math.sqrt(R)
+    wins = bucket_windows(P, w.bucket, lo, lo + S)
+    note(f"llama3-8b: P={P} S={S}, windows {wins}")
+    assert len(wins) == 6 and wins[0] == (8_025_000_000, 5_265_344)
+    rs = RankStep(plan, rank, len(wins), Hyper(), w.max_norm, dev(), gather=False)
+    synth.device_normal_f32(rs.master, w.seed, synth.KIND_MASTER, 0, 0, lo, phi, synth.MASTER_SIGMA)
+    scratch = torch.empty(S, dtype=torch.int16, device=dev())
+    for r in range(w.n_ranks):
+        if r != rank:
+            synth.device_normal_bf16(scratch, w.seed, synth.KIND_GRAD, 1, 0, r * S, phi, sigma_avg)
+            zm.zero_grad_sqnorm(scratch, rs.partials[r:r + 1], workspace=rs.workspace)
+    del scratch
+    reps = [torch.empty(w.bucket, dtype=torch.int16, device=dev()) for _ in range(R)]
+    for wi, (b0, cnt) in enumerate(wins):
+        for k in range(R):
+            synth.device_normal_bf16(reps[k], w.seed, synth.KIND_REPLICA, 1, k, b0, phi,
+                                     synth.GRAD_SIGMA, n=cnt)
+        zm.zero_grad_reduce_shard(plan, rank, [x[:cnt] for x in reps], b0, cnt, rs.grad,
+                                  sqnorm_out=rs.partials[w.n_ranks + wi:w.n_ranks + wi + 1],
+                                  workspace=rs.workspace)
+    rs.clip()
+    rs.adamw()
+    torch.cuda.synchronize()
+    del reps
+    got_parts = rs.partials.cpu().numpy()
+    got_scale = np.float32(rs.scale.item())
+
+    note("llama3-8b: oracle remote partials and the own shard's reduce (process pool)")
+    remote = grad_sqnorms([(w.seed, synth.KIND_GRAD, 1, 0, r * S, S, phi, sigma_avg)
+                           for r in range(w.n_ranks) if r != rank])
+    chunk = 1 << 22
+    tasks = [(w.numels, w.n_ranks, w.align, rank, w.seed, synth.KIND_REPLICA, 1, R, a,
+              min(a + chunk, lo + S), synth.GRAD_SIGMA) for a in range(lo, lo + S, chunk)]
+    res = reduce_windows(tasks)
+    grad = np.concatenate([b for b, _ in res])
+    acc = oracle.SqnormAccumulator()
+    for _, a in res:
+        acc.merge(a)
+    own = acc.value()
+    parts = remote[:rank] + [own]
+    scale = oracle.clip_scale(parts, w.max_norm)
+    note(f"llama3-8b: global norm {math.sqrt(sum(parts)):.4f}, clip {scale:.6f}")
+
+    assert_bits_equal(host_u16(rs.grad), grad, "reduced shard gradient")
+    others = np.array([i for i in range(w.n_ranks) if i != rank])
+    assert (np.abs(got_parts[others] - np.array(remote)) <= 1e-12 * np.array(remote)).all()
+    own_gpu = float(got_parts[w.n_ranks:].sum())
+    assert abs(own_gpu - own) <= 1e-12 * own, (own_gpu, own)
+    assert abs(int(got_scale.view(np.int32)) - int(np.float32(scale).view(np.int32))) <= 1
+    master = synth.normal_f32(S, w.seed, synth.KIND_MASTER, 0, 0, lo, phi, synth.MASTER_SIGMA)
+    z = np.zeros(S, np.float32)
+    p, m, v, bits = oracle.adamw_step(master, z, z, grad, 1, clip=scale, **HP)
+    for got, want, what in ((rs.master, p, "master"), (rs.exp_avg, m, "exp_avg"),
+                            (rs.exp_avg_sq, v, "exp_avg_sq")):
+        exact = assert_f32_close(host_f32(got), want, what)
+        note(f"llama3-8b: {what} bit-identical fraction {exact:.6f}")
+    assert_bf16_close(host_u16(rs.param_shards[rank]), bits, "param shard")
+    del rs
+    _free_gpu()
+
+
+def _windows_in_shards(points, half, S, n_ranks, total):
+    """Windows [c-half, c+half) around each point, clipped to [0, total) and split
+    at shard boundaries, merged when they overlap."""
+    spans = sorted((max(0, c - half), min(total, c + half)) for c in points)
+    merged = []
+    for a, b in spans:
+        if merged and a <= merged[-1][1]:
+            merged[-1] = (merged[-1][0], max(merged[-1][1], b))
+        else:
+            merged.append((a, b))
+    out = []
+    for a, b in merged:
+        while a < b:
+            end = min(b, (a // S + 1) * S)
+            out.append((a, end))
+            a = end
+    return [(a, b) for a, b in out if b > a]
+
+
+def test_gpt_1p3b_all_ranks_reduce_adamw_gather(zm):
+    from oracle_workers import _reduce_window, reduce_windows
+    w = synth.WORKLOADS["gpt-1.3b"]
+    R = w.replicas
+    ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
+    plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
+    P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
+    note(f"gpt-1.3b: P={P} S={S} T={len(w.numels)}, {R} replicas")
+    reps = []
+    for k in range(R):
+        t = torch.empty(P, dtype=torch.int16, device=dev())
+        synth.device_normal_bf16(t, w.seed, synth.KIND_REPLICA, 1, k, 0, phi, synth.GRAD_SIGMA)
+        reps.append(t)
+    master = torch.empty(P, dtype=torch.float32, device=dev())
+    synth.device_normal_f32(master, w.seed, synth.KIND_MASTER, 0, 0, 0, phi, synth.MASTER_SIGMA)
+    m = torch.zeros(P, dtype=torch.float32, device=dev())
+    v = torch.zeros(P, dtype=torch.float32, device=dev())
+    grad = torch.empty(P, dtype=torch.int16, device=dev())
+    param = torch.empty(P, dtype=torch.int16, device=dev())
+    parts = torch.zeros(w.n_ranks, dtype=torch.float64, device=dev())
+    ws = zm.sqnorm_workspace(dev())
+    for r in range(w.n_ranks):
+        sl = slice(r * S, (r + 1) * S)
+        zm.zero_grad_reduce_shard(plan, r, reps, 0, P, grad[sl], sqnorm_out=parts[r:r + 1],
+                                  workspace=ws)
+        zm.zero_shard_adamw_step(master[sl], m[sl], v[sl], grad[sl], param[sl], 1, **HP)
+    tensors = [torch.empty(n, dtype=torch.int16, device=dev()) for n in w.numels]
+    zm.zero_gather_params(plan, [param[r * S:(r + 1) * S] for r in range(w.n_ranks)], tensors)
+    torch.cuda.synchronize()
+    del reps
+    _free_gpu()
+
+    points = list(ref.offsets) + [r * S for r in range(w.n_ranks + 1)]
+    wins = _windows_in_shards(points, 256, S, w.n_ranks, phi)
+    note(f"gpt-1.3b: {len(wins)} oracle windows, {sum(b - a for a, b in wins)} elements")
+    flat_param = {}
+    for a, b in wins:
+        r = a // S
+        bits, _ = _reduce_window((w.numels, w.n_ranks, w.align, r, w.seed, synth.KIND_REPLICA, 1, R,
+                                  a, b, synth.GRAD_SIGMA))
+        p0 = synth.normal_f32(b - a, w.seed, synth.KIND_MASTER, 0, 0, a, phi, synth.MASTER_SIGMA)
+        z = np.zeros(b - a, np.float32)
+        P1, M1, V1, B1 = oracle.adamw_step(p0, z, z, bits, 1, **HP)
+        assert_bits_equal(host_u16(grad[a:b]), bits, f"grad [{a},{b})")
+        assert_f32_close(host_f32(master[a:b]), P1, f"master [{a},{b})")
+        assert_f32_close(host_f32(m[a:b]), M1, f"exp_avg [{a},{b})")
+        assert_f32_close(host_f32(v[a:b]), V1, f"exp_avg_sq [{a},{b})")
+        assert_bf16_close(host_u16(param[a:b]), B1, f"param [{a},{b})")
+        flat_param[(a, b)] = B1
+    # gathered tensors at every start and end, against the oracle's parameters
+    for t, (off, n) in enumerate(zip(ref.offsets, w.numels)):
+        for lo_t in (0, max(0, n - 256)):
+            hi_t = min(n, lo_t + 256)
+            g0, g1 = off + lo_t, off + hi_t
+            want = np.concatenate([bits[max(a, g0) - a:min(b, g1) - a]
+                                   for (a, b), bits in flat_param.items() if a < g1 and b > g0])
+            assert_bf16_close(host_u16(tensors[t][lo_t:hi_t]), want, f"tensor {t} [{lo_t},{hi_t})")
+    # exact squared-norm partials of the first and the last rank
+    note("gpt-1.3b: oracle norm partials of ranks 0 and 7 (process pool)")
+    chunk = 1 << 23
+    for r in (0, w.n_ranks - 1):
+        res = reduce_windows([(w.numels, w.n_ranks, w.align, r, w.seed, synth.KIND_REPLICA, 1, R,
+                               a, min(a + chunk, (r + 1) * S), synth.GRAD_SIGMA)
+                              for a in range(r * S, (r + 1) * S, chunk)])
+        acc = oracle.SqnormAccumulator()
+        for _, a in res:
+            acc.merge(a)
+        got = float(parts[r].item())
+        assert abs(got - acc.value()) <= 1e-12 * acc.value(), (r, got, acc.value())
+    del master, m, v, grad, param, tensors
+    _free_gpu()
+
+
+def test_gpt_1p3b_full_size_gather_of_synthetic_shards(zm):
+    w = synth.WORKLOADS["gpt-1.3b"]
+    ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
+    plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
+    S = ref.shard_numel
+    shards = []
+    for r in range(w.n_ranks):
+        t = torch.empty(S, dtype=torch.int16, device=dev())
+        synth.device_normal_bf16(t, w.seed, synth.KIND_PARAM, 0, 0, r * S, ref.numel, 0.02)
+        shards.append(t)
+    tensors = [torch.empty(n, dtype=torch.int16, device=dev()) for n in w.numels]
+    zm.zero_gather_params(plan, shards, tensors)
+    torch.cuda.synchronize()
+    note(f"gpt-1.3b gather: {ref.numel} parameters, {len(w.numels)} tensors")
+    host_shards = [synth.normal_bf16(S, w.seed, synth.KIND_PARAM, 0, 0, r * S, ref.numel, 0.02)
+                   for r in range(w.n_ranks)]
+    want = oracle.gather_params(ref, host_shards)
+    for i, (a, b) in enumerate(zip(tensors, want)):
+        assert_bits_equal(host_u16(a), b, f"tensor {i}")
+    del shards, tensors
+    _free_gpu()
+
+
+def test_llama3_70b_rank7_five_steps_windows(zm):
+    from oracle_workers import grad_sqnorms
+    from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep
+    w = synth.WORKLOADS["llama3-70b"]
+    rank = 7
+    ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
+    plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
+    P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
+    lo = rank * S
+    assert S > 2 ** 33
+    note(f"llama3-70b: S={S} (fp32 state {12 * S / 1e9:.1f} GB)")
+    rs = RankStep(plan, rank, 0, Hyper(), 0.0, dev(), gather=False)
+    synth.device_normal_f32(rs.master, w.seed, synth.KIND_MASTER, 0, 0, lo, phi, synth.MASTER_SIGMA)
+    # step-1 norm partials of this rank and of rank 0, and the clip coefficient
+    d_parts = torch.zeros(w.n_ranks, dtype=torch.float64, device=dev())
+    synth.device_normal_bf16(rs.grad, w.seed, synth.KIND_GRAD, 1, 0, 0, phi, synth.GRAD_SIGMA)
+    zm.zero_grad_sqnorm(rs.grad, d_parts[0:1], workspace=rs.workspace)
+    steps = w.steps
+    for t in range(1, steps + 1):
+        synth.device_normal_bf16(rs.grad, w.seed, synth.KIND_GRAD, t, 0, lo, phi, synth.GRAD_SIGMA)
+        if t == 1:
+            zm.zero_grad_sqnorm(rs.grad, d_parts[rank:rank + 1], workspace=rs.workspace)
+        rs.adamw()
+        note(f"llama3-70b: step {t} enqueued")
+    torch.cuda.synchronize()
+    got0, got7 = float(d_parts[0].item()), float(d_parts[rank].item())
+
+    rng = np.random.default_rng(70)
+    seg_starts = [soff for (_, _, soff, _) in ref.segments(rank)]
+    centers = [0, S, 2 ** 31, 2 ** 32, 2 ** 33] + seg_starts[1:12] + \
+        [int(x) for x in rng.integers(0, S, 8)]
+    wins = [(a, b) for a, b in _windows_in_shards([lo + c for c in centers], 2048, S, w.n_ranks, P)
+            if a >= lo and b <= lo + S]
+    note(f"llama3-70b: {len(wins)} windows, {sum(b - a for a, b in wins)} elements")
+    for a, b in wins:
+        n = b - a
+        p = synth.normal_f32(n, w.seed, synth.KIND_MASTER, 0, 0, a, phi, synth.MASTER_SIGMA)
+        m = np.zeros(n, np.float32)
+        v = np.zeros(n, np.float32)
+        bits = None
+        for t in range(1, steps + 1):
+            g = synth.normal_bf16(n, w.seed, synth.KIND_GRAD, t, 0, a, phi, synth.GRAD_SIGMA)
+            p, m, v, bits = oracle.adamw_step(p, m, v, g, t, **HP)
+        i0, i1 = a - lo, b - lo
+        assert_f32_close(host_f32(rs.master[i0:i1]), p, f"master [{i0},{i1})")
+        assert_f32_close(host_f32(rs.exp_avg[i0:i1]), m, f"exp_avg [{i0},{i1})")
+        assert_f32_close(host_f32(rs.exp_avg_sq[i0:i1]), v, f"exp_avg_sq [{i0},{i1})")
+        assert_bf16_close(host_u16(rs.param_shards[rank][i0:i1]), bits, f"param [{i0},{i1})")
+
+    note("llama3-70b: oracle norm partials of ranks 0 and 7 for step 1 (process pool)")
+    chunk = 1 << 28
+    tasks = [(w.seed, synth.KIND_GRAD, 1, 0, r * S + a, min(chunk, S - a), phi, synth.GRAD_SIGMA)
+             for r in (0, rank) for a in range(0, S, chunk)]
+    vals = grad_sqnorms(tasks, workers=16)
+    half = len(tasks) // 2
+    # chunk values are correctly rounded, so their fp64 sum is within a few ulp
+    want0, want7 = math.fsum(vals[:half]), math.fsum(vals[half:])
+    assert abs(got0 - want0) <= 1e-12 * want0, (got0, want0)
+    assert abs(got7 - want7) <= 1e-12 * want7, (got7, want7)
+    # the coefficient the clip kernel derives from device partials matches the
+    # oracle's on the same (oracle) partials
+    oparts = [want0] * w.n_ranks
+    oparts[rank] = want7
+    d_in = torch.tensor(oparts, dtype=torch.float64, device=dev())
+    d_scale = torch.zeros(1, dtype=torch.float32, device=dev())
+    zm.zero_clip_scale(d_in, 1.0, d_scale)
+    torch.cuda.synchronize()
+    assert np.float32(d_scale.item()) == oracle.clip_scale(oparts, 1.0)
+    del rs
+    _free_gpu()

@@ -386,3 +386,13 @@ def test_sqnorm_accumulator_chunks_equal_whole():
     for i in range(0, len(b), 7_777):
         acc.add(b[i:i + 7_777])
     assert acc.value() == oracle.sqnorm_fsum(b)
+
+
+def test_sqnorm_accumulator_merge_is_exact():
+    rng = np.random.default_rng(22)
+    b = _random_bf16(rng, 30_000, lo=-60, hi=60)
+    parts = [oracle.SqnormAccumulator().add(b[i:i + 4000]) for i in range(0, len(b), 4000)]
+    acc = oracle.SqnormAccumulator()
+    for p in parts:
+        acc.merge(p)
+    assert acc.value() == oracle.sqnorm_fsum(b)
