@@ -289,7 +289,7 @@ def main(argv=None):
         "adamw_frac_of_hbm_peak": adamw_gbs / HBM_PEAK_GBS,
         "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "kernels": kernels,
-        "roofline": {"bound": "hbm", "kernel": "adamw_vec", "achieved": adamw_gbs,
+        "roofline": {"bound": "hbm", "kernel": "adamw_kernel", "achieved": adamw_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": adamw_gbs / HBM_PEAK_GBS,
                      "traffic": traffic},
         "cpu_baseline": cpu,

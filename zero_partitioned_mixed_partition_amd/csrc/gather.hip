@@ -12,8 +12,9 @@
 // in the kernel arguments, kSegs segments per launch (no device-side table,
 // no host-to-device copy, nothing allocated): workgroup b finds its segment by
 // a binary search over the per-segment workgroup prefix, then copies a chunk
-// of kChunk elements with 16-byte non-temporal accesses when source and
-// destination are 16-byte co-aligned, element by element otherwise.
+// of kChunk elements, one access per lane (16 bytes by default) with
+// non-temporal hints when source and destination are co-aligned to the access
+// width, element by element otherwise.
 #include <hip/hip_runtime.h>
 
 #include <string>
@@ -26,10 +27,17 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSegs = 96;                       // segments per launch (kernarg ~3.1 KB of the 4 KB limit)
-#ifndef ZERO_GATHER_VECS_PER_THREAD
-#define ZERO_GATHER_VECS_PER_THREAD 1
+// One access per lane: ZERO_GATHER_LANE_ELEMS bf16 values (8 = 16 bytes).
+#ifndef ZERO_GATHER_LANE_ELEMS
+#define ZERO_GATHER_LANE_ELEMS 8
 #endif
-constexpr int64_t kChunk = int64_t(kThreads) * 8 * ZERO_GATHER_VECS_PER_THREAD;   // elements
+constexpr int kLane = ZERO_GATHER_LANE_ELEMS;
+constexpr int64_t kChunk = int64_t(kThreads) * kLane;   // elements per workgroup
+
+template <int E> struct LaneBits;
+template <> struct LaneBits<8> { typedef zero::dev::u32x4 T; };
+template <> struct LaneBits<4> { typedef zero::dev::u32x2 T; };
+template <> struct LaneBits<2> { typedef uint32_t T; };
 
 struct SegBatch {
     const uint16_t* src[kSegs];
@@ -40,6 +48,7 @@ struct SegBatch {
 };
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
+    typedef typename LaneBits<kLane>::T V;
     const int64_t blk = blockIdx.x;
     int lo = 0, hi = b.n - 1;                         // find s with first_block[s] <= blk < first_block[s+1]
     while (lo < hi) {
@@ -51,22 +60,19 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
     const int64_t len = b.len[s] - start < kChunk ? b.len[s] - start : kChunk;
     const uint16_t* src = b.src[s] + start;
     uint16_t* dst = b.dst[s] + start;
+    constexpr uintptr_t kBytes = 2 * kLane;
     const uintptr_t sa = reinterpret_cast<uintptr_t>(src), da = reinterpret_cast<uintptr_t>(dst);
-    if (((sa ^ da) & 15u) == 0) {
-        // Co-aligned: scalar head up to the 16-byte boundary, vector body, scalar tail.
-        int64_t head = static_cast<int64_t>(((16u - (da & 15u)) & 15u) / 2u);
+    if (((sa ^ da) & (kBytes - 1)) == 0) {
+        // Co-aligned: element head up to the access boundary, vector body, element tail.
+        int64_t head = static_cast<int64_t>(((kBytes - (da & (kBytes - 1))) & (kBytes - 1)) / 2u);
         if (head > len) head = len;
         if (threadIdx.x < head) dst[threadIdx.x] = src[threadIdx.x];
-        const int64_t body = (len - head) / 8;
-        const zero::dev::u32x4* s4 = reinterpret_cast<const zero::dev::u32x4*>(src + head);
-        zero::dev::u32x4* d4 = reinterpret_cast<zero::dev::u32x4*>(dst + head);
-#pragma unroll
-        for (int u = 0; u < ZERO_GATHER_VECS_PER_THREAD; ++u) {
-            const int64_t i = static_cast<int64_t>(u) * kThreads + threadIdx.x;
-            if (i < body) zero::dev::st_stream(d4 + i, zero::dev::ld_stream(s4 + i));
-        }
-        const int64_t done = head + body * 8;
-        const int64_t t = done + threadIdx.x;
+        const int64_t body = (len - head) / kLane;
+        const V* sv = reinterpret_cast<const V*>(src + head);
+        V* dv = reinterpret_cast<V*>(dst + head);
+        const int64_t i = threadIdx.x;
+        if (i < body) zero::dev::st_stream(dv + i, zero::dev::ld_stream(sv + i));
+        const int64_t t = head + body * kLane + threadIdx.x;
         if (t < len) dst[t] = src[t];
     } else {
         for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = src[i];

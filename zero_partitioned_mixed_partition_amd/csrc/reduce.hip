@@ -71,55 +71,81 @@ __device__ __forceinline__ void store_partial(double sq, double* partials) {
     if (threadIdx.x == 0) partials[blockIdx.x] = total;
 }
 
+#ifndef ZERO_REDUCE_EPT
+#define ZERO_REDUCE_EPT 8
+#endif
+constexpr int kEpt = ZERO_REDUCE_EPT;   // elements per lane per replica access
+
+template <int E> struct Bits;           // E bf16 values in one access
+template <> struct Bits<8> { typedef u32x4 T; };
+template <> struct Bits<4> { typedef zero::dev::u32x2 T; };
+template <> struct Bits<2> { typedef uint32_t T; };
+
+__device__ __forceinline__ uint32_t word(uint32_t x, int) { return x; }
+__device__ __forceinline__ uint32_t word(const zero::dev::u32x2& x, int j) { return x[j]; }
+__device__ __forceinline__ uint32_t word(const u32x4& x, int j) { return x[j]; }
+__device__ __forceinline__ void set_word(uint32_t& x, int, uint32_t w) { x = w; }
+__device__ __forceinline__ void set_word(zero::dev::u32x2& x, int j, uint32_t w) { x[j] = w; }
+__device__ __forceinline__ void set_word(u32x4& x, int j, uint32_t w) { x[j] = w; }
+
 // Vector path. src_off: element offset into each replica buffer of the first
 // element to reduce; out: first output element; n: elements to reduce. The
-// caller guarantees every replica + src_off and out are 16-byte aligned.
+// caller guarantees every replica + src_off and out are aligned to E elements.
 template <bool kNorm>
 __global__ __launch_bounds__(kThreads) void reduce_vec(ReplicaTable reps, int n_rep,
                                                        int64_t src_off,
                                                        uint16_t* __restrict__ out, int64_t n,
                                                        double* __restrict__ partials) {
+    typedef typename Bits<kEpt>::T V;
+    constexpr int kWords = kEpt / 2;
     const float r = static_cast<float>(n_rep);
-    const int64_t groups = n / 8;
+    const int64_t groups = n / kEpt;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     double sq = 0.0;
     for (int64_t i = tid; i < groups; i += stride) {
-        float acc[8];
+        float acc[kEpt];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int j = 0; j < kEpt; ++j) acc[j] = 0.0f;
         for (int k0 = 0; k0 < n_rep; k0 += kReplicaBatch) {
-            u32x4 x[kReplicaBatch];
+            V x[kReplicaBatch];
             const int kn = n_rep - k0 < kReplicaBatch ? n_rep - k0 : kReplicaBatch;
 #pragma unroll
             for (int k = 0; k < kReplicaBatch; ++k)
                 if (k < kn)
-                    x[k] = zero::dev::ld_stream(
-                        reinterpret_cast<const u32x4*>(reps.p[k0 + k] + src_off) + i);
+                    x[k] = zero::dev::ld_stream(reinterpret_cast<const V*>(reps.p[k0 + k] + src_off) + i);
 #pragma unroll
             for (int k = 0; k < kReplicaBatch; ++k) {
                 if (k < kn) {
-                    const uint32_t w[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(w[j]);
-                        acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(w[j]);
+                    for (int j = 0; j < kWords; ++j) {
+                        const uint32_t w = word(x[k], j);
+                        acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(w);
+                        acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(w);
                     }
                 }
             }
         }
-        u32x4 o;
-        o.x = zero::dev::pack_bf16(acc[0] / r, acc[1] / r);
-        o.y = zero::dev::pack_bf16(acc[2] / r, acc[3] / r);
-        o.z = zero::dev::pack_bf16(acc[4] / r, acc[5] / r);
-        o.w = zero::dev::pack_bf16(acc[6] / r, acc[7] / r);
-        zero::dev::st_stream(reinterpret_cast<u32x4*>(out) + i, o);
-        if (kNorm) sq += sq8(o);
+        V o;
+        uint32_t ow[kWords];
+#pragma unroll
+        for (int j = 0; j < kWords; ++j) {
+            ow[j] = zero::dev::pack_bf16(acc[2 * j] / r, acc[2 * j + 1] / r);
+            if (kNorm) {
+                const double a = static_cast<double>(zero::dev::lo_bf16(ow[j]));
+                const double b = static_cast<double>(zero::dev::hi_bf16(ow[j]));
+                sq += a * a;
+                sq += b * b;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kWords; ++j) set_word(o, j, ow[j]);
+        zero::dev::st_stream(reinterpret_cast<V*>(out) + i, o);
     }
-    // Ragged tail (< 8 elements), one per thread of the first threads.
-    const int64_t tail = n - groups * 8;
+    // Ragged tail (< E elements), one per thread of the first threads.
+    const int64_t tail = n - groups * kEpt;
     if (tid < tail) {
-        const int64_t e = groups * 8 + tid;
+        const int64_t e = groups * kEpt + tid;
         float acc = 0.0f;
         for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(reps.p[k][src_off + e]);
         const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
@@ -205,6 +231,7 @@ __global__ void clip_kernel(const double* __restrict__ partials, int n, double m
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int grid_for(int64_t work_items) {
     int64_t blocks = (work_items + kThreads - 1) / kThreads;
@@ -257,10 +284,10 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
     }
     const int64_t n = hi - lo, src_off = lo - begin;
     uint16_t* out = shard_grad + (lo - shard_lo);
-    bool vec = aligned16(out);
-    for (int32_t k = 0; k < n_replicas && vec; ++k) vec = aligned16(replicas[k] + src_off);
+    bool vec = aligned(out, 2 * kEpt);
+    for (int32_t k = 0; k < n_replicas && vec; ++k) vec = aligned(replicas[k] + src_off, 2 * kEpt);
     const bool norm = sqnorm_out != nullptr;
-    const int blocks = grid_for(vec ? n / 8 : n);
+    const int blocks = grid_for(vec ? n / kEpt : n);
     if (vec) {
         if (norm)
             hipLaunchKernelGGL(reduce_vec<true>, dim3(blocks), dim3(kThreads), 0, stream, table,
