@@ -1,26 +1,34 @@
-"""Benchmark: one data-parallel rank's partitioned optimizer step on one MI355X.
+"""Benchmark: the data-parallel rank's partitioned optimizer step on one MI355X.
 
-Default workload: the GPT-2-small tensor list (148 tensors, 124,439,808
-parameters) split over N_d = 8 ranks with 128-element alignment; the timed
-rank is rank 7 (15,555,072-element shard). One step is the whole hot path:
+Default workload (`gpt2-small`): the GPT-2-small tensor list (148 tensors,
+124,439,808 parameters) split over N_d = 8 ranks with 128-element alignment;
+the timed rank is rank 7 (15,555,072-element shard). One step is the whole hot
+path:
 
   reduce   rank 7's slice of 8 bf16 gradient replicas (full flat buffers in
            HBM), averaged, with its squared-norm partial fused in
-  clip     global-norm coefficient (max norm 1.0) from 8 partials on device
+  clip     global-norm coefficient (max norm 1.0) from the partials on device
   adamw    fp32 master/m/v update of the shard, bf16 parameters emitted
   gather   8 bf16 parameter shards -> 148 per-tensor parameters
 
-All inputs are seeded synthetic data resident in HBM before timing starts.
-The other ranks' norm partials and parameter shards are inputs (computed
-once, untimed, before the timed region): on a cluster they arrive through a
-scalar all-reduce and the parameter all-gather.
+Other workloads (`--workload`), each timed as its own configuration states:
+  llama3-8b   rank 63 of 64: six 25M-element buckets of 64 replicas reduced
+              into the 125,472,896-element shard, clip 1.0, AdamW
+  llama3-70b  rank 7 of 8: gradients arrive averaged; squared norm, clip 1.0,
+              AdamW on the 8,819,213,312-element shard
+  gpt-1.3b    all 8 ranks of the 1.3B GPT list: 8 replicas reduced for every
+              rank, AdamW on every shard, gather to 292 tensors
 
-Prints one JSON line. Only rank 0 at N = 1 exists: larger N is refused.
+All inputs are seeded synthetic data resident in HBM before timing starts. The
+other ranks' norm partials and parameter shards are inputs computed once,
+untimed (on a cluster they arrive through a scalar all-reduce and the
+parameter all-gather). Prints one JSON line. One GPU only: --gpus > 1 is refused.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -31,15 +39,16 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 METRIC = "shard AdamW step: params/sec and achieved HBM GB/s (% of MI355X peak)"
+WORKLOAD_NAMES = ["gpt2-small", "llama3-8b", "llama3-70b", "gpt-1.3b"]
 
 
 def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gpt2-small",
-                    choices=["gpt2-small", "gpt-1.3b-rank", "llama3-8b-rank"])
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200, or fewer for the large workloads)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="gpt2-small", choices=WORKLOAD_NAMES)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="rough budget for the oracle's host timing (0 disables it)")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -50,84 +59,220 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
-class Setup:
-    """Device buffers and inputs of one rank's step for a workload."""
+DEFAULT_STEPS = {"gpt2-small": (200, 20), "llama3-8b": (20, 3), "llama3-70b": (5, 1),
+                 "gpt-1.3b": (10, 2)}
+
+
+class RankWorkload:
+    """One rank's step: reduce (or plain squared norm), clip, AdamW, optional gather."""
+
+    SPECS = {
+        # name: tensor list, N_d, rank, replicas (0: gradients arrive averaged), bucket, gather
+        "gpt2-small": ("gpt2-small", 8, 7, 8, 0, True),
+        "llama3-8b": ("llama3-8b", 64, 63, 64, 25_000_000, False),
+        "llama3-70b": ("llama3-70b", 8, 7, 0, 0, False),
+    }
 
     def __init__(self, name: str, device):
         import torch
 
         import synth
         import zero_partitioned_mixed_partition_amd as zm
-        from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep
+        from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep, bucket_windows
 
-        spec = {
-            # name: (tensor list, N_d, rank, replicas, max_norm)
-            "gpt2-small": ("gpt2-small", 8, 7, 8, 1.0),
-            "gpt-1.3b-rank": ("gpt-1.3b", 8, 7, 8, 1.0),
-            "llama3-8b-rank": ("llama3-8b", 64, 63, 8, 1.0),
-        }[name]
-        w = synth.WORKLOADS[spec[0]]
-        self.name, self.workload = name, w
-        self.n_ranks, self.rank, self.replicas, self.max_norm = spec[1], spec[2], spec[3], spec[4]
+        lst, nd, rank, reps, bucket, gather = self.SPECS[name]
+        w = synth.WORKLOADS[lst]
+        self.name, self.workload, self.device = name, w, device
+        self.n_ranks, self.rank, self.replicas, self.bucket = nd, rank, reps, bucket
+        self.max_norm = w.max_norm if w.max_norm > 0 else 1.0
         self.seed = 1000 + w.seed
-        self.device = device
-        self.plan = zm.zero_partition_plan(w.numels, self.n_ranks, w.align)
+        self.plan = zm.zero_partition_plan(w.numels, nd, w.align)
+        P, S, phi = self.plan.padded_numel, self.plan.shard_numel, self.plan.numel
+        self.P, self.S, self.phi = P, S, phi
+        lo = rank * S
+        self.hyper = Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                           weight_decay=w.weight_decay)
+        spans = bucket_windows(P, bucket, lo, lo + S) if reps else []
+        self.rs = RankStep(self.plan, rank, len(spans), self.hyper, self.max_norm, device,
+                           gather=gather)
+        rs = self.rs
+        synth.device_normal_f32(rs.master, self.seed, synth.KIND_MASTER, 0, 0, lo, phi,
+                                synth.MASTER_SIGMA)
+        if gather:
+            for r in range(nd):
+                if r != rank:
+                    synth.device_normal_bf16(rs.param_shards[r], self.seed, synth.KIND_PARAM, 0, 0,
+                                             r * S, phi, synth.MASTER_SIGMA)
+        # gradient inputs
+        self.windows = []
+        if reps and not bucket:
+            full = []
+            for k in range(reps):
+                t = torch.empty(P, dtype=torch.int16, device=device)
+                synth.device_normal_bf16(t, self.seed, synth.KIND_REPLICA, 1, k, 0, phi,
+                                         synth.GRAD_SIGMA)
+                full.append(t)
+            self.windows = [(0, P, full)]
+        elif reps:
+            for b0, cnt in spans:
+                ws = []
+                for k in range(reps):
+                    t = torch.empty(cnt, dtype=torch.int16, device=device)
+                    synth.device_normal_bf16(t, self.seed, synth.KIND_REPLICA, 1, k, b0, phi,
+                                             synth.GRAD_SIGMA)
+                    ws.append(t)
+                self.windows.append((b0, cnt, ws))
+        else:
+            synth.device_normal_bf16(rs.grad, self.seed, synth.KIND_GRAD, 1, 0, lo, phi,
+                                     synth.GRAD_SIGMA)
+        # the other ranks' squared-norm partials
+        parts = torch.zeros(nd, dtype=torch.float64, device=device)
+        tmp = torch.empty(S, dtype=torch.int16, device=device)
+        for r in range(nd):
+            if r == rank:
+                continue
+            if reps and not bucket:          # their reduce over the same replicas
+                zm.zero_grad_reduce_shard(self.plan, r, self.windows[0][2], 0, P, tmp,
+                                          sqnorm_out=parts[r:r + 1], workspace=rs.workspace)
+            else:                            # their averaged gradients, drawn directly
+                sigma = synth.GRAD_SIGMA / math.sqrt(reps) if reps else synth.GRAD_SIGMA
+                synth.device_normal_bf16(tmp, self.seed, synth.KIND_GRAD, 1, 0, r * S, phi, sigma)
+                zm.zero_grad_sqnorm(tmp, parts[r:r + 1], workspace=rs.workspace)
+        del tmp
+        rs.partials[:nd].copy_(parts)
+        torch.cuda.synchronize()
+        if reps:
+            first = ("reduce", lambda: rs.reduce(self.windows))
+        else:
+            sq = zm._binding.Prepared(zm._binding._sqnorm, [
+                rs.grad.data_ptr(), S, rs.partials[rank:rank + 1].data_ptr(),
+                rs.workspace.data_ptr(), rs.workspace.numel(),
+                torch.cuda.current_stream(device).cuda_stream], "zero_grad_sqnorm")
+            first = ("sqnorm", sq)
+        self.phases = [first, ("clip", rs.clip), ("adamw", rs.adamw)]
+        if gather:
+            self.phases.append(("gather", rs.gather))
+        self.adamw_launches = 1
+        self.elems_per_step = S
+
+    def bytes_per_phase(self):
+        S = self.S
+        b = {"clip": 8 * (self.n_ranks + max(len(self.windows), 1)) + 4, "adamw": 28 * S}
+        if self.replicas:
+            b["reduce"] = (2 * self.replicas + 2) * S
+        else:
+            b["sqnorm"] = 2 * S
+        if any(p[0] == "gather" for p in self.phases):
+            b["gather"] = 4 * self.phi
+        return b
+
+    def describe(self):
+        red = (f"reduce of {self.replicas} bf16 replicas" +
+               (f" in {len(self.windows)} buckets of {self.bucket}" if self.bucket else "")
+               if self.replicas else "squared norm of the averaged bf16 gradient")
+        g = f" + gather of {len(self.workload.numels)} tensors" if self.rs.tensors else ""
+        return (f"{self.workload.name} tensor list, N_d={self.n_ranks}, rank {self.rank} shard of "
+                f"{self.S} elements; step = {red} + clip {self.max_norm} + AdamW{g}")
+
+
+class AllRanksWorkload:
+    """Every rank of one data-parallel job, in turn on one GPU: reduce, AdamW, then gather."""
+
+    def __init__(self, name: str, device):
+        import torch
+
+        import synth
+        import zero_partitioned_mixed_partition_amd as zm
+        from zero_partitioned_mixed_partition_amd import _binding as zb
+        from zero_partitioned_mixed_partition_amd.step import Hyper, _staggered_arena, plan_numels
+
+        w = synth.WORKLOADS[name]
+        self.name, self.workload, self.device = name, w, device
+        self.n_ranks, self.rank, self.replicas = w.n_ranks, None, w.replicas
+        self.seed = 1000 + w.seed
+        self.plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
         P, S, phi = self.plan.padded_numel, self.plan.shard_numel, self.plan.numel
         self.P, self.S, self.phi = P, S, phi
         self.hyper = Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                            weight_decay=w.weight_decay)
-        self.rs = RankStep(self.plan, self.rank, 1, self.hyper, self.max_norm, device)
-
-        # gradient replicas: full padded flat buffers, one per data-parallel replica
+        views, self.arena = _staggered_arena(
+            [(P, torch.float32), (P, torch.float32), (P, torch.float32), (P, torch.int16),
+             (P, torch.int16)], device)
+        self.master, self.m, self.v, self.grad, self.param = views
+        synth.device_normal_f32(self.master, self.seed, synth.KIND_MASTER, 0, 0, 0, phi,
+                                synth.MASTER_SIGMA)
         self.reps = []
         for k in range(self.replicas):
             t = torch.empty(P, dtype=torch.int16, device=device)
             synth.device_normal_bf16(t, self.seed, synth.KIND_REPLICA, 1, k, 0, phi, synth.GRAD_SIGMA)
             self.reps.append(t)
-        synth.device_normal_f32(self.rs.master, self.seed, synth.KIND_MASTER, 0, 0, self.rank * S, phi,
-                                synth.MASTER_SIGMA)
-        for r in range(self.n_ranks):
-            if r != self.rank:
-                synth.device_normal_bf16(self.rs.param_shards[r], self.seed, synth.KIND_PARAM, 0, 0,
-                                         r * S, phi, synth.MASTER_SIGMA)
-        # other ranks' squared-norm partials: their reduce, run once here
-        tmp = torch.empty(S, dtype=torch.int16, device=device)
-        parts = torch.zeros(self.n_ranks, dtype=torch.float64, device=device)
-        for r in range(self.n_ranks):
-            if r != self.rank:
-                zm.zero_grad_reduce_shard(self.plan, r, self.reps, 0, P, tmp,
-                                          sqnorm_out=parts[r:r + 1], workspace=self.rs.workspace)
-        self.rs.partials[:self.n_ranks].copy_(parts)
+        self.tensors = [torch.empty(n, dtype=torch.int16, device=device)
+                        for n in plan_numels(self.plan)]
+        self.partials = torch.zeros(w.n_ranks, dtype=torch.float64, device=device)
+        self.workspace = torch.empty(zb.zero_sqnorm_workspace_bytes(), dtype=torch.uint8,
+                                     device=device)
+        st = torch.cuda.current_stream(device).cuda_stream
+        sl = [slice(r * S, (r + 1) * S) for r in range(w.n_ranks)]
+        self._reduce = [zb.prepare_grad_reduce_shard(self.plan, r, self.reps, 0, P,
+                                                     self.grad[sl[r]], self.partials[r:r + 1],
+                                                     self.workspace, st)
+                        for r in range(w.n_ranks)]
+        self._adamw = [zb.prepare_shard_adamw_step(self.master[sl[r]], self.m[sl[r]],
+                                                   self.v[sl[r]], self.grad[sl[r]],
+                                                   self.param[sl[r]], clip_scale=None, stream=st,
+                                                   **self.hyper.as_kwargs())
+                       for r in range(w.n_ranks)]
+        self._gather = zb.prepare_gather_params(self.plan, [self.param[s] for s in sl],
+                                                self.tensors, st)
+        self.t = 0
         torch.cuda.synchronize()
-        self.windows = [(0, P, self.reps)]
 
-    def step(self):
-        self.rs.step(self.windows)
+        def reduce_all():
+            for f in self._reduce:
+                f()
 
-    # algorithmic bytes per step of each kernel (what the method must move)
-    def bytes_per_kernel(self):
-        S, R = self.S, self.replicas
-        return {"reduce": (2 * R + 2) * S, "clip": 8 * (self.n_ranks + 1) + 4,
-                "adamw": 28 * S, "gather": 4 * self.phi}
+        def adamw_all():
+            self.t += 1
+            for f in self._adamw:
+                f(self.t)
+
+        self.phases = [("reduce", reduce_all), ("adamw", adamw_all), ("gather", self._gather)]
+        self.adamw_launches = w.n_ranks
+        self.elems_per_step = P
+
+    def bytes_per_phase(self):
+        P = self.P
+        return {"reduce": (2 * self.replicas + 2) * P, "adamw": 28 * P, "gather": 4 * self.phi}
+
+    def describe(self):
+        return (f"{self.workload.name} tensor list, N_d={self.n_ranks}, all {self.n_ranks} ranks in "
+                f"turn ({self.S} elements each); step = reduce of {self.replicas} bf16 replicas per "
+                f"rank + AdamW per shard + gather of {len(self.workload.numels)} tensors")
 
 
-def time_kernels(setup: "Setup", steps: int):
-    """Per-kernel mean duration (ms) from HIP events on the launch stream."""
+def make_workload(name: str, device):
+    return AllRanksWorkload(name, device) if name == "gpt-1.3b" else RankWorkload(name, device)
+
+
+def run_step(wl) -> None:
+    for _, fn in wl.phases:
+        fn()
+
+
+def time_phases(wl, steps: int):
+    """Mean duration (ms) per step of each phase, HIP events on the launch stream."""
     import torch
-    names = ["reduce", "clip", "adamw", "gather"]
-    calls = {"reduce": lambda: setup.rs.reduce(setup.windows), "clip": setup.rs.clip,
-             "adamw": setup.rs.adamw, "gather": setup.rs.gather}
-    ev = {n: [] for n in names}
+    ev = {n: [] for n, _ in wl.phases}
     for _ in range(steps):
-        for n in names:
+        for n, fn in wl.phases:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
-            calls[n]()
+            fn()
             b.record()
             ev[n].append((a, b))
     torch.cuda.synchronize()
-    return {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
+    return {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in ev}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_traffic.json")
@@ -143,53 +288,81 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(setup: "Setup"):
+def measured_traffic(elems_per_launch: int):
     """HBM bytes per AdamW launch from the committed counter runs (FETCH_SIZE and
     WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel sources have
     changed since they were taken or they cover another shard size."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     d = json.load(open(TRAFFIC_FILE))
-    if d.get("source_sha256") != kernel_source_digest() or d.get("elems") != setup.S:
+    if d.get("source_sha256") != kernel_source_digest() or d.get("elems") != elems_per_launch:
         return None
     return d["bytes_per_launch"]
 
 
-def cpu_baseline(setup: "Setup", budget_s: float):
-    """The oracle's rank step on the host for the same workload, bounded in time."""
+def cpu_baseline(wl, budget_s: float):
+    """The oracle on the host for the same workload, bounded in time. The default
+    workload times the oracle's whole rank step; the large ones time the same
+    per-element work (reduce, exact norm, clip, AdamW) on a 2^24-element slice."""
     import numpy as np
 
     import oracle
     import synth
-    P, S, phi, rank = setup.P, setup.S, setup.phi, setup.rank
-    ref = oracle.partition_plan(setup.workload.numels, setup.n_ranks, setup.workload.align)
-    lo = rank * S
-    # the oracle needs only the rank's window of each replica for its reduce
-    reps = [synth.normal_bf16(S, setup.seed, synth.KIND_REPLICA, 1, k, lo, phi, synth.GRAD_SIGMA)
-            for k in range(setup.replicas)]
-    state = {"master": synth.normal_f32(S, setup.seed, synth.KIND_MASTER, 0, 0, lo, phi,
-                                        synth.MASTER_SIGMA),
-             "exp_avg": np.zeros(S, np.float32), "exp_avg_sq": np.zeros(S, np.float32)}
-    shards = [synth.normal_bf16(S, setup.seed, synth.KIND_PARAM, 0, 0, r * S, phi, synth.MASTER_SIGMA)
-              for r in range(setup.n_ranks)]
-    partials = [1.0] * setup.n_ranks
-    hp = dict(lr=setup.hyper.lr, beta1=setup.hyper.beta1, beta2=setup.hyper.beta2,
-              eps=setup.hyper.eps, weight_decay=setup.hyper.weight_decay)
-    # one untimed step first: the first touch of fresh host pages is not oracle work
-    oracle.rank_step(ref, rank, reps, lo, state, shards, partials, 1, hp, setup.max_norm)
+    hp = wl.hyper.as_kwargs()
+    if wl.name == "gpt2-small":
+        S, phi, rank = wl.S, wl.phi, wl.rank
+        ref = oracle.partition_plan(wl.workload.numels, wl.n_ranks, wl.workload.align)
+        lo = rank * S
+        reps = [synth.normal_bf16(S, wl.seed, synth.KIND_REPLICA, 1, k, lo, phi, synth.GRAD_SIGMA)
+                for k in range(wl.replicas)]
+        state = {"master": synth.normal_f32(S, wl.seed, synth.KIND_MASTER, 0, 0, lo, phi,
+                                            synth.MASTER_SIGMA),
+                 "exp_avg": np.zeros(S, np.float32), "exp_avg_sq": np.zeros(S, np.float32)}
+        shards = [synth.normal_bf16(S, wl.seed, synth.KIND_PARAM, 0, 0, r * S, phi,
+                                    synth.MASTER_SIGMA) for r in range(wl.n_ranks)]
+        partials = [1.0] * wl.n_ranks
+
+        def one(t):
+            oracle.rank_step(ref, rank, reps, lo, state, shards, partials, t, hp, wl.max_norm)
+        sample = (f"full rank-{rank} steps of the same workload (reduce of {wl.replicas} replica "
+                  f"windows, exact norm, clip, AdamW on {S} elements, gather of {phi} parameters)")
+        per_step = S
+    else:
+        n = min(wl.S, 1 << 24)
+        g0 = (wl.rank or 0) * wl.S
+        R = wl.replicas
+        if R:
+            reps = [synth.normal_bf16(n, wl.seed, synth.KIND_REPLICA, 1, k, g0, wl.phi,
+                                      synth.GRAD_SIGMA) for k in range(R)]
+        else:
+            reps = [synth.normal_bf16(n, wl.seed, synth.KIND_GRAD, 1, 0, g0, wl.phi,
+                                      synth.GRAD_SIGMA)]
+        window = oracle.partition_plan([n], 1, 1)
+        st = {"p": synth.normal_f32(n, wl.seed, synth.KIND_MASTER, 0, 0, g0, wl.phi,
+                                    synth.MASTER_SIGMA),
+              "m": np.zeros(n, np.float32), "v": np.zeros(n, np.float32)}
+
+        def one(t):
+            g = np.zeros(n, np.uint16)
+            oracle.reduce_shard(window, 0, reps, 0, g)
+            clip = oracle.clip_scale([oracle.sqnorm(g)], 1.0)
+            st["p"], st["m"], st["v"], _ = oracle.adamw_step(st["p"], st["m"], st["v"], g, t,
+                                                             clip=clip, **hp)
+        sample = (f"the per-element work of this workload (reduce of {max(R, 1)} replica windows, "
+                  f"exact norm, clip, AdamW) on a {n}-element slice of the shard")
+        per_step = n
+    one(1)          # untimed: the first touch of fresh host pages is not oracle work
     t0 = time.perf_counter()
-    n = 0
+    k = 0
     while True:
-        n += 1
-        oracle.rank_step(ref, rank, reps, lo, state, shards, partials, 1 + n, hp, setup.max_norm)
+        k += 1
+        one(1 + k)
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
+        if el >= budget_s or k >= 50:
             break
-    return {"value": S * n / el, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full rank-{rank} steps of the same workload (reduce of "
-                      f"{setup.replicas} replica windows, exact norm, clip, AdamW on "
-                      f"{S} elements, gather of {phi} parameters), single-threaded numpy",
-            "seconds": el, "host_cpus": len(os.sched_getaffinity(0))}
+    return {"value": per_step * k / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{k} {sample}, single-threaded numpy", "seconds": el,
+            "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def main(argv=None):
@@ -202,10 +375,12 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+    steps = args.steps if args.steps is not None else DEFAULT_STEPS[args.workload][0]
+    warmup = args.warmup if args.warmup is not None else DEFAULT_STEPS[args.workload][1]
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
-    setup = Setup(args.workload, device)
+    wl = make_workload(args.workload, device)
     if args.profile_steps:
         if args.calibrate_copy:
             src = torch.ones(1 << 28, dtype=torch.float32, device=device)
@@ -215,83 +390,80 @@ def main(argv=None):
             torch.cuda.synchronize()
             del src, dst
         for _ in range(args.profile_steps):
-            setup.step()
+            run_step(wl)
         torch.cuda.synchronize()
         print(f"[bench] ran {args.profile_steps} steps for profiling", file=sys.stderr, flush=True)
         return 0
 
-    for _ in range(args.warmup):
-        setup.step()
+    for _ in range(warmup):
+        run_step(wl)
     torch.cuda.synchronize()
-    # Timed region: whole steps; AdamW is bracketed by events on the stream it is
-    # launched on (torch's current stream, which every call here uses).
+    # Timed region: whole steps; the AdamW phase is bracketed by events on the
+    # stream it is launched on (torch's current stream, which every call here uses).
     adamw_ev = []
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps):
-        setup.rs.reduce(setup.windows)
-        setup.rs.clip()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        setup.rs.adamw()
-        b.record()
-        adamw_ev.append((a, b))
-        setup.rs.gather()
+    for _ in range(steps):
+        for name, fn in wl.phases:
+            if name == "adamw":
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                adamw_ev.append((a, b))
+            else:
+                fn()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
-    adamw_ms = sum(a.elapsed_time(b) for a, b in adamw_ev) / len(adamw_ev)
-    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s), "
-          f"adamw {adamw_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    ms_per_step = start.elapsed_time(end) / steps
+    adamw_ms = sum(a.elapsed_time(b) for a, b in adamw_ev) / len(adamw_ev) / wl.adamw_launches
+    print(f"[bench] {steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s), "
+          f"adamw {adamw_ms * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
 
-    kernel_ms = time_kernels(setup, max(20, min(args.steps, 200)))
-    kernel_ms["adamw"] = adamw_ms
-    bpk = setup.bytes_per_kernel()
-    kernels = {n: {"ms": kernel_ms[n], "bytes": bpk[n],
-                   "gbs": bpk[n] / (kernel_ms[n] * 1e-3) / 1e9,
-                   "frac_of_hbm_peak": bpk[n] / (kernel_ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS}
-               for n in kernel_ms}
-    step_bytes = sum(bpk.values())
-    adamw_gbs = kernels["adamw"]["gbs"]
-    value = setup.S / (ms_per_step * 1e-3)
-    traffic = measured_traffic(setup)
+    phase_ms = time_phases(wl, max(3, min(steps, 100)))
+    bpp = wl.bytes_per_phase()
+    kernels = {n: {"ms": phase_ms[n], "bytes": bpp[n],
+                   "gbs": bpp[n] / (phase_ms[n] * 1e-3) / 1e9,
+                   "frac_of_hbm_peak": bpp[n] / (phase_ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+               for n in phase_ms}
+    elems_per_launch = wl.elems_per_step // wl.adamw_launches
+    adamw_bytes = 28 * elems_per_launch
+    adamw_gbs = adamw_bytes / (adamw_ms * 1e-3) / 1e9
+    value = wl.elems_per_step / (ms_per_step * 1e-3)
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(setup, args.cpu_baseline_seconds)
+        cpu = cpu_baseline(wl, args.cpu_baseline_seconds)
 
     line = {
         "metric": METRIC,
         "value": value,
         "unit": "params/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{setup.workload.name} tensor list, N_d={setup.n_ranks}, "
-                               f"rank {setup.rank} shard of {setup.S} elements; step = reduce of "
-                               f"{setup.replicas} bf16 replicas + sqnorm + clip {setup.max_norm} + "
-                               f"AdamW + gather of {len(setup.workload.numels)} tensors",
-                   "params": setup.phi, "shard_elems": setup.S, "n_ranks": setup.n_ranks,
-                   "replicas": setup.replicas, "parallelism": "one rank of dp8 (one GPU)"},
-        "adamw_params_per_s": setup.S / (kernels["adamw"]["ms"] * 1e-3),
+        "config": {"workload": wl.describe(), "name": wl.name, "params": wl.phi,
+                   "shard_elems": wl.S, "n_ranks": wl.n_ranks, "replicas": wl.replicas,
+                   "parallelism": "one GPU's share of a dp job"},
+        "adamw_params_per_s": elems_per_launch / (adamw_ms * 1e-3),
         "adamw_hbm_gbs": adamw_gbs,
         "adamw_frac_of_hbm_peak": adamw_gbs / HBM_PEAK_GBS,
-        "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_hbm_gbs": sum(bpp.values()) / (ms_per_step * 1e-3) / 1e9,
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": "adamw_kernel", "achieved": adamw_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": adamw_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic},
+                     "traffic": measured_traffic(elems_per_launch)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

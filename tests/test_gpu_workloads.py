@@ -137,13 +137,13 @@ def test_gpt2_small_rank7_hundred_steps_clip(zm):
 
 def test_bench_pipeline_matches_oracle(zm):
     import bench
-    setup = bench.Setup("gpt2-small", dev())
+    setup = bench.make_workload("gpt2-small", dev())
     P, S, phi, rank, R = setup.P, setup.S, setup.phi, setup.rank, setup.replicas
     ref = oracle.partition_plan(setup.workload.numels, setup.n_ranks, setup.workload.align)
     note(f"bench pipeline: reduce of {R} replicas for rank {rank} of {setup.n_ranks}, S={S}")
     steps = 2
     for _ in range(steps):
-        setup.step()
+        bench.run_step(setup)
     torch.cuda.synchronize()
 
     # oracle: every rank's reduced gradient (for the partials), then rank 7's steps

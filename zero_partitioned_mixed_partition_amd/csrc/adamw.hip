@@ -14,8 +14,8 @@
 // bf16), about 15 flops: HBM-bound by a factor of ~40 against the fp32
 // vector ridge point, so no matrix cores. Each lane updates one element with
 // non-temporal accesses (dword per fp32 array, short for the bf16 gradient
-// and parameter). The grid covers the shard with one element per lane (up to
-// the 2^32 work-items of one dispatch, then lanes stride): measured on MI355X,
+// and parameter). The grid covers the shard with one element per lane (shards
+// past the 2^32 work-items of one dispatch take several launches): measured on MI355X,
 // short-lived waves with narrow accesses sustain more bandwidth on this
 // 4-read/4-write pattern than wide vectors or a persistent loop. The same
 // kernel serves any pointer alignment. Indices are 64-bit.
@@ -172,12 +172,8 @@ bool ranges_overlap(const void* a, size_t a_bytes, const void* b, size_t b_bytes
     return x < y + b_bytes && y < x + a_bytes;
 }
 
-// One lane group per thread; a dispatch holds fewer than 2^32 work-items, so
-// beyond that threads stride.
 int64_t blocks_for(int64_t items) {
-    constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
-    int64_t blocks = (items + kThreads - 1) / kThreads;
-    if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+    const int64_t blocks = (items + kThreads - 1) / kThreads;
     return blocks < 1 ? 1 : blocks;
 }
 
@@ -222,17 +218,28 @@ extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, floa
     c.sqrt_bc2 = static_cast<float>(std::sqrt(bc2));
     c.decay = static_cast<float>(1.0 - lr * weight_decay);
 
+    // One lane group per lane. A dispatch holds fewer than 2^32 work-items, so
+    // larger shards go out as consecutive single-pass launches over chunks
+    // (measured faster than lanes looping over a capped grid).
+    constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
     const bool vec = kEpt > 1 && aligned(master, 4 * kEpt) && aligned(exp_avg, 4 * kEpt) &&
                      aligned(exp_avg_sq, 4 * kEpt) && aligned(grad, 2 * kEpt) &&
                      aligned(param_out, 2 * kEpt);
-    if (vec) {
-        hipLaunchKernelGGL(adamw_kernel<kEpt>, dim3(static_cast<unsigned>(blocks_for(n / kEpt))),
-                           dim3(kThreads), 0, stream, master, exp_avg, exp_avg_sq, grad, param_out, n,
-                           c, clip_scale);
-    } else {
-        hipLaunchKernelGGL(adamw_kernel<1>, dim3(static_cast<unsigned>(blocks_for(n))),
-                           dim3(kThreads), 0, stream, master, exp_avg, exp_avg_sq, grad, param_out, n,
-                           c, clip_scale);
+    const int ept = vec ? kEpt : 1;
+    const int64_t chunk = kMaxBlocks * kThreads * ept;        // elements per launch
+    for (int64_t off = 0; off < n; off += chunk) {
+        const int64_t len = n - off < chunk ? n - off : chunk;
+        const int64_t blocks = blocks_for(len / ept + (len % ept ? 1 : 0));
+        if (vec)
+            hipLaunchKernelGGL(adamw_kernel<kEpt>, dim3(static_cast<unsigned>(blocks)),
+                               dim3(kThreads), 0, stream, master + off, exp_avg + off,
+                               exp_avg_sq + off, grad + off, param_out + off, len, c, clip_scale);
+        else
+            hipLaunchKernelGGL(adamw_kernel<1>, dim3(static_cast<unsigned>(blocks)),
+                               dim3(kThreads), 0, stream, master + off, exp_avg + off,
+                               exp_avg_sq + off, grad + off, param_out + off, len, c, clip_scale);
+        const zero_status st = zero::check_hip(hipGetLastError(), "zero_shard_adamw_step launch");
+        if (st != ZERO_OK) return st;
     }
-    return zero::check_hip(hipGetLastError(), "zero_shard_adamw_step launch");
+    return ZERO_OK;
 }

@@ -81,12 +81,12 @@ template <> struct Bits<8> { typedef u32x4 T; };
 template <> struct Bits<4> { typedef zero::dev::u32x2 T; };
 template <> struct Bits<2> { typedef uint32_t T; };
 
-__device__ __forceinline__ uint32_t word(uint32_t x, int) { return x; }
-__device__ __forceinline__ uint32_t word(const zero::dev::u32x2& x, int j) { return x[j]; }
-__device__ __forceinline__ uint32_t word(const u32x4& x, int j) { return x[j]; }
-__device__ __forceinline__ void set_word(uint32_t& x, int, uint32_t w) { x = w; }
-__device__ __forceinline__ void set_word(zero::dev::u32x2& x, int j, uint32_t w) { x[j] = w; }
-__device__ __forceinline__ void set_word(u32x4& x, int j, uint32_t w) { x[j] = w; }
+[[maybe_unused]] __device__ __forceinline__ uint32_t word(uint32_t x, int) { return x; }
+[[maybe_unused]] __device__ __forceinline__ uint32_t word(const zero::dev::u32x2& x, int j) { return x[j]; }
+[[maybe_unused]] __device__ __forceinline__ uint32_t word(const u32x4& x, int j) { return x[j]; }
+[[maybe_unused]] __device__ __forceinline__ void set_word(uint32_t& x, int, uint32_t w) { x = w; }
+[[maybe_unused]] __device__ __forceinline__ void set_word(zero::dev::u32x2& x, int j, uint32_t w) { x[j] = w; }
+[[maybe_unused]] __device__ __forceinline__ void set_word(u32x4& x, int j, uint32_t w) { x[j] = w; }
 
 // Vector path. src_off: element offset into each replica buffer of the first
 // element to reduce; out: first output element; n: elements to reduce. The

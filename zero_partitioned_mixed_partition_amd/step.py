@@ -65,8 +65,10 @@ class RankStep:
         # per-rank partials [0, N_d) (own slot left 0), then one per own window
         self.partials = torch.zeros(nd + n_windows, dtype=torch.float64, device=device)
         self.scale = torch.ones(1, dtype=torch.float32, device=device)
+        # other ranks' shards (gather inputs) exist only when this step gathers
         self.param_shards = [own_param if r == rank else
-                             torch.zeros(s, dtype=torch.int16, device=device) for r in range(nd)]
+                             (torch.zeros(s, dtype=torch.int16, device=device) if gather else None)
+                             for r in range(nd)]
         self.tensors: List[torch.Tensor] = []
         if gather:
             self.tensors = [torch.empty(max(n, 0), dtype=torch.int16, device=device)
