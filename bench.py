@@ -224,6 +224,18 @@ class AllRanksWorkload:
                        for r in range(w.n_ranks)]
         self._gather = zb.prepare_gather_params(self.plan, [self.param[s] for s in sl],
                                                 self.tensors, st)
+        # outside the step: one replica flattening its per-tensor gradients into a
+        # flat buffer (the step before the reduce)
+        offs = [self.plan.tensor_offset(t) for t in range(self.plan.num_tensors)]
+        self.grad_tensors = []
+        for n, off in zip(plan_numels(self.plan), offs):
+            g = torch.empty(n, dtype=torch.int16, device=device)
+            synth.device_normal_bf16(g, self.seed, synth.KIND_REPLICA, 1, 0, off, phi,
+                                     synth.GRAD_SIGMA)
+            self.grad_tensors.append(g)
+        self.flat_out = torch.empty(P, dtype=torch.int16, device=device)
+        self.extra_phases = [("flatten", zb.prepare_flatten_params(self.plan, self.grad_tensors,
+                                                                  self.flat_out, st))]
         self.t = 0
         torch.cuda.synchronize()
 
@@ -242,7 +254,8 @@ class AllRanksWorkload:
 
     def bytes_per_phase(self):
         P = self.P
-        return {"reduce": (2 * self.replicas + 2) * P, "adamw": 28 * P, "gather": 4 * self.phi}
+        return {"reduce": (2 * self.replicas + 2) * P, "adamw": 28 * P, "gather": 4 * self.phi,
+                "flatten": 4 * self.phi + 2 * (P - self.phi)}
 
     def describe(self):
         return (f"{self.workload.name} tensor list, N_d={self.n_ranks}, all {self.n_ranks} ranks in "
@@ -426,10 +439,16 @@ def main(argv=None):
 
     phase_ms = time_phases(wl, max(3, min(steps, 100)))
     bpp = wl.bytes_per_phase()
-    kernels = {n: {"ms": phase_ms[n], "bytes": bpp[n],
-                   "gbs": bpp[n] / (phase_ms[n] * 1e-3) / 1e9,
-                   "frac_of_hbm_peak": bpp[n] / (phase_ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS}
-               for n in phase_ms}
+
+    def rates(ms):
+        return {n: {"ms": ms[n], "bytes": bpp[n], "gbs": bpp[n] / (ms[n] * 1e-3) / 1e9,
+                    "frac_of_hbm_peak": bpp[n] / (ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS} for n in ms}
+    kernels = rates(phase_ms)
+    outside = None
+    if getattr(wl, "extra_phases", None):
+        class _Extra:
+            phases = wl.extra_phases
+        outside = rates(time_phases(_Extra, max(3, min(steps, 20))))
     elems_per_launch = wl.elems_per_step // wl.adamw_launches
     adamw_bytes = 28 * elems_per_launch
     adamw_gbs = adamw_bytes / (adamw_ms * 1e-3) / 1e9
@@ -459,8 +478,9 @@ def main(argv=None):
         "adamw_params_per_s": elems_per_launch / (adamw_ms * 1e-3),
         "adamw_hbm_gbs": adamw_gbs,
         "adamw_frac_of_hbm_peak": adamw_gbs / HBM_PEAK_GBS,
-        "step_hbm_gbs": sum(bpp.values()) / (ms_per_step * 1e-3) / 1e9,
+        "step_hbm_gbs": sum(bpp[n] for n, _ in wl.phases) / (ms_per_step * 1e-3) / 1e9,
         "kernels": kernels,
+        "kernels_outside_step": outside,
         "roofline": {"bound": "hbm", "kernel": "adamw_kernel", "achieved": adamw_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": adamw_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(elems_per_launch)},

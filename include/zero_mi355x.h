@@ -17,6 +17,8 @@
  *   zero_shard_adamw_step   fp32 master/m/v update and bf16 parameter emit
  *   zero_gather_params      bf16 shards back to per-tensor parameters
  *                           (all-gather output layout, then un-flatten)
+ *   zero_flatten_params     per-tensor bf16 buffers into the padded flat buffer
+ *                           (the step before the reduce; inverse of the gather)
  *
  * Conventions, for every function below:
  *   - bf16 values travel as raw uint16_t bit patterns; fp32 as float.
@@ -222,6 +224,23 @@ zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_
  * Errors: ZERO_EINVAL (null plan/arrays or a needed null pointer); ZERO_EHIP. */
 zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* shards,
                                uint16_t* const* tensors, hipStream_t stream);
+
+/* ------------------------------------------------------------------ flatten
+ *
+ * [ZF] "FSDP-1: FlatParameter and Module-Level Wrapping": a unit's tensors are
+ * flattened into one contiguous 1-D buffer, padded to a length divisible by
+ * the world size. This builds that buffer from per-tensor bf16 buffers: tensor
+ * t lands at flat elements [offset_t, offset_t + numel_t) and the padding
+ * [Phi, P) is set to +0. It is the inverse of zero_gather_params and the step
+ * before zero_grad_reduce_shard: each data-parallel replica flattens its
+ * per-tensor gradients into the flat buffer that the reduce-scatter cuts into
+ * N_d shards.
+ * tensors      host [T] of device pointers, tensor t to numel_t bf16 values
+ *              (may be NULL only for zero-sized tensors).
+ * flat         device [P] bf16, written entirely; must not overlap the tensors.
+ * Errors: ZERO_EINVAL (null plan/arrays or a needed null pointer); ZERO_EHIP. */
+zero_status zero_flatten_params(const zero_plan* plan, const uint16_t* const* tensors,
+                                uint16_t* flat, hipStream_t stream);
 
 /* ------------------------------------------------------------------ diagnostics */
 const char* zero_status_string(zero_status status);   /* static string */

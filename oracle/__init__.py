@@ -22,6 +22,7 @@ Pinning status (what each function is checked against, outside itself):
               torch.optim.AdamW (CPU fp32), pure-Python brute force,
               shard invariance
   gather.py   flatten/gather round trip
+  flatten.py  gather(flatten(x)) = x, padding zero, hand-worked case
 The fp32 evaluation order inside AdamW and the clip's 1e-6 guard are readings
 (the pages do not write the update out); they are pinned by the closed forms
 and the torch cross-check within tolerance, not bit for bit by the pages.
@@ -29,6 +30,7 @@ and the torch cross-check within tolerance, not bit for bit by the pages.
 from .adamw import AdamWConstants, adamw_constants, adamw_step  # noqa: F401
 from .bf16 import bf16_to_f32, f32_to_bf16  # noqa: F401
 from .clip import clip_scale  # noqa: F401
+from .flatten import flatten_params  # noqa: F401
 from .gather import gather_params  # noqa: F401
 from .plan import Plan, memory_bytes, partition_plan  # noqa: F401
 from .reduce import reduce_shard  # noqa: F401

@@ -263,3 +263,52 @@ def test_gather_workload_plans_and_misaligned_destinations(zm):
         for i, b in enumerate(bufs):
             off = ref.offsets[i]
             assert_bits_equal(host_u16(b)[1:], flat[off:off + w.numels[i]], f"{name} tensor {i}")
+
+
+# ----------------------------------------------------------------------------- flatten
+
+@pytest.mark.parametrize("seed", range(6))
+def test_flatten_random_plans(zm, seed):
+    rng = np.random.default_rng(100 + seed)
+    t = int(rng.integers(1, 9))
+    numels = [int(x) for x in rng.integers(0, 40_000, t)]
+    numels[-1] += 1
+    n_ranks = int(rng.choice([1, 2, 3, 4, 8]))
+    align = int(rng.choice([1, 8, 128]))
+    note(f"flatten numels={numels} N_d={n_ranks} A={align}")
+    ref = oracle.partition_plan(numels, n_ranks, align)
+    plan = zm.zero_partition_plan(numels, n_ranks, align)
+    tensors = [rng.integers(0, 1 << 16, n).astype(np.uint16) for n in numels]
+    want = oracle.flatten_params(ref, tensors)
+    # odd seeds place every source one element into its buffer (2-byte misaligned)
+    off = seed % 2
+    bufs = [to_dev_u16(np.concatenate([np.zeros(off, np.uint16), x])) for x in tensors]
+    flat = to_dev_u16(np.full(ref.padded_numel, 0x5555, np.uint16))
+    zm.zero_flatten_params(plan, [b[off:] for b in bufs], flat)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u16(flat), want, "flat buffer")
+
+
+def test_flatten_workload_plans_and_gather_round_trip(zm):
+    for name in ("tiny-b", "gpt2-small"):
+        w = synth.WORKLOADS[name]
+        ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
+        plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
+        note(f"flatten {name} T={len(w.numels)} P={ref.padded_numel}")
+        host = [synth.normal_bf16(n, 40, synth.KIND_GRAD, 1, 0, off, ref.numel, 1e-3)
+                for n, off in zip(w.numels, ref.offsets)]
+        d_t = [to_dev_u16(x) for x in host]
+        flat = torch.full((ref.padded_numel,), 0x2222, dtype=torch.int16, device=dev())
+        zm.zero_flatten_params(plan, d_t, flat)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_u16(flat), oracle.flatten_params(ref, host), f"{name} flat")
+        # the generator keys values by global index, so this flat buffer is also the
+        # generator's flat gradient with zero padding
+        assert_bits_equal(host_u16(flat), synth.normal_bf16(ref.padded_numel, 40, synth.KIND_GRAD,
+                                                            1, 0, 0, ref.numel, 1e-3), "generator")
+        S = ref.shard_numel
+        outs = [torch.empty(n, dtype=torch.int16, device=dev()) for n in w.numels]
+        zm.zero_gather_params(plan, [flat[r * S:(r + 1) * S] for r in range(w.n_ranks)], outs)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, host)):
+            assert_bits_equal(host_u16(a), b, f"{name} round trip tensor {i}")

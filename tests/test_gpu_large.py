@@ -299,3 +299,23 @@ def test_llama3_70b_rank7_five_steps_windows(zm):
     assert np.float32(d_scale.item()) == oracle.clip_scale(oparts, 1.0)
     del rs
     _free_gpu()
+
+
+def test_gpt_1p3b_full_size_flatten(zm):
+    w = synth.WORKLOADS["gpt-1.3b"]
+    ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
+    plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
+    tensors = []
+    for n, off in zip(w.numels, ref.offsets):
+        t = torch.empty(n, dtype=torch.int16, device=dev())
+        synth.device_normal_bf16(t, w.seed, synth.KIND_REPLICA, 1, 3, off, ref.numel, synth.GRAD_SIGMA)
+        tensors.append(t)
+    flat = torch.full((ref.padded_numel,), 0x1111, dtype=torch.int16, device=dev())
+    zm.zero_flatten_params(plan, tensors, flat)
+    torch.cuda.synchronize()
+    note(f"gpt-1.3b flatten: {ref.numel} parameters from {len(w.numels)} tensors")
+    host = [synth.normal_bf16(n, w.seed, synth.KIND_REPLICA, 1, 3, off, ref.numel, synth.GRAD_SIGMA)
+            for n, off in zip(w.numels, ref.offsets)]
+    assert_bits_equal(host_u16(flat), oracle.flatten_params(ref, host), "flat buffer")
+    del tensors, flat
+    _free_gpu()

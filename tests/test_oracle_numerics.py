@@ -396,3 +396,21 @@ def test_sqnorm_accumulator_merge_is_exact():
     for p in parts:
         acc.merge(p)
     assert acc.value() == oracle.sqnorm_fsum(b)
+
+
+def test_flatten_hand_worked_and_round_trips():
+    # [2], [3] over 2 ranks with 2-element alignment: Phi 5, P 8, S 4
+    plan = oracle.partition_plan([2, 3], 2, 2)
+    flat = oracle.flatten_params(plan, [np.array([1, 2], np.uint16), np.array([3, 4, 5], np.uint16)])
+    assert flat.tolist() == [1, 2, 3, 4, 5, 0, 0, 0]
+    rng = np.random.default_rng(31)
+    for seed in range(10):
+        numels = [int(x) for x in rng.integers(0, 700, int(rng.integers(1, 6)))]
+        p = oracle.partition_plan(numels, int(rng.choice([1, 2, 3, 8])), int(rng.choice([1, 8, 128])))
+        tensors = [rng.integers(0, 1 << 16, n).astype(np.uint16) for n in numels]
+        flat = oracle.flatten_params(p, tensors)
+        assert (flat[p.numel:] == 0).all()
+        S = p.shard_numel
+        back = oracle.gather_params(p, [flat[r * S:(r + 1) * S] for r in range(p.n_ranks)])
+        for a, b in zip(back, tensors):
+            assert (a == b).all()

@@ -61,6 +61,7 @@ _adamw = _fn("zero_shard_adamw_step", c_i32,
              [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl, c_vp,
               c_vp])
 _gather = _fn("zero_gather_params", c_i32, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp])
+_flatten = _fn("zero_flatten_params", c_i32, [c_vp, ctypes.POINTER(c_vp), c_vp, c_vp])
 _status_string = _fn("zero_status_string", ctypes.c_char_p, [c_i32])
 _last_error = _fn("zero_last_error", ctypes.c_char_p, [])
 
@@ -241,6 +242,17 @@ def zero_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, stream=N
            "zero_gather_params")
 
 
+def zero_flatten_params(plan: Plan, tensors: Sequence, flat, stream=None) -> None:
+    """tensors: T device buffers (2-byte elements, numel_t each); flat: device [P]."""
+    if len(tensors) != plan.num_tensors:
+        raise ValueError("need T tensors")
+    if flat.numel() < plan.padded_numel:
+        raise ValueError("flat holds fewer than P elements")
+    tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
+    _check(_flatten(plan.handle, tp, _ptr(flat, 2, "flat"), _stream(stream, flat)),
+           "zero_flatten_params")
+
+
 def zero_status_string(status: int) -> str:
     return _status_string(status).decode()
 
@@ -311,4 +323,14 @@ def prepare_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, strea
     tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
     p = Prepared(_gather, [plan.handle, sp, tp, _stream(stream, shards[0])], "zero_gather_params")
     p._keep = (sp, tp, shards, tensors)
+    return p
+
+
+def prepare_flatten_params(plan: Plan, tensors: Sequence, flat, stream) -> Prepared:
+    if len(tensors) != plan.num_tensors or flat.numel() < plan.padded_numel:
+        raise ValueError("need T tensors and a flat buffer of P elements")
+    tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
+    p = Prepared(_flatten, [plan.handle, tp, _ptr(flat, 2, "flat"), _stream(stream, flat)],
+                 "zero_flatten_params")
+    p._keep = (tp, tensors, flat)
     return p

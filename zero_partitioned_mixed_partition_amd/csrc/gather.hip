@@ -1,4 +1,5 @@
-// Gather of bf16 parameter shards into per-tensor parameters (gfx950).
+// Gather of bf16 parameter shards into per-tensor parameters, and its inverse,
+// the flatten of per-tensor buffers into the padded flat buffer (gfx950).
 //
 // "Zero Redundancy Optimizer (ZeRO) and Fully Sharded Data Parallelism (FSDP):
 // Mathematical Foundations ...", section "Execution Flow for ZeRO-1", step 4:
@@ -58,8 +59,17 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
     const int s = lo;
     const int64_t start = (blk - b.first_block[s]) * kChunk;
     const int64_t len = b.len[s] - start < kChunk ? b.len[s] - start : kChunk;
-    const uint16_t* src = b.src[s] + start;
     uint16_t* dst = b.dst[s] + start;
+    if (b.src[s] == nullptr) {                        // padding: fill with +0
+        const int64_t i = threadIdx.x;
+        if (i * kLane + kLane <= len && (reinterpret_cast<uintptr_t>(dst) & (2 * kLane - 1)) == 0) {
+            zero::dev::st_stream(reinterpret_cast<V*>(dst) + i, V{});
+        } else {
+            for (int64_t e = i * kLane; e < len && e < i * kLane + kLane; ++e) dst[e] = 0;
+        }
+        return;
+    }
+    const uint16_t* src = b.src[s] + start;
     constexpr uintptr_t kBytes = 2 * kLane;
     const uintptr_t sa = reinterpret_cast<uintptr_t>(src), da = reinterpret_cast<uintptr_t>(dst);
     if (((sa ^ da) & (kBytes - 1)) == 0) {
@@ -81,49 +91,91 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
 
 }  // namespace
 
+namespace {
+
+// Launches one segment-copy kernel per kSegs segments. Each piece is
+// (src, dst, len); a NULL src fills dst with zeros.
+struct Piece {
+    const uint16_t* src;
+    uint16_t* dst;
+    int64_t len;
+};
+
+zero_status launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const char* who) {
+    SegBatch batch{};
+    auto flush = [&]() -> zero_status {
+        if (batch.n == 0) return ZERO_OK;
+        const int64_t blocks = batch.first_block[batch.n];
+        hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                           stream, batch);
+        batch.n = 0;
+        batch.first_block[0] = 0;
+        return zero::check_hip(hipGetLastError(), who);
+    };
+    for (const Piece& pc : pieces) {
+        if (pc.len <= 0) continue;
+        const int64_t chunks = (pc.len + kChunk - 1) / kChunk;
+        if (batch.first_block[batch.n] + chunks > 0x7FFFFFFF) {   // one grid < 2^31 workgroups
+            const zero_status st = flush();
+            if (st != ZERO_OK) return st;
+        }
+        if (chunks > 0x7FFFFFFF) return zero::fail(ZERO_ERANGE, std::string(who) + ": segment too long");
+        const int i = batch.n;
+        batch.src[i] = pc.src;
+        batch.dst[i] = pc.dst;
+        batch.len[i] = pc.len;
+        batch.first_block[i + 1] = batch.first_block[i] + chunks;
+        batch.n = i + 1;
+        if (batch.n == kSegs) {
+            const zero_status st = flush();
+            if (st != ZERO_OK) return st;
+        }
+    }
+    return flush();
+}
+
+zero_status check_tensors(const zero_plan* plan, const uint16_t* const* tensors, const char* who) {
+    if (!plan->numels.empty() && tensors == nullptr)
+        return zero::fail(ZERO_EINVAL, std::string(who) + ": NULL tensors");
+    for (size_t t = 0; t < plan->numels.size(); ++t)
+        if (plan->numels[t] > 0 && tensors[t] == nullptr)
+            return zero::fail(ZERO_EINVAL, std::string(who) + ": NULL tensor " + std::to_string(t));
+    return ZERO_OK;
+}
+
+}  // namespace
+
 extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* shards,
                                           uint16_t* const* tensors, hipStream_t stream) {
     using zero::fail;
     zero::clear_error();
     if (plan == nullptr || shards == nullptr)
         return fail(ZERO_EINVAL, "zero_gather_params: NULL plan or shards");
-    if (!plan->numels.empty() && tensors == nullptr)
-        return fail(ZERO_EINVAL, "zero_gather_params: NULL tensors");
+    zero_status st = check_tensors(plan, tensors, "zero_gather_params");
+    if (st != ZERO_OK) return st;
     for (int32_t r = 0; r < plan->n_ranks; ++r)
         if (plan->shard > 0 && shards[r] == nullptr)
             return fail(ZERO_EINVAL, "zero_gather_params: NULL shard " + std::to_string(r));
-    for (size_t t = 0; t < plan->numels.size(); ++t)
-        if (plan->numels[t] > 0 && tensors[t] == nullptr)
-            return fail(ZERO_EINVAL, "zero_gather_params: NULL tensor " + std::to_string(t));
+    std::vector<Piece> pieces;
+    pieces.reserve(plan->all.size());
+    for (const zero_segment& seg : plan->all)
+        pieces.push_back({shards[seg.rank] + seg.shard_offset, tensors[seg.tensor] + seg.tensor_offset,
+                          seg.length});
+    return launch_pieces(pieces, stream, "zero_gather_params launch");
+}
 
-    SegBatch batch{};
-    auto flush = [&]() -> zero_status {
-        if (batch.n == 0) return ZERO_OK;
-        const int64_t blocks = batch.first_block[batch.n];
-        if (blocks > 0x7FFFFFFF) return fail(ZERO_ERANGE, "zero_gather_params: grid too large");
-        hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                           stream, batch);
-        batch.n = 0;
-        batch.first_block[0] = 0;
-        return zero::check_hip(hipGetLastError(), "zero_gather_params launch");
-    };
-    for (const zero_segment& seg : plan->all) {
-        const int64_t chunks = (seg.length + kChunk - 1) / kChunk;
-        const int64_t next = batch.first_block[batch.n] + chunks;
-        if (next > 0x7FFFFFFF) {   // keep one launch's grid within 2^31 workgroups
-            zero_status st = flush();
-            if (st != ZERO_OK) return st;
-        }
-        const int i = batch.n;
-        batch.src[i] = shards[seg.rank] + seg.shard_offset;
-        batch.dst[i] = tensors[seg.tensor] + seg.tensor_offset;
-        batch.len[i] = seg.length;
-        batch.first_block[i + 1] = batch.first_block[i] + chunks;
-        batch.n = i + 1;
-        if (batch.n == kSegs) {
-            zero_status st = flush();
-            if (st != ZERO_OK) return st;
-        }
-    }
-    return flush();
+extern "C" zero_status zero_flatten_params(const zero_plan* plan, const uint16_t* const* tensors,
+                                           uint16_t* flat, hipStream_t stream) {
+    using zero::fail;
+    zero::clear_error();
+    if (plan == nullptr) return fail(ZERO_EINVAL, "zero_flatten_params: NULL plan");
+    if (plan->padded > 0 && flat == nullptr) return fail(ZERO_EINVAL, "zero_flatten_params: NULL flat");
+    zero_status st = check_tensors(plan, tensors, "zero_flatten_params");
+    if (st != ZERO_OK) return st;
+    std::vector<Piece> pieces;
+    pieces.reserve(plan->numels.size() + 1);
+    for (size_t t = 0; t < plan->numels.size(); ++t)
+        pieces.push_back({tensors[t], flat + plan->offsets[t], plan->numels[t]});
+    pieces.push_back({nullptr, flat + plan->numel, plan->padded - plan->numel});
+    return launch_pieces(pieces, stream, "zero_flatten_params launch");
 }
