@@ -78,7 +78,8 @@ class RankWorkload:
 
         import synth
         import zero_partitioned_mixed_partition_amd as zm
-        from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep, bucket_windows
+        from zero_partitioned_mixed_partition_amd.step import (Hyper, RankStep, bucket_windows,
+                                                               staggered_replicas)
 
         lst, nd, rank, reps, bucket, gather = self.SPECS[name]
         w = synth.WORKLOADS[lst]
@@ -106,21 +107,17 @@ class RankWorkload:
         # gradient inputs
         self.windows = []
         if reps and not bucket:
-            full = []
-            for k in range(reps):
-                t = torch.empty(P, dtype=torch.int16, device=device)
+            full = staggered_replicas(reps, P, device)
+            for k, t in enumerate(full):
                 synth.device_normal_bf16(t, self.seed, synth.KIND_REPLICA, 1, k, 0, phi,
                                          synth.GRAD_SIGMA)
-                full.append(t)
             self.windows = [(0, P, full)]
         elif reps:
             for b0, cnt in spans:
-                ws = []
-                for k in range(reps):
-                    t = torch.empty(cnt, dtype=torch.int16, device=device)
+                ws = staggered_replicas(reps, cnt, device)
+                for k, t in enumerate(ws):
                     synth.device_normal_bf16(t, self.seed, synth.KIND_REPLICA, 1, k, b0, phi,
                                              synth.GRAD_SIGMA)
-                    ws.append(t)
                 self.windows.append((b0, cnt, ws))
         else:
             synth.device_normal_bf16(rs.grad, self.seed, synth.KIND_GRAD, 1, 0, lo, phi,
@@ -184,7 +181,8 @@ class AllRanksWorkload:
         import synth
         import zero_partitioned_mixed_partition_amd as zm
         from zero_partitioned_mixed_partition_amd import _binding as zb
-        from zero_partitioned_mixed_partition_amd.step import Hyper, _staggered_arena, plan_numels
+        from zero_partitioned_mixed_partition_amd.step import (Hyper, _staggered_arena, plan_numels,
+                                                               staggered_replicas)
 
         w = synth.WORKLOADS[name]
         self.name, self.workload, self.device = name, w, device
@@ -201,11 +199,9 @@ class AllRanksWorkload:
         self.master, self.m, self.v, self.grad, self.param = views
         synth.device_normal_f32(self.master, self.seed, synth.KIND_MASTER, 0, 0, 0, phi,
                                 synth.MASTER_SIGMA)
-        self.reps = []
-        for k in range(self.replicas):
-            t = torch.empty(P, dtype=torch.int16, device=device)
+        self.reps = staggered_replicas(self.replicas, P, device)
+        for k, t in enumerate(self.reps):
             synth.device_normal_bf16(t, self.seed, synth.KIND_REPLICA, 1, k, 0, phi, synth.GRAD_SIGMA)
-            self.reps.append(t)
         self.tensors = [torch.empty(n, dtype=torch.int16, device=device)
                         for n in plan_numels(self.plan)]
         self.partials = torch.zeros(w.n_ranks, dtype=torch.float64, device=device)
@@ -272,20 +268,24 @@ def run_step(wl) -> None:
         fn()
 
 
-def time_phases(wl, steps: int):
-    """Mean duration (ms) per step of each phase, HIP events on the launch stream."""
+def time_phases(wl, reps: int):
+    """Mean duration (ms) of each phase on its own: the phase is issued `reps`
+    times back to back between two HIP events on the launch stream, so the
+    queue never drains between calls."""
     import torch
-    ev = {n: [] for n, _ in wl.phases}
-    for _ in range(steps):
-        for n, fn in wl.phases:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
+    out = {}
+    for n, fn in wl.phases:
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
             fn()
-            b.record()
-            ev[n].append((a, b))
-    torch.cuda.synchronize()
-    return {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in ev}
+        b.record()
+        torch.cuda.synchronize()
+        out[n] = a.elapsed_time(b) / reps
+    return out
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_traffic.json")
@@ -437,7 +437,7 @@ def main(argv=None):
     print(f"[bench] {steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s), "
           f"adamw {adamw_ms * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
 
-    phase_ms = time_phases(wl, max(3, min(steps, 100)))
+    phase_ms = time_phases(wl, max(3, min(steps, 50)))
     bpp = wl.bytes_per_phase()
 
     def rates(ms):

@@ -33,14 +33,21 @@ namespace {
 using zero::dev::u32x4;
 
 constexpr int kThreads = 256;
-// Grid cap, and so the number of workgroup partials the workspace holds. Below
-// it each thread handles one group of 8 elements; above it threads stride.
+// Grid caps (measured on MI355X: the replica reduce keeps more bytes in flight
+// per lane and does best with fewer, longer-lived workgroups than the one-read
+// squared norm), and so the number of workgroup partials the workspace holds.
+// Below the cap each thread handles one group of 8 elements; above it threads
+// stride.
 // The grid depends on n only, so the summation order (and the fp64 result)
 // is the same on every device.
 #ifndef ZERO_REDUCE_MAX_BLOCKS
-#define ZERO_REDUCE_MAX_BLOCKS 4096
+#define ZERO_REDUCE_MAX_BLOCKS 2048
 #endif
-constexpr int kMaxPartials = ZERO_REDUCE_MAX_BLOCKS;
+#ifndef ZERO_SQNORM_MAX_BLOCKS
+#define ZERO_SQNORM_MAX_BLOCKS 4096
+#endif
+constexpr int kMaxPartials = ZERO_REDUCE_MAX_BLOCKS > ZERO_SQNORM_MAX_BLOCKS
+                                 ? ZERO_REDUCE_MAX_BLOCKS : ZERO_SQNORM_MAX_BLOCKS;
 constexpr int kReplicaBatch = 8;             // replica loads in flight per thread
 
 struct ReplicaTable {
@@ -233,9 +240,9 @@ __global__ void clip_kernel(const double* __restrict__ partials, int n, double m
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int grid_for(int64_t work_items) {
+int grid_for(int64_t work_items, int cap) {
     int64_t blocks = (work_items + kThreads - 1) / kThreads;
-    if (blocks > kMaxPartials) blocks = kMaxPartials;
+    if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     return static_cast<int>(blocks);
 }
@@ -287,7 +294,7 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
     bool vec = aligned(out, 2 * kEpt);
     for (int32_t k = 0; k < n_replicas && vec; ++k) vec = aligned(replicas[k] + src_off, 2 * kEpt);
     const bool norm = sqnorm_out != nullptr;
-    const int blocks = grid_for(vec ? n / kEpt : n);
+    const int blocks = grid_for(vec ? n / kEpt : n, ZERO_REDUCE_MAX_BLOCKS);
     if (vec) {
         if (norm)
             hipLaunchKernelGGL(reduce_vec<true>, dim3(blocks), dim3(kThreads), 0, stream, table,
@@ -325,7 +332,7 @@ extern "C" zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double*
         return zero::check_hip(hipGetLastError(), "zero_grad_sqnorm launch");
     }
     const bool vec = aligned16(grad);
-    const int blocks = grid_for(vec ? n / 8 : n);
+    const int blocks = grid_for(vec ? n / 8 : n, ZERO_SQNORM_MAX_BLOCKS);
     if (vec)
         hipLaunchKernelGGL(sqnorm_vec, dim3(blocks), dim3(kThreads), 0, stream, grad, n, partials);
     else

