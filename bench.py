@@ -18,6 +18,9 @@ Other workloads (`--workload`), each timed as its own configuration states:
               AdamW on the 8,819,213,312-element shard
   gpt-1.3b    all 8 ranks of the 1.3B GPT list: 8 replicas reduced for every
               rank, AdamW on every shard, gather to 292 tensors
+  gpt2-small-fsdp2  the default step on FSDP-2's per-parameter Shard(0) layout
+              (every tensor cut along dim 0; a rank's chunks in one coalesced
+              buffer); the replicas are per-tensor gradients flattened into it
 
 All inputs are seeded synthetic data resident in HBM before timing starts. The
 other ranks' norm partials and parameter shards are inputs computed once,
@@ -39,7 +42,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 METRIC = "shard AdamW step: params/sec and achieved HBM GB/s (% of MI355X peak)"
-WORKLOAD_NAMES = ["gpt2-small", "llama3-8b", "llama3-70b", "gpt-1.3b"]
+WORKLOAD_NAMES = ["gpt2-small", "llama3-8b", "llama3-70b", "gpt-1.3b", "gpt2-small-fsdp2"]
 
 
 def parse_args(argv=None):
@@ -60,17 +63,19 @@ def parse_args(argv=None):
 
 
 DEFAULT_STEPS = {"gpt2-small": (200, 20), "llama3-8b": (20, 3), "llama3-70b": (5, 1),
-                 "gpt-1.3b": (10, 2)}
+                 "gpt-1.3b": (10, 2), "gpt2-small-fsdp2": (200, 20)}
 
 
 class RankWorkload:
     """One rank's step: reduce (or plain squared norm), clip, AdamW, optional gather."""
 
     SPECS = {
-        # name: tensor list, N_d, rank, replicas (0: gradients arrive averaged), bucket, gather
-        "gpt2-small": ("gpt2-small", 8, 7, 8, 0, True),
-        "llama3-8b": ("llama3-8b", 64, 63, 64, 25_000_000, False),
-        "llama3-70b": ("llama3-70b", 8, 7, 0, 0, False),
+        # name: tensor list, N_d, rank, replicas (0: gradients arrive averaged), bucket, gather,
+        # layout (flat: FSDP-1 / ZeRO; shard0: FSDP-2 per-parameter)
+        "gpt2-small": ("gpt2-small", 8, 7, 8, 0, True, "flat"),
+        "llama3-8b": ("llama3-8b", 64, 63, 64, 25_000_000, False, "flat"),
+        "llama3-70b": ("llama3-70b", 8, 7, 0, 0, False, "flat"),
+        "gpt2-small-fsdp2": ("gpt2-small", 8, 7, 8, 0, True, "shard0"),
     }
 
     def __init__(self, name: str, device):
@@ -81,13 +86,17 @@ class RankWorkload:
         from zero_partitioned_mixed_partition_amd.step import (Hyper, RankStep, bucket_windows,
                                                                staggered_replicas)
 
-        lst, nd, rank, reps, bucket, gather = self.SPECS[name]
+        lst, nd, rank, reps, bucket, gather, layout = self.SPECS[name]
         w = synth.WORKLOADS[lst]
-        self.name, self.workload, self.device = name, w, device
+        self.name, self.workload, self.device, self.layout = name, w, device, layout
         self.n_ranks, self.rank, self.replicas, self.bucket = nd, rank, reps, bucket
         self.max_norm = w.max_norm if w.max_norm > 0 else 1.0
         self.seed = 1000 + w.seed
-        self.plan = zm.zero_partition_plan(w.numels, nd, w.align)
+        if layout == "shard0":
+            self.plan = zm.zero_partition_plan_shard0(w.numels, [s[0] for s in w.shapes], nd,
+                                                      w.align)
+        else:
+            self.plan = zm.zero_partition_plan(w.numels, nd, w.align)
         P, S, phi = self.plan.padded_numel, self.plan.shard_numel, self.plan.numel
         self.P, self.S, self.phi = P, S, phi
         lo = rank * S
@@ -97,8 +106,10 @@ class RankWorkload:
         self.rs = RankStep(self.plan, rank, len(spans), self.hyper, self.max_norm, device,
                            gather=gather)
         rs = self.rs
-        synth.device_normal_f32(rs.master, self.seed, synth.KIND_MASTER, 0, 0, lo, phi,
-                                synth.MASTER_SIGMA)
+        synth.device_normal_f32(rs.master, self.seed, synth.KIND_MASTER, 0, 0, lo,
+                                phi if layout == "flat" else P, synth.MASTER_SIGMA)
+        if layout == "shard0":       # padding inside the coalesced buffer starts at zero
+            rs.master.mul_(padding_mask(self.plan, rank).to(device))
         if gather:
             for r in range(nd):
                 if r != rank:
@@ -106,7 +117,21 @@ class RankWorkload:
                                              r * S, phi, synth.MASTER_SIGMA)
         # gradient inputs
         self.windows = []
-        if reps and not bucket:
+        if reps and not bucket and layout == "shard0":
+            # each replica's per-tensor gradients, flattened into the coalesced layout
+            full = staggered_replicas(reps, P, device)
+            offs = model_offsets(w.numels)
+            for k, t in enumerate(full):
+                per_tensor = []
+                for n, off in zip(w.numels, offs):
+                    g = torch.empty(n, dtype=torch.int16, device=device)
+                    synth.device_normal_bf16(g, self.seed, synth.KIND_REPLICA, 1, k, off, phi,
+                                             synth.GRAD_SIGMA)
+                    per_tensor.append(g)
+                zm.zero_flatten_params(self.plan, per_tensor, t)
+                del per_tensor
+            self.windows = [(0, P, full)]
+        elif reps and not bucket:
             full = staggered_replicas(reps, P, device)
             for k, t in enumerate(full):
                 synth.device_normal_bf16(t, self.seed, synth.KIND_REPLICA, 1, k, 0, phi,
@@ -168,8 +193,10 @@ class RankWorkload:
                (f" in {len(self.windows)} buckets of {self.bucket}" if self.bucket else "")
                if self.replicas else "squared norm of the averaged bf16 gradient")
         g = f" + gather of {len(self.workload.numels)} tensors" if self.rs.tensors else ""
-        return (f"{self.workload.name} tensor list, N_d={self.n_ranks}, rank {self.rank} shard of "
-                f"{self.S} elements; step = {red} + clip {self.max_norm} + AdamW{g}")
+        lay = (", FSDP-2 per-parameter Shard(0) layout (coalesced per-rank buffers)"
+               if self.layout == "shard0" else "")
+        return (f"{self.workload.name} tensor list{lay}, N_d={self.n_ranks}, rank {self.rank} shard "
+                f"of {self.S} elements; step = {red} + clip {self.max_norm} + AdamW{g}")
 
 
 class AllRanksWorkload:
@@ -257,6 +284,25 @@ class AllRanksWorkload:
         return (f"{self.workload.name} tensor list, N_d={self.n_ranks}, all {self.n_ranks} ranks in "
                 f"turn ({self.S} elements each); step = reduce of {self.replicas} bf16 replicas per "
                 f"rank + AdamW per shard + gather of {len(self.workload.numels)} tensors")
+
+
+def model_offsets(numels):
+    """Each tensor's start in the model's natural (definition-order) concatenation:
+    the generator keys a tensor's values by these, whatever the sharding layout."""
+    offs, pos = [], 0
+    for n in numels:
+        offs.append(pos)
+        pos += n
+    return offs
+
+
+def padding_mask(plan, rank: int):
+    """float32 [S]: 1 where the rank's buffer holds tensor elements, 0 on padding."""
+    import torch
+    mask = torch.zeros(plan.shard_numel, dtype=torch.float32)
+    for (_, _, soff, ln) in plan.segments(rank):
+        mask[soff:soff + ln] = 1.0
+    return mask
 
 
 def make_workload(name: str, device):

@@ -99,12 +99,40 @@ zero_status zero_partition_plan(const int64_t* numels, int32_t n_tensors, int32_
                                 int32_t align_elems, zero_plan** out);
 void zero_plan_free(zero_plan* plan);                       /* accepts NULL */
 
+/* FSDP-2 per-parameter layout. [ZF] "FSDP-2: Per-Parameter Sharding via
+ * DTensor (fully_shard)": each tensor is sharded on its own along its leading
+ * dimension (a Shard(0) placement) instead of being flattened with the others,
+ * and the shards of one unit travel in a coalesced communication buffer.
+ *
+ * Tensor t (numels[t] elements, dim0[t] >= 1 rows of inner_t = numels[t]/dim0[t]
+ * elements; dim0[t] must divide numels[t]; a zero-sized tensor may give 0)
+ * is cut into N_d chunks of c_t = ceil(dim0[t] / N_d) rows, as torch.chunk
+ * cuts it: rank r holds rows [r*c_t, min((r+1)*c_t, dim0[t])), possibly none.
+ * A rank's coalesced buffer holds its chunk of every tensor in order, each
+ * padded to c_t*inner_t elements, the whole padded to a multiple of
+ * align_elems: S = that length. The N_d coalesced buffers side by side form
+ * the plan's flat buffer of P = N_d*S elements, so zero_grad_reduce_shard,
+ * zero_shard_adamw_step, zero_gather_params and zero_flatten_params apply
+ * unchanged; padding positions hold zeros. zero_plan_tensor_offset(t) gives
+ * the start of tensor t's chunk inside every rank's buffer.
+ * Errors as zero_partition_plan, plus ZERO_EINVAL when dim0 does not divide
+ * a numel. */
+zero_status zero_partition_plan_shard0(const int64_t* numels, const int64_t* dim0,
+                                       int32_t n_tensors, int32_t n_ranks, int32_t align_elems,
+                                       zero_plan** out);
+
+/* 0 for a flat (FSDP-1 / ZeRO) plan, 1 for a Shard(0) plan, -1 for NULL. */
+int32_t zero_plan_kind(const zero_plan* plan);
+
 int64_t zero_plan_numel(const zero_plan* plan);             /* Phi, or -1 if plan is NULL */
 int64_t zero_plan_padded_numel(const zero_plan* plan);      /* P,   or -1 */
 int64_t zero_plan_shard_numel(const zero_plan* plan);       /* S,   or -1 */
 int32_t zero_plan_num_tensors(const zero_plan* plan);       /* T,   or -1 */
 int32_t zero_plan_num_ranks(const zero_plan* plan);         /* N_d, or -1 */
-int64_t zero_plan_tensor_offset(const zero_plan* plan, int32_t tensor);  /* -1 if out of range */
+int64_t zero_plan_tensor_offset(const zero_plan* plan, int32_t tensor);  /* -1 if out of range;
+                                                                           flat plans: the tensor's
+                                                                           flat start */
+int64_t zero_plan_tensor_numel(const zero_plan* plan, int32_t tensor);   /* -1 if out of range */
 int32_t zero_plan_num_segments(const zero_plan* plan, int32_t rank);     /* -1 if out of range */
 
 /* Copies rank's segments, in flat order, into host array out[capacity].
@@ -229,9 +257,11 @@ zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* sha
  *
  * [ZF] "FSDP-1: FlatParameter and Module-Level Wrapping": a unit's tensors are
  * flattened into one contiguous 1-D buffer, padded to a length divisible by
- * the world size. This builds that buffer from per-tensor bf16 buffers: tensor
- * t lands at flat elements [offset_t, offset_t + numel_t) and the padding
- * [Phi, P) is set to +0. It is the inverse of zero_gather_params and the step
+ * the world size. This builds that buffer from per-tensor bf16 buffers: every
+ * plan segment is copied from its tensor to its place in the flat buffer
+ * (flat plans: tensor t at [offset_t, offset_t + numel_t); Shard(0) plans:
+ * each rank's chunk into that rank's coalesced buffer) and every other
+ * position is set to +0. It is the inverse of zero_gather_params and the step
  * before zero_grad_reduce_shard: each data-parallel replica flattens its
  * per-tensor gradients into the flat buffer that the reduce-scatter cuts into
  * N_d shards.

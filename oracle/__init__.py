@@ -23,6 +23,7 @@ Pinning status (what each function is checked against, outside itself):
               shard invariance
   gather.py   flatten/gather round trip
   flatten.py  gather(flatten(x)) = x, padding zero, hand-worked case
+  Shard(0)    torch.chunk's row cut, round trips, hand-worked case
 The fp32 evaluation order inside AdamW and the clip's 1e-6 guard are readings
 (the pages do not write the update out); they are pinned by the closed forms
 and the torch cross-check within tolerance, not bit for bit by the pages.
@@ -30,9 +31,9 @@ and the torch cross-check within tolerance, not bit for bit by the pages.
 from .adamw import AdamWConstants, adamw_constants, adamw_step  # noqa: F401
 from .bf16 import bf16_to_f32, f32_to_bf16  # noqa: F401
 from .clip import clip_scale  # noqa: F401
-from .flatten import flatten_params  # noqa: F401
-from .gather import gather_params  # noqa: F401
-from .plan import Plan, memory_bytes, partition_plan  # noqa: F401
+from .flatten import flatten_params, flatten_params_shard0  # noqa: F401
+from .gather import gather_params, gather_params_shard0  # noqa: F401
+from .plan import Plan, Shard0Plan, memory_bytes, partition_plan, partition_plan_shard0  # noqa: F401
 from .reduce import reduce_shard  # noqa: F401
 from .sqnorm import SqnormAccumulator, sqnorm, sqnorm_fsum  # noqa: F401
 from .step import rank_step  # noqa: F401

@@ -19,3 +19,19 @@ def gather_params(plan: Plan, shards: Sequence[np.ndarray]) -> List[np.ndarray]:
     flat = np.concatenate([np.asarray(s, dtype=np.uint16) for s in shards]) if shards else \
         np.zeros(0, dtype=np.uint16)
     return [flat[off:off + n].copy() for off, n in zip(plan.offsets, plan.numels)]
+
+
+def gather_params_shard0(plan, shards: Sequence[np.ndarray]) -> List[np.ndarray]:
+    """FSDP-2 all-gather output: tensor t is its rank chunks' rows stacked in
+    rank order ([ZF] "FSDP-2: Per-Parameter Sharding via DTensor")."""
+    if len(shards) != plan.n_ranks or any(len(s) != plan.shard_numel for s in shards):
+        raise ValueError("need N_d shards of S elements each")
+    out = []
+    for t, (off, n) in enumerate(zip(plan.offsets, plan.numels)):
+        pieces = []
+        for r in range(plan.n_ranks):
+            rows = min(plan.chunk_rows[t], plan.dim0[t] - r * plan.chunk_rows[t]) if n else 0
+            if rows > 0:
+                pieces.append(np.asarray(shards[r][off:off + rows * plan.inner[t]], np.uint16))
+        out.append(np.concatenate(pieces) if pieces else np.zeros(0, np.uint16))
+    return out

@@ -74,3 +74,54 @@ def memory_bytes(plan: Plan, stage: int, padded: bool = False) -> float:
     if stage not in table:
         raise ValueError("stage must be 0, 1, 2 or 3")
     return float(table[stage])
+
+
+@dataclass
+class Shard0Plan(Plan):
+    """FSDP-2 per-parameter layout.
+
+    [ZF] "FSDP-2: Per-Parameter Sharding via DTensor (fully_shard)": each tensor
+    is sharded on its own along its leading dimension (a Shard(0) placement),
+    not flattened with the others; one rank's shards travel in a coalesced
+    buffer. Reading taken: torch.chunk's cut, ceil(dim0 / N_d) rows per chunk,
+    rank r holding rows [r*c, min((r+1)*c, dim0)) (possibly none); in a rank's
+    buffer the chunks follow tensor order, each padded to c*inner elements, the
+    buffer padded to a multiple of A. `offsets` are the chunk starts inside a
+    rank's buffer; the flat buffer is the N_d rank buffers side by side.
+    """
+    dim0: List[int] = None
+    chunk_rows: List[int] = None
+    inner: List[int] = None
+
+    def segments(self, rank: int) -> List[Segment]:
+        if not 0 <= rank < self.n_ranks:
+            raise ValueError("rank out of range")
+        out = []
+        for t, (off, n) in enumerate(zip(self.offsets, self.numels)):
+            if n == 0:
+                continue
+            first = rank * self.chunk_rows[t]
+            rows = min(self.chunk_rows[t], self.dim0[t] - first)
+            if rows > 0:
+                out.append((t, first * self.inner[t], off, rows * self.inner[t]))
+        return out
+
+
+def partition_plan_shard0(numels, dim0, n_ranks: int, align: int = 128) -> Shard0Plan:
+    numels = [int(n) for n in numels]
+    dim0 = [int(d) for d in dim0]
+    if n_ranks < 1 or align < 1 or len(numels) != len(dim0):
+        raise ValueError("invalid plan arguments")
+    offsets, rows_l, inner_l, buf = [], [], [], 0
+    for n, d in zip(numels, dim0):
+        if n < 0 or (n > 0 and (d < 1 or n % d)):
+            raise ValueError("dim0 must be >= 1 and divide numel")
+        inner = n // d if n else 0
+        rows = -(-d // n_ranks) if n else 0
+        offsets.append(buf)
+        rows_l.append(rows)
+        inner_l.append(inner)
+        buf += rows * inner
+    s = -(-buf // align) * align
+    return Shard0Plan(numels, n_ranks, align, offsets, sum(numels), s * n_ranks, s,
+                      dim0=dim0, chunk_rows=rows_l, inner=inner_l)

@@ -13,8 +13,8 @@ import numpy as np
 
 from .adamw import adamw_step
 from .clip import clip_scale
-from .gather import gather_params
-from .plan import Plan
+from .gather import gather_params, gather_params_shard0
+from .plan import Plan, Shard0Plan
 from .reduce import reduce_shard
 from .sqnorm import sqnorm
 
@@ -37,5 +37,6 @@ def rank_step(plan: Plan, rank: int, replicas: Sequence[np.ndarray], begin: int,
     state["master"], state["exp_avg"], state["exp_avg_sq"] = p, m, v
     if bits is not None:
         param_shards[rank] = bits
-    tensors = gather_params(plan, param_shards)
+    gather = gather_params_shard0 if isinstance(plan, Shard0Plan) else gather_params
+    tensors = gather(plan, param_shards)
     return {"shard_grad": shard_grad, "partials": parts, "clip": clip, "tensors": tensors}

@@ -120,3 +120,46 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu(zm):
     assert st == zm._binding.ZERO_EINVAL
     assert zm.zero_status_string(zm._binding.ZERO_ENOSPACE).startswith("workspace")
     assert zm.zero_sqnorm_workspace_bytes() >= 8
+
+
+@pytest.mark.parametrize("name,n_ranks", [("gpt2-small", 8), ("llama3-8b", 64), ("tiny-a", 4),
+                                          ("gpt-1.3b", 3)])
+def test_shard0_plan_matches_oracle_on_workloads(zm, name, n_ranks):
+    shapes = synth.WORKLOADS[name].shapes
+    numels = [int(np.prod(s)) for s in shapes]
+    dim0 = [s[0] for s in shapes]
+    ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, 128)
+    plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, 128)
+    assert plan.kind == 1
+    assert (plan.numel, plan.padded_numel, plan.shard_numel) == (
+        ref.numel, ref.padded_numel, ref.shard_numel)
+    assert [plan.tensor_offset(t) for t in range(len(numels))] == ref.offsets
+    assert [plan.tensor_numel(t) for t in range(len(numels))] == numels
+    for r in range(n_ranks):
+        assert plan.segments(r) == ref.segments(r), (name, r)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_shard0_plan_matches_oracle_random(zm, seed):
+    rng = np.random.default_rng(700 + seed)
+    t = int(rng.integers(0, 8))
+    dim0 = [int(x) for x in rng.integers(1, 50, t)]
+    numels = [d * int(k) for d, k in zip(dim0, rng.integers(1, 20, t))]
+    if t and seed % 4 == 0:
+        numels[0], dim0[0] = 0, 0
+    n_ranks = int(rng.choice([1, 2, 3, 8, 64]))
+    align = int(rng.choice([1, 8, 128]))
+    ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, align)
+    plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, align)
+    assert (plan.numel, plan.padded_numel, plan.shard_numel) == (
+        ref.numel, ref.padded_numel, ref.shard_numel)
+    for r in range(n_ranks):
+        assert plan.segments(r) == ref.segments(r)
+
+
+def test_shard0_plan_errors(zm):
+    with pytest.raises(zm.ZeroError):
+        zm.zero_partition_plan_shard0([10], [3], 2, 1)      # dim0 does not divide numel
+    with pytest.raises(zm.ZeroError):
+        zm.zero_partition_plan_shard0([10], [0], 2, 1)
+    assert zm.zero_partition_plan([4], 2, 1).kind == 0

@@ -312,3 +312,32 @@ def test_flatten_workload_plans_and_gather_round_trip(zm):
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(outs, host)):
             assert_bits_equal(host_u16(a), b, f"{name} round trip tensor {i}")
+
+
+# ----------------------------------------------------------------------------- FSDP-2 Shard(0)
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shard0_gather_and_flatten(zm, seed):
+    rng = np.random.default_rng(800 + seed)
+    t = int(rng.integers(1, 8))
+    dim0 = [int(x) for x in rng.integers(1, 3000, t)]
+    dim0[0] = int(rng.integers(1, 4))                     # fewer rows than ranks
+    numels = [d * int(k) for d, k in zip(dim0, rng.integers(1, 40, t))]
+    n_ranks = int(rng.choice([2, 3, 4, 8]))
+    align = int(rng.choice([1, 8, 128]))
+    note(f"shard0 dim0={dim0} numels={numels} N_d={n_ranks} A={align}")
+    ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, align)
+    plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, align)
+    tensors = [rng.integers(0, 1 << 16, n).astype(np.uint16) for n in numels]
+    flat = to_dev_u16(np.full(ref.padded_numel, 0x7777, np.uint16))
+    zm.zero_flatten_params(plan, [to_dev_u16(x) for x in tensors], flat)
+    torch.cuda.synchronize()
+    want = oracle.flatten_params_shard0(ref, tensors)
+    assert_bits_equal(host_u16(flat), want, "coalesced buffers")
+    S = ref.shard_numel
+    shards = [rng.integers(0, 1 << 16, S).astype(np.uint16) for _ in range(n_ranks)]
+    outs = [torch.full((n,), 0x1357, dtype=torch.int16, device=dev()) for n in numels]
+    zm.zero_gather_params(plan, [to_dev_u16(x) for x in shards], outs)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(outs, oracle.gather_params_shard0(ref, shards))):
+        assert_bits_equal(host_u16(a), b, f"tensor {i}")

@@ -135,28 +135,46 @@ def test_gpt2_small_rank7_hundred_steps_clip(zm):
         assert_bf16_close(host_u16(d_param[sl]), bits, f"param window {w0}")
 
 
-def test_bench_pipeline_matches_oracle(zm):
+@pytest.mark.parametrize("name", ["gpt2-small", "gpt2-small-fsdp2"])
+def test_bench_pipeline_matches_oracle(zm, name):
     import bench
-    setup = bench.make_workload("gpt2-small", dev())
+    setup = bench.make_workload(name, dev())
     P, S, phi, rank, R = setup.P, setup.S, setup.phi, setup.rank, setup.replicas
-    ref = oracle.partition_plan(setup.workload.numels, setup.n_ranks, setup.workload.align)
-    note(f"bench pipeline: reduce of {R} replicas for rank {rank} of {setup.n_ranks}, S={S}")
+    w = setup.workload
+    shard0 = setup.layout == "shard0"
+    if shard0:
+        ref = oracle.partition_plan_shard0(w.numels, [s[0] for s in w.shapes], setup.n_ranks, w.align)
+    else:
+        ref = oracle.partition_plan(w.numels, setup.n_ranks, w.align)
+    note(f"bench pipeline {name}: reduce of {R} replicas for rank {rank} of {setup.n_ranks}, S={S}")
     steps = 2
     for _ in range(steps):
         bench.run_step(setup)
     torch.cuda.synchronize()
 
     # oracle: every rank's reduced gradient (for the partials), then rank 7's steps
-    reps = [synth.normal_bf16(P, setup.seed, synth.KIND_REPLICA, 1, k, 0, phi, synth.GRAD_SIGMA)
-            for k in range(R)]
+    if shard0:
+        offs = bench.model_offsets(w.numels)
+        reps = [oracle.flatten_params_shard0(ref, [
+            synth.normal_bf16(n, setup.seed, synth.KIND_REPLICA, 1, k, off, phi, synth.GRAD_SIGMA)
+            for n, off in zip(w.numels, offs)]) for k in range(R)]
+    else:
+        reps = [synth.normal_bf16(P, setup.seed, synth.KIND_REPLICA, 1, k, 0, phi,
+                                  synth.GRAD_SIGMA) for k in range(R)]
     partials = []
     for r in range(setup.n_ranks):
         g = np.zeros(S, np.uint16)
         oracle.reduce_shard(ref, r, reps, 0, g)
         partials.append(oracle.sqnorm(g))
-    state = {"master": synth.normal_f32(S, setup.seed, synth.KIND_MASTER, 0, 0, rank * S, phi,
-                                        synth.MASTER_SIGMA),
-             "exp_avg": np.zeros(S, np.float32), "exp_avg_sq": np.zeros(S, np.float32)}
+    master = synth.normal_f32(S, setup.seed, synth.KIND_MASTER, 0, 0, rank * S, P if shard0 else phi,
+                              synth.MASTER_SIGMA)
+    if shard0:
+        mask = np.zeros(S, bool)
+        for (_, _, soff, ln) in ref.segments(rank):
+            mask[soff:soff + ln] = True
+        master[~mask] = 0.0
+    state = {"master": master, "exp_avg": np.zeros(S, np.float32),
+             "exp_avg_sq": np.zeros(S, np.float32)}
     shards = [synth.normal_bf16(S, setup.seed, synth.KIND_PARAM, 0, 0, r * S, phi, synth.MASTER_SIGMA)
               if r != rank else np.zeros(S, np.uint16) for r in range(setup.n_ranks)]
     out = None
@@ -174,6 +192,9 @@ def test_bench_pipeline_matches_oracle(zm):
     assert abs(int(got_scale.view(np.int32)) - int(np.float32(out["clip"]).view(np.int32))) <= 1
     for got, key in ((setup.rs.master, "master"), (setup.rs.exp_avg, "exp_avg"),
                      (setup.rs.exp_avg_sq, "exp_avg_sq")):
-        assert_f32_close(host_f32(got), state[key], key)
+        exact = assert_f32_close(host_f32(got), state[key], key)
+        note(f"bench pipeline {name}: {key} bit-identical fraction {exact:.6f}")
+    if shard0:
+        assert (host_f32(setup.rs.master)[~mask] == 0).all(), "padding stays zero"
     for i, (a, b) in enumerate(zip(setup.rs.tensors, out["tensors"])):
         assert_bf16_close(host_u16(a), b, f"gathered tensor {i}")

@@ -3,6 +3,7 @@
 The entry points mirror the C ABI in include/zero_mi355x.h one for one:
 
     zero_partition_plan     flat padded buffer -> N_d equal shards (host)
+    zero_partition_plan_shard0  FSDP-2 per-parameter Shard(0) layout (host)
     zero_grad_reduce_shard  a rank's averaged gradient slice from R replicas
     zero_grad_sqnorm        fp64 squared-norm partial of a bf16 gradient
     zero_clip_scale         global-norm clip coefficient (device scalar)
@@ -18,4 +19,5 @@ from ._binding import (LIB_PATH, ZERO_MAX_REPLICAS, Plan, ZeroError,  # noqa: F4
                        sqnorm_workspace, zero_clip_scale, zero_flatten_params, zero_gather_params,
                        zero_grad_reduce_shard,
                        zero_grad_sqnorm, zero_last_error, zero_partition_plan,
+                       zero_partition_plan_shard0,
                        zero_shard_adamw_step, zero_sqnorm_workspace_bytes, zero_status_string)

@@ -41,6 +41,11 @@ def _fn(name, restype, argtypes):
 
 _partition_plan = _fn("zero_partition_plan", c_i32,
                       [ctypes.POINTER(c_i64), c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)])
+_plan_shard0 = _fn("zero_partition_plan_shard0", c_i32,
+                   [ctypes.POINTER(c_i64), ctypes.POINTER(c_i64), c_i32, c_i32, c_i32,
+                    ctypes.POINTER(c_vp)])
+_plan_kind = _fn("zero_plan_kind", c_i32, [c_vp])
+_plan_tnumel = _fn("zero_plan_tensor_numel", c_i64, [c_vp, c_i32])
 _plan_free = _fn("zero_plan_free", None, [c_vp])
 _plan_numel = _fn("zero_plan_numel", c_i64, [c_vp])
 _plan_padded = _fn("zero_plan_padded_numel", c_i64, [c_vp])
@@ -116,8 +121,16 @@ class Plan:
     def num_ranks(self) -> int:
         return _plan_nranks(self._h)
 
+    @property
+    def kind(self) -> int:
+        """0: flat (FSDP-1 / ZeRO) layout; 1: FSDP-2 per-parameter Shard(0) layout."""
+        return _plan_kind(self._h)
+
     def tensor_offset(self, t: int) -> int:
         return _plan_offset(self._h, t)
+
+    def tensor_numel(self, t: int) -> int:
+        return _plan_tnumel(self._h, t)
 
     def num_segments(self, rank: int) -> int:
         return _plan_nsegs(self._h, rank)
@@ -137,6 +150,19 @@ class Plan:
         _check(_plan_memory(self._h, stage, int(padded), ctypes.byref(out)),
                "zero_plan_memory_bytes")
         return out.value
+
+
+def zero_partition_plan_shard0(numels: Sequence[int], dim0: Sequence[int], n_ranks: int,
+                               align_elems: int = 128) -> Plan:
+    n = len(numels)
+    if len(dim0) != n:
+        raise ValueError("one dim0 per tensor")
+    arr = (c_i64 * max(n, 1))(*[int(x) for x in numels])
+    d0 = (c_i64 * max(n, 1))(*[int(x) for x in dim0])
+    h = c_vp(None)
+    _check(_plan_shard0(arr, d0, n, n_ranks, align_elems, ctypes.byref(h)),
+           "zero_partition_plan_shard0")
+    return Plan(h.value)
 
 
 def zero_partition_plan(numels: Sequence[int], n_ranks: int, align_elems: int = 128) -> Plan:

@@ -172,10 +172,17 @@ extern "C" zero_status zero_flatten_params(const zero_plan* plan, const uint16_t
     if (plan->padded > 0 && flat == nullptr) return fail(ZERO_EINVAL, "zero_flatten_params: NULL flat");
     zero_status st = check_tensors(plan, tensors, "zero_flatten_params");
     if (st != ZERO_OK) return st;
+    // Every segment, in flat order, copied to its place; every gap between
+    // segments (and after the last) filled with zeros.
     std::vector<Piece> pieces;
-    pieces.reserve(plan->numels.size() + 1);
-    for (size_t t = 0; t < plan->numels.size(); ++t)
-        pieces.push_back({tensors[t], flat + plan->offsets[t], plan->numels[t]});
-    pieces.push_back({nullptr, flat + plan->numel, plan->padded - plan->numel});
+    pieces.reserve(2 * plan->all.size() + 1);
+    int64_t pos = 0;
+    for (const zero_segment& seg : plan->all) {
+        const int64_t at = static_cast<int64_t>(seg.rank) * plan->shard + seg.shard_offset;
+        if (at > pos) pieces.push_back({nullptr, flat + pos, at - pos});
+        pieces.push_back({tensors[seg.tensor] + seg.tensor_offset, flat + at, seg.length});
+        pos = at + seg.length;
+    }
+    if (plan->padded > pos) pieces.push_back({nullptr, flat + pos, plan->padded - pos});
     return launch_pieces(pieces, stream, "zero_flatten_params launch");
 }

@@ -8,13 +8,14 @@
 #include "zero_mi355x.h"
 
 struct zero_plan {
+    int32_t kind = 0;     // ZERO_PLAN_FLAT or ZERO_PLAN_SHARD0
     int32_t n_ranks = 0;
     int32_t align = 0;
     int64_t numel = 0;    // Phi
-    int64_t padded = 0;   // P
+    int64_t padded = 0;   // P (flat: padded flat length; Shard(0): N_d * S)
     int64_t shard = 0;    // S
     std::vector<int64_t> numels;
-    std::vector<int64_t> offsets;
+    std::vector<int64_t> offsets;   // flat: tensor start; Shard(0): chunk start within a shard
     std::vector<std::vector<zero_segment>> by_rank;   // segments of each rank, flat order
     std::vector<zero_segment> all;                    // every segment, flat order
 };

@@ -1,4 +1,5 @@
-// Flat-buffer partition plan (host only).
+// Partition plans (host only): the flat FSDP-1 / ZeRO layout, and FSDP-2's
+// per-parameter Shard(0) layout further below.
 //
 // "Zero Redundancy Optimizer (ZeRO) and Fully Sharded Data Parallelism (FSDP):
 // Mathematical Foundations ...", section "FSDP-1: FlatParameter and
@@ -91,6 +92,87 @@ extern "C" zero_status zero_partition_plan(const int64_t* numels, int32_t n_tens
     return ZERO_OK;
 }
 
+// FSDP-2 Shard(0): "Zero Redundancy Optimizer (ZeRO) and Fully Sharded Data
+// Parallelism (FSDP): Mathematical Foundations ...", section "FSDP-2:
+// Per-Parameter Sharding via DTensor (fully_shard)": every tensor is sharded on
+// its own along dim 0; one rank's shards share a coalesced buffer. Chunks of
+// ceil(dim0 / N_d) rows, as torch.chunk cuts them; each padded to full size.
+extern "C" zero_status zero_partition_plan_shard0(const int64_t* numels, const int64_t* dim0,
+                                                  int32_t n_tensors, int32_t n_ranks,
+                                                  int32_t align_elems, zero_plan** out) {
+    clear_error();
+    if (out == nullptr) return fail(ZERO_EINVAL, "zero_partition_plan_shard0: out is NULL");
+    *out = nullptr;
+    if (n_tensors < 0) return fail(ZERO_EINVAL, "zero_partition_plan_shard0: n_tensors < 0");
+    if (n_tensors > 0 && (numels == nullptr || dim0 == nullptr))
+        return fail(ZERO_EINVAL, "zero_partition_plan_shard0: numels or dim0 is NULL");
+    if (n_ranks < 1) return fail(ZERO_EINVAL, "zero_partition_plan_shard0: n_ranks < 1");
+    if (align_elems < 1) return fail(ZERO_EINVAL, "zero_partition_plan_shard0: align_elems < 1");
+    zero_plan* plan = new (std::nothrow) zero_plan;
+    if (plan == nullptr) return fail(ZERO_ENOMEM, "zero_partition_plan_shard0: allocation failed");
+    try {
+        plan->kind = 1;
+        plan->n_ranks = n_ranks;
+        plan->align = align_elems;
+        plan->numels.assign(numels, numels + n_tensors);
+        plan->offsets.resize(static_cast<size_t>(n_tensors));
+        std::vector<int64_t> chunk_rows(static_cast<size_t>(n_tensors)), inner(chunk_rows.size());
+        int64_t total = 0, buf = 0;
+        for (int32_t t = 0; t < n_tensors; ++t) {
+            const int64_t n = numels[t], d0 = dim0[t];
+            if (n < 0 || d0 < 0 || (n > 0 && (d0 == 0 || n % d0 != 0))) {
+                delete plan;
+                return fail(ZERO_EINVAL, "zero_partition_plan_shard0: tensor " + std::to_string(t) +
+                                             ": dim0 must be >= 1 and divide numel");
+            }
+            const int64_t in = n > 0 ? n / d0 : 0;
+            const int64_t rows = n > 0 ? (d0 + n_ranks - 1) / n_ranks : 0;
+            if (n > INT64_MAX - total || (in > 0 && rows > (INT64_MAX - buf) / in)) {
+                delete plan;
+                return fail(ZERO_ERANGE, "zero_partition_plan_shard0: sizes overflow int64");
+            }
+            total += n;
+            chunk_rows[static_cast<size_t>(t)] = rows;
+            inner[static_cast<size_t>(t)] = in;
+            plan->offsets[static_cast<size_t>(t)] = buf;
+            buf += rows * in;
+        }
+        const int64_t s = (buf + align_elems - 1) / align_elems * align_elems;
+        if (s > INT64_MAX / n_ranks) {
+            delete plan;
+            return fail(ZERO_ERANGE, "zero_partition_plan_shard0: padded length overflows int64");
+        }
+        plan->numel = total;
+        plan->shard = s;
+        plan->padded = s * n_ranks;
+        plan->by_rank.assign(static_cast<size_t>(n_ranks), {});
+        for (int32_t r = 0; r < n_ranks; ++r) {
+            for (int32_t t = 0; t < n_tensors; ++t) {
+                const size_t ti = static_cast<size_t>(t);
+                const int64_t d0 = plan->numels[ti] > 0 ? dim0[t] : 0;
+                const int64_t first = static_cast<int64_t>(r) * chunk_rows[ti];
+                const int64_t rows = d0 - first < chunk_rows[ti] ? d0 - first : chunk_rows[ti];
+                if (rows <= 0) continue;
+                zero_segment seg;
+                seg.tensor = t;
+                seg.rank = r;
+                seg.tensor_offset = first * inner[ti];
+                seg.shard_offset = plan->offsets[ti];
+                seg.length = rows * inner[ti];
+                plan->by_rank[static_cast<size_t>(r)].push_back(seg);
+                plan->all.push_back(seg);
+            }
+        }
+    } catch (const std::bad_alloc&) {
+        delete plan;
+        return fail(ZERO_ENOMEM, "zero_partition_plan_shard0: allocation failed");
+    }
+    *out = plan;
+    return ZERO_OK;
+}
+
+extern "C" int32_t zero_plan_kind(const zero_plan* p) { return p ? p->kind : -1; }
+
 extern "C" void zero_plan_free(zero_plan* plan) { delete plan; }
 
 extern "C" int64_t zero_plan_numel(const zero_plan* p) { return p ? p->numel : -1; }
@@ -104,6 +186,11 @@ extern "C" int32_t zero_plan_num_ranks(const zero_plan* p) { return p ? p->n_ran
 extern "C" int64_t zero_plan_tensor_offset(const zero_plan* p, int32_t t) {
     if (p == nullptr || t < 0 || static_cast<size_t>(t) >= p->offsets.size()) return -1;
     return p->offsets[static_cast<size_t>(t)];
+}
+
+extern "C" int64_t zero_plan_tensor_numel(const zero_plan* p, int32_t t) {
+    if (p == nullptr || t < 0 || static_cast<size_t>(t) >= p->numels.size()) return -1;
+    return p->numels[static_cast<size_t>(t)];
 }
 
 extern "C" int32_t zero_plan_num_segments(const zero_plan* p, int32_t rank) {

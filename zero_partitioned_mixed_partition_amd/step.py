@@ -154,9 +154,7 @@ def staggered_replicas(n_replicas: int, numel: int, device) -> List[torch.Tensor
 
 
 def plan_numels(plan: zb.Plan) -> List[int]:
-    t = plan.num_tensors
-    offs = [plan.tensor_offset(i) for i in range(t)] + [plan.numel]
-    return [offs[i + 1] - offs[i] for i in range(t)]
+    return [plan.tensor_numel(i) for i in range(plan.num_tensors)]
 
 
 def bucket_windows(padded_numel: int, bucket: int, lo: int, hi: int) -> List[Tuple[int, int]]:
