@@ -21,6 +21,10 @@ Other workloads (`--workload`), each timed as its own configuration states:
   gpt2-small-fsdp2  the default step on FSDP-2's per-parameter Shard(0) layout
               (every tensor cut along dim 0; a rank's chunks in one coalesced
               buffer); the replicas are per-tensor gradients flattened into it
+  gpt2-small-offload  the default step with ZeRO-Offload's update: the fp32
+              master/m/v live in host DRAM; the shard's bf16 gradients go to
+              the host, the host runs AdamW, the bf16 parameters come back, in
+              overlapped chunks (reduce, clip and gather stay on the GPU)
 
 All inputs are seeded synthetic data resident in HBM before timing starts. The
 other ranks' norm partials and parameter shards are inputs computed once,
@@ -42,7 +46,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 METRIC = "shard AdamW step: params/sec and achieved HBM GB/s (% of MI355X peak)"
-WORKLOAD_NAMES = ["gpt2-small", "llama3-8b", "llama3-70b", "gpt-1.3b", "gpt2-small-fsdp2"]
+WORKLOAD_NAMES = ["gpt2-small", "llama3-8b", "llama3-70b", "gpt-1.3b", "gpt2-small-fsdp2",
+                  "gpt2-small-offload"]
+PCIE_PEAK_GBS = 128.0          # PCIe 5.0 x16, both directions together (64 GB/s each way)
+OFFLOAD_CHUNK = 1 << 20        # elements per staging slot of the offload pipeline
 
 
 def parse_args(argv=None):
@@ -63,7 +70,8 @@ def parse_args(argv=None):
 
 
 DEFAULT_STEPS = {"gpt2-small": (200, 20), "llama3-8b": (20, 3), "llama3-70b": (5, 1),
-                 "gpt-1.3b": (10, 2), "gpt2-small-fsdp2": (200, 20)}
+                 "gpt-1.3b": (10, 2), "gpt2-small-fsdp2": (200, 20),
+                 "gpt2-small-offload": (30, 3)}
 
 
 class RankWorkload:
@@ -76,6 +84,7 @@ class RankWorkload:
         "llama3-8b": ("llama3-8b", 64, 63, 64, 25_000_000, False, "flat"),
         "llama3-70b": ("llama3-70b", 8, 7, 0, 0, False, "flat"),
         "gpt2-small-fsdp2": ("gpt2-small", 8, 7, 8, 0, True, "shard0"),
+        "gpt2-small-offload": ("gpt2-small", 8, 7, 8, 0, True, "flat"),
     }
 
     def __init__(self, name: str, device):
@@ -176,10 +185,80 @@ class RankWorkload:
             self.phases.append(("gather", rs.gather))
         self.adamw_launches = 1
         self.elems_per_step = S
+        self.offload = name.endswith("-offload")
+        if self.offload:
+            self._setup_offload(device)
+
+    def _setup_offload(self, device):
+        """Move the fp32 state to host DRAM and swap the AdamW phase for the
+        offload pipeline (device gradients in, host update, device params out)."""
+        import torch
+
+        from zero_partitioned_mixed_partition_amd import _binding as zb
+        rs = self.rs
+        self.h_master = rs.master.cpu()
+        self.h_m = torch.zeros(self.S, dtype=torch.float32)
+        self.h_v = torch.zeros(self.S, dtype=torch.float32)
+        self.staging = torch.empty(4 * OFFLOAD_CHUNK, dtype=torch.int16).pin_memory()
+        self.n_threads = len(os.sched_getaffinity(0))
+        st = torch.cuda.current_stream(device).cuda_stream
+        call = zb.prepare_offload_adamw_step(self.h_master, self.h_m, self.h_v, rs.grad,
+                                             rs.param_shards[self.rank], self.staging,
+                                             clip_scale=rs.scale, stream=st,
+                                             n_threads=self.n_threads, **self.hyper.as_kwargs())
+        self.t = 0
+
+        def offload_adamw():
+            self.t += 1
+            call(self.t)
+        self.phases = [(n, offload_adamw if n == "adamw" else fn) for n, fn in self.phases]
+        torch.cuda.synchronize()
+
+    def offload_parts(self, reps: int):
+        """The offload phase's two halves on their own, on copies of the state:
+        the host update alone (ms) and the shard's bf16 round trip over the link
+        alone (ms, pinned host memory, one copy each way)."""
+        import torch
+
+        import zero_partitioned_mixed_partition_amd as zm
+        p, m, v = self.h_master.clone(), self.h_m.clone(), self.h_v.clone()
+        g = torch.empty(self.S, dtype=torch.int16)
+        g.copy_(self.rs.grad.cpu())
+        out = torch.empty(self.S, dtype=torch.int16)
+        hp = self.hyper.as_kwargs()
+        zm.zero_host_adamw_step(p, m, v, g, out, 1, n_threads=self.n_threads, **hp)
+        t0 = time.perf_counter()
+        for k in range(reps):
+            zm.zero_host_adamw_step(p, m, v, g, out, 2 + k, n_threads=self.n_threads, **hp)
+        host_ms = (time.perf_counter() - t0) * 1e3 / reps
+        pin = torch.empty(self.S, dtype=torch.int16).pin_memory()
+        dev = self.rs.grad
+        pin.copy_(dev, non_blocking=True)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        c = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            pin.copy_(dev, non_blocking=True)
+        b.record()
+        for _ in range(reps):
+            self.rs.param_shards[self.rank].copy_(pin, non_blocking=True)
+        c.record()
+        torch.cuda.synchronize()
+        d2h, h2d = a.elapsed_time(b) / reps, b.elapsed_time(c) / reps
+        return {"host_adamw_ms": host_ms, "host_threads": self.n_threads,
+                "host_adamw_gbs": 28 * self.S / (host_ms * 1e-3) / 1e9,
+                "d2h_ms": d2h, "h2d_ms": h2d,
+                "d2h_gbs": 2 * self.S / (d2h * 1e-3) / 1e9,
+                "h2d_gbs": 2 * self.S / (h2d * 1e-3) / 1e9}
 
     def bytes_per_phase(self):
         S = self.S
-        b = {"clip": 8 * (self.n_ranks + max(len(self.windows), 1)) + 4, "adamw": 28 * S}
+        # the offload phase moves 2 B/elem each way over the host link; its
+        # 28 B/elem of state traffic is in host DRAM
+        b = {"clip": 8 * (self.n_ranks + max(len(self.windows), 1)) + 4,
+             "adamw": 4 * S if self.offload else 28 * S}
         if self.replicas:
             b["reduce"] = (2 * self.replicas + 2) * S
         else:
@@ -195,8 +274,11 @@ class RankWorkload:
         g = f" + gather of {len(self.workload.numels)} tensors" if self.rs.tensors else ""
         lay = (", FSDP-2 per-parameter Shard(0) layout (coalesced per-rank buffers)"
                if self.layout == "shard0" else "")
+        upd = (f"ZeRO-Offload AdamW (fp32 state in host DRAM, {self.n_threads} host threads, "
+               f"bf16 grads/params over PCIe in {OFFLOAD_CHUNK}-element chunks)"
+               if self.offload else "AdamW")
         return (f"{self.workload.name} tensor list{lay}, N_d={self.n_ranks}, rank {self.rank} shard "
-                f"of {self.S} elements; step = {red} + clip {self.max_norm} + AdamW{g}")
+                f"of {self.S} elements; step = {red} + clip {self.max_norm} + {upd}{g}")
 
 
 class AllRanksWorkload:
@@ -368,7 +450,7 @@ def cpu_baseline(wl, budget_s: float):
     import oracle
     import synth
     hp = wl.hyper.as_kwargs()
-    if wl.name == "gpt2-small":
+    if wl.name in ("gpt2-small", "gpt2-small-offload"):
         S, phi, rank = wl.S, wl.phi, wl.rank
         ref = oracle.partition_plan(wl.workload.numels, wl.n_ranks, wl.workload.align)
         lo = rank * S
@@ -486,9 +568,19 @@ def main(argv=None):
     phase_ms = time_phases(wl, max(3, min(steps, 50)))
     bpp = wl.bytes_per_phase()
 
+    offload = getattr(wl, "offload", False)
+
     def rates(ms):
-        return {n: {"ms": ms[n], "bytes": bpp[n], "gbs": bpp[n] / (ms[n] * 1e-3) / 1e9,
-                    "frac_of_hbm_peak": bpp[n] / (ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS} for n in ms}
+        out = {}
+        for n in ms:
+            gbs = bpp[n] / (ms[n] * 1e-3) / 1e9
+            if offload and n == "adamw":
+                out[n] = {"ms": ms[n], "link_bytes": bpp[n], "gbs": gbs,
+                          "frac_of_pcie_peak": gbs / PCIE_PEAK_GBS}
+            else:
+                out[n] = {"ms": ms[n], "bytes": bpp[n], "gbs": gbs,
+                          "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
+        return out
     kernels = rates(phase_ms)
     outside = None
     if getattr(wl, "extra_phases", None):
@@ -532,6 +624,19 @@ def main(argv=None):
                      "traffic": measured_traffic(elems_per_launch)},
         "cpu_baseline": cpu,
     }
+    if offload:
+        # The update runs on the host: the GPU-side figures above do not apply.
+        link_gbs = 4 * elems_per_launch / (adamw_ms * 1e-3) / 1e9
+        parts = wl.offload_parts(max(3, min(steps, 10)))
+        for k in ("adamw_hbm_gbs", "adamw_frac_of_hbm_peak"):
+            del line[k]
+        line["dtype"] = "f32"
+        line["offload"] = dict(parts, step_adamw_ms=adamw_ms,
+                               overlap=(parts["host_adamw_ms"] + parts["d2h_ms"] + parts["h2d_ms"])
+                               / adamw_ms)
+        line["roofline"] = {"bound": "pcie", "kernel": "zero_offload_adamw_step",
+                            "achieved": link_gbs, "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                            "frac": link_gbs / PCIE_PEAK_GBS, "traffic": None}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -19,6 +19,8 @@
  *                           (all-gather output layout, then un-flatten)
  *   zero_flatten_params     per-tensor bf16 buffers into the padded flat buffer
  *                           (the step before the reduce; inverse of the gather)
+ *   zero_offload_adamw_step ZeRO-Offload: the update on the host CPU, with the
+ *                           gradient and parameter transfers overlapped
  *
  * Conventions, for every function below:
  *   - bf16 values travel as raw uint16_t bit patterns; fp32 as float.
@@ -271,6 +273,41 @@ zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* sha
  * Errors: ZERO_EINVAL (null plan/arrays or a needed null pointer); ZERO_EHIP. */
 zero_status zero_flatten_params(const zero_plan* plan, const uint16_t* const* tensors,
                                 uint16_t* flat, hipStream_t stream);
+
+/* ------------------------------------------------------------------ ZeRO-Offload
+ *
+ * [ZF] "ZeRO-Offload Mechanics": the fp32 optimizer state lives in host DRAM;
+ * the GPU's bf16 gradients travel to the host over PCIe / CXL, the host CPU
+ * runs the fp32 Adam step and updates the fp32 weights, and the bf16
+ * parameters travel back, the transfers overlapping the host work.
+ *
+ * zero_host_adamw_step: the host CPU update alone, on host arrays [n], with
+ * zero_shard_adamw_step's exact per-element arithmetic (identical bits).
+ * clip_scale is a host float (a non-finite value skips the step); n_threads
+ * <= 0 uses every hardware thread. Errors: as zero_shard_adamw_step. */
+zero_status zero_host_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
+                                 const uint16_t* grad, uint16_t* param_out, int64_t n,
+                                 int64_t step, double lr, double beta1, double beta2, double eps,
+                                 double weight_decay, float clip_scale, int32_t n_threads);
+
+/* zero_offload_adamw_step: one offloaded step. The bf16 gradient (device
+ * d_grad [n]) is copied to the host chunk by chunk while the host updates the
+ * previous chunk (h_master, h_exp_avg, h_exp_avg_sq: host [n] fp32, in place)
+ * and the bf16 parameters of the chunk before go back to device
+ * d_param_out [n]. h_staging: pinned host memory (hipHostMalloc or a pinned
+ * torch tensor) of staging_elems bf16 values, split into two gradient and two
+ * parameter buffers of staging_elems/4 elements each (the chunk size).
+ * d_clip_scale: device float, nullable (1). Work already enqueued on `stream`
+ * happens before the gradient copies; work enqueued on `stream` afterwards
+ * sees the new parameters. The call returns when the host update is done and
+ * the staging buffers are free again.
+ * Errors: as zero_host_adamw_step; ZERO_ENOSPACE if staging_elems < 4; ZERO_EHIP. */
+zero_status zero_offload_adamw_step(float* h_master, float* h_exp_avg, float* h_exp_avg_sq,
+                                    const uint16_t* d_grad, uint16_t* d_param_out,
+                                    uint16_t* h_staging, int64_t staging_elems, int64_t n,
+                                    int64_t step, double lr, double beta1, double beta2,
+                                    double eps, double weight_decay, const float* d_clip_scale,
+                                    int32_t n_threads, hipStream_t stream);
 
 /* ------------------------------------------------------------------ diagnostics */
 const char* zero_status_string(zero_status status);   /* static string */

@@ -8,7 +8,8 @@ gpt2-small       GPT-2-small tensor list, N_d = 8, rank 7 (15.6M elements),
                  the oracle computes every step's global norm over all 8 ranks
                  (124M values) and the AdamW state on sampled windows.
 bench pipeline   the benchmark's own step (8 replicas reduced for rank 7, fused
-                 norm, clip, AdamW, gather of 148 tensors): full arrays for 2 steps.
+                 norm, clip, AdamW, gather of 148 tensors): full arrays for 2 steps;
+                 also on the Shard(0) layout and with the AdamW offloaded to the host.
 """
 import numpy as np
 import pytest
@@ -135,7 +136,7 @@ def test_gpt2_small_rank7_hundred_steps_clip(zm):
         assert_bf16_close(host_u16(d_param[sl]), bits, f"param window {w0}")
 
 
-@pytest.mark.parametrize("name", ["gpt2-small", "gpt2-small-fsdp2"])
+@pytest.mark.parametrize("name", ["gpt2-small", "gpt2-small-fsdp2", "gpt2-small-offload"])
 def test_bench_pipeline_matches_oracle(zm, name):
     import bench
     setup = bench.make_workload(name, dev())
@@ -190,8 +191,12 @@ def test_bench_pipeline_matches_oracle(zm, name):
     assert (np.abs(got_parts[others] - want_parts[others]) <= 1e-12 * want_parts[others]).all()
     got_scale = np.float32(setup.rs.scale.item())
     assert abs(int(got_scale.view(np.int32)) - int(np.float32(out["clip"]).view(np.int32))) <= 1
-    for got, key in ((setup.rs.master, "master"), (setup.rs.exp_avg, "exp_avg"),
-                     (setup.rs.exp_avg_sq, "exp_avg_sq")):
+    if setup.offload:     # the fp32 state lives in host memory
+        held = ((setup.h_master, "master"), (setup.h_m, "exp_avg"), (setup.h_v, "exp_avg_sq"))
+    else:
+        held = ((setup.rs.master, "master"), (setup.rs.exp_avg, "exp_avg"),
+                (setup.rs.exp_avg_sq, "exp_avg_sq"))
+    for got, key in held:
         exact = assert_f32_close(host_f32(got), state[key], key)
         note(f"bench pipeline {name}: {key} bit-identical fraction {exact:.6f}")
     if shard0:

@@ -10,6 +10,8 @@ The entry points mirror the C ABI in include/zero_mi355x.h one for one:
     zero_shard_adamw_step   fused fp32 AdamW update with bf16 parameter emit
     zero_gather_params      bf16 shards -> per-tensor parameters
     zero_flatten_params     per-tensor buffers -> padded flat buffer
+    zero_host_adamw_step    the same update on the host CPU (ZeRO-Offload)
+    zero_offload_adamw_step host update with overlapped grad/param transfers
 
 All arithmetic runs in the HIP kernels of libzero_mi355x.so (gfx950); this
 package only marshals torch tensors (device memory and streams) into the C
@@ -19,5 +21,5 @@ from ._binding import (LIB_PATH, ZERO_MAX_REPLICAS, Plan, ZeroError,  # noqa: F4
                        sqnorm_workspace, zero_clip_scale, zero_flatten_params, zero_gather_params,
                        zero_grad_reduce_shard,
                        zero_grad_sqnorm, zero_last_error, zero_partition_plan,
-                       zero_partition_plan_shard0,
+                       zero_partition_plan_shard0, zero_host_adamw_step, zero_offload_adamw_step,
                        zero_shard_adamw_step, zero_sqnorm_workspace_bytes, zero_status_string)

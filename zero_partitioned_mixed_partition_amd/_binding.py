@@ -67,6 +67,12 @@ _adamw = _fn("zero_shard_adamw_step", c_i32,
               c_vp])
 _gather = _fn("zero_gather_params", c_i32, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp])
 _flatten = _fn("zero_flatten_params", c_i32, [c_vp, ctypes.POINTER(c_vp), c_vp, c_vp])
+_host_adamw = _fn("zero_host_adamw_step", c_i32,
+                  [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl,
+                   ctypes.c_float, c_i32])
+_offload = _fn("zero_offload_adamw_step", c_i32,
+               [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_dbl, c_dbl, c_dbl, c_dbl,
+                c_dbl, c_vp, c_i32, c_vp])
 _status_string = _fn("zero_status_string", ctypes.c_char_p, [c_i32])
 _last_error = _fn("zero_last_error", ctypes.c_char_p, [])
 
@@ -279,6 +285,47 @@ def zero_flatten_params(plan: Plan, tensors: Sequence, flat, stream=None) -> Non
            "zero_flatten_params")
 
 
+def _host_ptr(a, itemsize: int, what: str) -> int:
+    """Host buffer: a C-contiguous numpy array or a CPU torch tensor."""
+    if hasattr(a, "ctypes"):
+        if not a.flags.c_contiguous or a.itemsize != itemsize or not a.flags.writeable and what != "grad":
+            raise ValueError(f"{what} must be a contiguous, writable host array of {itemsize}-byte items")
+        return a.ctypes.data
+    if a.is_cuda or not a.is_contiguous() or a.element_size() != itemsize:
+        raise ValueError(f"{what} must be a contiguous host tensor of {itemsize}-byte items")
+    return a.data_ptr()
+
+
+def zero_host_adamw_step(master, exp_avg, exp_avg_sq, grad, param_out, step: int, lr: float,
+                         beta1: float, beta2: float, eps: float, weight_decay: float,
+                         clip_scale: float = 1.0, n_threads: int = 0) -> None:
+    """Host arrays (numpy or CPU tensors): fp32 master/m/v, bf16 bits grad/param_out."""
+    n = len(master)
+    for a in (exp_avg, exp_avg_sq, grad, param_out):
+        if len(a) < n:
+            raise ValueError("an array holds fewer elements than master")
+    _check(_host_adamw(_host_ptr(master, 4, "master"), _host_ptr(exp_avg, 4, "exp_avg"),
+                       _host_ptr(exp_avg_sq, 4, "exp_avg_sq"), _host_ptr(grad, 2, "grad"),
+                       _host_ptr(param_out, 2, "param_out"), n, step, lr, beta1, beta2, eps,
+                       weight_decay, float(clip_scale), n_threads), "zero_host_adamw_step")
+
+
+def zero_offload_adamw_step(h_master, h_exp_avg, h_exp_avg_sq, d_grad, d_param_out, h_staging,
+                            step: int, lr: float, beta1: float, beta2: float, eps: float,
+                            weight_decay: float, clip_scale=None, n_threads: int = 0,
+                            stream=None) -> None:
+    """Host fp32 state (CPU tensors), device bf16 grad/params, pinned host staging."""
+    n = h_master.numel()
+    if not h_staging.is_pinned():
+        raise ValueError("h_staging must be pinned host memory")
+    _check(_offload(_host_ptr(h_master, 4, "master"), _host_ptr(h_exp_avg, 4, "exp_avg"),
+                    _host_ptr(h_exp_avg_sq, 4, "exp_avg_sq"), _ptr(d_grad, 2, "d_grad"),
+                    _ptr(d_param_out, 2, "d_param_out"), _host_ptr(h_staging, 2, "h_staging"),
+                    h_staging.numel(), n, step, lr, beta1, beta2, eps, weight_decay,
+                    _ptr(clip_scale, 4, "clip_scale"), n_threads, _stream(stream, d_grad)),
+           "zero_offload_adamw_step")
+
+
 def zero_status_string(status: int) -> str:
     return _status_string(status).decode()
 
@@ -339,6 +386,28 @@ def prepare_shard_adamw_step(master, exp_avg, exp_avg_sq, grad, param_out, lr: f
                           weight_decay, _ptr(clip_scale, 4, "clip_scale"),
                           _stream(stream, master)], "zero_shard_adamw_step", step_index=6)
     p._keep = (master, exp_avg, exp_avg_sq, grad, param_out, clip_scale)
+    return p
+
+
+def prepare_offload_adamw_step(h_master, h_exp_avg, h_exp_avg_sq, d_grad, d_param_out, h_staging,
+                               lr: float, beta1: float, beta2: float, eps: float,
+                               weight_decay: float, clip_scale, stream, n_threads: int = 0
+                               ) -> Prepared:
+    """Call the result with the 1-based step number."""
+    n = h_master.numel()
+    for t in (h_exp_avg, h_exp_avg_sq, d_grad, d_param_out):
+        if t.numel() < n:
+            raise ValueError("an array holds fewer elements than master")
+    if not h_staging.is_pinned():
+        raise ValueError("h_staging must be pinned host memory")
+    p = Prepared(_offload, [_host_ptr(h_master, 4, "master"), _host_ptr(h_exp_avg, 4, "exp_avg"),
+                            _host_ptr(h_exp_avg_sq, 4, "exp_avg_sq"), _ptr(d_grad, 2, "d_grad"),
+                            _ptr(d_param_out, 2, "d_param_out"),
+                            _host_ptr(h_staging, 2, "h_staging"), h_staging.numel(), n, 1, lr,
+                            beta1, beta2, eps, weight_decay, _ptr(clip_scale, 4, "clip_scale"),
+                            n_threads, _stream(stream, d_grad)],
+                 "zero_offload_adamw_step", step_index=8)
+    p._keep = (h_master, h_exp_avg, h_exp_avg_sq, d_grad, d_param_out, h_staging, clip_scale)
     return p
 
 

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzero_mi355x.so")
 
-SOURCES = ["status.cpp", "plan.cpp", "adamw.hip", "reduce.hip", "gather.hip"]
+SOURCES = ["status.cpp", "plan.cpp", "offload.cpp", "adamw.hip", "reduce.hip", "gather.hip"]
 
 # -ffp-contract=off: the AdamW and reduction arithmetic is specified operation
 # by operation; no multiply-add fusion. Packed fp32 instructions are disabled.
@@ -23,13 +23,16 @@ DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-pa
 
 
 def _compile(src: str, obj: str, defines: List[str], save_temps: Optional[str]) -> List[str]:
-    cmd = ["hipcc", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + defines
     if src.endswith(".hip"):
-        cmd += DEVICE
+        cmd = ["hipcc", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + defines + DEVICE
         if save_temps:
             cmd += [f"-save-temps={'obj'}"]
     else:
-        pass
+        # host-only C++ (no device code): compiled as plain C++ against the HIP runtime API;
+        # no errno from sqrtf, so the host AdamW loop vectorizes (IEEE results unchanged)
+        rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+        cmd = (["hipcc", "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + defines +
+               [f"-I{rocm}/include", "-D__HIP_PLATFORM_AMD__", "-fno-math-errno"])
     return cmd
 
 

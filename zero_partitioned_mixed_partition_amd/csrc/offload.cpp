@@ -1,0 +1,359 @@
+// ZeRO-Offload step: fp32 AdamW on the host CPU, bf16 gradients in from the GPU
+// and bf16 parameters back out, in overlapped chunks.
+//
+// "Zero Redundancy Optimizer (ZeRO) and Fully Sharded Data Parallelism (FSDP):
+// Mathematical Foundations ...", section "ZeRO-Offload Mechanics": the forward
+// and backward passes stay on the GPU; gradients go to host DRAM over PCIe /
+// CXL, the host runs the fp32 Adam step and updates the fp32 weights, and the
+// parameters go back; the transfers overlap the host work (the following
+// section on PCIe / CXL bandwidth limits, titled "...across Memory Biers" on
+// the page).
+//
+// The host update applies exactly the device kernel's per-element operations
+// (same order, IEEE fp32, no contraction, correctly rounded / and sqrt, the
+// same bf16 rounding), so host and device steps give identical bits. The loop
+// is compiled for AVX-512, AVX2 and baseline x86-64 and picked at load time;
+// vector / and sqrt are IEEE-exact on all of them.
+#include <hip/hip_runtime_api.h>
+
+#include <sched.h>
+
+#include <atomic>
+#include <cmath>
+#include <condition_variable>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+struct HostScalars {
+    float beta1, one_minus_beta1, beta2, one_minus_beta2, eps, step_size, sqrt_bc2, decay, clip;
+};
+
+inline uint16_t host_bf16(float x) {
+    uint32_t u;
+    std::memcpy(&u, &x, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+    return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+inline float host_widen(uint16_t h) {
+    const uint32_t u = static_cast<uint32_t>(h) << 16;
+    float x;
+    std::memcpy(&x, &u, 4);
+    return x;
+}
+
+__attribute__((target_clones("avx512f", "avx2", "default")))
+void host_adamw_range(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
+                      const uint16_t* __restrict__ g, uint16_t* __restrict__ out, int64_t n,
+                      const HostScalars c) {
+    for (int64_t i = 0; i < n; ++i) {
+        const float gi = host_widen(g[i]) * c.clip;
+        const float bm = c.beta1 * m[i];
+        const float gm = c.one_minus_beta1 * gi;
+        const float mi = bm + gm;
+        const float bv = c.beta2 * v[i];
+        const float gg = gi * gi;
+        const float gv = c.one_minus_beta2 * gg;
+        const float vi = bv + gv;
+        float pi = p[i] * c.decay;
+        const float root = std::sqrt(vi);
+        const float denom = root / c.sqrt_bc2 + c.eps;
+        const float ratio = mi / denom;
+        pi = pi - c.step_size * ratio;
+        m[i] = mi;
+        v[i] = vi;
+        p[i] = pi;
+        out[i] = host_bf16(pi);
+    }
+}
+
+// A persistent pool of host workers: the offload pipeline runs one parallel
+// update per chunk, many per step, and starting threads for each would cost
+// more than a chunk's arithmetic. run() hands out `tasks` task indices; the
+// caller's thread takes part and returns once every task has finished and no
+// worker is still inside the hand-out loop (so the next run cannot be mixed
+// with this one). Runs are serialised on run_mu_.
+class HostPool {
+  public:
+    static HostPool& get() {
+        static HostPool pool(affinity_cpus());
+        return pool;
+    }
+    void run(int tasks, const std::function<void(int)>& fn) {
+        std::lock_guard<std::mutex> serial(run_mu_);
+        if (tasks <= 1 || workers_.empty()) {
+            for (int t = 0; t < tasks; ++t) fn(t);
+            return;
+        }
+        {
+            std::unique_lock<std::mutex> lock(mu_);
+            done_cv_.wait(lock, [&] { return active_ == 0; });   // late wakers of the last run
+            fn_ = &fn;
+            tasks_ = tasks;
+            next_.store(0);
+            pending_ = tasks;
+            ++generation_;
+        }
+        cv_.notify_all();
+        const int done = drain();
+        std::unique_lock<std::mutex> lock(mu_);
+        pending_ -= done;
+        done_cv_.wait(lock, [&] { return pending_ == 0 && active_ == 0; });
+        fn_ = nullptr;
+    }
+    ~HostPool() {
+        {
+            std::lock_guard<std::mutex> lock(mu_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        for (auto& w : workers_) w.join();
+    }
+
+    static int affinity_cpus() {
+        cpu_set_t set;
+        CPU_ZERO(&set);
+        if (sched_getaffinity(0, sizeof(set), &set) == 0) {
+            const int n = CPU_COUNT(&set);
+            if (n > 0) return n;
+        }
+        const unsigned hw = std::thread::hardware_concurrency();
+        return hw > 0 ? static_cast<int>(hw) : 1;
+    }
+
+  private:
+    explicit HostPool(int threads) {
+        for (int i = 1; i < threads; ++i) workers_.emplace_back([this] { loop(); });
+    }
+    // Takes task indices until none are left; returns how many it ran. tasks_
+    // and fn_ stay fixed while any thread is in here (run() waits for that).
+    int drain() {
+        int done = 0;
+        for (int t; (t = next_.fetch_add(1)) < tasks_; ++done) (*fn_)(t);
+        return done;
+    }
+    void loop() {
+        uint64_t seen = 0;
+        for (;;) {
+            {
+                std::unique_lock<std::mutex> lock(mu_);
+                cv_.wait(lock, [&] { return stop_ || generation_ != seen; });
+                if (stop_) return;
+                seen = generation_;
+                ++active_;
+            }
+            const int done = drain();
+            std::lock_guard<std::mutex> lock(mu_);
+            pending_ -= done;
+            --active_;
+            if (active_ == 0) done_cv_.notify_all();
+        }
+    }
+
+    std::vector<std::thread> workers_;
+    std::mutex run_mu_, mu_;
+    std::condition_variable cv_, done_cv_;
+    const std::function<void(int)>* fn_ = nullptr;
+    std::atomic<int> next_{0};
+    int tasks_ = 0, pending_ = 0, active_ = 0;
+    uint64_t generation_ = 0;
+    bool stop_ = false;
+};
+
+void host_adamw_parallel(float* p, float* m, float* v, const uint16_t* g, uint16_t* out,
+                         int64_t n, const HostScalars& c, int threads) {
+    if (threads <= 1 || n < (int64_t(1) << 16)) {
+        host_adamw_range(p, m, v, g, out, n, c);
+        return;
+    }
+    // 64-element pieces keep every task's start on a cache line of each array.
+    const int64_t per = ((n + threads - 1) / threads + 63) / 64 * 64;
+    const int tasks = static_cast<int>((n + per - 1) / per);
+    HostPool::get().run(tasks, [=, &c](int t) {
+        const int64_t lo = t * per;
+        const int64_t len = n - lo < per ? n - lo : per;
+        host_adamw_range(p + lo, m + lo, v + lo, g + lo, out + lo, len, c);
+    });
+}
+
+zero_status make_scalars(int64_t step, double lr, double beta1, double beta2, double eps,
+                         double weight_decay, HostScalars* c, const char* who) {
+    using zero::fail;
+    if (step < 1) return fail(ZERO_EINVAL, std::string(who) + ": step must be >= 1");
+    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
+        return fail(ZERO_EINVAL, std::string(who) + ": betas must lie in [0, 1)");
+    if (!(eps > 0.0) || !std::isfinite(eps))
+        return fail(ZERO_EINVAL, std::string(who) + ": eps must be finite and > 0");
+    if (!(lr >= 0.0) || !std::isfinite(lr) || !std::isfinite(weight_decay))
+        return fail(ZERO_EINVAL, std::string(who) + ": lr and weight_decay must be finite, lr >= 0");
+    const double bc1 = 1.0 - std::pow(beta1, static_cast<double>(step));
+    const double bc2 = 1.0 - std::pow(beta2, static_cast<double>(step));
+    if (!(bc1 > 0.0) || !(bc2 > 0.0))
+        return fail(ZERO_EINVAL, std::string(who) + ": bias correction is zero");
+    c->beta1 = static_cast<float>(beta1);
+    c->one_minus_beta1 = static_cast<float>(1.0 - beta1);
+    c->beta2 = static_cast<float>(beta2);
+    c->one_minus_beta2 = static_cast<float>(1.0 - beta2);
+    c->eps = static_cast<float>(eps);
+    c->step_size = static_cast<float>(lr / bc1);
+    c->sqrt_bc2 = static_cast<float>(std::sqrt(bc2));
+    c->decay = static_cast<float>(1.0 - lr * weight_decay);
+    c->clip = 1.0f;
+    return ZERO_OK;
+}
+
+// 0 requests one task per CPU this process may run on.
+int default_threads(int32_t requested) {
+    return requested > 0 ? requested : HostPool::affinity_cpus();
+}
+
+// Two copy streams per device (default priority), made once.
+struct CopyStreams {
+    hipStream_t d2h = nullptr, h2d = nullptr;
+};
+
+zero_status copy_streams(CopyStreams* out) {
+    static std::mutex mu;
+    static CopyStreams per_dev[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return zero::fail(ZERO_EHIP, "zero_offload_adamw_step: no current device");
+    std::lock_guard<std::mutex> lock(mu);
+    CopyStreams& s = per_dev[dev];
+    if (s.d2h == nullptr) {
+        zero_status st = zero::check_hip(hipStreamCreateWithFlags(&s.d2h, hipStreamNonBlocking),
+                                         "zero_offload_adamw_step: stream");
+        if (st != ZERO_OK) return st;
+        st = zero::check_hip(hipStreamCreateWithFlags(&s.h2d, hipStreamNonBlocking),
+                             "zero_offload_adamw_step: stream");
+        if (st != ZERO_OK) return st;
+    }
+    *out = s;
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_host_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
+                                            const uint16_t* grad, uint16_t* param_out, int64_t n,
+                                            int64_t step, double lr, double beta1, double beta2,
+                                            double eps, double weight_decay, float clip_scale,
+                                            int32_t n_threads) {
+    using zero::fail;
+    zero::clear_error();
+    if (n < 0) return fail(ZERO_EINVAL, "zero_host_adamw_step: n < 0");
+    HostScalars c;
+    zero_status st = make_scalars(step, lr, beta1, beta2, eps, weight_decay, &c,
+                                  "zero_host_adamw_step");
+    if (st != ZERO_OK) return st;
+    if (n == 0) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !grad || !param_out)
+        return fail(ZERO_EINVAL, "zero_host_adamw_step: NULL array");
+    if (!std::isfinite(clip_scale)) return ZERO_OK;        // a non-finite norm skips the step
+    c.clip = clip_scale;
+    host_adamw_parallel(master, exp_avg, exp_avg_sq, grad, param_out, n, c,
+                        default_threads(n_threads));
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_offload_adamw_step(float* h_master, float* h_exp_avg,
+                                               float* h_exp_avg_sq, const uint16_t* d_grad,
+                                               uint16_t* d_param_out, uint16_t* h_staging,
+                                               int64_t staging_elems, int64_t n, int64_t step,
+                                               double lr, double beta1, double beta2, double eps,
+                                               double weight_decay, const float* d_clip_scale,
+                                               int32_t n_threads, hipStream_t stream) {
+    using zero::fail;
+    static const char* const who = "zero_offload_adamw_step";
+    zero::clear_error();
+    if (n < 0) return fail(ZERO_EINVAL, "zero_offload_adamw_step: n < 0");
+    HostScalars c;
+    zero_status st = make_scalars(step, lr, beta1, beta2, eps, weight_decay, &c, who);
+    if (st != ZERO_OK) return st;
+    if (n == 0) return ZERO_OK;
+    if (!h_master || !h_exp_avg || !h_exp_avg_sq || !d_grad || !d_param_out || !h_staging)
+        return fail(ZERO_EINVAL, "zero_offload_adamw_step: NULL array");
+    const int64_t chunk = staging_elems / 4;
+    if (chunk < 1) return fail(ZERO_ENOSPACE, "zero_offload_adamw_step: staging holds < 4 elements");
+    CopyStreams cs;
+    st = copy_streams(&cs);
+    if (st != ZERO_OK) return st;
+    const int threads = default_threads(n_threads);
+
+    hipEvent_t start = nullptr, ev_in[2] = {nullptr, nullptr}, ev_out[2] = {nullptr, nullptr};
+    // On every exit the copy streams have drained (staging is the caller's again)
+    // and the events are gone.
+    auto finish = [&](zero_status s) -> zero_status {
+        (void)hipStreamSynchronize(cs.d2h);
+        (void)hipStreamSynchronize(cs.h2d);
+        if (start) (void)hipEventDestroy(start);
+        for (int i = 0; i < 2; ++i) {
+            if (ev_in[i]) (void)hipEventDestroy(ev_in[i]);
+            if (ev_out[i]) (void)hipEventDestroy(ev_out[i]);
+        }
+        return s;
+    };
+#define ZERO_TRY(expr, what)                                                    \
+    do {                                                                        \
+        const hipError_t e_ = (expr);                                           \
+        if (e_ != hipSuccess)                                                   \
+            return finish(zero::check_hip(e_, "zero_offload_adamw_step: " what)); \
+    } while (0)
+    ZERO_TRY(hipEventCreateWithFlags(&start, hipEventDisableTiming), "event");
+    for (int i = 0; i < 2; ++i) {
+        ZERO_TRY(hipEventCreateWithFlags(&ev_in[i], hipEventDisableTiming), "event");
+        ZERO_TRY(hipEventCreateWithFlags(&ev_out[i], hipEventDisableTiming), "event");
+    }
+    // Whatever `stream` holds before the call (the gradients' producer) comes first.
+    ZERO_TRY(hipEventRecord(start, stream), "record");
+    ZERO_TRY(hipStreamWaitEvent(cs.d2h, start, 0), "wait");
+    ZERO_TRY(hipStreamWaitEvent(cs.h2d, start, 0), "wait");
+    if (d_clip_scale != nullptr) {
+        float clip = 1.0f;
+        ZERO_TRY(hipMemcpyAsync(&clip, d_clip_scale, sizeof(float), hipMemcpyDeviceToHost, cs.d2h),
+                 "clip copy");
+        ZERO_TRY(hipStreamSynchronize(cs.d2h), "clip sync");
+        if (!std::isfinite(clip)) return finish(ZERO_OK);   // a non-finite norm skips the step
+        c.clip = clip;
+    }
+    // Staging: two gradient slots and two parameter slots of `chunk` elements.
+    // Chunk k's gradients land in slot k%2 while chunk k-1 is updated; chunk k's
+    // parameters leave from slot k%2 while chunk k+1 is updated.
+    uint16_t* gstage[2] = {h_staging, h_staging + chunk};
+    uint16_t* pstage[2] = {h_staging + 2 * chunk, h_staging + 3 * chunk};
+    const int64_t chunks = (n + chunk - 1) / chunk;
+    for (int64_t k = 0; k <= chunks; ++k) {
+        if (k < chunks) {                       // chunk k's gradients start to travel
+            const int64_t off = k * chunk, len = n - off < chunk ? n - off : chunk;
+            ZERO_TRY(hipMemcpyAsync(gstage[k % 2], d_grad + off, len * sizeof(uint16_t),
+                                    hipMemcpyDeviceToHost, cs.d2h), "grad copy");
+            ZERO_TRY(hipEventRecord(ev_in[k % 2], cs.d2h), "record");
+        }
+        if (k == 0) continue;
+        const int64_t j = k - 1;                // chunk j is updated on the host now
+        const int slot = static_cast<int>(j % 2);
+        const int64_t off = j * chunk, len = n - off < chunk ? n - off : chunk;
+        ZERO_TRY(hipEventSynchronize(ev_in[slot]), "grad wait");
+        if (j >= 2) ZERO_TRY(hipEventSynchronize(ev_out[slot]), "param wait");
+        host_adamw_parallel(h_master + off, h_exp_avg + off, h_exp_avg_sq + off, gstage[slot],
+                            pstage[slot], len, c, threads);
+        ZERO_TRY(hipMemcpyAsync(d_param_out + off, pstage[slot], len * sizeof(uint16_t),
+                                hipMemcpyHostToDevice, cs.h2d), "param copy");
+        ZERO_TRY(hipEventRecord(ev_out[slot], cs.h2d), "record");
+    }
+    // Later work on `stream` sees the new parameters.
+    ZERO_TRY(hipEventRecord(start, cs.h2d), "record");
+    ZERO_TRY(hipStreamWaitEvent(stream, start, 0), "wait");
+#undef ZERO_TRY
+    return finish(ZERO_OK);
+}

@@ -1,5 +1,5 @@
 // Status strings, thread-local error detail, and per-device properties.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <array>
 #include <mutex>
