@@ -283,8 +283,11 @@ zero_status zero_flatten_params(const zero_plan* plan, const uint16_t* const* te
  *
  * zero_host_adamw_step: the host CPU update alone, on host arrays [n], with
  * zero_shard_adamw_step's exact per-element arithmetic (identical bits).
- * clip_scale is a host float (a non-finite value skips the step); n_threads
- * <= 0 uses every hardware thread. Errors: as zero_shard_adamw_step. */
+ * clip_scale is a host float (a non-finite value skips the step). The work is
+ * split over a persistent pool of host threads: n_threads tasks, or one per
+ * CPU in the calling process's affinity mask when n_threads <= 0. Calls from
+ * several threads are safe; their parallel parts run one after another.
+ * Errors: as zero_shard_adamw_step. */
 zero_status zero_host_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
                                  const uint16_t* grad, uint16_t* param_out, int64_t n,
                                  int64_t step, double lr, double beta1, double beta2, double eps,
@@ -297,10 +300,12 @@ zero_status zero_host_adamw_step(float* master, float* exp_avg, float* exp_avg_s
  * d_param_out [n]. h_staging: pinned host memory (hipHostMalloc or a pinned
  * torch tensor) of staging_elems bf16 values, split into two gradient and two
  * parameter buffers of staging_elems/4 elements each (the chunk size).
- * d_clip_scale: device float, nullable (1). Work already enqueued on `stream`
- * happens before the gradient copies; work enqueued on `stream` afterwards
- * sees the new parameters. The call returns when the host update is done and
- * the staging buffers are free again.
+ * d_clip_scale: device float, nullable (1); a non-finite value skips the step
+ * (nothing is written). n_threads: as zero_host_adamw_step. Work already
+ * enqueued on `stream` happens before the gradient copies; work enqueued on
+ * `stream` afterwards sees the new parameters. The copies run on two internal
+ * streams of the current device (default priority). The call returns when the
+ * host update is done and the staging buffers are free again, on errors too.
  * Errors: as zero_host_adamw_step; ZERO_ENOSPACE if staging_elems < 4; ZERO_EHIP. */
 zero_status zero_offload_adamw_step(float* h_master, float* h_exp_avg, float* h_exp_avg_sq,
                                     const uint16_t* d_grad, uint16_t* d_param_out,

@@ -5,9 +5,8 @@
 // Mathematical Foundations ...", section "ZeRO-Offload Mechanics": the forward
 // and backward passes stay on the GPU; gradients go to host DRAM over PCIe /
 // CXL, the host runs the fp32 Adam step and updates the fp32 weights, and the
-// parameters go back; the transfers overlap the host work (the following
-// section on PCIe / CXL bandwidth limits, titled "...across Memory Biers" on
-// the page).
+// parameters go back. The next section ("Communication Bandwidth Limits across
+// Memory Biers", sic: tiers) has the parameter transfer overlap the optimizer.
 //
 // The host update applies exactly the device kernel's per-element operations
 // (same order, IEEE fp32, no contraction, correctly rounded / and sqrt, the
