@@ -34,6 +34,7 @@ parameter all-gather). Prints one JSON line. One GPU only: --gpus > 1 is refused
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -536,6 +537,11 @@ def main(argv=None):
         print(f"[bench] ran {args.profile_steps} steps for profiling", file=sys.stderr, flush=True)
         return 0
 
+    # Python's cyclic garbage collector is off while steps are issued: a full
+    # collection pauses the issuing thread for tens of milliseconds, which the
+    # GPU would spend idle (as timeit does; the collector is run first).
+    gc.collect()
+    gc.disable()
     for _ in range(warmup):
         run_step(wl)
     torch.cuda.synchronize()
@@ -592,6 +598,8 @@ def main(argv=None):
     adamw_gbs = adamw_bytes / (adamw_ms * 1e-3) / 1e9
     value = wl.elems_per_step / (ms_per_step * 1e-3)
 
+    parts = wl.offload_parts(max(3, min(steps, 10))) if offload else None
+    gc.enable()
     cpu = None
     if args.cpu_baseline_seconds > 0:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -627,7 +635,6 @@ def main(argv=None):
     if offload:
         # The update runs on the host: the GPU-side figures above do not apply.
         link_gbs = 4 * elems_per_launch / (adamw_ms * 1e-3) / 1e9
-        parts = wl.offload_parts(max(3, min(steps, 10)))
         for k in ("adamw_hbm_gbs", "adamw_frac_of_hbm_peak"):
             del line[k]
         line["dtype"] = "f32"

@@ -341,3 +341,34 @@ def test_shard0_gather_and_flatten(zm, seed):
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(zip(outs, oracle.gather_params_shard0(ref, shards))):
         assert_bits_equal(host_u16(a), b, f"tensor {i}")
+
+
+@pytest.mark.parametrize("kind,n_ranks", [("flat", 1), ("flat", 64), ("flat", 65), ("flat", 100),
+                                          ("shard0", 64), ("shard0", 97)])
+def test_gather_rank_counts_many_tensors_misaligned(zm, kind, n_ranks):
+    """Up to 64 ranks the gather finds each element's rank by arithmetic; above
+    that it copies plan segments. Both must agree with the oracle, over more
+    tensors than one launch carries and with 2-byte-misaligned destinations."""
+    rng = np.random.default_rng(900 + n_ranks)
+    t = 150
+    dim0 = [int(x) for x in rng.integers(1, 300, t)]
+    numels = [d * int(k) for d, k in zip(dim0, rng.integers(1, 12, t))]
+    note(f"gather {kind} N_d={n_ranks} T={t} Phi={sum(numels)}")
+    if kind == "flat":
+        ref = oracle.partition_plan(numels, n_ranks, 8)
+        plan = zm.zero_partition_plan(numels, n_ranks, 8)
+        gather = oracle.gather_params
+    else:
+        ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, 8)
+        plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, 8)
+        gather = oracle.gather_params_shard0
+    S = ref.shard_numel
+    shards = [rng.integers(0, 1 << 16, S).astype(np.uint16) for _ in range(n_ranks)]
+    bufs = [torch.full((n + 1,), 0x3333, dtype=torch.int16, device=dev()) for n in numels]
+    zm.zero_gather_params(plan, [to_dev_u16(x) for x in shards],
+                          [b[1:] if i % 2 else b[:-1] for i, b in enumerate(bufs)])
+    torch.cuda.synchronize()
+    for i, (b, w) in enumerate(zip(bufs, gather(ref, shards))):
+        got = host_u16(b)
+        assert_bits_equal(got[1:] if i % 2 else got[:-1], w, f"tensor {i}")
+        assert (got[0] if i % 2 else got[-1]) == 0x3333, "wrote outside the tensor"

@@ -7,15 +7,20 @@
 // shard; section "FSDP-1": the shards are equal chunks of one flat buffer, so
 // each tensor is a slice of the shards' concatenation. The plan lists that
 // slice as segments (tensor, offset in tensor, shard, offset in shard,
-// length); this kernel copies every segment.
+// length). Section "FSDP-2: Per-Parameter Sharding via DTensor": with
+// per-parameter Shard(0) placement, each tensor is its ranks' dim-0 chunks
+// stacked in rank order.
 //
-// Memory: 2 bytes read and 2 written per parameter. The segment table travels
-// in the kernel arguments, kSegs segments per launch (no device-side table,
-// no host-to-device copy, nothing allocated): workgroup b finds its segment by
-// a binary search over the per-segment workgroup prefix, then copies a chunk
-// of kChunk elements, one access per lane (16 bytes by default) with
-// non-temporal hints when source and destination are co-aligned to the access
-// width, element by element otherwise.
+// Memory: 2 bytes read and 2 written per parameter. Two kernels, both with
+// their tables in the kernel arguments (no device-side table, no
+// host-to-device copy, nothing allocated), both copying kChunk elements per
+// workgroup, one access per lane (16 bytes by default) with non-temporal
+// hints when source and destination allow it, element by element otherwise:
+//   gather_kernel         one descriptor per plan segment (also the flatten);
+//   gather_tensor_kernel  one descriptor per tensor; the rank of an element is
+//                         found by arithmetic. A Shard(0) plan has about N_d
+//                         segments per tensor, so this needs N_d times fewer
+//                         descriptors, and launches, than the segment form.
 #include <hip/hip_runtime.h>
 
 #include <string>
@@ -33,7 +38,14 @@ constexpr int kSegs = 96;                       // segments per launch (kernarg 
 #define ZERO_GATHER_LANE_ELEMS 8
 #endif
 constexpr int kLane = ZERO_GATHER_LANE_ELEMS;
-constexpr int64_t kChunk = int64_t(kThreads) * kLane;   // elements per workgroup
+// Accesses per lane: a workgroup copies kVecs passes of kRow elements, so
+// its fixed start-up work (finding its descriptor) is paid once per kChunk.
+#ifndef ZERO_GATHER_VECS
+#define ZERO_GATHER_VECS 1
+#endif
+constexpr int kVecs = ZERO_GATHER_VECS;
+constexpr int64_t kRow = int64_t(kThreads) * kLane;     // elements per pass
+constexpr int64_t kChunk = kRow * kVecs;                // elements per workgroup
 
 template <int E> struct LaneBits;
 template <> struct LaneBits<8> { typedef zero::dev::u32x4 T; };
@@ -47,6 +59,7 @@ struct SegBatch {
     int64_t first_block[kSegs + 1];   // workgroups [first_block[s], first_block[s+1]) copy segment s
     int32_t n;
 };
+static_assert(sizeof(SegBatch) <= 4096, "kernel arguments are limited to 4 KB");
 
 __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
     typedef typename LaneBits<kLane>::T V;
@@ -61,11 +74,15 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
     const int64_t len = b.len[s] - start < kChunk ? b.len[s] - start : kChunk;
     uint16_t* dst = b.dst[s] + start;
     if (b.src[s] == nullptr) {                        // padding: fill with +0
-        const int64_t i = threadIdx.x;
-        if (i * kLane + kLane <= len && (reinterpret_cast<uintptr_t>(dst) & (2 * kLane - 1)) == 0) {
-            zero::dev::st_stream(reinterpret_cast<V*>(dst) + i, V{});
-        } else {
-            for (int64_t e = i * kLane; e < len && e < i * kLane + kLane; ++e) dst[e] = 0;
+        const bool aligned = (reinterpret_cast<uintptr_t>(dst) & (2 * kLane - 1)) == 0;
+#pragma unroll
+        for (int v = 0; v < kVecs; ++v) {
+            const int64_t i = int64_t(v) * kThreads + threadIdx.x;
+            if (aligned && i * kLane + kLane <= len) {
+                zero::dev::st_stream(reinterpret_cast<V*>(dst) + i, V{});
+            } else {
+                for (int64_t e = i * kLane; e < len && e < i * kLane + kLane; ++e) dst[e] = 0;
+            }
         }
         return;
     }
@@ -80,12 +97,126 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
         const int64_t body = (len - head) / kLane;
         const V* sv = reinterpret_cast<const V*>(src + head);
         V* dv = reinterpret_cast<V*>(dst + head);
-        const int64_t i = threadIdx.x;
-        if (i < body) zero::dev::st_stream(dv + i, zero::dev::ld_stream(sv + i));
+        V vals[kVecs];
+#pragma unroll
+        for (int v = 0; v < kVecs; ++v) {            // all loads first, then all stores
+            const int64_t i = int64_t(v) * kThreads + threadIdx.x;
+            if (i < body) vals[v] = zero::dev::ld_stream(sv + i);
+        }
+#pragma unroll
+        for (int v = 0; v < kVecs; ++v) {
+            const int64_t i = int64_t(v) * kThreads + threadIdx.x;
+            if (i < body) zero::dev::st_stream(dv + i, vals[v]);
+        }
         const int64_t t = head + body * kLane + threadIdx.x;
         if (t < len) dst[t] = src[t];
     } else {
         for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+    }
+}
+
+// Tensor-major gather: one descriptor per tensor instead of one per segment.
+// Element e of tensor t sits at g = e (+ the tensor's flat offset, flat plans)
+// of a rank-major sequence in which rank r holds [r*chunk_t, (r+1)*chunk_t);
+// it is read from shards[r] + (Shard(0): the chunk's start in a rank's
+// buffer) + (g - r*chunk_t). Flat plans: chunk_t = S. Shard(0) plans:
+// chunk_t = (rows per chunk) * (elements per row). A workgroup copies kChunk
+// elements of one tensor. It finds the rank of its first element once (a
+// double-precision reciprocal multiply, corrected to the exact quotient); when
+// chunk_t >= kChunk its lanes then lie in that rank or the next, two
+// workgroup-uniform shard pointers. Smaller chunks take a per-lane path.
+constexpr int kMaxRanks = 64;                   // shard pointer table in the kernel arguments
+constexpr int kTens = 72;                       // tensors per launch
+
+struct TensorBatch {
+    const uint16_t* shards[kMaxRanks];
+    uint16_t* dst[kTens];
+    int64_t numel[kTens];
+    int64_t chunk[kTens];
+    int64_t off[kTens];          // flat: the tensor's flat offset; Shard(0): its chunk start in a shard
+    double inv_chunk[kTens];     // 1.0 / chunk, rounded
+    int64_t first_block[kTens + 1];
+    int32_t n;
+    int32_t flat;                // 1: flat plan, 0: Shard(0) plan
+};
+static_assert(sizeof(TensorBatch) <= 4096, "kernel arguments are limited to 4 KB");
+
+__global__ __launch_bounds__(kThreads) void gather_tensor_kernel(TensorBatch b) {
+    typedef typename LaneBits<kLane>::T V;
+    const int64_t blk = blockIdx.x;
+    int lo = 0, hi = b.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
+    }
+    const int t = lo;
+    const int64_t e0 = (blk - b.first_block[t]) * kChunk;        // workgroup's first element
+    const int64_t numel = b.numel[t], chunk = b.chunk[t];
+    const int64_t g0 = b.flat ? b.off[t] + e0 : e0;
+    const int64_t soff = b.flat ? 0 : b.off[t];
+    // r0 = floor(g0 / chunk): g0 < 2^53, so the estimate is off by at most one.
+    int64_t q = static_cast<int64_t>(static_cast<double>(g0) * b.inv_chunk[t]);
+    int64_t rem = g0 - q * chunk;
+    if (rem < 0) { --q; rem += chunk; }
+    if (rem >= chunk) { ++q; rem -= chunk; }
+    const int r0 = __builtin_amdgcn_readfirstlane(static_cast<int>(q));
+    const int64_t local0 = rem;
+    uint16_t* dst = b.dst[t];
+    if (chunk >= kChunk) {
+        // local < chunk + kChunk <= 2 * chunk: rank r0, or r0 + 1 past the boundary.
+        const uint16_t* p0 = b.shards[r0] + soff;
+        const uint16_t* p1 = (r0 + 1 < kMaxRanks ? b.shards[r0 + 1] : b.shards[r0]) + soff;
+        V vals[kVecs];
+        bool fast[kVecs];
+#pragma unroll
+        for (int v = 0; v < kVecs; ++v) {            // all loads first, then all stores
+            const int64_t j = (int64_t(v) * kThreads + threadIdx.x) * kLane;
+            const int64_t e = e0 + j, local = local0 + j;
+            const bool next = local >= chunk;
+            const int64_t l = next ? local - chunk : local;
+            const uint16_t* src = (next ? p1 : p0) + l;
+            fast[v] = e + kLane <= numel && l + kLane <= chunk &&
+                      ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst + e)) &
+                       (2 * kLane - 1)) == 0;
+            if (fast[v]) vals[v] = zero::dev::ld_stream(reinterpret_cast<const V*>(src));
+        }
+#pragma unroll
+        for (int v = 0; v < kVecs; ++v) {
+            const int64_t j = (int64_t(v) * kThreads + threadIdx.x) * kLane;
+            const int64_t e = e0 + j, local = local0 + j;
+            if (fast[v]) {
+                zero::dev::st_stream(reinterpret_cast<V*>(dst + e), vals[v]);
+                continue;
+            }
+            // Straddles the boundary, misaligned, or the tensor's tail.
+            for (int k = 0; k < kLane && e + k < numel; ++k) {
+                const int64_t lk = local + k;
+                dst[e + k] = lk < chunk ? p0[lk] : p1[lk - chunk];
+            }
+        }
+        return;
+    }
+    // Small chunks: local < chunk + kChunk < 2 * kChunk, so 32-bit division,
+    // per lane; a lane's elements may lie in several ranks.
+    const uint32_t c32 = static_cast<uint32_t>(chunk);
+    for (int v = 0; v < kVecs; ++v) {
+        const int64_t j = (int64_t(v) * kThreads + threadIdx.x) * kLane;
+        const int64_t e = e0 + j;
+        if (e >= numel) break;
+        const uint32_t lj = static_cast<uint32_t>(local0 + j);
+        const uint32_t qj = lj / c32;
+        const uint32_t within = lj - qj * c32;
+        const uint16_t* src = b.shards[r0 + static_cast<int>(qj)] + soff + within;
+        if (e + kLane <= numel && within + kLane <= c32 &&
+            ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst + e)) & (2 * kLane - 1)) == 0) {
+            zero::dev::st_stream(reinterpret_cast<V*>(dst + e), zero::dev::ld_stream(reinterpret_cast<const V*>(src)));
+            continue;
+        }
+        for (int k = 0; k < kLane && e + k < numel; ++k) {
+            const uint32_t lk = lj + static_cast<uint32_t>(k);
+            const uint32_t qk = lk / c32;
+            dst[e + k] = b.shards[r0 + static_cast<int>(qk)][soff + (lk - qk * c32)];
+        }
     }
 }
 
@@ -143,7 +274,55 @@ zero_status check_tensors(const zero_plan* plan, const uint16_t* const* tensors,
     return ZERO_OK;
 }
 
+// One launch per kTens tensors. Each tensor: its descriptor (flat plans: the
+// tensor's flat offset, S, 0; Shard(0) plans: 0, its chunk length, its chunk
+// start in a rank's buffer).
+zero_status launch_tensors(const zero_plan* plan, const uint16_t* const* shards,
+                           uint16_t* const* tensors, hipStream_t stream) {
+    TensorBatch batch{};
+    for (int32_t r = 0; r < plan->n_ranks; ++r) batch.shards[r] = shards[r];
+    const bool shard0 = plan->kind == 1;
+    batch.flat = shard0 ? 0 : 1;
+    auto flush = [&]() -> zero_status {
+        if (batch.n == 0) return ZERO_OK;
+        const int64_t blocks = batch.first_block[batch.n];
+        hipLaunchKernelGGL(gather_tensor_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                           0, stream, batch);
+        batch.n = 0;
+        batch.first_block[0] = 0;
+        return zero::check_hip(hipGetLastError(), "zero_gather_params launch");
+    };
+    for (size_t t = 0; t < plan->numels.size(); ++t) {
+        const int64_t n = plan->numels[t];
+        if (n <= 0) continue;
+        const int64_t blocks = (n + kChunk - 1) / kChunk;
+        if (batch.first_block[batch.n] + blocks > 0x7FFFFFFF) {
+            const zero_status st = flush();
+            if (st != ZERO_OK) return st;
+        }
+        const int i = batch.n;
+        batch.dst[i] = tensors[t];
+        batch.numel[i] = n;
+        batch.chunk[i] = shard0 ? plan->chunk_elems[t] : plan->shard;
+        batch.off[i] = plan->offsets[t];
+        batch.inv_chunk[i] = 1.0 / static_cast<double>(batch.chunk[i]);
+        batch.first_block[i + 1] = batch.first_block[i] + blocks;
+        batch.n = i + 1;
+        if (batch.n == kTens) {
+            const zero_status st = flush();
+            if (st != ZERO_OK) return st;
+        }
+    }
+    return flush();
+}
+
 }  // namespace
+
+// Which gather serves which plan: 0 segment copies for all, 1 tensor-major
+// for Shard(0) plans, 2 tensor-major for all (both up to kMaxRanks ranks).
+#ifndef ZERO_GATHER_TENSOR_MAJOR
+#define ZERO_GATHER_TENSOR_MAJOR 1
+#endif
 
 extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* shards,
                                           uint16_t* const* tensors, hipStream_t stream) {
@@ -156,6 +335,10 @@ extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t*
     for (int32_t r = 0; r < plan->n_ranks; ++r)
         if (plan->shard > 0 && shards[r] == nullptr)
             return fail(ZERO_EINVAL, "zero_gather_params: NULL shard " + std::to_string(r));
+    // (The rank estimate in double precision is exact to within one below 2^52.)
+    if (plan->n_ranks <= kMaxRanks && plan->shard > 0 && plan->padded < (int64_t(1) << 52) &&
+        (ZERO_GATHER_TENSOR_MAJOR == 2 || (ZERO_GATHER_TENSOR_MAJOR == 1 && plan->kind == 1)))
+        return launch_tensors(plan, shards, tensors, stream);
     std::vector<Piece> pieces;
     pieces.reserve(plan->all.size());
     for (const zero_segment& seg : plan->all)

@@ -16,6 +16,7 @@ struct zero_plan {
     int64_t shard = 0;    // S
     std::vector<int64_t> numels;
     std::vector<int64_t> offsets;   // flat: tensor start; Shard(0): chunk start within a shard
+    std::vector<int64_t> chunk_elems;   // Shard(0): elements per full rank chunk (rows * row length)
     std::vector<std::vector<zero_segment>> by_rank;   // segments of each rank, flat order
     std::vector<zero_segment> all;                    // every segment, flat order
 };

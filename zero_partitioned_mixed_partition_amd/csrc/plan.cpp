@@ -135,6 +135,7 @@ extern "C" zero_status zero_partition_plan_shard0(const int64_t* numels, const i
             chunk_rows[static_cast<size_t>(t)] = rows;
             inner[static_cast<size_t>(t)] = in;
             plan->offsets[static_cast<size_t>(t)] = buf;
+            plan->chunk_elems.push_back(rows * in);
             buf += rows * in;
         }
         const int64_t s = (buf + align_elems - 1) / align_elems * align_elems;
