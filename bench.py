@@ -422,6 +422,28 @@ ADAMW_SOURCES = [os.path.join(ROOT, "zero_partitioned_mixed_partition_amd", "csr
                  for f in ("adamw.hip", "device_common.hpp")]
 
 
+def adamw_flushed(wl, reps: int):
+    """AdamW launch time (us) with HBM-side caches cold: before each timed
+    launch, 1 GiB is written (four times the 256 MB Infinity Cache), then the
+    AdamW phase alone runs between two events. Returns median and min."""
+    import torch
+    fn = dict(wl.phases)["adamw"]
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=wl.device)
+    times = []
+    for k in range(reps):
+        scratch.fill_(float(k))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3 / wl.adamw_launches)
+    del scratch
+    times.sort()
+    return {"median_us": times[len(times) // 2], "min_us": times[0], "launches": reps}
+
+
 def kernel_source_digest() -> str:
     import hashlib
     h = hashlib.sha256()
@@ -567,7 +589,8 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / steps
-    adamw_ms = sum(a.elapsed_time(b) for a, b in adamw_ev) / len(adamw_ev) / wl.adamw_launches
+    adamw_each = sorted(a.elapsed_time(b) / wl.adamw_launches for a, b in adamw_ev)
+    adamw_ms = sum(adamw_each) / len(adamw_each)
     print(f"[bench] {steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s), "
           f"adamw {adamw_ms * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
 
@@ -599,6 +622,7 @@ def main(argv=None):
     value = wl.elems_per_step / (ms_per_step * 1e-3)
 
     parts = wl.offload_parts(max(3, min(steps, 10))) if offload else None
+    flushed = None if offload else adamw_flushed(wl, 10)
     gc.enable()
     cpu = None
     if args.cpu_baseline_seconds > 0:
@@ -622,6 +646,11 @@ def main(argv=None):
                    "shard_elems": wl.S, "n_ranks": wl.n_ranks, "replicas": wl.replicas,
                    "parallelism": "one GPU's share of a dp job"},
         "adamw_params_per_s": elems_per_launch / (adamw_ms * 1e-3),
+        "adamw_event_us": {"mean": adamw_ms * 1e3, "median": adamw_each[len(adamw_each) // 2] * 1e3,
+                           "min": adamw_each[0] * 1e3, "launches": len(adamw_each)},
+        "adamw_flushed": flushed and dict(flushed, gbs=adamw_bytes / (flushed["median_us"] * 1e-6) / 1e9,
+                                          frac_of_hbm_peak=adamw_bytes / (flushed["median_us"] * 1e-6)
+                                          / 1e9 / HBM_PEAK_GBS),
         "adamw_hbm_gbs": adamw_gbs,
         "adamw_frac_of_hbm_peak": adamw_gbs / HBM_PEAK_GBS,
         "step_hbm_gbs": sum(bpp[n] for n, _ in wl.phases) / (ms_per_step * 1e-3) / 1e9,
