@@ -88,6 +88,8 @@ class HostPool {
         static HostPool pool(affinity_cpus());
         return pool;
     }
+    // Threads that can run tasks at the same time (the workers and the caller).
+    int concurrency() const { return static_cast<int>(workers_.size()) + 1; }
     void run(int tasks, const std::function<void(int)>& fn) {
         std::lock_guard<std::mutex> serial(run_mu_);
         if (tasks <= 1 || workers_.empty()) {
@@ -241,6 +243,92 @@ zero_status copy_streams(CopyStreams* out) {
     return ZERO_OK;
 }
 
+// The offload pipeline as dataflow, one pool run per call. Worker w owns
+// slice w of every chunk and walks the chunks in order: it waits until the
+// chunk's gradients have landed in their staging slot (and, from chunk 2 on,
+// until the parameters of the chunk two back have left the parameter slot it
+// is about to fill), updates its slice, and counts the chunk done. The worker
+// that completes a chunk queues that chunk's parameter copy, and the gradient
+// copy of the chunk two ahead into the slot just freed. Nothing joins the
+// workers between chunks; a worker blocks only on data that has not arrived.
+struct Pipeline {
+    int64_t n = 0, chunk = 0, chunks = 0;
+    int tasks = 1;
+    float *p = nullptr, *m = nullptr, *v = nullptr;
+    const uint16_t* d_grad = nullptr;
+    uint16_t* d_param = nullptr;
+    uint16_t* gstage[2] = {nullptr, nullptr};
+    uint16_t* pstage[2] = {nullptr, nullptr};
+    hipStream_t d2h = nullptr, h2d = nullptr;
+    hipEvent_t ev_in[2] = {nullptr, nullptr}, ev_out[2] = {nullptr, nullptr};
+    HostScalars c{};
+    std::mutex mu;                      // guards everything below
+    std::condition_variable cv;
+    std::vector<int> done;              // workers finished, per chunk
+    std::vector<uint8_t> in_queued;     // gradient copy and its event queued, per chunk
+    std::vector<uint8_t> out_queued;    // parameter copy and its event queued, per chunk
+    zero_status status = ZERO_OK;       // first failure; every worker stops on it
+
+    int64_t len(int64_t k) const { return n - k * chunk < chunk ? n - k * chunk : chunk; }
+
+    // Called with mu held (or before the workers start).
+    void queue_in(int64_t k) {
+        if (status != ZERO_OK) return;
+        const int s = static_cast<int>(k % 2);
+        hipError_t e = hipMemcpyAsync(gstage[s], d_grad + k * chunk, len(k) * sizeof(uint16_t),
+                                      hipMemcpyDeviceToHost, d2h);
+        if (e == hipSuccess) e = hipEventRecord(ev_in[s], d2h);
+        if (e != hipSuccess) {
+            status = zero::check_hip(e, "zero_offload_adamw_step: grad copy");
+            return;
+        }
+        in_queued[static_cast<size_t>(k)] = 1;
+    }
+    void fail_with(hipError_t e, const char* what) {
+        std::lock_guard<std::mutex> lock(mu);
+        if (status == ZERO_OK) status = zero::check_hip(e, what);
+        cv.notify_all();
+    }
+
+    void worker(int w) {
+        for (int64_t k = 0; k < chunks; ++k) {
+            const int s = static_cast<int>(k % 2);
+            {
+                std::unique_lock<std::mutex> lock(mu);
+                cv.wait(lock, [&] {
+                    return status != ZERO_OK ||
+                           (in_queued[static_cast<size_t>(k)] && (k < 2 || out_queued[static_cast<size_t>(k - 2)]));
+                });
+                if (status != ZERO_OK) return;
+            }
+            hipError_t e = hipEventSynchronize(ev_in[s]);
+            if (e == hipSuccess && k >= 2) e = hipEventSynchronize(ev_out[s]);
+            if (e != hipSuccess) return fail_with(e, "zero_offload_adamw_step: copy wait");
+            const int64_t off = k * chunk, lk = len(k);
+            // 64-element pieces keep every slice's start on a cache line of each array.
+            const int64_t per = ((lk + tasks - 1) / tasks + 63) / 64 * 64;
+            const int64_t lo = w * per;
+            if (lo < lk) {
+                const int64_t cnt = lk - lo < per ? lk - lo : per;
+                host_adamw_range(p + off + lo, m + off + lo, v + off + lo, gstage[s] + lo,
+                                 pstage[s] + lo, cnt, c);
+            }
+            std::lock_guard<std::mutex> lock(mu);
+            if (++done[static_cast<size_t>(k)] < tasks) continue;
+            if (status != ZERO_OK) return;
+            e = hipMemcpyAsync(d_param + off, pstage[s], lk * sizeof(uint16_t), hipMemcpyHostToDevice, h2d);
+            if (e == hipSuccess) e = hipEventRecord(ev_out[s], h2d);
+            if (e != hipSuccess) {
+                status = zero::check_hip(e, "zero_offload_adamw_step: param copy");
+            } else {
+                out_queued[static_cast<size_t>(k)] = 1;
+                if (k + 2 < chunks) queue_in(k + 2);
+            }
+            cv.notify_all();
+        }
+    }
+};
+
 }  // namespace
 
 extern "C" zero_status zero_host_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
@@ -325,31 +413,41 @@ extern "C" zero_status zero_offload_adamw_step(float* h_master, float* h_exp_avg
         if (!std::isfinite(clip)) return finish(ZERO_OK);   // a non-finite norm skips the step
         c.clip = clip;
     }
-    // Staging: two gradient slots and two parameter slots of `chunk` elements.
-    // Chunk k's gradients land in slot k%2 while chunk k-1 is updated; chunk k's
-    // parameters leave from slot k%2 while chunk k+1 is updated.
-    uint16_t* gstage[2] = {h_staging, h_staging + chunk};
-    uint16_t* pstage[2] = {h_staging + 2 * chunk, h_staging + 3 * chunk};
-    const int64_t chunks = (n + chunk - 1) / chunk;
-    for (int64_t k = 0; k <= chunks; ++k) {
-        if (k < chunks) {                       // chunk k's gradients start to travel
-            const int64_t off = k * chunk, len = n - off < chunk ? n - off : chunk;
-            ZERO_TRY(hipMemcpyAsync(gstage[k % 2], d_grad + off, len * sizeof(uint16_t),
-                                    hipMemcpyDeviceToHost, cs.d2h), "grad copy");
-            ZERO_TRY(hipEventRecord(ev_in[k % 2], cs.d2h), "record");
-        }
-        if (k == 0) continue;
-        const int64_t j = k - 1;                // chunk j is updated on the host now
-        const int slot = static_cast<int>(j % 2);
-        const int64_t off = j * chunk, len = n - off < chunk ? n - off : chunk;
-        ZERO_TRY(hipEventSynchronize(ev_in[slot]), "grad wait");
-        if (j >= 2) ZERO_TRY(hipEventSynchronize(ev_out[slot]), "param wait");
-        host_adamw_parallel(h_master + off, h_exp_avg + off, h_exp_avg_sq + off, gstage[slot],
-                            pstage[slot], len, c, threads);
-        ZERO_TRY(hipMemcpyAsync(d_param_out + off, pstage[slot], len * sizeof(uint16_t),
-                                hipMemcpyHostToDevice, cs.h2d), "param copy");
-        ZERO_TRY(hipEventRecord(ev_out[slot], cs.h2d), "record");
+    // Staging: two gradient slots and two parameter slots of `chunk` elements;
+    // chunk k uses slot k % 2 of each.
+    Pipeline pl;
+    pl.n = n;
+    pl.chunk = chunk;
+    pl.chunks = (n + chunk - 1) / chunk;
+    pl.tasks = threads < HostPool::get().concurrency() ? threads : HostPool::get().concurrency();
+    if (n < (int64_t(1) << 16)) pl.tasks = 1;
+    pl.p = h_master;
+    pl.m = h_exp_avg;
+    pl.v = h_exp_avg_sq;
+    pl.d_grad = d_grad;
+    pl.d_param = d_param_out;
+    pl.gstage[0] = h_staging;
+    pl.gstage[1] = h_staging + chunk;
+    pl.pstage[0] = h_staging + 2 * chunk;
+    pl.pstage[1] = h_staging + 3 * chunk;
+    pl.d2h = cs.d2h;
+    pl.h2d = cs.h2d;
+    for (int i = 0; i < 2; ++i) {
+        pl.ev_in[i] = ev_in[i];
+        pl.ev_out[i] = ev_out[i];
     }
+    pl.c = c;
+    try {
+        pl.done.assign(static_cast<size_t>(pl.chunks), 0);
+        pl.in_queued.assign(static_cast<size_t>(pl.chunks), 0);
+        pl.out_queued.assign(static_cast<size_t>(pl.chunks), 0);
+    } catch (const std::bad_alloc&) {
+        return finish(fail(ZERO_ENOMEM, "zero_offload_adamw_step: allocation failed"));
+    }
+    pl.queue_in(0);
+    if (pl.chunks > 1) pl.queue_in(1);
+    if (pl.status == ZERO_OK) HostPool::get().run(pl.tasks, [&pl](int w) { pl.worker(w); });
+    if (pl.status != ZERO_OK) return finish(pl.status);
     // Later work on `stream` sees the new parameters.
     ZERO_TRY(hipEventRecord(start, cs.h2d), "record");
     ZERO_TRY(hipStreamWaitEvent(stream, start, 0), "wait");
