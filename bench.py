@@ -113,11 +113,18 @@ class RankWorkload:
         self.hyper = Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                            weight_decay=w.weight_decay)
         spans = bucket_windows(P, bucket, lo, lo + S) if reps else []
+        self.offload = name.endswith("-offload")
+        self.n_threads = len(os.sched_getaffinity(0))
         self.rs = RankStep(self.plan, rank, len(spans), self.hyper, self.max_norm, device,
-                           gather=gather)
+                           gather=gather, offload=self.offload, offload_chunk=OFFLOAD_CHUNK,
+                           host_threads=self.n_threads)
         rs = self.rs
-        synth.device_normal_f32(rs.master, self.seed, synth.KIND_MASTER, 0, 0, lo,
-                                phi if layout == "flat" else P, synth.MASTER_SIGMA)
+        if self.offload:         # the fp32 master lives in host memory
+            rs.master.copy_(torch.from_numpy(synth.normal_f32(S, self.seed, synth.KIND_MASTER, 0, 0,
+                                                              lo, phi, synth.MASTER_SIGMA)))
+        else:
+            synth.device_normal_f32(rs.master, self.seed, synth.KIND_MASTER, 0, 0, lo,
+                                    phi if layout == "flat" else P, synth.MASTER_SIGMA)
         if layout == "shard0":       # padding inside the coalesced buffer starts at zero
             rs.master.mul_(padding_mask(self.plan, rank).to(device))
         if gather:
@@ -186,33 +193,6 @@ class RankWorkload:
             self.phases.append(("gather", rs.gather))
         self.adamw_launches = 1
         self.elems_per_step = S
-        self.offload = name.endswith("-offload")
-        if self.offload:
-            self._setup_offload(device)
-
-    def _setup_offload(self, device):
-        """Move the fp32 state to host DRAM and swap the AdamW phase for the
-        offload pipeline (device gradients in, host update, device params out)."""
-        import torch
-
-        from zero_partitioned_mixed_partition_amd import _binding as zb
-        rs = self.rs
-        self.h_master = rs.master.cpu()
-        self.h_m = torch.zeros(self.S, dtype=torch.float32)
-        self.h_v = torch.zeros(self.S, dtype=torch.float32)
-        self.staging = torch.empty(4 * OFFLOAD_CHUNK, dtype=torch.int16).pin_memory()
-        self.n_threads = len(os.sched_getaffinity(0))
-        st = torch.cuda.current_stream(device).cuda_stream
-        call = zb.prepare_offload_adamw_step(self.h_master, self.h_m, self.h_v, rs.grad,
-                                             rs.param_shards[self.rank], self.staging,
-                                             clip_scale=rs.scale, stream=st,
-                                             n_threads=self.n_threads, **self.hyper.as_kwargs())
-        self.t = 0
-
-        def offload_adamw():
-            self.t += 1
-            call(self.t)
-        self.phases = [(n, offload_adamw if n == "adamw" else fn) for n, fn in self.phases]
         torch.cuda.synchronize()
 
     def offload_parts(self, reps: int):
@@ -222,9 +202,9 @@ class RankWorkload:
         import torch
 
         import zero_partitioned_mixed_partition_amd as zm
-        p, m, v = self.h_master.clone(), self.h_m.clone(), self.h_v.clone()
-        g = torch.empty(self.S, dtype=torch.int16)
-        g.copy_(self.rs.grad.cpu())
+        rs = self.rs
+        p, m, v = rs.master.clone(), rs.exp_avg.clone(), rs.exp_avg_sq.clone()
+        g = rs.grad.cpu()
         out = torch.empty(self.S, dtype=torch.int16)
         hp = self.hyper.as_kwargs()
         zm.zero_host_adamw_step(p, m, v, g, out, 1, n_threads=self.n_threads, **hp)
@@ -233,18 +213,17 @@ class RankWorkload:
             zm.zero_host_adamw_step(p, m, v, g, out, 2 + k, n_threads=self.n_threads, **hp)
         host_ms = (time.perf_counter() - t0) * 1e3 / reps
         pin = torch.empty(self.S, dtype=torch.int16).pin_memory()
-        dev = self.rs.grad
-        pin.copy_(dev, non_blocking=True)
+        pin.copy_(rs.grad, non_blocking=True)
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         c = torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
-            pin.copy_(dev, non_blocking=True)
+            pin.copy_(rs.grad, non_blocking=True)
         b.record()
         for _ in range(reps):
-            self.rs.param_shards[self.rank].copy_(pin, non_blocking=True)
+            rs.param_shards[self.rank].copy_(pin, non_blocking=True)
         c.record()
         torch.cuda.synchronize()
         d2h, h2d = a.elapsed_time(b) / reps, b.elapsed_time(c) / reps

@@ -191,11 +191,10 @@ def test_bench_pipeline_matches_oracle(zm, name):
     assert (np.abs(got_parts[others] - want_parts[others]) <= 1e-12 * want_parts[others]).all()
     got_scale = np.float32(setup.rs.scale.item())
     assert abs(int(got_scale.view(np.int32)) - int(np.float32(out["clip"]).view(np.int32))) <= 1
-    if setup.offload:     # the fp32 state lives in host memory
-        held = ((setup.h_master, "master"), (setup.h_m, "exp_avg"), (setup.h_v, "exp_avg_sq"))
-    else:
-        held = ((setup.rs.master, "master"), (setup.rs.exp_avg, "exp_avg"),
-                (setup.rs.exp_avg_sq, "exp_avg_sq"))
+    # (with the offload the fp32 state is in host memory; host_f32 reads either)
+    held = ((setup.rs.master, "master"), (setup.rs.exp_avg, "exp_avg"),
+            (setup.rs.exp_avg_sq, "exp_avg_sq"))
+    assert setup.rs.master.is_cuda != setup.offload
     for got, key in held:
         exact = assert_f32_close(host_f32(got), state[key], key)
         note(f"bench pipeline {name}: {key} bit-identical fraction {exact:.6f}")

@@ -47,21 +47,37 @@ class RankStep:
     n_windows    gradient windows reduced per step (1 for a whole flat buffer,
                  the number of buckets that meet the shard otherwise).
     max_norm     clip threshold (<= 0: no clipping).
+    offload      ZeRO-Offload ("ZeRO-Offload Mechanics"): the fp32 master, m and
+                 v live in host memory (CPU tensors) and the update runs on the
+                 host through zero_offload_adamw_step, with `offload_chunk`
+                 elements per pinned staging slot and `host_threads` workers
+                 (0: one per CPU this process may use). Reduce, clip and gather
+                 stay on the device.
     """
 
     def __init__(self, plan: zb.Plan, rank: int, n_windows: int, hyper: Hyper, max_norm: float,
-                 device: torch.device, gather: bool = True):
+                 device: torch.device, gather: bool = True, offload: bool = False,
+                 offload_chunk: int = 1 << 20, host_threads: int = 0):
         self.plan, self.rank, self.hyper, self.max_norm = plan, rank, hyper, max_norm
         self.device = device
+        self.offload, self.host_threads = offload, host_threads
         s, nd = plan.shard_numel, plan.num_ranks
-        # The five arrays the AdamW kernel streams live in one arena, each start
+        # The arrays the AdamW kernel streams live in one arena, each start
         # moved STAGGER bytes past the previous end: arrays whose bases differ
         # by multiples of large powers of two meet the same HBM channels at the
         # same time; the stagger was measured to add ~4% bandwidth on MI355X.
-        views, self.arena = _staggered_arena(
-            [(s, torch.float32), (s, torch.float32), (s, torch.float32), (s, torch.int16),
-             (s, torch.int16)], device)
-        self.master, self.exp_avg, self.exp_avg_sq, self.grad, own_param = views
+        if offload:
+            views, self.arena = _staggered_arena([(s, torch.int16), (s, torch.int16)], device)
+            self.grad, own_param = views
+            self.master = torch.zeros(s, dtype=torch.float32)
+            self.exp_avg = torch.zeros(s, dtype=torch.float32)
+            self.exp_avg_sq = torch.zeros(s, dtype=torch.float32)
+            self.staging = torch.empty(4 * max(int(offload_chunk), 1), dtype=torch.int16).pin_memory()
+        else:
+            views, self.arena = _staggered_arena(
+                [(s, torch.float32), (s, torch.float32), (s, torch.float32), (s, torch.int16),
+                 (s, torch.int16)], device)
+            self.master, self.exp_avg, self.exp_avg_sq, self.grad, own_param = views
         # per-rank partials [0, N_d) (own slot left 0), then one per own window
         self.partials = torch.zeros(nd + n_windows, dtype=torch.float64, device=device)
         self.scale = torch.ones(1, dtype=torch.float32, device=device)
@@ -112,10 +128,16 @@ class RankStep:
 
     def adamw(self, stream=None):
         self.t += 1
+        clip = self.scale if self.max_norm > 0 else None
+        if self.offload:        # returns once the host update is done; `stream` orders the copies
+            self._prepared("adamw", stream, lambda st: zb.prepare_offload_adamw_step(
+                self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
+                self.staging, clip_scale=clip, stream=st, n_threads=self.host_threads,
+                **self.hyper.as_kwargs()))(self.t)
+            return
         self._prepared("adamw", stream, lambda st: zb.prepare_shard_adamw_step(
             self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
-            clip_scale=self.scale if self.max_norm > 0 else None, stream=st,
-            **self.hyper.as_kwargs()))(self.t)
+            clip_scale=clip, stream=st, **self.hyper.as_kwargs()))(self.t)
 
     def gather(self, stream=None):
         if self.tensors:
