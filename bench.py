@@ -50,7 +50,7 @@ METRIC = "shard AdamW step: params/sec and achieved HBM GB/s (% of MI355X peak)"
 WORKLOAD_NAMES = ["gpt2-small", "llama3-8b", "llama3-70b", "gpt-1.3b", "gpt2-small-fsdp2",
                   "gpt2-small-offload"]
 PCIE_PEAK_GBS = 128.0          # PCIe 5.0 x16, both directions together (64 GB/s each way)
-OFFLOAD_CHUNK = 1 << 20        # elements per staging slot of the offload pipeline
+OFFLOAD_CHUNK = 1 << 21        # elements per staging slot of the offload pipeline
 
 
 def parse_args(argv=None):

@@ -57,7 +57,7 @@ class RankStep:
 
     def __init__(self, plan: zb.Plan, rank: int, n_windows: int, hyper: Hyper, max_norm: float,
                  device: torch.device, gather: bool = True, offload: bool = False,
-                 offload_chunk: int = 1 << 20, host_threads: int = 0):
+                 offload_chunk: int = 1 << 21, host_threads: int = 0):
         self.plan, self.rank, self.hyper, self.max_norm = plan, rank, hyper, max_norm
         self.device = device
         self.offload, self.host_threads = offload, host_threads
