@@ -32,7 +32,8 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSegs = 96;                       // segments per launch (kernarg ~3.1 KB of the 4 KB limit)
+constexpr int kSegs = 160;                      // segments per launch (kernarg ~3.8 KB of the 4 KB limit)
+constexpr int64_t kMaxPiece = int64_t(1) << 30; // longer pieces are split: lengths fit 32 bits
 // One access per lane: ZERO_GATHER_LANE_ELEMS bf16 values (8 = 16 bytes).
 #ifndef ZERO_GATHER_LANE_ELEMS
 #define ZERO_GATHER_LANE_ELEMS 8
@@ -55,8 +56,8 @@ template <> struct LaneBits<2> { typedef uint32_t T; };
 struct SegBatch {
     const uint16_t* src[kSegs];
     uint16_t* dst[kSegs];
-    int64_t len[kSegs];
-    int64_t first_block[kSegs + 1];   // workgroups [first_block[s], first_block[s+1]) copy segment s
+    int32_t len[kSegs];               // elements, at most kMaxPiece
+    int32_t first_block[kSegs + 1];   // workgroups [first_block[s], first_block[s+1]) copy segment s
     int32_t n;
 };
 static_assert(sizeof(SegBatch) <= 4096, "kernel arguments are limited to 4 KB");
@@ -71,7 +72,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
     }
     const int s = lo;
     const int64_t start = (blk - b.first_block[s]) * kChunk;
-    const int64_t len = b.len[s] - start < kChunk ? b.len[s] - start : kChunk;
+    const int64_t seg_len = b.len[s];
+    const int64_t len = seg_len - start < kChunk ? seg_len - start : kChunk;
     uint16_t* dst = b.dst[s] + start;
     if (b.src[s] == nullptr) {                        // padding: fill with +0
         const bool aligned = (reinterpret_cast<uintptr_t>(dst) & (2 * kLane - 1)) == 0;
@@ -243,23 +245,24 @@ zero_status launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, 
         batch.first_block[0] = 0;
         return zero::check_hip(hipGetLastError(), who);
     };
-    for (const Piece& pc : pieces) {
-        if (pc.len <= 0) continue;
-        const int64_t chunks = (pc.len + kChunk - 1) / kChunk;
-        if (batch.first_block[batch.n] + chunks > 0x7FFFFFFF) {   // one grid < 2^31 workgroups
-            const zero_status st = flush();
-            if (st != ZERO_OK) return st;
-        }
-        if (chunks > 0x7FFFFFFF) return zero::fail(ZERO_ERANGE, std::string(who) + ": segment too long");
-        const int i = batch.n;
-        batch.src[i] = pc.src;
-        batch.dst[i] = pc.dst;
-        batch.len[i] = pc.len;
-        batch.first_block[i + 1] = batch.first_block[i] + chunks;
-        batch.n = i + 1;
-        if (batch.n == kSegs) {
-            const zero_status st = flush();
-            if (st != ZERO_OK) return st;
+    for (const Piece& whole : pieces) {
+        for (int64_t at = 0; at < whole.len; at += kMaxPiece) {
+            const int64_t len = whole.len - at < kMaxPiece ? whole.len - at : kMaxPiece;
+            const int64_t chunks = (len + kChunk - 1) / kChunk;
+            if (int64_t(batch.first_block[batch.n]) + chunks > 0x7FFFFFFF) {   // grid < 2^31 workgroups
+                const zero_status st = flush();
+                if (st != ZERO_OK) return st;
+            }
+            const int i = batch.n;
+            batch.src[i] = whole.src != nullptr ? whole.src + at : nullptr;
+            batch.dst[i] = whole.dst + at;
+            batch.len[i] = static_cast<int32_t>(len);
+            batch.first_block[i + 1] = batch.first_block[i] + static_cast<int32_t>(chunks);
+            batch.n = i + 1;
+            if (batch.n == kSegs) {
+                const zero_status st = flush();
+                if (st != ZERO_OK) return st;
+            }
         }
     }
     return flush();
