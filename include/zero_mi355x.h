@@ -246,7 +246,10 @@ zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_
  * [ZF] "Execution Flow for ZeRO-1", step 4 and "FSDP-1": the N_d bf16 shards,
  * concatenated in rank order, are the flat parameter buffer; tensor t is its
  * slice [offset_t, offset_t + numel_t). This copies every plan segment from
- * its shard into its tensor (padding is not copied).
+ * its shard into its tensor (padding is not copied). For a Shard(0) plan
+ * ([ZF] "FSDP-2: Per-Parameter Sharding via DTensor"), tensor t is its ranks'
+ * dim-0 chunks stacked in rank order, each read from its chunk's place in
+ * that rank's coalesced buffer.
  * shards       host [N_d] of device pointers, each to S bf16 values.
  * tensors      host [T] of device pointers, tensor t to numel_t bf16 values
  *              (may be NULL only for zero-sized tensors). Outputs must not
