@@ -309,6 +309,8 @@ zero_status zero_host_adamw_step(float* master, float* exp_avg, float* exp_avg_s
  * `stream` afterwards sees the new parameters. The copies run on two internal
  * streams of the current device (default priority). The call returns when the
  * host update is done and the staging buffers are free again, on errors too.
+ * Calls from several host threads are safe: they share the worker pool and the
+ * copy streams and so run one after another.
  * Errors: as zero_host_adamw_step; ZERO_ENOSPACE if staging_elems < 4; ZERO_EHIP. */
 zero_status zero_offload_adamw_step(float* h_master, float* h_exp_avg, float* h_exp_avg_sq,
                                     const uint16_t* d_grad, uint16_t* d_param_out,
