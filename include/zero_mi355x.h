@@ -15,6 +15,8 @@
  *   zero_grad_sqnorm        squared-norm partial of a gradient shard
  *   zero_clip_scale         global-norm clip coefficient from all partials
  *   zero_shard_adamw_step   fp32 master/m/v update and bf16 parameter emit
+ *   zero_multi_tensor_adamw_step  the same over a ragged list of tensors
+ *                           (FSDP-2's per-parameter shards)
  *   zero_gather_params      bf16 shards back to per-tensor parameters
  *                           (all-gather output layout, then un-flatten)
  *   zero_flatten_params     per-tensor bf16 buffers into the padded flat buffer
@@ -240,6 +242,26 @@ zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_
                                   int64_t step, double lr, double beta1, double beta2, double eps,
                                   double weight_decay, const float* clip_scale,
                                   hipStream_t stream);
+
+/* Multi-tensor form. [ZF] "FSDP-2: Per-Parameter Sharding via DTensor
+ * (fully_shard)": each parameter keeps its own local shard, so the rank's
+ * optimizer step runs over a ragged list of per-parameter tensors rather than
+ * one flat buffer. Tensor t has its own arrays masters[t], exp_avgs[t],
+ * exp_avg_sqs[t] (device [numels[t]] fp32, in place), grads[t] (device bf16,
+ * read only) and params_out[t] (device bf16, written; must not overlap tensor
+ * t's fp32 arrays); the pointer arrays and numels are host arrays of
+ * n_tensors entries. Every element gets zero_shard_adamw_step's arithmetic
+ * (identical bits), with one step, one set of hyperparameters and one clip
+ * coefficient for the whole list. Zero-sized tensors are skipped (their
+ * pointers may be NULL). Any pointer alignment. One launch per 72 tensors.
+ * Errors: as zero_shard_adamw_step, per tensor (ZERO_EINVAL names it);
+ * ZERO_ERANGE for a tensor of 2^39 elements or more; ZERO_EHIP. */
+zero_status zero_multi_tensor_adamw_step(float* const* masters, float* const* exp_avgs,
+                                         float* const* exp_avg_sqs, const uint16_t* const* grads,
+                                         uint16_t* const* params_out, const int64_t* numels,
+                                         int32_t n_tensors, int64_t step, double lr, double beta1,
+                                         double beta2, double eps, double weight_decay,
+                                         const float* clip_scale, hipStream_t stream);
 
 /* ------------------------------------------------------------------ gather
  *

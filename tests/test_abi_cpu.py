@@ -163,3 +163,34 @@ def test_shard0_plan_errors(zm):
     with pytest.raises(zm.ZeroError):
         zm.zero_partition_plan_shard0([10], [0], 2, 1)
     assert zm.zero_partition_plan([4], 2, 1).kind == 0
+
+
+def test_multi_tensor_adamw_rejects_bad_arguments_before_touching_the_gpu(zm):
+    lib = zm._binding
+    f = lib._mt_adamw
+    args = (1e-3, 0.9, 0.999, 1e-8, 0.0, None, None)
+    assert f(None, None, None, None, None, None, 0, 1, *args) == lib.ZERO_OK          # empty list
+    assert f(None, None, None, None, None, None, -1, 1, *args) == lib.ZERO_EINVAL     # n_tensors < 0
+    assert f(None, None, None, None, None, None, 2, 1, *args) == lib.ZERO_EINVAL      # NULL tables
+    assert f(None, None, None, None, None, None, 0, 0, *args) == lib.ZERO_EINVAL      # step < 1
+    one = (ctypes.c_void_p * 1)(None)
+    n = (ctypes.c_int64 * 1)(5)
+    assert f(one, one, one, one, one, n, 1, 1, *args) == lib.ZERO_EINVAL              # NULL arrays
+    assert "tensor 0" in zm.zero_last_error()
+    n[0] = -3
+    assert f(one, one, one, one, one, n, 1, 1, *args) == lib.ZERO_EINVAL              # numel < 0
+    n[0] = 0
+    assert f(one, one, one, one, one, n, 1, 1, *args) == lib.ZERO_OK                  # empty tensor
+
+
+def test_builder_loads_without_importing_the_package():
+    """build() must work when the in-tree library is stale or missing, so its
+    build script is loaded without importing the package (which loads the
+    library)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import __graft_entry__ as g; m = g._load_builder(); "
+            "assert callable(m.build); "
+            "assert 'zero_partitioned_mixed_partition_amd' not in sys.modules; print('ok')" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stderr

@@ -372,3 +372,73 @@ def test_gather_rank_counts_many_tensors_misaligned(zm, kind, n_ranks):
         got = host_u16(b)
         assert_bits_equal(got[1:] if i % 2 else got[:-1], w, f"tensor {i}")
         assert (got[0] if i % 2 else got[-1]) == 0x3333, "wrote outside the tensor"
+
+
+# ----------------------------------------------------------------------------- multi-tensor AdamW
+
+@pytest.mark.parametrize("seed", range(3))
+def test_multi_tensor_adamw_matches_oracle(zm, seed):
+    """A ragged list (sizes around the 256-lane workgroup, empty tensors, more
+    tensors than one launch carries, misaligned starts) against the oracle per
+    tensor, three steps, device clip coefficient; then the NaN skip."""
+    rng = np.random.default_rng(1200 + seed)
+    sizes = [int(x) for x in rng.choice([0, 1, 7, 255, 256, 257, 1000, 4099, 70_001], 90)]
+    note(f"multi-tensor AdamW: {len(sizes)} tensors, {sum(sizes)} elements")
+    off = seed % 2                                   # odd seeds: every array starts 1 element in
+
+    def dev_f32(a):
+        return to_dev_f32(np.concatenate([np.zeros(off, np.float32), a]))[off:]
+
+    def dev_u16(a):
+        return to_dev_u16(np.concatenate([np.zeros(off, np.uint16), a]))[off:]
+    P = [synth.normal_f32(n, 70 + seed, synth.KIND_MASTER, 0, 0, 0, None, 0.02) for n in sizes]
+    M = [np.zeros(n, np.float32) for n in sizes]
+    V = [np.zeros(n, np.float32) for n in sizes]
+    dp, dm, dv = [dev_f32(x) for x in P], [dev_f32(x) for x in M], [dev_f32(x) for x in V]
+    dg = [dev_u16(np.zeros(n, np.uint16)) for n in sizes]
+    do = [dev_u16(np.full(n, 0x4444, np.uint16)) for n in sizes]
+    scale = torch.tensor([0.8125], dtype=torch.float32, device=dev())
+    bits = [None] * len(sizes)
+    for t in (1, 2, 3):
+        G = [synth.normal_bf16(n, 70 + seed, synth.KIND_GRAD, t, i, 0, None, 1e-3)
+             for i, n in enumerate(sizes)]
+        for d, g in zip(dg, G):
+            d.copy_(torch.from_numpy(g.view(np.int16)))
+        zm.zero_multi_tensor_adamw_step(dp, dm, dv, dg, do, t, clip_scale=scale, **HP)
+        for i in range(len(sizes)):
+            P[i], M[i], V[i], bits[i] = oracle.adamw_step(P[i], M[i], V[i], G[i], t,
+                                                         clip=np.float32(0.8125), **HP)
+    torch.cuda.synchronize()
+    for i in range(len(sizes)):
+        assert_bits_equal(host_f32(dp[i]).view(np.uint32), P[i].view(np.uint32), f"master {i}")
+        assert_bits_equal(host_f32(dm[i]).view(np.uint32), M[i].view(np.uint32), f"exp_avg {i}")
+        assert_bits_equal(host_f32(dv[i]).view(np.uint32), V[i].view(np.uint32), f"exp_avg_sq {i}")
+        assert_bits_equal(host_u16(do[i]), bits[i], f"param {i}")
+    before = [x.clone() for x in dp]
+    zm.zero_multi_tensor_adamw_step(dp, dm, dv, dg, do, 4,
+                                    clip_scale=torch.tensor([float("nan")], device=dev()), **HP)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(before, dp))
+
+
+def test_multi_tensor_adamw_equals_the_flat_kernel_on_views(zm):
+    """Tensors that are views into one flat buffer give the flat kernel's bits."""
+    sizes = [768, 768, 2304 * 768, 2304, 3, 50_000]
+    n = sum(sizes)
+    p0 = synth.normal_f32(n, 80, synth.KIND_MASTER, 0, 0, 0, None, 0.02)
+    g = to_dev_u16(synth.normal_bf16(n, 80, synth.KIND_GRAD, 1, 0, 0, None, 1e-3))
+    flat = [to_dev_f32(p0), torch.zeros(n, device=dev()), torch.zeros(n, device=dev()),
+            torch.zeros(n, dtype=torch.int16, device=dev())]
+    multi = [to_dev_f32(p0), torch.zeros(n, device=dev()), torch.zeros(n, device=dev()),
+             torch.zeros(n, dtype=torch.int16, device=dev())]
+    offs = np.cumsum([0] + sizes)
+
+    def views(x):
+        return [x[a:b] for a, b in zip(offs[:-1], offs[1:])]
+    for t in (1, 2):
+        zm.zero_shard_adamw_step(flat[0], flat[1], flat[2], g, flat[3], t, **HP)
+        zm.zero_multi_tensor_adamw_step(views(multi[0]), views(multi[1]), views(multi[2]), views(g),
+                                        views(multi[3]), t, **HP)
+    torch.cuda.synchronize()
+    for a, b, name in zip(flat, multi, ("master", "exp_avg", "exp_avg_sq", "param")):
+        assert torch.equal(a, b), name

@@ -22,4 +22,5 @@ from ._binding import (LIB_PATH, ZERO_MAX_REPLICAS, Plan, ZeroError,  # noqa: F4
                        zero_grad_reduce_shard,
                        zero_grad_sqnorm, zero_last_error, zero_partition_plan,
                        zero_partition_plan_shard0, zero_host_adamw_step, zero_offload_adamw_step,
+                       zero_multi_tensor_adamw_step,
                        zero_shard_adamw_step, zero_sqnorm_workspace_bytes, zero_status_string)

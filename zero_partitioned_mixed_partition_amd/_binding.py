@@ -73,6 +73,9 @@ _host_adamw = _fn("zero_host_adamw_step", c_i32,
 _offload = _fn("zero_offload_adamw_step", c_i32,
                [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_dbl, c_dbl, c_dbl, c_dbl,
                 c_dbl, c_vp, c_i32, c_vp])
+_mt_adamw = _fn("zero_multi_tensor_adamw_step", c_i32,
+                [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl,
+                 c_vp, c_vp])
 _status_string = _fn("zero_status_string", ctypes.c_char_p, [c_i32])
 _last_error = _fn("zero_last_error", ctypes.c_char_p, [])
 
@@ -283,6 +286,38 @@ def zero_flatten_params(plan: Plan, tensors: Sequence, flat, stream=None) -> Non
     tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
     _check(_flatten(plan.handle, tp, _ptr(flat, 2, "flat"), _stream(stream, flat)),
            "zero_flatten_params")
+
+
+def prepare_multi_tensor_adamw_step(masters, exp_avgs, exp_avg_sqs, grads, params_out, lr: float,
+                                    beta1: float, beta2: float, eps: float, weight_decay: float,
+                                    clip_scale, stream) -> Prepared:
+    """Lists of T device tensors (fp32 state; 2-byte grads and params), tensor t
+    updated over masters[t].numel() elements. Call the result with the step."""
+    lists = (masters, exp_avgs, exp_avg_sqs, grads, params_out)
+    T = len(masters)
+    if any(len(x) != T for x in lists):
+        raise ValueError("the five lists must have the same length")
+    numels = [t.numel() for t in masters]
+    for lst in lists[1:]:
+        if any(x.numel() < n for x, n in zip(lst, numels)):
+            raise ValueError("a tensor holds fewer elements than its master")
+    tabs = []
+    for lst, size, what in zip(lists, (4, 4, 4, 2, 2), ("master", "exp_avg", "exp_avg_sq", "grad", "param")):
+        tabs.append((c_vp * max(T, 1))(*[_ptr(x, size, what) for x in lst]))
+    ns = (c_i64 * max(T, 1))(*numels)
+    st = _stream(stream, masters[0]) if T else (stream or 0)
+    p = Prepared(_mt_adamw, tabs + [ns, T, 1, lr, beta1, beta2, eps, weight_decay,
+                                    _ptr(clip_scale, 4, "clip_scale"), st],
+                 "zero_multi_tensor_adamw_step", step_index=7)
+    p._keep = (lists, tabs, ns, clip_scale)
+    return p
+
+
+def zero_multi_tensor_adamw_step(masters, exp_avgs, exp_avg_sqs, grads, params_out, step: int,
+                                 lr: float, beta1: float, beta2: float, eps: float,
+                                 weight_decay: float, clip_scale=None, stream=None) -> None:
+    prepare_multi_tensor_adamw_step(masters, exp_avgs, exp_avg_sqs, grads, params_out, lr, beta1,
+                                    beta2, eps, weight_decay, clip_scale, stream)(step)
 
 
 def _host_ptr(a, itemsize: int, what: str) -> int:

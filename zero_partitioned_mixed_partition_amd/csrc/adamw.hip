@@ -165,6 +165,40 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ mas
     }
 }
 
+// Multi-tensor form: a ragged list of tensors, each with its own five arrays,
+// in one launch per kMtTensors tensors. The descriptors travel in the kernel
+// arguments; workgroup b finds its tensor by a binary search over the
+// per-tensor workgroup prefix and updates one element per lane with the same
+// per-element code as the flat kernel (so the bits are the same).
+constexpr int kMtTensors = 72;
+
+struct MtBatch {
+    float* p[kMtTensors];
+    float* m[kMtTensors];
+    float* v[kMtTensors];
+    const uint16_t* g[kMtTensors];
+    uint16_t* o[kMtTensors];
+    int64_t n[kMtTensors];
+    int32_t first_block[kMtTensors + 1];
+    int32_t count;
+};
+static_assert(sizeof(MtBatch) <= 4096, "kernel arguments are limited to 4 KB");
+
+__global__ __launch_bounds__(kThreads) void adamw_multi_kernel(MtBatch b, AdamScalars c,
+                                                               const float* __restrict__ clip_scale) {
+    const float clip = read_clip(clip_scale);
+    if (!isfinite(clip)) return;
+    const int32_t blk = static_cast<int32_t>(blockIdx.x);
+    int lo = 0, hi = b.count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
+    }
+    const int t = lo;
+    const int64_t i = static_cast<int64_t>(blk - b.first_block[t]) * kThreads + threadIdx.x;
+    if (i < b.n[t]) Lane<1>::update(b.p[t], b.m[t], b.v[t], b.g[t], b.o[t], i, clip, c);
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool ranges_overlap(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
@@ -177,6 +211,38 @@ int64_t blocks_for(int64_t items) {
     return blocks < 1 ? 1 : blocks;
 }
 
+zero_status check_hyper(int64_t step, double lr, double beta1, double beta2, double eps,
+                        double weight_decay, const char* who) {
+    using zero::fail;
+    const std::string w(who);
+    if (step < 1) return fail(ZERO_EINVAL, w + ": step must be >= 1");
+    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
+        return fail(ZERO_EINVAL, w + ": betas must lie in [0, 1)");
+    if (!(eps > 0.0) || !std::isfinite(eps))
+        return fail(ZERO_EINVAL, w + ": eps must be finite and > 0");
+    if (!(lr >= 0.0) || !std::isfinite(lr) || !std::isfinite(weight_decay))
+        return fail(ZERO_EINVAL, w + ": lr and weight_decay must be finite, lr >= 0");
+    return ZERO_OK;
+}
+
+// Scalars in fp64, each rounded once to fp32.
+zero_status make_scalars(int64_t step, double lr, double beta1, double beta2, double weight_decay,
+                         double eps, AdamScalars* c, const char* who) {
+    const double bc1 = 1.0 - std::pow(beta1, static_cast<double>(step));
+    const double bc2 = 1.0 - std::pow(beta2, static_cast<double>(step));
+    if (!(bc1 > 0.0) || !(bc2 > 0.0))
+        return zero::fail(ZERO_EINVAL, std::string(who) + ": bias correction is zero");
+    c->beta1 = static_cast<float>(beta1);
+    c->one_minus_beta1 = static_cast<float>(1.0 - beta1);
+    c->beta2 = static_cast<float>(beta2);
+    c->one_minus_beta2 = static_cast<float>(1.0 - beta2);
+    c->eps = static_cast<float>(eps);
+    c->step_size = static_cast<float>(lr / bc1);
+    c->sqrt_bc2 = static_cast<float>(std::sqrt(bc2));
+    c->decay = static_cast<float>(1.0 - lr * weight_decay);
+    return ZERO_OK;
+}
+
 }  // namespace
 
 extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
@@ -187,13 +253,8 @@ extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, floa
     using zero::fail;
     zero::clear_error();
     if (n < 0) return fail(ZERO_EINVAL, "zero_shard_adamw_step: n < 0");
-    if (step < 1) return fail(ZERO_EINVAL, "zero_shard_adamw_step: step must be >= 1");
-    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
-        return fail(ZERO_EINVAL, "zero_shard_adamw_step: betas must lie in [0, 1)");
-    if (!(eps > 0.0) || !std::isfinite(eps))
-        return fail(ZERO_EINVAL, "zero_shard_adamw_step: eps must be finite and > 0");
-    if (!(lr >= 0.0) || !std::isfinite(lr) || !std::isfinite(weight_decay))
-        return fail(ZERO_EINVAL, "zero_shard_adamw_step: lr and weight_decay must be finite, lr >= 0");
+    zero_status st = check_hyper(step, lr, beta1, beta2, eps, weight_decay, "zero_shard_adamw_step");
+    if (st != ZERO_OK) return st;
     if (n == 0) return ZERO_OK;
     if (!master || !exp_avg || !exp_avg_sq || !grad || !param_out)
         return fail(ZERO_EINVAL, "zero_shard_adamw_step: NULL array");
@@ -203,20 +264,9 @@ extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, floa
         ranges_overlap(param_out, hbytes, exp_avg_sq, fbytes))
         return fail(ZERO_EINVAL, "zero_shard_adamw_step: param_out overlaps the fp32 state");
 
-    // Scalars in fp64, each rounded once to fp32.
-    const double bc1 = 1.0 - std::pow(beta1, static_cast<double>(step));
-    const double bc2 = 1.0 - std::pow(beta2, static_cast<double>(step));
-    if (!(bc1 > 0.0) || !(bc2 > 0.0))
-        return fail(ZERO_EINVAL, "zero_shard_adamw_step: bias correction is zero");
     AdamScalars c;
-    c.beta1 = static_cast<float>(beta1);
-    c.one_minus_beta1 = static_cast<float>(1.0 - beta1);
-    c.beta2 = static_cast<float>(beta2);
-    c.one_minus_beta2 = static_cast<float>(1.0 - beta2);
-    c.eps = static_cast<float>(eps);
-    c.step_size = static_cast<float>(lr / bc1);
-    c.sqrt_bc2 = static_cast<float>(std::sqrt(bc2));
-    c.decay = static_cast<float>(1.0 - lr * weight_decay);
+    st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, "zero_shard_adamw_step");
+    if (st != ZERO_OK) return st;
 
     // One lane group per lane. A dispatch holds fewer than 2^32 work-items, so
     // larger shards go out as consecutive single-pass launches over chunks
@@ -238,8 +288,77 @@ extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, floa
             hipLaunchKernelGGL(adamw_kernel<1>, dim3(static_cast<unsigned>(blocks)),
                                dim3(kThreads), 0, stream, master + off, exp_avg + off,
                                exp_avg_sq + off, grad + off, param_out + off, len, c, clip_scale);
-        const zero_status st = zero::check_hip(hipGetLastError(), "zero_shard_adamw_step launch");
+        st = zero::check_hip(hipGetLastError(), "zero_shard_adamw_step launch");
         if (st != ZERO_OK) return st;
     }
     return ZERO_OK;
+}
+
+extern "C" zero_status zero_multi_tensor_adamw_step(float* const* masters, float* const* exp_avgs,
+                                                    float* const* exp_avg_sqs,
+                                                    const uint16_t* const* grads,
+                                                    uint16_t* const* params_out,
+                                                    const int64_t* numels, int32_t n_tensors,
+                                                    int64_t step, double lr, double beta1,
+                                                    double beta2, double eps, double weight_decay,
+                                                    const float* clip_scale, hipStream_t stream) {
+    using zero::fail;
+    static const char* const who = "zero_multi_tensor_adamw_step";
+    zero::clear_error();
+    if (n_tensors < 0) return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: n_tensors < 0");
+    zero_status st = check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
+    if (st != ZERO_OK) return st;
+    if (n_tensors == 0) return ZERO_OK;
+    if (!masters || !exp_avgs || !exp_avg_sqs || !grads || !params_out || !numels)
+        return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: NULL array of pointers");
+    for (int32_t t = 0; t < n_tensors; ++t) {
+        const int64_t n = numels[t];
+        if (n < 0) return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: numel < 0 for tensor " + std::to_string(t));
+        if (n == 0) continue;
+        if (!masters[t] || !exp_avgs[t] || !exp_avg_sqs[t] || !grads[t] || !params_out[t])
+            return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: NULL array for tensor " + std::to_string(t));
+        const size_t fb = static_cast<size_t>(n) * 4, hb = static_cast<size_t>(n) * 2;
+        if (ranges_overlap(params_out[t], hb, masters[t], fb) ||
+            ranges_overlap(params_out[t], hb, exp_avgs[t], fb) ||
+            ranges_overlap(params_out[t], hb, exp_avg_sqs[t], fb))
+            return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: param overlaps the fp32 state of tensor " +
+                                         std::to_string(t));
+        if (blocks_for(n) > 0x7FFFFFFF)
+            return fail(ZERO_ERANGE, "zero_multi_tensor_adamw_step: tensor " + std::to_string(t) + " too large");
+    }
+    AdamScalars c;
+    st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
+    if (st != ZERO_OK) return st;
+    MtBatch batch{};
+    auto flush = [&]() -> zero_status {
+        if (batch.count == 0) return ZERO_OK;
+        hipLaunchKernelGGL(adamw_multi_kernel, dim3(static_cast<unsigned>(batch.first_block[batch.count])),
+                           dim3(kThreads), 0, stream, batch, c, clip_scale);
+        batch.count = 0;
+        batch.first_block[0] = 0;
+        return zero::check_hip(hipGetLastError(), "zero_multi_tensor_adamw_step launch");
+    };
+    for (int32_t t = 0; t < n_tensors; ++t) {
+        const int64_t n = numels[t];
+        if (n == 0) continue;
+        const int64_t blocks = blocks_for(n);
+        if (int64_t(batch.first_block[batch.count]) + blocks > 0x7FFFFFFF) {   // grid < 2^31 workgroups
+            st = flush();
+            if (st != ZERO_OK) return st;
+        }
+        const int i = batch.count;
+        batch.p[i] = masters[t];
+        batch.m[i] = exp_avgs[t];
+        batch.v[i] = exp_avg_sqs[t];
+        batch.g[i] = grads[t];
+        batch.o[i] = params_out[t];
+        batch.n[i] = n;
+        batch.first_block[i + 1] = batch.first_block[i] + static_cast<int32_t>(blocks);
+        batch.count = i + 1;
+        if (batch.count == kMtTensors) {
+            st = flush();
+            if (st != ZERO_OK) return st;
+        }
+    }
+    return flush();
 }
