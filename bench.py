@@ -21,6 +21,9 @@ Other workloads (`--workload`), each timed as its own configuration states:
   gpt2-small-fsdp2  the default step on FSDP-2's per-parameter Shard(0) layout
               (every tensor cut along dim 0; a rank's chunks in one coalesced
               buffer); the replicas are per-tensor gradients flattened into it
+  gpt2-small-fsdp2-pertensor  the Shard(0) step with per-parameter optimizer
+              state: every local chunk has its own fp32 tensors, updated by the
+              multi-tensor AdamW over the ragged list
   gpt2-small-offload  the default step with ZeRO-Offload's update: the fp32
               master/m/v live in host DRAM; the shard's bf16 gradients go to
               the host, the host runs AdamW, the bf16 parameters come back, in
@@ -48,7 +51,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 METRIC = "shard AdamW step: params/sec and achieved HBM GB/s (% of MI355X peak)"
 WORKLOAD_NAMES = ["gpt2-small", "llama3-8b", "llama3-70b", "gpt-1.3b", "gpt2-small-fsdp2",
-                  "gpt2-small-offload"]
+                  "gpt2-small-offload", "gpt2-small-fsdp2-pertensor"]
 PCIE_PEAK_GBS = 128.0          # PCIe 5.0 x16, both directions together (64 GB/s each way)
 OFFLOAD_CHUNK = 1 << 21        # elements per staging slot of the offload pipeline
 
@@ -72,7 +75,7 @@ def parse_args(argv=None):
 
 DEFAULT_STEPS = {"gpt2-small": (200, 20), "llama3-8b": (20, 3), "llama3-70b": (5, 1),
                  "gpt-1.3b": (10, 2), "gpt2-small-fsdp2": (200, 20),
-                 "gpt2-small-offload": (30, 3)}
+                 "gpt2-small-offload": (30, 3), "gpt2-small-fsdp2-pertensor": (200, 20)}
 
 
 class RankWorkload:
@@ -86,6 +89,7 @@ class RankWorkload:
         "llama3-70b": ("llama3-70b", 8, 7, 0, 0, False, "flat"),
         "gpt2-small-fsdp2": ("gpt2-small", 8, 7, 8, 0, True, "shard0"),
         "gpt2-small-offload": ("gpt2-small", 8, 7, 8, 0, True, "flat"),
+        "gpt2-small-fsdp2-pertensor": ("gpt2-small", 8, 7, 8, 0, True, "shard0"),
     }
 
     def __init__(self, name: str, device):
@@ -193,7 +197,52 @@ class RankWorkload:
             self.phases.append(("gather", rs.gather))
         self.adamw_launches = 1
         self.elems_per_step = S
+        self.per_tensor = name.endswith("-pertensor")
+        if self.per_tensor:
+            self._setup_per_tensor(device)
         torch.cuda.synchronize()
+
+    def _setup_per_tensor(self, device):
+        """FSDP-2 as its optimizer sees it: every parameter's local chunk has its
+        own fp32 master/m/v tensors (separate allocations), and the update is
+        the multi-tensor AdamW over that ragged list. Gradients and parameters
+        stay views into the rank's coalesced buffers (the reduce output and the
+        gather input)."""
+        import torch
+
+        from zero_partitioned_mixed_partition_amd import _binding as zb
+        rs = self.rs
+        self.segs = self.plan.segments(self.rank)
+        sl = [slice(soff, soff + ln) for (_, _, soff, ln) in self.segs]
+        self.pt_master = [rs.master[x].clone() for x in sl]
+        self.pt_m = [torch.zeros(x.stop - x.start, dtype=torch.float32, device=device) for x in sl]
+        self.pt_v = [torch.zeros(x.stop - x.start, dtype=torch.float32, device=device) for x in sl]
+        grads = [rs.grad[x] for x in sl]
+        params = [rs.param_shards[self.rank][x] for x in sl]
+        st = torch.cuda.current_stream(device).cuda_stream
+        call = zb.prepare_multi_tensor_adamw_step(self.pt_master, self.pt_m, self.pt_v, grads, params,
+                                                  clip_scale=rs.scale, stream=st,
+                                                  **self.hyper.as_kwargs())
+        self.t = 0
+
+        def adamw_pt():
+            self.t += 1
+            call(self.t)
+        self.phases = [(n, adamw_pt if n == "adamw" else fn) for n, fn in self.phases]
+        self.elems_per_step = sum(x.stop - x.start for x in sl)
+
+    def state_arrays(self):
+        """The rank's fp32 master, m and v over its coalesced buffer, on the host
+        (per-parameter state is placed at its chunk's offset, padding zero)."""
+        import numpy as np
+        rs = self.rs
+        if not getattr(self, "per_tensor", False):
+            return [x.detach().cpu().numpy() for x in (rs.master, rs.exp_avg, rs.exp_avg_sq)]
+        out = [np.zeros(self.S, np.float32) for _ in range(3)]
+        for (_, _, soff, ln), *arrs in zip(self.segs, self.pt_master, self.pt_m, self.pt_v):
+            for o, a in zip(out, arrs):
+                o[soff:soff + ln] = a.cpu().numpy()
+        return out
 
     def offload_parts(self, reps: int):
         """The offload phase's two halves on their own, on copies of the state:
@@ -236,9 +285,10 @@ class RankWorkload:
     def bytes_per_phase(self):
         S = self.S
         # the offload phase moves 2 B/elem each way over the host link; its
-        # 28 B/elem of state traffic is in host DRAM
+        # 28 B/elem of state traffic is in host DRAM. The per-parameter update
+        # covers the chunks' elements only (not the coalesced buffer's padding).
         b = {"clip": 8 * (self.n_ranks + max(len(self.windows), 1)) + 4,
-             "adamw": 4 * S if self.offload else 28 * S}
+             "adamw": 4 * S if self.offload else 28 * self.elems_per_step}
         if self.replicas:
             b["reduce"] = (2 * self.replicas + 2) * S
         else:

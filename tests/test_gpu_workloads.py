@@ -136,7 +136,8 @@ def test_gpt2_small_rank7_hundred_steps_clip(zm):
         assert_bf16_close(host_u16(d_param[sl]), bits, f"param window {w0}")
 
 
-@pytest.mark.parametrize("name", ["gpt2-small", "gpt2-small-fsdp2", "gpt2-small-offload"])
+@pytest.mark.parametrize("name", ["gpt2-small", "gpt2-small-fsdp2", "gpt2-small-offload",
+                                  "gpt2-small-fsdp2-pertensor"])
 def test_bench_pipeline_matches_oracle(zm, name):
     import bench
     setup = bench.make_workload(name, dev())
@@ -191,14 +192,13 @@ def test_bench_pipeline_matches_oracle(zm, name):
     assert (np.abs(got_parts[others] - want_parts[others]) <= 1e-12 * want_parts[others]).all()
     got_scale = np.float32(setup.rs.scale.item())
     assert abs(int(got_scale.view(np.int32)) - int(np.float32(out["clip"]).view(np.int32))) <= 1
-    # (with the offload the fp32 state is in host memory; host_f32 reads either)
-    held = ((setup.rs.master, "master"), (setup.rs.exp_avg, "exp_avg"),
-            (setup.rs.exp_avg_sq, "exp_avg_sq"))
+    # (offload: the fp32 state is in host memory; per-tensor: one array per chunk,
+    # placed back at the chunk offsets with zero padding, which the oracle keeps at zero)
     assert setup.rs.master.is_cuda != setup.offload
-    for got, key in held:
-        exact = assert_f32_close(host_f32(got), state[key], key)
+    for got, key in zip(setup.state_arrays(), ("master", "exp_avg", "exp_avg_sq")):
+        exact = assert_f32_close(got, state[key], key)
         note(f"bench pipeline {name}: {key} bit-identical fraction {exact:.6f}")
     if shard0:
-        assert (host_f32(setup.rs.master)[~mask] == 0).all(), "padding stays zero"
+        assert (setup.state_arrays()[0][~mask] == 0).all(), "padding stays zero"
     for i, (a, b) in enumerate(zip(setup.rs.tensors, out["tensors"])):
         assert_bf16_close(host_u16(a), b, f"gathered tensor {i}")

@@ -170,7 +170,15 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ mas
 // arguments; workgroup b finds its tensor by a binary search over the
 // per-tensor workgroup prefix and updates one element per lane with the same
 // per-element code as the flat kernel (so the bits are the same).
-constexpr int kMtTensors = 72;
+constexpr int kMtTensors = 78;
+// Elements per lane in the multi-tensor kernel: a workgroup covers kMtPer
+// rows of kThreads elements (each row one coalesced access per array), so its
+// tensor lookup is paid once per kMtPer * kThreads elements.
+#ifndef ZERO_MT_ELEMS_PER_LANE
+#define ZERO_MT_ELEMS_PER_LANE 2
+#endif
+constexpr int kMtPer = ZERO_MT_ELEMS_PER_LANE;
+constexpr int64_t kMtChunk = int64_t(kThreads) * kMtPer;
 
 struct MtBatch {
     float* p[kMtTensors];
@@ -189,14 +197,41 @@ __global__ __launch_bounds__(kThreads) void adamw_multi_kernel(MtBatch b, AdamSc
     const float clip = read_clip(clip_scale);
     if (!isfinite(clip)) return;
     const int32_t blk = static_cast<int32_t>(blockIdx.x);
-    int lo = 0, hi = b.count - 1;
+    int lo = 0, hi = b.count - 1;              // t with first_block[t] <= blk < first_block[t + 1]
     while (lo < hi) {
         const int mid = (lo + hi + 1) / 2;
         if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
     }
     const int t = lo;
-    const int64_t i = static_cast<int64_t>(blk - b.first_block[t]) * kThreads + threadIdx.x;
-    if (i < b.n[t]) Lane<1>::update(b.p[t], b.m[t], b.v[t], b.g[t], b.o[t], i, clip, c);
+    float* __restrict__ P = b.p[t];
+    float* __restrict__ M = b.m[t];
+    float* __restrict__ V = b.v[t];
+    const uint16_t* __restrict__ G = b.g[t];
+    uint16_t* __restrict__ O = b.o[t];
+    const int64_t n = b.n[t];
+    const int64_t base = static_cast<int64_t>(blk - b.first_block[t]) * kMtChunk + threadIdx.x;
+    float p[kMtPer], m[kMtPer], v[kMtPer], g[kMtPer];
+#pragma unroll
+    for (int k = 0; k < kMtPer; ++k) {          // every load first
+        const int64_t i = base + int64_t(k) * kThreads;
+        if (i < n) {
+            p[k] = zero::dev::ld_stream(P + i);
+            m[k] = zero::dev::ld_stream(M + i);
+            v[k] = zero::dev::ld_stream(V + i);
+            g[k] = zero::dev::bf16_to_f32(zero::dev::ld_stream(G + i));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kMtPer; ++k) {
+        const int64_t i = base + int64_t(k) * kThreads;
+        if (i < n) {
+            adam_elem(p[k], m[k], v[k], g[k] * clip, c);
+            zero::dev::st_stream(P + i, p[k]);
+            zero::dev::st_stream(M + i, m[k]);
+            zero::dev::st_stream(V + i, v[k]);
+            zero::dev::st_stream(O + i, static_cast<uint16_t>(zero::dev::f32_to_bf16(p[k])));
+        }
+    }
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -323,7 +358,7 @@ extern "C" zero_status zero_multi_tensor_adamw_step(float* const* masters, float
             ranges_overlap(params_out[t], hb, exp_avg_sqs[t], fb))
             return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: param overlaps the fp32 state of tensor " +
                                          std::to_string(t));
-        if (blocks_for(n) > 0x7FFFFFFF)
+        if ((n + kMtChunk - 1) / kMtChunk > 0x7FFFFFFF)
             return fail(ZERO_ERANGE, "zero_multi_tensor_adamw_step: tensor " + std::to_string(t) + " too large");
     }
     AdamScalars c;
@@ -341,7 +376,7 @@ extern "C" zero_status zero_multi_tensor_adamw_step(float* const* masters, float
     for (int32_t t = 0; t < n_tensors; ++t) {
         const int64_t n = numels[t];
         if (n == 0) continue;
-        const int64_t blocks = blocks_for(n);
+        const int64_t blocks = (n + kMtChunk - 1) / kMtChunk;
         if (int64_t(batch.first_block[batch.count]) + blocks > 0x7FFFFFFF) {   // grid < 2^31 workgroups
             st = flush();
             if (st != ZERO_OK) return st;
