@@ -117,29 +117,26 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
     }
 }
 
-// Tensor-major gather: one descriptor per tensor instead of one per segment.
-// Element e of tensor t sits at g = e (+ the tensor's flat offset, flat plans)
-// of a rank-major sequence in which rank r holds [r*chunk_t, (r+1)*chunk_t);
-// it is read from shards[r] + (Shard(0): the chunk's start in a rank's
-// buffer) + (g - r*chunk_t). Flat plans: chunk_t = S. Shard(0) plans:
-// chunk_t = (rows per chunk) * (elements per row). A workgroup copies kChunk
-// elements of one tensor. It finds the rank of its first element once (a
-// double-precision reciprocal multiply, corrected to the exact quotient); when
-// chunk_t >= kChunk its lanes then lie in that rank or the next, two
-// workgroup-uniform shard pointers. Smaller chunks take a per-lane path.
+// Tensor-major gather for Shard(0) plans: one descriptor per tensor instead of
+// one per segment. Element e of tensor t lies in rank r = e / chunk_t
+// (chunk_t = rows per chunk * elements per row) and is read from shards[r] +
+// off_t + (e - r*chunk_t), off_t being the chunk's start in every rank's
+// coalesced buffer. A workgroup copies kChunk elements of one tensor: it finds
+// the rank of its first element once (32-bit division: tensors here hold fewer
+// than 2^31 elements), and when chunk_t >= kChunk its lanes lie in that rank
+// or the next, two workgroup-uniform shard pointers. Smaller chunks take a
+// per-lane path.
 constexpr int kMaxRanks = 64;                   // shard pointer table in the kernel arguments
-constexpr int kTens = 72;                       // tensors per launch
+constexpr int kTens = 120;                      // tensors per launch
 
 struct TensorBatch {
     const uint16_t* shards[kMaxRanks];
     uint16_t* dst[kTens];
-    int64_t numel[kTens];
-    int64_t chunk[kTens];
-    int64_t off[kTens];          // flat: the tensor's flat offset; Shard(0): its chunk start in a shard
-    double inv_chunk[kTens];     // 1.0 / chunk, rounded
-    int64_t first_block[kTens + 1];
+    int64_t off[kTens];          // the chunk's start in a rank's coalesced buffer
+    int32_t numel[kTens];
+    int32_t chunk[kTens];
+    int32_t first_block[kTens + 1];
     int32_t n;
-    int32_t flat;                // 1: flat plan, 0: Shard(0) plan
 };
 static_assert(sizeof(TensorBatch) <= 4096, "kernel arguments are limited to 4 KB");
 
@@ -154,15 +151,10 @@ __global__ __launch_bounds__(kThreads) void gather_tensor_kernel(TensorBatch b) 
     const int t = lo;
     const int64_t e0 = (blk - b.first_block[t]) * kChunk;        // workgroup's first element
     const int64_t numel = b.numel[t], chunk = b.chunk[t];
-    const int64_t g0 = b.flat ? b.off[t] + e0 : e0;
-    const int64_t soff = b.flat ? 0 : b.off[t];
-    // r0 = floor(g0 / chunk): g0 < 2^53, so the estimate is off by at most one.
-    int64_t q = static_cast<int64_t>(static_cast<double>(g0) * b.inv_chunk[t]);
-    int64_t rem = g0 - q * chunk;
-    if (rem < 0) { --q; rem += chunk; }
-    if (rem >= chunk) { ++q; rem -= chunk; }
-    const int r0 = __builtin_amdgcn_readfirstlane(static_cast<int>(q));
-    const int64_t local0 = rem;
+    const int64_t soff = b.off[t];
+    const uint32_t q0 = static_cast<uint32_t>(e0) / static_cast<uint32_t>(chunk);
+    const int r0 = __builtin_amdgcn_readfirstlane(static_cast<int>(q0));
+    const int64_t local0 = e0 - static_cast<int64_t>(r0) * chunk;
     uint16_t* dst = b.dst[t];
     if (chunk >= kChunk) {
         // local < chunk + kChunk <= 2 * chunk: rank r0, or r0 + 1 past the boundary.
@@ -277,15 +269,11 @@ zero_status check_tensors(const zero_plan* plan, const uint16_t* const* tensors,
     return ZERO_OK;
 }
 
-// One launch per kTens tensors. Each tensor: its descriptor (flat plans: the
-// tensor's flat offset, S, 0; Shard(0) plans: 0, its chunk length, its chunk
-// start in a rank's buffer).
+// One launch per kTens tensors of a Shard(0) plan.
 zero_status launch_tensors(const zero_plan* plan, const uint16_t* const* shards,
                            uint16_t* const* tensors, hipStream_t stream) {
     TensorBatch batch{};
     for (int32_t r = 0; r < plan->n_ranks; ++r) batch.shards[r] = shards[r];
-    const bool shard0 = plan->kind == 1;
-    batch.flat = shard0 ? 0 : 1;
     auto flush = [&]() -> zero_status {
         if (batch.n == 0) return ZERO_OK;
         const int64_t blocks = batch.first_block[batch.n];
@@ -299,17 +287,16 @@ zero_status launch_tensors(const zero_plan* plan, const uint16_t* const* shards,
         const int64_t n = plan->numels[t];
         if (n <= 0) continue;
         const int64_t blocks = (n + kChunk - 1) / kChunk;
-        if (batch.first_block[batch.n] + blocks > 0x7FFFFFFF) {
+        if (int64_t(batch.first_block[batch.n]) + blocks > 0x7FFFFFFF) {
             const zero_status st = flush();
             if (st != ZERO_OK) return st;
         }
         const int i = batch.n;
         batch.dst[i] = tensors[t];
-        batch.numel[i] = n;
-        batch.chunk[i] = shard0 ? plan->chunk_elems[t] : plan->shard;
+        batch.numel[i] = static_cast<int32_t>(n);
+        batch.chunk[i] = static_cast<int32_t>(plan->chunk_elems[t]);
         batch.off[i] = plan->offsets[t];
-        batch.inv_chunk[i] = 1.0 / static_cast<double>(batch.chunk[i]);
-        batch.first_block[i + 1] = batch.first_block[i] + blocks;
+        batch.first_block[i + 1] = batch.first_block[i] + static_cast<int32_t>(blocks);
         batch.n = i + 1;
         if (batch.n == kTens) {
             const zero_status st = flush();
@@ -319,10 +306,17 @@ zero_status launch_tensors(const zero_plan* plan, const uint16_t* const* shards,
     return flush();
 }
 
+bool fits_tensor_major(const zero_plan* plan) {
+    if (plan->kind != 1 || plan->n_ranks > kMaxRanks || plan->shard <= 0) return false;
+    for (const int64_t n : plan->numels)
+        if (n >= (int64_t(1) << 31)) return false;
+    return true;
+}
+
 }  // namespace
 
-// Which gather serves which plan: 0 segment copies for all, 1 tensor-major
-// for Shard(0) plans, 2 tensor-major for all (both up to kMaxRanks ranks).
+// Shard(0) plans use the tensor-major kernel (ZERO_GATHER_TENSOR_MAJOR=0
+// forces segment copies); flat plans copy segments (measured faster there).
 #ifndef ZERO_GATHER_TENSOR_MAJOR
 #define ZERO_GATHER_TENSOR_MAJOR 1
 #endif
@@ -338,9 +332,7 @@ extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t*
     for (int32_t r = 0; r < plan->n_ranks; ++r)
         if (plan->shard > 0 && shards[r] == nullptr)
             return fail(ZERO_EINVAL, "zero_gather_params: NULL shard " + std::to_string(r));
-    // (The rank estimate in double precision is exact to within one below 2^52.)
-    if (plan->n_ranks <= kMaxRanks && plan->shard > 0 && plan->padded < (int64_t(1) << 52) &&
-        (ZERO_GATHER_TENSOR_MAJOR == 2 || (ZERO_GATHER_TENSOR_MAJOR == 1 && plan->kind == 1)))
+    if (ZERO_GATHER_TENSOR_MAJOR && fits_tensor_major(plan))
         return launch_tensors(plan, shards, tensors, stream);
     std::vector<Piece> pieces;
     pieces.reserve(plan->all.size());
