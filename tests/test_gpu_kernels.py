@@ -442,3 +442,25 @@ def test_multi_tensor_adamw_equals_the_flat_kernel_on_views(zm):
     torch.cuda.synchronize()
     for a, b, name in zip(flat, multi, ("master", "exp_avg", "exp_avg_sq", "param")):
         assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("R", [3, 8])
+def test_reduce_two_groups_per_pass_full_array(zm, R):
+    """Shards of 2^26 elements and more with at most 8 replicas take the
+    two-groups-per-pass kernel: full array and exact norm against the oracle,
+    with a ragged tail."""
+    n = (1 << 26) + 4099
+    plan = zm.zero_partition_plan([n], 1, 1)
+    ref = oracle.partition_plan([n], 1, 1)
+    note(f"reduce two groups: n={n} R={R}")
+    reps = [synth.normal_bf16(n, 91, synth.KIND_REPLICA, 1, k, 0, n, 1e-3) for k in range(R)]
+    want = np.zeros(n, np.uint16)
+    oracle.reduce_shard(ref, 0, reps, 0, want)
+    d_reps = [to_dev_u16(x) for x in reps]
+    out = torch.empty(n, dtype=torch.int16, device=dev())
+    sq = torch.zeros(1, dtype=torch.float64, device=dev())
+    zm.zero_grad_reduce_shard(plan, 0, d_reps, 0, n, out, sqnorm_out=sq)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u16(out), want, "reduced")
+    want_sq = oracle.sqnorm(want)
+    assert abs(sq.item() - want_sq) <= 1e-12 * want_sq

@@ -98,7 +98,16 @@ template <> struct Bits<2> { typedef uint32_t T; };
 // Vector path. src_off: element offset into each replica buffer of the first
 // element to reduce; out: first output element; n: elements to reduce. The
 // caller guarantees every replica + src_off and out are aligned to E elements.
-template <bool kNorm>
+// kGroups: groups per pass when the replicas fit one load batch. A lane then
+// issues the loads of kGroups groups (kGroups * R accesses in flight) before
+// it adds them; each lane still adds its groups to the fp64 norm in index
+// order, so every variant gives the same bits. A separate kernel per value,
+// so the one-group form keeps its lower register count and occupancy.
+// Measured on MI355X with 8 replicas: 2 groups +4.5% at 164 M elements,
+// -2% at 15.6 M; with 64 replicas the wider form would cost 13%.
+constexpr int64_t kTwoGroupsFrom = int64_t(1) << 26;   // shard elements
+
+template <bool kNorm, int kGroups>
 __global__ __launch_bounds__(kThreads) void reduce_vec(ReplicaTable reps, int n_rep,
                                                        int64_t src_off,
                                                        uint16_t* __restrict__ out, int64_t n,
@@ -110,29 +119,7 @@ __global__ __launch_bounds__(kThreads) void reduce_vec(ReplicaTable reps, int n_
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     double sq = 0.0;
-    for (int64_t i = tid; i < groups; i += stride) {
-        float acc[kEpt];
-#pragma unroll
-        for (int j = 0; j < kEpt; ++j) acc[j] = 0.0f;
-        for (int k0 = 0; k0 < n_rep; k0 += kReplicaBatch) {
-            V x[kReplicaBatch];
-            const int kn = n_rep - k0 < kReplicaBatch ? n_rep - k0 : kReplicaBatch;
-#pragma unroll
-            for (int k = 0; k < kReplicaBatch; ++k)
-                if (k < kn)
-                    x[k] = zero::dev::ld_stream(reinterpret_cast<const V*>(reps.p[k0 + k] + src_off) + i);
-#pragma unroll
-            for (int k = 0; k < kReplicaBatch; ++k) {
-                if (k < kn) {
-#pragma unroll
-                    for (int j = 0; j < kWords; ++j) {
-                        const uint32_t w = word(x[k], j);
-                        acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(w);
-                        acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(w);
-                    }
-                }
-            }
-        }
+    auto finish_group = [&](int64_t i, const float* acc) {
         V o;
         uint32_t ow[kWords];
 #pragma unroll
@@ -148,6 +135,65 @@ __global__ __launch_bounds__(kThreads) void reduce_vec(ReplicaTable reps, int n_
 #pragma unroll
         for (int j = 0; j < kWords; ++j) set_word(o, j, ow[j]);
         zero::dev::st_stream(reinterpret_cast<V*>(out) + i, o);
+    };
+    if (kGroups > 1 && n_rep <= kReplicaBatch) {
+        for (int64_t i0 = tid; i0 < groups; i0 += kGroups * stride) {
+            V x[kGroups][kReplicaBatch];
+#pragma unroll
+            for (int q = 0; q < kGroups; ++q) {
+                const int64_t i = i0 + q * stride;
+#pragma unroll
+                for (int k = 0; k < kReplicaBatch; ++k)
+                    if (k < n_rep && i < groups)
+                        x[q][k] = zero::dev::ld_stream(reinterpret_cast<const V*>(reps.p[k] + src_off) + i);
+            }
+#pragma unroll
+            for (int q = 0; q < kGroups; ++q) {
+                const int64_t i = i0 + q * stride;
+                if (i >= groups) break;
+                float acc[kEpt];
+#pragma unroll
+                for (int j = 0; j < kEpt; ++j) acc[j] = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kReplicaBatch; ++k) {
+                    if (k < n_rep) {
+#pragma unroll
+                        for (int j = 0; j < kWords; ++j) {
+                            const uint32_t w = word(x[q][k], j);
+                            acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(w);
+                            acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(w);
+                        }
+                    }
+                }
+                finish_group(i, acc);
+            }
+        }
+    } else {
+        for (int64_t i = tid; i < groups; i += stride) {
+            float acc[kEpt];
+#pragma unroll
+            for (int j = 0; j < kEpt; ++j) acc[j] = 0.0f;
+            for (int k0 = 0; k0 < n_rep; k0 += kReplicaBatch) {
+                V x[kReplicaBatch];
+                const int kn = n_rep - k0 < kReplicaBatch ? n_rep - k0 : kReplicaBatch;
+#pragma unroll
+                for (int k = 0; k < kReplicaBatch; ++k)
+                    if (k < kn)
+                        x[k] = zero::dev::ld_stream(reinterpret_cast<const V*>(reps.p[k0 + k] + src_off) + i);
+#pragma unroll
+                for (int k = 0; k < kReplicaBatch; ++k) {
+                    if (k < kn) {
+#pragma unroll
+                        for (int j = 0; j < kWords; ++j) {
+                            const uint32_t w = word(x[k], j);
+                            acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(w);
+                            acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(w);
+                        }
+                    }
+                }
+            }
+            finish_group(i, acc);
+        }
     }
     // Ragged tail (< E elements), one per thread of the first threads.
     const int64_t tail = n - groups * kEpt;
@@ -296,11 +342,18 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
     const bool norm = sqnorm_out != nullptr;
     const int blocks = grid_for(vec ? n / kEpt : n, ZERO_REDUCE_MAX_BLOCKS);
     if (vec) {
-        if (norm)
-            hipLaunchKernelGGL(reduce_vec<true>, dim3(blocks), dim3(kThreads), 0, stream, table,
+        const bool two = n_replicas <= kReplicaBatch && n >= kTwoGroupsFrom;
+        if (norm && two)
+            hipLaunchKernelGGL((reduce_vec<true, 2>), dim3(blocks), dim3(kThreads), 0, stream, table,
+                               n_replicas, src_off, out, n, partials);
+        else if (norm)
+            hipLaunchKernelGGL((reduce_vec<true, 1>), dim3(blocks), dim3(kThreads), 0, stream, table,
+                               n_replicas, src_off, out, n, partials);
+        else if (two)
+            hipLaunchKernelGGL((reduce_vec<false, 2>), dim3(blocks), dim3(kThreads), 0, stream, table,
                                n_replicas, src_off, out, n, partials);
         else
-            hipLaunchKernelGGL(reduce_vec<false>, dim3(blocks), dim3(kThreads), 0, stream, table,
+            hipLaunchKernelGGL((reduce_vec<false, 1>), dim3(blocks), dim3(kThreads), 0, stream, table,
                                n_replicas, src_off, out, n, partials);
     } else {
         if (norm)
