@@ -21,7 +21,7 @@ calls. Importing it without the built library raises ImportError.
 step.RankStep holds one rank's device state and issues its step (reduce,
 clip, AdamW, gather) on one stream, e.g. for GPT-2 small over 8 ranks:
 
-    plan = zero_partition_plan(numels, n_ranks=8, align=128)
+    plan = zero_partition_plan(numels, n_ranks=8, align_elems=128)
     rs = RankStep(plan, rank=7, n_windows=1, hyper=Hyper(), max_norm=1.0,
                   device=torch.device("cuda:0"))
     rs.set_remote_partials(other_ranks_sqnorms)       # from the scalar all-reduce
