@@ -176,7 +176,10 @@ zero_status zero_plan_memory_bytes(const zero_plan* plan, int32_t stage, int32_t
  *              values this call wrote (0 if it wrote nothing). Deterministic for a
  *              given device.
  * workspace    device, required when sqnorm_out is non-null; at least
- *              zero_sqnorm_workspace_bytes() bytes, 8-byte aligned.
+ *              zero_sqnorm_workspace_bytes() bytes, 8-byte aligned. It holds
+ *              per-workgroup partials between the call's two kernels, so
+ *              calls that may run at the same time (on different streams)
+ *              need separate workspaces; calls on one stream may share one.
  * Errors: ZERO_EINVAL (null plan/replicas/shard_grad, a null replica pointer,
  * R out of range, rank out of range, bad window); ZERO_ENOSPACE; ZERO_EHIP. */
 zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,

@@ -207,7 +207,9 @@ _ws_cache = {}
 
 
 def sqnorm_workspace(device) -> "object":
-    """A cached device workspace of zero_sqnorm_workspace_bytes() bytes (torch-allocated)."""
+    """A cached device workspace of zero_sqnorm_workspace_bytes() bytes (torch-allocated),
+    one per device, used by every call that passes no workspace of its own. Calls
+    issued on different streams that may overlap must pass their own workspaces."""
     import torch
     dev = torch.device(device)
     key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
