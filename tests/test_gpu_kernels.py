@@ -464,3 +464,23 @@ def test_reduce_two_groups_per_pass_full_array(zm, R):
     assert_bits_equal(host_u16(out), want, "reduced")
     want_sq = oracle.sqnorm(want)
     assert abs(sq.item() - want_sq) <= 1e-12 * want_sq
+
+
+@pytest.mark.parametrize("n_ranks", [3, 8, 64, 97])
+def test_shard0_flatten_many_tensors_misaligned(zm, n_ranks):
+    """Shard(0) flatten over more tensors than one launch carries, from
+    2-byte-misaligned sources, padding included, against the oracle (64 ranks
+    and fewer: tensor-major kernel; 97: segment copies)."""
+    rng = np.random.default_rng(1300 + n_ranks)
+    t = 150
+    dim0 = [int(x) for x in rng.integers(1, 400, t)]
+    numels = [d * int(k) for d, k in zip(dim0, rng.integers(1, 40, t))]
+    note(f"shard0 flatten N_d={n_ranks} T={t} Phi={sum(numels)}")
+    ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, 8)
+    plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, 8)
+    tensors = [rng.integers(0, 1 << 16, n).astype(np.uint16) for n in numels]
+    bufs = [to_dev_u16(np.concatenate([np.zeros(1, np.uint16), x])) for x in tensors]
+    flat = to_dev_u16(np.full(ref.padded_numel, 0x6666, np.uint16))
+    zm.zero_flatten_params(plan, [b[1:] for b in bufs], flat)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u16(flat), oracle.flatten_params_shard0(ref, tensors), "coalesced buffers")

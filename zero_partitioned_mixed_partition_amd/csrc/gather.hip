@@ -130,8 +130,8 @@ constexpr int kMaxRanks = 64;                   // shard pointer table in the ke
 constexpr int kTens = 120;                      // tensors per launch
 
 struct TensorBatch {
-    const uint16_t* shards[kMaxRanks];
-    uint16_t* dst[kTens];
+    uint16_t* shards[kMaxRanks];  // rank buffers (read by the gather, written by the flatten)
+    uint16_t* dst[kTens];         // tensors (written by the gather, read by the flatten)
     int64_t off[kTens];          // the chunk's start in a rank's coalesced buffer
     int32_t numel[kTens];
     int32_t chunk[kTens];
@@ -140,6 +140,14 @@ struct TensorBatch {
 };
 static_assert(sizeof(TensorBatch) <= 4096, "kernel arguments are limited to 4 KB");
 
+// kScatter = false: the gather (rank buffers -> tensors); true: the flatten
+// (tensors -> rank buffers), the same index map copied the other way.
+template <bool kScatter>
+__device__ __forceinline__ void copy_elem(uint16_t* tens, uint16_t* buf) {
+    if (kScatter) *buf = *tens; else *tens = *buf;
+}
+
+template <bool kScatter>
 __global__ __launch_bounds__(kThreads) void gather_tensor_kernel(TensorBatch b) {
     typedef typename LaneBits<kLane>::T V;
     const int64_t blk = blockIdx.x;
@@ -158,8 +166,8 @@ __global__ __launch_bounds__(kThreads) void gather_tensor_kernel(TensorBatch b) 
     uint16_t* dst = b.dst[t];
     if (chunk >= kChunk) {
         // local < chunk + kChunk <= 2 * chunk: rank r0, or r0 + 1 past the boundary.
-        const uint16_t* p0 = b.shards[r0] + soff;
-        const uint16_t* p1 = (r0 + 1 < kMaxRanks ? b.shards[r0 + 1] : b.shards[r0]) + soff;
+        uint16_t* p0 = b.shards[r0] + soff;
+        uint16_t* p1 = (r0 + 1 < kMaxRanks ? b.shards[r0 + 1] : b.shards[r0]) + soff;
         V vals[kVecs];
         bool fast[kVecs];
 #pragma unroll
@@ -168,24 +176,26 @@ __global__ __launch_bounds__(kThreads) void gather_tensor_kernel(TensorBatch b) 
             const int64_t e = e0 + j, local = local0 + j;
             const bool next = local >= chunk;
             const int64_t l = next ? local - chunk : local;
-            const uint16_t* src = (next ? p1 : p0) + l;
+            uint16_t* buf = (next ? p1 : p0) + l;
             fast[v] = e + kLane <= numel && l + kLane <= chunk &&
-                      ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst + e)) &
+                      ((reinterpret_cast<uintptr_t>(buf) | reinterpret_cast<uintptr_t>(dst + e)) &
                        (2 * kLane - 1)) == 0;
-            if (fast[v]) vals[v] = zero::dev::ld_stream(reinterpret_cast<const V*>(src));
+            if (fast[v]) vals[v] = zero::dev::ld_stream(reinterpret_cast<const V*>(kScatter ? dst + e : buf));
         }
 #pragma unroll
         for (int v = 0; v < kVecs; ++v) {
             const int64_t j = (int64_t(v) * kThreads + threadIdx.x) * kLane;
             const int64_t e = e0 + j, local = local0 + j;
             if (fast[v]) {
-                zero::dev::st_stream(reinterpret_cast<V*>(dst + e), vals[v]);
+                const bool next = local >= chunk;
+                uint16_t* buf = (next ? p1 : p0) + (next ? local - chunk : local);
+                zero::dev::st_stream(reinterpret_cast<V*>(kScatter ? buf : dst + e), vals[v]);
                 continue;
             }
             // Straddles the boundary, misaligned, or the tensor's tail.
             for (int k = 0; k < kLane && e + k < numel; ++k) {
                 const int64_t lk = local + k;
-                dst[e + k] = lk < chunk ? p0[lk] : p1[lk - chunk];
+                copy_elem<kScatter>(dst + e + k, lk < chunk ? p0 + lk : p1 + (lk - chunk));
             }
         }
         return;
@@ -200,16 +210,19 @@ __global__ __launch_bounds__(kThreads) void gather_tensor_kernel(TensorBatch b) 
         const uint32_t lj = static_cast<uint32_t>(local0 + j);
         const uint32_t qj = lj / c32;
         const uint32_t within = lj - qj * c32;
-        const uint16_t* src = b.shards[r0 + static_cast<int>(qj)] + soff + within;
+        uint16_t* buf = b.shards[r0 + static_cast<int>(qj)] + soff + within;
         if (e + kLane <= numel && within + kLane <= c32 &&
-            ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst + e)) & (2 * kLane - 1)) == 0) {
-            zero::dev::st_stream(reinterpret_cast<V*>(dst + e), zero::dev::ld_stream(reinterpret_cast<const V*>(src)));
+            ((reinterpret_cast<uintptr_t>(buf) | reinterpret_cast<uintptr_t>(dst + e)) & (2 * kLane - 1)) == 0) {
+            if (kScatter)
+                zero::dev::st_stream(reinterpret_cast<V*>(buf), zero::dev::ld_stream(reinterpret_cast<const V*>(dst + e)));
+            else
+                zero::dev::st_stream(reinterpret_cast<V*>(dst + e), zero::dev::ld_stream(reinterpret_cast<const V*>(buf)));
             continue;
         }
         for (int k = 0; k < kLane && e + k < numel; ++k) {
             const uint32_t lk = lj + static_cast<uint32_t>(k);
             const uint32_t qk = lk / c32;
-            dst[e + k] = b.shards[r0 + static_cast<int>(qk)][soff + (lk - qk * c32)];
+            copy_elem<kScatter>(dst + e + k, b.shards[r0 + static_cast<int>(qk)] + soff + (lk - qk * c32));
         }
     }
 }
@@ -269,19 +282,21 @@ zero_status check_tensors(const zero_plan* plan, const uint16_t* const* tensors,
     return ZERO_OK;
 }
 
-// One launch per kTens tensors of a Shard(0) plan.
-zero_status launch_tensors(const zero_plan* plan, const uint16_t* const* shards,
-                           uint16_t* const* tensors, hipStream_t stream) {
+// One launch per kTens tensors of a Shard(0) plan. bufs: the N_d rank
+// buffers; tensors: the T tensors. kScatter picks the direction.
+template <bool kScatter>
+zero_status launch_tensors(const zero_plan* plan, uint16_t* const* bufs, uint16_t* const* tensors,
+                           hipStream_t stream, const char* who) {
     TensorBatch batch{};
-    for (int32_t r = 0; r < plan->n_ranks; ++r) batch.shards[r] = shards[r];
+    for (int32_t r = 0; r < plan->n_ranks; ++r) batch.shards[r] = bufs[r];
     auto flush = [&]() -> zero_status {
         if (batch.n == 0) return ZERO_OK;
         const int64_t blocks = batch.first_block[batch.n];
-        hipLaunchKernelGGL(gather_tensor_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                           0, stream, batch);
+        hipLaunchKernelGGL(gather_tensor_kernel<kScatter>, dim3(static_cast<unsigned>(blocks)),
+                           dim3(kThreads), 0, stream, batch);
         batch.n = 0;
         batch.first_block[0] = 0;
-        return zero::check_hip(hipGetLastError(), "zero_gather_params launch");
+        return zero::check_hip(hipGetLastError(), who);
     };
     for (size_t t = 0; t < plan->numels.size(); ++t) {
         const int64_t n = plan->numels[t];
@@ -333,7 +348,8 @@ extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t*
         if (plan->shard > 0 && shards[r] == nullptr)
             return fail(ZERO_EINVAL, "zero_gather_params: NULL shard " + std::to_string(r));
     if (ZERO_GATHER_TENSOR_MAJOR && fits_tensor_major(plan))
-        return launch_tensors(plan, shards, tensors, stream);
+        return launch_tensors<false>(plan, const_cast<uint16_t* const*>(shards), tensors, stream,
+                                     "zero_gather_params launch");
     std::vector<Piece> pieces;
     pieces.reserve(plan->all.size());
     for (const zero_segment& seg : plan->all)
@@ -350,8 +366,26 @@ extern "C" zero_status zero_flatten_params(const zero_plan* plan, const uint16_t
     if (plan->padded > 0 && flat == nullptr) return fail(ZERO_EINVAL, "zero_flatten_params: NULL flat");
     zero_status st = check_tensors(plan, tensors, "zero_flatten_params");
     if (st != ZERO_OK) return st;
-    // Every segment, in flat order, copied to its place; every gap between
-    // segments (and after the last) filled with zeros.
+    // Every gap between segments (and after the last) is filled with zeros;
+    // Shard(0) plans copy the tensors with the tensor-major kernel, flat plans
+    // copy every segment, in flat order, to its place.
+    const bool tensor_major = ZERO_GATHER_TENSOR_MAJOR && fits_tensor_major(plan);
+    if (tensor_major) {
+        std::vector<Piece> gaps;
+        int64_t pos = 0;
+        for (const zero_segment& seg : plan->all) {
+            const int64_t at = static_cast<int64_t>(seg.rank) * plan->shard + seg.shard_offset;
+            if (at > pos) gaps.push_back({nullptr, flat + pos, at - pos});
+            pos = at + seg.length;
+        }
+        if (plan->padded > pos) gaps.push_back({nullptr, flat + pos, plan->padded - pos});
+        st = launch_pieces(gaps, stream, "zero_flatten_params launch");
+        if (st != ZERO_OK) return st;
+        std::vector<uint16_t*> bufs(static_cast<size_t>(plan->n_ranks));
+        for (int32_t r = 0; r < plan->n_ranks; ++r) bufs[static_cast<size_t>(r)] = flat + int64_t(r) * plan->shard;
+        return launch_tensors<true>(plan, bufs.data(), const_cast<uint16_t* const*>(tensors), stream,
+                                    "zero_flatten_params launch");
+    }
     std::vector<Piece> pieces;
     pieces.reserve(2 * plan->all.size() + 1);
     int64_t pos = 0;
