@@ -21,6 +21,7 @@ Other workloads (`--workload`), each timed as its own configuration states:
   gpt2-small-fsdp2  the default step on FSDP-2's per-parameter Shard(0) layout
               (every tensor cut along dim 0; a rank's chunks in one coalesced
               buffer); the replicas are per-tensor gradients flattened into it
+              (one replica's flatten is also timed, outside the step)
   gpt2-small-fsdp2-pertensor  the Shard(0) step with per-parameter optimizer
               state: every local chunk has its own fp32 tensors, updated by the
               multi-tensor AdamW over the ragged list
@@ -150,8 +151,14 @@ class RankWorkload:
                                              synth.GRAD_SIGMA)
                     per_tensor.append(g)
                 zm.zero_flatten_params(self.plan, per_tensor, t)
+                if k == 0:          # kept: replica 0's flatten is timed outside the step
+                    self.flatten_in = per_tensor
                 del per_tensor
             self.windows = [(0, P, full)]
+            self.flatten_out = torch.empty(P, dtype=torch.int16, device=device)
+            self.extra_phases = [("flatten", zm._binding.prepare_flatten_params(
+                self.plan, self.flatten_in, self.flatten_out,
+                torch.cuda.current_stream(device).cuda_stream))]
         elif reps and not bucket:
             full = staggered_replicas(reps, P, device)
             for k, t in enumerate(full):
@@ -295,6 +302,8 @@ class RankWorkload:
             b["sqnorm"] = 2 * S
         if any(p[0] == "gather" for p in self.phases):
             b["gather"] = 4 * self.phi
+        if getattr(self, "extra_phases", None):
+            b["flatten"] = 4 * self.phi + 2 * (self.P - self.phi)
         return b
 
     def describe(self):
