@@ -11,9 +11,11 @@ gpt-1.3b    1.3B GPT list, N_d = 8: 8 replicas reduced for every rank, AdamW on
             oracle (every rank boundary and every tensor start), exact norm
             partials for two ranks, and a full-size gather of synthetic shards.
 llama3-70b  Llama-3-70B list, N_d = 8, rank 7 (8,819,213,312 elements, indices
-            past 2^33): 5 AdamW steps on windows at the shard ends, around 2^31,
-            2^32 and 2^33, at tensor boundaries and at random; exact norm partials
-            of the own and one other rank; the clip coefficient on device.
+            past 2^33): 5 steps as the benchmark runs them (every rank's norm
+            partial and the clip-1.0 coefficient on the device, then AdamW);
+            windows at the shard ends, around 2^31, 2^32 and 2^33, at tensor
+            starts and 32 random 1M windows; the coefficient against the
+            oracle's every step; exact norm partials of two ranks.
 """
 import math
 
@@ -230,6 +232,12 @@ def test_gpt_1p3b_full_size_gather_of_synthetic_shards(zm):
 
 
 def test_llama3_70b_rank7_five_steps_windows(zm):
+    """The benchmark's Llama-3-70B configuration: rank 7 of 8 (S > 2^33), five
+    steps, each with every rank's norm partial and the clip-1.0 coefficient
+    computed on the device, then AdamW with that coefficient. Checked: the
+    coefficient against the oracle's clip of the same partials (every step),
+    two ranks' step-1 partials exactly, and the state on windows at the shard
+    ends, around 2^31, 2^32, 2^33, at tensor starts and 32 random 1M windows."""
     from oracle_workers import grad_sqnorms
     from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep
     w = synth.WORKLOADS["llama3-70b"]
@@ -240,28 +248,35 @@ def test_llama3_70b_rank7_five_steps_windows(zm):
     lo = rank * S
     assert S > 2 ** 33
     note(f"llama3-70b: S={S} (fp32 state {12 * S / 1e9:.1f} GB)")
-    rs = RankStep(plan, rank, 0, Hyper(), 0.0, dev(), gather=False)
+    rs = RankStep(plan, rank, 0, Hyper(), 1.0, dev(), gather=False)
     synth.device_normal_f32(rs.master, w.seed, synth.KIND_MASTER, 0, 0, lo, phi, synth.MASTER_SIGMA)
-    # step-1 norm partials of this rank and of rank 0, and the clip coefficient
+    scratch = torch.empty(S, dtype=torch.int16, device=dev())   # the other ranks' gradients
     d_parts = torch.zeros(w.n_ranks, dtype=torch.float64, device=dev())
-    synth.device_normal_bf16(rs.grad, w.seed, synth.KIND_GRAD, 1, 0, 0, phi, synth.GRAD_SIGMA)
-    zm.zero_grad_sqnorm(rs.grad, d_parts[0:1], workspace=rs.workspace)
     steps = w.steps
+    parts, coefs = [], []
     for t in range(1, steps + 1):
-        synth.device_normal_bf16(rs.grad, w.seed, synth.KIND_GRAD, t, 0, lo, phi, synth.GRAD_SIGMA)
-        if t == 1:
-            zm.zero_grad_sqnorm(rs.grad, d_parts[rank:rank + 1], workspace=rs.workspace)
+        for r in range(w.n_ranks):          # own rank last: rs.grad keeps its gradient
+            rr = r if r < rank else (r + 1 if r < w.n_ranks - 1 else rank)
+            buf = rs.grad if rr == rank else scratch
+            synth.device_normal_bf16(buf, w.seed, synth.KIND_GRAD, t, 0, rr * S, phi, synth.GRAD_SIGMA)
+            zm.zero_grad_sqnorm(buf, d_parts[rr:rr + 1], workspace=rs.workspace)
+        zm.zero_clip_scale(d_parts, 1.0, rs.scale)
         rs.adamw()
-        note(f"llama3-70b: step {t} enqueued")
-    torch.cuda.synchronize()
-    got0, got7 = float(d_parts[0].item()), float(d_parts[rank].item())
+        torch.cuda.synchronize()
+        parts.append(d_parts.cpu().numpy().copy())
+        coefs.append(np.float32(rs.scale.item()))
+        note(f"llama3-70b: step {t} done, clip coefficient {coefs[-1]}")
+    del scratch
+    for t in range(steps):                  # the device coefficient is the oracle's, bit for bit
+        assert coefs[t] == oracle.clip_scale(list(parts[t]), 1.0), (t, coefs[t])
+    assert all(0.0 < c < 1.0 for c in coefs)
 
     rng = np.random.default_rng(70)
     seg_starts = [soff for (_, _, soff, _) in ref.segments(rank)]
-    centers = [0, S, 2 ** 31, 2 ** 32, 2 ** 33] + seg_starts[1:12] + \
-        [int(x) for x in rng.integers(0, S, 8)]
+    centers = [0, S, 2 ** 31, 2 ** 32, 2 ** 33] + seg_starts[1:12]
     wins = [(a, b) for a, b in _windows_in_shards([lo + c for c in centers], 2048, S, w.n_ranks, P)
             if a >= lo and b <= lo + S]
+    wins += [(lo + int(x), lo + int(x) + (1 << 20)) for x in rng.integers(0, S - (1 << 20), 32)]
     note(f"llama3-70b: {len(wins)} windows, {sum(b - a for a, b in wins)} elements")
     for a, b in wins:
         n = b - a
@@ -271,7 +286,7 @@ def test_llama3_70b_rank7_five_steps_windows(zm):
         bits = None
         for t in range(1, steps + 1):
             g = synth.normal_bf16(n, w.seed, synth.KIND_GRAD, t, 0, a, phi, synth.GRAD_SIGMA)
-            p, m, v, bits = oracle.adamw_step(p, m, v, g, t, **HP)
+            p, m, v, bits = oracle.adamw_step(p, m, v, g, t, clip=coefs[t - 1], **HP)
         i0, i1 = a - lo, b - lo
         assert_f32_close(host_f32(rs.master[i0:i1]), p, f"master [{i0},{i1})")
         assert_f32_close(host_f32(rs.exp_avg[i0:i1]), m, f"exp_avg [{i0},{i1})")
@@ -286,17 +301,9 @@ def test_llama3_70b_rank7_five_steps_windows(zm):
     half = len(tasks) // 2
     # chunk values are correctly rounded, so their fp64 sum is within a few ulp
     want0, want7 = math.fsum(vals[:half]), math.fsum(vals[half:])
+    got0, got7 = float(parts[0][0]), float(parts[0][rank])
     assert abs(got0 - want0) <= 1e-12 * want0, (got0, want0)
     assert abs(got7 - want7) <= 1e-12 * want7, (got7, want7)
-    # the coefficient the clip kernel derives from device partials matches the
-    # oracle's on the same (oracle) partials
-    oparts = [want0] * w.n_ranks
-    oparts[rank] = want7
-    d_in = torch.tensor(oparts, dtype=torch.float64, device=dev())
-    d_scale = torch.zeros(1, dtype=torch.float32, device=dev())
-    zm.zero_clip_scale(d_in, 1.0, d_scale)
-    torch.cuda.synchronize()
-    assert np.float32(d_scale.item()) == oracle.clip_scale(oparts, 1.0)
     del rs
     _free_gpu()
 
