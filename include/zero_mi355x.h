@@ -275,7 +275,10 @@ zero_status zero_multi_tensor_adamw_step(float* const* masters, float* const* ex
  * ([ZF] "FSDP-2: Per-Parameter Sharding via DTensor"), tensor t is its ranks'
  * dim-0 chunks stacked in rank order, each read from its chunk's place in
  * that rank's coalesced buffer.
- * shards       host [N_d] of device pointers, each to S bf16 values.
+ * shards       host [N_d] of device pointers, each to S bf16 values. A NULL
+ *              entry skips that rank's segments (their tensor elements are
+ *              left as they are): ranks can be gathered in separate calls, for
+ *              example the other ranks' while the own shard is being updated.
  * tensors      host [T] of device pointers, tensor t to numel_t bf16 values
  *              (may be NULL only for zero-sized tensors). Outputs must not
  *              overlap the shards or each other.

@@ -484,3 +484,34 @@ def test_shard0_flatten_many_tensors_misaligned(zm, n_ranks):
     zm.zero_flatten_params(plan, [b[1:] for b in bufs], flat)
     torch.cuda.synchronize()
     assert_bits_equal(host_u16(flat), oracle.flatten_params_shard0(ref, tensors), "coalesced buffers")
+
+
+@pytest.mark.parametrize("kind", ["flat", "shard0"])
+def test_gather_skips_null_shards(zm, kind):
+    """A NULL shard skips its rank's segments: gathering the other ranks first
+    and the remaining rank afterwards gives the full gather."""
+    rng = np.random.default_rng(1400)
+    dim0 = [int(x) for x in rng.integers(1, 300, 12)]
+    numels = [d * int(k) for d, k in zip(dim0, rng.integers(1, 30, 12))]
+    n_ranks, rank = 4, 2
+    if kind == "flat":
+        ref = oracle.partition_plan(numels, n_ranks, 8)
+        plan = zm.zero_partition_plan(numels, n_ranks, 8)
+        gather = oracle.gather_params
+    else:
+        ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, 8)
+        plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, 8)
+        gather = oracle.gather_params_shard0
+    S = ref.shard_numel
+    shards = [rng.integers(0, 1 << 16, S).astype(np.uint16) for _ in range(n_ranks)]
+    d = [to_dev_u16(x) for x in shards]
+    outs = [torch.full((n,), 0x2468, dtype=torch.int16, device=dev()) for n in numels]
+    zm.zero_gather_params(plan, [None if r == rank else x for r, x in enumerate(d)], outs)
+    torch.cuda.synchronize()
+    marker = [np.full(S, 0x2468, np.uint16) if r == rank else x for r, x in enumerate(shards)]
+    for i, (o, w) in enumerate(zip(outs, gather(ref, marker))):
+        assert_bits_equal(host_u16(o), w, f"others only, tensor {i}")   # own rank untouched
+    zm.zero_gather_params(plan, [x if r == rank else None for r, x in enumerate(d)], outs)
+    torch.cuda.synchronize()
+    for i, (o, w) in enumerate(zip(outs, gather(ref, shards))):
+        assert_bits_equal(host_u16(o), w, f"complete, tensor {i}")

@@ -272,9 +272,9 @@ def zero_shard_adamw_step(master, exp_avg, exp_avg_sq, grad, param_out, step: in
 def zero_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, stream=None) -> None:
     if len(shards) != plan.num_ranks or len(tensors) != plan.num_tensors:
         raise ValueError("need N_d shards and T tensors")
-    sp = (c_vp * max(len(shards), 1))(*[_ptr(s, 2, "shard") for s in shards])
+    sp = (c_vp * max(len(shards), 1))(*[_ptr(s, 2, "shard") for s in shards])   # None skips a rank
     tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
-    ref = shards[0] if len(shards) else None
+    ref = next((x for x in list(shards) + list(tensors) if x is not None), None)
     _check(_gather(plan.handle, sp, tp, _stream(stream, ref) if ref is not None else 0),
            "zero_gather_params")
 
@@ -453,7 +453,9 @@ def prepare_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, strea
         raise ValueError("need N_d shards and T tensors")
     sp = (c_vp * max(len(shards), 1))(*[_ptr(s, 2, "shard") for s in shards])
     tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
-    p = Prepared(_gather, [plan.handle, sp, tp, _stream(stream, shards[0])], "zero_gather_params")
+    ref = next((x for x in list(shards) + list(tensors) if x is not None), None)
+    p = Prepared(_gather, [plan.handle, sp, tp, _stream(stream, ref) if ref is not None else 0],
+                 "zero_gather_params")
     p._keep = (sp, tp, shards, tensors)
     return p
 

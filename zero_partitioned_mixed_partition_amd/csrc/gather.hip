@@ -344,17 +344,19 @@ extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t*
         return fail(ZERO_EINVAL, "zero_gather_params: NULL plan or shards");
     zero_status st = check_tensors(plan, tensors, "zero_gather_params");
     if (st != ZERO_OK) return st;
-    for (int32_t r = 0; r < plan->n_ranks; ++r)
-        if (plan->shard > 0 && shards[r] == nullptr)
-            return fail(ZERO_EINVAL, "zero_gather_params: NULL shard " + std::to_string(r));
-    if (ZERO_GATHER_TENSOR_MAJOR && fits_tensor_major(plan))
+    // A NULL shard skips that rank's segments (a caller gathers ranks as their
+    // shards become ready, or the others while the own shard is still updated).
+    bool all_present = true;
+    for (int32_t r = 0; r < plan->n_ranks; ++r) all_present = all_present && shards[r] != nullptr;
+    if (all_present && ZERO_GATHER_TENSOR_MAJOR && fits_tensor_major(plan))
         return launch_tensors<false>(plan, const_cast<uint16_t* const*>(shards), tensors, stream,
                                      "zero_gather_params launch");
     std::vector<Piece> pieces;
     pieces.reserve(plan->all.size());
     for (const zero_segment& seg : plan->all)
-        pieces.push_back({shards[seg.rank] + seg.shard_offset, tensors[seg.tensor] + seg.tensor_offset,
-                          seg.length});
+        if (shards[seg.rank] != nullptr)
+            pieces.push_back({shards[seg.rank] + seg.shard_offset,
+                              tensors[seg.tensor] + seg.tensor_offset, seg.length});
     return launch_pieces(pieces, stream, "zero_gather_params launch");
 }
 
