@@ -99,11 +99,15 @@ class Plan:
 
     def __init__(self, handle: int):
         self._h = c_vp(handle)
+        # held by the instance: at interpreter exit the module's globals may be
+        # cleared before the last plan is collected
+        self._free = _plan_free
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            _plan_free(h)
+        free = getattr(self, "_free", None)
+        if h is not None and h.value and free is not None:
+            free(h)
             self._h = c_vp(None)
 
     @property
