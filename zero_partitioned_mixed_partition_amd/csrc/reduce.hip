@@ -254,8 +254,21 @@ __global__ __launch_bounds__(kThreads) void sqnorm_scalar(const uint16_t* __rest
 __global__ __launch_bounds__(kThreads) void finish_sum(const double* __restrict__ partials,
                                                        int count, double* __restrict__ out) {
     __shared__ double lds[kThreads / zero::dev::kWave];
+    // Thread t adds partials t, t + kThreads, t + 2*kThreads, ... in that
+    // order; the loads of each batch of 8 are issued together.
+    constexpr int kBatch = 8;
     double s = 0.0;
-    for (int i = threadIdx.x; i < count; i += kThreads) s += partials[i];
+    for (int i0 = threadIdx.x; i0 < count; i0 += kBatch * kThreads) {
+        double x[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int i = i0 + k * kThreads;
+            x[k] = i < count ? partials[i] : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (i0 + k * kThreads < count) s += x[k];
+    }
     const double total = zero::dev::block_sum<kThreads>(s, lds);
     if (threadIdx.x == 0) out[0] = total;
 }
@@ -268,9 +281,17 @@ __global__ void write_zero(double* out) {
 // clip-by-total-norm convention, NaN when the norm is not finite.
 __global__ void clip_kernel(const double* __restrict__ partials, int n, double max_norm,
                             float* __restrict__ scale) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    // One wave: each lane loads one partial of a batch of 64 (all loads in
+    // flight together), then the batch is added in index order, value by value
+    // through cross-lane reads, so the sum is the sequential one.
+    const int lane = threadIdx.x;
     double total = 0.0;
-    for (int i = 0; i < n; ++i) total += partials[i];
+    for (int b = 0; b < n; b += zero::dev::kWave) {
+        const double mine = b + lane < n ? partials[b + lane] : 0.0;
+        const int m = n - b < zero::dev::kWave ? n - b : zero::dev::kWave;
+        for (int j = 0; j < m; ++j) total += __shfl(mine, j, zero::dev::kWave);
+    }
+    if (lane != 0) return;
     float out;
     if (!isfinite(total)) {
         out = __builtin_nanf("");
