@@ -108,7 +108,7 @@ class Plan:
         free = getattr(self, "_free", None)
         if h is not None and h.value and free is not None:
             free(h)
-            self._h = c_vp(None)
+            h.value = None      # no module globals here: they may be gone at exit
 
     @property
     def handle(self) -> c_vp:
