@@ -326,3 +326,41 @@ def test_gpt_1p3b_full_size_flatten(zm):
     assert_bits_equal(host_u16(flat), oracle.flatten_params(ref, host), "flat buffer")
     del tensors, flat
     _free_gpu()
+
+
+@pytest.mark.parametrize("kind", ["flat", "shard0"])
+def test_pieces_longer_than_2p30_flatten_and_gather(zm, kind):
+    """Segments longer than 2^30 elements are split into several kernel
+    pieces, and a Shard(0) tensor of 2^31 elements or more takes the segment
+    kernels instead of the tensor-major one. A full-size round trip: flatten,
+    then gather, must give back every tensor bit for bit, with zero padding."""
+    if kind == "flat":
+        numels, dim0, n_ranks = [(1 << 30) + 4099, 3], None, 1
+        plan = zm.zero_partition_plan(numels, n_ranks, 128)
+    else:
+        rows = (1 << 20) + 1
+        numels, dim0, n_ranks = [rows * 2048, 5 * 7], [rows, 5], 2
+        plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, 128)
+    note(f"long pieces ({kind}): numels={numels} P={plan.padded_numel} S={plan.shard_numel}")
+    offs = [0, numels[0]]
+    tensors = [torch.empty(n, dtype=torch.int16, device=dev()) for n in numels]
+    for t, off in zip(tensors, offs):
+        synth.device_normal_bf16(t, 95, synth.KIND_PARAM, 0, 0, off, sum(numels), 0.02)
+    flat = torch.full((plan.padded_numel,), 0x1111, dtype=torch.int16, device=dev())
+    zm.zero_flatten_params(plan, tensors, flat)
+    S = plan.shard_numel
+    back = [torch.full((n,), 0x2222, dtype=torch.int16, device=dev()) for n in numels]
+    zm.zero_gather_params(plan, [flat[r * S:(r + 1) * S] for r in range(n_ranks)], back)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(tensors, back)):
+        assert torch.equal(a, b), f"tensor {i} round trip"
+    # the padding is zero and every flat element outside it holds some tensor element
+    covered = torch.zeros(plan.padded_numel, dtype=torch.bool, device=dev())
+    for r in range(n_ranks):
+        for (t, toff, soff, ln) in plan.segments(r):
+            a = r * S + soff
+            assert torch.equal(flat[a:a + ln], tensors[t][toff:toff + ln]), (r, t)
+            covered[a:a + ln] = True
+    assert int(((flat != 0) & ~covered).sum().item()) == 0, "padding is zero"
+    del tensors, back, flat, covered
+    _free_gpu()
