@@ -176,12 +176,15 @@ zero_status zero_plan_memory_bytes(const zero_plan* plan, int32_t stage, int32_t
  *              values this call wrote (0 if it wrote nothing). Deterministic for a
  *              given device.
  * workspace    device, required when sqnorm_out is non-null; at least
- *              zero_sqnorm_workspace_bytes() bytes, 8-byte aligned. It holds
- *              per-workgroup partials between the call's two kernels, so
- *              calls that may run at the same time (on different streams)
- *              need separate workspaces; calls on one stream may share one.
+ *              zero_sqnorm_workspace_bytes() bytes, 8-byte aligned, owned by
+ *              the caller. It holds the per-workgroup partials between the
+ *              call's two kernels; it needs no initialisation and its contents
+ *              on return are unspecified. Calls that may run
+ *              at the same time (on different streams) need separate
+ *              workspaces; calls on one stream may share one.
  * Errors: ZERO_EINVAL (null plan/replicas/shard_grad, a null replica pointer,
- * R out of range, rank out of range, bad window); ZERO_ENOSPACE; ZERO_EHIP. */
+ * R out of range, rank out of range, bad window, workspace not 8-byte
+ * aligned); ZERO_ENOSPACE; ZERO_EHIP. */
 zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
                                    const uint16_t* const* replicas, int32_t n_replicas,
                                    int64_t begin, int64_t count, uint16_t* shard_grad,
@@ -194,8 +197,10 @@ zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
  * square is exact), written to device sqnorm_out[0]. Two fixed-order
  * reduction levels, no floating-point atomics: the result is reproducible on
  * a given device. The norm clip is not on the cited pages; the global norm it
- * needs is the sum of these partials over every rank.
- * Errors: ZERO_EINVAL (null pointers with n > 0, n < 0); ZERO_ENOSPACE; ZERO_EHIP. */
+ * needs is the sum of these partials over every rank. workspace as for
+ * zero_grad_reduce_shard.
+ * Errors: ZERO_EINVAL (null pointers with n > 0, n < 0, workspace not 8-byte
+ * aligned); ZERO_ENOSPACE; ZERO_EHIP. */
 zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double* sqnorm_out,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 

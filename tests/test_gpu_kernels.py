@@ -208,6 +208,68 @@ def test_sqnorm_constant_closed_form_and_unaligned(zm):
     assert out.item() == n * cv * cv
 
 
+def test_norm_workspace_needs_no_initialisation(zm):
+    """The workspace may hold anything before a call (here: all ones, then
+    random bytes) and may be shared by calls of different grid sizes in turn;
+    every result is the oracle's, and equal to a fresh workspace's."""
+    nbytes = zm.zero_sqnorm_workspace_bytes()
+    sizes = [(1 << 22) + 5, 2049, 9, 50_000_001, 1 << 20]
+    grads = [synth.normal_bf16(n, 21, synth.KIND_GRAD, 2, 0, sigma=1e-3) for n in sizes]
+    d = [to_dev_u16(g) for g in grads]
+    want = [oracle.sqnorm(g) for g in grads]
+    rng = np.random.default_rng(5)
+    for fill in ("ones", "random"):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev())
+        if fill == "ones":
+            ws.fill_(255)
+        else:
+            ws.copy_(torch.from_numpy(rng.integers(0, 256, nbytes, dtype=np.uint8)))
+        outs = torch.full((2 * len(sizes),), -1.0, dtype=torch.float64, device=dev())
+        for i, g in enumerate(d):
+            zm.zero_grad_sqnorm(g, outs[i:i + 1], workspace=ws)
+        for i, g in enumerate(d):            # again, in reverse: other grids before each
+            j = len(sizes) - 1 - i
+            zm.zero_grad_sqnorm(d[j], outs[len(sizes) + j:len(sizes) + j + 1], workspace=ws)
+        torch.cuda.synchronize()
+        got = outs.cpu().numpy()
+        fresh = torch.zeros(len(sizes), dtype=torch.float64, device=dev())
+        for i, g in enumerate(d):
+            zm.zero_grad_sqnorm(g, fresh[i:i + 1])
+        torch.cuda.synchronize()
+        for i, w in enumerate(want):
+            note(f"fill={fill} n={sizes[i]}")
+            assert abs(got[i] - w) <= 1e-12 * w, (sizes[i], got[i], w)
+            assert got[i] == got[len(sizes) + i] == fresh[i].item()
+    # a reduce with its norm on the same workspace, between the sqnorm calls
+    numels = [300_001, 17, 4096 * 1000]
+    plan = zm.zero_partition_plan(numels, 4, 128)
+    ref = oracle.partition_plan(numels, 4, 128)
+    reps = [synth.normal_bf16(ref.padded_numel, 22, synth.KIND_REPLICA, 1, k, 0, ref.numel, 0.05)
+            for k in range(3)]
+    d_reps = [to_dev_u16(r) for r in reps]
+    sq = torch.zeros(2, dtype=torch.float64, device=dev())
+    out = torch.zeros(ref.shard_numel, dtype=torch.int16, device=dev())
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev()).fill_(255)
+    zm.zero_grad_sqnorm(d[0], sq[0:1], workspace=ws)
+    zm.zero_grad_reduce_shard(plan, 1, d_reps, 0, ref.padded_numel, out, sqnorm_out=sq[1:2],
+                              workspace=ws)
+    torch.cuda.synchronize()
+    want_grad = np.zeros(ref.shard_numel, np.uint16)
+    oracle.reduce_shard(ref, 1, reps, 0, want_grad)
+    assert_bits_equal(host_u16(out), want_grad, "reduce on a shared workspace")
+    w1 = oracle.sqnorm(want_grad)
+    assert abs(sq[1].item() - w1) <= 1e-12 * w1
+    assert sq[0].item() == got[0]
+
+
+def test_norm_workspace_alignment_is_checked(zm):
+    ws = torch.zeros(zm.zero_sqnorm_workspace_bytes() + 8, dtype=torch.uint8, device=dev())
+    g = torch.zeros(64, dtype=torch.int16, device=dev())
+    out = torch.zeros(1, dtype=torch.float64, device=dev())
+    with pytest.raises(zm.ZeroError):
+        zm.zero_grad_sqnorm(g, out, workspace=ws[4:])
+
+
 @pytest.mark.parametrize("partials,max_norm", [
     ([0.25, 0.75], 0.5), ([0.25, 0.75], 2.0), ([3.0], 0.0), ([1.0, math.inf], 1.0),
     ([124.44096632917478], 1.0), ([1e-30] * 64, 1.0), ([0.0], 1.0)])

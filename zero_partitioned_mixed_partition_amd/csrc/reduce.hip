@@ -336,6 +336,8 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
         return fail(ZERO_EINVAL, "zero_grad_reduce_shard: window outside [0, P)");
     if (sqnorm_out != nullptr) {
         if (workspace == nullptr) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: NULL workspace");
+        if (!aligned(workspace, 8))
+            return fail(ZERO_EINVAL, "zero_grad_reduce_shard: workspace not 8-byte aligned");
         if (workspace_bytes < zero_sqnorm_workspace_bytes())
             return fail(ZERO_ENOSPACE, "zero_grad_reduce_shard: workspace too small");
     }
@@ -398,6 +400,8 @@ extern "C" zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double*
     if (n < 0) return fail(ZERO_EINVAL, "zero_grad_sqnorm: n < 0");
     if (sqnorm_out == nullptr || (n > 0 && grad == nullptr) || workspace == nullptr)
         return fail(ZERO_EINVAL, "zero_grad_sqnorm: NULL pointer");
+    if (!aligned(workspace, 8))
+        return fail(ZERO_EINVAL, "zero_grad_sqnorm: workspace not 8-byte aligned");
     if (workspace_bytes < zero_sqnorm_workspace_bytes())
         return fail(ZERO_ENOSPACE, "zero_grad_sqnorm: workspace too small");
     double* partials = static_cast<double*>(workspace);
