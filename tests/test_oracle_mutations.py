@@ -235,3 +235,96 @@ def test_gather_reversed_shards_is_caught(monkeypatch):
         return real(plan, list(reversed(shards)))
     monkeypatch.setattr(oracle, "gather_params", reversed_gather)
     assert _caught([lambda s=s: num.test_gather_round_trip_and_segments(s) for s in range(10)])
+
+
+# ----------------------------------------------------------------------------- Shard(0), flatten
+
+import test_oracle_shard0 as sh0  # noqa: E402
+from oracle.plan import Shard0Plan  # noqa: E402
+
+
+def _shard0_with(mistake):
+    """partition_plan_shard0 carrying one mistake."""
+    def partition_plan_shard0(numels, dim0, n_ranks, align=128):
+        numels = [int(n) for n in numels]
+        dim0 = [int(d) for d in dim0]
+        offsets, rows_l, inner_l, buf = [], [], [], 0
+        for n, d in zip(numels, dim0):
+            inner = n // d if n else 0
+            rows = -(-d // n_ranks) if n else 0
+            if mistake == "floor_rows" and n:
+                rows = max(d // n_ranks, 1)
+            if mistake == "element_chunks" and n:      # cut the flattened tensor, not its rows
+                rows, inner = -(-n // n_ranks), 1
+            offsets.append(buf)
+            rows_l.append(rows)
+            inner_l.append(inner)
+            buf += rows * inner
+            if mistake == "chunks_unpadded" and n:     # the last rank's short chunk sets the stride
+                buf -= rows * inner - max(d - (n_ranks - 1) * rows, 0) * inner
+        s = buf if mistake == "ignore_align" else -(-buf // align) * align
+        return Shard0Plan(numels, n_ranks, align, offsets, sum(numels), s * n_ranks, s,
+                          dim0=dim0, chunk_rows=rows_l, inner=inner_l)
+    return partition_plan_shard0
+
+
+SHARD0_PINS = [sh0.test_shard0_hand_worked,
+               *[lambda s=s: sh0.test_shard0_matches_torch_chunk(s) for s in range(25)],
+               *[lambda s=s: sh0.test_shard0_round_trip_and_coverage(s) for s in range(10)]]
+
+
+def _caught_any(checks) -> bool:
+    """As _caught, but a mistake may also surface as an exception other than an
+    assertion (an index past a buffer, a shape mismatch)."""
+    for check in checks:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("mistake", ["floor_rows", "element_chunks", "chunks_unpadded",
+                                     "ignore_align"])
+def test_shard0_plan_mistakes_are_caught(monkeypatch, mistake):
+    monkeypatch.setattr(oracle, "partition_plan_shard0", _shard0_with(mistake))
+    assert _caught_any(SHARD0_PINS), mistake
+
+
+def test_unmutated_shard0_passes_its_pins():
+    assert not _caught_any(SHARD0_PINS)
+
+
+@pytest.mark.parametrize("mistake", ["padding_not_zeroed", "ranks_reversed"])
+def test_shard0_flatten_gather_mistakes_are_caught(monkeypatch, mistake):
+    real_flatten, real_gather = oracle.flatten_params_shard0, oracle.gather_params_shard0
+    if mistake == "padding_not_zeroed":
+        def flatten(plan, tensors):
+            flat = real_flatten(plan, tensors)
+            covered = np.zeros(plan.padded_numel, bool)
+            for r in range(plan.n_ranks):
+                for (_, _, soff, ln) in plan.segments(r):
+                    covered[r * plan.shard_numel + soff:r * plan.shard_numel + soff + ln] = True
+            flat[~covered] = 0x3F80                  # what an uncleared buffer might hold
+            return flat
+        monkeypatch.setattr(oracle, "flatten_params_shard0", flatten)
+    else:
+        def gather(plan, shards):
+            return real_gather(plan, list(reversed(shards)))
+        monkeypatch.setattr(oracle, "gather_params_shard0", gather)
+    assert _caught_any([lambda s=s: sh0.test_shard0_round_trip_and_coverage(s) for s in range(10)]), \
+        mistake
+
+
+@pytest.mark.parametrize("mistake", ["offset_off_by_one", "padding_not_zeroed"])
+def test_flatten_mistakes_are_caught(monkeypatch, mistake):
+    def flatten(plan, tensors):
+        flat = np.zeros(plan.padded_numel, dtype=np.uint16)
+        if mistake == "padding_not_zeroed":
+            flat[:] = 0x3F80
+        for t, off, n in zip(tensors, plan.offsets, plan.numels):
+            o = off + (1 if mistake == "offset_off_by_one" and off else 0)
+            flat[o:o + n] = np.asarray(t, dtype=np.uint16)[:len(flat[o:o + n])]
+        return flat
+    monkeypatch.setattr(oracle, "flatten_params", flatten)
+    assert _caught_any([num.test_flatten_hand_worked_and_round_trips]), mistake
