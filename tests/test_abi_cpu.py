@@ -194,3 +194,37 @@ def test_builder_loads_without_importing_the_package():
             "assert 'zero_partitioned_mixed_partition_amd' not in sys.modules; print('ok')" % ROOT)
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stderr
+
+
+def test_binding_refuses_buffers_shorter_than_the_call_touches(zm):
+    """The C ABI sees bare device pointers; the binding checks every buffer's
+    length first, so a short tensor raises ValueError naming it (here with CPU
+    tensors: the check comes before any pointer is taken)."""
+    import torch
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    f = lambda n: torch.zeros(n, dtype=torch.float32)      # noqa: E731
+    h = lambda n: torch.zeros(n, dtype=torch.int16)        # noqa: E731
+    d = lambda n: torch.zeros(n, dtype=torch.float64)      # noqa: E731
+    with pytest.raises(ValueError, match="master"):
+        zm.zero_shard_adamw_step(f(8), f(16), f(16), h(16), h(16), 1, n=16, **hp)
+    with pytest.raises(ValueError, match="param_out"):
+        zm.zero_shard_adamw_step(f(16), f(16), f(16), h(16), h(8), 1, **hp)
+    with pytest.raises(ValueError, match="grad"):
+        zm.zero_grad_sqnorm(h(10), d(1), n=11)
+    with pytest.raises(ValueError, match="sqnorm_out"):
+        zm.zero_grad_sqnorm(h(10), d(0))
+    with pytest.raises(ValueError, match="partials"):
+        zm.zero_clip_scale(d(3), 1.0, f(1), n_partials=4)
+    plan = zm.zero_partition_plan([100, 28], 2, 8)       # P = 128, S = 64
+    with pytest.raises(ValueError, match="replica"):
+        zm.zero_grad_reduce_shard(plan, 0, [h(128), h(127)], 0, 128, h(64))
+    with pytest.raises(ValueError, match="shard_grad"):
+        zm.zero_grad_reduce_shard(plan, 0, [h(128)], 0, 128, h(63))
+    with pytest.raises(ValueError, match="tensor 1"):
+        zm.zero_gather_params(plan, [h(64), h(64)], [h(100), h(27)])
+    with pytest.raises(ValueError, match="shard"):
+        zm.zero_gather_params(plan, [h(64), h(60)], [h(100), h(28)])
+    with pytest.raises(ValueError, match="flat"):
+        zm.zero_flatten_params(plan, [h(100), h(28)], h(127))
+    with pytest.raises(ValueError, match="tensor 0"):
+        zm.zero_flatten_params(plan, [h(99), h(28)], h(128))

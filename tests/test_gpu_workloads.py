@@ -202,3 +202,33 @@ def test_bench_pipeline_matches_oracle(zm, name):
         assert (setup.state_arrays()[0][~mask] == 0).all(), "padding stays zero"
     for i, (a, b) in enumerate(zip(setup.rs.tensors, out["tensors"])):
         assert_bf16_close(host_u16(a), b, f"gathered tensor {i}")
+
+
+def test_rank_step_fresh_replica_buffers_are_not_retained(zm):
+    """A caller that hands RankStep new gradient buffers every step (as a fresh
+    allocation per backward pass would) gets correct reduces, and the step keeps
+    one marshalled call per window: earlier buffers are released."""
+    import gc
+    import weakref
+
+    from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep
+    numels = [1000, 37, 4096, 3]
+    plan = zm.zero_partition_plan(numels, 4, 128)
+    ref = oracle.partition_plan(numels, 4, 128)
+    P = ref.padded_numel
+    rs = RankStep(plan, 2, 1, Hyper(), 1.0, dev(), gather=False)
+    held = []
+    for k in range(4):
+        reps_h = [synth.normal_bf16(P, 30 + k, synth.KIND_REPLICA, 1, j, 0, ref.numel, 0.05)
+                  for j in range(3)]
+        reps = [to_dev_u16(r) for r in reps_h]
+        held.append(weakref.ref(reps[0]))
+        rs.reduce([(0, P, reps)])
+        torch.cuda.synchronize()
+        want = np.zeros(ref.shard_numel, np.uint16)
+        oracle.reduce_shard(ref, 2, reps_h, 0, want)
+        assert_bits_equal(host_u16(rs.grad), want, f"reduce call {k}")
+        del reps
+    gc.collect()
+    assert len(rs._calls) == 1
+    assert all(r() is None for r in held[:-1]), "earlier replica buffers are still referenced"

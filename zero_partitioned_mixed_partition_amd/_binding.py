@@ -207,6 +207,43 @@ def _ptr(t, elem_size: int, what: str) -> int:
     return t.data_ptr()
 
 
+def _need(t, n: int, what: str) -> None:
+    """The C ABI receives bare device pointers and cannot see buffer sizes:
+    refuse here a tensor shorter than what the call will read or write."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{what} holds {t.numel()} elements; the call touches {n}")
+
+
+def _check_reduce_args(plan: "Plan", replicas, count: int, shard_grad, sqnorm_out) -> None:
+    for r in replicas:
+        _need(r, count, "a replica")
+    _need(shard_grad, plan.shard_numel, "shard_grad")
+    _need(sqnorm_out, 1, "sqnorm_out")
+
+
+def _check_gather_args(plan: "Plan", shards, tensors) -> None:
+    if len(shards) != plan.num_ranks or len(tensors) != plan.num_tensors:
+        raise ValueError("need N_d shards and T tensors")
+    for sh in shards:
+        _need(sh, plan.shard_numel, "a shard")
+    for i, t in enumerate(tensors):
+        _need(t, plan.tensor_numel(i), f"tensor {i}")
+
+
+def _check_flatten_args(plan: "Plan", tensors, flat) -> None:
+    if len(tensors) != plan.num_tensors:
+        raise ValueError("need T tensors")
+    _need(flat, plan.padded_numel, "flat")
+    for i, t in enumerate(tensors):
+        _need(t, plan.tensor_numel(i), f"tensor {i}")
+
+
+def _check_adamw_args(n: int, arrays, clip_scale) -> None:
+    for t, what in zip(arrays, ("master", "exp_avg", "exp_avg_sq", "grad", "param_out")):
+        _need(t, n, what)
+    _need(clip_scale, 1, "clip_scale")
+
+
 _ws_cache = {}
 
 
@@ -231,6 +268,7 @@ def zero_sqnorm_workspace_bytes() -> int:
 def zero_grad_reduce_shard(plan: Plan, rank: int, replicas: Sequence, begin: int, count: int,
                            shard_grad, sqnorm_out=None, workspace=None, stream=None) -> None:
     """replicas: R device tensors (2-byte elements) covering flat window [begin, begin+count)."""
+    _check_reduce_args(plan, replicas, count, shard_grad, sqnorm_out)
     ptrs = (c_vp * max(len(replicas), 1))(*[_ptr(r, 2, "replica") for r in replicas])
     out = _ptr(shard_grad, 2, "shard_grad")
     sq = _ptr(sqnorm_out, 8, "sqnorm_out")
@@ -244,6 +282,8 @@ def zero_grad_reduce_shard(plan: Plan, rank: int, replicas: Sequence, begin: int
 
 def zero_grad_sqnorm(grad, sqnorm_out, n: Optional[int] = None, workspace=None, stream=None) -> None:
     n = grad.numel() if n is None else n
+    _need(grad, n, "grad")
+    _need(sqnorm_out, 1, "sqnorm_out")
     if workspace is None:
         workspace = sqnorm_workspace(grad.device)
     _check(_sqnorm(_ptr(grad, 2, "grad"), n, _ptr(sqnorm_out, 8, "sqnorm_out"), workspace.data_ptr(),
@@ -254,6 +294,8 @@ def zero_grad_sqnorm(grad, sqnorm_out, n: Optional[int] = None, workspace=None, 
 def zero_clip_scale(partials, max_norm: float, scale_out, n_partials: Optional[int] = None,
                     stream=None) -> None:
     n = partials.numel() if n_partials is None else n_partials
+    _need(partials, n, "partials")
+    _need(scale_out, 1, "scale_out")
     _check(_clip(_ptr(partials, 8, "partials"), n, float(max_norm), _ptr(scale_out, 4, "scale_out"),
                  _stream(stream, partials)), "zero_clip_scale")
 
@@ -262,10 +304,7 @@ def zero_shard_adamw_step(master, exp_avg, exp_avg_sq, grad, param_out, step: in
                           beta1: float, beta2: float, eps: float, weight_decay: float,
                           clip_scale=None, n: Optional[int] = None, stream=None) -> None:
     n = master.numel() if n is None else n
-    for t, what in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad"),
-                    (param_out, "param_out")):
-        if t.numel() < n:
-            raise ValueError(f"{what} holds fewer than n elements")
+    _check_adamw_args(n, (master, exp_avg, exp_avg_sq, grad, param_out), clip_scale)
     _check(_adamw(_ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
                   _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(grad, 2, "grad"),
                   _ptr(param_out, 2, "param_out"), n, step, lr, beta1, beta2, eps, weight_decay,
@@ -274,8 +313,7 @@ def zero_shard_adamw_step(master, exp_avg, exp_avg_sq, grad, param_out, step: in
 
 
 def zero_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, stream=None) -> None:
-    if len(shards) != plan.num_ranks or len(tensors) != plan.num_tensors:
-        raise ValueError("need N_d shards and T tensors")
+    _check_gather_args(plan, shards, tensors)
     sp = (c_vp * max(len(shards), 1))(*[_ptr(s, 2, "shard") for s in shards])   # None skips a rank
     tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
     ref = next((x for x in list(shards) + list(tensors) if x is not None), None)
@@ -285,10 +323,7 @@ def zero_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, stream=N
 
 def zero_flatten_params(plan: Plan, tensors: Sequence, flat, stream=None) -> None:
     """tensors: T device buffers (2-byte elements, numel_t each); flat: device [P]."""
-    if len(tensors) != plan.num_tensors:
-        raise ValueError("need T tensors")
-    if flat.numel() < plan.padded_numel:
-        raise ValueError("flat holds fewer than P elements")
+    _check_flatten_args(plan, tensors, flat)
     tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
     _check(_flatten(plan.handle, tp, _ptr(flat, 2, "flat"), _stream(stream, flat)),
            "zero_flatten_params")
@@ -307,6 +342,7 @@ def prepare_multi_tensor_adamw_step(masters, exp_avgs, exp_avg_sqs, grads, param
     for lst in lists[1:]:
         if any(x.numel() < n for x, n in zip(lst, numels)):
             raise ValueError("a tensor holds fewer elements than its master")
+    _need(clip_scale, 1, "clip_scale")
     tabs = []
     for lst, size, what in zip(lists, (4, 4, 4, 2, 2), ("master", "exp_avg", "exp_avg_sq", "grad", "param")):
         tabs.append((c_vp * max(T, 1))(*[_ptr(x, size, what) for x in lst]))
@@ -357,6 +393,10 @@ def zero_offload_adamw_step(h_master, h_exp_avg, h_exp_avg_sq, d_grad, d_param_o
                             stream=None) -> None:
     """Host fp32 state (CPU tensors), device bf16 grad/params, pinned host staging."""
     n = h_master.numel()
+    for t, what in ((h_exp_avg, "exp_avg"), (h_exp_avg_sq, "exp_avg_sq"), (d_grad, "d_grad"),
+                    (d_param_out, "d_param_out")):
+        _need(t, n, what)
+    _need(clip_scale, 1, "clip_scale")
     if not h_staging.is_pinned():
         raise ValueError("h_staging must be pinned host memory")
     _check(_offload(_host_ptr(h_master, 4, "master"), _host_ptr(h_exp_avg, 4, "exp_avg"),
@@ -395,6 +435,7 @@ class Prepared:
 
 def prepare_grad_reduce_shard(plan: Plan, rank: int, replicas: Sequence, begin: int, count: int,
                               shard_grad, sqnorm_out, workspace, stream) -> Prepared:
+    _check_reduce_args(plan, replicas, count, shard_grad, sqnorm_out)
     ptrs = (c_vp * max(len(replicas), 1))(*[_ptr(r, 2, "replica") for r in replicas])
     ws = workspace.data_ptr() if workspace is not None else 0
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -406,6 +447,7 @@ def prepare_grad_reduce_shard(plan: Plan, rank: int, replicas: Sequence, begin: 
 
 
 def prepare_clip_scale(partials, max_norm: float, scale_out, stream) -> Prepared:
+    _need(scale_out, 1, "scale_out")
     p = Prepared(_clip, [_ptr(partials, 8, "partials"), partials.numel(), float(max_norm),
                          _ptr(scale_out, 4, "scale_out"), _stream(stream, partials)],
                  "zero_clip_scale")
@@ -418,9 +460,7 @@ def prepare_shard_adamw_step(master, exp_avg, exp_avg_sq, grad, param_out, lr: f
                              ) -> Prepared:
     """Call the result with the 1-based step number."""
     n = master.numel()
-    for t in (exp_avg, exp_avg_sq, grad, param_out):
-        if t.numel() < n:
-            raise ValueError("an array holds fewer elements than master")
+    _check_adamw_args(n, (master, exp_avg, exp_avg_sq, grad, param_out), clip_scale)
     p = Prepared(_adamw, [_ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
                           _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(grad, 2, "grad"),
                           _ptr(param_out, 2, "param_out"), n, 1, lr, beta1, beta2, eps,
@@ -439,6 +479,7 @@ def prepare_offload_adamw_step(h_master, h_exp_avg, h_exp_avg_sq, d_grad, d_para
     for t in (h_exp_avg, h_exp_avg_sq, d_grad, d_param_out):
         if t.numel() < n:
             raise ValueError("an array holds fewer elements than master")
+    _need(clip_scale, 1, "clip_scale")
     if not h_staging.is_pinned():
         raise ValueError("h_staging must be pinned host memory")
     p = Prepared(_offload, [_host_ptr(h_master, 4, "master"), _host_ptr(h_exp_avg, 4, "exp_avg"),
@@ -453,8 +494,7 @@ def prepare_offload_adamw_step(h_master, h_exp_avg, h_exp_avg_sq, d_grad, d_para
 
 
 def prepare_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, stream) -> Prepared:
-    if len(shards) != plan.num_ranks or len(tensors) != plan.num_tensors:
-        raise ValueError("need N_d shards and T tensors")
+    _check_gather_args(plan, shards, tensors)
     sp = (c_vp * max(len(shards), 1))(*[_ptr(s, 2, "shard") for s in shards])
     tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
     ref = next((x for x in list(shards) + list(tensors) if x is not None), None)
@@ -465,8 +505,7 @@ def prepare_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, strea
 
 
 def prepare_flatten_params(plan: Plan, tensors: Sequence, flat, stream) -> Prepared:
-    if len(tensors) != plan.num_tensors or flat.numel() < plan.padded_numel:
-        raise ValueError("need T tensors and a flat buffer of P elements")
+    _check_flatten_args(plan, tensors, flat)
     tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
     p = Prepared(_flatten, [plan.handle, tp, _ptr(flat, 2, "flat"), _stream(stream, flat)],
                  "zero_flatten_params")

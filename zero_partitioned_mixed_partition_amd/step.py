@@ -100,15 +100,17 @@ class RankStep:
         p[self.rank] = 0.0
         self.partials[:self.plan.num_ranks].copy_(p.to(self.device))
 
-    def _prepared(self, key, stream, build):
-        """Marshal a call's arguments once per (call, stream); reuse afterwards."""
+    def _prepared(self, key, stream, build, sig=None):
+        """Marshal a call's arguments once and reuse them while the stream and
+        `sig` (the caller's buffers) stay the same. One entry per key: a new
+        signature replaces the old entry and releases the buffers it held."""
         if stream is None:
             stream = torch.cuda.current_stream(self.device).cuda_stream
         cached = self._calls.get(key)
-        if cached is None or cached[0] != stream:
-            cached = (stream, build(stream))
+        if cached is None or cached[0] != stream or cached[1] != sig:
+            cached = (stream, sig, build(stream))
             self._calls[key] = cached
-        return cached[1]
+        return cached[2]
 
     def reduce(self, windows: Sequence[Tuple[int, int, Sequence[torch.Tensor]]], stream=None):
         """windows: (begin, count, replica tensors) per window, in arrival order."""
@@ -116,10 +118,10 @@ class RankStep:
             raise ValueError("window count differs from the one the step was built for")
         nd = self.plan.num_ranks
         for w, (begin, count, reps) in enumerate(windows):
-            key = ("reduce", w, begin, count, tuple(r.data_ptr() for r in reps))
-            self._prepared(key, stream, lambda st: zb.prepare_grad_reduce_shard(
+            sig = (begin, count, tuple(r.data_ptr() for r in reps))
+            self._prepared(("reduce", w), stream, lambda st: zb.prepare_grad_reduce_shard(
                 self.plan, self.rank, reps, begin, count, self.grad,
-                self.partials[nd + w:nd + w + 1], self.workspace, st))()
+                self.partials[nd + w:nd + w + 1], self.workspace, st), sig)()
 
     def clip(self, stream=None):
         if self.max_norm > 0:
