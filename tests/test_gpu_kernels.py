@@ -405,14 +405,15 @@ def test_shard0_gather_and_flatten(zm, seed):
         assert_bits_equal(host_u16(a), b, f"tensor {i}")
 
 
-@pytest.mark.parametrize("kind,n_ranks", [("flat", 1), ("flat", 64), ("flat", 65), ("flat", 100),
-                                          ("shard0", 64), ("shard0", 97)])
-def test_gather_rank_counts_many_tensors_misaligned(zm, kind, n_ranks):
-    """Up to 64 ranks the gather finds each element's rank by arithmetic; above
-    that it copies plan segments. Both must agree with the oracle, over more
-    tensors than one launch carries and with 2-byte-misaligned destinations."""
+@pytest.mark.parametrize("kind,n_ranks,t", [("flat", 1, 150), ("flat", 64, 150), ("flat", 65, 150),
+                                            ("flat", 100, 150), ("shard0", 3, 400), ("shard0", 8, 400),
+                                            ("shard0", 9, 300), ("shard0", 64, 150), ("shard0", 97, 150)])
+def test_gather_rank_counts_many_tensors_misaligned(zm, kind, n_ranks, t):
+    """Up to 64 ranks the gather finds each element's rank by arithmetic (the
+    compact descriptor table up to 8 ranks, the wide one above); above that it
+    copies plan segments. All must agree with the oracle, over more tensors
+    than one launch carries and with 2-byte-misaligned destinations."""
     rng = np.random.default_rng(900 + n_ranks)
-    t = 150
     dim0 = [int(x) for x in rng.integers(1, 300, t)]
     numels = [d * int(k) for d, k in zip(dim0, rng.integers(1, 12, t))]
     note(f"gather {kind} N_d={n_ranks} T={t} Phi={sum(numels)}")
@@ -528,13 +529,12 @@ def test_reduce_two_groups_per_pass_full_array(zm, R):
     assert abs(sq.item() - want_sq) <= 1e-12 * want_sq
 
 
-@pytest.mark.parametrize("n_ranks", [3, 8, 64, 97])
-def test_shard0_flatten_many_tensors_misaligned(zm, n_ranks):
+@pytest.mark.parametrize("n_ranks,t", [(3, 400), (8, 400), (9, 300), (64, 150), (97, 150)])
+def test_shard0_flatten_many_tensors_misaligned(zm, n_ranks, t):
     """Shard(0) flatten over more tensors than one launch carries, from
     2-byte-misaligned sources, padding included, against the oracle (64 ranks
-    and fewer: tensor-major kernel; 97: segment copies)."""
+    and fewer: tensor-major kernel, compact table up to 8; 97: segment copies)."""
     rng = np.random.default_rng(1300 + n_ranks)
-    t = 150
     dim0 = [int(x) for x in rng.integers(1, 400, t)]
     numels = [d * int(k) for d, k in zip(dim0, rng.integers(1, 40, t))]
     note(f"shard0 flatten N_d={n_ranks} T={t} Phi={sum(numels)}")

@@ -126,19 +126,31 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
 // than 2^31 elements), and when chunk_t >= kChunk its lanes lie in that rank
 // or the next, two workgroup-uniform shard pointers. Smaller chunks take a
 // per-lane path.
-constexpr int kMaxRanks = 64;                   // shard pointer table in the kernel arguments
-constexpr int kTens = 120;                      // tensors per launch
-
+//
+// The descriptors travel in the kernel arguments (4 KB). The wide table has
+// room for 64 rank pointers and 64-bit chunk offsets (127 tensors per launch);
+// plans with at most 8 ranks and shards under 2^31 elements use the compact
+// table, 8 rank pointers and 32-bit offsets, which fits 167 tensors: GPT-2
+// small's 148 in one launch instead of two.
+template <int kR, typename Off>
 struct TensorBatch {
-    uint16_t* shards[kMaxRanks];  // rank buffers (read by the gather, written by the flatten)
+    using OffT = Off;
+    static constexpr int kRanks = kR;
+    static constexpr int kTens = (4096 - 8 * kR - 8) / (8 + static_cast<int>(sizeof(Off)) + 12);
+    uint16_t* shards[kR];         // rank buffers (read by the gather, written by the flatten)
     uint16_t* dst[kTens];         // tensors (written by the gather, read by the flatten)
-    int64_t off[kTens];          // the chunk's start in a rank's coalesced buffer
+    Off off[kTens];               // the chunk's start in a rank's coalesced buffer
     int32_t numel[kTens];
     int32_t chunk[kTens];
     int32_t first_block[kTens + 1];
     int32_t n;
 };
-static_assert(sizeof(TensorBatch) <= 4096, "kernel arguments are limited to 4 KB");
+using WideBatch = TensorBatch<64, int64_t>;
+using CompactBatch = TensorBatch<8, int32_t>;
+constexpr int kMaxRanks = WideBatch::kRanks;
+static_assert(sizeof(WideBatch) <= 4096 && sizeof(CompactBatch) <= 4096,
+              "kernel arguments are limited to 4 KB");
+static_assert(WideBatch::kTens >= 120 && CompactBatch::kTens >= 160, "table capacities");
 
 // kScatter = false: the gather (rank buffers -> tensors); true: the flatten
 // (tensors -> rank buffers), the same index map copied the other way.
@@ -147,8 +159,8 @@ __device__ __forceinline__ void copy_elem(uint16_t* tens, uint16_t* buf) {
     if (kScatter) *buf = *tens; else *tens = *buf;
 }
 
-template <bool kScatter>
-__global__ __launch_bounds__(kThreads) void gather_tensor_kernel(TensorBatch b) {
+template <bool kScatter, class Batch>
+__global__ __launch_bounds__(kThreads) void gather_tensor_kernel(Batch b) {
     typedef typename LaneBits<kLane>::T V;
     const int64_t blk = blockIdx.x;
     int lo = 0, hi = b.n - 1;
@@ -167,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void gather_tensor_kernel(TensorBatch b) 
     if (chunk >= kChunk) {
         // local < chunk + kChunk <= 2 * chunk: rank r0, or r0 + 1 past the boundary.
         uint16_t* p0 = b.shards[r0] + soff;
-        uint16_t* p1 = (r0 + 1 < kMaxRanks ? b.shards[r0 + 1] : b.shards[r0]) + soff;
+        uint16_t* p1 = (r0 + 1 < Batch::kRanks ? b.shards[r0 + 1] : b.shards[r0]) + soff;
         V vals[kVecs];
         bool fast[kVecs];
 #pragma unroll
@@ -282,17 +294,17 @@ zero_status check_tensors(const zero_plan* plan, const uint16_t* const* tensors,
     return ZERO_OK;
 }
 
-// One launch per kTens tensors of a Shard(0) plan. bufs: the N_d rank
+// One launch per Batch::kTens tensors of a Shard(0) plan. bufs: the N_d rank
 // buffers; tensors: the T tensors. kScatter picks the direction.
-template <bool kScatter>
+template <bool kScatter, class Batch>
 zero_status launch_tensors(const zero_plan* plan, uint16_t* const* bufs, uint16_t* const* tensors,
                            hipStream_t stream, const char* who) {
-    TensorBatch batch{};
+    Batch batch{};
     for (int32_t r = 0; r < plan->n_ranks; ++r) batch.shards[r] = bufs[r];
     auto flush = [&]() -> zero_status {
         if (batch.n == 0) return ZERO_OK;
         const int64_t blocks = batch.first_block[batch.n];
-        hipLaunchKernelGGL(gather_tensor_kernel<kScatter>, dim3(static_cast<unsigned>(blocks)),
+        hipLaunchKernelGGL((gather_tensor_kernel<kScatter, Batch>), dim3(static_cast<unsigned>(blocks)),
                            dim3(kThreads), 0, stream, batch);
         batch.n = 0;
         batch.first_block[0] = 0;
@@ -310,10 +322,10 @@ zero_status launch_tensors(const zero_plan* plan, uint16_t* const* bufs, uint16_
         batch.dst[i] = tensors[t];
         batch.numel[i] = static_cast<int32_t>(n);
         batch.chunk[i] = static_cast<int32_t>(plan->chunk_elems[t]);
-        batch.off[i] = plan->offsets[t];
+        batch.off[i] = static_cast<typename Batch::OffT>(plan->offsets[t]);
         batch.first_block[i + 1] = batch.first_block[i] + static_cast<int32_t>(blocks);
         batch.n = i + 1;
-        if (batch.n == kTens) {
+        if (batch.n == Batch::kTens) {
             const zero_status st = flush();
             if (st != ZERO_OK) return st;
         }
@@ -326,6 +338,19 @@ bool fits_tensor_major(const zero_plan* plan) {
     for (const int64_t n : plan->numels)
         if (n >= (int64_t(1) << 31)) return false;
     return true;
+}
+
+// The compact table holds every chunk offset (< S) in 32 bits.
+bool fits_compact(const zero_plan* plan) {
+    return plan->n_ranks <= CompactBatch::kRanks && plan->shard < (int64_t(1) << 31);
+}
+
+template <bool kScatter>
+zero_status launch_tensors_any(const zero_plan* plan, uint16_t* const* bufs,
+                               uint16_t* const* tensors, hipStream_t stream, const char* who) {
+    return fits_compact(plan)
+               ? launch_tensors<kScatter, CompactBatch>(plan, bufs, tensors, stream, who)
+               : launch_tensors<kScatter, WideBatch>(plan, bufs, tensors, stream, who);
 }
 
 }  // namespace
@@ -349,8 +374,8 @@ extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t*
     bool all_present = true;
     for (int32_t r = 0; r < plan->n_ranks; ++r) all_present = all_present && shards[r] != nullptr;
     if (all_present && ZERO_GATHER_TENSOR_MAJOR && fits_tensor_major(plan))
-        return launch_tensors<false>(plan, const_cast<uint16_t* const*>(shards), tensors, stream,
-                                     "zero_gather_params launch");
+        return launch_tensors_any<false>(plan, const_cast<uint16_t* const*>(shards), tensors, stream,
+                                         "zero_gather_params launch");
     std::vector<Piece> pieces;
     pieces.reserve(plan->all.size());
     for (const zero_segment& seg : plan->all)
@@ -385,8 +410,8 @@ extern "C" zero_status zero_flatten_params(const zero_plan* plan, const uint16_t
         if (st != ZERO_OK) return st;
         std::vector<uint16_t*> bufs(static_cast<size_t>(plan->n_ranks));
         for (int32_t r = 0; r < plan->n_ranks; ++r) bufs[static_cast<size_t>(r)] = flat + int64_t(r) * plan->shard;
-        return launch_tensors<true>(plan, bufs.data(), const_cast<uint16_t* const*>(tensors), stream,
-                                    "zero_flatten_params launch");
+        return launch_tensors_any<true>(plan, bufs.data(), const_cast<uint16_t* const*>(tensors),
+                                        stream, "zero_flatten_params launch");
     }
     std::vector<Piece> pieces;
     pieces.reserve(2 * plan->all.size() + 1);
