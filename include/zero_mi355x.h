@@ -261,9 +261,10 @@ zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_
  * n_tensors entries. Every element gets zero_shard_adamw_step's arithmetic
  * (identical bits), with one step, one set of hyperparameters and one clip
  * coefficient for the whole list. Zero-sized tensors are skipped (their
- * pointers may be NULL). Any pointer alignment. One launch per 78 tensors.
+ * pointers may be NULL). Any pointer alignment. The tensors are batched
+ * largest first, 78 per launch (the order changes no result).
  * Errors: as zero_shard_adamw_step, per tensor (ZERO_EINVAL names it);
- * ZERO_ERANGE for a tensor of 2^39 elements or more; ZERO_EHIP. */
+ * ZERO_ERANGE for a tensor of 2^39 elements or more; ZERO_ENOMEM; ZERO_EHIP. */
 zero_status zero_multi_tensor_adamw_step(float* const* masters, float* const* exp_avgs,
                                          float* const* exp_avg_sqs, const uint16_t* const* grads,
                                          uint16_t* const* params_out, const int64_t* numels,
