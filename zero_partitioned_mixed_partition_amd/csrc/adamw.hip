@@ -12,9 +12,9 @@
 //
 // Memory: 28 bytes per element (read 12 fp32 + 2 bf16, write 12 fp32 + 2
 // bf16), about 15 flops: HBM-bound by a factor of ~40 against the fp32
-// vector ridge point, so no matrix cores. Each lane updates one element with
-// non-temporal accesses (dword per fp32 array, short for the bf16 gradient
-// and parameter). The grid covers the shard with one element per lane (shards
+// vector ridge point, so no matrix cores. Each lane updates one element
+// (dword per fp32 array, short for the bf16 gradient and parameter) with
+// non-temporal loads and write-through stores. The grid covers the shard with one element per lane (shards
 // past the 2^32 work-items of one dispatch take several launches): measured on MI355X,
 // short-lived waves with narrow accesses sustain more bandwidth on this
 // 4-read/4-write pattern than wide vectors or a persistent loop. The same

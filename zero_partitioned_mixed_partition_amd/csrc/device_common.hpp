@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace zero {
 namespace dev {
@@ -40,13 +41,28 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float x) { return pack_bf16(x, x) & 0xFFFFu; }
 
-// Streaming (non-temporal) 16-byte accesses: every byte is touched once per
-// step, so nothing is worth keeping in the caches.
+// Streaming accesses: every byte is touched once per step, so nothing is worth
+// keeping in the caches. Loads are non-temporal.
+//
+// Stores write through to memory: a buffer store carrying the device-scope
+// (sc1) and non-temporal (nt) cache bits, where a plain non-temporal store
+// leaves dirty lines in the XCD's L2 to be written back later. Measured on
+// MI355X: AdamW 66.6 us against 69.3 us at 15.6 M elements, 528 us against
+// 540 us at 125 M; a 16-byte-per-lane copy of 2.6 GB 786-789 us against
+// 809-812 us. Cache bits on the loads measured no difference.
+//
+// The buffer's base is the first active lane's address less 2 GiB, and each
+// lane passes its distance from that base as the 32-bit offset, so every lane
+// of a wave must store within 2 GiB of that lane's address. Every kernel here
+// stores one contiguous run per wave. The record count is the full 32-bit
+// range, so the buffer's own range check never drops a store (bounds are the
+// callers', as with a global store).
 #ifndef ZERO_NT_LOADS
 #define ZERO_NT_LOADS 1
 #endif
-#ifndef ZERO_NT_STORES
-#define ZERO_NT_STORES 1
+// 1: write-through buffer stores (sc1 nt); 0: global non-temporal stores.
+#ifndef ZERO_THROUGH_STORES
+#define ZERO_THROUGH_STORES 1
 #endif
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p) {
@@ -56,12 +72,56 @@ __device__ __forceinline__ T ld_stream(const T* p) {
     return *p;
 #endif
 }
+
+constexpr int kRawBufferWord3 = 0x00020000;   // untyped buffer, 32-bit data format
+constexpr int kThroughCpol = 0x12;            // sc1 (device scope) | nt
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t through_base(const void* p, uint32_t& off) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    const uint64_t first = (static_cast<uint64_t>(hi) << 32) | lo;
+    const uint64_t base = first >= (uint64_t(1) << 31) ? first - (uint64_t(1) << 31) : 0;
+    off = static_cast<uint32_t>(a - base);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, -1, kRawBufferWord3);
+}
+
+__device__ __forceinline__ void st_through(uint16_t* p, uint16_t v) {
+    uint32_t off;
+    const __amdgpu_buffer_rsrc_t r = through_base(p, off);
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kThroughCpol);
+}
+__device__ __forceinline__ void st_through(uint32_t* p, uint32_t v) {
+    uint32_t off;
+    const __amdgpu_buffer_rsrc_t r = through_base(p, off);
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kThroughCpol);
+}
+__device__ __forceinline__ void st_through(float* p, float v) {
+    st_through(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v));
+}
+__device__ __forceinline__ void st_through(u32x2* p, u32x2 v) {
+    uint32_t off;
+    const __amdgpu_buffer_rsrc_t r = through_base(p, off);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kThroughCpol);
+}
+__device__ __forceinline__ void st_through(u32x4* p, u32x4 v) {
+    uint32_t off;
+    const __amdgpu_buffer_rsrc_t r = through_base(p, off);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kThroughCpol);
+}
+template <typename T>
+__device__ __forceinline__ void st_through(T* p, const T& v) {
+    static_assert(sizeof(T) == 8 || sizeof(T) == 16, "8- or 16-byte vector");
+    typedef typename std::conditional<sizeof(T) == 8, u32x2, u32x4>::type W;
+    st_through(reinterpret_cast<W*>(p), __builtin_bit_cast(W, v));
+}
+
 template <typename T>
 __device__ __forceinline__ void st_stream(T* p, const T& v) {
-#if ZERO_NT_STORES
-    __builtin_nontemporal_store(v, p);
+#if ZERO_THROUGH_STORES
+    st_through(p, v);
 #else
-    *p = v;
+    __builtin_nontemporal_store(v, p);
 #endif
 }
 
