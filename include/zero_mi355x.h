@@ -17,6 +17,8 @@
  *   zero_shard_adamw_step   fp32 master/m/v update and bf16 parameter emit
  *   zero_multi_tensor_adamw_step  the same over a ragged list of tensors
  *                           (FSDP-2's per-parameter shards)
+ *   zero_mt_table_*         the same list described once in device memory,
+ *                           stepped in one launch
  *   zero_gather_params      bf16 shards back to per-tensor parameters
  *                           (all-gather output layout, then un-flatten)
  *   zero_flatten_params     per-tensor bf16 buffers into the padded flat buffer
@@ -271,6 +273,41 @@ zero_status zero_multi_tensor_adamw_step(float* const* masters, float* const* ex
                                          int32_t n_tensors, int64_t step, double lr, double beta1,
                                          double beta2, double eps, double weight_decay,
                                          const float* clip_scale, hipStream_t stream);
+
+/* The multi-tensor form for a fixed list, with its table in device memory.
+ * [ZF] "FSDP-2: Per-Parameter Sharding via DTensor (fully_shard)": the same
+ * per-parameter list is stepped every iteration, so its description can be
+ * built once. zero_mt_table_create checks the list exactly as
+ * zero_multi_tensor_adamw_step does and copies, to device memory that the
+ * table owns, one 64-byte descriptor per non-empty tensor (its five device
+ * pointers and its size) and one 4-byte tensor index per workgroup of 512
+ * elements (about 0.8 bytes per 100 elements). zero_mt_table_adamw_step then
+ * updates every tensor of the list in one launch (a list of 2^24 workgroups or
+ * more, above 8.6e9 elements, in several), with zero_shard_adamw_step's
+ * arithmetic: identical bits to both other AdamW entry points.
+ * Create: the arguments as zero_multi_tensor_adamw_step's list; out receives
+ * the table. It calls hipMalloc and a synchronous hipMemcpy on the current
+ * device, once. The table keeps the device pointers (not the data): the
+ * caller keeps those buffers alive and in place for the table's lifetime.
+ * Errors: as zero_multi_tensor_adamw_step's list checks; ZERO_EINVAL for a
+ * NULL out; ZERO_ERANGE for 2^31 workgroups or more; ZERO_ENOMEM; ZERO_EHIP
+ * (allocation or copy failed).
+ * Step: step, hyperparameters and clip_scale as zero_shard_adamw_step. It must
+ * run with the table's device current (ZERO_EINVAL otherwise). An empty list
+ * enqueues nothing.
+ * Free: releases the device memory (hipFree, which waits for the device);
+ * no step using the table may still be running. Accepts NULL.
+ * Blocks: the workgroups of one step, or -1 for NULL. */
+typedef struct zero_mt_table zero_mt_table;
+zero_status zero_mt_table_create(float* const* masters, float* const* exp_avgs,
+                                 float* const* exp_avg_sqs, const uint16_t* const* grads,
+                                 uint16_t* const* params_out, const int64_t* numels,
+                                 int32_t n_tensors, zero_mt_table** out);
+void zero_mt_table_free(zero_mt_table* table);
+int64_t zero_mt_table_blocks(const zero_mt_table* table);
+zero_status zero_mt_table_adamw_step(const zero_mt_table* table, int64_t step, double lr,
+                                     double beta1, double beta2, double eps, double weight_decay,
+                                     const float* clip_scale, hipStream_t stream);
 
 /* ------------------------------------------------------------------ gather
  *

@@ -183,6 +183,31 @@ def test_multi_tensor_adamw_rejects_bad_arguments_before_touching_the_gpu(zm):
     assert f(one, one, one, one, one, n, 1, 1, *args) == lib.ZERO_OK                  # empty tensor
 
 
+def test_multi_tensor_table_rejects_bad_arguments_before_touching_the_gpu(zm):
+    """Table creation checks the list as the list call does; an empty list needs
+    no device, and its step enqueues nothing."""
+    lib = zm._binding
+    out = ctypes.c_void_p()
+    assert lib._mt_create(None, None, None, None, None, None, 1, None) == lib.ZERO_EINVAL  # NULL out
+    assert lib._mt_create(None, None, None, None, None, None, -1, ctypes.byref(out)) == lib.ZERO_EINVAL
+    assert lib._mt_create(None, None, None, None, None, None, 2, ctypes.byref(out)) == lib.ZERO_EINVAL
+    one = (ctypes.c_void_p * 1)(None)
+    n = (ctypes.c_int64 * 1)(5)
+    assert lib._mt_create(one, one, one, one, one, n, 1, ctypes.byref(out)) == lib.ZERO_EINVAL
+    assert "tensor 0" in zm.zero_last_error()
+    assert not out.value
+    n[0] = 0
+    assert lib._mt_create(one, one, one, one, one, n, 1, ctypes.byref(out)) == lib.ZERO_OK
+    assert out.value and lib._mt_blocks(out) == 0
+    hp = (1e-3, 0.9, 0.999, 1e-8, 0.0, None, None)
+    assert lib._mt_step(out, 1, *hp) == lib.ZERO_OK
+    assert lib._mt_step(out, 0, *hp) == lib.ZERO_EINVAL                               # step < 1
+    assert lib._mt_step(None, 1, *hp) == lib.ZERO_EINVAL                              # NULL table
+    lib._mt_free(out)
+    lib._mt_free(None)
+    assert lib._mt_blocks(None) == -1
+
+
 def test_builder_loads_without_importing_the_package():
     """build() must work when the in-tree library is stale or missing, so its
     build script is loaded without importing the package (which loads the

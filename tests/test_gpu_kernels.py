@@ -439,8 +439,19 @@ def test_gather_rank_counts_many_tensors_misaligned(zm, kind, n_ranks, t):
 
 # ----------------------------------------------------------------------------- multi-tensor AdamW
 
+def _mt_stepper(zm, form, dp, dm, dv, dg, do):
+    """The multi-tensor update of a fixed list, through the list call or the
+    device-resident table."""
+    if form == "table":
+        tab = zm.MultiTensorTable(dp, dm, dv, dg, do)
+        return lambda t, scale=None: tab.step(t, clip_scale=scale, **HP)
+    return lambda t, scale=None: zm.zero_multi_tensor_adamw_step(dp, dm, dv, dg, do, t,
+                                                                  clip_scale=scale, **HP)
+
+
+@pytest.mark.parametrize("form", ["list", "table"])
 @pytest.mark.parametrize("seed", range(3))
-def test_multi_tensor_adamw_matches_oracle(zm, seed):
+def test_multi_tensor_adamw_matches_oracle(zm, seed, form):
     """A ragged list (sizes around the 256-lane workgroup, empty tensors, more
     tensors than one launch carries, misaligned starts) against the oracle per
     tensor, three steps, device clip coefficient; then the NaN skip."""
@@ -462,12 +473,13 @@ def test_multi_tensor_adamw_matches_oracle(zm, seed):
     do = [dev_u16(np.full(n, 0x4444, np.uint16)) for n in sizes]
     scale = torch.tensor([0.8125], dtype=torch.float32, device=dev())
     bits = [None] * len(sizes)
+    step = _mt_stepper(zm, form, dp, dm, dv, dg, do)
     for t in (1, 2, 3):
         G = [synth.normal_bf16(n, 70 + seed, synth.KIND_GRAD, t, i, 0, None, 1e-3)
              for i, n in enumerate(sizes)]
         for d, g in zip(dg, G):
             d.copy_(torch.from_numpy(g.view(np.int16)))
-        zm.zero_multi_tensor_adamw_step(dp, dm, dv, dg, do, t, clip_scale=scale, **HP)
+        step(t, scale)
         for i in range(len(sizes)):
             P[i], M[i], V[i], bits[i] = oracle.adamw_step(P[i], M[i], V[i], G[i], t,
                                                          clip=np.float32(0.8125), **HP)
@@ -478,13 +490,13 @@ def test_multi_tensor_adamw_matches_oracle(zm, seed):
         assert_bits_equal(host_f32(dv[i]).view(np.uint32), V[i].view(np.uint32), f"exp_avg_sq {i}")
         assert_bits_equal(host_u16(do[i]), bits[i], f"param {i}")
     before = [x.clone() for x in dp]
-    zm.zero_multi_tensor_adamw_step(dp, dm, dv, dg, do, 4,
-                                    clip_scale=torch.tensor([float("nan")], device=dev()), **HP)
+    step(4, torch.tensor([float("nan")], device=dev()))
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(before, dp))
 
 
-def test_multi_tensor_adamw_equals_the_flat_kernel_on_views(zm):
+@pytest.mark.parametrize("form", ["list", "table"])
+def test_multi_tensor_adamw_equals_the_flat_kernel_on_views(zm, form):
     """Tensors that are views into one flat buffer give the flat kernel's bits."""
     sizes = [768, 768, 2304 * 768, 2304, 3, 50_000]
     n = sum(sizes)
@@ -498,13 +510,47 @@ def test_multi_tensor_adamw_equals_the_flat_kernel_on_views(zm):
 
     def views(x):
         return [x[a:b] for a, b in zip(offs[:-1], offs[1:])]
+    step = _mt_stepper(zm, form, views(multi[0]), views(multi[1]), views(multi[2]), views(g),
+                       views(multi[3]))
     for t in (1, 2):
         zm.zero_shard_adamw_step(flat[0], flat[1], flat[2], g, flat[3], t, **HP)
-        zm.zero_multi_tensor_adamw_step(views(multi[0]), views(multi[1]), views(multi[2]), views(g),
-                                        views(multi[3]), t, **HP)
+        step(t)
     torch.cuda.synchronize()
     for a, b, name in zip(flat, multi, ("master", "exp_avg", "exp_avg_sq", "param")):
         assert torch.equal(a, b), name
+
+
+def test_multi_tensor_table_blocks_prepared_call_and_empty_list(zm):
+    """The table's workgroup count (512 elements each, empty tensors none), its
+    prepared call against the list call over two steps, and an all-empty list."""
+    sizes = [0, 1, 511, 512, 513, 0, 100_000]
+    n = sum(sizes)
+    p0 = synth.normal_f32(n, 81, synth.KIND_MASTER, 0, 0, 0, None, 0.02)
+    g = to_dev_u16(synth.normal_bf16(n, 81, synth.KIND_GRAD, 1, 0, 0, None, 1e-3))
+    offs = np.cumsum([0] + sizes)
+
+    def views(x):
+        return [x[a:b] for a, b in zip(offs[:-1], offs[1:])]
+    bufs = [[to_dev_f32(p0), torch.zeros(n, device=dev()), torch.zeros(n, device=dev()),
+             torch.zeros(n, dtype=torch.int16, device=dev())] for _ in range(2)]
+    tab = zm.MultiTensorTable(views(bufs[0][0]), views(bufs[0][1]), views(bufs[0][2]), views(g),
+                              views(bufs[0][3]))
+    assert tab.blocks == sum((k + 511) // 512 for k in sizes)
+    scale = torch.tensor([0.5], dtype=torch.float32, device=dev())
+    call = tab.prepare_step(clip_scale=scale, stream=None, **HP)
+    for t in (1, 2):
+        call(t)
+        zm.zero_multi_tensor_adamw_step(views(bufs[1][0]), views(bufs[1][1]), views(bufs[1][2]),
+                                        views(g), views(bufs[1][3]), t, clip_scale=scale, **HP)
+    torch.cuda.synchronize()
+    for a, b, name in zip(bufs[0], bufs[1], ("master", "exp_avg", "exp_avg_sq", "param")):
+        assert torch.equal(a, b), name
+    e = torch.zeros(0, device=dev())
+    eh = torch.zeros(0, dtype=torch.int16, device=dev())
+    empty = zm.MultiTensorTable([e, e], [e, e], [e, e], [eh, eh], [eh, eh])
+    assert empty.blocks == 0
+    empty.step(1, **HP)
+    del tab, empty
 
 
 @pytest.mark.parametrize("R", [3, 8])

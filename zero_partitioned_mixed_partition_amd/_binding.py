@@ -76,6 +76,12 @@ _offload = _fn("zero_offload_adamw_step", c_i32,
 _mt_adamw = _fn("zero_multi_tensor_adamw_step", c_i32,
                 [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl,
                  c_vp, c_vp])
+_mt_create = _fn("zero_mt_table_create", c_i32,
+                 [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, ctypes.POINTER(c_vp)])
+_mt_free = _fn("zero_mt_table_free", None, [c_vp])
+_mt_blocks = _fn("zero_mt_table_blocks", c_i64, [c_vp])
+_mt_step = _fn("zero_mt_table_adamw_step", c_i32,
+               [c_vp, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl, c_vp, c_vp])
 _status_string = _fn("zero_status_string", ctypes.c_char_p, [c_i32])
 _last_error = _fn("zero_last_error", ctypes.c_char_p, [])
 
@@ -360,6 +366,70 @@ def zero_multi_tensor_adamw_step(masters, exp_avgs, exp_avg_sqs, grads, params_o
                                  weight_decay: float, clip_scale=None, stream=None) -> None:
     prepare_multi_tensor_adamw_step(masters, exp_avgs, exp_avg_sqs, grads, params_out, lr, beta1,
                                     beta2, eps, weight_decay, clip_scale, stream)(step)
+
+
+class MultiTensorTable:
+    """Owner of a zero_mt_table: a fixed list of per-parameter tensors described
+    once in device memory (on the current device), stepped in one launch. The
+    tensors are held here, so their buffers outlive the table."""
+
+    def __init__(self, masters, exp_avgs, exp_avg_sqs, grads, params_out):
+        lists = (masters, exp_avgs, exp_avg_sqs, grads, params_out)
+        T = len(masters)
+        if any(len(x) != T for x in lists):
+            raise ValueError("the five lists must have the same length")
+        numels = [t.numel() for t in masters]
+        for lst in lists[1:]:
+            if any(x.numel() < n for x, n in zip(lst, numels)):
+                raise ValueError("a tensor holds fewer elements than its master")
+        tabs = []
+        for lst, size, what in zip(lists, (4, 4, 4, 2, 2),
+                                   ("master", "exp_avg", "exp_avg_sq", "grad", "param")):
+            tabs.append((c_vp * max(T, 1))(*[_ptr(x, size, what) for x in lst]))
+        ns = (c_i64 * max(T, 1))(*numels)
+        h = c_vp()
+        _check(_mt_create(*tabs, ns, T, ctypes.byref(h)), "zero_mt_table_create")
+        self._h = h
+        self._free = _mt_free          # held by the instance for interpreter exit
+        self._keep = lists
+        self.device = masters[0].device if T else None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        free = getattr(self, "_free", None)
+        if h is not None and h.value and free is not None:
+            free(h)
+            h.value = None
+
+    @property
+    def handle(self) -> c_vp:
+        return self._h
+
+    @property
+    def blocks(self) -> int:
+        return int(_mt_blocks(self._h))
+
+    def prepare_step(self, lr: float, beta1: float, beta2: float, eps: float,
+                     weight_decay: float, clip_scale, stream) -> "Prepared":
+        """zero_mt_table_adamw_step with its arguments marshalled once; call the
+        result with the step."""
+        _need(clip_scale, 1, "clip_scale")
+        st = stream if stream is not None else (
+            _stream(None, self._keep[0][0]) if self._keep[0] else 0)
+        p = Prepared(_mt_step, [self._h, 1, lr, beta1, beta2, eps, weight_decay,
+                                _ptr(clip_scale, 4, "clip_scale"), st],
+                     "zero_mt_table_adamw_step", step_index=1)
+        p._keep = (self, clip_scale)
+        return p
+
+    def step(self, step: int, lr: float, beta1: float, beta2: float, eps: float,
+             weight_decay: float, clip_scale=None, stream=None) -> None:
+        if clip_scale is not None:
+            _need(clip_scale, 1, "clip_scale")
+        st = stream if stream is not None else (
+            _stream(None, self._keep[0][0]) if self._keep[0] else 0)
+        _check(_mt_step(self._h, step, lr, beta1, beta2, eps, weight_decay,
+                        _ptr(clip_scale, 4, "clip_scale"), st), "zero_mt_table_adamw_step")
 
 
 def _host_ptr(a, itemsize: int, what: str) -> int:

@@ -195,22 +195,12 @@ struct MtBatch {
 };
 static_assert(sizeof(MtBatch) <= 4096, "kernel arguments are limited to 4 KB");
 
-__global__ __launch_bounds__(kThreads) void adamw_multi_kernel(MtBatch b, AdamScalars c,
-                                                               const float* __restrict__ clip_scale) {
-    const int32_t blk = static_cast<int32_t>(blockIdx.x);
-    int lo = 0, hi = b.count - 1;              // t with first_block[t] <= blk < first_block[t + 1]
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
-    }
-    const int t = lo;
-    float* __restrict__ P = b.p[t];
-    float* __restrict__ M = b.m[t];
-    float* __restrict__ V = b.v[t];
-    const uint16_t* __restrict__ G = b.g[t];
-    uint16_t* __restrict__ O = b.o[t];
-    const int64_t n = b.n[t];
-    const int64_t base = static_cast<int64_t>(blk - b.first_block[t]) * kMtChunk + threadIdx.x;
+// One workgroup's share of tensor (P, M, V, G, O) of n elements: lane element
+// base + k * kThreads for k < kMtPer, the flat kernel's per-element code.
+__device__ __forceinline__ void mt_update(float* __restrict__ P, float* __restrict__ M,
+                                          float* __restrict__ V, const uint16_t* __restrict__ G,
+                                          uint16_t* __restrict__ O, int64_t n, int64_t base,
+                                          const AdamScalars& c, const float* __restrict__ clip_scale) {
     float p[kMtPer], m[kMtPer], v[kMtPer], g[kMtPer];
 #pragma unroll
     for (int k = 0; k < kMtPer; ++k) {          // every load first
@@ -240,6 +230,46 @@ __global__ __launch_bounds__(kThreads) void adamw_multi_kernel(MtBatch b, AdamSc
     }
 }
 
+__global__ __launch_bounds__(kThreads) void adamw_multi_kernel(MtBatch b, AdamScalars c,
+                                                               const float* __restrict__ clip_scale) {
+    const int32_t blk = static_cast<int32_t>(blockIdx.x);
+    int lo = 0, hi = b.count - 1;              // t with first_block[t] <= blk < first_block[t + 1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
+    }
+    const int t = lo;
+    mt_update(b.p[t], b.m[t], b.v[t], b.g[t], b.o[t], b.n[t],
+              static_cast<int64_t>(blk - b.first_block[t]) * kMtChunk + threadIdx.x, c, clip_scale);
+}
+
+// Device-resident form of the list, for a fixed list updated every step: one
+// 64-byte descriptor per non-empty tensor and, per workgroup, the index of its
+// descriptor. A workgroup then finds its tensor with two dependent scalar
+// loads instead of a binary search, and the whole list goes out in one launch
+// (the kernel arguments hold no table).
+struct alignas(64) MtDesc {
+    float* p;
+    float* m;
+    float* v;
+    const uint16_t* g;
+    uint16_t* o;
+    int64_t n;
+    int64_t first_block;
+    int64_t unused;
+};
+static_assert(sizeof(MtDesc) == 64, "one 64-byte descriptor per tensor");
+
+__global__ __launch_bounds__(kThreads) void adamw_table_kernel(const MtDesc* __restrict__ table,
+                                                               const uint32_t* __restrict__ index,
+                                                               int64_t blk0, AdamScalars c,
+                                                               const float* __restrict__ clip_scale) {
+    const int64_t blk = blk0 + static_cast<int64_t>(blockIdx.x);
+    const MtDesc d = table[index[blk]];
+    mt_update(d.p, d.m, d.v, d.g, d.o, d.n, (blk - d.first_block) * kMtChunk + threadIdx.x, c,
+              clip_scale);
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool ranges_overlap(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
@@ -263,6 +293,31 @@ zero_status check_hyper(int64_t step, double lr, double beta1, double beta2, dou
         return fail(ZERO_EINVAL, w + ": eps must be finite and > 0");
     if (!(lr >= 0.0) || !std::isfinite(lr) || !std::isfinite(weight_decay))
         return fail(ZERO_EINVAL, w + ": lr and weight_decay must be finite, lr >= 0");
+    return ZERO_OK;
+}
+
+// The checks every multi-tensor call makes on its list (n_tensors > 0).
+zero_status check_mt_list(float* const* masters, float* const* exp_avgs, float* const* exp_avg_sqs,
+                          const uint16_t* const* grads, uint16_t* const* params_out,
+                          const int64_t* numels, int32_t n_tensors, const char* who) {
+    using zero::fail;
+    const std::string w(who);
+    if (!masters || !exp_avgs || !exp_avg_sqs || !grads || !params_out || !numels)
+        return fail(ZERO_EINVAL, w + ": NULL array of pointers");
+    for (int32_t t = 0; t < n_tensors; ++t) {
+        const int64_t n = numels[t];
+        if (n < 0) return fail(ZERO_EINVAL, w + ": numel < 0 for tensor " + std::to_string(t));
+        if (n == 0) continue;
+        if (!masters[t] || !exp_avgs[t] || !exp_avg_sqs[t] || !grads[t] || !params_out[t])
+            return fail(ZERO_EINVAL, w + ": NULL array for tensor " + std::to_string(t));
+        const size_t fb = static_cast<size_t>(n) * 4, hb = static_cast<size_t>(n) * 2;
+        if (ranges_overlap(params_out[t], hb, masters[t], fb) ||
+            ranges_overlap(params_out[t], hb, exp_avgs[t], fb) ||
+            ranges_overlap(params_out[t], hb, exp_avg_sqs[t], fb))
+            return fail(ZERO_EINVAL, w + ": param overlaps the fp32 state of tensor " + std::to_string(t));
+        if ((n + kMtChunk - 1) / kMtChunk > 0x7FFFFFFF)
+            return fail(ZERO_ERANGE, w + ": tensor " + std::to_string(t) + " too large");
+    }
     return ZERO_OK;
 }
 
@@ -350,23 +405,8 @@ extern "C" zero_status zero_multi_tensor_adamw_step(float* const* masters, float
     zero_status st = check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
     if (st != ZERO_OK) return st;
     if (n_tensors == 0) return ZERO_OK;
-    if (!masters || !exp_avgs || !exp_avg_sqs || !grads || !params_out || !numels)
-        return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: NULL array of pointers");
-    for (int32_t t = 0; t < n_tensors; ++t) {
-        const int64_t n = numels[t];
-        if (n < 0) return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: numel < 0 for tensor " + std::to_string(t));
-        if (n == 0) continue;
-        if (!masters[t] || !exp_avgs[t] || !exp_avg_sqs[t] || !grads[t] || !params_out[t])
-            return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: NULL array for tensor " + std::to_string(t));
-        const size_t fb = static_cast<size_t>(n) * 4, hb = static_cast<size_t>(n) * 2;
-        if (ranges_overlap(params_out[t], hb, masters[t], fb) ||
-            ranges_overlap(params_out[t], hb, exp_avgs[t], fb) ||
-            ranges_overlap(params_out[t], hb, exp_avg_sqs[t], fb))
-            return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: param overlaps the fp32 state of tensor " +
-                                         std::to_string(t));
-        if ((n + kMtChunk - 1) / kMtChunk > 0x7FFFFFFF)
-            return fail(ZERO_ERANGE, "zero_multi_tensor_adamw_step: tensor " + std::to_string(t) + " too large");
-    }
+    st = check_mt_list(masters, exp_avgs, exp_avg_sqs, grads, params_out, numels, n_tensors, who);
+    if (st != ZERO_OK) return st;
     AdamScalars c;
     st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
     if (st != ZERO_OK) return st;
@@ -415,4 +455,126 @@ extern "C" zero_status zero_multi_tensor_adamw_step(float* const* masters, float
         }
     }
     return flush();
+}
+
+// ------------------------------------------------------------ device table
+
+struct zero_mt_table {
+    int device = -1;
+    void* mem = nullptr;          // descriptors, then the per-workgroup index
+    const MtDesc* table = nullptr;
+    const uint32_t* index = nullptr;
+    int64_t blocks = 0;           // workgroups of one step
+};
+
+extern "C" zero_status zero_mt_table_create(float* const* masters, float* const* exp_avgs,
+                                            float* const* exp_avg_sqs, const uint16_t* const* grads,
+                                            uint16_t* const* params_out, const int64_t* numels,
+                                            int32_t n_tensors, zero_mt_table** out) {
+    using zero::fail;
+    static const char* const who = "zero_mt_table_create";
+    zero::clear_error();
+    if (!out) return fail(ZERO_EINVAL, "zero_mt_table_create: NULL out");
+    *out = nullptr;
+    if (n_tensors < 0) return fail(ZERO_EINVAL, "zero_mt_table_create: n_tensors < 0");
+    zero_status st = ZERO_OK;
+    if (n_tensors > 0) {
+        st = check_mt_list(masters, exp_avgs, exp_avg_sqs, grads, params_out, numels, n_tensors, who);
+        if (st != ZERO_OK) return st;
+    }
+    std::vector<MtDesc> descs;
+    std::vector<uint32_t> index;
+    zero_mt_table* tab = nullptr;
+    try {
+        int64_t blocks = 0;
+        for (int32_t t = 0; t < n_tensors; ++t) {
+            const int64_t n = numels[t];
+            if (n == 0) continue;
+            const int64_t b = (n + kMtChunk - 1) / kMtChunk;
+            if (blocks + b > 0x7FFFFFFF)
+                return fail(ZERO_ERANGE, "zero_mt_table_create: more than 2^31 workgroups in one list");
+            MtDesc d{};
+            d.p = masters[t];
+            d.m = exp_avgs[t];
+            d.v = exp_avg_sqs[t];
+            d.g = grads[t];
+            d.o = params_out[t];
+            d.n = n;
+            d.first_block = blocks;
+            index.insert(index.end(), static_cast<size_t>(b), static_cast<uint32_t>(descs.size()));
+            descs.push_back(d);
+            blocks += b;
+        }
+        tab = new zero_mt_table;
+        tab->blocks = blocks;
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "zero_mt_table_create: host allocation failed");
+    }
+    if (tab->blocks > 0)          // an empty list needs no device
+        st = zero::check_hip(hipGetDevice(&tab->device), "zero_mt_table_create: hipGetDevice");
+    if (st == ZERO_OK && tab->blocks > 0) {
+        const size_t table_bytes = (descs.size() * sizeof(MtDesc) + 255) / 256 * 256;
+        const size_t bytes = table_bytes + index.size() * sizeof(uint32_t);
+        st = zero::check_hip(hipMalloc(&tab->mem, bytes), "zero_mt_table_create: hipMalloc");
+        if (st == ZERO_OK) {
+            tab->table = static_cast<const MtDesc*>(tab->mem);
+            tab->index = reinterpret_cast<const uint32_t*>(static_cast<char*>(tab->mem) + table_bytes);
+            st = zero::check_hip(hipMemcpy(tab->mem, descs.data(), descs.size() * sizeof(MtDesc),
+                                           hipMemcpyHostToDevice), "zero_mt_table_create: hipMemcpy");
+        }
+        if (st == ZERO_OK)
+            st = zero::check_hip(hipMemcpy(const_cast<uint32_t*>(tab->index), index.data(),
+                                           index.size() * sizeof(uint32_t), hipMemcpyHostToDevice),
+                                 "zero_mt_table_create: hipMemcpy");
+    }
+    if (st != ZERO_OK) {
+        if (tab->mem) (void)hipFree(tab->mem);
+        delete tab;
+        return st;
+    }
+    *out = tab;
+    return ZERO_OK;
+}
+
+extern "C" void zero_mt_table_free(zero_mt_table* table) {
+    if (!table) return;
+    if (table->mem) (void)hipFree(table->mem);
+    delete table;
+}
+
+extern "C" int64_t zero_mt_table_blocks(const zero_mt_table* table) {
+    return table ? table->blocks : -1;
+}
+
+extern "C" zero_status zero_mt_table_adamw_step(const zero_mt_table* table, int64_t step, double lr,
+                                                double beta1, double beta2, double eps,
+                                                double weight_decay, const float* clip_scale,
+                                                hipStream_t stream) {
+    using zero::fail;
+    static const char* const who = "zero_mt_table_adamw_step";
+    zero::clear_error();
+    if (!table) return fail(ZERO_EINVAL, "zero_mt_table_adamw_step: NULL table");
+    zero_status st = check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
+    if (st != ZERO_OK) return st;
+    if (table->blocks == 0) return ZERO_OK;
+    int dev = -1;
+    st = zero::check_hip(hipGetDevice(&dev), "zero_mt_table_adamw_step: hipGetDevice");
+    if (st != ZERO_OK) return st;
+    if (dev != table->device)
+        return fail(ZERO_EINVAL, "zero_mt_table_adamw_step: the table lives on device " +
+                                     std::to_string(table->device) + ", the current device is " +
+                                     std::to_string(dev));
+    AdamScalars c;
+    st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
+    if (st != ZERO_OK) return st;
+    // A dispatch holds fewer than 2^32 work-items: longer lists take several launches.
+    constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
+    for (int64_t b0 = 0; b0 < table->blocks; b0 += kMaxBlocks) {
+        const int64_t nb = table->blocks - b0 < kMaxBlocks ? table->blocks - b0 : kMaxBlocks;
+        hipLaunchKernelGGL(adamw_table_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0,
+                           stream, table->table, table->index, b0, c, clip_scale);
+        st = zero::check_hip(hipGetLastError(), "zero_mt_table_adamw_step launch");
+        if (st != ZERO_OK) return st;
+    }
+    return ZERO_OK;
 }
