@@ -9,7 +9,9 @@ path:
            HBM), averaged, with its squared-norm partial fused in
   clip     global-norm coefficient (max norm 1.0) from the partials on device
   adamw    fp32 master/m/v update of the shard, bf16 parameters emitted
-  gather   8 bf16 parameter shards -> 148 per-tensor parameters
+  gather   8 bf16 parameter shards -> 148 per-tensor parameters, through a
+           device-resident copy table (the call-based gather is timed beside
+           it, outside the step)
 
 Other workloads (`--workload`), each timed as its own configuration states:
   llama3-8b   rank 63 of 64: six 25M-element buckets of 64 replicas reduced
@@ -157,9 +159,11 @@ class RankWorkload:
                 del per_tensor
             self.windows = [(0, P, full)]
             self.flatten_out = torch.empty(P, dtype=torch.int16, device=device)
-            self.extra_phases = [("flatten", zm._binding.prepare_flatten_params(
-                self.plan, self.flatten_in, self.flatten_out,
-                torch.cuda.current_stream(device).cuda_stream))]
+            self._ft = zm.CopyTable.flatten(self.plan, self.flatten_in, self.flatten_out)
+            st0 = torch.cuda.current_stream(device).cuda_stream
+            self.extra_phases = [("flatten", self._ft.prepare_run(st0)),
+                                 ("flatten_call", zm._binding.prepare_flatten_params(
+                                     self.plan, self.flatten_in, self.flatten_out, st0))]
         elif reps and not bucket:
             full = staggered_replicas(reps, P, device)
             for k, t in enumerate(full):
@@ -201,8 +205,16 @@ class RankWorkload:
                 torch.cuda.current_stream(device).cuda_stream], "zero_grad_sqnorm")
             first = ("sqnorm", sq)
         self.phases = [first, ("clip", rs.clip), ("adamw", rs.adamw)]
+        st0 = torch.cuda.current_stream(device).cuda_stream
+        extra = list(getattr(self, "extra_phases", None) or [])
+        # Outside the step, the call-based gather (and flatten) beside the copy
+        # tables that the step uses.
         if gather:
             self.phases.append(("gather", rs.gather))
+            extra.append(("gather_call", zm._binding.prepare_gather_params(
+                self.plan, rs.param_shards, rs.tensors, st0)))
+        if extra:
+            self.extra_phases = extra
         self.adamw_launches = 1
         self.elems_per_step = S
         self.per_tensor = name.endswith("-pertensor")
@@ -315,7 +327,9 @@ class RankWorkload:
         if any(p[0] == "gather" for p in self.phases):
             b["gather"] = 4 * self.phi
         if any(p[0] == "flatten" for p in getattr(self, "extra_phases", None) or []):
-            b["flatten"] = 4 * self.phi + 2 * (self.P - self.phi)
+            b["flatten"] = b["flatten_call"] = 4 * self.phi + 2 * (self.P - self.phi)
+        if "gather" in b:
+            b["gather_call"] = b["gather"]
         if getattr(self, "per_tensor", False):
             b["adamw_list"] = 28 * self.elems_per_step
         return b
@@ -380,8 +394,8 @@ class AllRanksWorkload:
                                                    self.param[sl[r]], clip_scale=None, stream=st,
                                                    **self.hyper.as_kwargs())
                        for r in range(w.n_ranks)]
-        self._gather = zb.prepare_gather_params(self.plan, [self.param[s] for s in sl],
-                                                self.tensors, st)
+        self._gt = zb.CopyTable.gather(self.plan, [self.param[s] for s in sl], self.tensors)
+        self._gather = self._gt.prepare_run(st)
         # outside the step: one replica flattening its per-tensor gradients into a
         # flat buffer (the step before the reduce)
         offs = [self.plan.tensor_offset(t) for t in range(self.plan.num_tensors)]
@@ -392,8 +406,12 @@ class AllRanksWorkload:
                                      synth.GRAD_SIGMA)
             self.grad_tensors.append(g)
         self.flat_out = torch.empty(P, dtype=torch.int16, device=device)
-        self.extra_phases = [("flatten", zb.prepare_flatten_params(self.plan, self.grad_tensors,
-                                                                  self.flat_out, st))]
+        self._ft = zb.CopyTable.flatten(self.plan, self.grad_tensors, self.flat_out)
+        self.extra_phases = [("flatten", self._ft.prepare_run(st)),
+                             ("flatten_call", zb.prepare_flatten_params(self.plan, self.grad_tensors,
+                                                                       self.flat_out, st)),
+                             ("gather_call", zb.prepare_gather_params(
+                                 self.plan, [self.param[s] for s in sl], self.tensors, st))]
         self.t = 0
         torch.cuda.synchronize()
 
@@ -413,7 +431,8 @@ class AllRanksWorkload:
     def bytes_per_phase(self):
         P = self.P
         return {"reduce": (2 * self.replicas + 2) * P, "adamw": 28 * P, "gather": 4 * self.phi,
-                "flatten": 4 * self.phi + 2 * (P - self.phi)}
+                "flatten": 4 * self.phi + 2 * (P - self.phi), "gather_call": 4 * self.phi,
+                "flatten_call": 4 * self.phi + 2 * (P - self.phi)}
 
     def describe(self):
         return (f"{self.workload.name} tensor list, N_d={self.n_ranks}, all {self.n_ranks} ranks in "

@@ -23,6 +23,8 @@
  *                           (all-gather output layout, then un-flatten)
  *   zero_flatten_params     per-tensor bf16 buffers into the padded flat buffer
  *                           (the step before the reduce; inverse of the gather)
+ *   zero_*_table_create, zero_copy_table_run  the gather or flatten of fixed
+ *                           buffers, described once in device memory
  *   zero_offload_adamw_step ZeRO-Offload: the update on the host CPU, with the
  *                           gradient and parameter transfers overlapped
  *
@@ -347,6 +349,40 @@ zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* sha
  * Errors: ZERO_EINVAL (null plan/arrays or a needed null pointer); ZERO_EHIP. */
 zero_status zero_flatten_params(const zero_plan* plan, const uint16_t* const* tensors,
                                 uint16_t* flat, hipStream_t stream);
+
+/* Gather and flatten for fixed buffers, with their tables in device memory.
+ * A training loop gathers the same shards into the same tensors every step
+ * (and flattens the same per-tensor gradients into the same flat buffer), so
+ * the copy can be described once. zero_gather_table_create takes the
+ * arguments of zero_gather_params, zero_flatten_table_create those of
+ * zero_flatten_params, with the same checks. Each lists every plan segment
+ * (for the flatten also every zero-filled gap) as a piece, and copies to
+ * device memory that the table owns one 32-byte descriptor per piece (source,
+ * destination, length) and one 4-byte piece index per workgroup of 2,048
+ * elements (0.1% of the bytes copied). zero_copy_table_run then performs the
+ * whole copy in one launch (several only past 2^24 workgroups, above 3.4e10
+ * elements), for flat and Shard(0) plans alike, with the same result as the
+ * call the table was made from: the same bits are copied, and the same
+ * positions zero-filled.
+ * Create: hipMalloc and a synchronous hipMemcpy on the current device, once.
+ * The table keeps the device pointers, not the data: the caller keeps those
+ * buffers alive and in place for the table's lifetime. A NULL shard skips its
+ * rank, as in zero_gather_params. out receives the table.
+ * Errors: as the call it mirrors; ZERO_EINVAL for a NULL out; ZERO_ERANGE for
+ * 2^31 workgroups or more; ZERO_ENOMEM; ZERO_EHIP (allocation or copy).
+ * Run: enqueued on stream; it must run with the table's device current
+ * (ZERO_EINVAL otherwise). An empty table enqueues nothing.
+ * Free: releases the device memory (hipFree, which waits for the device);
+ * no run using the table may still be in flight. Accepts NULL.
+ * Blocks: the workgroups of one run, or -1 for NULL. */
+typedef struct zero_copy_table zero_copy_table;
+zero_status zero_gather_table_create(const zero_plan* plan, const uint16_t* const* shards,
+                                     uint16_t* const* tensors, zero_copy_table** out);
+zero_status zero_flatten_table_create(const zero_plan* plan, const uint16_t* const* tensors,
+                                      uint16_t* flat, zero_copy_table** out);
+zero_status zero_copy_table_run(const zero_copy_table* table, hipStream_t stream);
+int64_t zero_copy_table_blocks(const zero_copy_table* table);
+void zero_copy_table_free(zero_copy_table* table);
 
 /* ------------------------------------------------------------------ ZeRO-Offload
  *

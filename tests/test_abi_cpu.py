@@ -208,6 +208,32 @@ def test_multi_tensor_table_rejects_bad_arguments_before_touching_the_gpu(zm):
     assert lib._mt_blocks(None) == -1
 
 
+def test_copy_tables_reject_bad_arguments_before_touching_the_gpu(zm):
+    """Gather and flatten tables check their arguments as the calls do; a plan
+    with nothing to copy makes an empty table, which needs no device."""
+    lib = zm._binding
+    out = ctypes.c_void_p()
+    plan = zm.zero_partition_plan([5, 3], 2, 8)
+    two = (ctypes.c_void_p * 2)(None, None)
+    assert lib._gt_create(plan.handle, two, two, None) == lib.ZERO_EINVAL             # NULL out
+    assert lib._gt_create(None, two, two, ctypes.byref(out)) == lib.ZERO_EINVAL       # NULL plan
+    assert lib._gt_create(plan.handle, None, two, ctypes.byref(out)) == lib.ZERO_EINVAL
+    assert lib._gt_create(plan.handle, two, two, ctypes.byref(out)) == lib.ZERO_EINVAL  # NULL tensor
+    assert "tensor 0" in zm.zero_last_error()
+    assert lib._ft_create(plan.handle, two, None, ctypes.byref(out)) == lib.ZERO_EINVAL  # NULL flat
+    assert lib._ft_create(None, two, None, ctypes.byref(out)) == lib.ZERO_EINVAL
+    assert not out.value
+    # NULL shards skip every rank: an empty gather table
+    empty = zm.zero_partition_plan([0, 0], 2, 8)
+    assert lib._gt_create(empty.handle, two, two, ctypes.byref(out)) == lib.ZERO_OK
+    assert out.value and lib._ct_blocks(out) == 0
+    assert lib._ct_run(out, None) == lib.ZERO_OK
+    lib._ct_free(out)
+    assert lib._ct_run(None, None) == lib.ZERO_EINVAL
+    assert lib._ct_blocks(None) == -1
+    lib._ct_free(None)
+
+
 def test_builder_loads_without_importing_the_package():
     """build() must work when the in-tree library is stale or missing, so its
     build script is loaded without importing the package (which loads the

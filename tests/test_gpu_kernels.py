@@ -623,3 +623,91 @@ def test_gather_skips_null_shards(zm, kind):
     torch.cuda.synchronize()
     for i, (o, w) in enumerate(zip(outs, gather(ref, shards))):
         assert_bits_equal(host_u16(o), w, f"complete, tensor {i}")
+
+
+# ----------------------------------------------------------------------------- copy tables
+
+def _random_plan(zm, rng, kind):
+    t = int(rng.integers(1, 9))
+    dim0 = [int(x) for x in rng.integers(1, 3000, t)]
+    dim0[0] = int(rng.integers(1, 4))                     # fewer rows than ranks
+    numels = [d * int(k) for d, k in zip(dim0, rng.integers(1, 40, t))]
+    n_ranks = int(rng.choice([1, 2, 3, 4, 8]))
+    align = int(rng.choice([1, 8, 128]))
+    note(f"copy table {kind} dim0={dim0} numels={numels} N_d={n_ranks} A={align}")
+    if kind == "flat":
+        return (oracle.partition_plan(numels, n_ranks, align), zm.zero_partition_plan(numels, n_ranks, align),
+                oracle.gather_params, oracle.flatten_params, numels)
+    return (oracle.partition_plan_shard0(numels, dim0, n_ranks, align),
+            zm.zero_partition_plan_shard0(numels, dim0, n_ranks, align),
+            oracle.gather_params_shard0, oracle.flatten_params_shard0, numels)
+
+
+@pytest.mark.parametrize("kind", ["flat", "shard0"])
+@pytest.mark.parametrize("seed", range(4))
+def test_copy_tables_match_the_oracle(zm, seed, kind):
+    """Gather and flatten through device tables on random plans, with buffers
+    2 bytes off alignment on odd seeds; each table runs twice, with new data in
+    its source buffers before the second run."""
+    rng = np.random.default_rng(1500 + seed)
+    ref, plan, gather, flatten, numels = _random_plan(zm, rng, kind)
+    S = ref.shard_numel
+    off = seed % 2
+    d_sh = [torch.zeros(S + off, dtype=torch.int16, device=dev())[off:] for _ in range(ref.n_ranks)]
+    outs = [torch.full((n + off,), 0x5555, dtype=torch.int16, device=dev())[off:] for n in numels]
+    tab = zm.CopyTable.gather(plan, d_sh, outs)
+    assert tab.blocks == sum((seg[3] + 2047) // 2048 for r in range(ref.n_ranks)
+                             for seg in plan.segments(r) if seg[3] > 0)
+    for run in range(2):
+        shards = [rng.integers(0, 1 << 16, S).astype(np.uint16) for _ in range(ref.n_ranks)]
+        for d, x in zip(d_sh, shards):
+            d.copy_(torch.from_numpy(x.view(np.int16)))
+        tab.run()
+        torch.cuda.synchronize()
+        for i, (o, w) in enumerate(zip(outs, gather(ref, shards))):
+            assert_bits_equal(host_u16(o), w, f"gather run {run} tensor {i}")
+    d_t = [torch.zeros(n + off, dtype=torch.int16, device=dev())[off:] for n in numels]
+    flat = torch.full((ref.padded_numel + off,), 0x5555, dtype=torch.int16, device=dev())[off:]
+    ftab = zm.CopyTable.flatten(plan, d_t, flat)
+    for run in range(2):
+        tensors = [rng.integers(0, 1 << 16, n).astype(np.uint16) for n in numels]
+        for d, x in zip(d_t, tensors):
+            d.copy_(torch.from_numpy(x.view(np.int16)))
+        flat.fill_(0x3333)
+        ftab.run()
+        torch.cuda.synchronize()
+        assert_bits_equal(host_u16(flat), flatten(ref, tensors), f"flatten run {run}")
+
+
+@pytest.mark.parametrize("kind", ["flat", "shard0"])
+def test_copy_tables_equal_the_calls_on_gpt2_small_and_skip_null_shards(zm, kind):
+    """On the GPT-2-small list at N_d = 8, the gather table's output equals
+    zero_gather_params's and the flatten table's equals zero_flatten_params's;
+    a table made with a NULL shard leaves that rank's elements untouched."""
+    w = synth.WORKLOADS["gpt2-small"]
+    if kind == "flat":
+        plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
+    else:
+        plan = zm.zero_partition_plan_shard0(w.numels, [s[0] for s in w.shapes], w.n_ranks, w.align)
+    S, P = plan.shard_numel, plan.padded_numel
+    flat = to_dev_u16(synth.normal_bf16(P, 31, synth.KIND_PARAM, 0, 0, 0, None, 0.02))
+    shards = [flat[r * S:(r + 1) * S] for r in range(w.n_ranks)]
+    a = [torch.full((n,), 0x1111, dtype=torch.int16, device=dev()) for n in w.numels]
+    b = [torch.full((n,), 0x1111, dtype=torch.int16, device=dev()) for n in w.numels]
+    zm.zero_gather_params(plan, shards, a)
+    zm.CopyTable.gather(plan, shards, b).run()
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    fa = torch.full((P,), 0x2222, dtype=torch.int16, device=dev())
+    fb = torch.full((P,), 0x2222, dtype=torch.int16, device=dev())
+    zm.zero_flatten_params(plan, a, fa)
+    zm.CopyTable.flatten(plan, a, fb).run()
+    torch.cuda.synchronize()
+    assert torch.equal(fa, fb)
+    c = [torch.full((n,), 0x1111, dtype=torch.int16, device=dev()) for n in w.numels]
+    d = [torch.full((n,), 0x1111, dtype=torch.int16, device=dev()) for n in w.numels]
+    skip = [None if r == 3 else x for r, x in enumerate(shards)]
+    zm.zero_gather_params(plan, skip, c)
+    zm.CopyTable.gather(plan, skip, d).run()
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(c, d))

@@ -82,6 +82,13 @@ _mt_free = _fn("zero_mt_table_free", None, [c_vp])
 _mt_blocks = _fn("zero_mt_table_blocks", c_i64, [c_vp])
 _mt_step = _fn("zero_mt_table_adamw_step", c_i32,
                [c_vp, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl, c_vp, c_vp])
+_gt_create = _fn("zero_gather_table_create", c_i32,
+                 [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), ctypes.POINTER(c_vp)])
+_ft_create = _fn("zero_flatten_table_create", c_i32,
+                 [c_vp, ctypes.POINTER(c_vp), c_vp, ctypes.POINTER(c_vp)])
+_ct_run = _fn("zero_copy_table_run", c_i32, [c_vp, c_vp])
+_ct_blocks = _fn("zero_copy_table_blocks", c_i64, [c_vp])
+_ct_free = _fn("zero_copy_table_free", None, [c_vp])
 _status_string = _fn("zero_status_string", ctypes.c_char_p, [c_i32])
 _last_error = _fn("zero_last_error", ctypes.c_char_p, [])
 
@@ -430,6 +437,61 @@ class MultiTensorTable:
             _stream(None, self._keep[0][0]) if self._keep[0] else 0)
         _check(_mt_step(self._h, step, lr, beta1, beta2, eps, weight_decay,
                         _ptr(clip_scale, 4, "clip_scale"), st), "zero_mt_table_adamw_step")
+
+
+class CopyTable:
+    """Owner of a zero_copy_table: the gather (CopyTable.gather) or flatten
+    (CopyTable.flatten) of fixed buffers, described once in device memory (on
+    the current device) and run in one launch. The plan and the buffers are
+    held here, so they outlive the table."""
+
+    def __init__(self, handle: c_vp, keep):
+        self._h = handle
+        self._free = _ct_free          # held by the instance for interpreter exit
+        self._keep = keep
+
+    @classmethod
+    def gather(cls, plan: Plan, shards: Sequence, tensors: Sequence) -> "CopyTable":
+        _check_gather_args(plan, shards, tensors)
+        sp = (c_vp * max(len(shards), 1))(*[_ptr(x, 2, "shard") for x in shards])
+        tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
+        h = c_vp()
+        _check(_gt_create(plan.handle, sp, tp, ctypes.byref(h)), "zero_gather_table_create")
+        return cls(h, (plan, list(shards), list(tensors)))
+
+    @classmethod
+    def flatten(cls, plan: Plan, tensors: Sequence, flat) -> "CopyTable":
+        _check_flatten_args(plan, tensors, flat)
+        tp = (c_vp * max(len(tensors), 1))(*[_ptr(t, 2, "tensor") for t in tensors])
+        h = c_vp()
+        _check(_ft_create(plan.handle, tp, _ptr(flat, 2, "flat"), ctypes.byref(h)),
+               "zero_flatten_table_create")
+        return cls(h, (plan, list(tensors), flat))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        free = getattr(self, "_free", None)
+        if h is not None and h.value and free is not None:
+            free(h)
+            h.value = None
+
+    @property
+    def blocks(self) -> int:
+        return int(_ct_blocks(self._h))
+
+    def run(self, stream=None) -> None:
+        _check(_ct_run(self._h, int(stream) if stream is not None else self._default_stream()),
+               "zero_copy_table_run")
+
+    def prepare_run(self, stream) -> "Prepared":
+        p = Prepared(_ct_run, [self._h, int(stream) if stream is not None else
+                               self._default_stream()], "zero_copy_table_run")
+        p._keep = self
+        return p
+
+    def _default_stream(self) -> int:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
 
 
 def _host_ptr(a, itemsize: int, what: str) -> int:

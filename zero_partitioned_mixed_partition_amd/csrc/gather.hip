@@ -23,6 +23,7 @@
 //                         descriptors, and launches, than the segment form.
 #include <hip/hip_runtime.h>
 
+#include <new>
 #include <string>
 #include <vector>
 
@@ -62,20 +63,11 @@ struct SegBatch {
 };
 static_assert(sizeof(SegBatch) <= 4096, "kernel arguments are limited to 4 KB");
 
-__global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
+// One workgroup's chunk of a piece: len (<= kChunk) elements from src to dst,
+// or zeros when src is NULL.
+__device__ __forceinline__ void copy_chunk(const uint16_t* src, uint16_t* dst, int64_t len) {
     typedef typename LaneBits<kLane>::T V;
-    const int64_t blk = blockIdx.x;
-    int lo = 0, hi = b.n - 1;                         // find s with first_block[s] <= blk < first_block[s+1]
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
-    }
-    const int s = lo;
-    const int64_t start = (blk - b.first_block[s]) * kChunk;
-    const int64_t seg_len = b.len[s];
-    const int64_t len = seg_len - start < kChunk ? seg_len - start : kChunk;
-    uint16_t* dst = b.dst[s] + start;
-    if (b.src[s] == nullptr) {                        // padding: fill with +0
+    if (src == nullptr) {                             // padding: fill with +0
         const bool aligned = (reinterpret_cast<uintptr_t>(dst) & (2 * kLane - 1)) == 0;
 #pragma unroll
         for (int v = 0; v < kVecs; ++v) {
@@ -88,7 +80,6 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
         }
         return;
     }
-    const uint16_t* src = b.src[s] + start;
     constexpr uintptr_t kBytes = 2 * kLane;
     const uintptr_t sa = reinterpret_cast<uintptr_t>(src), da = reinterpret_cast<uintptr_t>(dst);
     if (((sa ^ da) & (kBytes - 1)) == 0) {
@@ -115,6 +106,42 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
     } else {
         for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
     }
+}
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
+    const int64_t blk = blockIdx.x;
+    int lo = 0, hi = b.n - 1;                         // find s with first_block[s] <= blk < first_block[s+1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (b.first_block[mid] <= blk) lo = mid; else hi = mid - 1;
+    }
+    const int s = lo;
+    const int64_t start = (blk - b.first_block[s]) * kChunk;
+    const int64_t seg_len = b.len[s];
+    const int64_t len = seg_len - start < kChunk ? seg_len - start : kChunk;
+    copy_chunk(b.src[s] != nullptr ? b.src[s] + start : nullptr, b.dst[s] + start, len);
+}
+
+// Device-resident form for fixed buffers: one 32-byte descriptor per piece and,
+// per workgroup, the index of its descriptor, so a workgroup finds its piece
+// with two dependent scalar loads and every piece of a plan (a Shard(0) plan
+// has about N_d per tensor) goes out in one launch.
+struct alignas(32) PieceDesc {
+    const uint16_t* src;        // NULL: fill with zeros
+    uint16_t* dst;
+    int64_t len;
+    int64_t first_block;
+};
+static_assert(sizeof(PieceDesc) == 32, "one 32-byte descriptor per piece");
+
+__global__ __launch_bounds__(kThreads) void copy_table_kernel(const PieceDesc* __restrict__ table,
+                                                              const uint32_t* __restrict__ index,
+                                                              int64_t blk0) {
+    const int64_t blk = blk0 + static_cast<int64_t>(blockIdx.x);
+    const PieceDesc d = table[index[blk]];
+    const int64_t start = (blk - d.first_block) * kChunk;
+    const int64_t len = d.len - start < kChunk ? d.len - start : kChunk;
+    copy_chunk(d.src != nullptr ? d.src + start : nullptr, d.dst + start, len);
 }
 
 // Tensor-major gather for Shard(0) plans: one descriptor per tensor instead of
@@ -333,6 +360,38 @@ zero_status launch_tensors(const zero_plan* plan, uint16_t* const* bufs, uint16_
     return flush();
 }
 
+// Every segment of the plan as a piece from its shard to its tensor (a NULL
+// shard skips its rank's segments).
+std::vector<Piece> gather_pieces(const zero_plan* plan, const uint16_t* const* shards,
+                                 uint16_t* const* tensors) {
+    std::vector<Piece> pieces;
+    pieces.reserve(plan->all.size());
+    for (const zero_segment& seg : plan->all)
+        if (shards[seg.rank] != nullptr)
+            pieces.push_back({shards[seg.rank] + seg.shard_offset,
+                              tensors[seg.tensor] + seg.tensor_offset, seg.length});
+    return pieces;
+}
+
+// Every segment from its tensor to its place in the flat buffer, in flat order,
+// with a zero-fill piece for every gap (and after the last segment). With
+// with_copies false, the gaps only.
+std::vector<Piece> flatten_pieces(const zero_plan* plan, const uint16_t* const* tensors,
+                                  uint16_t* flat, bool with_copies) {
+    std::vector<Piece> pieces;
+    pieces.reserve(2 * plan->all.size() + 1);
+    int64_t pos = 0;
+    for (const zero_segment& seg : plan->all) {
+        const int64_t at = static_cast<int64_t>(seg.rank) * plan->shard + seg.shard_offset;
+        if (at > pos) pieces.push_back({nullptr, flat + pos, at - pos});
+        if (with_copies)
+            pieces.push_back({tensors[seg.tensor] + seg.tensor_offset, flat + at, seg.length});
+        pos = at + seg.length;
+    }
+    if (plan->padded > pos) pieces.push_back({nullptr, flat + pos, plan->padded - pos});
+    return pieces;
+}
+
 bool fits_tensor_major(const zero_plan* plan) {
     if (plan->kind != 1 || plan->n_ranks > kMaxRanks || plan->shard <= 0) return false;
     for (const int64_t n : plan->numels)
@@ -377,11 +436,11 @@ extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t*
         return launch_tensors_any<false>(plan, const_cast<uint16_t* const*>(shards), tensors, stream,
                                          "zero_gather_params launch");
     std::vector<Piece> pieces;
-    pieces.reserve(plan->all.size());
-    for (const zero_segment& seg : plan->all)
-        if (shards[seg.rank] != nullptr)
-            pieces.push_back({shards[seg.rank] + seg.shard_offset,
-                              tensors[seg.tensor] + seg.tensor_offset, seg.length});
+    try {
+        pieces = gather_pieces(plan, shards, tensors);
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "zero_gather_params: allocation failed");
+    }
     return launch_pieces(pieces, stream, "zero_gather_params launch");
 }
 
@@ -397,31 +456,152 @@ extern "C" zero_status zero_flatten_params(const zero_plan* plan, const uint16_t
     // Shard(0) plans copy the tensors with the tensor-major kernel, flat plans
     // copy every segment, in flat order, to its place.
     const bool tensor_major = ZERO_GATHER_TENSOR_MAJOR && fits_tensor_major(plan);
+    std::vector<Piece> pieces;
+    try {
+        pieces = flatten_pieces(plan, tensors, flat, !tensor_major);
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "zero_flatten_params: allocation failed");
+    }
     if (tensor_major) {
-        std::vector<Piece> gaps;
-        int64_t pos = 0;
-        for (const zero_segment& seg : plan->all) {
-            const int64_t at = static_cast<int64_t>(seg.rank) * plan->shard + seg.shard_offset;
-            if (at > pos) gaps.push_back({nullptr, flat + pos, at - pos});
-            pos = at + seg.length;
-        }
-        if (plan->padded > pos) gaps.push_back({nullptr, flat + pos, plan->padded - pos});
-        st = launch_pieces(gaps, stream, "zero_flatten_params launch");
+        st = launch_pieces(pieces, stream, "zero_flatten_params launch");   // the gaps
         if (st != ZERO_OK) return st;
         std::vector<uint16_t*> bufs(static_cast<size_t>(plan->n_ranks));
         for (int32_t r = 0; r < plan->n_ranks; ++r) bufs[static_cast<size_t>(r)] = flat + int64_t(r) * plan->shard;
         return launch_tensors_any<true>(plan, bufs.data(), const_cast<uint16_t* const*>(tensors),
                                         stream, "zero_flatten_params launch");
     }
-    std::vector<Piece> pieces;
-    pieces.reserve(2 * plan->all.size() + 1);
-    int64_t pos = 0;
-    for (const zero_segment& seg : plan->all) {
-        const int64_t at = static_cast<int64_t>(seg.rank) * plan->shard + seg.shard_offset;
-        if (at > pos) pieces.push_back({nullptr, flat + pos, at - pos});
-        pieces.push_back({tensors[seg.tensor] + seg.tensor_offset, flat + at, seg.length});
-        pos = at + seg.length;
-    }
-    if (plan->padded > pos) pieces.push_back({nullptr, flat + pos, plan->padded - pos});
     return launch_pieces(pieces, stream, "zero_flatten_params launch");
+}
+
+// ------------------------------------------------------------ device table
+
+struct zero_copy_table {
+    int device = -1;
+    void* mem = nullptr;          // descriptors, then the per-workgroup index
+    const PieceDesc* table = nullptr;
+    const uint32_t* index = nullptr;
+    int64_t blocks = 0;
+};
+
+namespace {
+
+zero_status make_copy_table(const std::vector<Piece>& pieces, zero_copy_table** out, const char* who) {
+    using zero::fail;
+    std::vector<PieceDesc> descs;
+    std::vector<uint32_t> index;
+    zero_copy_table* tab = nullptr;
+    try {
+        int64_t blocks = 0;
+        for (const Piece& pc : pieces) {
+            if (pc.len <= 0) continue;
+            const int64_t b = (pc.len + kChunk - 1) / kChunk;
+            if (blocks + b > 0x7FFFFFFF || descs.size() >= 0xFFFFFFFFu)
+                return fail(ZERO_ERANGE, std::string(who) + ": more than 2^31 workgroups");
+            index.insert(index.end(), static_cast<size_t>(b), static_cast<uint32_t>(descs.size()));
+            descs.push_back({pc.src, pc.dst, pc.len, blocks});
+            blocks += b;
+        }
+        tab = new zero_copy_table;
+        tab->blocks = blocks;
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, std::string(who) + ": host allocation failed");
+    }
+    zero_status st = ZERO_OK;
+    if (tab->blocks > 0) {        // an empty table needs no device
+        st = zero::check_hip(hipGetDevice(&tab->device), who);
+        const size_t table_bytes = (descs.size() * sizeof(PieceDesc) + 255) / 256 * 256;
+        if (st == ZERO_OK)
+            st = zero::check_hip(hipMalloc(&tab->mem, table_bytes + index.size() * sizeof(uint32_t)), who);
+        if (st == ZERO_OK) {
+            tab->table = static_cast<const PieceDesc*>(tab->mem);
+            tab->index = reinterpret_cast<const uint32_t*>(static_cast<char*>(tab->mem) + table_bytes);
+            st = zero::check_hip(hipMemcpy(tab->mem, descs.data(), descs.size() * sizeof(PieceDesc),
+                                           hipMemcpyHostToDevice), who);
+        }
+        if (st == ZERO_OK)
+            st = zero::check_hip(hipMemcpy(const_cast<uint32_t*>(tab->index), index.data(),
+                                           index.size() * sizeof(uint32_t), hipMemcpyHostToDevice), who);
+    }
+    if (st != ZERO_OK) {
+        if (tab->mem) (void)hipFree(tab->mem);
+        delete tab;
+        return st;
+    }
+    *out = tab;
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_gather_table_create(const zero_plan* plan, const uint16_t* const* shards,
+                                                uint16_t* const* tensors, zero_copy_table** out) {
+    using zero::fail;
+    zero::clear_error();
+    if (out == nullptr) return fail(ZERO_EINVAL, "zero_gather_table_create: NULL out");
+    *out = nullptr;
+    if (plan == nullptr || shards == nullptr)
+        return fail(ZERO_EINVAL, "zero_gather_table_create: NULL plan or shards");
+    zero_status st = check_tensors(plan, tensors, "zero_gather_table_create");
+    if (st != ZERO_OK) return st;
+    std::vector<Piece> pieces;
+    try {
+        pieces = gather_pieces(plan, shards, tensors);
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "zero_gather_table_create: allocation failed");
+    }
+    return make_copy_table(pieces, out, "zero_gather_table_create");
+}
+
+extern "C" zero_status zero_flatten_table_create(const zero_plan* plan, const uint16_t* const* tensors,
+                                                 uint16_t* flat, zero_copy_table** out) {
+    using zero::fail;
+    zero::clear_error();
+    if (out == nullptr) return fail(ZERO_EINVAL, "zero_flatten_table_create: NULL out");
+    *out = nullptr;
+    if (plan == nullptr) return fail(ZERO_EINVAL, "zero_flatten_table_create: NULL plan");
+    if (plan->padded > 0 && flat == nullptr)
+        return fail(ZERO_EINVAL, "zero_flatten_table_create: NULL flat");
+    zero_status st = check_tensors(plan, tensors, "zero_flatten_table_create");
+    if (st != ZERO_OK) return st;
+    std::vector<Piece> pieces;
+    try {
+        pieces = flatten_pieces(plan, tensors, flat, true);
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "zero_flatten_table_create: allocation failed");
+    }
+    return make_copy_table(pieces, out, "zero_flatten_table_create");
+}
+
+extern "C" zero_status zero_copy_table_run(const zero_copy_table* table, hipStream_t stream) {
+    using zero::fail;
+    zero::clear_error();
+    if (table == nullptr) return fail(ZERO_EINVAL, "zero_copy_table_run: NULL table");
+    if (table->blocks == 0) return ZERO_OK;
+    int dev = -1;
+    zero_status st = zero::check_hip(hipGetDevice(&dev), "zero_copy_table_run: hipGetDevice");
+    if (st != ZERO_OK) return st;
+    if (dev != table->device)
+        return fail(ZERO_EINVAL, "zero_copy_table_run: the table lives on device " +
+                                     std::to_string(table->device) + ", the current device is " +
+                                     std::to_string(dev));
+    // A dispatch holds fewer than 2^32 work-items: longer tables take several launches.
+    constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
+    for (int64_t b0 = 0; b0 < table->blocks; b0 += kMaxBlocks) {
+        const int64_t nb = table->blocks - b0 < kMaxBlocks ? table->blocks - b0 : kMaxBlocks;
+        hipLaunchKernelGGL(copy_table_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0,
+                           stream, table->table, table->index, b0);
+        st = zero::check_hip(hipGetLastError(), "zero_copy_table_run launch");
+        if (st != ZERO_OK) return st;
+    }
+    return ZERO_OK;
+}
+
+extern "C" int64_t zero_copy_table_blocks(const zero_copy_table* table) {
+    return table ? table->blocks : -1;
+}
+
+extern "C" void zero_copy_table_free(zero_copy_table* table) {
+    if (!table) return;
+    if (table->mem) (void)hipFree(table->mem);
+    delete table;
 }

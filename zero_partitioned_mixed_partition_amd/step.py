@@ -9,7 +9,8 @@ with section "ZeRO-Stage 2"'s bucketed reduction:
   2. zero_clip_scale         global-norm clip coefficient from every partial
   3. zero_shard_adamw_step   fp32 master/m/v update, bf16 shard emitted into
                              the rank's slot of the parameter shards
-  4. zero_gather_params      all shards -> per-tensor bf16 parameters
+  4. zero_gather_params      all shards -> per-tensor bf16 parameters (through a
+                             copy table: zero_gather_table_create, zero_copy_table_run)
 
 Everything stays on the device and on one stream; nothing synchronises with
 the host inside a step. The other ranks' norm partials and parameter shards
@@ -142,9 +143,11 @@ class RankStep:
             clip_scale=clip, stream=st, **self.hyper.as_kwargs()))(self.t)
 
     def gather(self, stream=None):
+        # The shards and tensors are this object's fixed buffers, so the gather
+        # goes through a device-resident copy table, built on first use.
         if self.tensors:
-            self._prepared("gather", stream, lambda st: zb.prepare_gather_params(
-                self.plan, self.param_shards, self.tensors, st))()
+            self._prepared("gather", stream, lambda st: zb.CopyTable.gather(
+                self.plan, self.param_shards, self.tensors).prepare_run(st))()
 
     def step(self, windows, stream=None) -> None:
         self.reduce(windows, stream)
