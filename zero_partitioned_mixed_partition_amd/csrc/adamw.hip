@@ -262,10 +262,10 @@ static_assert(sizeof(MtDesc) == 64, "one 64-byte descriptor per tensor");
 
 __global__ __launch_bounds__(kThreads) void adamw_table_kernel(const MtDesc* __restrict__ table,
                                                                const uint32_t* __restrict__ index,
-                                                               int64_t blk0, AdamScalars c,
+                                                               int64_t blk0, int64_t per, AdamScalars c,
                                                                const float* __restrict__ clip_scale) {
     const int64_t blk = blk0 + static_cast<int64_t>(blockIdx.x);
-    const MtDesc d = table[index[blk]];
+    const MtDesc d = table[index[zero::dev::xcd_major_entry(blk0, per)]];
     mt_update(d.p, d.m, d.v, d.g, d.o, d.n, (blk - d.first_block) * kMtChunk + threadIdx.x, c,
               clip_scale);
 }
@@ -505,6 +505,7 @@ extern "C" zero_status zero_mt_table_create(float* const* masters, float* const*
             descs.push_back(d);
             blocks += b;
         }
+        if (blocks > 0) index = zero::xcd_major_index(index);
         tab = new zero_mt_table;
         tab->blocks = blocks;
     } catch (const std::bad_alloc&) {
@@ -568,11 +569,12 @@ extern "C" zero_status zero_mt_table_adamw_step(const zero_mt_table* table, int6
     st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
     if (st != ZERO_OK) return st;
     // A dispatch holds fewer than 2^32 work-items: longer lists take several launches.
-    constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
+    constexpr int64_t kMaxBlocks = zero::kTableLaunchBlocks;
     for (int64_t b0 = 0; b0 < table->blocks; b0 += kMaxBlocks) {
         const int64_t nb = table->blocks - b0 < kMaxBlocks ? table->blocks - b0 : kMaxBlocks;
+        const int64_t per = (nb + 7) / 8;
         hipLaunchKernelGGL(adamw_table_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0,
-                           stream, table->table, table->index, b0, c, clip_scale);
+                           stream, table->table, table->index, b0, per, c, clip_scale);
         st = zero::check_hip(hipGetLastError(), "zero_mt_table_adamw_step launch");
         if (st != ZERO_OK) return st;
     }

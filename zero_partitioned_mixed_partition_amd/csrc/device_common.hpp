@@ -125,6 +125,13 @@ __device__ __forceinline__ void st_stream(T* p, const T& v) {
 #endif
 }
 
+// Entry of workgroup blockIdx.x in a launch's XCD-major table index (the
+// layout is described with xcd_major_index on the host side).
+__device__ __forceinline__ int64_t xcd_major_entry(int64_t blk0, int64_t per) {
+    const int64_t x = blockIdx.x;
+    return blk0 + (x & 7) * per + (x >> 3);
+}
+
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);

@@ -136,9 +136,9 @@ static_assert(sizeof(PieceDesc) == 32, "one 32-byte descriptor per piece");
 
 __global__ __launch_bounds__(kThreads) void copy_table_kernel(const PieceDesc* __restrict__ table,
                                                               const uint32_t* __restrict__ index,
-                                                              int64_t blk0) {
+                                                              int64_t blk0, int64_t per) {
     const int64_t blk = blk0 + static_cast<int64_t>(blockIdx.x);
-    const PieceDesc d = table[index[blk]];
+    const PieceDesc d = table[index[zero::dev::xcd_major_entry(blk0, per)]];
     const int64_t start = (blk - d.first_block) * kChunk;
     const int64_t len = d.len - start < kChunk ? d.len - start : kChunk;
     copy_chunk(d.src != nullptr ? d.src + start : nullptr, d.dst + start, len);
@@ -501,6 +501,7 @@ zero_status make_copy_table(const std::vector<Piece>& pieces, zero_copy_table** 
             descs.push_back({pc.src, pc.dst, pc.len, blocks});
             blocks += b;
         }
+        if (blocks > 0) index = zero::xcd_major_index(index);
         tab = new zero_copy_table;
         tab->blocks = blocks;
     } catch (const std::bad_alloc&) {
@@ -585,11 +586,12 @@ extern "C" zero_status zero_copy_table_run(const zero_copy_table* table, hipStre
                                      std::to_string(table->device) + ", the current device is " +
                                      std::to_string(dev));
     // A dispatch holds fewer than 2^32 work-items: longer tables take several launches.
-    constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
+    constexpr int64_t kMaxBlocks = zero::kTableLaunchBlocks;
     for (int64_t b0 = 0; b0 < table->blocks; b0 += kMaxBlocks) {
         const int64_t nb = table->blocks - b0 < kMaxBlocks ? table->blocks - b0 : kMaxBlocks;
+        const int64_t per = (nb + 7) / 8;
         hipLaunchKernelGGL(copy_table_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0,
-                           stream, table->table, table->index, b0);
+                           stream, table->table, table->index, b0, per);
         st = zero::check_hip(hipGetLastError(), "zero_copy_table_run launch");
         if (st != ZERO_OK) return st;
     }

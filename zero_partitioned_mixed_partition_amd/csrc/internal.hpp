@@ -38,4 +38,27 @@ int device_cu_count();
 // registers and LDS. Falls back to 4 per CU if the query fails.
 int device_resident_blocks(const void* kernel, int threads);
 
+// Device-resident tables (multi-tensor AdamW, gather/flatten copies) hold one
+// descriptor index per workgroup. The dispatcher deals a launch's workgroups
+// round-robin to the 8 XCDs, so the index is stored XCD-major within each
+// launch: workgroup x of a launch of nb reads entry (x % 8) * per + x / 8,
+// per = ceil(nb / 8). Each XCD then reads one contiguous run and each index
+// line is fetched once, instead of once per XCD. Launches hold a multiple of 8
+// workgroups (all but the last), so launch j's entries start at its first
+// workgroup; the last launch pads its run by at most 7 entries.
+constexpr int64_t kTableLaunchBlocks = ((int64_t(1) << 32) / 256 - 1) / 8 * 8;
+
+// The XCD-major index of `plain` (entry b = descriptor of workgroup b).
+inline std::vector<uint32_t> xcd_major_index(const std::vector<uint32_t>& plain) {
+    const int64_t total = static_cast<int64_t>(plain.size());
+    std::vector<uint32_t> out(plain.size() + 7, 0u);
+    for (int64_t b0 = 0; b0 < total; b0 += kTableLaunchBlocks) {
+        const int64_t nb = total - b0 < kTableLaunchBlocks ? total - b0 : kTableLaunchBlocks;
+        const int64_t per = (nb + 7) / 8;
+        for (int64_t x = 0; x < nb; ++x)
+            out[static_cast<size_t>(b0 + (x % 8) * per + x / 8)] = plain[static_cast<size_t>(b0 + x)];
+    }
+    return out;
+}
+
 }  // namespace zero

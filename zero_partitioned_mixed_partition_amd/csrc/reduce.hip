@@ -48,7 +48,10 @@ constexpr int kThreads = 256;
 #endif
 constexpr int kMaxPartials = ZERO_REDUCE_MAX_BLOCKS > ZERO_SQNORM_MAX_BLOCKS
                                  ? ZERO_REDUCE_MAX_BLOCKS : ZERO_SQNORM_MAX_BLOCKS;
-constexpr int kReplicaBatch = 8;             // replica loads in flight per thread
+#ifndef ZERO_REDUCE_BATCH
+#define ZERO_REDUCE_BATCH 8
+#endif
+constexpr int kReplicaBatch = ZERO_REDUCE_BATCH;   // replica loads in flight per thread
 
 struct ReplicaTable {
     const uint16_t* p[ZERO_MAX_REPLICAS];
