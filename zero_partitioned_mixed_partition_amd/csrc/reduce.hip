@@ -108,7 +108,10 @@ template <> struct Bits<2> { typedef uint32_t T; };
 // so the one-group form keeps its lower register count and occupancy.
 // Measured on MI355X with 8 replicas: 2 groups +4.5% at 164 M elements,
 // -2% at 15.6 M; with 64 replicas the wider form would cost 13%.
-constexpr int64_t kTwoGroupsFrom = int64_t(1) << 26;   // shard elements
+#ifndef ZERO_REDUCE_TWO_GROUPS_FROM
+#define ZERO_REDUCE_TWO_GROUPS_FROM (int64_t(1) << 26)
+#endif
+constexpr int64_t kTwoGroupsFrom = ZERO_REDUCE_TWO_GROUPS_FROM;   // shard elements
 
 template <bool kNorm, int kGroups>
 __global__ __launch_bounds__(kThreads) void reduce_vec(ReplicaTable reps, int n_rep,
