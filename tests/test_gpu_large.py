@@ -220,14 +220,20 @@ def test_gpt_1p3b_full_size_gather_of_synthetic_shards(zm):
         shards.append(t)
     tensors = [torch.empty(n, dtype=torch.int16, device=dev()) for n in w.numels]
     zm.zero_gather_params(plan, shards, tensors)
+    # the same gather through a device-resident copy table
+    t_tensors = [torch.full((n,), 0x3333, dtype=torch.int16, device=dev()) for n in w.numels]
+    table = zm.CopyTable.gather(plan, shards, t_tensors)
+    table.run()
     torch.cuda.synchronize()
-    note(f"gpt-1.3b gather: {ref.numel} parameters, {len(w.numels)} tensors")
+    note(f"gpt-1.3b gather: {ref.numel} parameters, {len(w.numels)} tensors, "
+         f"copy table {table.blocks} workgroups")
     host_shards = [synth.normal_bf16(S, w.seed, synth.KIND_PARAM, 0, 0, r * S, ref.numel, 0.02)
                    for r in range(w.n_ranks)]
     want = oracle.gather_params(ref, host_shards)
-    for i, (a, b) in enumerate(zip(tensors, want)):
+    for i, (a, t, b) in enumerate(zip(tensors, t_tensors, want)):
         assert_bits_equal(host_u16(a), b, f"tensor {i}")
-    del shards, tensors
+        assert_bits_equal(host_u16(t), b, f"copy table, tensor {i}")
+    del shards, tensors, t_tensors, table
     _free_gpu()
 
 
@@ -354,6 +360,19 @@ def test_pieces_longer_than_2p30_flatten_and_gather(zm, kind):
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(zip(tensors, back)):
         assert torch.equal(a, b), f"tensor {i} round trip"
+    # the same round trip through copy tables (pieces longer than 2^30 elements are not
+    # split there: 64-bit lengths and offsets)
+    flat2 = torch.full((plan.padded_numel,), 0x4444, dtype=torch.int16, device=dev())
+    zm.CopyTable.flatten(plan, tensors, flat2).run()
+    torch.cuda.synchronize()
+    assert torch.equal(flat2, flat), "copy-table flatten"
+    del flat2
+    back2 = [torch.full((n,), 0x5555, dtype=torch.int16, device=dev()) for n in numels]
+    zm.CopyTable.gather(plan, [flat[r * S:(r + 1) * S] for r in range(n_ranks)], back2).run()
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(tensors, back2)):
+        assert torch.equal(a, b), f"tensor {i} copy-table round trip"
+    del back2
     # the padding is zero and every flat element outside it holds some tensor element
     covered = torch.zeros(plan.padded_numel, dtype=torch.bool, device=dev())
     for r in range(n_ranks):
