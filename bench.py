@@ -381,8 +381,7 @@ class AllRanksWorkload:
         self.tensors = [torch.empty(n, dtype=torch.int16, device=device)
                         for n in plan_numels(self.plan)]
         self.partials = torch.zeros(w.n_ranks, dtype=torch.float64, device=device)
-        self.workspace = torch.empty(zb.zero_sqnorm_workspace_bytes(), dtype=torch.uint8,
-                                     device=device)
+        self.workspace = zb.reduce_workspace(S, device)
         st = torch.cuda.current_stream(device).cuda_stream
         sl = [slice(r * S, (r + 1) * S) for r in range(w.n_ranks)]
         self._reduce = [zb.prepare_grad_reduce_shard(self.plan, r, self.reps, 0, P,

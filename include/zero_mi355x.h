@@ -178,14 +178,22 @@ zero_status zero_plan_memory_bytes(const zero_plan* plan, int32_t stage, int32_t
  *              the sum and the division in IEEE fp32.
  * sqnorm_out   device, nullable: receives the fp64 sum of squares of the bf16
  *              values this call wrote (0 if it wrote nothing). Deterministic for a
- *              given device.
+ *              given window and workspace size.
  * workspace    device, required when sqnorm_out is non-null; at least
  *              zero_sqnorm_workspace_bytes() bytes, 8-byte aligned, owned by
  *              the caller. It holds the per-workgroup partials between the
- *              call's two kernels; it needs no initialisation and its contents
+ *              call's kernels; it needs no initialisation and its contents
  *              on return are unspecified. Calls that may run
  *              at the same time (on different streams) need separate
  *              workspaces; calls on one stream may share one.
+ *              With zero_reduce_workspace_bytes(n) bytes or more, where n is
+ *              the number of elements written (at most count), a window of
+ *              2^24 elements or more, of at most 8 replicas, whose slices are
+ *              4-byte aligned takes the one-pass kernel: one workgroup per 512 elements, a partial per
+ *              workgroup and a two-level final sum. It is faster on windows too
+ *              large for the caches. The bf16 output is the same either way.
+ *              The fp64 sum is grouped differently, so its last bits may
+ *              differ. Without a norm the one-pass kernel needs no workspace.
  * Errors: ZERO_EINVAL (null plan/replicas/shard_grad, a null replica pointer,
  * R out of range, rank out of range, bad window, workspace not 8-byte
  * aligned); ZERO_ENOSPACE; ZERO_EHIP. */
@@ -211,6 +219,11 @@ zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double* sqnorm_out
 /* Workspace bytes that zero_grad_sqnorm and zero_grad_reduce_shard need: a
  * fixed bound, independent of n and of the device. */
 size_t zero_sqnorm_workspace_bytes(void);
+
+/* Workspace bytes with which zero_grad_reduce_shard can take its one-pass
+ * kernel (with the norm) on windows of up to count elements: about 8 bytes per
+ * 512 elements, never less than zero_sqnorm_workspace_bytes(). Host only. */
+size_t zero_reduce_workspace_bytes(int64_t count);
 
 /* ------------------------------------------------------------------ clip coefficient
  *

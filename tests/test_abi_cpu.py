@@ -208,6 +208,18 @@ def test_multi_tensor_table_rejects_bad_arguments_before_touching_the_gpu(zm):
     assert lib._mt_blocks(None) == -1
 
 
+def test_reduce_workspace_bytes(zm):
+    """The one-pass reduce's workspace: the fixed size below 2^24 elements, then
+    a partial per 512 elements plus the first-level sums (8 bytes each)."""
+    fixed = zm.zero_sqnorm_workspace_bytes()
+    assert zm.zero_reduce_workspace_bytes(0) == fixed
+    assert zm.zero_reduce_workspace_bytes((1 << 24) - 1) == fixed
+    for n in ((1 << 24), (1 << 24) + 4097, 164_465_408, 8_819_213_312):
+        blocks = ((n + 1) // 2 + 255) // 256
+        want = 8 * (blocks + (blocks + 2047) // 2048)
+        assert zm.zero_reduce_workspace_bytes(n) == max(want, fixed), n
+
+
 def test_copy_tables_reject_bad_arguments_before_touching_the_gpu(zm):
     """Gather and flatten tables check their arguments as the calls do; a plan
     with nothing to copy makes an empty table, which needs no device."""

@@ -575,6 +575,54 @@ def test_reduce_two_groups_per_pass_full_array(zm, R):
     assert abs(sq.item() - want_sq) <= 1e-12 * want_sq
 
 
+@pytest.mark.parametrize("case", ["odd-window", "eight-replicas", "nine-replicas", "window-in-shard",
+                                  "misaligned"])
+def test_reduce_one_pass(zm, case):
+    """Windows of 2^24 elements or more of at most 8 replicas, with a workspace
+    of zero_reduce_workspace_bytes, take the one-pass kernel (a lane per element
+    pair, a partial per workgroup, a two-level final sum): bits and exact norm
+    against the oracle; the same bf16 output as the grid-stride kernel (fixed
+    workspace); the same norm bits when repeated. Nine replicas and a
+    2-byte-misaligned window fall back to the other kernels, same result."""
+    big = (1 << 24) + 4097                                  # odd: the last element alone
+    n_ranks, rank, R, begin, count = {
+        "odd-window": (1, 0, 3, 0, big),
+        "eight-replicas": (1, 0, 8, 0, big - 1),            # the one-pass maximum
+        "nine-replicas": (1, 0, 9, 0, big - 1),             # grid-stride kernels
+        "window-in-shard": (2, 1, 4, None, big - 3),         # 6 into rank 1's shard
+        "misaligned": (1, 0, 3, 1, big),                    # odd begin: 2-byte offsets
+    }[case]
+    numels = [2 * big + 8] if n_ranks == 2 else [big + 8]
+    ref = oracle.partition_plan(numels, n_ranks, 8)
+    plan = zm.zero_partition_plan(numels, n_ranks, 8)
+    S, phi = ref.shard_numel, ref.numel
+    if begin is None:
+        begin = S + 6
+    assert begin + count <= min((rank + 1) * S, ref.padded_numel)
+    note(f"one-pass reduce {case}: R={R} begin={begin} count={count} S={S}")
+    reps = [synth.normal_bf16(count, 93, synth.KIND_REPLICA, 1, k, begin, phi, 1e-3) for k in range(R)]
+    want = np.full(S, 0x1234, np.uint16)
+    lo, hi = oracle.reduce_shard(ref, rank, reps, begin, want)
+    want_sq = oracle.sqnorm(want[lo - rank * S:hi - rank * S])
+    d_reps = [to_dev_u16(x) for x in reps]
+    ws = zm.reduce_workspace(count, dev())
+    assert ws.numel() > zm.zero_sqnorm_workspace_bytes()
+    outs, sqs = [], []
+    for workspace in (ws, ws, None):                       # one-pass twice, then the fixed workspace
+        out = to_dev_u16(np.full(S, 0x1234, np.uint16))
+        sq = torch.full((1,), -1.0, dtype=torch.float64, device=dev())
+        zm.zero_grad_reduce_shard(plan, rank, d_reps, begin, count, out, sqnorm_out=sq,
+                                  workspace=workspace)
+        outs.append(out)
+        sqs.append(sq)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u16(outs[0]), want, "reduced shard")
+    for sq in sqs:
+        assert abs(sq.item() - want_sq) <= 1e-12 * want_sq, (sq.item(), want_sq)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    assert sqs[0].item() == sqs[1].item()                # repeatable
+
+
 @pytest.mark.parametrize("n_ranks,t", [(3, 400), (8, 400), (9, 300), (64, 150), (97, 150)])
 def test_shard0_flatten_many_tensors_misaligned(zm, n_ranks, t):
     """Shard(0) flatten over more tensors than one launch carries, from

@@ -61,6 +61,7 @@ _reduce = _fn("zero_grad_reduce_shard", c_i32,
               [c_vp, c_i32, ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp])
 _sqnorm = _fn("zero_grad_sqnorm", c_i32, [c_vp, c_i64, c_vp, c_vp, c_sz, c_vp])
 _ws_bytes = _fn("zero_sqnorm_workspace_bytes", c_sz, [])
+_rws_bytes = _fn("zero_reduce_workspace_bytes", c_sz, [c_i64])
 _clip = _fn("zero_clip_scale", c_i32, [c_vp, c_i32, c_dbl, c_vp, c_vp])
 _adamw = _fn("zero_shard_adamw_step", c_i32,
              [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl, c_vp,
@@ -276,6 +277,18 @@ def sqnorm_workspace(device) -> "object":
 
 def zero_sqnorm_workspace_bytes() -> int:
     return _ws_bytes()
+
+
+def zero_reduce_workspace_bytes(count: int) -> int:
+    return int(_rws_bytes(int(count)))
+
+
+def reduce_workspace(count: int, device) -> "object":
+    """A new device workspace of zero_reduce_workspace_bytes(count) bytes: with it,
+    zero_grad_reduce_shard takes its one-pass kernel, with the norm, on windows
+    of up to count elements."""
+    import torch
+    return torch.empty(zero_reduce_workspace_bytes(count), dtype=torch.uint8, device=torch.device(device))
 
 
 def zero_grad_reduce_shard(plan: Plan, rank: int, replicas: Sequence, begin: int, count: int,
