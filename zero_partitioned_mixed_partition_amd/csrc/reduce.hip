@@ -239,60 +239,73 @@ __global__ __launch_bounds__(kThreads) void reduce_scalar(ReplicaTable reps, int
     if (kNorm) store_partial(sq, partials);
 }
 
-// One-pass form for large windows of at most kReplicaBatch replicas: each
-// lane reduces one 32-bit pair of
-// elements (one access per replica) and the grid covers the window once, so
+// One-pass form for large windows: each lane reduces W 32-bit words (2W
+// elements), one access per replica, and the grid covers the window once, so
 // workgroups retire in dispatch order and the chip works on a narrow sliding
 // window of every replica. Measured on MI355X with 8 replicas over the 1.3 B
-// GPT's 164 M-element shards: 3.79 ms against 4.11 ms for the grid-stride
-// kernel over all 8 ranks; below 2^24 elements the grid-stride kernel is
-// faster (the GPT-2 shard: 48.7 against 51.1-51.8 us). Same
+// GPT's 164 M-element shards (W = 1): 3.79 ms against 4.11 ms for the
+// grid-stride kernel over all 8 ranks; below 2^24 elements the grid-stride
+// kernel is faster (the GPT-2 shard: 48.7 against 51.1-51.8 us). Same
 // per-element arithmetic as reduce_vec (replica order, one division, one
-// rounding), so the same bits. Lane i = pair0 + blockIdx.x * kThreads +
-// threadIdx.x reduces window elements 2i and 2i + 1; an odd last element is
-// reduced alone. The workgroup's squared-norm partial goes to
+// rounding), so the same bits. Lane i = lane0 + blockIdx.x * kThreads +
+// threadIdx.x reduces window elements [2W i, 2W i + 2W); a ragged end is
+// reduced element by element. The workgroup's squared-norm partial goes to
 // partials[blockIdx.x].
-template <bool kNorm>
+template <bool kNorm, int W>
 __global__ __launch_bounds__(kThreads) void reduce_pass(ReplicaTable reps, int n_rep,
                                                         int64_t src_off,
                                                         uint16_t* __restrict__ out, int64_t n,
-                                                        int64_t pair0,
+                                                        int64_t lane0,
                                                         double* __restrict__ partials) {
+    typedef typename Bits<2 * W>::T V;
+    constexpr int64_t E = 2 * W;
     const float r = static_cast<float>(n_rep);
-    const int64_t i = pair0 + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t i = lane0 + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     double sq = 0.0;
-    if (2 * i + 1 < n) {
-        float a0 = 0.0f, a1 = 0.0f;
+    if (E * i + E <= n) {
+        float acc[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc[j] = 0.0f;
         for (int k0 = 0; k0 < n_rep; k0 += kReplicaBatch) {
-            uint32_t x[kReplicaBatch];
+            V x[kReplicaBatch];
             const int kn = n_rep - k0 < kReplicaBatch ? n_rep - k0 : kReplicaBatch;
 #pragma unroll
             for (int k = 0; k < kReplicaBatch; ++k)
                 if (k < kn)
-                    x[k] = zero::dev::ld_stream(reinterpret_cast<const uint32_t*>(reps.p[k0 + k] + src_off) + i);
+                    x[k] = zero::dev::ld_stream(reinterpret_cast<const V*>(reps.p[k0 + k] + src_off) + i);
 #pragma unroll
             for (int k = 0; k < kReplicaBatch; ++k) {
                 if (k < kn) {
-                    a0 = a0 + zero::dev::lo_bf16(x[k]);
-                    a1 = a1 + zero::dev::hi_bf16(x[k]);
+#pragma unroll
+                    for (int j = 0; j < W; ++j) {
+                        const uint32_t w = word(x[k], j);
+                        acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(w);
+                        acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(w);
+                    }
                 }
             }
         }
-        const uint32_t o = zero::dev::pack_bf16(a0 / r, a1 / r);
-        zero::dev::st_stream(reinterpret_cast<uint32_t*>(out) + i, o);
-        if (kNorm) {
-            const double a = static_cast<double>(zero::dev::lo_bf16(o));
-            const double b = static_cast<double>(zero::dev::hi_bf16(o));
-            sq += a * a;
-            sq += b * b;
+        V o;
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            const uint32_t ow = zero::dev::pack_bf16(acc[2 * j] / r, acc[2 * j + 1] / r);
+            set_word(o, j, ow);
+            if (kNorm) {
+                const double a = static_cast<double>(zero::dev::lo_bf16(ow));
+                const double b = static_cast<double>(zero::dev::hi_bf16(ow));
+                sq += a * a;
+                sq += b * b;
+            }
         }
-    } else if (2 * i < n) {                         // odd window: the last element alone
-        const int64_t e = 2 * i;
-        float acc = 0.0f;
-        for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(reps.p[k][src_off + e]);
-        const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
-        out[e] = h;
-        if (kNorm) sq += sq1(h);
+        zero::dev::st_stream(reinterpret_cast<V*>(out) + i, o);
+    } else {                                          // ragged end: element by element
+        for (int64_t e = E * i; e < n; ++e) {
+            float acc = 0.0f;
+            for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(reps.p[k][src_off + e]);
+            const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
+            out[e] = h;
+            if (kNorm) sq += sq1(h);
+        }
     }
     if (kNorm) store_partial(sq, partials);
 }
@@ -407,14 +420,24 @@ int grid_for(int64_t work_items, int cap) {
     return static_cast<int>(blocks);
 }
 
-// Workgroups of the one-pass reduce over n elements (one lane per pair).
-int64_t pass_blocks(int64_t n) { return ((n + 1) / 2 + kThreads - 1) / kThreads; }
+// Workgroups of the one-pass reduce over n elements, W words (2W elements) per lane.
+int64_t pass_blocks(int64_t n, int w) {
+    const int64_t lanes = (n + 2 * w - 1) / (2 * w);
+    return (lanes + kThreads - 1) / kThreads;
+}
 
-// Its partials, then the first-level sums of finish_chunks (doubles).
+// Its partials, then the first-level sums of finish_chunks (doubles); W = 1
+// has the most.
 int64_t pass_partials(int64_t n) {
-    const int64_t b = pass_blocks(n);
+    const int64_t b = pass_blocks(n, 1);
     return b + (b + kFinishChunk - 1) / kFinishChunk;
 }
+
+// Words per lane of the one-pass kernel for windows of more than one load
+// batch of replicas; 0 keeps those on the grid-stride kernels.
+#ifndef ZERO_REDUCE_PASS_WIDE_WORDS
+#define ZERO_REDUCE_PASS_WIDE_WORDS 0
+#endif
 
 }  // namespace
 
@@ -476,22 +499,36 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
     // round trip per batch of 4-byte loads, and the grid-stride kernel's
     // 16-byte loads measured faster: 64 replicas over 25 M elements, 2.66 ms
     // against 2.72 ms per 125 M-element shard.)
-    bool pass = n >= kOnePassFrom && n_replicas <= kReplicaBatch && aligned(out, 4) &&
+    const int pw = n_replicas <= kReplicaBatch ? 1 : ZERO_REDUCE_PASS_WIDE_WORDS;
+    bool pass = pw > 0 && n >= kOnePassFrom && aligned(out, 4 * pw) &&
                 (!norm || workspace_bytes >= static_cast<size_t>(pass_partials(n)) * sizeof(double));
-    for (int32_t k = 0; k < n_replicas && pass; ++k) pass = aligned(replicas[k] + src_off, 4);
+    for (int32_t k = 0; k < n_replicas && pass; ++k) pass = aligned(replicas[k] + src_off, 4 * pw);
     if (pass) {
         constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
-        const int64_t blocks = pass_blocks(n);
+        const int64_t blocks = pass_blocks(n, pw);
         for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks) {
             const int64_t nb = blocks - b0 < kMaxBlocks ? blocks - b0 : kMaxBlocks;
-            if (norm)
-                hipLaunchKernelGGL(reduce_pass<true>, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0,
-                                   stream, table, n_replicas, src_off, out, n, b0 * kThreads,
-                                   partials + b0);
+            const dim3 grid(static_cast<unsigned>(nb));
+            const int64_t lane0 = b0 * kThreads;
+            double* const part = norm ? partials + b0 : partials;
+            if (norm && pw == 1)
+                hipLaunchKernelGGL((reduce_pass<true, 1>), grid, dim3(kThreads), 0, stream, table,
+                                   n_replicas, src_off, out, n, lane0, part);
+            else if (norm && pw == 2)
+                hipLaunchKernelGGL((reduce_pass<true, 2>), grid, dim3(kThreads), 0, stream, table,
+                                   n_replicas, src_off, out, n, lane0, part);
+            else if (norm)
+                hipLaunchKernelGGL((reduce_pass<true, 4>), grid, dim3(kThreads), 0, stream, table,
+                                   n_replicas, src_off, out, n, lane0, part);
+            else if (pw == 1)
+                hipLaunchKernelGGL((reduce_pass<false, 1>), grid, dim3(kThreads), 0, stream, table,
+                                   n_replicas, src_off, out, n, lane0, part);
+            else if (pw == 2)
+                hipLaunchKernelGGL((reduce_pass<false, 2>), grid, dim3(kThreads), 0, stream, table,
+                                   n_replicas, src_off, out, n, lane0, part);
             else
-                hipLaunchKernelGGL(reduce_pass<false>, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0,
-                                   stream, table, n_replicas, src_off, out, n, b0 * kThreads,
-                                   partials);
+                hipLaunchKernelGGL((reduce_pass<false, 4>), grid, dim3(kThreads), 0, stream, table,
+                                   n_replicas, src_off, out, n, lane0, part);
             zero_status st = zero::check_hip(hipGetLastError(), "zero_grad_reduce_shard launch");
             if (st != ZERO_OK) return st;
         }
