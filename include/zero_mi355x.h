@@ -210,7 +210,10 @@ zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
  * reduction levels, no floating-point atomics: the result is reproducible on
  * a given device. The norm clip is not on the cited pages; the global norm it
  * needs is the sum of these partials over every rank. workspace as for
- * zero_grad_reduce_shard.
+ * zero_grad_reduce_shard; with zero_reduce_workspace_bytes(n) bytes or more, a
+ * 16-byte-aligned input of 2^24 elements or more takes a one-pass kernel (a
+ * partial per 16,384 elements, two-level final sum; the fp64 grouping differs,
+ * so the last bits may too).
  * Errors: ZERO_EINVAL (null pointers with n > 0, n < 0, workspace not 8-byte
  * aligned); ZERO_ENOSPACE; ZERO_EHIP. */
 zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double* sqnorm_out,
@@ -220,9 +223,10 @@ zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double* sqnorm_out
  * fixed bound, independent of n and of the device. */
 size_t zero_sqnorm_workspace_bytes(void);
 
-/* Workspace bytes with which zero_grad_reduce_shard can take its one-pass
- * kernel (with the norm) on windows of up to count elements: about 8 bytes per
- * 512 elements, never less than zero_sqnorm_workspace_bytes(). Host only. */
+/* Workspace bytes with which zero_grad_reduce_shard (with the norm) and
+ * zero_grad_sqnorm can take their one-pass kernels on up to count elements:
+ * about 8 bytes per 512 elements, never less than zero_sqnorm_workspace_bytes().
+ * Host only. */
 size_t zero_reduce_workspace_bytes(int64_t count);
 
 /* ------------------------------------------------------------------ clip coefficient

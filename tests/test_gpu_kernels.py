@@ -623,6 +623,30 @@ def test_reduce_one_pass(zm, case):
     assert sqs[0].item() == sqs[1].item()                # repeatable
 
 
+@pytest.mark.parametrize("off", [0, 1])
+def test_sqnorm_one_pass(zm, off):
+    """2^24 elements and more, 16-byte aligned, with a workspace of
+    zero_reduce_workspace_bytes: the one-pass squared norm (a ragged tail of
+    n % 8 values) against the oracle's exact sum, repeatable bit for bit; the
+    grid-stride kernel (fixed workspace) agrees within the same bound. A start
+    2 bytes off alignment (off = 1) takes the scalar kernel."""
+    n = (1 << 24) + 4099
+    note(f"one-pass sqnorm n={n} offset={off}")
+    g = synth.normal_bf16(n, 94, synth.KIND_GRAD, 1, 0, 0, None, 1e-3)
+    want = oracle.sqnorm(g)
+    buf = to_dev_u16(np.concatenate([np.zeros(off, np.uint16), g]))[off:]
+    ws = zm.reduce_workspace(n, dev())
+    got = []
+    for workspace in (ws, ws, None):
+        sq = torch.full((1,), -1.0, dtype=torch.float64, device=dev())
+        zm.zero_grad_sqnorm(buf, sq, workspace=workspace)
+        got.append(sq)
+    torch.cuda.synchronize()
+    for sq in got:
+        assert abs(sq.item() - want) <= 1e-12 * want, (sq.item(), want)
+    assert got[0].item() == got[1].item()
+
+
 @pytest.mark.parametrize("n_ranks,t", [(3, 400), (8, 400), (9, 300), (64, 150), (97, 150)])
 def test_shard0_flatten_many_tensors_misaligned(zm, n_ranks, t):
     """Shard(0) flatten over more tensors than one launch carries, from

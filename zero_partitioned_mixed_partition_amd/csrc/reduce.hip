@@ -247,64 +247,76 @@ __global__ __launch_bounds__(kThreads) void reduce_scalar(ReplicaTable reps, int
 // grid-stride kernel over all 8 ranks; below 2^24 elements the grid-stride
 // kernel is faster (the GPT-2 shard: 48.7 against 51.1-51.8 us). Same
 // per-element arithmetic as reduce_vec (replica order, one division, one
-// rounding), so the same bits. Lane i = lane0 + blockIdx.x * kThreads +
-// threadIdx.x reduces window elements [2W i, 2W i + 2W); a ragged end is
-// reduced element by element. The workgroup's squared-norm partial goes to
-// partials[blockIdx.x].
+// rounding), so the same bits. Workgroup b = block0 + blockIdx.x reduces
+// units [b * kThreads * kPassQ, (b + 1) * kThreads * kPassQ) of 2W elements,
+// each lane kPassQ units kThreads apart (one contiguous run per workgroup); a
+// ragged end is reduced element by element. The workgroup's squared-norm
+// partial goes to partials[blockIdx.x].
+// Units per lane, kThreads units apart. Measured on the 1.3 B GPT's shards
+// (8 replicas): 1 unit 3.70 ms over all 8 ranks, 2 units 3.81, 4 units 4.02.
+#ifndef ZERO_REDUCE_PASS_Q
+#define ZERO_REDUCE_PASS_Q 1
+#endif
+constexpr int kPassQ = ZERO_REDUCE_PASS_Q;
+
 template <bool kNorm, int W>
 __global__ __launch_bounds__(kThreads) void reduce_pass(ReplicaTable reps, int n_rep,
                                                         int64_t src_off,
                                                         uint16_t* __restrict__ out, int64_t n,
-                                                        int64_t lane0,
+                                                        int64_t block0,
                                                         double* __restrict__ partials) {
     typedef typename Bits<2 * W>::T V;
     constexpr int64_t E = 2 * W;
     const float r = static_cast<float>(n_rep);
-    const int64_t i = lane0 + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t base = (block0 + static_cast<int64_t>(blockIdx.x)) * kThreads * kPassQ;
     double sq = 0.0;
-    if (E * i + E <= n) {
-        float acc[E];
 #pragma unroll
-        for (int j = 0; j < E; ++j) acc[j] = 0.0f;
-        for (int k0 = 0; k0 < n_rep; k0 += kReplicaBatch) {
-            V x[kReplicaBatch];
-            const int kn = n_rep - k0 < kReplicaBatch ? n_rep - k0 : kReplicaBatch;
+    for (int q = 0; q < kPassQ; ++q) {
+        const int64_t i = base + int64_t(q) * kThreads + threadIdx.x;
+        if (E * i + E <= n) {
+            float acc[E];
 #pragma unroll
-            for (int k = 0; k < kReplicaBatch; ++k)
-                if (k < kn)
-                    x[k] = zero::dev::ld_stream(reinterpret_cast<const V*>(reps.p[k0 + k] + src_off) + i);
+            for (int j = 0; j < E; ++j) acc[j] = 0.0f;
+            for (int k0 = 0; k0 < n_rep; k0 += kReplicaBatch) {
+                V x[kReplicaBatch];
+                const int kn = n_rep - k0 < kReplicaBatch ? n_rep - k0 : kReplicaBatch;
 #pragma unroll
-            for (int k = 0; k < kReplicaBatch; ++k) {
-                if (k < kn) {
+                for (int k = 0; k < kReplicaBatch; ++k)
+                    if (k < kn)
+                        x[k] = zero::dev::ld_stream(reinterpret_cast<const V*>(reps.p[k0 + k] + src_off) + i);
 #pragma unroll
-                    for (int j = 0; j < W; ++j) {
-                        const uint32_t w = word(x[k], j);
-                        acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(w);
-                        acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(w);
+                for (int k = 0; k < kReplicaBatch; ++k) {
+                    if (k < kn) {
+#pragma unroll
+                        for (int j = 0; j < W; ++j) {
+                            const uint32_t w = word(x[k], j);
+                            acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(w);
+                            acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(w);
+                        }
                     }
                 }
             }
-        }
-        V o;
+            V o;
 #pragma unroll
-        for (int j = 0; j < W; ++j) {
-            const uint32_t ow = zero::dev::pack_bf16(acc[2 * j] / r, acc[2 * j + 1] / r);
-            set_word(o, j, ow);
-            if (kNorm) {
-                const double a = static_cast<double>(zero::dev::lo_bf16(ow));
-                const double b = static_cast<double>(zero::dev::hi_bf16(ow));
-                sq += a * a;
-                sq += b * b;
+            for (int j = 0; j < W; ++j) {
+                const uint32_t ow = zero::dev::pack_bf16(acc[2 * j] / r, acc[2 * j + 1] / r);
+                set_word(o, j, ow);
+                if (kNorm) {
+                    const double a = static_cast<double>(zero::dev::lo_bf16(ow));
+                    const double b = static_cast<double>(zero::dev::hi_bf16(ow));
+                    sq += a * a;
+                    sq += b * b;
+                }
             }
-        }
-        zero::dev::st_stream(reinterpret_cast<V*>(out) + i, o);
-    } else {                                          // ragged end: element by element
-        for (int64_t e = E * i; e < n; ++e) {
-            float acc = 0.0f;
-            for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(reps.p[k][src_off + e]);
-            const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
-            out[e] = h;
-            if (kNorm) sq += sq1(h);
+            zero::dev::st_stream(reinterpret_cast<V*>(out) + i, o);
+        } else {                                      // ragged end: element by element
+            for (int64_t e = E * i; e < n && e < E * i + E; ++e) {
+                float acc = 0.0f;
+                for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(reps.p[k][src_off + e]);
+                const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
+                out[e] = h;
+                if (kNorm) sq += sq1(h);
+            }
         }
     }
     if (kNorm) store_partial(sq, partials);
@@ -320,6 +332,47 @@ __global__ __launch_bounds__(kThreads) void sqnorm_vec(const uint16_t* __restric
         sq += sq8(zero::dev::ld_stream(reinterpret_cast<const u32x4*>(g) + i));
     const int64_t tail = n - groups * 8;
     if (tid < tail) sq += sq1(g[groups * 8 + tid]);
+    store_partial(sq, partials);
+}
+
+// One-pass squared norm for large inputs: each lane reads kSqPassGroups
+// groups of 8 values (16 bytes each, kThreads groups apart, so a workgroup
+// reads one contiguous run); the grid covers the input once, a partial per
+// workgroup (the reduce's one-pass reasoning: workgroups retire in dispatch
+// order, a narrow sliding window). The n % 8 tail takes the slots just past
+// the last group.
+// 16-byte groups per lane (a workgroup reads 32 KB). Measured on MI355X over
+// 2^30 values: 1 group 409-489 us, 4 groups 315-334, 8 groups 316-319 (84-85%
+// of peak), 16 groups 331; the grid-stride kernel 360-365 us (74%).
+#ifndef ZERO_SQNORM_PASS_GROUPS
+#define ZERO_SQNORM_PASS_GROUPS 8
+#endif
+constexpr int kSqPassGroups = ZERO_SQNORM_PASS_GROUPS;
+
+__global__ __launch_bounds__(kThreads) void sqnorm_pass(const uint16_t* __restrict__ g, int64_t n,
+                                                        int64_t slot0,
+                                                        double* __restrict__ partials) {
+    // Workgroup b covers slots [(slot0 + b) * kThreads * Q, ... + kThreads * Q): slot s
+    // is group s (s < n / 8) or tail element n/8*8 + (s - n/8).
+    const int64_t groups = n / 8;
+    const int64_t base = (slot0 + static_cast<int64_t>(blockIdx.x)) * kThreads * kSqPassGroups;
+    u32x4 x[kSqPassGroups];
+#pragma unroll
+    for (int q = 0; q < kSqPassGroups; ++q) {
+        const int64_t i = base + int64_t(q) * kThreads + threadIdx.x;
+        if (i < groups) x[q] = zero::dev::ld_stream(reinterpret_cast<const u32x4*>(g) + i);
+    }
+    double sq = 0.0;
+#pragma unroll
+    for (int q = 0; q < kSqPassGroups; ++q) {
+        const int64_t i = base + int64_t(q) * kThreads + threadIdx.x;
+        if (i < groups) {
+            sq += sq8(x[q]);
+        } else {
+            const int64_t e = groups * 8 + (i - groups);
+            if (e < n) sq += sq1(g[e]);
+        }
+    }
     store_partial(sq, partials);
 }
 
@@ -422,8 +475,8 @@ int grid_for(int64_t work_items, int cap) {
 
 // Workgroups of the one-pass reduce over n elements, W words (2W elements) per lane.
 int64_t pass_blocks(int64_t n, int w) {
-    const int64_t lanes = (n + 2 * w - 1) / (2 * w);
-    return (lanes + kThreads - 1) / kThreads;
+    const int64_t units = (n + 2 * w - 1) / (2 * w);
+    return (units + kThreads * kPassQ - 1) / (kThreads * kPassQ);
 }
 
 // Its partials, then the first-level sums of finish_chunks (doubles); W = 1
@@ -509,26 +562,25 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
         for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks) {
             const int64_t nb = blocks - b0 < kMaxBlocks ? blocks - b0 : kMaxBlocks;
             const dim3 grid(static_cast<unsigned>(nb));
-            const int64_t lane0 = b0 * kThreads;
             double* const part = norm ? partials + b0 : partials;
             if (norm && pw == 1)
                 hipLaunchKernelGGL((reduce_pass<true, 1>), grid, dim3(kThreads), 0, stream, table,
-                                   n_replicas, src_off, out, n, lane0, part);
+                                   n_replicas, src_off, out, n, b0, part);
             else if (norm && pw == 2)
                 hipLaunchKernelGGL((reduce_pass<true, 2>), grid, dim3(kThreads), 0, stream, table,
-                                   n_replicas, src_off, out, n, lane0, part);
+                                   n_replicas, src_off, out, n, b0, part);
             else if (norm)
                 hipLaunchKernelGGL((reduce_pass<true, 4>), grid, dim3(kThreads), 0, stream, table,
-                                   n_replicas, src_off, out, n, lane0, part);
+                                   n_replicas, src_off, out, n, b0, part);
             else if (pw == 1)
                 hipLaunchKernelGGL((reduce_pass<false, 1>), grid, dim3(kThreads), 0, stream, table,
-                                   n_replicas, src_off, out, n, lane0, part);
+                                   n_replicas, src_off, out, n, b0, part);
             else if (pw == 2)
                 hipLaunchKernelGGL((reduce_pass<false, 2>), grid, dim3(kThreads), 0, stream, table,
-                                   n_replicas, src_off, out, n, lane0, part);
+                                   n_replicas, src_off, out, n, b0, part);
             else
                 hipLaunchKernelGGL((reduce_pass<false, 4>), grid, dim3(kThreads), 0, stream, table,
-                                   n_replicas, src_off, out, n, lane0, part);
+                                   n_replicas, src_off, out, n, b0, part);
             zero_status st = zero::check_hip(hipGetLastError(), "zero_grad_reduce_shard launch");
             if (st != ZERO_OK) return st;
         }
@@ -592,6 +644,28 @@ extern "C" zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double*
         return zero::check_hip(hipGetLastError(), "zero_grad_sqnorm launch");
     }
     const bool vec = aligned16(grad);
+    // Large aligned inputs with a workspace for a partial per workgroup: one pass.
+    const int64_t lanes = n / 8 + n % 8;
+    const int64_t pblocks = (lanes + kThreads * kSqPassGroups - 1) / (kThreads * kSqPassGroups);
+    const int64_t plevel1 = (pblocks + kFinishChunk - 1) / kFinishChunk;
+    if (vec && n >= kOnePassFrom &&
+        workspace_bytes >= static_cast<size_t>(pblocks + plevel1) * sizeof(double)) {
+        constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
+        for (int64_t b0 = 0; b0 < pblocks; b0 += kMaxBlocks) {
+            const int64_t nb = pblocks - b0 < kMaxBlocks ? pblocks - b0 : kMaxBlocks;
+            hipLaunchKernelGGL(sqnorm_pass, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, stream,
+                               grad, n, b0, partials + b0);
+            zero_status st = zero::check_hip(hipGetLastError(), "zero_grad_sqnorm launch");
+            if (st != ZERO_OK) return st;
+        }
+        hipLaunchKernelGGL(finish_chunks, dim3(static_cast<unsigned>(plevel1)), dim3(kThreads), 0, stream,
+                           partials, pblocks, partials + pblocks);
+        zero_status st = zero::check_hip(hipGetLastError(), "zero_grad_sqnorm finish launch");
+        if (st != ZERO_OK) return st;
+        hipLaunchKernelGGL(finish_sum, dim3(1), dim3(kThreads), 0, stream, partials + pblocks,
+                           static_cast<int>(plevel1), sqnorm_out);
+        return zero::check_hip(hipGetLastError(), "zero_grad_sqnorm finish launch");
+    }
     const int blocks = grid_for(vec ? n / 8 : n, ZERO_SQNORM_MAX_BLOCKS);
     if (vec)
         hipLaunchKernelGGL(sqnorm_vec, dim3(blocks), dim3(kThreads), 0, stream, grad, n, partials);

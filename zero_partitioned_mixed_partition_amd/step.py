@@ -90,10 +90,8 @@ class RankStep:
         if gather:
             self.tensors = [torch.empty(max(n, 0), dtype=torch.int16, device=device)
                             for n in plan_numels(plan)]
-        # sized for the one-pass reduce of a window as large as the shard
-        self.workspace = (zb.reduce_workspace(s, device) if n_windows > 0 else
-                          torch.empty(zb.zero_sqnorm_workspace_bytes(), dtype=torch.uint8,
-                                      device=device))
+        # sized for the one-pass reduce (or squared norm) of as much as the whole shard
+        self.workspace = zb.reduce_workspace(s, device)
         self.n_windows = n_windows
         self.t = 0
         self._calls = {}
