@@ -576,7 +576,7 @@ def test_reduce_two_groups_per_pass_full_array(zm, R):
 
 
 @pytest.mark.parametrize("case", ["odd-window", "eight-replicas", "nine-replicas", "window-in-shard",
-                                  "misaligned"])
+                                  "misaligned", "no-norm"])
 def test_reduce_one_pass(zm, case):
     """Windows of 2^24 elements or more of at most 8 replicas, with a workspace
     of zero_reduce_workspace_bytes, take the one-pass kernel (a lane per element
@@ -591,6 +591,7 @@ def test_reduce_one_pass(zm, case):
         "nine-replicas": (1, 0, 9, 0, big - 1),             # grid-stride kernels
         "window-in-shard": (2, 1, 4, None, big - 3),         # 6 into rank 1's shard
         "misaligned": (1, 0, 3, 1, big),                    # odd begin: 2-byte offsets
+        "no-norm": (1, 0, 5, 0, big),                       # no squared norm: no workspace
     }[case]
     numels = [2 * big + 8] if n_ranks == 2 else [big + 8]
     ref = oracle.partition_plan(numels, n_ranks, 8)
@@ -605,6 +606,12 @@ def test_reduce_one_pass(zm, case):
     lo, hi = oracle.reduce_shard(ref, rank, reps, begin, want)
     want_sq = oracle.sqnorm(want[lo - rank * S:hi - rank * S])
     d_reps = [to_dev_u16(x) for x in reps]
+    if case == "no-norm":
+        out = to_dev_u16(np.full(S, 0x1234, np.uint16))
+        zm.zero_grad_reduce_shard(plan, rank, d_reps, begin, count, out)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_u16(out), want, "reduced shard, no norm")
+        return
     ws = zm.reduce_workspace(count, dev())
     assert ws.numel() > zm.zero_sqnorm_workspace_bytes()
     outs, sqs = [], []
