@@ -10,14 +10,19 @@
 //
 // Memory: per shard element R bf16 reads and one bf16 write, (2R + 2) bytes.
 // Each thread handles 8 elements per 16-byte access and keeps up to 8 replica
-// loads in flight before it adds them, in order, into its accumulators.
+// loads in flight before it adds them, in order, into its accumulators; the
+// grid is capped and threads stride. Large windows of at most 8 replicas,
+// given a workspace for a partial per workgroup, take a one-pass form instead
+// (a lane per element pair, the grid covering the window once); so does the
+// standalone squared norm on large inputs. Both sum the partials in two
+// fixed-order levels.
 //
 // The squared norm (not on the pages; needed by the global-norm clip) sums
 // exact fp64 squares of bf16 values: per-thread fp64 partials, a butterfly in
 // each wavefront, waves in order through LDS, one partial per workgroup in the
-// caller's workspace, then a single-workgroup pass adds the workgroup partials
-// in a fixed order. No floating-point atomics, and a grid that depends on n
-// alone: results repeat bit for bit, on any device.
+// caller's workspace, then one or two fixed-order passes add the workgroup
+// partials. No floating-point atomics, and a grid that depends only on n and on
+// which form the workspace allows: results repeat bit for bit, on any device.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void finish_sum(const double* __restrict_
 }
 
 // First level of the final sum when there are many partials (the one-pass
-// reduce): workgroup j adds partials [j * kFinishChunk, (j + 1) * kFinishChunk)
+// reduce and squared norm): workgroup j adds partials [j * kFinishChunk, (j + 1) * kFinishChunk)
 // in finish_sum's order and writes out[j]; finish_sum then adds those.
 constexpr int64_t kFinishChunk = 8 * kThreads;
 __global__ __launch_bounds__(kThreads) void finish_chunks(const double* __restrict__ partials,
