@@ -11,16 +11,21 @@
 // per-parameter Shard(0) placement, each tensor is its ranks' dim-0 chunks
 // stacked in rank order.
 //
-// Memory: 2 bytes read and 2 written per parameter. Two kernels, both with
-// their tables in the kernel arguments (no device-side table, no
-// host-to-device copy, nothing allocated), both copying kChunk elements per
-// workgroup, one access per lane (16 bytes by default) with non-temporal
-// hints when source and destination allow it, element by element otherwise:
-//   gather_kernel         one descriptor per plan segment (also the flatten);
-//   gather_tensor_kernel  one descriptor per tensor; the rank of an element is
-//                         found by arithmetic. A Shard(0) plan has about N_d
-//                         segments per tensor, so this needs N_d times fewer
-//                         descriptors, and launches, than the segment form.
+// Memory: 2 bytes read and 2 written per parameter. Three kernels, all copying
+// kChunk elements per workgroup, one access per lane (16 bytes by default)
+// when source and destination allow it, element by element otherwise:
+//   gather_kernel         one descriptor per plan segment (also the flatten),
+//                         tables in the kernel arguments;
+//   gather_tensor_kernel  one descriptor per tensor, tables in the kernel
+//                         arguments; the rank of an element is found by
+//                         arithmetic. A Shard(0) plan has about N_d segments
+//                         per tensor, so this needs N_d times fewer
+//                         descriptors, and launches, than the segment form;
+//   copy_table_kernel     for fixed buffers: every piece described once in
+//                         device memory (a copy table), with a descriptor
+//                         index per workgroup, in one launch.
+// The call forms allocate nothing and copy nothing to the device; a copy table
+// does both once, at creation.
 #include <hip/hip_runtime.h>
 
 #include <new>
