@@ -594,7 +594,8 @@ def measured_traffic(elems_per_launch: int):
 def cpu_baseline(wl, budget_s: float):
     """The oracle on the host for the same workload, bounded in time. The default
     workload times the oracle's whole rank step; the large ones time the same
-    per-element work (reduce, exact norm, clip, AdamW) on a 2^24-element slice."""
+    per-element work (the reduce where the step has one, exact norm, clip, AdamW)
+    on a 2^24-element slice."""
     import numpy as np
 
     import oracle
@@ -634,13 +635,17 @@ def cpu_baseline(wl, budget_s: float):
               "m": np.zeros(n, np.float32), "v": np.zeros(n, np.float32)}
 
         def one(t):
-            g = np.zeros(n, np.uint16)
-            oracle.reduce_shard(window, 0, reps, 0, g)
+            if R:
+                g = np.zeros(n, np.uint16)
+                oracle.reduce_shard(window, 0, reps, 0, g)
+            else:                   # gradients arrive averaged: no reduce in the step
+                g = reps[0]
             clip = oracle.clip_scale([oracle.sqnorm(g)], 1.0)
             st["p"], st["m"], st["v"], _ = oracle.adamw_step(st["p"], st["m"], st["v"], g, t,
                                                              clip=clip, **hp)
-        sample = (f"the per-element work of this workload (reduce of {max(R, 1)} replica windows, "
-                  f"exact norm, clip, AdamW) on a {n}-element slice of the shard")
+        work = f"reduce of {R} replica windows, " if R else ""
+        sample = (f"the per-element work of this workload ({work}exact norm, clip, AdamW) "
+                  f"on a {n}-element slice of the shard")
         per_step = n
     one(1)          # untimed: the first touch of fresh host pages is not oracle work
     t0 = time.perf_counter()
