@@ -2,6 +2,8 @@
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -10,6 +12,7 @@ import oracle
 import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
 @pytest.fixture(scope="module")
@@ -291,3 +294,25 @@ def test_binding_refuses_buffers_shorter_than_the_call_touches(zm):
         zm.zero_flatten_params(plan, [h(100), h(28)], h(127))
     with pytest.raises(ValueError, match="tensor 0"):
         zm.zero_flatten_params(plan, [h(99), h(28)], h(128))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None or shutil.which("g++") is None
+                    or not os.path.exists(os.path.join(ROCM, "include", "hip")),
+                    reason="needs gcc, g++ and the HIP headers")
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_header_compiles_as_c_and_cpp(tmp_path, lang):
+    """include/zero_mi355x.h is a C interface: it compiles as C99 (gcc) and as
+    C++17 (g++), and a translation unit can name every declared type."""
+    src = tmp_path / ("use.c" if lang == "c" else "use.cpp")
+    src.write_text('#include "zero_mi355x.h"\n'
+                   "int main(void) {\n"
+                   "    zero_plan* p = 0; zero_mt_table* t = 0; zero_copy_table* c = 0;\n"
+                   "    zero_segment s; zero_status st = ZERO_OK;\n"
+                   "    (void)p; (void)t; (void)c; (void)s; (void)st;\n"
+                   "    return (int)(zero_sqnorm_workspace_bytes() * 0);\n"
+                   "}\n")
+    cc, std = ("gcc", "-std=c99") if lang == "c" else ("g++", "-std=c++17")
+    r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        f"-I{os.path.join(ROOT, 'include')}", f"-isystem{os.path.join(ROCM, 'include')}",
+                        "-D__HIP_PLATFORM_AMD__", str(src)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
