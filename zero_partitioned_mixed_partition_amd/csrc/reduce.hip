@@ -496,6 +496,10 @@ int64_t pass_partials(int64_t n) {
 #ifndef ZERO_REDUCE_PASS_WIDE_WORDS
 #define ZERO_REDUCE_PASS_WIDE_WORDS 0
 #endif
+// Words per lane of the one-pass kernel for at most one load batch of replicas.
+#ifndef ZERO_REDUCE_PASS_WORDS
+#define ZERO_REDUCE_PASS_WORDS 1
+#endif
 
 }  // namespace
 
@@ -557,7 +561,7 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
     // round trip per batch of 4-byte loads, and the grid-stride kernel's
     // 16-byte loads measured faster: 64 replicas over 25 M elements, 2.66 ms
     // against 2.72 ms per 125 M-element shard.)
-    const int pw = n_replicas <= kReplicaBatch ? 1 : ZERO_REDUCE_PASS_WIDE_WORDS;
+    const int pw = n_replicas <= kReplicaBatch ? ZERO_REDUCE_PASS_WORDS : ZERO_REDUCE_PASS_WIDE_WORDS;
     bool pass = pw > 0 && n >= kOnePassFrom && aligned(out, 4 * pw) &&
                 (!norm || workspace_bytes >= static_cast<size_t>(pass_partials(n)) * sizeof(double));
     for (int32_t k = 0; k < n_replicas && pass; ++k) pass = aligned(replicas[k] + src_off, 4 * pw);
