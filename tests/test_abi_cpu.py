@@ -294,6 +294,21 @@ def test_binding_refuses_buffers_shorter_than_the_call_touches(zm):
         zm.zero_flatten_params(plan, [h(100), h(28)], h(127))
     with pytest.raises(ValueError, match="tensor 0"):
         zm.zero_flatten_params(plan, [h(99), h(28)], h(128))
+    # the device tables check the same way before anything is created
+    with pytest.raises(ValueError, match="tensor 1"):
+        zm.CopyTable.gather(plan, [h(64), h(64)], [h(100), h(27)])
+    with pytest.raises(ValueError, match="need N_d shards"):
+        zm.CopyTable.gather(plan, [h(64)], [h(100), h(28)])
+    with pytest.raises(ValueError, match="flat"):
+        zm.CopyTable.flatten(plan, [h(100), h(28)], h(127))
+    with pytest.raises(ValueError, match="device tensor"):  # host tensors are refused
+        zm.CopyTable.gather(plan, [h(64), h(64)], [h(100), h(28)])
+    with pytest.raises(ValueError, match="same length"):
+        zm.MultiTensorTable([f(4)], [f(4)], [f(4)], [h(4)], [])
+    with pytest.raises(ValueError, match="fewer elements"):
+        zm.MultiTensorTable([f(4)], [f(4)], [f(3)], [h(4)], [h(4)])
+    with pytest.raises(ValueError, match="device tensor"):
+        zm.MultiTensorTable([f(4)], [f(4)], [f(4)], [h(4)], [h(4)])
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None or shutil.which("g++") is None
