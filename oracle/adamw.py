@@ -27,7 +27,6 @@ A non-finite clip coefficient skips the update: state and param untouched.
 """
 import math
 from dataclasses import dataclass
-from typing import Optional
 
 import numpy as np
 
@@ -83,12 +82,3 @@ def adamw_step(master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
     p = p - c.step_size * (m / denom)
     return p, m, v, f32_to_bf16(p)
 
-
-def adamw_apply(state: dict, grad_bits: np.ndarray, step: int, hp: dict,
-                clip: float = 1.0, param_out: Optional[np.ndarray] = None) -> None:
-    """In-place convenience wrapper over adamw_step for dict-held shard state."""
-    p, m, v, bits = adamw_step(state["master"], state["exp_avg"], state["exp_avg_sq"],
-                               grad_bits, step, clip=clip, **hp)
-    state["master"], state["exp_avg"], state["exp_avg_sq"] = p, m, v
-    if bits is not None and param_out is not None:
-        param_out[:] = bits

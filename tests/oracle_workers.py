@@ -59,3 +59,59 @@ def _reduce_window(args):
 def reduce_windows(tasks, workers=None):
     with _pool(workers) as ex:
         return list(ex.map(_reduce_window, tasks, chunksize=1))
+
+
+def digest(a) -> str:
+    """128-bit digest of an array's bytes: two arrays agree bit for bit exactly
+    when their digests do (up to a 2^-128 collision)."""
+    import numpy as np
+    import xxhash
+    return xxhash.xxh3_128_hexdigest(np.ascontiguousarray(a).view(np.uint8))
+
+
+def _adamw_steps_digests(args):
+    """The oracle's AdamW over one window of a shard for steps 1..T, with the
+    generated gradient of each step and the given clip coefficients; returns,
+    per step, the digests of (master, exp_avg, exp_avg_sq, param bits)."""
+    import numpy as np
+    import oracle
+    import synth
+    seed, g0, n, phi, scales, hp = args
+    p = synth.normal_f32(n, seed, synth.KIND_MASTER, 0, 0, g0, phi, synth.MASTER_SIGMA)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    out = []
+    for t, clip in enumerate(scales, start=1):
+        g = synth.normal_bf16(n, seed, synth.KIND_GRAD, t, 0, g0, phi, synth.GRAD_SIGMA)
+        p, m, v, bits = oracle.adamw_step(p, m, v, g, t, clip=clip, **hp)
+        out.append((digest(p), digest(m), digest(v), digest(bits)))
+    return out
+
+
+def adamw_steps_digests(tasks, workers=None):
+    with _pool(workers) as ex:
+        return list(ex.map(_adamw_steps_digests, tasks, chunksize=1))
+
+
+def _reduce_adamw_digests(args):
+    """One step of a window of a rank's shard, from R generated replicas: the
+    oracle's reduce, then AdamW step 1 from master ~ N(0, 0.02) and zero moments.
+    Returns the digests of (grad bits, master, exp_avg, exp_avg_sq, param bits)
+    and the exact squared-norm state of the reduced gradient."""
+    import numpy as np
+    import oracle
+    import synth
+    numels, n_ranks, align, rank, seed, n_rep, w0, w1, hp = args
+    bits, acc = _reduce_window((numels, n_ranks, align, rank, seed, synth.KIND_REPLICA, 1, n_rep,
+                                w0, w1, synth.GRAD_SIGMA))
+    phi = sum(numels)
+    p0 = synth.normal_f32(w1 - w0, seed, synth.KIND_MASTER, 0, 0, w0, phi, synth.MASTER_SIGMA)
+    z = np.zeros(w1 - w0, np.float32)
+    P1, M1, V1, B1 = oracle.adamw_step(p0, z, z, bits, 1, **hp)
+    return (digest(bits), digest(P1), digest(M1), digest(V1), digest(B1)), acc
+
+
+def reduce_adamw_digests(tasks, workers=None):
+    with _pool(workers) as ex:
+        for r in ex.map(_reduce_adamw_digests, tasks, chunksize=1):
+            yield r

@@ -92,6 +92,58 @@ def test_adamw_special_values(zm):
     assert_bf16_close(host_u16(dout), B, "param")
 
 
+def _bf16_rounding_cases() -> np.ndarray:
+    """Every bf16 high half (2^16 patterns: both signs, zeros, subnormals,
+    normals, infinities, NaNs) under the low halves that decide the rounding:
+    exact (0), just above zero (1), below, at and above the tie (0x3FFF, 0x7FFF,
+    0x8000, 0x8001, 0xBFFF) and the largest (0xFFFF); then 4,096 NaNs with
+    random payloads of both signs."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0, 1, 0x3FFF, 0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xFFFF], np.uint32)
+    grid = (hi[:, None] | lows[None, :]).ravel()
+    rng = np.random.default_rng(5)
+    payload = rng.integers(1, 1 << 23, size=4096, dtype=np.uint32)
+    sign = rng.integers(0, 2, size=4096, dtype=np.uint32) << np.uint32(31)
+    nans = sign | np.uint32(0x7F800000) | payload
+    return np.concatenate([grid, nans]).view(np.float32)
+
+
+@pytest.mark.parametrize("entry", ["flat", "list", "table"])
+def test_adamw_bf16_emit_every_rounding_case(zm, entry):
+    """The kernels emit bf16 parameters with gfx950's packed convert. With lr = 0
+    and m = v = g = 0 the update leaves the master as it is (p * 1 - 0 * 0), so the
+    emitted parameter is the master rounded to bf16: compared bit for bit with the
+    oracle's integer round-to-nearest-even (NaN quieted, payload's top bits and
+    sign kept) on every rounding case, through each AdamW entry point. [ZF]
+    "Static Memory Allocation" (16-bit parameters from fp32 masters)."""
+    x = _bf16_rounding_cases()
+    n = x.size
+    note(f"bf16 emit ({entry}): {n} patterns")
+    hp = dict(HP, lr=0.0)
+    zeros = np.zeros(n, np.float32)
+    P, M, V, B = oracle.adamw_step(x, zeros, zeros, np.zeros(n, np.uint16), 1, **hp)
+    assert_bits_equal(B, oracle.f32_to_bf16(x), "oracle: lr = 0 emits the rounded master")
+    dp, dm, dv = to_dev_f32(x), to_dev_f32(zeros), to_dev_f32(zeros)
+    dg = torch.zeros(n, dtype=torch.int16, device=dev())
+    dout = torch.full((n,), 0x5555, dtype=torch.int16, device=dev())
+    if entry == "flat":
+        zm.zero_shard_adamw_step(dp, dm, dv, dg, dout, 1, **hp)
+    else:
+        cuts = [0, 1, 8, 100_003, 263_000, n]          # ragged tensors, tails inside waves
+        sl = [slice(a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+        lists = ([dp[s] for s in sl], [dm[s] for s in sl], [dv[s] for s in sl], [dg[s] for s in sl],
+                 [dout[s] for s in sl])
+        if entry == "list":
+            zm.zero_multi_tensor_adamw_step(*lists, 1, **hp)
+        else:
+            zm.MultiTensorTable(*lists).step(1, **hp)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u16(dout), B, f"param bf16 ({entry})")
+    assert_f32_close(host_f32(dp), P, f"master ({entry})")
+    assert_bits_equal(host_f32(dm).view(np.uint32), M.view(np.uint32), f"exp_avg ({entry})")
+    assert_bits_equal(host_f32(dv).view(np.uint32), V.view(np.uint32), f"exp_avg_sq ({entry})")
+
+
 def test_adamw_nonfinite_scale_skips_and_lr0_keeps(zm):
     n = 3000
     p, m, v, g = _adamw_inputs(n, 9)

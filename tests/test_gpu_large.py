@@ -7,9 +7,9 @@ llama3-8b   Llama-3-8B tensor list, N_d = 64, rank 63 (125,472,896 elements):
             arrays against the oracle (the oracle reduces the shard in chunks
             across a process pool).
 gpt-1.3b    1.3B GPT list, N_d = 8: 8 replicas reduced for every rank, AdamW on
-            every shard, gather to 292 tensors. Sampled windows against the
-            oracle (every rank boundary and every tensor start), exact norm
-            partials for two ranks, and a full-size gather of synthetic shards.
+            every shard, gather to 292 tensors. Full arrays against the oracle
+            (per-window digests from a process pool), exact norm partials of
+            every rank, and a full-size gather of synthetic shards.
 llama3-70b  Llama-3-70B list, N_d = 8, rank 7 (8,819,213,312 elements, indices
             past 2^33): 5 steps as the benchmark runs them (every rank's norm
             partial and the clip-1.0 coefficient on the device, then AdamW);
@@ -136,7 +136,11 @@ def _windows_in_shards(points, half, S, n_ranks, total):
 
 
 def test_gpt_1p3b_all_ranks_reduce_adamw_gather(zm):
-    from oracle_workers import _reduce_window, reduce_windows
+    """Full arrays: every rank's reduced gradient, fp32 state and bf16 parameters
+    against the oracle, bit for bit (the oracle runs 2^23-element windows across
+    a process pool and returns digests of each array), every rank's exact
+    squared-norm partial, and the gathered tensors against the parameters."""
+    from oracle_workers import digest, reduce_adamw_digests
     w = synth.WORKLOADS["gpt-1.3b"]
     R = w.replicas
     ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
@@ -167,43 +171,27 @@ def test_gpt_1p3b_all_ranks_reduce_adamw_gather(zm):
     del reps
     _free_gpu()
 
-    points = list(ref.offsets) + [r * S for r in range(w.n_ranks + 1)]
-    wins = _windows_in_shards(points, 256, S, w.n_ranks, phi)
-    note(f"gpt-1.3b: {len(wins)} oracle windows, {sum(b - a for a, b in wins)} elements")
-    flat_param = {}
-    for a, b in wins:
-        r = a // S
-        bits, _ = _reduce_window((w.numels, w.n_ranks, w.align, r, w.seed, synth.KIND_REPLICA, 1, R,
-                                  a, b, synth.GRAD_SIGMA))
-        p0 = synth.normal_f32(b - a, w.seed, synth.KIND_MASTER, 0, 0, a, phi, synth.MASTER_SIGMA)
-        z = np.zeros(b - a, np.float32)
-        P1, M1, V1, B1 = oracle.adamw_step(p0, z, z, bits, 1, **HP)
-        assert_bits_equal(host_u16(grad[a:b]), bits, f"grad [{a},{b})")
-        assert_f32_close(host_f32(master[a:b]), P1, f"master [{a},{b})")
-        assert_f32_close(host_f32(m[a:b]), M1, f"exp_avg [{a},{b})")
-        assert_f32_close(host_f32(v[a:b]), V1, f"exp_avg_sq [{a},{b})")
-        assert_bf16_close(host_u16(param[a:b]), B1, f"param [{a},{b})")
-        flat_param[(a, b)] = B1
-    # gathered tensors at every start and end, against the oracle's parameters
+    # the gather: every tensor is its slice of the flat parameter buffer
     for t, (off, n) in enumerate(zip(ref.offsets, w.numels)):
-        for lo_t in (0, max(0, n - 256)):
-            hi_t = min(n, lo_t + 256)
-            g0, g1 = off + lo_t, off + hi_t
-            want = np.concatenate([bits[max(a, g0) - a:min(b, g1) - a]
-                                   for (a, b), bits in flat_param.items() if a < g1 and b > g0])
-            assert_bf16_close(host_u16(tensors[t][lo_t:hi_t]), want, f"tensor {t} [{lo_t},{hi_t})")
-    # exact squared-norm partials of the first and the last rank
-    note("gpt-1.3b: oracle norm partials of ranks 0 and 7 (process pool)")
+        assert torch.equal(tensors[t], param[off:off + n]), f"gathered tensor {t}"
     chunk = 1 << 23
-    for r in (0, w.n_ranks - 1):
-        res = reduce_windows([(w.numels, w.n_ranks, w.align, r, w.seed, synth.KIND_REPLICA, 1, R,
-                               a, min(a + chunk, (r + 1) * S), synth.GRAD_SIGMA)
-                              for a in range(r * S, (r + 1) * S, chunk)])
-        acc = oracle.SqnormAccumulator()
-        for _, a in res:
-            acc.merge(a)
-        got = float(parts[r].item())
-        assert abs(got - acc.value()) <= 1e-12 * acc.value(), (r, got, acc.value())
+    wins = [(a, min(a + chunk, (r + 1) * S)) for r in range(w.n_ranks)
+            for a in range(r * S, (r + 1) * S, chunk)]
+    note(f"gpt-1.3b: oracle reduce + AdamW over all {P} elements in {len(wins)} windows "
+         "(process pool), compared by digest")
+    tasks = [(w.numels, w.n_ranks, w.align, a // S, w.seed, R, a, b, HP) for a, b in wins]
+    accs = [oracle.SqnormAccumulator() for _ in range(w.n_ranks)]
+    names = ("grad", "master", "exp_avg", "exp_avg_sq", "param")
+    for (a, b), (want, acc) in zip(wins, reduce_adamw_digests(tasks, workers=16)):
+        got = (host_u16(grad[a:b]), host_f32(master[a:b]), host_f32(m[a:b]), host_f32(v[a:b]),
+               host_u16(param[a:b]))
+        for name, x, d in zip(names, got, want):
+            assert digest(x) == d, f"{name} differs from the oracle in [{a}, {b})"
+        accs[a // S].merge(acc)
+    for r in range(w.n_ranks):
+        got, want = float(parts[r].item()), accs[r].value()
+        assert abs(got - want) <= 1e-12 * want, (r, got, want)
+    note(f"gpt-1.3b: {P} elements x 5 arrays bit-identical, {w.n_ranks} norm partials within 1e-12")
     del master, m, v, grad, param, tensors
     _free_gpu()
 
@@ -382,4 +370,44 @@ def test_pieces_longer_than_2p30_flatten_and_gather(zm, kind):
             covered[a:a + ln] = True
     assert int(((flat != 0) & ~covered).sum().item()) == 0, "padding is zero"
     del tensors, back, flat, covered
+    _free_gpu()
+
+
+def test_shard0_flatten_waves_across_rank_buffers_past_2p31_bytes(zm):
+    """The Shard(0) flatten's waves that cross a rank boundary store into two
+    rank buffers S elements apart. Here S is past 2^30 elements, so those waves
+    span more than 2^31 bytes: three [524294, 2056] tensors (538,974,232-element
+    chunks, a multiple of 8 but not of a wave's 512 elements, so whole 16-byte
+    lanes sit on both sides of the boundary) and small tensors whose chunks end
+    inside waves. The whole flat buffer against oracle.flatten_params_shard0,
+    then the tensor-major gather back to the tensors. [ZF] "FSDP-2: Per-Parameter
+    Sharding via DTensor (fully_shard)"."""
+    shapes = [(2 * 262147, 2056), (3001,), (2 * 262147, 2056), (7, 4097), (2 * 262147, 2056),
+              (40001, 1234), (5,)]
+    numels = [int(np.prod(s)) for s in shapes]
+    dim0 = [s[0] for s in shapes]
+    n_ranks = 2
+    ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, 128)
+    plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, 128)
+    assert (plan.shard_numel, plan.padded_numel) == (ref.shard_numel, ref.padded_numel)
+    S, P, phi = ref.shard_numel, ref.padded_numel, ref.numel
+    assert S > 1 << 30
+    note(f"shard0 flatten past 2^31-byte waves: P={P} S={S}")
+    offs = np.concatenate([[0], np.cumsum(numels)[:-1]]).tolist()
+    host = [synth.normal_bf16(n, 96, synth.KIND_PARAM, 0, 0, off, phi, 0.02)
+            for n, off in zip(numels, offs)]
+    tensors = [torch.from_numpy(h.view(np.int16)).to(dev()) for h in host]
+    flat = torch.full((P,), 0x1111, dtype=torch.int16, device=dev())
+    zm.zero_flatten_params(plan, tensors, flat)
+    torch.cuda.synchronize()
+    note("shard0 flatten past 2^31-byte waves: comparing the flat buffer with the oracle")
+    want = oracle.flatten_params_shard0(ref, host)
+    assert_bits_equal(host_u16(flat), want, "Shard(0) flat buffer")
+    del want
+    back = [torch.full((n,), 0x2222, dtype=torch.int16, device=dev()) for n in numels]
+    zm.zero_gather_params(plan, [flat[r * S:(r + 1) * S] for r in range(n_ranks)], back)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(tensors, back)):
+        assert torch.equal(a, b), f"tensor {i} round trip"
+    del tensors, back, flat, host
     _free_gpu()

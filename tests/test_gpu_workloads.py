@@ -6,7 +6,8 @@ tiny-a / tiny-b  1M-parameter flat model, N_d = 4, every shard stepped in turn,
 gpt2-small       GPT-2-small tensor list, N_d = 8, rank 7 (15.6M elements),
                  already-averaged gradients, global-norm clip 1.0, 100 steps:
                  the oracle computes every step's global norm over all 8 ranks
-                 (124M values) and the AdamW state on sampled windows.
+                 (124M values), and the full fp32 state and bf16 parameters of
+                 every step, compared bit for bit through per-window digests.
 bench pipeline   the benchmark's own step (8 replicas reduced for rank 7, fused
                  norm, clip, AdamW, gather of 148 tensors): full arrays for 2 steps;
                  also on the Shard(0) layout and with the AdamW offloaded to the host.
@@ -74,15 +75,14 @@ def test_tiny_all_shards_ten_steps(zm, name):
     assert (host_f32(d_master)[phi:] == 0).all(), "padding must stay zero"
 
 
-def test_gpt2_small_rank7_hundred_steps_clip(zm):
-    from oracle_workers import grad_sqnorms
-    w = synth.WORKLOADS["gpt2-small"]
-    ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
-    P, S, phi, rank = ref.padded_numel, ref.shard_numel, ref.numel, 7
-    steps = w.steps
-    note(f"gpt2-small: P={P} S={S}, {steps} steps on the GPU")
-    lo = rank * S
-    d_grad = torch.empty(P, dtype=torch.int16, device=dev())
+def _gpt2_rank_steps(zm, w, S, lo, phi, steps, chunks, scales=None):
+    """Rank 7's steps on the GPU: every rank's squared norm of the generated
+    gradient, the clip coefficient, AdamW. After each step the fp32 state and
+    the bf16 parameters are copied back and digested chunk by chunk. With
+    `scales`, each step's coefficient is overwritten with the given one before
+    AdamW (the update then sees the oracle's coefficient)."""
+    from oracle_workers import digest
+    d_grad = torch.empty(w.n_ranks * S, dtype=torch.int16, device=dev())
     d_master = torch.empty(S, dtype=torch.float32, device=dev())
     synth.device_normal_f32(d_master, w.seed, synth.KIND_MASTER, 0, 0, lo, phi, synth.MASTER_SIGMA)
     d_m = torch.zeros(S, dtype=torch.float32, device=dev())
@@ -90,50 +90,67 @@ def test_gpt2_small_rank7_hundred_steps_clip(zm):
     d_param = torch.zeros(S, dtype=torch.int16, device=dev())
     d_parts = torch.zeros(w.n_ranks, dtype=torch.float64, device=dev())
     d_scale = torch.zeros(1, dtype=torch.float32, device=dev())
-    d_scales = torch.zeros(steps, dtype=torch.float32, device=dev())
-    d_parts_all = torch.zeros(steps, w.n_ranks, dtype=torch.float64, device=dev())
+    got_scales, got_parts, digests = [], [], []
     for t in range(1, steps + 1):
         synth.device_normal_bf16(d_grad, w.seed, synth.KIND_GRAD, t, 0, 0, phi, synth.GRAD_SIGMA)
         for r in range(w.n_ranks):
             zm.zero_grad_sqnorm(d_grad[r * S:(r + 1) * S], d_parts[r:r + 1])
         zm.zero_clip_scale(d_parts, w.max_norm, d_scale)
+        got_scales.append(np.float32(d_scale.item()))
+        got_parts.append(d_parts.cpu().numpy().copy())
+        if scales is not None:
+            d_scale.fill_(float(scales[t - 1]))
         zm.zero_shard_adamw_step(d_master, d_m, d_v, d_grad[lo:lo + S], d_param, t,
                                  clip_scale=d_scale, **HP)
-        d_scales[t - 1:t].copy_(d_scale)
-        d_parts_all[t - 1].copy_(d_parts)
-    torch.cuda.synchronize()
+        host = (host_f32(d_master), host_f32(d_m), host_f32(d_v), host_u16(d_param))
+        digests.append([tuple(digest(x[a:b]) for x in host) for a, b in chunks])
+    return digests, np.array(got_scales, np.float32), np.array(got_parts)
+
+
+def test_gpt2_small_rank7_hundred_steps_clip(zm):
+    """Full arrays, every step: rank 7's master, exp_avg, exp_avg_sq and bf16
+    parameters after each of the 100 steps, against the oracle's, bit for bit
+    (the oracle runs the shard in 16 windows across a process pool and returns
+    per-step digests of each array)."""
+    from oracle_workers import adamw_steps_digests, grad_sqnorms
+    w = synth.WORKLOADS["gpt2-small"]
+    ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
+    P, S, phi, rank = ref.padded_numel, ref.shard_numel, ref.numel, 7
+    steps = w.steps
+    lo = rank * S
+    cuts = [k * S // 16 for k in range(17)]
+    chunks = list(zip(cuts[:-1], cuts[1:]))
+    note(f"gpt2-small: P={P} S={S}, {steps} steps on the GPU, full-array digests every step")
+    gpu_digests, got_scales, got_parts = _gpt2_rank_steps(zm, w, S, lo, phi, steps, chunks)
 
     note("gpt2-small: oracle norms over all ranks for every step (process pool)")
     tasks = [(w.seed, synth.KIND_GRAD, t, 0, r * S, S, phi, synth.GRAD_SIGMA)
              for t in range(1, steps + 1) for r in range(w.n_ranks)]
     parts = np.array(grad_sqnorms(tasks)).reshape(steps, w.n_ranks)
-    got_parts = d_parts_all.cpu().numpy()
     assert (np.abs(got_parts - parts) <= 1e-12 * parts).all(), "per-rank norm partials"
     scales = np.array([oracle.clip_scale(list(parts[t]), w.max_norm) for t in range(steps)],
                       dtype=np.float32)
-    got_scales = d_scales.cpu().numpy()
     ulps = np.abs(got_scales.view(np.int32) - scales.view(np.int32))
     assert ulps.max() <= 1, "clip coefficients"
+    same = int((ulps == 0).sum())
     note(f"gpt2-small: clip coefficients {scales.min():.6f}..{scales.max():.6f}, "
-         f"{int((ulps == 0).sum())}/{steps} bit-identical")
+         f"{same}/{steps} bit-identical")
+    if same != steps:
+        # The update's parity is then checked with the oracle's coefficient as its input.
+        note("gpt2-small: rerunning the GPU steps with the oracle's clip coefficients")
+        gpu_digests, _, _ = _gpt2_rank_steps(zm, w, S, lo, phi, steps, chunks, scales)
 
-    rng = np.random.default_rng(0)
-    starts = [0, S // 2 - 2048, S - 4096, int(rng.integers(0, S - 4096))]
-    for w0 in starts:
-        n = 4096
-        st = {"master": synth.normal_f32(n, w.seed, synth.KIND_MASTER, 0, 0, lo + w0, phi,
-                                         synth.MASTER_SIGMA),
-              "exp_avg": np.zeros(n, np.float32), "exp_avg_sq": np.zeros(n, np.float32)}
-        bits = None
-        for t in range(1, steps + 1):
-            g = synth.normal_bf16(n, w.seed, synth.KIND_GRAD, t, 0, lo + w0, phi, synth.GRAD_SIGMA)
-            st["master"], st["exp_avg"], st["exp_avg_sq"], bits = oracle.adamw_step(
-                st["master"], st["exp_avg"], st["exp_avg_sq"], g, t, clip=scales[t - 1], **HP)
-        sl = slice(w0, w0 + n)
-        assert_f32_close(host_f32(d_master[sl]), st["master"], f"master window {w0}")
-        assert_f32_close(host_f32(d_m[sl]), st["exp_avg"], f"exp_avg window {w0}")
-        assert_f32_close(host_f32(d_v[sl]), st["exp_avg_sq"], f"exp_avg_sq window {w0}")
-        assert_bf16_close(host_u16(d_param[sl]), bits, f"param window {w0}")
+    note("gpt2-small: oracle AdamW over 16 windows for every step (process pool)")
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    want = adamw_steps_digests([(w.seed, lo + a, b - a, phi, [float(x) for x in scales], hp)
+                                for a, b in chunks])
+    names = ("master", "exp_avg", "exp_avg_sq", "param")
+    for t in range(steps):
+        for c, (a, b) in enumerate(chunks):
+            for k, name in enumerate(names):
+                assert gpu_digests[t][c][k] == want[c][t][k], \
+                    f"step {t + 1}: {name} differs from the oracle in [{a}, {b})"
+    note(f"gpt2-small: {steps} steps x {len(chunks)} windows x 4 arrays bit-identical")
 
 
 @pytest.mark.parametrize("name", ["gpt2-small", "gpt2-small-fsdp2", "gpt2-small-offload",
@@ -232,3 +249,48 @@ def test_rank_step_fresh_replica_buffers_are_not_retained(zm):
     gc.collect()
     assert len(rs._calls) == 1
     assert all(r() is None for r in held[:-1]), "earlier replica buffers are still referenced"
+
+
+def test_rank_step_skipped_step_counts_as_an_iteration(zm):
+    """A non-finite global norm (here a remote rank's partial is NaN) makes the
+    clip coefficient NaN and the AdamW kernel skip the update: master, m, v and
+    the bf16 shard stay as they were. RankStep's step counter counts issued
+    iterations, skipped ones included, so the next step's bias correction uses
+    t = 2; the oracle's rank step, run with the same inputs and step numbers,
+    must match after both steps."""
+    from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep
+    numels = [1000, 37, 4096, 3]
+    n_ranks, rank, R = 4, 1, 3
+    plan = zm.zero_partition_plan(numels, n_ranks, 128)
+    ref = oracle.partition_plan(numels, n_ranks, 128)
+    P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
+    hyper = Hyper()
+    rs = RankStep(plan, rank, 1, hyper, 1.0, dev(), gather=True)
+    master = synth.normal_f32(S, 41, synth.KIND_MASTER, 0, 0, rank * S, phi, 0.02)
+    rs.master.copy_(torch.from_numpy(master))
+    shards = [synth.normal_bf16(S, 41, synth.KIND_PARAM, 0, 0, r * S, phi, 0.02) for r in range(n_ranks)]
+    for r in range(n_ranks):
+        if r != rank:
+            rs.param_shards[r].copy_(to_dev_u16(shards[r]))
+    shards[rank] = np.zeros(S, np.uint16)
+    state = {"master": master.copy(), "exp_avg": np.zeros(S, np.float32),
+             "exp_avg_sq": np.zeros(S, np.float32)}
+    for t, remote in ((1, [0.4, 0.0, float("nan"), 0.3]), (2, [0.4, 0.0, 0.2, 0.3])):
+        reps_h = [synth.normal_bf16(P, 42, synth.KIND_REPLICA, t, k, 0, phi, 0.05) for k in range(R)]
+        rs.set_remote_partials(remote)
+        rs.step([(0, P, [to_dev_u16(x) for x in reps_h])])
+        want = oracle.rank_step(ref, rank, reps_h, 0, state, shards, remote, t, hyper.as_kwargs(), 1.0)
+        torch.cuda.synchronize()
+        assert rs.t == t
+        if t == 1:
+            assert np.isnan(want["clip"]) and np.isnan(rs.scale.item()), "the step is skipped"
+            assert_bits_equal(host_f32(rs.master).view(np.uint32), master.view(np.uint32),
+                              "skipped step: master untouched")
+            assert not host_u16(rs.param_shards[rank]).any(), "skipped step: shard untouched"
+        # (the device sums the partials in another order than the oracle, so the
+        # coefficient may differ in its last bit: the bars, not bit identity)
+        for got, key in ((rs.master, "master"), (rs.exp_avg, "exp_avg"), (rs.exp_avg_sq, "exp_avg_sq")):
+            assert_f32_close(host_f32(got), state[key], f"step {t} {key}")
+        assert_bf16_close(host_u16(rs.param_shards[rank]), shards[rank], f"step {t} shard")
+        for i, (a, b) in enumerate(zip(rs.tensors, want["tensors"])):
+            assert_bf16_close(host_u16(a), b, f"step {t} tensor {i}")

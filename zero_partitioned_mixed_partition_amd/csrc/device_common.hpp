@@ -51,12 +51,27 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) { return pack_bf16(x, x
 // 540 us at 125 M; a 16-byte-per-lane copy of 2.6 GB 786-789 us against
 // 809-812 us. Cache bits on the loads measured no difference.
 //
-// The buffer's base is the first active lane's address less 2 GiB, and each
-// lane passes its distance from that base as the 32-bit offset, so every lane
-// of a wave must store within 2 GiB of that lane's address. Every kernel here
-// stores one contiguous run per wave. The record count is the full 32-bit
-// range, so the buffer's own range check never drops a store (bounds are the
-// callers', as with a global store).
+// A buffer store addresses memory as a 64-bit base, which must be the same
+// for every lane of the wave, plus a 32-bit offset per lane. Three forms:
+//
+//   st_stream(p, v)          the base is the first active lane's address less
+//                            2 GiB, each lane's offset its distance from that
+//                            base. Contract: every active lane stores within
+//                            2 GiB of the first active lane's address. Used by
+//                            kernels whose waves store one contiguous run of at
+//                            most 64 accesses (AdamW, the reduce, the copy of
+//                            one piece, the gather into one tensor).
+//   st_stream_at(b, off, v)  the caller passes the base b, the same pointer in
+//                            every lane, and each lane's byte offset off from it
+//                            (below 2^32). For waves that store into several
+//                            buffers far apart (the Shard(0) flatten into two
+//                            ranks' buffers): one call per buffer, each with
+//                            that buffer's base.
+//   st_stream_any(p, v)      a global non-temporal store: any address.
+//
+// The record count of the buffer is the full 32-bit range, so the buffer's own
+// range check never drops a store (bounds are the callers', as with a global
+// store).
 #ifndef ZERO_NT_LOADS
 #define ZERO_NT_LOADS 1
 #endif
@@ -76,6 +91,12 @@ __device__ __forceinline__ T ld_stream(const T* p) {
 constexpr int kRawBufferWord3 = 0x00020000;   // untyped buffer, 32-bit data format
 constexpr int kThroughCpol = 0x12;            // sc1 (device scope) | nt
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t through_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, kRawBufferWord3);
+}
+
+// The first active lane's address less 2 GiB (or 0), as the wave's base; `off`
+// receives this lane's distance from it.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t through_base(const void* p, uint32_t& off) {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
@@ -83,46 +104,54 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t through_base(const void* p, ui
     const uint64_t first = (static_cast<uint64_t>(hi) << 32) | lo;
     const uint64_t base = first >= (uint64_t(1) << 31) ? first - (uint64_t(1) << 31) : 0;
     off = static_cast<uint32_t>(a - base);
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, -1, kRawBufferWord3);
+    return through_rsrc(reinterpret_cast<const void*>(base));
 }
 
-__device__ __forceinline__ void st_through(uint16_t* p, uint16_t v) {
-    uint32_t off;
-    const __amdgpu_buffer_rsrc_t r = through_base(p, off);
+__device__ __forceinline__ void through_store(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
     __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kThroughCpol);
 }
-__device__ __forceinline__ void st_through(uint32_t* p, uint32_t v) {
-    uint32_t off;
-    const __amdgpu_buffer_rsrc_t r = through_base(p, off);
+__device__ __forceinline__ void through_store(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kThroughCpol);
 }
-__device__ __forceinline__ void st_through(float* p, float v) {
-    st_through(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v));
+__device__ __forceinline__ void through_store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    through_store(r, off, __builtin_bit_cast(uint32_t, v));
 }
-__device__ __forceinline__ void st_through(u32x2* p, u32x2 v) {
-    uint32_t off;
-    const __amdgpu_buffer_rsrc_t r = through_base(p, off);
+__device__ __forceinline__ void through_store(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kThroughCpol);
 }
-__device__ __forceinline__ void st_through(u32x4* p, u32x4 v) {
-    uint32_t off;
-    const __amdgpu_buffer_rsrc_t r = through_base(p, off);
+__device__ __forceinline__ void through_store(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kThroughCpol);
 }
 template <typename T>
-__device__ __forceinline__ void st_through(T* p, const T& v) {
+__device__ __forceinline__ void through_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const T& v) {
     static_assert(sizeof(T) == 8 || sizeof(T) == 16, "8- or 16-byte vector");
     typedef typename std::conditional<sizeof(T) == 8, u32x2, u32x4>::type W;
-    st_through(reinterpret_cast<W*>(p), __builtin_bit_cast(W, v));
+    through_store(r, off, __builtin_bit_cast(W, v));
 }
 
 template <typename T>
 __device__ __forceinline__ void st_stream(T* p, const T& v) {
 #if ZERO_THROUGH_STORES
-    st_through(p, v);
+    uint32_t off;
+    const __amdgpu_buffer_rsrc_t r = through_base(p, off);
+    through_store(r, off, v);
 #else
     __builtin_nontemporal_store(v, p);
 #endif
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream_at(const void* base, uint32_t off, const T& v) {
+#if ZERO_THROUGH_STORES
+    through_store(through_rsrc(base), off, v);
+#else
+    __builtin_nontemporal_store(v, reinterpret_cast<T*>(static_cast<char*>(const_cast<void*>(base)) + off));
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream_any(T* p, const T& v) {
+    __builtin_nontemporal_store(v, p);
 }
 
 // Entry of workgroup blockIdx.x in a launch's XCD-major table index (the

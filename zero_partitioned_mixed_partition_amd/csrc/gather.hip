@@ -34,25 +34,16 @@
 
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "tensor_major.hpp"
 
 namespace {
 
-constexpr int kThreads = 256;
+using zero::copy::kChunk;
+using zero::copy::kLane;
+using zero::copy::kThreads;
+using zero::copy::kVecs;
 constexpr int kSegs = 160;                      // segments per launch (kernarg ~3.8 KB of the 4 KB limit)
 constexpr int64_t kMaxPiece = int64_t(1) << 30; // longer pieces are split: lengths fit 32 bits
-// One access per lane: ZERO_GATHER_LANE_ELEMS bf16 values (8 = 16 bytes).
-#ifndef ZERO_GATHER_LANE_ELEMS
-#define ZERO_GATHER_LANE_ELEMS 8
-#endif
-constexpr int kLane = ZERO_GATHER_LANE_ELEMS;
-// Accesses per lane: a workgroup copies kVecs passes of kRow elements, so
-// its fixed start-up work (finding its descriptor) is paid once per kChunk.
-#ifndef ZERO_GATHER_VECS
-#define ZERO_GATHER_VECS 1
-#endif
-constexpr int kVecs = ZERO_GATHER_VECS;
-constexpr int64_t kRow = int64_t(kThreads) * kLane;     // elements per pass
-constexpr int64_t kChunk = kRow * kVecs;                // elements per workgroup
 
 template <int E> struct LaneBits;
 template <> struct LaneBits<8> { typedef zero::dev::u32x4 T; };
@@ -153,11 +144,17 @@ __global__ __launch_bounds__(kThreads) void copy_table_kernel(const PieceDesc* _
 // one per segment. Element e of tensor t lies in rank r = e / chunk_t
 // (chunk_t = rows per chunk * elements per row) and is read from shards[r] +
 // off_t + (e - r*chunk_t), off_t being the chunk's start in every rank's
-// coalesced buffer. A workgroup copies kChunk elements of one tensor: it finds
-// the rank of its first element once (32-bit division: tensors here hold fewer
-// than 2^31 elements), and when chunk_t >= kChunk its lanes lie in that rank
-// or the next, two workgroup-uniform shard pointers. Smaller chunks take a
-// per-lane path.
+// coalesced buffer (the index map is in tensor_major.hpp). A workgroup copies
+// kChunk elements of one tensor: it finds the rank of its first element once,
+// and when chunk_t >= kChunk its lanes lie in that rank or the next, two
+// workgroup-uniform shard pointers. Smaller chunks take a per-lane division.
+//
+// Stores: the gather writes one tensor, so each wave's stores are one
+// contiguous run (st_stream). The flatten writes rank buffers, which lie S
+// elements apart, and one wave can span a chunk boundary: with large chunks
+// each store takes its own rank's chunk start as the buffer base (st_stream_at,
+// offsets below 2 * chunk_t < 2^32 bytes), with small chunks a lane's rank is
+// its own and the stores are global ones (st_stream_any).
 //
 // The descriptors travel in the kernel arguments (4 KB). The wide table has
 // room for 64 rank pointers and 64-bit chunk offsets (127 tensors per launch);
@@ -177,9 +174,8 @@ struct TensorBatch {
     int32_t first_block[kTens + 1];
     int32_t n;
 };
-using WideBatch = TensorBatch<64, int64_t>;
-using CompactBatch = TensorBatch<8, int32_t>;
-constexpr int kMaxRanks = WideBatch::kRanks;
+using WideBatch = TensorBatch<zero::copy::kMaxRanks, int64_t>;
+using CompactBatch = TensorBatch<zero::copy::kCompactRanks, int32_t>;
 static_assert(sizeof(WideBatch) <= 4096 && sizeof(CompactBatch) <= 4096,
               "kernel arguments are limited to 4 KB");
 static_assert(WideBatch::kTens >= 120 && CompactBatch::kTens >= 160, "table capacities");
@@ -194,6 +190,9 @@ __device__ __forceinline__ void copy_elem(uint16_t* tens, uint16_t* buf) {
 template <bool kScatter, class Batch>
 __global__ __launch_bounds__(kThreads) void gather_tensor_kernel(Batch b) {
     typedef typename LaneBits<kLane>::T V;
+    using zero::copy::LanePlace;
+    using zero::copy::lane_place;
+    using zero::copy::lane_whole;
     const int64_t blk = blockIdx.x;
     int lo = 0, hi = b.n - 1;
     while (lo < hi) {
@@ -204,39 +203,44 @@ __global__ __launch_bounds__(kThreads) void gather_tensor_kernel(Batch b) {
     const int64_t e0 = (blk - b.first_block[t]) * kChunk;        // workgroup's first element
     const int64_t numel = b.numel[t], chunk = b.chunk[t];
     const int64_t soff = b.off[t];
-    const uint32_t q0 = static_cast<uint32_t>(e0) / static_cast<uint32_t>(chunk);
-    const int r0 = __builtin_amdgcn_readfirstlane(static_cast<int>(q0));
-    const int64_t local0 = e0 - static_cast<int64_t>(r0) * chunk;
+    zero::copy::WorkgroupStart ws = zero::copy::workgroup_start(e0, chunk);
+    ws.r0 = __builtin_amdgcn_readfirstlane(ws.r0);
     uint16_t* dst = b.dst[t];
     if (chunk >= kChunk) {
-        // local < chunk + kChunk <= 2 * chunk: rank r0, or r0 + 1 past the boundary.
-        uint16_t* p0 = b.shards[r0] + soff;
-        uint16_t* p1 = (r0 + 1 < Batch::kRanks ? b.shards[r0 + 1] : b.shards[r0]) + soff;
+        // rank r0, or r0 + 1 past the boundary
+        uint16_t* p0 = b.shards[ws.r0] + soff;
+        uint16_t* p1 = (ws.r0 + 1 < Batch::kRanks ? b.shards[ws.r0 + 1] : b.shards[ws.r0]) + soff;
         V vals[kVecs];
         bool fast[kVecs];
 #pragma unroll
         for (int v = 0; v < kVecs; ++v) {            // all loads first, then all stores
             const int64_t j = (int64_t(v) * kThreads + threadIdx.x) * kLane;
-            const int64_t e = e0 + j, local = local0 + j;
-            const bool next = local >= chunk;
-            const int64_t l = next ? local - chunk : local;
-            uint16_t* buf = (next ? p1 : p0) + l;
-            fast[v] = e + kLane <= numel && l + kLane <= chunk &&
-                      ((reinterpret_cast<uintptr_t>(buf) | reinterpret_cast<uintptr_t>(dst + e)) &
-                       (2 * kLane - 1)) == 0;
+            const int64_t e = e0 + j;
+            const LanePlace pl = lane_place(ws, chunk, j, true);
+            const uint16_t* buf = (pl.rank != ws.r0 ? p1 : p0) + pl.within;
+            fast[v] = lane_whole(e, numel, pl.within, chunk, reinterpret_cast<uintptr_t>(buf),
+                                 reinterpret_cast<uintptr_t>(dst + e));
             if (fast[v]) vals[v] = zero::dev::ld_stream(reinterpret_cast<const V*>(kScatter ? dst + e : buf));
         }
 #pragma unroll
         for (int v = 0; v < kVecs; ++v) {
             const int64_t j = (int64_t(v) * kThreads + threadIdx.x) * kLane;
-            const int64_t e = e0 + j, local = local0 + j;
+            const int64_t e = e0 + j;
+            const LanePlace pl = lane_place(ws, chunk, j, true);
             if (fast[v]) {
-                const bool next = local >= chunk;
-                uint16_t* buf = (next ? p1 : p0) + (next ? local - chunk : local);
-                zero::dev::st_stream(reinterpret_cast<V*>(kScatter ? buf : dst + e), vals[v]);
+                if (kScatter) {
+                    const uint32_t off = static_cast<uint32_t>(pl.within * 2);
+                    if (pl.rank != ws.r0)
+                        zero::dev::st_stream_at(p1, off, vals[v]);
+                    else
+                        zero::dev::st_stream_at(p0, off, vals[v]);
+                } else {
+                    zero::dev::st_stream(reinterpret_cast<V*>(dst + e), vals[v]);
+                }
                 continue;
             }
             // Straddles the boundary, misaligned, or the tensor's tail.
+            const int64_t local = ws.local0 + j;
             for (int k = 0; k < kLane && e + k < numel; ++k) {
                 const int64_t lk = local + k;
                 copy_elem<kScatter>(dst + e + k, lk < chunk ? p0 + lk : p1 + (lk - chunk));
@@ -244,29 +248,28 @@ __global__ __launch_bounds__(kThreads) void gather_tensor_kernel(Batch b) {
         }
         return;
     }
-    // Small chunks: local < chunk + kChunk < 2 * kChunk, so 32-bit division,
-    // per lane; a lane's elements may lie in several ranks.
+    // Small chunks: a lane's rank by a 32-bit division; a lane's elements may
+    // lie in several ranks.
     const uint32_t c32 = static_cast<uint32_t>(chunk);
     for (int v = 0; v < kVecs; ++v) {
         const int64_t j = (int64_t(v) * kThreads + threadIdx.x) * kLane;
         const int64_t e = e0 + j;
         if (e >= numel) break;
-        const uint32_t lj = static_cast<uint32_t>(local0 + j);
-        const uint32_t qj = lj / c32;
-        const uint32_t within = lj - qj * c32;
-        uint16_t* buf = b.shards[r0 + static_cast<int>(qj)] + soff + within;
-        if (e + kLane <= numel && within + kLane <= c32 &&
-            ((reinterpret_cast<uintptr_t>(buf) | reinterpret_cast<uintptr_t>(dst + e)) & (2 * kLane - 1)) == 0) {
+        const LanePlace pl = lane_place(ws, chunk, j, false);
+        uint16_t* buf = b.shards[pl.rank] + soff + pl.within;
+        if (lane_whole(e, numel, pl.within, chunk, reinterpret_cast<uintptr_t>(buf),
+                       reinterpret_cast<uintptr_t>(dst + e))) {
             if (kScatter)
-                zero::dev::st_stream(reinterpret_cast<V*>(buf), zero::dev::ld_stream(reinterpret_cast<const V*>(dst + e)));
+                zero::dev::st_stream_any(reinterpret_cast<V*>(buf), zero::dev::ld_stream(reinterpret_cast<const V*>(dst + e)));
             else
                 zero::dev::st_stream(reinterpret_cast<V*>(dst + e), zero::dev::ld_stream(reinterpret_cast<const V*>(buf)));
             continue;
         }
+        const uint32_t lj = static_cast<uint32_t>(ws.local0 + j);
         for (int k = 0; k < kLane && e + k < numel; ++k) {
             const uint32_t lk = lj + static_cast<uint32_t>(k);
             const uint32_t qk = lk / c32;
-            copy_elem<kScatter>(dst + e + k, b.shards[r0 + static_cast<int>(qk)] + soff + (lk - qk * c32));
+            copy_elem<kScatter>(dst + e + k, b.shards[ws.r0 + static_cast<int>(qk)] + soff + (lk - qk * c32));
         }
     }
 }
@@ -397,17 +400,8 @@ std::vector<Piece> flatten_pieces(const zero_plan* plan, const uint16_t* const* 
     return pieces;
 }
 
-bool fits_tensor_major(const zero_plan* plan) {
-    if (plan->kind != 1 || plan->n_ranks > kMaxRanks || plan->shard <= 0) return false;
-    for (const int64_t n : plan->numels)
-        if (n >= (int64_t(1) << 31)) return false;
-    return true;
-}
-
-// The compact table holds every chunk offset (< S) in 32 bits.
-bool fits_compact(const zero_plan* plan) {
-    return plan->n_ranks <= CompactBatch::kRanks && plan->shard < (int64_t(1) << 31);
-}
+using zero::copy::fits_compact;
+using zero::copy::fits_tensor_major;
 
 template <bool kScatter>
 zero_status launch_tensors_any(const zero_plan* plan, uint16_t* const* bufs,

@@ -130,6 +130,13 @@ class RankStep:
                 self.partials, self.max_norm, self.scale, st))()
 
     def adamw(self, stream=None):
+        """The AdamW update with bias-correction step t = self.t + 1. self.t
+        counts the iterations issued, skipped ones included: a non-finite global
+        norm makes the kernel skip the update on the device, and nothing reports
+        that back to the host inside a step, so after a skipped iteration the
+        state holds one update fewer than t. (A caller that wants skipped
+        iterations left uncounted reads the coefficient back, self.scale, and
+        lowers self.t.)"""
         self.t += 1
         clip = self.scale if self.max_norm > 0 else None
         if self.offload:        # returns once the host update is done; `stream` orders the copies
