@@ -512,29 +512,15 @@ extern "C" size_t zero_reduce_workspace_bytes(int64_t count) {
     return need > fixed ? need : fixed;
 }
 
-extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
-                                              const uint16_t* const* replicas, int32_t n_replicas,
-                                              int64_t begin, int64_t count, uint16_t* shard_grad,
-                                              double* sqnorm_out, void* workspace,
-                                              size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// The reduce after its arguments (and, for the norm, the partials buffer: 8-byte
+// aligned, at least zero_sqnorm_workspace_bytes()) have been checked.
+zero_status reduce_shard(const zero_plan* plan, int32_t rank, const uint16_t* const* replicas,
+                         int32_t n_replicas, int64_t begin, int64_t count, uint16_t* shard_grad,
+                         double* sqnorm_out, double* partials, size_t workspace_bytes,
+                         hipStream_t stream) {
     using zero::fail;
-    zero::clear_error();
-    if (plan == nullptr || replicas == nullptr || shard_grad == nullptr)
-        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: NULL plan, replicas or shard_grad");
-    if (rank < 0 || rank >= plan->n_ranks)
-        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: rank out of range");
-    if (n_replicas < 1 || n_replicas > ZERO_MAX_REPLICAS)
-        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: n_replicas must be 1.." +
-                                     std::to_string(ZERO_MAX_REPLICAS));
-    if (begin < 0 || count < 0 || begin > plan->padded || count > plan->padded - begin)
-        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: window outside [0, P)");
-    if (sqnorm_out != nullptr) {
-        if (workspace == nullptr) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: NULL workspace");
-        if (!aligned(workspace, 8))
-            return fail(ZERO_EINVAL, "zero_grad_reduce_shard: workspace not 8-byte aligned");
-        if (workspace_bytes < zero_sqnorm_workspace_bytes())
-            return fail(ZERO_ENOSPACE, "zero_grad_reduce_shard: workspace too small");
-    }
     ReplicaTable table{};
     for (int32_t k = 0; k < n_replicas; ++k) {
         if (replicas[k] == nullptr) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: NULL replica");
@@ -544,7 +530,6 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
     const int64_t lo = begin > shard_lo ? begin : shard_lo;
     const int64_t end = begin + count, shard_hi = shard_lo + plan->shard;
     const int64_t hi = end < shard_hi ? end : shard_hi;
-    double* partials = static_cast<double*>(workspace);
     if (lo >= hi) {
         if (sqnorm_out != nullptr) {
             hipLaunchKernelGGL(write_zero, dim3(1), dim3(64), 0, stream, sqnorm_out);
@@ -633,6 +618,46 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
     if (st != ZERO_OK || !norm) return st;
     hipLaunchKernelGGL(finish_sum, dim3(1), dim3(kThreads), 0, stream, partials, blocks, sqnorm_out);
     return zero::check_hip(hipGetLastError(), "zero_grad_reduce_shard finish launch");
+}
+
+
+// Checks the arguments every form of the reduce shares.
+zero_status check_reduce_args(const zero_plan* plan, int32_t rank, const uint16_t* const* replicas,
+                              int32_t n_replicas, int64_t begin, int64_t count,
+                              const uint16_t* shard_grad) {
+    using zero::fail;
+    if (plan == nullptr || replicas == nullptr || shard_grad == nullptr)
+        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: NULL plan, replicas or shard_grad");
+    if (rank < 0 || rank >= plan->n_ranks)
+        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: rank out of range");
+    if (n_replicas < 1 || n_replicas > ZERO_MAX_REPLICAS)
+        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: n_replicas must be 1.." +
+                                     std::to_string(ZERO_MAX_REPLICAS));
+    if (begin < 0 || count < 0 || begin > plan->padded || count > plan->padded - begin)
+        return fail(ZERO_EINVAL, "zero_grad_reduce_shard: window outside [0, P)");
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
+                                              const uint16_t* const* replicas, int32_t n_replicas,
+                                              int64_t begin, int64_t count, uint16_t* shard_grad,
+                                              double* sqnorm_out, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+    using zero::fail;
+    zero::clear_error();
+    zero_status st = check_reduce_args(plan, rank, replicas, n_replicas, begin, count, shard_grad);
+    if (st != ZERO_OK) return st;
+    if (sqnorm_out != nullptr) {
+        if (workspace == nullptr) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: NULL workspace");
+        if (!aligned(workspace, 8))
+            return fail(ZERO_EINVAL, "zero_grad_reduce_shard: workspace not 8-byte aligned");
+        if (workspace_bytes < zero_sqnorm_workspace_bytes())
+            return fail(ZERO_ENOSPACE, "zero_grad_reduce_shard: workspace too small");
+    }
+    return reduce_shard(plan, rank, replicas, n_replicas, begin, count, shard_grad, sqnorm_out,
+                        static_cast<double*>(workspace), workspace_bytes, stream);
 }
 
 extern "C" zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double* sqnorm_out,
