@@ -203,6 +203,29 @@ zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
                                    double* sqnorm_out, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): zero_grad_reduce_shard
+ * with the same arguments except the workspace, which is a device array the
+ * library owns, ZERO_NOALLOC_SCRATCH_BYTES bytes on each device, kept from the
+ * library's load until the process ends. The call allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library routine. The first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress) with
+ * the device current. The bf16 output is zero_grad_reduce_shard's. The norm
+ * equals zero_grad_reduce_shard's with a workspace of
+ * ZERO_NOALLOC_SCRATCH_BYTES bytes: windows of 2^24 elements or more whose
+ * one-pass partials fit the array (up to about 2.7e8 elements) take the
+ * one-pass kernel, larger windows the grid-stride kernel and its fixed 2,048
+ * partials, so no window size is refused. Every call on one device shares
+ * that device's array: calls that may overlap on one device (other streams,
+ * other host threads) race on it and must be ordered by the caller; calls in
+ * order on one stream are safe. Errors: as zero_grad_reduce_shard (no
+ * workspace errors); ZERO_ERANGE for a device index above 63; ZERO_EHIP. */
+#define ZERO_NOALLOC_SCRATCH_BYTES (4u << 20)
+zero_status zero_grad_reduce_shard_noalloc(const zero_plan* plan, int32_t rank,
+                                           const uint16_t* const* replicas, int32_t n_replicas,
+                                           int64_t begin, int64_t count, uint16_t* shard_grad,
+                                           double* sqnorm_out, hipStream_t stream);
+
 /* ------------------------------------------------------------------ squared norm
  *
  * Sum of squares of n bf16 values (device [n]), accumulated in fp64 (each

@@ -59,6 +59,8 @@ _plan_segments = _fn("zero_plan_segments", c_i32,
 _plan_memory = _fn("zero_plan_memory_bytes", c_i32, [c_vp, c_i32, c_i32, ctypes.POINTER(c_dbl)])
 _reduce = _fn("zero_grad_reduce_shard", c_i32,
               [c_vp, c_i32, ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp])
+_reduce_noalloc = _fn("zero_grad_reduce_shard_noalloc", c_i32,
+                      [c_vp, c_i32, ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_vp, c_vp, c_vp])
 _sqnorm = _fn("zero_grad_sqnorm", c_i32, [c_vp, c_i64, c_vp, c_vp, c_sz, c_vp])
 _ws_bytes = _fn("zero_sqnorm_workspace_bytes", c_sz, [])
 _rws_bytes = _fn("zero_reduce_workspace_bytes", c_sz, [c_i64])
@@ -304,6 +306,20 @@ def zero_grad_reduce_shard(plan: Plan, rank: int, replicas: Sequence, begin: int
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_reduce(plan.handle, rank, ptrs, len(replicas), begin, count, out, sq, ws, wsb,
                    _stream(stream, shard_grad)), "zero_grad_reduce_shard")
+
+
+ZERO_NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def zero_grad_reduce_shard_noalloc(plan: Plan, rank: int, replicas: Sequence, begin: int, count: int,
+                                   shard_grad, sqnorm_out=None, stream=None) -> None:
+    """zero_grad_reduce_shard with the norm partials in the library's own device
+    array: no workspace, no allocation. Calls that may overlap on one device race."""
+    _check_reduce_args(plan, replicas, count, shard_grad, sqnorm_out)
+    ptrs = (c_vp * max(len(replicas), 1))(*[_ptr(r, 2, "replica") for r in replicas])
+    _check(_reduce_noalloc(plan.handle, rank, ptrs, len(replicas), begin, count,
+                           _ptr(shard_grad, 2, "shard_grad"), _ptr(sqnorm_out, 8, "sqnorm_out"),
+                           _stream(stream, shard_grad)), "zero_grad_reduce_shard_noalloc")
 
 
 def zero_grad_sqnorm(grad, sqnorm_out, n: Optional[int] = None, workspace=None, stream=None) -> None:

@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "device_common.hpp"
@@ -658,6 +659,67 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
     }
     return reduce_shard(plan, rank, replicas, n_replicas, begin, count, shard_grad, sqnorm_out,
                         static_cast<double*>(workspace), workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------ no allocation
+//
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the reduce with its norm partials in a library-owned device array.
+// Each device holds its own copy of `scratch` from the library's load until the
+// process ends; host code never passes the array's name to a kernel (on the
+// host it is only a stand-in), but the address hipGetSymbolAddress gives for
+// the current device, looked up once per device and kept.
+constexpr size_t kStaticScratchBytes = ZERO_NOALLOC_SCRATCH_BYTES;
+static_assert(kStaticScratchBytes >= kMaxPartials * sizeof(double),
+              "the scratch holds the grid-stride kernels' partials");
+static __device__ __align__(256) double scratch[kStaticScratchBytes / sizeof(double)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`.
+zero_status device_scratch(double** out) {
+    int dev = -1;
+    zero_status st = zero::check_hip(hipGetDevice(&dev), "zero_grad_reduce_shard_noalloc: hipGetDevice");
+    if (st != ZERO_OK) return st;
+    if (dev < 0 || dev >= kMaxDevices)
+        return zero::fail(ZERO_ERANGE, "zero_grad_reduce_shard_noalloc: device index " +
+                                           std::to_string(dev) + " past " + std::to_string(kMaxDevices - 1));
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        st = zero::check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                             "zero_grad_reduce_shard_noalloc: hipGetSymbolAddress");
+        if (st != ZERO_OK) return st;
+        if (p == nullptr)
+            return zero::fail(ZERO_EHIP, "zero_grad_reduce_shard_noalloc: no device address for the scratch");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<double*>(g_scratch_ptr[dev]);
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_grad_reduce_shard_noalloc(const zero_plan* plan, int32_t rank,
+                                                      const uint16_t* const* replicas,
+                                                      int32_t n_replicas, int64_t begin,
+                                                      int64_t count, uint16_t* shard_grad,
+                                                      double* sqnorm_out, hipStream_t stream) {
+    zero::clear_error();
+    zero_status st = check_reduce_args(plan, rank, replicas, n_replicas, begin, count, shard_grad);
+    if (st != ZERO_OK) return st;
+    double* partials = nullptr;
+    if (sqnorm_out != nullptr) {
+        st = device_scratch(&partials);
+        if (st != ZERO_OK) return st;
+    }
+    // The partials need no clearing: each kernel writes every slot it later reads.
+    return reduce_shard(plan, rank, replicas, n_replicas, begin, count, shard_grad, sqnorm_out,
+                        partials, sqnorm_out != nullptr ? kStaticScratchBytes : 0, stream);
 }
 
 extern "C" zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double* sqnorm_out,
