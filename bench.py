@@ -74,6 +74,10 @@ def parse_args(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="with --profile-steps: first copy 1 GiB once (a plain copy kernel of known "
                          "size, to scale hardware byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: read two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) "
+                         "of a '--profile-steps N --calibrate-copy' run of this workload, and record "
+                         "the AdamW call's HBM bytes in profiles/adamw_traffic.json")
     return ap.parse_args(argv)
 
 
@@ -593,6 +597,84 @@ def measured_traffic(elems_per_launch: int):
     return None
 
 
+def _counter_means(folder: str, counter: str):
+    """Per kernel name, the per-dispatch values of one rocprofv3 counter (summed
+    over the rows a dispatch reports, e.g. one per L2 channel), in KiB."""
+    import collections
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"bench.py: no counter_collection.csv under {folder}")
+    per, names = collections.defaultdict(float), {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (f, r["Dispatch_Id"])
+            per[key] += float(r["Counter_Value"])
+            names[key] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for k in sorted(per, key=lambda k: (k[0], int(k[1]))):
+        out[names[k]].append(per[k])
+    return out
+
+
+def write_traffic(args) -> int:
+    """profiles/adamw_traffic.json's entry for this workload, from the counter runs."""
+    import zero_partitioned_mixed_partition_amd as zm
+    if args.workload not in RankWorkload.SPECS or args.workload.endswith("-pertensor") \
+            or args.workload.endswith("-offload"):
+        raise SystemExit("bench.py: --write-traffic covers the flat-array AdamW workloads")
+    lst, nd, rank, *_rest, layout = RankWorkload.SPECS[args.workload]
+    import synth
+    w = synth.WORKLOADS[lst]
+    plan = (zm.zero_partition_plan_shard0(w.numels, [x[0] for x in w.shapes], nd, w.align)
+            if layout == "shard0" else zm.zero_partition_plan(w.numels, nd, w.align))
+    S = plan.shard_numel
+    calls = args.profile_steps
+    if calls < 1:
+        raise SystemExit("bench.py: give --profile-steps as in the counter runs")
+    fetch = _counter_means(args.write_traffic[0], "FETCH_SIZE")
+    write = _counter_means(args.write_traffic[1], "WRITE_SIZE")
+    cp = [n for n in fetch if "copyBuffer" in n]
+    if not cp or not [n for n in write if "copyBuffer" in n]:
+        raise SystemExit("bench.py: the runs need --calibrate-copy (a 1 GiB copy to scale by)")
+    gib_kib = float(1 << 20)
+    f_scale = gib_kib / max(fetch[cp[0]])
+    w_scale = gib_kib / max(write[[n for n in write if "copyBuffer" in n][0]])
+    ad = [n for n in fetch if n.startswith("adamw_kernel")]
+    if len(ad) != 1:
+        raise SystemExit(f"bench.py: expected one AdamW kernel name, found {ad}")
+    ad = ad[0]
+    f_bytes = sum(fetch[ad]) * 1024 * f_scale / calls
+    w_bytes = sum(write[ad]) * 1024 * w_scale / calls
+    entry = {"kernel": "adamw_kernel", "workload": f"{args.workload} rank {rank} of {nd}",
+             "elems": S, "dispatches_per_call": len(fetch[ad]) // calls,
+             "fetch_bytes": f_bytes, "write_bytes": w_bytes, "bytes_per_launch": f_bytes + w_bytes,
+             "algorithmic_bytes": 28 * S, "fetch_scale": f_scale, "write_scale": w_scale,
+             "source_sha256": kernel_source_digest(),
+             "commands": [
+                 f"rocprofv3 --pmc FETCH_SIZE -T -d {args.write_traffic[0]} -o fetch -f csv -- "
+                 f"python3 bench.py --workload {args.workload} --profile-steps {calls} --calibrate-copy",
+                 f"rocprofv3 --pmc WRITE_SIZE -T -d {args.write_traffic[1]} -o write -f csv -- "
+                 f"python3 bench.py --workload {args.workload} --profile-steps {calls} --calibrate-copy"]}
+    d = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    runs = [e for e in d.get("runs", []) if e.get("elems") != S]
+    d["runs"] = runs + [entry]
+    json.dump(d, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(entry, indent=1))
+    print(f"AdamW traffic / algorithmic bytes: {(f_bytes + w_bytes) / (28 * S):.6f}")
+    print(f"calibration: {cp[0]} fetch x{f_scale:.4f}, write x{w_scale:.4f}")
+    print("| Kernel | Dispatches | Read per dispatch (KiB, scaled) | Written per dispatch (KiB, scaled) |")
+    print("|---|---|---|---|")
+    for n in sorted(fetch):
+        if n in write:
+            print(f"| {n} | {len(fetch[n])} | {sum(fetch[n]) / len(fetch[n]) * f_scale:,.1f} | "
+                  f"{sum(write[n]) / len(write[n]) * w_scale:,.1f} |")
+    return 0
+
+
 def cpu_baseline(wl, budget_s: float):
     """The oracle on the host for the same workload, bounded in time. The default
     workload times the oracle's whole rank step; the large ones time the same
@@ -665,6 +747,8 @@ def cpu_baseline(wl, budget_s: float):
 
 def main(argv=None):
     args = parse_args(argv)
+    if args.write_traffic:
+        return write_traffic(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the per-rank step is measured on one GPU's share)", file=sys.stderr)

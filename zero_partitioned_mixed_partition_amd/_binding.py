@@ -11,7 +11,10 @@ import ctypes
 import os
 from typing import List, Optional, Sequence, Tuple
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_mi355x.so")
+# ZERO_MI355X_LIB may name another build of the same sources (one built with
+# other compile-time switches by _build.py, for a measured comparison).
+LIB_PATH = os.environ.get("ZERO_MI355X_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libzero_mi355x.so")
 
 ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_ENOMEM, ZERO_EHIP, ZERO_ENOSPACE = range(6)
 ZERO_MAX_REPLICAS = 64

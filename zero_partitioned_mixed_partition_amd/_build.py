@@ -37,10 +37,10 @@ def _compile(src: str, obj: str, defines: List[str], save_temps: Optional[str]) 
 
 
 def build(out: str = LIB, defines: Optional[List[str]] = None, save_temps: Optional[str] = None,
-          verbose: bool = False) -> str:
+          verbose: bool = False, objdir: Optional[str] = None) -> str:
     """Compile every source and link the shared library; returns its path."""
     defines = list(defines or [])
-    objdir = save_temps or os.path.join(ROOT, "_build")
+    objdir = save_temps or objdir or os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     cmds = []
     objs = []
@@ -64,4 +64,17 @@ def build(out: str = LIB, defines: Optional[List[str]] = None, save_temps: Optio
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    # python _build.py [-v] [-D NAME=VALUE ...] [-o OUT]: OUT defaults to the product
+    # library; a build with switches (-D) for a measured comparison goes elsewhere,
+    # loaded through the ZERO_MI355X_LIB environment variable.
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("-D", action="append", default=[], metavar="NAME=VALUE")
+    ap.add_argument("-o", default=LIB)
+    a = ap.parse_args()
+    out = os.path.abspath(a.o)
+    objdir = None
+    if out != LIB:
+        objdir = os.path.join(ROOT, "_build", "variant_" + os.path.splitext(os.path.basename(out))[0])
+    build(out, defines=[f"-D{d}" for d in a.D], objdir=objdir, verbose=a.v)
