@@ -34,6 +34,7 @@
 
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "pieces.hpp"
 #include "tensor_major.hpp"
 
 namespace {
@@ -122,13 +123,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(SegBatch b) {
 // per workgroup, the index of its descriptor, so a workgroup finds its piece
 // with two dependent scalar loads and every piece of a plan (a Shard(0) plan
 // has about N_d per tensor) goes out in one launch.
-struct alignas(32) PieceDesc {
-    const uint16_t* src;        // NULL: fill with zeros
-    uint16_t* dst;
-    int64_t len;
-    int64_t first_block;
-};
-static_assert(sizeof(PieceDesc) == 32, "one 32-byte descriptor per piece");
+using zero::copy::PieceDesc;
 
 __global__ __launch_bounds__(kThreads) void copy_table_kernel(const PieceDesc* __restrict__ table,
                                                               const uint32_t* __restrict__ index,
@@ -280,11 +275,7 @@ namespace {
 
 // Launches one segment-copy kernel per kSegs segments. Each piece is
 // (src, dst, len); a NULL src fills dst with zeros.
-struct Piece {
-    const uint16_t* src;
-    uint16_t* dst;
-    int64_t len;
-};
+using zero::copy::Piece;
 
 zero_status launch_pieces(const std::vector<Piece>& pieces, hipStream_t stream, const char* who) {
     SegBatch batch{};
@@ -368,37 +359,8 @@ zero_status launch_tensors(const zero_plan* plan, uint16_t* const* bufs, uint16_
     return flush();
 }
 
-// Every segment of the plan as a piece from its shard to its tensor (a NULL
-// shard skips its rank's segments).
-std::vector<Piece> gather_pieces(const zero_plan* plan, const uint16_t* const* shards,
-                                 uint16_t* const* tensors) {
-    std::vector<Piece> pieces;
-    pieces.reserve(plan->all.size());
-    for (const zero_segment& seg : plan->all)
-        if (shards[seg.rank] != nullptr)
-            pieces.push_back({shards[seg.rank] + seg.shard_offset,
-                              tensors[seg.tensor] + seg.tensor_offset, seg.length});
-    return pieces;
-}
-
-// Every segment from its tensor to its place in the flat buffer, in flat order,
-// with a zero-fill piece for every gap (and after the last segment). With
-// with_copies false, the gaps only.
-std::vector<Piece> flatten_pieces(const zero_plan* plan, const uint16_t* const* tensors,
-                                  uint16_t* flat, bool with_copies) {
-    std::vector<Piece> pieces;
-    pieces.reserve(2 * plan->all.size() + 1);
-    int64_t pos = 0;
-    for (const zero_segment& seg : plan->all) {
-        const int64_t at = static_cast<int64_t>(seg.rank) * plan->shard + seg.shard_offset;
-        if (at > pos) pieces.push_back({nullptr, flat + pos, at - pos});
-        if (with_copies)
-            pieces.push_back({tensors[seg.tensor] + seg.tensor_offset, flat + at, seg.length});
-        pos = at + seg.length;
-    }
-    if (plan->padded > pos) pieces.push_back({nullptr, flat + pos, plan->padded - pos});
-    return pieces;
-}
+using zero::copy::flatten_pieces;
+using zero::copy::gather_pieces;
 
 using zero::copy::fits_compact;
 using zero::copy::fits_tensor_major;
@@ -491,16 +453,8 @@ zero_status make_copy_table(const std::vector<Piece>& pieces, zero_copy_table** 
     zero_copy_table* tab = nullptr;
     try {
         int64_t blocks = 0;
-        for (const Piece& pc : pieces) {
-            if (pc.len <= 0) continue;
-            const int64_t b = (pc.len + kChunk - 1) / kChunk;
-            if (blocks + b > 0x7FFFFFFF || descs.size() >= 0xFFFFFFFFu)
-                return fail(ZERO_ERANGE, std::string(who) + ": more than 2^31 workgroups");
-            index.insert(index.end(), static_cast<size_t>(b), static_cast<uint32_t>(descs.size()));
-            descs.push_back({pc.src, pc.dst, pc.len, blocks});
-            blocks += b;
-        }
-        if (blocks > 0) index = zero::xcd_major_index(index);
+        const zero_status cs = zero::copy::copy_table_contents(pieces, kChunk, &descs, &index, &blocks, who);
+        if (cs != ZERO_OK) return cs;
         tab = new zero_copy_table;
         tab->blocks = blocks;
     } catch (const std::bad_alloc&) {

@@ -126,7 +126,7 @@ extern "C" zero_status zero_partition_plan_shard0(const int64_t* numels, const i
                                              ": dim0 must be >= 1 and divide numel");
             }
             const int64_t in = n > 0 ? n / d0 : 0;
-            const int64_t rows = n > 0 ? (d0 + n_ranks - 1) / n_ranks : 0;
+            const int64_t rows = n > 0 ? d0 / n_ranks + (d0 % n_ranks != 0 ? 1 : 0) : 0;
             if (n > INT64_MAX - total || (in > 0 && rows > (INT64_MAX - buf) / in)) {
                 delete plan;
                 return fail(ZERO_ERANGE, "zero_partition_plan_shard0: sizes overflow int64");
@@ -137,6 +137,10 @@ extern "C" zero_status zero_partition_plan_shard0(const int64_t* numels, const i
             plan->offsets[static_cast<size_t>(t)] = buf;
             plan->chunk_elems.push_back(rows * in);
             buf += rows * in;
+        }
+        if (buf > INT64_MAX - (align_elems - 1)) {
+            delete plan;
+            return fail(ZERO_ERANGE, "zero_partition_plan_shard0: padded length overflows int64");
         }
         const int64_t s = (buf + align_elems - 1) / align_elems * align_elems;
         if (s > INT64_MAX / n_ranks) {
@@ -151,6 +155,8 @@ extern "C" zero_status zero_partition_plan_shard0(const int64_t* numels, const i
             for (int32_t t = 0; t < n_tensors; ++t) {
                 const size_t ti = static_cast<size_t>(t);
                 const int64_t d0 = plan->numels[ti] > 0 ? dim0[t] : 0;
+                // rank r holds rows only if r * chunk_rows < d0 (checked without the product)
+                if (d0 == 0 || r > (d0 - 1) / chunk_rows[ti]) continue;
                 const int64_t first = static_cast<int64_t>(r) * chunk_rows[ti];
                 const int64_t rows = d0 - first < chunk_rows[ti] ? d0 - first : chunk_rows[ti];
                 if (rows <= 0) continue;
