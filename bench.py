@@ -33,6 +33,11 @@ Other workloads (`--workload`), each timed as its own configuration states:
               the host, the host runs AdamW, the bf16 parameters come back, in
               overlapped chunks (reduce, clip and gather stay on the GPU)
 
+With the default workload the run then measures the Llama-3-8B step too and
+reports it under the line's "also" key (`--also` picks other workloads, or
+none), so one command gives both configurations the headline roofline comes
+from.
+
 All inputs are seeded synthetic data resident in HBM before timing starts. The
 other ranks' norm partials and parameter shards are inputs computed once,
 untimed (on a cluster they arrive through a scalar all-reduce and the
@@ -74,6 +79,9 @@ def parse_args(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="with --profile-steps: first copy 1 GiB once (a plain copy kernel of known "
                          "size, to scale hardware byte counters)")
+    ap.add_argument("--also", nargs="*", default=None, choices=WORKLOAD_NAMES, metavar="WORKLOAD",
+                    help="after the line's workload, measure these too (their figures go under "
+                         "'also'); default: llama3-8b with the llama3-70b line, none otherwise")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: read two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) "
                          "of a '--profile-steps N --calibrate-copy' run of this workload, and record "
@@ -745,6 +753,97 @@ def cpu_baseline(wl, budget_s: float):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def measure(wl, steps: int, warmup: int) -> dict:
+    """Warmup, then `steps` timed steps (the AdamW phase bracketed by events on its
+    launch stream), then each phase on its own, the cold-cache AdamW launch, and
+    (offload) the host update and the link on their own."""
+    import torch
+    # Python's cyclic garbage collector is off while steps are issued: a full
+    # collection pauses the issuing thread for tens of milliseconds, which the
+    # GPU would spend idle (as timeit does; the collector is run first).
+    gc.collect()
+    gc.disable()
+    for _ in range(warmup):
+        run_step(wl)
+    torch.cuda.synchronize()
+    # Timed region: whole steps; the AdamW phase is bracketed by events on the
+    # stream it is launched on (torch's current stream, which every call here uses).
+    adamw_ev = AdamWEvents(steps * sum(1 for name, _ in wl.phases if name == "adamw"))
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        for name, fn in wl.phases:
+            if name == "adamw":
+                adamw_ev.record()
+                fn()
+                adamw_ev.record()
+            else:
+                fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / steps
+    adamw_each = sorted(t / wl.adamw_launches for t in adamw_ev.elapsed_ms())
+    adamw_ms = sum(adamw_each) / len(adamw_each)
+    print(f"[bench] {wl.name}: {steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s), "
+          f"adamw {adamw_ms * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
+
+    phase_ms = time_phases(wl, max(3, min(steps, 50)))
+    bpp = wl.bytes_per_phase()
+    offload = getattr(wl, "offload", False)
+
+    def rates(ms):
+        out = {}
+        for n in ms:
+            gbs = bpp[n] / (ms[n] * 1e-3) / 1e9
+            if offload and n == "adamw":
+                out[n] = {"ms": ms[n], "link_bytes": bpp[n], "gbs": gbs,
+                          "frac_of_pcie_peak": gbs / PCIE_PEAK_GBS}
+            else:
+                out[n] = {"ms": ms[n], "bytes": bpp[n], "gbs": gbs,
+                          "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
+        return out
+    kernels = rates(phase_ms)
+    outside = None
+    if getattr(wl, "extra_phases", None):
+        class _Extra:
+            phases = wl.extra_phases
+        outside = rates(time_phases(_Extra, max(3, min(steps, 20))))
+    parts = wl.offload_parts(max(3, min(steps, 10))) if offload else None
+    flushed = None if offload else adamw_flushed(wl, 10)
+    gc.enable()
+    return {"ms_per_step": ms_per_step, "adamw_ms": adamw_ms, "adamw_each": adamw_each,
+            "kernels": kernels, "outside": outside, "bpp": bpp, "flushed": flushed, "parts": parts,
+            "elems_per_launch": wl.elems_per_step // wl.adamw_launches, "offload": offload}
+
+
+def also_line(name: str, device) -> dict:
+    """Another workload measured in the same run, summarised: its step and AdamW
+    figures (default steps and warmup)."""
+    import torch
+    print(f"[bench] setting up {name} (extra keys)", file=sys.stderr, flush=True)
+    wl = make_workload(name, device)
+    steps, warmup = DEFAULT_STEPS[name]
+    m = measure(wl, steps, warmup)
+    elems = m["elems_per_launch"]
+    gbs = 28 * elems / (m["adamw_ms"] * 1e-3) / 1e9
+    out = {"workload": wl.describe(), "steps": steps, "warmup": warmup,
+           "ms_per_step": m["ms_per_step"], "value": wl.elems_per_step / (m["ms_per_step"] * 1e-3),
+           "adamw_params_per_s": elems / (m["adamw_ms"] * 1e-3),
+           "adamw_event_us": {"mean": m["adamw_ms"] * 1e3,
+                              "median": m["adamw_each"][len(m["adamw_each"]) // 2] * 1e3,
+                              "min": m["adamw_each"][0] * 1e3, "launches": len(m["adamw_each"])},
+           "adamw_hbm_gbs": gbs, "adamw_frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+           "kernels": m["kernels"], "traffic": measured_traffic(elems)}
+    del wl
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.write_traffic:
@@ -777,72 +876,17 @@ def main(argv=None):
         print(f"[bench] ran {args.profile_steps} steps for profiling", file=sys.stderr, flush=True)
         return 0
 
-    # Python's cyclic garbage collector is off while steps are issued: a full
-    # collection pauses the issuing thread for tens of milliseconds, which the
-    # GPU would spend idle (as timeit does; the collector is run first).
-    gc.collect()
-    gc.disable()
-    for _ in range(warmup):
-        run_step(wl)
-    torch.cuda.synchronize()
-    # Timed region: whole steps; the AdamW phase is bracketed by events on the
-    # stream it is launched on (torch's current stream, which every call here uses).
-    adamw_ev = AdamWEvents(steps * sum(1 for name, _ in wl.phases if name == "adamw"))
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
-        for name, fn in wl.phases:
-            if name == "adamw":
-                adamw_ev.record()
-                fn()
-                adamw_ev.record()
-            else:
-                fn()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / steps
-    adamw_each = sorted(t / wl.adamw_launches for t in adamw_ev.elapsed_ms())
-    adamw_ms = sum(adamw_each) / len(adamw_each)
-    print(f"[bench] {steps} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s), "
-          f"adamw {adamw_ms * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
-
-    phase_ms = time_phases(wl, max(3, min(steps, 50)))
-    bpp = wl.bytes_per_phase()
-
-    offload = getattr(wl, "offload", False)
-
-    def rates(ms):
-        out = {}
-        for n in ms:
-            gbs = bpp[n] / (ms[n] * 1e-3) / 1e9
-            if offload and n == "adamw":
-                out[n] = {"ms": ms[n], "link_bytes": bpp[n], "gbs": gbs,
-                          "frac_of_pcie_peak": gbs / PCIE_PEAK_GBS}
-            else:
-                out[n] = {"ms": ms[n], "bytes": bpp[n], "gbs": gbs,
-                          "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
-        return out
-    kernels = rates(phase_ms)
-    outside = None
-    if getattr(wl, "extra_phases", None):
-        class _Extra:
-            phases = wl.extra_phases
-        outside = rates(time_phases(_Extra, max(3, min(steps, 20))))
-    elems_per_launch = wl.elems_per_step // wl.adamw_launches
-    adamw_bytes = 28 * elems_per_launch
-    adamw_gbs = adamw_bytes / (adamw_ms * 1e-3) / 1e9
-    value = wl.elems_per_step / (ms_per_step * 1e-3)
-
-    parts = wl.offload_parts(max(3, min(steps, 10))) if offload else None
-    flushed = None if offload else adamw_flushed(wl, 10)
-    gc.enable()
+    m = measure(wl, steps, warmup)
     cpu = None
     if args.cpu_baseline_seconds > 0:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, args.cpu_baseline_seconds)
+    ms_per_step, adamw_ms, adamw_each = m["ms_per_step"], m["adamw_ms"], m["adamw_each"]
+    kernels, outside, bpp, flushed, parts = m["kernels"], m["outside"], m["bpp"], m["flushed"], m["parts"]
+    elems_per_launch, offload = m["elems_per_launch"], m["offload"]
+    adamw_bytes = 28 * elems_per_launch
+    adamw_gbs = adamw_bytes / (adamw_ms * 1e-3) / 1e9
+    value = wl.elems_per_step / (ms_per_step * 1e-3)
 
     line = {
         "metric": METRIC,
@@ -876,6 +920,14 @@ def main(argv=None):
                      "traffic": measured_traffic(elems_per_launch)},
         "cpu_baseline": cpu,
     }
+    also = args.also if args.also is not None else (
+        ["llama3-8b"] if args.workload == "llama3-70b" else [])
+    if also:
+        del wl, m
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        line["also"] = {name: also_line(name, device) for name in also}
     if offload:
         # The update runs on the host: the GPU-side figures above do not apply.
         link_gbs = 4 * elems_per_launch / (adamw_ms * 1e-3) / 1e9
