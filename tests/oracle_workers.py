@@ -115,3 +115,43 @@ def reduce_adamw_digests(tasks, workers=None):
     with _pool(workers) as ex:
         for r in ex.map(_reduce_adamw_digests, tasks, chunksize=1):
             yield r
+
+
+def canonical_nan_f32(a):
+    """float32 bits with every NaN replaced by one quiet NaN (0x7FC00000): NaN
+    signs and payloads that IEEE leaves open (the sign of sqrt of a negative
+    number) compare equal."""
+    import numpy as np
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).copy()
+    u[(u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)] = np.uint32(0x7FC00000)
+    return u
+
+
+def canonical_nan_bf16(a):
+    import numpy as np
+    u = np.ascontiguousarray(a, dtype=np.uint16).copy()
+    u[(u & np.uint16(0x7FFF)) > np.uint16(0x7F80)] = np.uint16(0x7FC0)
+    return u
+
+
+def _adamw_sweep_digests(args):
+    """The oracle's AdamW step on n elements whose second moment runs over the
+    float32 bit patterns [lo, lo + n) (mod 2^32), with master p0, first moment m0
+    and a zero gradient; digests of (master, exp_avg, exp_avg_sq, param) after
+    NaN canonicalisation."""
+    import numpy as np
+    import oracle
+    lo, n, p0, m0, step, hp = args
+    v = (np.arange(lo, lo + n, dtype=np.uint64) & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.float32)
+    p = np.full(n, p0, np.float32)
+    m = np.full(n, m0, np.float32)
+    with np.errstate(all="ignore"):
+        P, M, V, B = oracle.adamw_step(p, m, v, np.zeros(n, np.uint16), step, **hp)
+    return (digest(canonical_nan_f32(P)), digest(canonical_nan_f32(M)), digest(canonical_nan_f32(V)),
+            digest(canonical_nan_bf16(B)))
+
+
+def adamw_sweep_digests(tasks, workers=None):
+    with _pool(workers) as ex:
+        for r in ex.map(_adamw_sweep_digests, tasks, chunksize=1):
+            yield r
