@@ -33,10 +33,8 @@ Other workloads (`--workload`), each timed as its own configuration states:
               the host, the host runs AdamW, the bf16 parameters come back, in
               overlapped chunks (reduce, clip and gather stay on the GPU)
 
-With the default workload the run then measures the Llama-3-8B step too and
-reports it under the line's "also" key (`--also` picks other workloads, or
-none), so one command gives both configurations the headline roofline comes
-from.
+`--also W ...` measures further workloads after the line's and reports them
+under the line's "also" key (summaries: step, AdamW events, kernels, traffic).
 
 All inputs are seeded synthetic data resident in HBM before timing starts. The
 other ranks' norm partials and parameter shards are inputs computed once,
@@ -81,7 +79,7 @@ def parse_args(argv=None):
                          "size, to scale hardware byte counters)")
     ap.add_argument("--also", nargs="*", default=None, choices=WORKLOAD_NAMES, metavar="WORKLOAD",
                     help="after the line's workload, measure these too (their figures go under "
-                         "'also'); default: llama3-8b with the llama3-70b line, none otherwise")
+                         "'also')")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: read two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) "
                          "of a '--profile-steps N --calibrate-copy' run of this workload, and record "
@@ -920,8 +918,7 @@ def main(argv=None):
                      "traffic": measured_traffic(elems_per_launch)},
         "cpu_baseline": cpu,
     }
-    also = args.also if args.also is not None else (
-        ["llama3-8b"] if args.workload == "llama3-70b" else [])
+    also = args.also or []
     if also:
         del wl, m
         gc.collect()

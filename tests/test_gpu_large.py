@@ -11,11 +11,12 @@ gpt-1.3b    1.3B GPT list, N_d = 8: 8 replicas reduced for every rank, AdamW on
             (per-window digests from a process pool), exact norm partials of
             every rank, and a full-size gather of synthetic shards.
 llama3-70b  Llama-3-70B list, N_d = 8, rank 7 (8,819,213,312 elements, indices
-            past 2^33): 5 steps as the benchmark runs them (every rank's norm
-            partial and the clip-1.0 coefficient on the device, then AdamW);
-            windows at the shard ends, around 2^31, 2^32 and 2^33, at tensor
-            starts and 32 random 1M windows; the coefficient against the
-            oracle's every step; exact norm partials of two ranks.
+            past 2^33): step 1 as the benchmark runs it (every rank's norm
+            partial and the clip-1.0 coefficient on the device, then AdamW),
+            all eight partials and the coefficient against the oracle's; four
+            more steps with the oracle's coefficient; windows at the shard ends,
+            around 2^31, 2^32 and 2^33 and the AdamW grid's rows, at tensor
+            starts and 32 random 1M windows.
 """
 import math
 
@@ -227,11 +228,15 @@ def test_gpt_1p3b_full_size_gather_of_synthetic_shards(zm):
 
 def test_llama3_70b_rank7_five_steps_windows(zm):
     """The benchmark's Llama-3-70B configuration: rank 7 of 8 (S > 2^33), five
-    steps, each with every rank's norm partial and the clip-1.0 coefficient
-    computed on the device, then AdamW with that coefficient. Checked: the
-    coefficient against the oracle's clip of the same partials (every step),
-    two ranks' step-1 partials exactly, and the state on windows at the shard
-    ends, around 2^31, 2^32, 2^33, at tensor starts and 32 random 1M windows."""
+    AdamW steps. Step 1 runs the benchmark's pipeline: every rank's norm partial
+    and the clip-1.0 coefficient on the device, then AdamW with that device
+    coefficient; all eight partials are checked against the oracle's exact sums
+    of the generated gradients, and the coefficient against the oracle's clip of
+    those. Steps 2-5 take the oracle's step-1 coefficient, uploaded (the oracle's
+    exact norms of all ranks for five steps would take minutes on the host). The
+    fp32 state and bf16 parameters are checked after the five steps on windows at
+    the shard ends, around 2^31, 2^32, 2^33, around the rows of the AdamW
+    dispatch's grid, at tensor starts and 32 random 1M windows."""
     from oracle_workers import grad_sqnorms
     from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep
     w = synth.WORKLOADS["llama3-70b"]
@@ -241,33 +246,49 @@ def test_llama3_70b_rank7_five_steps_windows(zm):
     P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
     lo = rank * S
     assert S > 2 ** 33
-    note(f"llama3-70b: S={S} (fp32 state {12 * S / 1e9:.1f} GB)")
+    steps = w.steps
+    note(f"llama3-70b: S={S} (fp32 state {12 * S / 1e9:.1f} GB); oracle norms of all "
+         f"{w.n_ranks} ranks for step 1 (process pool)")
+    chunk = 1 << 28
+    tasks = [(w.seed, synth.KIND_GRAD, 1, 0, r * S + a, min(chunk, S - a), phi, synth.GRAD_SIGMA)
+             for r in range(w.n_ranks) for a in range(0, S, chunk)]
+    vals = grad_sqnorms(tasks, workers=16)
+    per = len(tasks) // w.n_ranks
+    # chunk values are correctly rounded, so their fp64 sum is within a few ulp
+    want_parts = [math.fsum(vals[r * per:(r + 1) * per]) for r in range(w.n_ranks)]
+    coef1 = np.float32(oracle.clip_scale(want_parts, 1.0))
+    assert 0.0 < coef1 < 1.0
+
     rs = RankStep(plan, rank, 0, Hyper(), 1.0, dev(), gather=False)
     synth.device_normal_f32(rs.master, w.seed, synth.KIND_MASTER, 0, 0, lo, phi, synth.MASTER_SIGMA)
     scratch = torch.empty(S, dtype=torch.int16, device=dev())   # the other ranks' gradients
     d_parts = torch.zeros(w.n_ranks, dtype=torch.float64, device=dev())
-    steps = w.steps
-    parts, coefs = [], []
-    for t in range(1, steps + 1):
-        for r in range(w.n_ranks):          # own rank last: rs.grad keeps its gradient
-            rr = r if r < rank else (r + 1 if r < w.n_ranks - 1 else rank)
-            buf = rs.grad if rr == rank else scratch
-            synth.device_normal_bf16(buf, w.seed, synth.KIND_GRAD, t, 0, rr * S, phi, synth.GRAD_SIGMA)
-            zm.zero_grad_sqnorm(buf, d_parts[rr:rr + 1], workspace=rs.workspace)
-        zm.zero_clip_scale(d_parts, 1.0, rs.scale)
+    for r in list(range(w.n_ranks - 1)) + [rank]:                # own rank last: rs.grad keeps it
+        buf = rs.grad if r == rank else scratch
+        synth.device_normal_bf16(buf, w.seed, synth.KIND_GRAD, 1, 0, r * S, phi, synth.GRAD_SIGMA)
+        zm.zero_grad_sqnorm(buf, d_parts[r:r + 1], workspace=rs.workspace)
+    zm.zero_clip_scale(d_parts, 1.0, rs.scale)
+    rs.adamw()
+    torch.cuda.synchronize()
+    del scratch
+    got_parts = d_parts.cpu().numpy()
+    for r in range(w.n_ranks):
+        assert abs(got_parts[r] - want_parts[r]) <= 1e-12 * want_parts[r], (r, got_parts[r], want_parts[r])
+    got_coef = np.float32(rs.scale.item())
+    assert abs(int(got_coef.view(np.int32)) - int(coef1.view(np.int32))) <= 1, (got_coef, coef1)
+    note(f"llama3-70b: step 1 done, clip coefficient {got_coef} (oracle {coef1})")
+    coefs = [coef1] * steps
+    for t in range(2, steps + 1):
+        synth.device_normal_bf16(rs.grad, w.seed, synth.KIND_GRAD, t, 0, lo, phi, synth.GRAD_SIGMA)
+        rs.scale.fill_(float(coef1))
         rs.adamw()
         torch.cuda.synchronize()
-        parts.append(d_parts.cpu().numpy().copy())
-        coefs.append(np.float32(rs.scale.item()))
-        note(f"llama3-70b: step {t} done, clip coefficient {coefs[-1]}")
-    del scratch
-    for t in range(steps):                  # the device coefficient is the oracle's, bit for bit
-        assert coefs[t] == oracle.clip_scale(list(parts[t]), 1.0), (t, coefs[t])
-    assert all(0.0 < c < 1.0 for c in coefs)
+        note(f"llama3-70b: step {t} done")
 
     rng = np.random.default_rng(70)
     seg_starts = [soff for (_, _, soff, _) in ref.segments(rank)]
-    centers = [0, S, 2 ** 31, 2 ** 32, 2 ** 33] + seg_starts[1:12]
+    per_row = -(-(-(-S // 256)) // 3) * 256        # the AdamW grid's rows (3 rows of workgroups)
+    centers = [0, S, 2 ** 31, 2 ** 32, 2 ** 33, per_row, 2 * per_row] + seg_starts[1:12]
     wins = [(a, b) for a, b in _windows_in_shards([lo + c for c in centers], 2048, S, w.n_ranks, P)
             if a >= lo and b <= lo + S]
     wins += [(lo + int(x), lo + int(x) + (1 << 20)) for x in rng.integers(0, S - (1 << 20), 32)]
@@ -286,18 +307,6 @@ def test_llama3_70b_rank7_five_steps_windows(zm):
         assert_f32_close(host_f32(rs.exp_avg[i0:i1]), m, f"exp_avg [{i0},{i1})")
         assert_f32_close(host_f32(rs.exp_avg_sq[i0:i1]), v, f"exp_avg_sq [{i0},{i1})")
         assert_bf16_close(host_u16(rs.param_shards[rank][i0:i1]), bits, f"param [{i0},{i1})")
-
-    note("llama3-70b: oracle norm partials of ranks 0 and 7 for step 1 (process pool)")
-    chunk = 1 << 28
-    tasks = [(w.seed, synth.KIND_GRAD, 1, 0, r * S + a, min(chunk, S - a), phi, synth.GRAD_SIGMA)
-             for r in (0, rank) for a in range(0, S, chunk)]
-    vals = grad_sqnorms(tasks, workers=16)
-    half = len(tasks) // 2
-    # chunk values are correctly rounded, so their fp64 sum is within a few ulp
-    want0, want7 = math.fsum(vals[:half]), math.fsum(vals[half:])
-    got0, got7 = float(parts[0][0]), float(parts[0][rank])
-    assert abs(got0 - want0) <= 1e-12 * want0, (got0, want0)
-    assert abs(got7 - want7) <= 1e-12 * want7, (got7, want7)
     del rs
     _free_gpu()
 

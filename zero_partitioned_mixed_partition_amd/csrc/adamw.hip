@@ -14,8 +14,8 @@
 // bf16), about 15 flops: HBM-bound by a factor of ~40 against the fp32
 // vector ridge point, so no matrix cores. Each lane updates one element
 // (dword per fp32 array, short for the bf16 gradient and parameter) with
-// non-temporal loads and write-through stores. The grid covers the shard with one element per lane (shards
-// past the 2^32 work-items of one dispatch take several launches): measured on MI355X,
+// non-temporal loads and write-through stores. The grid covers the shard with one element per lane, in
+// one dispatch (rows of workgroups past 2^32 work-items): measured on MI355X,
 // short-lived waves with narrow accesses sustain more bandwidth on this
 // 4-read/4-write pattern than wide vectors or a persistent loop. The same
 // kernel serves any pointer alignment. Indices are 64-bit.
@@ -167,9 +167,13 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ mas
     const float clip = read_clip(clip_scale);
     if (!isfinite(clip)) return;
     const int64_t groups = n / E;
-    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    // The grid is one row of workgroups, or, past the 2^32 work-items one grid
+    // dimension holds, several rows; the dispatcher issues them row after row,
+    // so workgroup blockIdx.y * gridDim.x + blockIdx.x covers the shard in order.
+    const int64_t blk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+    const int64_t tid = blk * kThreads + threadIdx.x;
     if (kPersistPerCu > 0) {
-        const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+        const int64_t stride = static_cast<int64_t>(gridDim.x) * gridDim.y * kThreads;
         for (int64_t i = tid; i < groups; i += stride) Lane<E>::update(master, m, v, grad, param, i, clip, c);
     } else {
         // The host launches a lane per group (and per tail element): one pass
@@ -378,34 +382,31 @@ extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, floa
     st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, "zero_shard_adamw_step");
     if (st != ZERO_OK) return st;
 
-    // One lane group per lane. A dispatch holds fewer than 2^32 work-items, so
-    // larger shards go out as consecutive single-pass launches over chunks
-    // (measured faster than lanes looping over a capped grid).
-    constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
+    // One lane group per lane, the whole shard in one dispatch. A grid dimension
+    // holds fewer than 2^32 work-items, so a larger shard (Llama-3-70B's rank:
+    // 8.8e9 elements) takes a grid of up to kMaxRow workgroups per row and as
+    // many rows as it needs, at most rows - 1 workgroups past the shard's end.
+    constexpr int64_t kMaxRow = (int64_t(1) << 32) / kThreads - 1;
     const bool vec = kEpt > 1 && aligned(master, 4 * kEpt) && aligned(exp_avg, 4 * kEpt) &&
                      aligned(exp_avg_sq, 4 * kEpt) && aligned(grad, 2 * kEpt) &&
                      aligned(param_out, 2 * kEpt);
     const int ept = vec ? kEpt : 1;
-    const int64_t chunk = kMaxBlocks * kThreads * ept;        // elements per launch
-    for (int64_t off = 0; off < n; off += chunk) {
-        const int64_t len = n - off < chunk ? n - off : chunk;
-        int64_t blocks = blocks_for(len / ept + (len % ept ? 1 : 0));
-        if (kPersistPerCu > 0) {
-            const int64_t cap = static_cast<int64_t>(kPersistPerCu) * zero::device_cu_count();
-            if (blocks > cap) blocks = cap;
-        }
-        if (vec)
-            hipLaunchKernelGGL(adamw_kernel<kEpt>, dim3(static_cast<unsigned>(blocks)),
-                               dim3(kThreads), 0, stream, master + off, exp_avg + off,
-                               exp_avg_sq + off, grad + off, param_out + off, len, c, clip_scale);
-        else
-            hipLaunchKernelGGL(adamw_kernel<1>, dim3(static_cast<unsigned>(blocks)),
-                               dim3(kThreads), 0, stream, master + off, exp_avg + off,
-                               exp_avg_sq + off, grad + off, param_out + off, len, c, clip_scale);
-        st = zero::check_hip(hipGetLastError(), "zero_shard_adamw_step launch");
-        if (st != ZERO_OK) return st;
+    int64_t blocks = blocks_for(n / ept + (n % ept ? 1 : 0));
+    if (kPersistPerCu > 0) {
+        const int64_t cap = static_cast<int64_t>(kPersistPerCu) * zero::device_cu_count();
+        if (blocks > cap) blocks = cap;
     }
-    return ZERO_OK;
+    const int64_t rows = (blocks + kMaxRow - 1) / kMaxRow;
+    if (rows > 0x7FFFFFFF)
+        return fail(ZERO_ERANGE, "zero_shard_adamw_step: n too large for one dispatch");
+    const dim3 grid(static_cast<unsigned>((blocks + rows - 1) / rows), static_cast<unsigned>(rows));
+    if (vec)
+        hipLaunchKernelGGL(adamw_kernel<kEpt>, grid, dim3(kThreads), 0, stream, master, exp_avg,
+                           exp_avg_sq, grad, param_out, n, c, clip_scale);
+    else
+        hipLaunchKernelGGL(adamw_kernel<1>, grid, dim3(kThreads), 0, stream, master, exp_avg,
+                           exp_avg_sq, grad, param_out, n, c, clip_scale);
+    return zero::check_hip(hipGetLastError(), "zero_shard_adamw_step launch");
 }
 
 extern "C" zero_status zero_multi_tensor_adamw_step(float* const* masters, float* const* exp_avgs,
