@@ -33,11 +33,6 @@ void clear_error();
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
-// Workgroups of `kernel` (at `threads` per workgroup, no dynamic LDS) that fit on
-// the whole current device at once: CU count times the occupancy limit from
-// registers and LDS. Falls back to 4 per CU if the query fails.
-int device_resident_blocks(const void* kernel, int threads);
-
 // Device-resident tables (multi-tensor AdamW, gather/flatten copies) hold one
 // descriptor index per workgroup. The dispatcher deals a launch's workgroups
 // round-robin to the 8 XCDs, so the index is stored XCD-major within each

@@ -42,14 +42,6 @@ int device_cu_count() {
     return cache[dev];
 }
 
-int device_resident_blocks(const void* kernel, int threads) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
-        per_cu <= 0)
-        per_cu = 4;
-    return per_cu * device_cu_count();
-}
-
 }  // namespace zero
 
 extern "C" const char* zero_status_string(zero_status status) {
