@@ -79,10 +79,31 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int E> struct Lane;   // one lane's elements and their access widths
 
+// Addressing of the one-element lanes: 0 (default) gives each access its own
+// 64-bit address; 1 addresses every array through the wave's first element (a
+// wave-uniform base) plus the lane's distance from it, shared by the 8 accesses.
+#ifndef ZERO_ADAMW_WAVE_BASE
+#define ZERO_ADAMW_WAVE_BASE 0
+#endif
+
 template <> struct Lane<1> {
     static __device__ __forceinline__ void update(float* P, float* M, float* V, const uint16_t* G,
                                                   uint16_t* O, int64_t i, float clip,
                                                   const AdamScalars& c) {
+#if ZERO_ADAMW_WAVE_BASE
+        // Active lanes of a wave hold consecutive i, so i - w0 < 64.
+        const int64_t w0 = zero::dev::first_lane(i);
+        const uint32_t d = static_cast<uint32_t>(i - w0);
+        float p = __builtin_bit_cast(float, zero::dev::ld_stream_at_b32(P + w0, d * 4));
+        float m = __builtin_bit_cast(float, zero::dev::ld_stream_at_b32(M + w0, d * 4));
+        float v = __builtin_bit_cast(float, zero::dev::ld_stream_at_b32(V + w0, d * 4));
+        const uint16_t g = zero::dev::ld_stream_at_b16(G + w0, d * 2);
+        adam_elem(p, m, v, zero::dev::bf16_to_f32(g) * clip, c);
+        zero::dev::st_stream_at(P + w0, d * 4, p);
+        zero::dev::st_stream_at(M + w0, d * 4, m);
+        zero::dev::st_stream_at(V + w0, d * 4, v);
+        zero::dev::st_stream_at(O + w0, d * 2, static_cast<uint16_t>(zero::dev::f32_to_bf16(p)));
+#else
         float p = zero::dev::ld_stream(P + i);
         float m = zero::dev::ld_stream(M + i);
         float v = zero::dev::ld_stream(V + i);
@@ -92,6 +113,7 @@ template <> struct Lane<1> {
         zero::dev::st_stream(M + i, m);
         zero::dev::st_stream(V + i, v);
         zero::dev::st_stream(O + i, static_cast<uint16_t>(zero::dev::f32_to_bf16(p)));
+#endif
     }
 };
 

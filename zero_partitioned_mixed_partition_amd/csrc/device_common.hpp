@@ -154,6 +154,28 @@ __device__ __forceinline__ void st_stream_any(T* p, const T& v) {
     __builtin_nontemporal_store(v, p);
 }
 
+// Loads through a wave-uniform base (the counterpart of st_stream_at): `base`
+// the same in every lane, `off` the lane's byte offset from it (below 2^32);
+// non-temporal as ld_stream.
+#if ZERO_NT_LOADS
+constexpr int kLoadCpol = 0x2;                // nt
+#else
+constexpr int kLoadCpol = 0;
+#endif
+__device__ __forceinline__ uint32_t ld_stream_at_b32(const void* base, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(through_rsrc(base), off, 0, kLoadCpol);
+}
+__device__ __forceinline__ uint16_t ld_stream_at_b16(const void* base, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(through_rsrc(base), off, 0, kLoadCpol);
+}
+
+// The first active lane's value of a 64-bit quantity (wave-uniform).
+__device__ __forceinline__ int64_t first_lane(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Entry of workgroup blockIdx.x in a launch's XCD-major table index (the
 // layout is described with xcd_major_index on the host side).
 __device__ __forceinline__ int64_t xcd_major_entry(int64_t blk0, int64_t per) {
