@@ -46,7 +46,6 @@ from __future__ import annotations
 import argparse
 import gc
 import json
-import math
 import os
 import sys
 import time
@@ -190,20 +189,37 @@ class RankWorkload:
         else:
             synth.device_normal_bf16(rs.grad, self.seed, synth.KIND_GRAD, 1, 0, lo, phi,
                                      synth.GRAD_SIGMA)
-        # the other ranks' squared-norm partials
+        # the other ranks' squared-norm partials, each from its own gradient as the
+        # configuration produces it: the reduce of the same replicas, the reduce of
+        # its bucket windows of generated replicas, or (gradients that arrive
+        # averaged) the norm of its generated averaged gradient
         parts = torch.zeros(nd, dtype=torch.float64, device=device)
         tmp = torch.empty(S, dtype=torch.int16, device=device)
+        bucket_reps = staggered_replicas(reps, bucket, device) if reps and bucket else None
+        win_part = torch.zeros(1, dtype=torch.float64, device=device)
         for r in range(nd):
             if r == rank:
                 continue
-            if reps and not bucket:          # their reduce over the same replicas
+            if reps and not bucket:
                 zm.zero_grad_reduce_shard(self.plan, r, self.windows[0][2], 0, P, tmp,
                                           sqnorm_out=parts[r:r + 1], workspace=rs.workspace)
-            else:                            # their averaged gradients, drawn directly
-                sigma = synth.GRAD_SIGMA / math.sqrt(reps) if reps else synth.GRAD_SIGMA
-                synth.device_normal_bf16(tmp, self.seed, synth.KIND_GRAD, 1, 0, r * S, phi, sigma)
+            elif reps:
+                total = 0.0                  # the window partials, summed in arrival order
+                for b0, cnt in bucket_windows(P, bucket, r * S, (r + 1) * S):
+                    a, e = max(b0, r * S), min(b0 + cnt, (r + 1) * S)
+                    for k, t in enumerate(bucket_reps):
+                        synth.device_normal_bf16(t, self.seed, synth.KIND_REPLICA, 1, k, a, phi,
+                                                 synth.GRAD_SIGMA, n=e - a)
+                    zm.zero_grad_reduce_shard(self.plan, r, [t[:e - a] for t in bucket_reps], a,
+                                              e - a, tmp, sqnorm_out=win_part,
+                                              workspace=rs.workspace)
+                    total += float(win_part.item())
+                parts[r] = total
+            else:
+                synth.device_normal_bf16(tmp, self.seed, synth.KIND_GRAD, 1, 0, r * S, phi,
+                                         synth.GRAD_SIGMA)
                 zm.zero_grad_sqnorm(tmp, parts[r:r + 1], workspace=rs.workspace)
-        del tmp
+        del tmp, bucket_reps
         rs.partials[:nd].copy_(parts)
         torch.cuda.synchronize()
         if reps:
