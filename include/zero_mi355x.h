@@ -210,7 +210,8 @@ zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
  * library's load until the process ends. The call allocates nothing: no
  * hipMalloc, no hipFree, no allocating library routine. The first call on a
  * device looks up that device's copy of the array (hipGetSymbolAddress) with
- * the device current. The bf16 output is zero_grad_reduce_shard's. The norm
+ * the device current; a caller that captures graphs makes that first call
+ * before capturing. The bf16 output is zero_grad_reduce_shard's. The norm
  * equals zero_grad_reduce_shard's with a workspace of
  * ZERO_NOALLOC_SCRATCH_BYTES bytes: windows of 2^24 elements or more whose
  * one-pass partials fit the array (up to about 2.7e8 elements) take the
