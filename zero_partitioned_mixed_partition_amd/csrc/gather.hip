@@ -28,6 +28,7 @@
 // does both once, at creation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <new>
 #include <string>
 #include <vector>
@@ -453,7 +454,19 @@ zero_status make_copy_table(const std::vector<Piece>& pieces, zero_copy_table** 
     zero_copy_table* tab = nullptr;
     try {
         int64_t blocks = 0;
-        const zero_status cs = zero::copy::copy_table_contents(pieces, kChunk, &descs, &index, &blocks, who);
+        // Piece order in the table, so in dispatch order: 0 (default) the plan's flat
+        // order (the source shards front to back); 1 by destination address.
+#ifndef ZERO_TABLE_BY_DESTINATION
+#define ZERO_TABLE_BY_DESTINATION 0
+#endif
+        std::vector<Piece> ordered;
+        if (ZERO_TABLE_BY_DESTINATION) {
+            ordered = pieces;
+            std::stable_sort(ordered.begin(), ordered.end(),
+                             [](const Piece& a, const Piece& b) { return a.dst < b.dst; });
+        }
+        const zero_status cs = zero::copy::copy_table_contents(
+            ZERO_TABLE_BY_DESTINATION ? ordered : pieces, kChunk, &descs, &index, &blocks, who);
         if (cs != ZERO_OK) return cs;
         tab = new zero_copy_table;
         tab->blocks = blocks;

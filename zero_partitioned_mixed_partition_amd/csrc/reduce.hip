@@ -472,9 +472,24 @@ __global__ void clip_kernel(const double* __restrict__ partials, int n, double m
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Past the cap, 0 keeps the grid at the cap (the last pass of the grid-stride
+// loop then runs on a fraction of the lanes); 1 takes as many passes as the cap
+// needs and divides the work evenly over them (every lane the same number of
+// passes, within one).
+#ifndef ZERO_REDUCE_BALANCED
+#define ZERO_REDUCE_BALANCED 0
+#endif
+
 int grid_for(int64_t work_items, int cap) {
     int64_t blocks = (work_items + kThreads - 1) / kThreads;
-    if (blocks > cap) blocks = cap;
+    if (blocks > cap) {
+        if (ZERO_REDUCE_BALANCED) {
+            const int64_t passes = (blocks + cap - 1) / cap;
+            blocks = (blocks + passes - 1) / passes;
+        } else {
+            blocks = cap;
+        }
+    }
     if (blocks < 1) blocks = 1;
     return static_cast<int>(blocks);
 }
