@@ -19,6 +19,8 @@
  *                           (FSDP-2's per-parameter shards)
  *   zero_mt_table_*         the same list described once in device memory,
  *                           stepped in one launch
+ *   zero_reduce_adamw_step  the reduce and the update in one pass, for a step
+ *                           with no global norm between them
  *   zero_gather_params      bf16 shards back to per-tensor parameters
  *                           (all-gather output layout, then un-flatten)
  *   zero_flatten_params     per-tensor bf16 buffers into the padded flat buffer
@@ -295,6 +297,37 @@ zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_
                                   int64_t step, double lr, double beta1, double beta2, double eps,
                                   double weight_decay, const float* clip_scale,
                                   hipStream_t stream);
+
+/* Reduce and update in one pass. [ZF] "Execution Flow for ZeRO-1", steps 2-3:
+ * the rank receives the averaged gradient of its slice and updates its master
+ * weights and optimizer state from it. When the step needs no global norm
+ * between the two (no clipping, or a clip coefficient the caller already
+ * holds), they run as one pass over the rank's window: for every element of
+ * [begin, begin + count) within the rank's shard, the averaged gradient is
+ * zero_grad_reduce_shard's (fp32 sum in replica order, one fp32 division by
+ * R, bf16 round-to-nearest-even) and the update zero_shard_adamw_step's on
+ * it, bit for bit the two calls in sequence, without the gradient's round trip
+ * through HBM (2R + 26 bytes per element instead of 2R + 30).
+ * plan, rank, replicas, n_replicas, begin, count: as zero_grad_reduce_shard.
+ * master, exp_avg, exp_avg_sq  device [S] fp32, the rank's shard state, in place.
+ * param_out    device [S] bf16, the rank's parameter shard; must not overlap
+ *              the fp32 arrays. Element i of these arrays is global element
+ *              rank*S + i; only the window's part of the shard is read and written.
+ * shard_grad   device [S] bf16, nullable: when given, also receives the
+ *              averaged gradient, as zero_grad_reduce_shard writes it.
+ * step, lr, beta1, beta2, eps, weight_decay, clip_scale: as
+ *              zero_shard_adamw_step; a non-finite coefficient skips the
+ *              update (shard_grad, when given, is still written).
+ * Errors: ZERO_EINVAL (null plan or replicas, a null replica or state array
+ * for a non-empty window, R or rank out of range, bad window, bad
+ * hyperparameters, param_out overlapping the state); ZERO_EHIP. */
+zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t rank,
+                                   const uint16_t* const* replicas, int32_t n_replicas,
+                                   int64_t begin, int64_t count, float* master, float* exp_avg,
+                                   float* exp_avg_sq, uint16_t* param_out, uint16_t* shard_grad,
+                                   int64_t step, double lr, double beta1, double beta2, double eps,
+                                   double weight_decay, const float* clip_scale,
+                                   hipStream_t stream);
 
 /* Multi-tensor form. [ZF] "FSDP-2: Per-Parameter Sharding via DTensor
  * (fully_shard)": each parameter keeps its own local shard, so the rank's

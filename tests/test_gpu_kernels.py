@@ -842,3 +842,77 @@ def test_copy_tables_equal_the_calls_on_gpt2_small_and_skip_null_shards(zm, kind
     zm.CopyTable.gather(plan, skip, d).run()
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(c, d))
+
+
+# ----------------------------------------------------------------------------- reduce + AdamW
+
+@pytest.mark.parametrize("case", ["full-window", "nine-replicas-window", "sixty-four", "unaligned",
+                                  "skip"])
+def test_reduce_adamw_one_pass_matches_the_two_calls_and_the_oracle(zm, case):
+    """zero_reduce_adamw_step against zero_grad_reduce_shard followed by
+    zero_shard_adamw_step on the GPU, and against the oracle's reduce then AdamW,
+    bit for bit, over three steps: the averaged gradient (when asked for), the
+    fp32 state and the bf16 parameters; elements of the shard outside the window
+    stay as they were. [ZF] "Execution Flow for ZeRO-1", steps 2-3."""
+    numels, n_ranks, rank, R = [100_000, 77_777, 5], 4, 1, 3
+    begin_off, count_cut, clip, with_grad = 0, 0, 0.37, True
+    if case == "nine-replicas-window":
+        R, begin_off, count_cut, clip, with_grad = 9, 20_001, 13_337, None, False
+    elif case == "sixty-four":
+        R = 64
+    elif case == "unaligned":
+        begin_off, count_cut = 3, 1
+    elif case == "skip":
+        clip = float("nan")
+    ref = oracle.partition_plan(numels, n_ranks, 128)
+    plan = zm.zero_partition_plan(numels, n_ranks, 128)
+    P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
+    lo_s = rank * S
+    begin = lo_s + begin_off - 7 if begin_off else 0        # windows that start before the shard too
+    count = (lo_s + S - count_cut) - begin if count_cut else P - begin
+    note(f"reduce+adamw {case}: R={R} window [{begin},{begin + count}) shard [{lo_s},{lo_s + S})")
+    master = synth.normal_f32(S, 31, synth.KIND_MASTER, 0, 0, lo_s, phi, 0.02)
+    d = {}
+    for way in ("fused", "calls"):
+        d[way] = dict(p=to_dev_f32(master), m=torch.zeros(S, dtype=torch.float32, device=dev()),
+                      v=torch.zeros(S, dtype=torch.float32, device=dev()),
+                      o=torch.full((S,), 0x2222, dtype=torch.int16, device=dev()),
+                      g=torch.full((S,), 0x1111, dtype=torch.int16, device=dev()))
+    scale = None if clip is None else torch.tensor([clip], dtype=torch.float32, device=dev())
+    st = {"p": master.copy(), "m": np.zeros(S, np.float32), "v": np.zeros(S, np.float32),
+          "o": np.full(S, 0x2222, np.uint16), "g": np.full(S, 0x1111, np.uint16)}
+    a, b = max(begin, lo_s) - lo_s, min(begin + count, lo_s + S) - lo_s
+    for t in (1, 2, 3):
+        reps_h = [synth.normal_bf16(count, 31, synth.KIND_REPLICA, t, k, begin, phi, 0.05)
+                  for k in range(R)]
+        reps = [to_dev_u16(x) for x in reps_h]
+        f, c = d["fused"], d["calls"]
+        zm.zero_reduce_adamw_step(plan, rank, reps, begin, count, f["p"], f["m"], f["v"], f["o"], t,
+                                  clip_scale=scale, shard_grad=f["g"] if with_grad else None, **HP)
+        zm.zero_grad_reduce_shard(plan, rank, reps, begin, count, c["g"])
+        zm.zero_shard_adamw_step(c["p"][a:b], c["m"][a:b], c["v"][a:b], c["g"][a:b], c["o"][a:b], t,
+                                 clip_scale=scale, **HP)
+        g = st["g"].copy()
+        oracle.reduce_shard(ref, rank, reps_h, begin, g)
+        P1, M1, V1, B1 = oracle.adamw_step(st["p"][a:b], st["m"][a:b], st["v"][a:b], g[a:b], t,
+                                           clip=1.0 if clip is None else clip, **HP)
+        st["g"] = g
+        st["p"][a:b], st["m"][a:b], st["v"][a:b] = P1, M1, V1
+        if B1 is not None:
+            st["o"][a:b] = B1
+    torch.cuda.synchronize()
+    f, c = d["fused"], d["calls"]
+    for key, what in (("p", "master"), ("m", "exp_avg"), ("v", "exp_avg_sq")):
+        assert_bits_equal(host_f32(f[key]).view(np.uint32), host_f32(c[key]).view(np.uint32),
+                          f"{what}: one pass against the two calls")
+        assert_bits_equal(host_f32(f[key]).view(np.uint32), st[key].view(np.uint32),
+                          f"{what}: one pass against the oracle")
+    assert_bits_equal(host_u16(f["o"]), host_u16(c["o"]), "param: one pass against the two calls")
+    assert_bits_equal(host_u16(f["o"]), st["o"], "param: one pass against the oracle")
+    if with_grad:
+        assert_bits_equal(host_u16(f["g"]), st["g"], "averaged gradient against the oracle")
+    else:
+        assert (host_u16(f["g"]) == 0x1111).all(), "no gradient written when none is asked for"
+    if case == "skip":
+        assert_bits_equal(host_f32(f["p"]).view(np.uint32), master.view(np.uint32), "skipped: master")
+        assert (host_u16(f["o"]) == 0x2222).all(), "skipped: param untouched"

@@ -136,18 +136,22 @@ def _windows_in_shards(points, half, S, n_ranks, total):
     return [(a, b) for a, b in out if b > a]
 
 
-def test_gpt_1p3b_all_ranks_reduce_adamw_gather(zm):
+@pytest.mark.parametrize("way", ["two-calls", "one-pass"])
+def test_gpt_1p3b_all_ranks_reduce_adamw_gather(zm, way):
     """Full arrays: every rank's reduced gradient, fp32 state and bf16 parameters
     against the oracle, bit for bit (the oracle runs 2^23-element windows across
     a process pool and returns digests of each array), every rank's exact
-    squared-norm partial, and the gathered tensors against the parameters."""
+    squared-norm partial, and the gathered tensors against the parameters. The
+    step runs as the reduce (one-pass kernel, fused norm) then AdamW, or as the
+    one-pass reduce-and-update (zero_reduce_adamw_step, writing the gradient too;
+    the norm then by zero_grad_sqnorm on it): the configuration has no clip."""
     from oracle_workers import digest, reduce_adamw_digests
     w = synth.WORKLOADS["gpt-1.3b"]
     R = w.replicas
     ref = oracle.partition_plan(w.numels, w.n_ranks, w.align)
     plan = zm.zero_partition_plan(w.numels, w.n_ranks, w.align)
     P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
-    note(f"gpt-1.3b: P={P} S={S} T={len(w.numels)}, {R} replicas")
+    note(f"gpt-1.3b ({way}): P={P} S={S} T={len(w.numels)}, {R} replicas")
     reps = []
     for k in range(R):
         t = torch.empty(P, dtype=torch.int16, device=dev())
@@ -163,9 +167,14 @@ def test_gpt_1p3b_all_ranks_reduce_adamw_gather(zm):
     ws = zm.reduce_workspace(S, dev())       # the benchmark's path: the one-pass reduce
     for r in range(w.n_ranks):
         sl = slice(r * S, (r + 1) * S)
-        zm.zero_grad_reduce_shard(plan, r, reps, 0, P, grad[sl], sqnorm_out=parts[r:r + 1],
-                                  workspace=ws)
-        zm.zero_shard_adamw_step(master[sl], m[sl], v[sl], grad[sl], param[sl], 1, **HP)
+        if way == "two-calls":
+            zm.zero_grad_reduce_shard(plan, r, reps, 0, P, grad[sl], sqnorm_out=parts[r:r + 1],
+                                      workspace=ws)
+            zm.zero_shard_adamw_step(master[sl], m[sl], v[sl], grad[sl], param[sl], 1, **HP)
+        else:
+            zm.zero_reduce_adamw_step(plan, r, reps, 0, P, master[sl], m[sl], v[sl], param[sl], 1,
+                                      shard_grad=grad[sl], **HP)
+            zm.zero_grad_sqnorm(grad[sl], parts[r:r + 1], workspace=ws)
     tensors = [torch.empty(n, dtype=torch.int16, device=dev()) for n in w.numels]
     zm.zero_gather_params(plan, [param[r * S:(r + 1) * S] for r in range(w.n_ranks)], tensors)
     torch.cuda.synchronize()

@@ -33,6 +33,7 @@ from ._binding import (LIB_PATH, ZERO_MAX_REPLICAS, CopyTable, MultiTensorTable,
                        ZeroError, reduce_workspace, zero_reduce_workspace_bytes,
                        sqnorm_workspace, zero_clip_scale, zero_flatten_params, zero_gather_params,
                        zero_grad_reduce_shard, zero_grad_reduce_shard_noalloc,
+                       zero_reduce_adamw_step,
                        ZERO_NOALLOC_SCRATCH_BYTES,
                        zero_grad_sqnorm, zero_last_error, zero_partition_plan,
                        zero_partition_plan_shard0, zero_host_adamw_step, zero_offload_adamw_step,

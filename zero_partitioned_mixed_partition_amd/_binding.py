@@ -71,6 +71,9 @@ _clip = _fn("zero_clip_scale", c_i32, [c_vp, c_i32, c_dbl, c_vp, c_vp])
 _adamw = _fn("zero_shard_adamw_step", c_i32,
              [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl, c_vp,
               c_vp])
+_reduce_adamw = _fn("zero_reduce_adamw_step", c_i32,
+                    [c_vp, c_i32, ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
+                     c_vp, c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl, c_vp, c_vp])
 _gather = _fn("zero_gather_params", c_i32, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_vp])
 _flatten = _fn("zero_flatten_params", c_i32, [c_vp, ctypes.POINTER(c_vp), c_vp, c_vp])
 _host_adamw = _fn("zero_host_adamw_step", c_i32,
@@ -355,6 +358,42 @@ def zero_shard_adamw_step(master, exp_avg, exp_avg_sq, grad, param_out, step: in
                   _ptr(param_out, 2, "param_out"), n, step, lr, beta1, beta2, eps, weight_decay,
                   _ptr(clip_scale, 4, "clip_scale"), _stream(stream, master)),
            "zero_shard_adamw_step")
+
+
+def prepare_reduce_adamw_step(plan: Plan, rank: int, replicas: Sequence, begin: int, count: int,
+                              master, exp_avg, exp_avg_sq, param_out, lr: float, beta1: float,
+                              beta2: float, eps: float, weight_decay: float, clip_scale=None,
+                              shard_grad=None, stream=None) -> "Prepared":
+    """zero_reduce_adamw_step with its arguments marshalled once; call the result
+    with the 1-based step number. The state arrays are the rank's shard ([S])."""
+    S = plan.shard_numel
+    for r in replicas:
+        _need(r, count, "a replica")
+    for t, what in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"),
+                    (param_out, "param_out")):
+        _need(t, S, what)
+    _need(shard_grad, S, "shard_grad")
+    _need(clip_scale, 1, "clip_scale")
+    ptrs = (c_vp * max(len(replicas), 1))(*[_ptr(r, 2, "replica") for r in replicas])
+    p = Prepared(_reduce_adamw, [plan.handle, rank, ptrs, len(replicas), begin, count,
+                                 _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                                 _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"),
+                                 _ptr(shard_grad, 2, "shard_grad"), 1, lr, beta1, beta2, eps,
+                                 weight_decay, _ptr(clip_scale, 4, "clip_scale"),
+                                 _stream(stream, master)], "zero_reduce_adamw_step", step_index=11)
+    p._keep = (ptrs, replicas, master, exp_avg, exp_avg_sq, param_out, shard_grad, clip_scale)
+    return p
+
+
+def zero_reduce_adamw_step(plan: Plan, rank: int, replicas: Sequence, begin: int, count: int,
+                           master, exp_avg, exp_avg_sq, param_out, step: int, lr: float,
+                           beta1: float, beta2: float, eps: float, weight_decay: float,
+                           clip_scale=None, shard_grad=None, stream=None) -> None:
+    """The rank's averaged gradient and its AdamW update in one pass (no global
+    norm between them): the bits of zero_grad_reduce_shard then zero_shard_adamw_step."""
+    prepare_reduce_adamw_step(plan, rank, replicas, begin, count, master, exp_avg, exp_avg_sq,
+                              param_out, lr, beta1, beta2, eps, weight_decay, clip_scale, shard_grad,
+                              stream)(step)
 
 
 def zero_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, stream=None) -> None:

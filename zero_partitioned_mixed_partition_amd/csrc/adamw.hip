@@ -310,6 +310,61 @@ __global__ __launch_bounds__(kThreads) void adamw_table_kernel(const MtDesc* __r
               clip_scale);
 }
 
+// Reduce and update in one pass, for a step whose clip coefficient is known
+// before the update (no clipping, or a coefficient the caller has): lane e
+// averages element e of the R replicas exactly as the reduce does (an fp32 sum
+// in replica order, one fp32 division by R, one rounding to bf16), optionally
+// stores that bf16 gradient, and updates element e of the shard with
+// adam_elem. The averaged gradient never goes through HBM: per element 2R + 24
+// + 2 bytes instead of the reduce's 2R + 2 plus AdamW's 28. One element per
+// lane (2-byte replica loads, 4-byte state accesses) in a one-pass grid of
+// rows, as the flat AdamW; replicas are loaded 8 at a time.
+struct FusedReplicas {
+    const uint16_t* p[ZERO_MAX_REPLICAS];
+};
+constexpr int kFusedBatch = 8;
+
+__global__ __launch_bounds__(kThreads) void reduce_adamw_kernel(FusedReplicas reps, int n_rep,
+                                                                int64_t src_off,
+                                                                float* __restrict__ master,
+                                                                float* __restrict__ m,
+                                                                float* __restrict__ v,
+                                                                uint16_t* __restrict__ param,
+                                                                uint16_t* __restrict__ grad_out,
+                                                                int64_t n, AdamScalars c,
+                                                                const float* __restrict__ clip_scale) {
+    const int64_t blk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+    const int64_t i = blk * kThreads + threadIdx.x;
+    if (i >= n) return;
+    const float clip = read_clip(clip_scale);
+    const bool update = isfinite(clip);
+    float p = 0.0f, mm = 0.0f, vv = 0.0f;
+    if (update) {                                // state loads in flight beside the replicas'
+        p = zero::dev::ld_stream(master + i);
+        mm = zero::dev::ld_stream(m + i);
+        vv = zero::dev::ld_stream(v + i);
+    }
+    float acc = 0.0f;
+    for (int k0 = 0; k0 < n_rep; k0 += kFusedBatch) {
+        uint16_t x[kFusedBatch];
+        const int kn = n_rep - k0 < kFusedBatch ? n_rep - k0 : kFusedBatch;
+#pragma unroll
+        for (int k = 0; k < kFusedBatch; ++k)
+            if (k < kn) x[k] = zero::dev::ld_stream(reps.p[k0 + k] + src_off + i);
+#pragma unroll
+        for (int k = 0; k < kFusedBatch; ++k)
+            if (k < kn) acc = acc + zero::dev::bf16_to_f32(x[k]);
+    }
+    const uint16_t g = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / static_cast<float>(n_rep)));
+    if (grad_out != nullptr) zero::dev::st_stream(grad_out + i, g);
+    if (!update) return;
+    adam_elem(p, mm, vv, zero::dev::bf16_to_f32(g) * clip, c);
+    zero::dev::st_stream(master + i, p);
+    zero::dev::st_stream(m + i, mm);
+    zero::dev::st_stream(v + i, vv);
+    zero::dev::st_stream(param + i, static_cast<uint16_t>(zero::dev::f32_to_bf16(p)));
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool ranges_overlap(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
@@ -620,4 +675,57 @@ extern "C" zero_status zero_mt_table_adamw_step(const zero_mt_table* table, int6
         if (st != ZERO_OK) return st;
     }
     return ZERO_OK;
+}
+
+extern "C" zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t rank,
+                                              const uint16_t* const* replicas, int32_t n_replicas,
+                                              int64_t begin, int64_t count, float* master,
+                                              float* exp_avg, float* exp_avg_sq, uint16_t* param_out,
+                                              uint16_t* shard_grad, int64_t step, double lr,
+                                              double beta1, double beta2, double eps,
+                                              double weight_decay, const float* clip_scale,
+                                              hipStream_t stream) {
+    using zero::fail;
+    static const char* const who = "zero_reduce_adamw_step";
+    zero::clear_error();
+    if (plan == nullptr || replicas == nullptr)
+        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: NULL plan or replicas");
+    if (rank < 0 || rank >= plan->n_ranks)
+        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: rank out of range");
+    if (n_replicas < 1 || n_replicas > ZERO_MAX_REPLICAS)
+        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: n_replicas must be 1.." +
+                                     std::to_string(ZERO_MAX_REPLICAS));
+    if (begin < 0 || count < 0 || begin > plan->padded || count > plan->padded - begin)
+        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: window outside [0, P)");
+    zero_status st = check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
+    if (st != ZERO_OK) return st;
+    const int64_t shard_lo = static_cast<int64_t>(rank) * plan->shard;
+    const int64_t lo = begin > shard_lo ? begin : shard_lo;
+    const int64_t end = begin + count, shard_hi = shard_lo + plan->shard;
+    const int64_t hi = end < shard_hi ? end : shard_hi;
+    if (lo >= hi) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !param_out)
+        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: NULL state array");
+    FusedReplicas table{};
+    for (int32_t k = 0; k < n_replicas; ++k) {
+        if (replicas[k] == nullptr) return fail(ZERO_EINVAL, "zero_reduce_adamw_step: NULL replica");
+        table.p[k] = replicas[k];
+    }
+    const int64_t n = hi - lo, src_off = lo - begin, at = lo - shard_lo;
+    const size_t fbytes = static_cast<size_t>(n) * 4, hbytes = static_cast<size_t>(n) * 2;
+    if (ranges_overlap(param_out + at, hbytes, master + at, fbytes) ||
+        ranges_overlap(param_out + at, hbytes, exp_avg + at, fbytes) ||
+        ranges_overlap(param_out + at, hbytes, exp_avg_sq + at, fbytes))
+        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: param_out overlaps the fp32 state");
+    AdamScalars c;
+    st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
+    if (st != ZERO_OK) return st;
+    constexpr int64_t kMaxRow = (int64_t(1) << 32) / kThreads - 1;
+    const int64_t blocks = blocks_for(n);
+    const int64_t rows = (blocks + kMaxRow - 1) / kMaxRow;
+    const dim3 grid(static_cast<unsigned>((blocks + rows - 1) / rows), static_cast<unsigned>(rows));
+    hipLaunchKernelGGL(reduce_adamw_kernel, grid, dim3(kThreads), 0, stream, table, n_replicas,
+                       src_off, master + at, exp_avg + at, exp_avg_sq + at, param_out + at,
+                       shard_grad != nullptr ? shard_grad + at : nullptr, n, c, clip_scale);
+    return zero::check_hip(hipGetLastError(), "zero_reduce_adamw_step launch");
 }
