@@ -20,6 +20,8 @@ Other workloads (`--workload`), each timed as its own configuration states:
               into the 125,472,896-element shard, clip 1.0, AdamW
   gpt-1.3b    all 8 ranks of the 1.3B GPT list: 8 replicas reduced for every
               rank, AdamW on every shard, gather to 292 tensors
+  gpt-1.3b-fused  the same with each rank's reduce and AdamW in one pass
+              (zero_reduce_adamw_step: no global norm or clip between them)
   gpt2-small-fsdp2  the gpt2-small step on FSDP-2's per-parameter Shard(0) layout
               (every tensor cut along dim 0; a rank's chunks in one coalesced
               buffer); the replicas are per-tensor gradients flattened into it
@@ -56,8 +58,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 METRIC = "shard AdamW step: params/sec and achieved HBM GB/s (% of MI355X peak)"
-WORKLOAD_NAMES = ["gpt2-small", "llama3-8b", "llama3-70b", "gpt-1.3b", "gpt2-small-fsdp2",
-                  "gpt2-small-offload", "gpt2-small-fsdp2-pertensor"]
+WORKLOAD_NAMES = ["gpt2-small", "llama3-8b", "llama3-70b", "gpt-1.3b", "gpt-1.3b-fused",
+                  "gpt2-small-fsdp2", "gpt2-small-offload", "gpt2-small-fsdp2-pertensor"]
 PCIE_PEAK_GBS = 128.0          # PCIe 5.0 x16, both directions together (64 GB/s each way)
 OFFLOAD_CHUNK = 1 << 21        # elements per staging slot of the offload pipeline
 
@@ -87,7 +89,7 @@ def parse_args(argv=None):
 
 
 DEFAULT_STEPS = {"gpt2-small": (200, 20), "llama3-8b": (20, 3), "llama3-70b": (5, 1),
-                 "gpt-1.3b": (10, 2), "gpt2-small-fsdp2": (200, 20),
+                 "gpt-1.3b": (10, 2), "gpt-1.3b-fused": (10, 2), "gpt2-small-fsdp2": (200, 20),
                  "gpt2-small-offload": (30, 3), "gpt2-small-fsdp2-pertensor": (200, 20)}
 
 
@@ -386,7 +388,9 @@ class AllRanksWorkload:
         from zero_partitioned_mixed_partition_amd.step import (Hyper, _staggered_arena, plan_numels,
                                                                staggered_replicas)
 
-        w = synth.WORKLOADS[name]
+        # "-fused": each rank's reduce and AdamW in one pass (no clip between them)
+        self.fused = name.endswith("-fused")
+        w = synth.WORKLOADS[name[:-len("-fused")] if self.fused else name]
         self.name, self.workload, self.device = name, w, device
         self.n_ranks, self.rank, self.replicas = w.n_ranks, None, w.replicas
         self.seed = 1000 + w.seed
@@ -450,19 +454,38 @@ class AllRanksWorkload:
                 f(self.t)
 
         self.phases = [("reduce", reduce_all), ("adamw", adamw_all), ("gather", self._gather)]
+        # AdamW-phase bytes per element and the kernel that phase runs
+        self.adamw_bpe, self.adamw_kernel = 28, "adamw_kernel"
+        if self.fused:
+            self._fused = [zb.prepare_reduce_adamw_step(
+                self.plan, r, self.reps, 0, P, self.master[sl[r]], self.m[sl[r]], self.v[sl[r]],
+                self.param[sl[r]], clip_scale=None, stream=st, **self.hyper.as_kwargs())
+                for r in range(w.n_ranks)]
+
+            def fused_all():
+                self.t += 1
+                for f in self._fused:
+                    f(self.t)
+            self.phases = [("adamw", fused_all), ("gather", self._gather)]
+            # R bf16 replicas read, master/m/v read and written, bf16 parameter written
+            self.adamw_bpe, self.adamw_kernel = 2 * self.replicas + 26, "reduce_adamw_kernel"
         self.adamw_launches = w.n_ranks
         self.elems_per_step = P
 
     def bytes_per_phase(self):
         P = self.P
-        return {"reduce": (2 * self.replicas + 2) * P, "adamw": 28 * P, "gather": 4 * self.phi,
+        return {"reduce": (2 * self.replicas + 2) * P, "adamw": self.adamw_bpe * P,
+                "gather": 4 * self.phi,
                 "flatten": 4 * self.phi + 2 * (P - self.phi), "gather_call": 4 * self.phi,
                 "flatten_call": 4 * self.phi + 2 * (P - self.phi)}
 
     def describe(self):
+        update = (f"reduce of {self.replicas} bf16 replicas and AdamW in one pass per rank (no clip)"
+                  if self.fused else
+                  f"reduce of {self.replicas} bf16 replicas per rank + AdamW per shard")
         return (f"{self.workload.name} tensor list, N_d={self.n_ranks}, all {self.n_ranks} ranks in "
-                f"turn ({self.S} elements each); step = reduce of {self.replicas} bf16 replicas per "
-                f"rank + AdamW per shard + gather of {len(self.workload.numels)} tensors")
+                f"turn ({self.S} elements each); step = {update} + gather of "
+                f"{len(self.workload.numels)} tensors")
 
 
 def model_offsets(numels):
@@ -485,7 +508,8 @@ def padding_mask(plan, rank: int):
 
 
 def make_workload(name: str, device):
-    return AllRanksWorkload(name, device) if name == "gpt-1.3b" else RankWorkload(name, device)
+    return (AllRanksWorkload(name, device) if name.startswith("gpt-1.3b")
+            else RankWorkload(name, device))
 
 
 def run_step(wl) -> None:
@@ -605,7 +629,7 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(elems_per_launch: int):
+def measured_traffic(elems_per_launch: int, kernel: str = "adamw_kernel"):
     """HBM bytes per AdamW call from the committed counter runs (FETCH_SIZE and
     WRITE_SIZE, scaled by a 1 GiB copy, summed over the call's dispatches), or
     None when the kernel sources have changed since they were taken or no run
@@ -614,7 +638,8 @@ def measured_traffic(elems_per_launch: int):
         return None
     d = json.load(open(TRAFFIC_FILE))
     for e in d.get("runs", []):
-        if e.get("source_sha256") == kernel_source_digest() and e.get("elems") == elems_per_launch:
+        if (e.get("source_sha256") == kernel_source_digest() and e.get("elems") == elems_per_launch
+                and e.get("kernel", "adamw_kernel") == kernel):
             return e["bytes_per_launch"]
     return None
 
@@ -727,6 +752,7 @@ def cpu_baseline(wl, budget_s: float):
         per_step = S
     else:
         n = min(wl.S, 1 << 24)
+        fused = getattr(wl, "fused", False)
         g0 = (wl.rank or 0) * wl.S
         R = wl.replicas
         if R:
@@ -746,11 +772,13 @@ def cpu_baseline(wl, budget_s: float):
                 oracle.reduce_shard(window, 0, reps, 0, g)
             else:                   # gradients arrive averaged: no reduce in the step
                 g = reps[0]
-            clip = oracle.clip_scale([oracle.sqnorm(g)], 1.0)
+            # the one-pass workload updates with no clip between reduce and AdamW
+            clip = 1.0 if fused else oracle.clip_scale([oracle.sqnorm(g)], 1.0)
             st["p"], st["m"], st["v"], _ = oracle.adamw_step(st["p"], st["m"], st["v"], g, t,
                                                              clip=clip, **hp)
         work = f"reduce of {R} replica windows, " if R else ""
-        sample = (f"the per-element work of this workload ({work}exact norm, clip, AdamW) "
+        work += "AdamW" if fused else "exact norm, clip, AdamW"
+        sample = (f"the per-element work of this workload ({work}) "
                   f"on a {n}-element slice of the shard")
         per_step = n
     one(1)          # untimed: the first touch of fresh host pages is not oracle work
@@ -842,7 +870,8 @@ def also_line(name: str, device) -> dict:
     steps, warmup = DEFAULT_STEPS[name]
     m = measure(wl, steps, warmup)
     elems = m["elems_per_launch"]
-    gbs = 28 * elems / (m["adamw_ms"] * 1e-3) / 1e9
+    bpe, kern = getattr(wl, "adamw_bpe", 28), getattr(wl, "adamw_kernel", "adamw_kernel")
+    gbs = bpe * elems / (m["adamw_ms"] * 1e-3) / 1e9
     out = {"workload": wl.describe(), "steps": steps, "warmup": warmup,
            "ms_per_step": m["ms_per_step"], "value": wl.elems_per_step / (m["ms_per_step"] * 1e-3),
            "adamw_params_per_s": elems / (m["adamw_ms"] * 1e-3),
@@ -850,7 +879,7 @@ def also_line(name: str, device) -> dict:
                               "median": m["adamw_each"][len(m["adamw_each"]) // 2] * 1e3,
                               "min": m["adamw_each"][0] * 1e3, "launches": len(m["adamw_each"])},
            "adamw_hbm_gbs": gbs, "adamw_frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
-           "kernels": m["kernels"], "traffic": measured_traffic(elems)}
+           "kernels": m["kernels"], "traffic": measured_traffic(elems, kern)}
     del wl
     gc.collect()
     torch.cuda.synchronize()
@@ -898,7 +927,8 @@ def main(argv=None):
     ms_per_step, adamw_ms, adamw_each = m["ms_per_step"], m["adamw_ms"], m["adamw_each"]
     kernels, outside, bpp, flushed, parts = m["kernels"], m["outside"], m["bpp"], m["flushed"], m["parts"]
     elems_per_launch, offload = m["elems_per_launch"], m["offload"]
-    adamw_bytes = 28 * elems_per_launch
+    adamw_kernel = getattr(wl, "adamw_kernel", "adamw_kernel")
+    adamw_bytes = getattr(wl, "adamw_bpe", 28) * elems_per_launch
     adamw_gbs = adamw_bytes / (adamw_ms * 1e-3) / 1e9
     value = wl.elems_per_step / (ms_per_step * 1e-3)
 
@@ -929,9 +959,9 @@ def main(argv=None):
         "step_hbm_gbs": sum(bpp[n] for n, _ in wl.phases) / (ms_per_step * 1e-3) / 1e9,
         "kernels": kernels,
         "kernels_outside_step": outside,
-        "roofline": {"bound": "hbm", "kernel": "adamw_kernel", "achieved": adamw_gbs,
+        "roofline": {"bound": "hbm", "kernel": adamw_kernel, "achieved": adamw_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": adamw_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(elems_per_launch)},
+                     "traffic": measured_traffic(elems_per_launch, adamw_kernel)},
         "cpu_baseline": cpu,
     }
     also = args.also or []

@@ -345,16 +345,9 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_kernel(FusedReplicas re
         vv = zero::dev::ld_stream(v + i);
     }
     float acc = 0.0f;
-    for (int k0 = 0; k0 < n_rep; k0 += kFusedBatch) {
-        uint16_t x[kFusedBatch];
-        const int kn = n_rep - k0 < kFusedBatch ? n_rep - k0 : kFusedBatch;
-#pragma unroll
-        for (int k = 0; k < kFusedBatch; ++k)
-            if (k < kn) x[k] = zero::dev::ld_stream(reps.p[k0 + k] + src_off + i);
-#pragma unroll
-        for (int k = 0; k < kFusedBatch; ++k)
-            if (k < kn) acc = acc + zero::dev::bf16_to_f32(x[k]);
-    }
+    zero::dev::for_replicas<kFusedBatch, uint16_t>(reps.p, n_rep, src_off, i, [&](uint16_t x) {
+        acc = acc + zero::dev::bf16_to_f32(x);
+    });
     const uint16_t g = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / static_cast<float>(n_rep)));
     if (grad_out != nullptr) zero::dev::st_stream(grad_out + i, g);
     if (!update) return;

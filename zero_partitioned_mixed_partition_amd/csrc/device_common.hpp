@@ -209,5 +209,37 @@ __device__ __forceinline__ double block_sum(double x, double* lds) {
     return total;
 }
 
+// Visits R replicas' V-sized values at index i (V units past p[k] + src_off),
+// in replica order, with B loads in flight: each batch's loads are issued
+// together, unconditionally, before the first value is used. A batch of fewer
+// than B replicas (the last R mod B) loads the batch's first replica in place
+// of the missing ones and does not visit those copies. (A guarded load per
+// replica becomes a branch per load, and the compiler then waits for each load
+// before issuing the next: measured on MI355X, the one-pass reduce and AdamW
+// over 8 replicas of a 164 M-element shard ran at 46% of HBM peak that way
+// and at 81% with this form.) `p` is indexed with wave-uniform values only.
+template <int B, typename V, typename Visit>
+__device__ __forceinline__ void for_replicas(const uint16_t* const* p, int n_rep, int64_t src_off,
+                                             int64_t i, Visit visit) {
+    int k0 = 0;
+    for (; k0 + B <= n_rep; k0 += B) {
+        V x[B];
+#pragma unroll
+        for (int k = 0; k < B; ++k) x[k] = ld_stream(reinterpret_cast<const V*>(p[k0 + k] + src_off) + i);
+#pragma unroll
+        for (int k = 0; k < B; ++k) visit(x[k]);
+    }
+    const int kn = n_rep - k0;
+    if (kn > 0) {
+        V x[B];
+#pragma unroll
+        for (int k = 0; k < B; ++k)
+            x[k] = ld_stream(reinterpret_cast<const V*>(p[k0 + (k < kn ? k : 0)] + src_off) + i);
+#pragma unroll
+        for (int k = 0; k < B; ++k)
+            if (k < kn) visit(x[k]);
+    }
+}
+
 }  // namespace dev
 }  // namespace zero
