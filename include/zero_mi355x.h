@@ -314,13 +314,15 @@ zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_
  *              the fp32 arrays. Element i of these arrays is global element
  *              rank*S + i; only the window's part of the shard is read and written.
  * shard_grad   device [S] bf16, nullable: when given, also receives the
- *              averaged gradient, as zero_grad_reduce_shard writes it.
+ *              averaged gradient, as zero_grad_reduce_shard writes it; must
+ *              not overlap the fp32 arrays or param_out.
  * step, lr, beta1, beta2, eps, weight_decay, clip_scale: as
  *              zero_shard_adamw_step; a non-finite coefficient skips the
  *              update (shard_grad, when given, is still written).
  * Errors: ZERO_EINVAL (null plan or replicas, a null replica or state array
  * for a non-empty window, R or rank out of range, bad window, bad
- * hyperparameters, param_out overlapping the state); ZERO_EHIP. */
+ * hyperparameters, param_out or shard_grad overlapping the state, shard_grad
+ * overlapping param_out); ZERO_EHIP. */
 zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t rank,
                                    const uint16_t* const* replicas, int32_t n_replicas,
                                    int64_t begin, int64_t count, float* master, float* exp_avg,

@@ -125,6 +125,41 @@ def test_device_calls_reject_bad_arguments_before_touching_the_gpu(zm):
     assert zm.zero_sqnorm_workspace_bytes() >= 8
 
 
+def test_reduce_adamw_rejects_bad_arguments_before_touching_the_gpu(zm):
+    """zero_reduce_adamw_step's argument checks, which all run before any HIP
+    call (the addresses below are never dereferenced)."""
+    import ctypes
+    lib = zm._binding
+    plan = zm.zero_partition_plan([1000], 2, 1)          # S = 500
+    reps = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    hp = (1e-3, 0.9, 0.999, 1e-8, 0.01)
+    f32 = [ctypes.c_void_p(0x100000 * (k + 1)) for k in range(3)]   # disjoint 500-float arrays
+    par, grd = ctypes.c_void_p(0x900000), ctypes.c_void_p(0xA00000)
+
+    def call(plan_h=plan.handle, rank=1, n_rep=2, begin=0, count=1000, state=f32, param=par,
+             grad=grd, step=1, h=hp, replicas=reps):
+        return lib._reduce_adamw(plan_h, rank, replicas, n_rep, begin, count, *state, param, grad,
+                                 step, *h, None, None)
+    E = lib.ZERO_EINVAL
+    assert call(plan_h=None) == E
+    assert call(replicas=None) == E
+    assert call(rank=2) == E and call(rank=-1) == E
+    assert call(n_rep=0) == E and call(n_rep=65) == E
+    assert call(begin=-1) == E and call(count=1001) == E and call(begin=600, count=401) == E
+    assert call(step=0) == E
+    assert call(h=(1e-3, 1.0, 0.999, 1e-8, 0.01)) == E          # beta1 outside [0, 1)
+    assert call(h=(1e-3, 0.9, 0.999, 0.0, 0.01)) == E           # eps <= 0
+    assert call(begin=0, count=500) == lib.ZERO_OK              # window misses rank 1's shard
+    assert call(state=[f32[0], None, f32[2]]) == E              # NULL state array
+    assert "NULL" in zm.zero_last_error()
+    assert call(replicas=(ctypes.c_void_p * 2)(0x10000, None)) == E   # NULL replica
+    assert call(param=ctypes.c_void_p(0x100000 + 1000)) == E    # param_out inside master
+    assert "overlaps" in zm.zero_last_error()
+    assert call(grad=ctypes.c_void_p(0x300000 + 200)) == E      # shard_grad inside exp_avg_sq
+    assert call(grad=ctypes.c_void_p(0x900000 + 100)) == E      # shard_grad over param_out
+    assert "shard_grad" in zm.zero_last_error()
+
+
 @pytest.mark.parametrize("name,n_ranks", [("gpt2-small", 8), ("llama3-8b", 64), ("tiny-a", 4),
                                           ("gpt-1.3b", 3)])
 def test_shard0_plan_matches_oracle_on_workloads(zm, name, n_ranks):

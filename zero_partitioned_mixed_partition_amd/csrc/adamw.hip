@@ -710,6 +710,12 @@ extern "C" zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t ran
         ranges_overlap(param_out + at, hbytes, exp_avg + at, fbytes) ||
         ranges_overlap(param_out + at, hbytes, exp_avg_sq + at, fbytes))
         return fail(ZERO_EINVAL, "zero_reduce_adamw_step: param_out overlaps the fp32 state");
+    if (shard_grad != nullptr &&
+        (ranges_overlap(shard_grad + at, hbytes, master + at, fbytes) ||
+         ranges_overlap(shard_grad + at, hbytes, exp_avg + at, fbytes) ||
+         ranges_overlap(shard_grad + at, hbytes, exp_avg_sq + at, fbytes) ||
+         ranges_overlap(shard_grad + at, hbytes, param_out + at, hbytes)))
+        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: shard_grad overlaps the state or param_out");
     AdamScalars c;
     st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
     if (st != ZERO_OK) return st;
