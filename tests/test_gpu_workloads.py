@@ -294,3 +294,53 @@ def test_rank_step_skipped_step_counts_as_an_iteration(zm):
         assert_bf16_close(host_u16(rs.param_shards[rank]), shards[rank], f"step {t} shard")
         for i, (a, b) in enumerate(zip(rs.tensors, want["tensors"])):
             assert_bf16_close(host_u16(a), b, f"step {t} tensor {i}")
+
+
+@pytest.mark.parametrize("fuse", [True, False], ids=["one-pass", "two-calls"])
+def test_rank_step_without_clip_over_bucket_windows(zm, fuse):
+    """RankStep without clipping over three disjoint bucket windows of 5
+    replicas, 3 steps, with the gather: the one-pass path (reduce_update, one
+    zero_reduce_adamw_step per window) and the reduce/AdamW calls must both give
+    the oracle's rank step bit for bit (no clip, so nothing depends on the
+    order of the norm partials)."""
+    from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep, rank_step_plan_windows
+    numels = [1000, 37, 4096, 3, 777]
+    n_ranks, rank, R, bucket = 4, 2, 5, 700
+    plan = zm.zero_partition_plan(numels, n_ranks, 128)
+    ref = oracle.partition_plan(numels, n_ranks, 128)
+    P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
+    wins = rank_step_plan_windows(plan, rank, bucket)
+    assert len(wins) == 3
+    hyper = Hyper()
+    rs = RankStep(plan, rank, len(wins), hyper, 0.0, dev(), gather=True, fuse=fuse)
+    master = synth.normal_f32(S, 51, synth.KIND_MASTER, 0, 0, rank * S, phi, 0.02)
+    rs.master.copy_(torch.from_numpy(master))
+    shards = [synth.normal_bf16(S, 51, synth.KIND_PARAM, 0, 0, r * S, phi, 0.02) for r in range(n_ranks)]
+    for r in range(n_ranks):
+        if r != rank:
+            rs.param_shards[r].copy_(to_dev_u16(shards[r]))
+    shards[rank] = np.zeros(S, np.uint16)
+    state = {"master": master.copy(), "exp_avg": np.zeros(S, np.float32),
+             "exp_avg_sq": np.zeros(S, np.float32)}
+    grad_before = host_u16(rs.grad).copy()
+    for t in (1, 2, 3):
+        full = [synth.normal_bf16(P, 52, synth.KIND_REPLICA, t, k, 0, phi, 0.05) for k in range(R)]
+        rs.step([(b, c, [to_dev_u16(x[b:b + c]) for x in full]) for b, c in wins])
+        want = oracle.rank_step(ref, rank, full, 0, state, shards, [0.0] * n_ranks, t,
+                                hyper.as_kwargs(), 0.0)
+        torch.cuda.synchronize()
+        assert want["clip"] == 1.0
+        for got, key in ((rs.master, "master"), (rs.exp_avg, "exp_avg"), (rs.exp_avg_sq, "exp_avg_sq")):
+            assert_bits_equal(host_f32(got).view(np.uint32), state[key].view(np.uint32),
+                              f"step {t} {key}")
+        assert_bits_equal(host_u16(rs.param_shards[rank]), shards[rank], f"step {t} shard")
+        for i, (a, b) in enumerate(zip(rs.tensors, want["tensors"])):
+            assert_bits_equal(host_u16(a), b, f"step {t} tensor {i}")
+        if fuse:
+            assert_bits_equal(host_u16(rs.grad), grad_before, "the one-pass step stores no gradient")
+        else:
+            assert_bits_equal(host_u16(rs.grad), want["shard_grad"], f"step {t} gradient")
+    assert rs.t == 3
+    assert sorted(k[0] if isinstance(k, tuple) else k for k in rs._calls) == (
+        ["gather"] + ["reduce_update"] * 3 if fuse else ["adamw", "gather"] + ["reduce"] * 3)
+

@@ -12,6 +12,10 @@ with section "ZeRO-Stage 2"'s bucketed reduction:
   4. zero_gather_params      all shards -> per-tensor bf16 parameters (through a
                              copy table: zero_gather_table_create, zero_copy_table_run)
 
+Without clipping, nothing waits on the global norm, and steps 1 and 3 run as
+one pass per window (zero_reduce_adamw_step): the averaged gradient is used
+where it is formed instead of going through HBM.
+
 Everything stays on the device and on one stream; nothing synchronises with
 the host inside a step. The other ranks' norm partials and parameter shards
 are inputs: on a cluster they arrive through a scalar all-reduce and the
@@ -54,14 +58,18 @@ class RankStep:
                  elements per pinned staging slot and `host_threads` workers
                  (0: one per CPU this process may use). Reduce, clip and gather
                  stay on the device.
+    fuse         with max_norm <= 0 (and no offload), step() reduces and
+                 updates each window in one pass (reduce_update). Such a step
+                 leaves self.grad and the own norm partials as they were.
     """
 
     def __init__(self, plan: zb.Plan, rank: int, n_windows: int, hyper: Hyper, max_norm: float,
                  device: torch.device, gather: bool = True, offload: bool = False,
-                 offload_chunk: int = 1 << 21, host_threads: int = 0):
+                 offload_chunk: int = 1 << 21, host_threads: int = 0, fuse: bool = True):
         self.plan, self.rank, self.hyper, self.max_norm = plan, rank, hyper, max_norm
         self.device = device
         self.offload, self.host_threads = offload, host_threads
+        self.fuse = fuse
         s, nd = plan.shard_numel, plan.num_ranks
         # The arrays the AdamW kernel streams live in one arena, each start
         # moved STAGGER bytes past the previous end: arrays whose bases differ
@@ -149,6 +157,28 @@ class RankStep:
             self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
             clip_scale=clip, stream=st, **self.hyper.as_kwargs()))(self.t)
 
+    def reduce_update(self, windows: Sequence[Tuple[int, int, Sequence[torch.Tensor]]],
+                      stream=None):
+        """reduce() then adamw() with no clip, as one pass per window
+        (zero_reduce_adamw_step), every window with the bias-correction step
+        t = self.t + 1. The update is elementwise, so over disjoint windows this
+        is the same as the two calls; overlapping windows raise ValueError. The
+        averaged gradient is not stored and no norm partial is taken."""
+        if len(windows) != self.n_windows:
+            raise ValueError("window count differs from the one the step was built for")
+        if self.offload or self.max_norm > 0:
+            raise ValueError("the one-pass update runs on the device and without clipping")
+        spans = sorted((b, b + c) for b, c, _ in windows if c > 0)
+        if any(a[1] > b[0] for a, b in zip(spans, spans[1:])):
+            raise ValueError("windows overlap: the one-pass update needs disjoint windows")
+        self.t += 1
+        for w, (begin, count, reps) in enumerate(windows):
+            sig = (begin, count, tuple(r.data_ptr() for r in reps))
+            self._prepared(("reduce_update", w), stream, lambda st: zb.prepare_reduce_adamw_step(
+                self.plan, self.rank, reps, begin, count, self.master, self.exp_avg,
+                self.exp_avg_sq, self.param_shards[self.rank], clip_scale=None, stream=st,
+                **self.hyper.as_kwargs()), sig)(self.t)
+
     def gather(self, stream=None):
         # The shards and tensors are this object's fixed buffers, so the gather
         # goes through a device-resident copy table, built on first use.
@@ -157,9 +187,14 @@ class RankStep:
                 self.plan, self.param_shards, self.tensors).prepare_run(st))()
 
     def step(self, windows, stream=None) -> None:
-        self.reduce(windows, stream)
-        self.clip(stream)
-        self.adamw(stream)
+        spans = sorted((b, b + c) for b, c, _ in windows if c > 0)
+        disjoint = all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        if self.fuse and self.max_norm <= 0 and not self.offload and disjoint:
+            self.reduce_update(windows, stream)
+        else:
+            self.reduce(windows, stream)
+            self.clip(stream)
+            self.adamw(stream)
         self.gather(stream)
 
 
