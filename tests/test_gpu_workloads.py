@@ -296,16 +296,19 @@ def test_rank_step_skipped_step_counts_as_an_iteration(zm):
             assert_bf16_close(host_u16(a), b, f"step {t} tensor {i}")
 
 
-@pytest.mark.parametrize("fuse", [True, False], ids=["one-pass", "two-calls"])
-def test_rank_step_without_clip_over_bucket_windows(zm, fuse):
-    """RankStep without clipping over three disjoint bucket windows of 5
+@pytest.mark.parametrize("fuse,R", [(True, 5), (False, 5), (True, 9)],
+                         ids=["one-pass", "two-calls", "nine-replicas-two-calls"])
+def test_rank_step_without_clip_over_bucket_windows(zm, fuse, R):
+    """RankStep without clipping over three disjoint bucket windows of R
     replicas, 3 steps, with the gather: the one-pass path (reduce_update, one
     zero_reduce_adamw_step per window) and the reduce/AdamW calls must both give
     the oracle's rank step bit for bit (no clip, so nothing depends on the
-    order of the norm partials)."""
+    order of the norm partials). Windows of more than 8 replicas keep the two
+    calls even when fusing is on."""
     from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep, rank_step_plan_windows
     numels = [1000, 37, 4096, 3, 777]
-    n_ranks, rank, R, bucket = 4, 2, 5, 700
+    n_ranks, rank, bucket = 4, 2, 700
+    fused = fuse and R <= RankStep.FUSE_MAX_REPLICAS
     plan = zm.zero_partition_plan(numels, n_ranks, 128)
     ref = oracle.partition_plan(numels, n_ranks, 128)
     P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
@@ -336,11 +339,11 @@ def test_rank_step_without_clip_over_bucket_windows(zm, fuse):
         assert_bits_equal(host_u16(rs.param_shards[rank]), shards[rank], f"step {t} shard")
         for i, (a, b) in enumerate(zip(rs.tensors, want["tensors"])):
             assert_bits_equal(host_u16(a), b, f"step {t} tensor {i}")
-        if fuse:
+        if fused:
             assert_bits_equal(host_u16(rs.grad), grad_before, "the one-pass step stores no gradient")
         else:
             assert_bits_equal(host_u16(rs.grad), want["shard_grad"], f"step {t} gradient")
     assert rs.t == 3
     assert sorted(k[0] if isinstance(k, tuple) else k for k in rs._calls) == (
-        ["gather"] + ["reduce_update"] * 3 if fuse else ["adamw", "gather"] + ["reduce"] * 3)
+        ["gather"] + ["reduce_update"] * 3 if fused else ["adamw", "gather"] + ["reduce"] * 3)
 
