@@ -65,3 +65,45 @@ def test_staggered_arena_layout(step):
         prev_end = start + n * v.element_size()
         assert (v == 0).all()                                       # zero-filled
     assert prev_end <= arena.numel()
+
+
+def test_rank_step_chooses_the_one_pass_update_only_where_it_applies(step):
+    """RankStep.step's choice between the one-pass update (reduce_update) and
+    reduce, clip, AdamW, checked on the host with the device calls replaced by
+    recorders: one pass only without clipping, without offload, with fusing on,
+    over disjoint windows of at most FUSE_MAX_REPLICAS replicas."""
+    import zero_partitioned_mixed_partition_amd as zm
+    plan = zm.zero_partition_plan([1000, 37, 4096, 3, 777], 4, 128)
+    reps = lambda n: [torch.zeros(700, dtype=torch.int16) for _ in range(n)]   # noqa: E731
+
+    def taken(max_norm, windows, fuse=True):
+        rs = step.RankStep(plan, 2, len(windows), step.Hyper(), max_norm, torch.device("cpu"),
+                           gather=False, fuse=fuse)
+        calls = []
+        rs.reduce_update = lambda w, s=None: calls.append("one-pass")
+        rs.reduce = lambda w, s=None: calls.append("reduce")
+        rs.clip = lambda s=None: calls.append("clip")
+        rs.adamw = lambda s=None: calls.append("adamw")
+        rs.gather = lambda s=None: calls.append("gather")
+        rs.step(windows)
+        return calls
+
+    disjoint = [(4200, 700, reps(5)), (3500, 700, reps(5)), (2800, 700, reps(5))]
+    two_calls = ["reduce", "clip", "adamw", "gather"]
+    assert taken(0.0, disjoint) == ["one-pass", "gather"]
+    assert taken(1.0, disjoint) == two_calls                      # clipping needs the norm first
+    assert taken(0.0, disjoint, fuse=False) == two_calls
+    assert taken(0.0, [(3500, 700, reps(9))]) == two_calls        # more than 8 replicas
+    assert taken(0.0, [(3500, 700, reps(8)), (4200, 0, reps(9))]) == two_calls
+    assert taken(0.0, [(3500, 700, reps(8))]) == ["one-pass", "gather"]
+    assert taken(0.0, [(3500, 700, reps(5)), (3900, 700, reps(5))]) == two_calls   # overlap
+
+    rs = step.RankStep(plan, 2, 2, step.Hyper(), 0.0, torch.device("cpu"), gather=False)
+    with pytest.raises(ValueError, match="overlap"):
+        rs.reduce_update([(3500, 700, reps(5)), (3900, 700, reps(5))])
+    with pytest.raises(ValueError, match="window count"):
+        rs.reduce_update([(3500, 700, reps(5))])
+    rs = step.RankStep(plan, 2, 1, step.Hyper(), 1.0, torch.device("cpu"), gather=False)
+    with pytest.raises(ValueError, match="without clipping"):
+        rs.reduce_update([(3500, 700, reps(5))])
+    assert rs.t == 0
