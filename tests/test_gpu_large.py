@@ -17,6 +17,9 @@ llama3-70b  Llama-3-70B list, N_d = 8, rank 7 (8,819,213,312 elements, indices
             more steps with the oracle's coefficient; windows at the shard ends,
             around 2^31, 2^32 and 2^33 and the AdamW grid's rows, at tensor
             starts and 32 random 1M windows.
+past 2^32   the one-pass reduce and AdamW over a 4,299,161,984-element shard
+            (two rows of workgroups), on windows around 2^31, 2^32, the row
+            boundary and the padding.
 """
 import math
 
@@ -428,4 +431,58 @@ def test_shard0_flatten_waves_across_rank_buffers_past_2p31_bytes(zm):
     for i, (a, b) in enumerate(zip(tensors, back)):
         assert torch.equal(a, b), f"tensor {i} round trip"
     del tensors, back, flat, host
+    _free_gpu()
+
+
+def test_reduce_adamw_one_pass_past_2p32_elements(zm):
+    """zero_reduce_adamw_step over a shard of more than 2^32 elements (one tensor
+    of 2^32 + 2^22 + 333 parameters, N_d = 1, 2 replicas): the one-pass grid
+    then has two rows of workgroups. Step 1 from m = v = 0, no clip, with the
+    averaged gradient stored too; gradient, fp32 state and bf16 parameters
+    against the oracle bit for bit on windows at both ends, around 2^31, 2^32,
+    the grid's row boundary and the padding."""
+    phi = 2 ** 32 + 2 ** 22 + 333
+    ref = oracle.partition_plan([phi], 1, 128)
+    plan = zm.zero_partition_plan([phi], 1, 128)
+    P, S = ref.padded_numel, ref.shard_numel
+    R, seed = 2, 77
+    blocks = -(-S // 256)
+    max_row = (1 << 32) // 256 - 1
+    rows = -(-blocks // max_row)
+    per_row = -(-blocks // rows) * 256
+    assert rows == 2 and S > 2 ** 32 and P > phi
+    note(f"one pass past 2^32: S={S}, {rows} rows of {per_row // 256} workgroups, R={R}")
+    reps = [torch.empty(P, dtype=torch.int16, device=dev()) for _ in range(R)]
+    for k, t in enumerate(reps):
+        synth.device_normal_bf16(t, seed, synth.KIND_REPLICA, 1, k, 0, phi, synth.GRAD_SIGMA)
+    master = torch.empty(S, dtype=torch.float32, device=dev())
+    synth.device_normal_f32(master, seed, synth.KIND_MASTER, 0, 0, 0, phi, synth.MASTER_SIGMA)
+    m = torch.zeros(S, dtype=torch.float32, device=dev())
+    v = torch.zeros(S, dtype=torch.float32, device=dev())
+    param = torch.zeros(S, dtype=torch.int16, device=dev())
+    grad = torch.zeros(S, dtype=torch.int16, device=dev())
+    zm.zero_reduce_adamw_step(plan, 0, reps, 0, P, master, m, v, param, 1, shard_grad=grad, **HP)
+    torch.cuda.synchronize()
+    del reps
+    centers = [0, 2 ** 31, 2 ** 32, per_row, phi, S]
+    wins = _windows_in_shards(centers, 2048, S, 1, S)
+    note(f"one pass past 2^32: {len(wins)} windows, {sum(b - a for a, b in wins)} elements")
+    for a, b in wins:
+        n = b - a
+        rh = [synth.normal_bf16(n, seed, synth.KIND_REPLICA, 1, k, a, phi, synth.GRAD_SIGMA)
+              for k in range(R)]
+        window_plan = oracle.partition_plan([n], 1, 1)   # the reduce is elementwise
+        g = np.zeros(n, np.uint16)
+        oracle.reduce_shard(window_plan, 0, rh, 0, g)
+        p0 = synth.normal_f32(n, seed, synth.KIND_MASTER, 0, 0, a, phi, synth.MASTER_SIGMA)
+        z = np.zeros(n, np.float32)
+        p1, m1, v1, bits = oracle.adamw_step(p0, z, z, g, 1, clip=1.0, **HP)
+        assert_bits_equal(host_u16(grad[a:b]), g, f"gradient [{a},{b})")
+        assert_bits_equal(host_f32(master[a:b]).view(np.uint32), p1.view(np.uint32), f"master [{a},{b})")
+        assert_bits_equal(host_f32(m[a:b]).view(np.uint32), m1.view(np.uint32), f"exp_avg [{a},{b})")
+        assert_bits_equal(host_f32(v[a:b]).view(np.uint32), v1.view(np.uint32), f"exp_avg_sq [{a},{b})")
+        assert_bits_equal(host_u16(param[a:b]), bits, f"param [{a},{b})")
+    if phi < S:                                           # padding: zero gradient, state stays 0
+        assert not host_u16(grad[phi:S]).any() and not host_f32(master[phi:S]).any()
+    del master, m, v, param, grad
     _free_gpu()
