@@ -81,6 +81,13 @@ def parse_args(argv=None):
     ap.add_argument("--also", nargs="*", default=None, choices=WORKLOAD_NAMES, metavar="WORKLOAD",
                     help="after the line's workload, measure these too (their figures go under "
                          "'also')")
+    ap.add_argument("--stagger", type=int, default=None, metavar="BYTES",
+                    help="gap between consecutive arrays of an arena and between replica buffers "
+                         "(default: the step module's STAGGER; 0 packs them end to end at "
+                         "256-byte-aligned starts)")
+    ap.add_argument("--separate-arrays", action="store_true",
+                    help="give every state array and replica buffer an allocation of its own "
+                         "instead of one staggered arena (a layout comparison)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: read two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) "
                          "of a '--profile-steps N --calibrate-copy' run of this workload, and record "
@@ -887,6 +894,15 @@ def also_line(name: str, device) -> dict:
     return out
 
 
+def _separate_arrays(specs, device):
+    """The arena's arrays as separate zeroed allocations (the caching allocator
+    starts each large one on its own 2 MiB-aligned segment): the layout a
+    caller gets from one torch.zeros per array."""
+    import torch
+    views = [torch.zeros(max(numel, 1), dtype=dtype, device=device)[:numel] for numel, dtype in specs]
+    return views, views
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.write_traffic:
@@ -903,6 +919,14 @@ def main(argv=None):
     warmup = args.warmup if args.warmup is not None else DEFAULT_STEPS[args.workload][1]
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    import zero_partitioned_mixed_partition_amd.step as step_module
+    if args.stagger is not None:
+        if args.stagger < 0:
+            print("bench.py: --stagger must be >= 0", file=sys.stderr)
+            return 2
+        step_module.STAGGER = args.stagger
+    if args.separate_arrays:
+        step_module._staggered_arena = _separate_arrays
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     wl = make_workload(args.workload, device)
     if args.profile_steps:
@@ -947,7 +971,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": wl.describe(), "name": wl.name, "params": wl.phi,
                    "shard_elems": wl.S, "n_ranks": wl.n_ranks, "replicas": wl.replicas,
-                   "parallelism": "one GPU's share of a dp job"},
+                   "parallelism": "one GPU's share of a dp job",
+                   "arena_stagger_bytes": None if args.separate_arrays else step_module.STAGGER},
         "adamw_params_per_s": elems_per_launch / (adamw_ms * 1e-3),
         "adamw_event_us": {"mean": adamw_ms * 1e3, "median": adamw_each[len(adamw_each) // 2] * 1e3,
                            "min": adamw_each[0] * 1e3, "launches": len(adamw_each)},

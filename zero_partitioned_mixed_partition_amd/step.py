@@ -79,9 +79,8 @@ class RankStep:
         self.fuse = fuse
         s, nd = plan.shard_numel, plan.num_ranks
         # The arrays the AdamW kernel streams live in one arena, each start
-        # moved STAGGER bytes past the previous end: arrays whose bases differ
-        # by multiples of large powers of two meet the same HBM channels at the
-        # same time; the stagger was measured to add ~4% bandwidth on MI355X.
+        # moved STAGGER bytes past the previous end (the value measured best
+        # on MI355X; see STAGGER).
         if offload:
             views, self.arena = _staggered_arena([(s, torch.int16), (s, torch.int16)], device)
             self.grad, own_param = views
@@ -206,7 +205,13 @@ class RankStep:
         self.gather(stream)
 
 
-STAGGER = 4096 + 256
+# Gap between consecutive arrays of an arena (and between replica buffers).
+# Measured on MI355X over the benchmark's steps, two rounds each: 2048 bytes was
+# the fastest or level on every workload; against 4352 bytes it took the 1.3B
+# GPT step from 10.04 to 9.83-9.88 ms, Llama-3-8B's from 3.12 to 3.06 ms and
+# Llama-3-70B's from 40.51-40.55 to 40.10-40.11 ms (AdamW 81.5% -> 82.2% of
+# HBM peak); 0 (packed) was level with 2048 except on the 1.3B GPT (10.02 ms).
+STAGGER = 2048
 
 
 def _staggered_arena(specs, device):
@@ -223,9 +228,8 @@ def _staggered_arena(specs, device):
 
 
 def staggered_replicas(n_replicas: int, numel: int, device) -> List[torch.Tensor]:
-    """R bf16 buffers of numel elements in one allocation, STAGGER bytes apart:
-    replica streams read in lockstep by the reduce then meet different HBM
-    channels (measured up to ~10% faster on MI355X at 64 replicas)."""
+    """R bf16 buffers of numel elements in one allocation, STAGGER bytes apart
+    (the reduce reads the replica streams in lockstep)."""
     views, _ = _staggered_arena([(numel, torch.int16)] * n_replicas, device)
     return views      # each view keeps the shared allocation alive
 
