@@ -250,12 +250,47 @@ class RankWorkload:
                 self.plan, rs.param_shards, rs.tensors, st0)))
         if extra:
             self.extra_phases = extra
+        if reps and not bucket and not self.offload and not name.endswith("-pertensor"):
+            self._setup_reduce_tensors(device)
         self.adamw_launches = 1
         self.elems_per_step = S
         self.per_tensor = name.endswith("-pertensor")
         if self.per_tensor:
             self._setup_per_tensor(device)
         torch.cuda.synchronize()
+
+    def _setup_reduce_tensors(self, device):
+        """Outside the step: the same reduce from replicas that are still
+        per-tensor (each of the R replicas' tensors its own allocation, the
+        values the flat replicas hold), through a zero_reduce_table, which needs
+        no flatten of each replica first. Checked here against the step's own
+        reduce over the flat replicas, bit for bit."""
+        import torch
+
+        import synth
+        from zero_partitioned_mixed_partition_amd import _binding as zb
+        w, rs = self.workload, self.rs
+        offs = (model_offsets(w.numels) if self.layout == "shard0"
+                else [self.plan.tensor_offset(t) for t in range(self.plan.num_tensors)])
+        self.rt_reps = []
+        for k in range(self.replicas):
+            rep = []
+            for n, off in zip(w.numels, offs):
+                g = torch.empty(n, dtype=torch.int16, device=device)
+                synth.device_normal_bf16(g, self.seed, synth.KIND_REPLICA, 1, k, off, self.phi,
+                                         synth.GRAD_SIGMA)
+                rep.append(g)
+            self.rt_reps.append(rep)
+        self.rt_grad = torch.empty(self.S, dtype=torch.int16, device=device)
+        self.rt_sq = torch.zeros(1, dtype=torch.float64, device=device)
+        self.rt_table = zb.ReduceTable(self.plan, self.rank, self.rt_reps, self.rt_grad)
+        run = self.rt_table.prepare_run(self.rt_sq, torch.cuda.current_stream(device).cuda_stream)
+        run()
+        rs.reduce(self.windows)
+        torch.cuda.synchronize()
+        if not torch.equal(self.rt_grad, rs.grad):
+            raise RuntimeError("the reduce from per-tensor replicas differs from the flat reduce")
+        self.extra_phases = list(getattr(self, "extra_phases", None) or []) + [("reduce_tensors", run)]
 
     def _setup_per_tensor(self, device):
         """FSDP-2 as its optimizer sees it: every parameter's local chunk has its
@@ -367,6 +402,8 @@ class RankWorkload:
             b["gather_call"] = b["gather"]
         if getattr(self, "per_tensor", False):
             b["adamw_list"] = 28 * self.elems_per_step
+        if getattr(self, "rt_table", None) is not None:
+            b["reduce_tensors"] = (2 * self.replicas + 2) * S
         return b
 
     def describe(self):

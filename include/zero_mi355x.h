@@ -27,6 +27,8 @@
  *                           (the step before the reduce; inverse of the gather)
  *   zero_*_table_create, zero_copy_table_run  the gather or flatten of fixed
  *                           buffers, described once in device memory
+ *   zero_reduce_table_*     the reduce straight from per-tensor replicas of
+ *                           fixed buffers (no flatten of each replica first)
  *   zero_offload_adamw_step ZeRO-Offload: the update on the host CPU, with the
  *                           gradient and parameter transfers overlapped
  *
@@ -459,6 +461,51 @@ zero_status zero_flatten_table_create(const zero_plan* plan, const uint16_t* con
 zero_status zero_copy_table_run(const zero_copy_table* table, hipStream_t stream);
 int64_t zero_copy_table_blocks(const zero_copy_table* table);
 void zero_copy_table_free(zero_copy_table* table);
+
+/* Reduce from per-tensor replicas, for fixed buffers. [ZF] "FSDP-1:
+ * FlatParameter and Module-Level Wrapping" (every tensor's place in the flat
+ * padded buffer) with "Execution Flow for ZeRO-1", step 2 (the rank's slice
+ * of the gradient averaged over the replicas). When the R replicas are still
+ * per-tensor buffers, the rank's averaged gradient is reduced from them
+ * directly, without first flattening each replica (zero_flatten_params): for
+ * every segment of the rank's shard, tensor elements [tensor_offset,
+ * tensor_offset + length) of each replica are reduced into shard elements
+ * [shard_offset, shard_offset + length), and every other shard position
+ * (padding) is set to +0. The bits are those of zero_flatten_params on each
+ * replica followed by zero_grad_reduce_shard over the whole shard (fp32 sum in
+ * replica order, one fp32 division by R, bf16 round-to-nearest-even); the
+ * squared-norm partial, when asked for, is the same fp64 sum to within
+ * rounding. Per shard element (2R + 2) bytes move, against 6R + 2 with the
+ * flattens. Flat and Shard(0) plans alike.
+ * plan, rank      the plan and this rank.
+ * replica_tensors host [R * T] of device pointers: entry k * T + t is replica
+ *                 k's tensor t, numel_t bf16 values; may be NULL only for
+ *                 tensors with no segment in this rank's shard.
+ * n_replicas      R, 1..ZERO_MAX_REPLICAS.
+ * shard_grad      device [S] bf16, written entirely by each run; must not
+ *                 overlap the replicas.
+ * Create: lists the rank's segments and padding gaps as pieces and copies to
+ * device memory that the table owns one 64-byte descriptor per piece, one
+ * 4-byte piece index per workgroup of 2,048 shard elements, the R * T replica
+ * pointers and room for one fp64 partial per workgroup (hipMalloc and a
+ * synchronous hipMemcpy on the current device, once). The table keeps the
+ * pointers, not the data: the caller keeps the buffers alive and in place.
+ * Errors: ZERO_EINVAL (NULL out, plan, replica_tensors or shard_grad; rank or
+ * R out of range; a NULL replica tensor the shard needs); ZERO_ERANGE (2^31
+ * workgroups or more); ZERO_ENOMEM; ZERO_EHIP.
+ * Run: enqueued on stream, with the table's device current (ZERO_EINVAL
+ * otherwise); sqnorm_out (device double, nullable) receives the squared
+ * norm of the written gradient. Runs of one table must not overlap (they
+ * share its partials). Free: hipFree; accepts NULL. Blocks: the workgroups of
+ * one run, or -1 for NULL. */
+typedef struct zero_reduce_table zero_reduce_table;
+zero_status zero_reduce_table_create(const zero_plan* plan, int32_t rank,
+                                     const uint16_t* const* replica_tensors, int32_t n_replicas,
+                                     uint16_t* shard_grad, zero_reduce_table** out);
+zero_status zero_reduce_table_run(const zero_reduce_table* table, double* sqnorm_out,
+                                  hipStream_t stream);
+int64_t zero_reduce_table_blocks(const zero_reduce_table* table);
+void zero_reduce_table_free(zero_reduce_table* table);
 
 /* ------------------------------------------------------------------ ZeRO-Offload
  *

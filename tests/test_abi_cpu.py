@@ -160,6 +160,36 @@ def test_reduce_adamw_rejects_bad_arguments_before_touching_the_gpu(zm):
     assert "shard_grad" in zm.zero_last_error()
 
 
+def test_reduce_table_rejects_bad_arguments_before_touching_the_gpu(zm):
+    """zero_reduce_table_create's argument checks, all before any HIP call (the
+    addresses are never dereferenced)."""
+    import ctypes
+    lib = zm._binding
+    plan = zm.zero_partition_plan([1000, 24, 3000], 2, 8)      # S = 2016
+    T, R = 3, 2
+    good = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(T * R)]
+    grad = ctypes.c_void_p(0x900000)
+    out = ctypes.c_void_p()
+    E = lib.ZERO_EINVAL
+
+    def create(plan_h=plan.handle, rank=0, reps=good, n_rep=R, g=grad, o=ctypes.byref(out)):
+        arr = None if reps is None else (ctypes.c_void_p * len(reps))(*reps)
+        return lib._rt_create(plan_h, rank, arr, n_rep, g, o)
+    assert create(o=None) == E
+    assert create(plan_h=None) == E
+    assert create(reps=None) == E
+    assert create(rank=2) == E and create(rank=-1) == E
+    assert create(n_rep=0) == E and create(n_rep=65) == E
+    assert create(g=None) == E
+    missing = list(good)
+    missing[1 * T + 2] = None               # replica 1's tensor 2, which rank 1's shard needs
+    assert create(rank=1, reps=missing) == E
+    assert "replica 1" in zm.zero_last_error()
+    assert lib._rt_run(None, None, None) == E
+    assert lib._rt_blocks(None) == -1
+    lib._rt_free(None)
+
+
 @pytest.mark.parametrize("name,n_ranks", [("gpt2-small", 8), ("llama3-8b", 64), ("tiny-a", 4),
                                           ("gpt-1.3b", 3)])
 def test_shard0_plan_matches_oracle_on_workloads(zm, name, n_ranks):

@@ -916,3 +916,166 @@ def test_reduce_adamw_one_pass_matches_the_two_calls_and_the_oracle(zm, case):
     if case == "skip":
         assert_bits_equal(host_f32(f["p"]).view(np.uint32), master.view(np.uint32), "skipped: master")
         assert (host_u16(f["o"]) == 0x2222).all(), "skipped: param untouched"
+
+
+# ----------------------------------------------------------------------------- reduce from per-tensor replicas
+
+def _tensor_replicas(rng, numels, R):
+    """R replicas, each a list of per-tensor bf16 arrays of finite values."""
+    return [[oracle.f32_to_bf16((rng.standard_normal(n) * 0.05).astype(np.float32)) for n in numels]
+            for _ in range(R)]
+
+
+def _device_tensors(rep, misalign=False):
+    """Device copies, each tensor in an allocation of its own; with misalign,
+    every tensor starts 2 bytes into its allocation."""
+    out = []
+    for a in rep:
+        if misalign:
+            buf = torch.empty(len(a) + 1, dtype=torch.int16, device=dev())
+            v = buf[1:]
+            v.copy_(to_dev_u16(a))
+            out.append(v)
+        else:
+            out.append(to_dev_u16(a))
+    return out
+
+
+def _oracle_reduce_from_tensors(ref, rank, reps, shard0):
+    """The oracle's flatten of every replica, then its reduce of the rank's shard."""
+    flatten = oracle.flatten_params_shard0 if shard0 else oracle.flatten_params
+    flats = [flatten(ref, rep) for rep in reps]
+    want = np.zeros(ref.shard_numel, np.uint16)
+    oracle.reduce_shard(ref, rank, flats, 0, want)
+    return want, oracle.sqnorm(want)
+
+
+def _check_reduce_table(zm, ref, plan, reps_h, shard0, misalign=False, note_prefix=""):
+    S = ref.shard_numel
+    d_reps = [_device_tensors(rep, misalign) for rep in reps_h]
+    for rank in range(ref.n_ranks):
+        grad = torch.full((S,), 0x1234, dtype=torch.int16, device=dev())
+        sq = torch.full((1,), -1.0, dtype=torch.float64, device=dev())
+        table = zm.ReduceTable(plan, rank, d_reps, grad)
+        table.run(sqnorm_out=sq)
+        torch.cuda.synchronize()
+        want, want_sq = _oracle_reduce_from_tensors(ref, rank, reps_h, shard0)
+        assert_bits_equal(host_u16(grad), want, f"{note_prefix}rank {rank} gradient")
+        got_sq = float(sq.item())
+        assert abs(got_sq - want_sq) <= 1e-12 * want_sq, (rank, got_sq, want_sq)
+        del table
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_reduce_table_flat_plans(zm, seed):
+    """zero_reduce_table_*: every rank's averaged gradient straight from R
+    per-tensor replicas, against the oracle's flatten of each replica and its
+    reduce; ragged tensor sizes (16-byte and element-wise pieces), padding at
+    the end, R from 1 to 9."""
+    rng = np.random.default_rng(1300 + seed)
+    t = int(rng.integers(1, 9))
+    numels = [int(x) for x in rng.integers(1, 9000, t)]
+    numels[0] = int(rng.integers(1, 5)) * 8                # an aligned small one
+    n_ranks = int(rng.choice([1, 2, 4, 8]))
+    align = int(rng.choice([1, 8, 128]))
+    R = [1, 3, 8, 9][seed]
+    ref = oracle.partition_plan(numels, n_ranks, align)
+    plan = zm.zero_partition_plan(numels, n_ranks, align)
+    note(f"reduce table flat: numels={numels} N_d={n_ranks} A={align} R={R}")
+    _check_reduce_table(zm, ref, plan, _tensor_replicas(rng, numels, R), False)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_reduce_table_shard0_plans(zm, seed):
+    """The same on FSDP-2 Shard(0) plans: each rank's chunks of every tensor,
+    with the rows' padding in between written as zeros."""
+    rng = np.random.default_rng(1400 + seed)
+    t = int(rng.integers(1, 8))
+    dim0 = [int(x) for x in rng.integers(1, 3000, t)]
+    dim0[0] = int(rng.integers(1, 4))                      # fewer rows than ranks
+    numels = [d * int(k) for d, k in zip(dim0, rng.integers(1, 40, t))]
+    n_ranks = int(rng.choice([2, 3, 4, 8]))
+    align = int(rng.choice([1, 8, 128]))
+    R = [2, 5, 8, 12][seed]
+    ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, align)
+    plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, align)
+    note(f"reduce table shard0: dim0={dim0} numels={numels} N_d={n_ranks} A={align} R={R}")
+    _check_reduce_table(zm, ref, plan, _tensor_replicas(rng, numels, R), True)
+
+
+def test_reduce_table_misaligned_replicas_and_reruns(zm):
+    """Replica tensors 2 bytes into their allocations take the element-wise
+    path with the same bits; a table run again after its buffers are rewritten
+    in place reduces the new contents; a run without sqnorm_out writes the same
+    gradient."""
+    rng = np.random.default_rng(1500)
+    numels = [4096, 37, 8000, 3, 2048 * 3 + 5]
+    ref = oracle.partition_plan(numels, 4, 128)
+    plan = zm.zero_partition_plan(numels, 4, 128)
+    reps_h = _tensor_replicas(rng, numels, 4)
+    _check_reduce_table(zm, ref, plan, reps_h, False, misalign=True, note_prefix="misaligned ")
+    rank, S = 2, ref.shard_numel
+    d_reps = [_device_tensors(rep) for rep in reps_h]
+    grad = torch.zeros(S, dtype=torch.int16, device=dev())
+    table = zm.ReduceTable(plan, rank, d_reps, grad)
+    assert table.blocks == sum(-(-ln // 2048) for ln in _pieces_lengths(ref, rank))
+    for call in range(3):
+        new_h = _tensor_replicas(rng, numels, 4)
+        for dr, hr in zip(d_reps, new_h):
+            for d, h in zip(dr, hr):
+                d.copy_(to_dev_u16(h))
+        sq = torch.zeros(1, dtype=torch.float64, device=dev())
+        table.run(sqnorm_out=sq if call != 1 else None)
+        torch.cuda.synchronize()
+        want, want_sq = _oracle_reduce_from_tensors(ref, rank, new_h, False)
+        assert_bits_equal(host_u16(grad), want, f"run {call}")
+        if call != 1:
+            assert abs(float(sq.item()) - want_sq) <= 1e-12 * want_sq
+
+
+def _pieces_lengths(ref, rank):
+    """Lengths of the rank's segments and of the padding gaps around them."""
+    out, pos = [], 0
+    for (_, _, soff, ln) in ref.segments(rank):
+        if soff > pos:
+            out.append(soff - pos)
+        out.append(ln)
+        pos = soff + ln
+    if ref.shard_numel > pos:
+        out.append(ref.shard_numel - pos)
+    return out
+
+
+def test_reduce_table_gpt2_small_rank7_eight_replicas(zm):
+    """The GPT-2-small list, rank 7 of 8, 8 per-tensor replicas generated on
+    the device (each tensor keyed by its flat offset, so a flattened replica is
+    the generator's flat buffer): the table's gradient and squared norm against
+    the oracle's reduce of the generated flat replicas' slice."""
+    w = synth.WORKLOADS["gpt2-small"]
+    rank, R, seed = 7, 8, 1600
+    ref = oracle.partition_plan(w.numels, 8, w.align)
+    plan = zm.zero_partition_plan(w.numels, 8, w.align)
+    S, phi = ref.shard_numel, ref.numel
+    reps = []
+    for k in range(R):
+        rep = []
+        for n, off in zip(w.numels, ref.offsets):
+            t = torch.empty(n, dtype=torch.int16, device=dev())
+            synth.device_normal_bf16(t, seed, synth.KIND_REPLICA, 1, k, off, phi, synth.GRAD_SIGMA)
+            rep.append(t)
+        reps.append(rep)
+    grad = torch.full((S,), 0x4321, dtype=torch.int16, device=dev())
+    sq = torch.zeros(1, dtype=torch.float64, device=dev())
+    table = zm.ReduceTable(plan, rank, reps, grad)
+    table.run(sqnorm_out=sq)
+    torch.cuda.synchronize()
+    flats = [synth.normal_bf16(S, seed, synth.KIND_REPLICA, 1, k, rank * S, phi, synth.GRAD_SIGMA)
+             for k in range(R)]
+    window = oracle.partition_plan([S], 1, 1)              # the reduce is elementwise
+    want = np.zeros(S, np.uint16)
+    oracle.reduce_shard(window, 0, flats, 0, want)
+    assert_bits_equal(host_u16(grad), want, "gpt2-small rank 7 gradient")
+    want_sq = oracle.sqnorm(want)
+    assert abs(float(sq.item()) - want_sq) <= 1e-12 * want_sq
+    note(f"gpt2-small rank 7: {S} elements from {R} x {len(w.numels)} tensors, "
+         f"{table.blocks} workgroups, bit-identical")

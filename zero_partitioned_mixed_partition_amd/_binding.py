@@ -98,6 +98,11 @@ _ft_create = _fn("zero_flatten_table_create", c_i32,
 _ct_run = _fn("zero_copy_table_run", c_i32, [c_vp, c_vp])
 _ct_blocks = _fn("zero_copy_table_blocks", c_i64, [c_vp])
 _ct_free = _fn("zero_copy_table_free", None, [c_vp])
+_rt_create = _fn("zero_reduce_table_create", c_i32,
+                 [c_vp, c_i32, ctypes.POINTER(c_vp), c_i32, c_vp, ctypes.POINTER(c_vp)])
+_rt_run = _fn("zero_reduce_table_run", c_i32, [c_vp, c_vp, c_vp])
+_rt_blocks = _fn("zero_reduce_table_blocks", c_i64, [c_vp])
+_rt_free = _fn("zero_reduce_table_free", None, [c_vp])
 _status_string = _fn("zero_status_string", ctypes.c_char_p, [c_i32])
 _last_error = _fn("zero_last_error", ctypes.c_char_p, [])
 
@@ -563,6 +568,52 @@ class CopyTable:
     def _default_stream(self) -> int:
         import torch
         return torch.cuda.current_stream().cuda_stream
+
+
+class ReduceTable:
+    """Owner of a zero_reduce_table: the rank's averaged gradient reduced
+    straight from R per-tensor replicas (replicas[k][t] = replica k's tensor t)
+    into shard_grad, described once in device memory (on the current device).
+    The plan and the buffers are held here, so they outlive the table."""
+
+    def __init__(self, plan: Plan, rank: int, replicas: Sequence[Sequence], shard_grad):
+        T = plan.num_tensors
+        for k, rep in enumerate(replicas):
+            if len(rep) != T:
+                raise ValueError(f"replica {k} lists {len(rep)} tensors; the plan has {T}")
+            for t, x in enumerate(rep):
+                _need(x, plan.tensor_numel(t), f"tensor {t} of replica {k}")
+        _need(shard_grad, plan.shard_numel, "shard_grad")
+        ptrs = (c_vp * max(len(replicas) * T, 1))(
+            *[_ptr(x, 2, "replica tensor") for rep in replicas for x in rep])
+        h = c_vp()
+        _check(_rt_create(plan.handle, rank, ptrs, len(replicas), _ptr(shard_grad, 2, "shard_grad"),
+                          ctypes.byref(h)), "zero_reduce_table_create")
+        self._h = h
+        self._free = _rt_free          # held by the instance for interpreter exit
+        self._keep = (plan, [list(r) for r in replicas], shard_grad)
+        self._device_ref = shard_grad
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        free = getattr(self, "_free", None)
+        if h is not None and h.value and free is not None:
+            free(h)
+            h.value = None
+
+    @property
+    def blocks(self) -> int:
+        return int(_rt_blocks(self._h))
+
+    def run(self, sqnorm_out=None, stream=None) -> None:
+        self.prepare_run(sqnorm_out, stream)()
+
+    def prepare_run(self, sqnorm_out=None, stream=None) -> "Prepared":
+        _need(sqnorm_out, 1, "sqnorm_out")
+        p = Prepared(_rt_run, [self._h, _ptr(sqnorm_out, 8, "sqnorm_out"),
+                               _stream(stream, self._device_ref)], "zero_reduce_table_run")
+        p._keep = (self, sqnorm_out)
+        return p
 
 
 def _host_ptr(a, itemsize: int, what: str) -> int:

@@ -696,6 +696,285 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
                         static_cast<double*>(workspace), workspace_bytes, stream);
 }
 
+// ------------------------------------------------------------ per-tensor replicas
+//
+// "FSDP-1: FlatParameter and Module-Level Wrapping" places every tensor in the
+// flat padded buffer; "Execution Flow for ZeRO-1", step 2, averages the rank's
+// slice of it over the replicas. When the replicas are still per-tensor (as a
+// backward pass leaves them), the rank's slice can be reduced from them
+// directly, with no flatten of each replica first: for every segment of the
+// rank's shard, elements [tensor_offset, tensor_offset + length) of tensor t in
+// each replica, reduced into shard elements [shard_offset, shard_offset +
+// length); the shard's padding is written as zeros. The arithmetic is
+// reduce_vec's (fp32 sum in replica order, one division by R, one rounding), so
+// the bits are those of zero_grad_reduce_shard over the flattened replicas.
+// Per shard element: R bf16 reads and one bf16 write, (2R + 2) bytes, against
+// 4R more for flattening R replicas first.
+//
+// The table is built once for fixed buffers: one 64-byte descriptor per piece
+// (a segment, or a gap of padding), an XCD-major per-workgroup index, the
+// replica pointers tensor-major (pointer of replica k's tensor t at t * R + k,
+// so a workgroup's R pointers are contiguous), and a partial per workgroup for
+// the squared norm. A workgroup reduces kRChunk elements of one piece, 8 per
+// lane through 16-byte accesses where every replica's tensor, the offsets and
+// the shard are 8-element aligned, element by element otherwise.
+struct alignas(64) RPieceDesc {
+    int64_t src_off;       // element offset into tensor `tensor` of every replica
+    int64_t dst_off;       // element offset into the shard gradient
+    int64_t len;
+    int64_t first_block;
+    int32_t tensor;        // -1: padding, written as zeros
+    int32_t vec;           // 16-byte accesses
+    int64_t unused[2];
+};
+static_assert(sizeof(RPieceDesc) == 64, "one 64-byte descriptor per piece");
+
+namespace {
+
+constexpr int64_t kRChunk = int64_t(kThreads) * 8;   // elements per workgroup
+
+__global__ __launch_bounds__(kThreads) void reduce_table_kernel(const RPieceDesc* __restrict__ table,
+                                                                const uint32_t* __restrict__ index,
+                                                                const uint16_t* const* __restrict__ ptrs,
+                                                                int n_rep, uint16_t* __restrict__ out,
+                                                                int64_t blk0, int64_t per,
+                                                                double* __restrict__ partials) {
+    const int64_t blk = blk0 + static_cast<int64_t>(blockIdx.x);
+    const RPieceDesc d = table[index[zero::dev::xcd_major_entry(blk0, per)]];
+    const int64_t start = (blk - d.first_block) * kRChunk;
+    const int64_t len = d.len - start < kRChunk ? d.len - start : kRChunk;
+    uint16_t* const o = out + d.dst_off + start;
+    double sq = 0.0;
+    if (d.tensor < 0) {
+        for (int64_t e = threadIdx.x; e < len; e += kThreads) o[e] = 0;
+    } else {
+        const uint16_t* const* const p = ptrs + static_cast<int64_t>(d.tensor) * n_rep;
+        const int64_t src = d.src_off + start;
+        const float r = static_cast<float>(n_rep);
+        auto one = [&](int64_t e) {                       // element e of the chunk
+            float acc = 0.0f;
+            for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(p[k][src + e]);
+            const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
+            o[e] = h;
+            sq += sq1(h);
+        };
+        const int64_t e = static_cast<int64_t>(threadIdx.x) * 8;
+        if (d.vec && e + 8 <= len) {
+            float acc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+            for (int k0 = 0; k0 < n_rep; k0 += kReplicaBatch) {
+                u32x4 x[kReplicaBatch];
+                const int kn = n_rep - k0 < kReplicaBatch ? n_rep - k0 : kReplicaBatch;
+#pragma unroll
+                for (int k = 0; k < kReplicaBatch; ++k)
+                    if (k < kn) x[k] = zero::dev::ld_stream(reinterpret_cast<const u32x4*>(p[k0 + k] + src + e));
+#pragma unroll
+                for (int k = 0; k < kReplicaBatch; ++k) {
+                    if (k < kn) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            acc[2 * j] = acc[2 * j] + zero::dev::lo_bf16(x[k][j]);
+                            acc[2 * j + 1] = acc[2 * j + 1] + zero::dev::hi_bf16(x[k][j]);
+                        }
+                    }
+                }
+            }
+            u32x4 w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = zero::dev::pack_bf16(acc[2 * j] / r, acc[2 * j + 1] / r);
+            sq += sq8(w);
+            zero::dev::st_stream(reinterpret_cast<u32x4*>(o + e), w);
+        } else if (d.vec) {                               // the chunk's ragged end
+            for (int64_t i = e; i < len; ++i) one(i);
+        } else {
+            for (int64_t i = threadIdx.x; i < len; i += kThreads) one(i);
+        }
+    }
+    if (partials != nullptr) store_partial(sq, partials + blk0);
+}
+
+}  // namespace
+
+struct zero_reduce_table {
+    int device = -1;
+    void* mem = nullptr;            // descriptors, index, replica pointers, partials
+    const RPieceDesc* table = nullptr;
+    const uint32_t* index = nullptr;
+    const uint16_t* const* ptrs = nullptr;
+    double* partials = nullptr;     // blocks, then the first-level sums
+    uint16_t* out = nullptr;
+    int32_t n_rep = 0;
+    int64_t blocks = 0;
+};
+
+extern "C" zero_status zero_reduce_table_create(const zero_plan* plan, int32_t rank,
+                                                const uint16_t* const* replica_tensors,
+                                                int32_t n_replicas, uint16_t* shard_grad,
+                                                zero_reduce_table** out) {
+    using zero::fail;
+    static const char* const who = "zero_reduce_table_create";
+    zero::clear_error();
+    if (out == nullptr) return fail(ZERO_EINVAL, "zero_reduce_table_create: NULL out");
+    *out = nullptr;
+    if (plan == nullptr || replica_tensors == nullptr)
+        return fail(ZERO_EINVAL, "zero_reduce_table_create: NULL plan or replica_tensors");
+    if (rank < 0 || rank >= plan->n_ranks)
+        return fail(ZERO_EINVAL, "zero_reduce_table_create: rank out of range");
+    if (n_replicas < 1 || n_replicas > ZERO_MAX_REPLICAS)
+        return fail(ZERO_EINVAL, "zero_reduce_table_create: n_replicas must be 1.." +
+                                     std::to_string(ZERO_MAX_REPLICAS));
+    if (plan->shard > 0 && shard_grad == nullptr)
+        return fail(ZERO_EINVAL, "zero_reduce_table_create: NULL shard_grad");
+    const int64_t T = static_cast<int64_t>(plan->numels.size());
+    const std::vector<zero_segment>& segs = plan->by_rank[static_cast<size_t>(rank)];
+    std::vector<RPieceDesc> descs;
+    std::vector<uint32_t> index;
+    std::vector<const uint16_t*> ptrs;
+    int64_t blocks = 0;
+    try {
+        ptrs.assign(static_cast<size_t>(T * n_replicas), nullptr);
+        std::vector<char> vec_ok(static_cast<size_t>(T), 1);
+        for (int64_t t = 0; t < T; ++t)
+            for (int32_t k = 0; k < n_replicas; ++k) {
+                const uint16_t* q = replica_tensors[static_cast<int64_t>(k) * T + t];
+                ptrs[static_cast<size_t>(t * n_replicas + k)] = q;
+                if ((reinterpret_cast<uintptr_t>(q) & 15) != 0) vec_ok[static_cast<size_t>(t)] = 0;
+            }
+        const bool out_ok = (reinterpret_cast<uintptr_t>(shard_grad) & 15) == 0;
+        auto add = [&](int32_t t, int64_t src_off, int64_t dst_off, int64_t len) -> zero_status {
+            if (len <= 0) return ZERO_OK;
+            const int64_t b = len / kRChunk + (len % kRChunk != 0 ? 1 : 0);
+            if (b > 0x7FFFFFFF - blocks || descs.size() >= 0xFFFFFFFFu)
+                return fail(ZERO_ERANGE, std::string(who) + ": more than 2^31 workgroups");
+            RPieceDesc dsc{};
+            dsc.src_off = src_off;
+            dsc.dst_off = dst_off;
+            dsc.len = len;
+            dsc.first_block = blocks;
+            dsc.tensor = t;
+            dsc.vec = t >= 0 && out_ok && vec_ok[static_cast<size_t>(t)] && src_off % 8 == 0 &&
+                      dst_off % 8 == 0;
+            index.insert(index.end(), static_cast<size_t>(b), static_cast<uint32_t>(descs.size()));
+            descs.push_back(dsc);
+            blocks += b;
+            return ZERO_OK;
+        };
+        int64_t pos = 0;
+        for (const zero_segment& seg : segs) {
+            if (seg.length <= 0) continue;
+            for (int32_t k = 0; k < n_replicas; ++k)
+                if (ptrs[static_cast<size_t>(seg.tensor * static_cast<int64_t>(n_replicas) + k)] == nullptr)
+                    return fail(ZERO_EINVAL, std::string(who) + ": NULL tensor " +
+                                                 std::to_string(seg.tensor) + " of replica " + std::to_string(k));
+            zero_status st = add(-1, 0, pos, seg.shard_offset - pos);
+            if (st == ZERO_OK) st = add(seg.tensor, seg.tensor_offset, seg.shard_offset, seg.length);
+            if (st != ZERO_OK) return st;
+            pos = seg.shard_offset + seg.length;
+        }
+        const zero_status st = add(-1, 0, pos, plan->shard - pos);
+        if (st != ZERO_OK) return st;
+        if (blocks > 0) index = zero::xcd_major_index(index);
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, std::string(who) + ": host allocation failed");
+    }
+    zero_reduce_table* tab = nullptr;
+    try {
+        tab = new zero_reduce_table;
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, std::string(who) + ": host allocation failed");
+    }
+    tab->out = shard_grad;
+    tab->n_rep = n_replicas;
+    tab->blocks = blocks;
+    zero_status st = ZERO_OK;
+    if (blocks > 0) {                // an empty shard needs no device
+        auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+        const size_t desc_bytes = up(descs.size() * sizeof(RPieceDesc));
+        const size_t index_bytes = up(index.size() * sizeof(uint32_t));
+        const size_t ptr_bytes = up(ptrs.size() * sizeof(const uint16_t*));
+        const int64_t level1 = (blocks + kFinishChunk - 1) / kFinishChunk;
+        const size_t part_bytes = static_cast<size_t>(blocks + level1) * sizeof(double);
+        st = zero::check_hip(hipGetDevice(&tab->device), who);
+        if (st == ZERO_OK)
+            st = zero::check_hip(hipMalloc(&tab->mem, desc_bytes + index_bytes + ptr_bytes + part_bytes), who);
+        if (st == ZERO_OK) {
+            char* m = static_cast<char*>(tab->mem);
+            tab->table = reinterpret_cast<const RPieceDesc*>(m);
+            tab->index = reinterpret_cast<const uint32_t*>(m + desc_bytes);
+            tab->ptrs = reinterpret_cast<const uint16_t* const*>(m + desc_bytes + index_bytes);
+            tab->partials = reinterpret_cast<double*>(m + desc_bytes + index_bytes + ptr_bytes);
+            st = zero::check_hip(hipMemcpy(m, descs.data(), descs.size() * sizeof(RPieceDesc),
+                                           hipMemcpyHostToDevice), who);
+            if (st == ZERO_OK)
+                st = zero::check_hip(hipMemcpy(m + desc_bytes, index.data(), index.size() * sizeof(uint32_t),
+                                               hipMemcpyHostToDevice), who);
+            if (st == ZERO_OK)
+                st = zero::check_hip(hipMemcpy(m + desc_bytes + index_bytes, ptrs.data(),
+                                               ptrs.size() * sizeof(const uint16_t*), hipMemcpyHostToDevice),
+                                     who);
+        }
+    }
+    if (st != ZERO_OK) {
+        if (tab->mem) (void)hipFree(tab->mem);
+        delete tab;
+        return st;
+    }
+    *out = tab;
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_reduce_table_run(const zero_reduce_table* table, double* sqnorm_out,
+                                             hipStream_t stream) {
+    using zero::fail;
+    zero::clear_error();
+    if (table == nullptr) return fail(ZERO_EINVAL, "zero_reduce_table_run: NULL table");
+    if (table->blocks == 0) {
+        if (sqnorm_out == nullptr) return ZERO_OK;
+        hipLaunchKernelGGL(write_zero, dim3(1), dim3(64), 0, stream, sqnorm_out);
+        return zero::check_hip(hipGetLastError(), "zero_reduce_table_run launch");
+    }
+    int dev = -1;
+    zero_status st = zero::check_hip(hipGetDevice(&dev), "zero_reduce_table_run: hipGetDevice");
+    if (st != ZERO_OK) return st;
+    if (dev != table->device)
+        return fail(ZERO_EINVAL, "zero_reduce_table_run: the table lives on device " +
+                                     std::to_string(table->device) + ", the current device is " +
+                                     std::to_string(dev));
+    double* const parts = sqnorm_out != nullptr ? table->partials : nullptr;
+    // A dispatch holds fewer than 2^32 work-items: longer tables take several launches.
+    constexpr int64_t kMaxBlocks = zero::kTableLaunchBlocks;
+    for (int64_t b0 = 0; b0 < table->blocks; b0 += kMaxBlocks) {
+        const int64_t nb = table->blocks - b0 < kMaxBlocks ? table->blocks - b0 : kMaxBlocks;
+        const int64_t per = (nb + 7) / 8;
+        hipLaunchKernelGGL(reduce_table_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, stream,
+                           table->table, table->index, table->ptrs, table->n_rep, table->out, b0, per,
+                           parts);
+        st = zero::check_hip(hipGetLastError(), "zero_reduce_table_run launch");
+        if (st != ZERO_OK) return st;
+    }
+    if (sqnorm_out == nullptr) return ZERO_OK;
+    // partials[0, blocks) -> first-level sums after them -> the total
+    const int64_t level1 = (table->blocks + kFinishChunk - 1) / kFinishChunk;
+    hipLaunchKernelGGL(finish_chunks, dim3(static_cast<unsigned>(level1)), dim3(kThreads), 0, stream,
+                       table->partials, table->blocks, table->partials + table->blocks);
+    st = zero::check_hip(hipGetLastError(), "zero_reduce_table_run finish launch");
+    if (st != ZERO_OK) return st;
+    hipLaunchKernelGGL(finish_sum, dim3(1), dim3(kThreads), 0, stream, table->partials + table->blocks,
+                       static_cast<int>(level1), sqnorm_out);
+    return zero::check_hip(hipGetLastError(), "zero_reduce_table_run finish launch");
+}
+
+extern "C" int64_t zero_reduce_table_blocks(const zero_reduce_table* table) {
+    return table ? table->blocks : -1;
+}
+
+extern "C" void zero_reduce_table_free(zero_reduce_table* table) {
+    if (!table) return;
+    if (table->mem) (void)hipFree(table->mem);
+    delete table;
+}
+
 // ------------------------------------------------------------ no allocation
 //
 // For callers that cannot allocate (code under graph capture, tight serving
