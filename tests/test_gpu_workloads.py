@@ -347,3 +347,65 @@ def test_rank_step_without_clip_over_bucket_windows(zm, fuse, R):
     assert sorted(k[0] if isinstance(k, tuple) else k for k in rs._calls) == (
         ["gather"] + ["reduce_update"] * 3 if fused else ["adamw", "gather"] + ["reduce"] * 3)
 
+
+@pytest.mark.parametrize("layout", ["flat", "shard0"])
+def test_rank_step_reduce_from_per_tensor_replicas(zm, layout):
+    """RankStep.reduce_tensors (a zero_reduce_table over per-tensor replicas),
+    then clip and AdamW, two steps with new values in the same buffers: the
+    oracle's rank step over the flattened replicas, bit for bit except the
+    clip coefficient's last bit (the partials' order)."""
+    from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep
+    numels = [1000 * 16, 37 * 16, 4096, 3 * 16, 777 * 16]
+    dim0 = [1000, 37, 4096, 3, 777]
+    n_ranks, rank, R = 4, 2, 3
+    if layout == "flat":
+        plan = zm.zero_partition_plan(numels, n_ranks, 128)
+        ref = oracle.partition_plan(numels, n_ranks, 128)
+        flatten = oracle.flatten_params
+    else:
+        plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, 128)
+        ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, 128)
+        flatten = oracle.flatten_params_shard0
+    S = ref.shard_numel
+    hyper = Hyper()
+    rs = RankStep(plan, rank, 1, hyper, 1.0, dev(), gather=True)
+    rng = np.random.default_rng(61)
+    master = np.zeros(S, np.float32)
+    covered = np.zeros(S, bool)
+    for (_, _, soff, ln) in ref.segments(rank):
+        covered[soff:soff + ln] = True
+    master[covered] = (rng.standard_normal(int(covered.sum())) * 0.02).astype(np.float32)
+    rs.master.copy_(torch.from_numpy(master))
+    shards = [oracle.f32_to_bf16((rng.standard_normal(S) * 0.02).astype(np.float32)) for _ in range(n_ranks)]
+    for r in range(n_ranks):
+        if r != rank:
+            rs.param_shards[r].copy_(to_dev_u16(shards[r]))
+    shards[rank] = np.zeros(S, np.uint16)
+    state = {"master": master.copy(), "exp_avg": np.zeros(S, np.float32),
+             "exp_avg_sq": np.zeros(S, np.float32)}
+    d_reps = [[torch.empty(n, dtype=torch.int16, device=dev()) for n in numels] for _ in range(R)]
+    remote = [0.4, 0.0, 0.0, 0.3]
+    for t in (1, 2):
+        reps_h = [[oracle.f32_to_bf16((rng.standard_normal(n) * 0.05).astype(np.float32)) for n in numels]
+                  for _ in range(R)]
+        for dr, hr in zip(d_reps, reps_h):
+            for d, h in zip(dr, hr):
+                d.copy_(to_dev_u16(h))
+        rs.set_remote_partials(remote)
+        rs.reduce_tensors(d_reps)
+        rs.clip()
+        rs.adamw()
+        rs.gather()
+        flats = [flatten(ref, rep) for rep in reps_h]
+        want = oracle.rank_step(ref, rank, flats, 0, state, shards, remote, t, hyper.as_kwargs(), 1.0)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_u16(rs.grad), want["shard_grad"], f"step {t} gradient")
+        got_part = float(rs.partials[n_ranks].item())
+        assert abs(got_part - want["partials"][rank]) <= 1e-12 * want["partials"][rank]
+        for got, key in ((rs.master, "master"), (rs.exp_avg, "exp_avg"), (rs.exp_avg_sq, "exp_avg_sq")):
+            assert_f32_close(host_f32(got), state[key], f"step {t} {key}")
+        assert_bf16_close(host_u16(rs.param_shards[rank]), shards[rank], f"step {t} shard")
+        for i, (a, b) in enumerate(zip(rs.tensors, want["tensors"])):
+            assert_bf16_close(host_u16(a), b, f"step {t} tensor {i}")
+    assert list(rs._calls).count("reduce_tensors") == 1
+

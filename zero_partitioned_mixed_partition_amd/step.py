@@ -138,6 +138,21 @@ class RankStep:
                 self.plan, self.rank, reps, begin, count, self.grad,
                 self.partials[nd + w:nd + w + 1], self.workspace, st), sig)()
 
+    def reduce_tensors(self, replicas: Sequence[Sequence[torch.Tensor]], stream=None):
+        """The reduce from replicas that are still per-tensor (replicas[k][t]
+        = replica k's tensor t), through a zero_reduce_table built on first use
+        for these buffers: the same gradient as flattening every replica and
+        calling reduce() over the whole flat buffer, with the rank's norm
+        partial in the one window slot (the step must be built with
+        n_windows=1)."""
+        if self.n_windows != 1:
+            raise ValueError("the per-tensor reduce fills one window slot: build the step with n_windows=1")
+        nd = self.plan.num_ranks
+        sig = tuple(t.data_ptr() for rep in replicas for t in rep)
+        self._prepared("reduce_tensors", stream, lambda st: zb.ReduceTable(
+            self.plan, self.rank, replicas, self.grad).prepare_run(
+                self.partials[nd:nd + 1], st), sig)()
+
     def clip(self, stream=None):
         if self.max_norm > 0:
             self._prepared("clip", stream, lambda st: zb.prepare_clip_scale(
