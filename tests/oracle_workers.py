@@ -61,6 +61,19 @@ def reduce_windows(tasks, workers=None):
         return list(ex.map(_reduce_window, tasks, chunksize=1))
 
 
+def _reduce_window_sqnorm(args):
+    """The exact squared-norm state of the oracle's reduce over one window
+    (as _reduce_window, without returning the bits)."""
+    return _reduce_window(args)[1]
+
+
+def reduce_window_sqnorms(tasks, workers=None):
+    """Per task (as reduce_windows), the exact squared-norm state of the
+    oracle's reduced gradient over that window, in task order."""
+    with _pool(workers) as ex:
+        return list(ex.map(_reduce_window_sqnorm, tasks, chunksize=1))
+
+
 def digest(a) -> str:
     """128-bit digest of an array's bytes: two arrays agree bit for bit exactly
     when their digests do (up to a 2^-128 collision)."""

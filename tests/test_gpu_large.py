@@ -19,7 +19,9 @@ llama3-70b  Llama-3-70B list, N_d = 8, rank 7 (8,819,213,312 elements, indices
             starts and 32 random 1M windows.
 past 2^32   the one-pass reduce and AdamW over a 4,299,161,984-element shard
             (two rows of workgroups), on windows around 2^31, 2^32, the row
-            boundary and the padding.
+            boundary and the padding; the reduce table over a 4,296,020,096-
+            element shard from per-tensor replicas (windows, and the whole
+            squared norm against the oracle's reduce of every window).
 """
 import math
 
@@ -485,4 +487,56 @@ def test_reduce_adamw_one_pass_past_2p32_elements(zm):
     if phi < S:                                           # padding: zero gradient, state stays 0
         assert not host_u16(grad[phi:S]).any() and not host_f32(master[phi:S]).any()
     del master, m, v, param, grad
+    _free_gpu()
+
+
+def test_reduce_table_past_2p32_elements(zm):
+    """zero_reduce_table_* over a shard of more than 2^32 elements (N_d = 1,
+    one tensor of 2^32 + 2^20 + 5 parameters and a small one after it, 2
+    per-tensor replicas): gradient bits on windows at both ends, around 2^31,
+    2^32, the tensor boundary and the padding, and the full squared norm,
+    against the oracle over the generated flat replicas."""
+    big = 2 ** 32 + 2 ** 20 + 5
+    numels = [big, 4099]
+    ref = oracle.partition_plan(numels, 1, 128)
+    plan = zm.zero_partition_plan(numels, 1, 128)
+    S, phi, R, seed = ref.shard_numel, ref.numel, 2, 88
+    assert S > 2 ** 32 and S > phi
+    reps = []
+    for k in range(R):
+        rep = []
+        for n, off in zip(numels, ref.offsets):
+            t = torch.empty(n, dtype=torch.int16, device=dev())
+            synth.device_normal_bf16(t, seed, synth.KIND_REPLICA, 1, k, off, phi, synth.GRAD_SIGMA)
+            rep.append(t)
+        reps.append(rep)
+    grad = torch.full((S,), 0x5555, dtype=torch.int16, device=dev())
+    sq = torch.zeros(1, dtype=torch.float64, device=dev())
+    table = zm.ReduceTable(plan, 0, reps, grad)
+    note(f"reduce table past 2^32: S={S}, {table.blocks} workgroups, R={R}")
+    table.run(sqnorm_out=sq)
+    torch.cuda.synchronize()
+    del table, reps
+    wins = _windows_in_shards([0, 2 ** 31, 2 ** 32, big, phi, S], 2048, S, 1, S)
+    for a, b in wins:
+        n = b - a
+        flats = [synth.normal_bf16(n, seed, synth.KIND_REPLICA, 1, k, a, phi, synth.GRAD_SIGMA)
+                 for k in range(R)]
+        window = oracle.partition_plan([n], 1, 1)          # the reduce is elementwise
+        want = np.zeros(n, np.uint16)
+        oracle.reduce_shard(window, 0, flats, 0, want)
+        assert_bits_equal(host_u16(grad[a:b]), want, f"gradient [{a},{b})")
+    # the whole squared norm: the oracle's reduce of every window of the
+    # generated replicas (process pool), its exact norm states merged in order
+    from oracle_workers import reduce_window_sqnorms
+    chunk = 1 << 26
+    tasks = [(numels, 1, 128, 0, seed, synth.KIND_REPLICA, 1, R, a, min(a + chunk, S), synth.GRAD_SIGMA)
+             for a in range(0, S, chunk)]
+    note(f"reduce table past 2^32: oracle norm over {len(tasks)} windows (process pool)")
+    acc = oracle.SqnormAccumulator()
+    for part in reduce_window_sqnorms(tasks, workers=16):
+        acc.merge(part)
+    want_sq = acc.value()
+    assert abs(float(sq.item()) - want_sq) <= 1e-12 * want_sq, (float(sq.item()), want_sq)
+    del grad
     _free_gpu()
