@@ -732,6 +732,13 @@ static_assert(sizeof(RPieceDesc) == 64, "one 64-byte descriptor per piece");
 namespace {
 
 constexpr int64_t kRChunk = int64_t(kThreads) * 8;   // elements per workgroup
+// Workgroups of the grid-stride form (0, default: one workgroup per chunk, one
+// pass). Measured on MI355X, GPT-2 rank 7 from 8 per-tensor replicas, two
+// rounds: one pass 50.5-50.9 us; grids of 1,024, 2,048 and 4,096 workgroups
+// 55.7-56.1, 55.8-56.1 and 51.9-52.1 us.
+#ifndef ZERO_RTABLE_GRID
+#define ZERO_RTABLE_GRID 0
+#endif
 // 1: the 16-byte path issues each batch of replica loads together
 // (zero::dev::for_replicas); 0 (default): a guarded load per replica. Measured
 // on MI355X, GPT-2 rank 7 from 8 per-tensor replicas, two rounds: 51.3-51.5 us
@@ -740,18 +747,14 @@ constexpr int64_t kRChunk = int64_t(kThreads) * 8;   // elements per workgroup
 #define ZERO_RTABLE_BATCHED_ISSUE 0
 #endif
 
-__global__ __launch_bounds__(kThreads) void reduce_table_kernel(const RPieceDesc* __restrict__ table,
-                                                                const uint32_t* __restrict__ index,
-                                                                const uint16_t* const* __restrict__ ptrs,
-                                                                int n_rep, uint16_t* __restrict__ out,
-                                                                int64_t blk0, int64_t per,
-                                                                double* __restrict__ partials) {
-    const int64_t blk = blk0 + static_cast<int64_t>(blockIdx.x);
-    const RPieceDesc d = table[index[zero::dev::xcd_major_entry(blk0, per)]];
+// Workgroup chunk `blk` of piece d: its gradient elements, and their squares
+// added to this thread's sq.
+__device__ __forceinline__ void reduce_table_chunk(const RPieceDesc& d, int64_t blk,
+                                                   const uint16_t* const* __restrict__ ptrs, int n_rep,
+                                                   uint16_t* __restrict__ out, double& sq) {
     const int64_t start = (blk - d.first_block) * kRChunk;
     const int64_t len = d.len - start < kRChunk ? d.len - start : kRChunk;
     uint16_t* const o = out + d.dst_off + start;
-    double sq = 0.0;
     if (d.tensor < 0) {
         for (int64_t e = threadIdx.x; e < len; e += kThreads) o[e] = 0;
     } else {
@@ -808,7 +811,31 @@ __global__ __launch_bounds__(kThreads) void reduce_table_kernel(const RPieceDesc
             for (int64_t i = threadIdx.x; i < len; i += kThreads) one(i);
         }
     }
+}
+
+__global__ __launch_bounds__(kThreads) void reduce_table_kernel(const RPieceDesc* __restrict__ table,
+                                                                const uint32_t* __restrict__ index,
+                                                                const uint16_t* const* __restrict__ ptrs,
+                                                                int n_rep, uint16_t* __restrict__ out,
+                                                                int64_t blk0, int64_t per,
+                                                                double* __restrict__ partials) {
+    const int64_t blk = blk0 + static_cast<int64_t>(blockIdx.x);
+    double sq = 0.0;
+    reduce_table_chunk(table[index[zero::dev::xcd_major_entry(blk0, per)]], blk, ptrs, n_rep, out, sq);
     if (partials != nullptr) store_partial(sq, partials + blk0);
+}
+
+// Grid-stride form (one launch of at most kTableLaunchBlocks chunks): workgroup
+// x takes chunks x, x + G, x + 2G, ... (G = gridDim.x), each found through the
+// launch's XCD-major index, and leaves one partial.
+__global__ __launch_bounds__(kThreads) void reduce_table_stride_kernel(
+        const RPieceDesc* __restrict__ table, const uint32_t* __restrict__ index,
+        const uint16_t* const* __restrict__ ptrs, int n_rep, uint16_t* __restrict__ out,
+        int64_t blocks, int64_t per, double* __restrict__ partials) {
+    double sq = 0.0;
+    for (int64_t blk = blockIdx.x; blk < blocks; blk += gridDim.x)
+        reduce_table_chunk(table[index[(blk & 7) * per + (blk >> 3)]], blk, ptrs, n_rep, out, sq);
+    if (partials != nullptr) store_partial(sq, partials);
 }
 
 }  // namespace
@@ -961,7 +988,15 @@ extern "C" zero_status zero_reduce_table_run(const zero_reduce_table* table, dou
     double* const parts = sqnorm_out != nullptr ? table->partials : nullptr;
     // A dispatch holds fewer than 2^32 work-items: longer tables take several launches.
     constexpr int64_t kMaxBlocks = zero::kTableLaunchBlocks;
-    for (int64_t b0 = 0; b0 < table->blocks; b0 += kMaxBlocks) {
+    int64_t n_parts = table->blocks;
+    if (ZERO_RTABLE_GRID > 0 && table->blocks <= kMaxBlocks) {
+        n_parts = table->blocks < ZERO_RTABLE_GRID ? table->blocks : ZERO_RTABLE_GRID;
+        hipLaunchKernelGGL(reduce_table_stride_kernel, dim3(static_cast<unsigned>(n_parts)), dim3(kThreads),
+                           0, stream, table->table, table->index, table->ptrs, table->n_rep, table->out,
+                           table->blocks, (table->blocks + 7) / 8, parts);
+        st = zero::check_hip(hipGetLastError(), "zero_reduce_table_run launch");
+        if (st != ZERO_OK) return st;
+    } else for (int64_t b0 = 0; b0 < table->blocks; b0 += kMaxBlocks) {
         const int64_t nb = table->blocks - b0 < kMaxBlocks ? table->blocks - b0 : kMaxBlocks;
         const int64_t per = (nb + 7) / 8;
         hipLaunchKernelGGL(reduce_table_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, stream,
@@ -971,13 +1006,13 @@ extern "C" zero_status zero_reduce_table_run(const zero_reduce_table* table, dou
         if (st != ZERO_OK) return st;
     }
     if (sqnorm_out == nullptr) return ZERO_OK;
-    // partials[0, blocks) -> first-level sums after them -> the total
-    const int64_t level1 = (table->blocks + kFinishChunk - 1) / kFinishChunk;
+    // partials[0, n_parts) -> first-level sums after them -> the total
+    const int64_t level1 = (n_parts + kFinishChunk - 1) / kFinishChunk;
     hipLaunchKernelGGL(finish_chunks, dim3(static_cast<unsigned>(level1)), dim3(kThreads), 0, stream,
-                       table->partials, table->blocks, table->partials + table->blocks);
+                       table->partials, n_parts, table->partials + n_parts);
     st = zero::check_hip(hipGetLastError(), "zero_reduce_table_run finish launch");
     if (st != ZERO_OK) return st;
-    hipLaunchKernelGGL(finish_sum, dim3(1), dim3(kThreads), 0, stream, table->partials + table->blocks,
+    hipLaunchKernelGGL(finish_sum, dim3(1), dim3(kThreads), 0, stream, table->partials + n_parts,
                        static_cast<int>(level1), sqnorm_out);
     return zero::check_hip(hipGetLastError(), "zero_reduce_table_run finish launch");
 }
