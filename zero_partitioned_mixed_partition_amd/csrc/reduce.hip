@@ -9,9 +9,10 @@
 // summed in replica order in fp32, divided by R, rounded once to bf16.
 //
 // Memory: per shard element R bf16 reads and one bf16 write, (2R + 2) bytes.
-// Each thread handles 8 elements per 16-byte access and keeps up to 8 replica
-// loads in flight before it adds them, in order, into its accumulators; the
-// grid is capped and threads stride. Large windows of at most 8 replicas,
+// Each thread handles 8 elements per 16-byte access and takes the replicas in
+// batches of 8, adding them in order into its accumulators (the guarded load
+// per replica compiles to one load in flight at a time, which measured faster
+// here than issuing a batch at once); the grid is capped and threads stride. Large windows of at most 8 replicas,
 // given a workspace for a partial per workgroup, take a one-pass form instead
 // (a lane per element pair, the grid covering the window once); so does the
 // standalone squared norm on large inputs. Both sum the partials in two
@@ -57,7 +58,7 @@ constexpr int kMaxPartials = ZERO_REDUCE_MAX_BLOCKS > ZERO_SQNORM_MAX_BLOCKS
 #ifndef ZERO_REDUCE_BATCH
 #define ZERO_REDUCE_BATCH 8
 #endif
-constexpr int kReplicaBatch = ZERO_REDUCE_BATCH;   // replica loads in flight per thread
+constexpr int kReplicaBatch = ZERO_REDUCE_BATCH;   // replicas per load batch
 // 1: the grid-stride kernel's replica loads through zero::dev::for_replicas
 // (each batch issued at once, the adds after). 0 (default): a guarded load per
 // replica, which the compiler issues one at a time. Measured on MI355X, 64
