@@ -75,6 +75,9 @@ def parse_args(argv=None):
                     help="rough budget for the oracle's host timing (0 disables it)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only this many steps, untimed, for a profiler (no JSON)")
+    ap.add_argument("--profile-extra", action="store_true",
+                    help="with --profile-steps: first run each phase timed outside the step once "
+                         "(the step's dispatches stay the run's last ones)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="with --profile-steps: first copy 1 GiB once (a plain copy kernel of known "
                          "size, to scale hardware byte counters)")
@@ -974,6 +977,9 @@ def main(argv=None):
             dst.copy_(src)                      # reads 1 GiB, writes 1 GiB
             torch.cuda.synchronize()
             del src, dst
+        if args.profile_extra:
+            for _, fn in getattr(wl, "extra_phases", None) or []:
+                fn()
         for _ in range(args.profile_steps):
             run_step(wl)
         torch.cuda.synchronize()
