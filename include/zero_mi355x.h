@@ -491,7 +491,8 @@ void zero_copy_table_free(zero_copy_table* table);
  * synchronous hipMemcpy on the current device, once). The table keeps the
  * pointers, not the data: the caller keeps the buffers alive and in place.
  * Errors: ZERO_EINVAL (NULL out, plan, replica_tensors or shard_grad; rank or
- * R out of range; a NULL replica tensor the shard needs); ZERO_ERANGE (2^31
+ * R out of range; a NULL replica tensor the shard needs, or one that overlaps
+ * shard_grad); ZERO_ERANGE (2^31
  * workgroups or more); ZERO_ENOMEM; ZERO_EHIP.
  * Run: enqueued on stream, with the table's device current (ZERO_EINVAL
  * otherwise); sqnorm_out (device double, nullable) receives the squared

@@ -185,6 +185,9 @@ def test_reduce_table_rejects_bad_arguments_before_touching_the_gpu(zm):
     missing[1 * T + 2] = None               # replica 1's tensor 2, which rank 1's shard needs
     assert create(rank=1, reps=missing) == E
     assert "replica 1" in zm.zero_last_error()
+    # shard_grad (2016 elements) inside replica 0's tensor 2 (3000 elements at 0x300000)
+    assert create(rank=1, g=ctypes.c_void_p(0x300000 + 1000)) == E
+    assert "overlaps" in zm.zero_last_error()
     assert lib._rt_run(None, None, None) == E
     assert lib._rt_blocks(None) == -1
     lib._rt_free(None)

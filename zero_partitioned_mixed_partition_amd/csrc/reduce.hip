@@ -905,13 +905,22 @@ extern "C" zero_status zero_reduce_table_create(const zero_plan* plan, int32_t r
             blocks += b;
             return ZERO_OK;
         };
+        const uintptr_t out_lo = reinterpret_cast<uintptr_t>(shard_grad);
+        const uintptr_t out_hi = out_lo + static_cast<uintptr_t>(plan->shard) * 2;
         int64_t pos = 0;
         for (const zero_segment& seg : segs) {
             if (seg.length <= 0) continue;
-            for (int32_t k = 0; k < n_replicas; ++k)
-                if (ptrs[static_cast<size_t>(seg.tensor * static_cast<int64_t>(n_replicas) + k)] == nullptr)
+            for (int32_t k = 0; k < n_replicas; ++k) {
+                const uint16_t* q = ptrs[static_cast<size_t>(seg.tensor * static_cast<int64_t>(n_replicas) + k)];
+                if (q == nullptr)
                     return fail(ZERO_EINVAL, std::string(who) + ": NULL tensor " +
                                                  std::to_string(seg.tensor) + " of replica " + std::to_string(k));
+                const uintptr_t lo = reinterpret_cast<uintptr_t>(q);
+                const uintptr_t hi = lo + static_cast<uintptr_t>(plan->numels[static_cast<size_t>(seg.tensor)]) * 2;
+                if (lo < out_hi && out_lo < hi)
+                    return fail(ZERO_EINVAL, std::string(who) + ": shard_grad overlaps tensor " +
+                                                 std::to_string(seg.tensor) + " of replica " + std::to_string(k));
+            }
             zero_status st = add(-1, 0, pos, seg.shard_offset - pos);
             if (st == ZERO_OK) st = add(seg.tensor, seg.tensor_offset, seg.shard_offset, seg.length);
             if (st != ZERO_OK) return st;
