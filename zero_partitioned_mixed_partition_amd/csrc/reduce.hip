@@ -732,7 +732,15 @@ static_assert(sizeof(RPieceDesc) == 64, "one 64-byte descriptor per piece");
 
 namespace {
 
-constexpr int64_t kRChunk = int64_t(kThreads) * 8;   // elements per workgroup
+// 2,048-element groups per workgroup (the descriptor lookup is paid once per
+// workgroup). Measured on MI355X, GPT-2 rank 7 from 8 per-tensor replicas, two
+// rounds, flat plan: 1 group 49.4-49.9 us, 2 groups 50.7-50.8 us, 4 groups
+// 54.7-54.8 us (Shard(0): 51.8-52.0, 52.7-52.9, 57.7-58.0 us). One stays.
+#ifndef ZERO_RTABLE_GROUPS
+#define ZERO_RTABLE_GROUPS 1
+#endif
+constexpr int kRGroups = ZERO_RTABLE_GROUPS;
+constexpr int64_t kRChunk = int64_t(kThreads) * 8 * kRGroups;   // elements per workgroup
 // Workgroups of the grid-stride form (0, default: one workgroup per chunk, one
 // pass). Measured on MI355X, GPT-2 rank 7 from 8 per-tensor replicas, two
 // rounds: one pass 50.5-50.9 us; grids of 1,024, 2,048 and 4,096 workgroups
@@ -769,7 +777,8 @@ __device__ __forceinline__ void reduce_table_chunk(const RPieceDesc& d, int64_t 
             o[e] = h;
             sq += sq1(h);
         };
-        const int64_t e = static_cast<int64_t>(threadIdx.x) * 8;
+        for (int g = 0; g < kRGroups; ++g) {
+        const int64_t e = (static_cast<int64_t>(g) * kThreads + threadIdx.x) * 8;
         if (d.vec && e + 8 <= len) {
             float acc[8];
 #pragma unroll
@@ -808,8 +817,9 @@ __device__ __forceinline__ void reduce_table_chunk(const RPieceDesc& d, int64_t 
             zero::dev::st_stream(reinterpret_cast<u32x4*>(o + e), w);
         } else if (d.vec) {                               // the chunk's ragged end
             for (int64_t i = e; i < len; ++i) one(i);
-        } else {
+        } else if (g == 0) {
             for (int64_t i = threadIdx.x; i < len; i += kThreads) one(i);
+        }
         }
     }
 }
