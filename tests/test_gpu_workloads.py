@@ -409,3 +409,60 @@ def test_rank_step_reduce_from_per_tensor_replicas(zm, layout):
             assert_bf16_close(host_u16(a), b, f"step {t} tensor {i}")
     assert list(rs._calls).count("reduce_tensors") == 1
 
+
+
+def test_rank_step_per_parameter_state_matches_flat_state(zm):
+    """RankStep(per_param=True), FSDP-2's optimizer layout (fp32 state per
+    parameter chunk, the multi-tensor AdamW through its table), against the
+    flat-state RankStep on the same Shard(0) plan and inputs, three clipped
+    steps: every chunk's master, m and v equal the flat state's slice bit for
+    bit, and so do the parameter shard and the gathered tensors; the flat
+    step itself is the oracle's (checked on the last step)."""
+    from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep
+    numels = [1000 * 16, 37 * 16, 4096, 3 * 16, 777 * 16]
+    dim0 = [1000, 37, 4096, 3, 777]
+    n_ranks, rank, R = 4, 1, 3
+    plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, 128)
+    ref = oracle.partition_plan_shard0(numels, dim0, n_ranks, 128)
+    P, S = ref.padded_numel, ref.shard_numel
+    hyper = Hyper()
+    flat = RankStep(plan, rank, 1, hyper, 1.0, dev(), gather=True)
+    pp = RankStep(plan, rank, 1, hyper, 1.0, dev(), gather=True, per_param=True)
+    rng = np.random.default_rng(71)
+    segs = ref.segments(rank)
+    master = np.zeros(S, np.float32)
+    for (_, _, soff, ln) in segs:
+        master[soff:soff + ln] = (rng.standard_normal(ln) * 0.02).astype(np.float32)
+    flat.master.copy_(torch.from_numpy(master))
+    for t, (_, _, soff, ln) in zip(pp.master_tensors, segs):
+        t.copy_(torch.from_numpy(master[soff:soff + ln]))
+    shards = [oracle.f32_to_bf16((rng.standard_normal(S) * 0.02).astype(np.float32)) for _ in range(n_ranks)]
+    for r in range(n_ranks):
+        if r != rank:
+            flat.param_shards[r].copy_(to_dev_u16(shards[r]))
+            pp.param_shards[r].copy_(to_dev_u16(shards[r]))
+    shards[rank] = np.zeros(S, np.uint16)
+    state = {"master": master.copy(), "exp_avg": np.zeros(S, np.float32),
+             "exp_avg_sq": np.zeros(S, np.float32)}
+    remote = [0.4, 0.0, 0.2, 0.3]
+    for t in (1, 2, 3):
+        reps_h = [synth.normal_bf16(P, 72, synth.KIND_REPLICA, t, k, 0, ref.numel, 0.05) for k in range(R)]
+        reps = [to_dev_u16(x) for x in reps_h]
+        for rs in (flat, pp):
+            rs.set_remote_partials(remote)
+            rs.step([(0, P, reps)])
+        want = oracle.rank_step(ref, rank, reps_h, 0, state, shards, remote, t, hyper.as_kwargs(), 1.0)
+    torch.cuda.synchronize()
+    for name, flat_arr, tensors in (("master", flat.master, pp.master_tensors),
+                                    ("exp_avg", flat.exp_avg, pp.exp_avg_tensors),
+                                    ("exp_avg_sq", flat.exp_avg_sq, pp.exp_avg_sq_tensors)):
+        fa = host_f32(flat_arr)
+        for i, (x, (_, _, soff, ln)) in enumerate(zip(tensors, segs)):
+            assert_bits_equal(host_f32(x).view(np.uint32), fa[soff:soff + ln].view(np.uint32),
+                              f"{name} of chunk {i}")
+        assert_f32_close(fa, state[name], f"flat {name} against the oracle")
+    assert_bits_equal(host_u16(pp.param_shards[rank]), host_u16(flat.param_shards[rank]), "parameter shard")
+    for i, (a, b) in enumerate(zip(pp.tensors, flat.tensors)):
+        assert_bits_equal(host_u16(a), host_u16(b), f"tensor {i}")
+    for i, (a, b) in enumerate(zip(flat.tensors, want["tensors"])):
+        assert_bf16_close(host_u16(a), b, f"tensor {i} against the oracle")

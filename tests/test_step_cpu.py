@@ -104,6 +104,21 @@ def test_rank_step_chooses_the_one_pass_update_only_where_it_applies(step):
     with pytest.raises(ValueError, match="window count"):
         rs.reduce_update([(3500, 700, reps(5))])
     rs = step.RankStep(plan, 2, 1, step.Hyper(), 1.0, torch.device("cpu"), gather=False)
-    with pytest.raises(ValueError, match="without clipping"):
+    with pytest.raises(ValueError, match="without"):
         rs.reduce_update([(3500, 700, reps(5))])
     assert rs.t == 0
+    # per-parameter state keeps the two calls, and cannot be combined with offload
+    rs = step.RankStep(plan, 2, 3, step.Hyper(), 0.0, torch.device("cpu"), gather=False,
+                       per_param=True)
+    calls = []
+    rs.reduce_update = lambda w, s=None: calls.append("one-pass")
+    rs.reduce = lambda w, s=None: calls.append("reduce")
+    rs.clip = lambda s=None: calls.append("clip")
+    rs.adamw = lambda s=None: calls.append("adamw")
+    rs.gather = lambda s=None: calls.append("gather")
+    rs.step(disjoint)
+    assert calls == two_calls
+    assert rs.master is None and len(rs.master_tensors) == len(plan.segments(2))
+    assert [t.numel() for t in rs.master_tensors] == [ln for (_, _, _, ln) in plan.segments(2)]
+    with pytest.raises(ValueError, match="separate layouts"):
+        step.RankStep(plan, 2, 1, step.Hyper(), 1.0, torch.device("cpu"), offload=True, per_param=True)

@@ -62,6 +62,17 @@ class RankStep:
                  updates each window in one pass (reduce_update) when every
                  window has at most FUSE_MAX_REPLICAS replicas. Such a step
                  leaves self.grad and the own norm partials as they were.
+    per_param    FSDP-2's optimizer-state layout ("FSDP-2: Per-Parameter
+                 Sharding via DTensor (fully_shard)"): every segment of the
+                 rank's shard (a parameter's local chunk) has fp32 master, m
+                 and v tensors of its own (self.master_tensors,
+                 self.exp_avg_tensors, self.exp_avg_sq_tensors, in segment
+                 order), updated by the multi-tensor AdamW through a
+                 device-resident table; self.master, self.exp_avg and
+                 self.exp_avg_sq are then None. The gradient and the
+                 parameter shard stay coalesced buffers (the reduce's output
+                 and the gather's input), and the shard's padding is never
+                 updated.
     """
 
     # Measured on MI355X, no clip: with 8 replicas per window the one pass takes
@@ -72,16 +83,28 @@ class RankStep:
 
     def __init__(self, plan: zb.Plan, rank: int, n_windows: int, hyper: Hyper, max_norm: float,
                  device: torch.device, gather: bool = True, offload: bool = False,
-                 offload_chunk: int = 1 << 21, host_threads: int = 0, fuse: bool = True):
+                 offload_chunk: int = 1 << 21, host_threads: int = 0, fuse: bool = True,
+                 per_param: bool = False):
+        if per_param and offload:
+            raise ValueError("per-parameter state and ZeRO-Offload are separate layouts")
         self.plan, self.rank, self.hyper, self.max_norm = plan, rank, hyper, max_norm
         self.device = device
         self.offload, self.host_threads = offload, host_threads
-        self.fuse = fuse
+        self.fuse, self.per_param = fuse, per_param
         s, nd = plan.shard_numel, plan.num_ranks
         # The arrays the AdamW kernel streams live in one arena, each start
         # moved STAGGER bytes past the previous end (the value measured best
         # on MI355X; see STAGGER).
-        if offload:
+        self.segments = plan.segments(rank) if per_param else []
+        if per_param:
+            views, self.arena = _staggered_arena([(s, torch.int16), (s, torch.int16)], device)
+            self.grad, own_param = views
+            self.master = self.exp_avg = self.exp_avg_sq = None
+            lens = [ln for (_, _, _, ln) in self.segments]
+            self.master_tensors = [torch.zeros(n, dtype=torch.float32, device=device) for n in lens]
+            self.exp_avg_tensors = [torch.zeros(n, dtype=torch.float32, device=device) for n in lens]
+            self.exp_avg_sq_tensors = [torch.zeros(n, dtype=torch.float32, device=device) for n in lens]
+        elif offload:
             views, self.arena = _staggered_arena([(s, torch.int16), (s, torch.int16)], device)
             self.grad, own_param = views
             self.master = torch.zeros(s, dtype=torch.float32)
@@ -168,6 +191,14 @@ class RankStep:
         lowers self.t.)"""
         self.t += 1
         clip = self.scale if self.max_norm > 0 else None
+        if self.per_param:
+            own = self.param_shards[self.rank]
+            sl = [slice(soff, soff + ln) for (_, _, soff, ln) in self.segments]
+            self._prepared("adamw", stream, lambda st: zb.MultiTensorTable(
+                self.master_tensors, self.exp_avg_tensors, self.exp_avg_sq_tensors,
+                [self.grad[x] for x in sl], [own[x] for x in sl]).prepare_step(
+                    clip_scale=clip, stream=st, **self.hyper.as_kwargs()))(self.t)
+            return
         if self.offload:        # returns once the host update is done; `stream` orders the copies
             self._prepared("adamw", stream, lambda st: zb.prepare_offload_adamw_step(
                 self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
@@ -187,8 +218,9 @@ class RankStep:
         averaged gradient is not stored and no norm partial is taken."""
         if len(windows) != self.n_windows:
             raise ValueError("window count differs from the one the step was built for")
-        if self.offload or self.max_norm > 0:
-            raise ValueError("the one-pass update runs on the device and without clipping")
+        if self.offload or self.per_param or self.max_norm > 0:
+            raise ValueError("the one-pass update runs on the device, over flat state, without "
+                             "clipping")
         spans = sorted((b, b + c) for b, c, _ in windows if c > 0)
         if any(a[1] > b[0] for a, b in zip(spans, spans[1:])):
             raise ValueError("windows overlap: the one-pass update needs disjoint windows")
@@ -211,7 +243,8 @@ class RankStep:
         spans = sorted((b, b + c) for b, c, _ in windows if c > 0)
         disjoint = all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
         narrow = all(len(reps) <= self.FUSE_MAX_REPLICAS for _, _, reps in windows)
-        if self.fuse and self.max_norm <= 0 and not self.offload and disjoint and narrow:
+        if (self.fuse and self.max_norm <= 0 and not self.offload and not self.per_param
+                and disjoint and narrow):
             self.reduce_update(windows, stream)
         else:
             self.reduce(windows, stream)
