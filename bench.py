@@ -144,18 +144,25 @@ class RankWorkload:
         spans = bucket_windows(P, bucket, lo, lo + S) if reps else []
         self.offload = name.endswith("-offload")
         self.n_threads = len(os.sched_getaffinity(0))
+        self.per_tensor = name.endswith("-pertensor")
         self.rs = RankStep(self.plan, rank, len(spans), self.hyper, self.max_norm, device,
                            gather=gather, offload=self.offload, offload_chunk=OFFLOAD_CHUNK,
-                           host_threads=self.n_threads)
+                           host_threads=self.n_threads, per_param=self.per_tensor)
         rs = self.rs
         if self.offload:         # the fp32 master lives in host memory
             rs.master.copy_(torch.from_numpy(synth.normal_f32(S, self.seed, synth.KIND_MASTER, 0, 0,
                                                               lo, phi, synth.MASTER_SIGMA)))
         else:
-            synth.device_normal_f32(rs.master, self.seed, synth.KIND_MASTER, 0, 0, lo,
+            master = rs.master if not self.per_tensor else torch.empty(S, dtype=torch.float32,
+                                                                       device=device)
+            synth.device_normal_f32(master, self.seed, synth.KIND_MASTER, 0, 0, lo,
                                     phi if layout == "flat" else P, synth.MASTER_SIGMA)
-        if layout == "shard0":       # padding inside the coalesced buffer starts at zero
-            rs.master.mul_(padding_mask(self.plan, rank).to(device))
+            if layout == "shard0":   # padding inside the coalesced buffer starts at zero
+                master.mul_(padding_mask(self.plan, rank).to(device))
+            if self.per_tensor:      # each parameter chunk's own fp32 tensor
+                for t, (_, _, soff, ln) in zip(rs.master_tensors, rs.segments):
+                    t.copy_(master[soff:soff + ln])
+                del master
         if gather:
             for r in range(nd):
                 if r != rank:
@@ -257,7 +264,6 @@ class RankWorkload:
             self._setup_reduce_tensors(device)
         self.adamw_launches = 1
         self.elems_per_step = S
-        self.per_tensor = name.endswith("-pertensor")
         if self.per_tensor:
             self._setup_per_tensor(device)
         torch.cuda.synchronize()
@@ -296,41 +302,32 @@ class RankWorkload:
         self.extra_phases = list(getattr(self, "extra_phases", None) or []) + [("reduce_tensors", run)]
 
     def _setup_per_tensor(self, device):
-        """FSDP-2 as its optimizer sees it: every parameter's local chunk has its
-        own fp32 master/m/v tensors (separate allocations), and the update is
-        the multi-tensor AdamW over that ragged list. Gradients and parameters
-        stay views into the rank's coalesced buffers (the reduce output and the
-        gather input)."""
+        """FSDP-2 as its optimizer sees it (RankStep(per_param=True)): every
+        parameter's local chunk has its own fp32 master/m/v tensors, and the
+        step's update is the multi-tensor AdamW through its device-resident
+        table (one launch). Gradients and parameters stay views into the rank's
+        coalesced buffers. The list call, which carries its descriptors in the
+        kernel arguments, is timed beside it outside the step, on copies of the
+        state."""
         import torch
 
         from zero_partitioned_mixed_partition_amd import _binding as zb
         rs = self.rs
-        self.segs = self.plan.segments(self.rank)
+        self.segs = rs.segments
         sl = [slice(soff, soff + ln) for (_, _, soff, ln) in self.segs]
-        self.pt_master = [rs.master[x].clone() for x in sl]
-        self.pt_m = [torch.zeros(x.stop - x.start, dtype=torch.float32, device=device) for x in sl]
-        self.pt_v = [torch.zeros(x.stop - x.start, dtype=torch.float32, device=device) for x in sl]
-        grads = [rs.grad[x] for x in sl]
-        params = [rs.param_shards[self.rank][x] for x in sl]
+        lm = [t.clone() for t in rs.master_tensors]
+        lmm = [torch.zeros_like(t) for t in rs.master_tensors]
+        lv = [torch.zeros_like(t) for t in rs.master_tensors]
+        self._list_state = (lm, lmm, lv)
         st = torch.cuda.current_stream(device).cuda_stream
-        # The list is fixed, so the step goes through its device-resident table
-        # (one launch); the list call, which carries its descriptors in the
-        # kernel arguments, is timed beside it outside the step.
-        self.mt_table = zb.MultiTensorTable(self.pt_master, self.pt_m, self.pt_v, grads, params)
-        call = self.mt_table.prepare_step(clip_scale=rs.scale, stream=st, **self.hyper.as_kwargs())
-        call_list = zb.prepare_multi_tensor_adamw_step(self.pt_master, self.pt_m, self.pt_v, grads,
-                                                       params, clip_scale=rs.scale, stream=st,
-                                                       **self.hyper.as_kwargs())
-        self.t = 0
-
-        def adamw_pt():
-            self.t += 1
-            call(self.t)
+        call_list = zb.prepare_multi_tensor_adamw_step(
+            lm, lmm, lv, [rs.grad[x] for x in sl], [rs.param_shards[self.rank][x] for x in sl],
+            clip_scale=rs.scale, stream=st, **self.hyper.as_kwargs())
+        self.t_list = 0
 
         def adamw_list():
-            self.t += 1
-            call_list(self.t)
-        self.phases = [(n, adamw_pt if n == "adamw" else fn) for n, fn in self.phases]
+            self.t_list += 1
+            call_list(self.t_list)
         self.extra_phases = (list(getattr(self, "extra_phases", None) or [])
                              + [("adamw_list", adamw_list)])
         self.elems_per_step = sum(x.stop - x.start for x in sl)
@@ -343,7 +340,8 @@ class RankWorkload:
         if not getattr(self, "per_tensor", False):
             return [x.detach().cpu().numpy() for x in (rs.master, rs.exp_avg, rs.exp_avg_sq)]
         out = [np.zeros(self.S, np.float32) for _ in range(3)]
-        for (_, _, soff, ln), *arrs in zip(self.segs, self.pt_master, self.pt_m, self.pt_v):
+        for (_, _, soff, ln), *arrs in zip(self.segs, rs.master_tensors, rs.exp_avg_tensors,
+                                           rs.exp_avg_sq_tensors):
             for o, a in zip(out, arrs):
                 o[soff:soff + ln] = a.cpu().numpy()
         return out

@@ -211,7 +211,10 @@ def test_bench_pipeline_matches_oracle(zm, name):
     assert abs(int(got_scale.view(np.int32)) - int(np.float32(out["clip"]).view(np.int32))) <= 1
     # (offload: the fp32 state is in host memory; per-tensor: one array per chunk,
     # placed back at the chunk offsets with zero padding, which the oracle keeps at zero)
-    assert setup.rs.master.is_cuda != setup.offload
+    if setup.per_tensor:
+        assert setup.rs.master is None and all(t.is_cuda for t in setup.rs.master_tensors)
+    else:
+        assert setup.rs.master.is_cuda != setup.offload
     for got, key in zip(setup.state_arrays(), ("master", "exp_avg", "exp_avg_sq")):
         exact = assert_f32_close(got, state[key], key)
         note(f"bench pipeline {name}: {key} bit-identical fraction {exact:.6f}")
