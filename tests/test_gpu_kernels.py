@@ -1079,3 +1079,18 @@ def test_reduce_table_gpt2_small_rank7_eight_replicas(zm):
     assert abs(float(sq.item()) - want_sq) <= 1e-12 * want_sq
     note(f"gpt2-small rank 7: {S} elements from {R} x {len(w.numels)} tensors, "
          f"{table.blocks} workgroups, bit-identical")
+
+
+def test_reduce_table_edge_cases(zm):
+    """The reduce table at R = 64 (the most replicas the ABI takes), on a plan
+    whose last ranks hold only padding (written as zeros, squared norm exactly
+    0), and on a one-rank plan (the whole model is the shard)."""
+    rng = np.random.default_rng(1700)
+    numels = [3000, 17, 500]
+    ref = oracle.partition_plan(numels, 8, 512)                # P = 4096: ranks 7.. hold padding
+    plan = zm.zero_partition_plan(numels, 8, 512)
+    assert ref.segments(7) == [] and ref.shard_numel == 512
+    _check_reduce_table(zm, ref, plan, _tensor_replicas(rng, numels, 64), False, note_prefix="R=64 ")
+    ref1 = oracle.partition_plan(numels, 1, 8)
+    plan1 = zm.zero_partition_plan(numels, 1, 8)
+    _check_reduce_table(zm, ref1, plan1, _tensor_replicas(rng, numels, 2), False, note_prefix="one rank ")
