@@ -377,6 +377,22 @@ def test_binding_refuses_buffers_shorter_than_the_call_touches(zm):
         zm.MultiTensorTable([f(4)], [f(4)], [f(3)], [h(4)], [h(4)])
     with pytest.raises(ValueError, match="device tensor"):
         zm.MultiTensorTable([f(4)], [f(4)], [f(4)], [h(4)], [h(4)])
+    # the one-pass reduce and update, and the reduce table
+    with pytest.raises(ValueError, match="replica"):
+        zm.zero_reduce_adamw_step(plan, 0, [h(128), h(120)], 0, 128, f(64), f(64), f(64), h(64), 1, **hp)
+    with pytest.raises(ValueError, match="exp_avg_sq"):
+        zm.zero_reduce_adamw_step(plan, 0, [h(128)], 0, 128, f(64), f(64), f(63), h(64), 1, **hp)
+    with pytest.raises(ValueError, match="shard_grad"):
+        zm.zero_reduce_adamw_step(plan, 0, [h(128)], 0, 128, f(64), f(64), f(64), h(64), 1,
+                                  shard_grad=h(32), **hp)
+    with pytest.raises(ValueError, match="lists 1 tensors"):
+        zm.ReduceTable(plan, 0, [[h(100)]], h(64))
+    with pytest.raises(ValueError, match="tensor 1 of replica 1"):
+        zm.ReduceTable(plan, 0, [[h(100), h(28)], [h(100), h(27)]], h(64))
+    with pytest.raises(ValueError, match="shard_grad"):
+        zm.ReduceTable(plan, 0, [[h(100), h(28)]], h(63))
+    with pytest.raises(ValueError, match="device tensor"):
+        zm.ReduceTable(plan, 0, [[h(100), h(28)]], h(64))
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None or shutil.which("g++") is None
