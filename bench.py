@@ -833,7 +833,7 @@ def cpu_baseline(wl, budget_s: float):
         k += 1
         one(1 + k)
         el = time.perf_counter() - t0
-        if el >= budget_s or k >= 50:
+        if el >= budget_s or k >= 1000:
             break
     return {"value": per_step * k / el, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"{k} {sample}, single-threaded numpy", "seconds": el,
