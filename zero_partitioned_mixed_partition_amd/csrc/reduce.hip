@@ -758,6 +758,14 @@ namespace {
 #endif
 constexpr int kRGroups = ZERO_RTABLE_GROUPS;
 constexpr int64_t kRChunk = int64_t(kThreads) * 8 * kRGroups;   // elements per workgroup
+// 1: the one-pass form leaves one norm partial per wave (no LDS, no barrier;
+// four times the partials); 0 (default): one per workgroup. Measured on MI355X,
+// GPT-2 rank 7 from 8 per-tensor replicas, two rounds: 50.4-50.5 us against
+// 49.8-50.0 us (Shard(0): 51.7 against 50.9-51.1 us).
+#ifndef ZERO_RTABLE_WAVE_PARTIALS
+#define ZERO_RTABLE_WAVE_PARTIALS 0
+#endif
+constexpr int64_t kRPartialsPerBlock = ZERO_RTABLE_WAVE_PARTIALS ? kThreads / 64 : 1;
 // Workgroups of the grid-stride form (0, default: one workgroup per chunk, one
 // pass). Measured on MI355X, GPT-2 rank 7 from 8 per-tensor replicas, two
 // rounds: one pass 50.5-50.9 us; grids of 1,024, 2,048 and 4,096 workgroups
@@ -850,7 +858,15 @@ __global__ __launch_bounds__(kThreads) void reduce_table_kernel(const RPieceDesc
     const int64_t blk = blk0 + static_cast<int64_t>(blockIdx.x);
     double sq = 0.0;
     reduce_table_chunk(table[index[zero::dev::xcd_major_entry(blk0, per)]], blk, ptrs, n_rep, out, sq);
-    if (partials != nullptr) store_partial(sq, partials + blk0);
+    if (partials == nullptr) return;
+#if ZERO_RTABLE_WAVE_PARTIALS
+    // one partial per wave, in (workgroup, wave) order: no LDS, no barrier
+    const double w = zero::dev::wave_sum(sq);
+    if (threadIdx.x % zero::dev::kWave == 0)
+        partials[blk * (kThreads / zero::dev::kWave) + threadIdx.x / zero::dev::kWave] = w;
+#else
+    store_partial(sq, partials + blk0);
+#endif
 }
 
 // Grid-stride form (one launch of at most kTableLaunchBlocks chunks): workgroup
@@ -974,8 +990,9 @@ extern "C" zero_status zero_reduce_table_create(const zero_plan* plan, int32_t r
         const size_t desc_bytes = up(descs.size() * sizeof(RPieceDesc));
         const size_t index_bytes = up(index.size() * sizeof(uint32_t));
         const size_t ptr_bytes = up(ptrs.size() * sizeof(const uint16_t*));
-        const int64_t level1 = (blocks + kFinishChunk - 1) / kFinishChunk;
-        const size_t part_bytes = static_cast<size_t>(blocks + level1) * sizeof(double);
+        const int64_t n_part = blocks * kRPartialsPerBlock;
+        const int64_t level1 = (n_part + kFinishChunk - 1) / kFinishChunk;
+        const size_t part_bytes = static_cast<size_t>(n_part + level1) * sizeof(double);
         st = zero::check_hip(hipGetDevice(&tab->device), who);
         if (st == ZERO_OK)
             st = zero::check_hip(hipMalloc(&tab->mem, desc_bytes + index_bytes + ptr_bytes + part_bytes), who);
@@ -1025,8 +1042,8 @@ extern "C" zero_status zero_reduce_table_run(const zero_reduce_table* table, dou
     double* const parts = sqnorm_out != nullptr ? table->partials : nullptr;
     // A dispatch holds fewer than 2^32 work-items: longer tables take several launches.
     constexpr int64_t kMaxBlocks = zero::kTableLaunchBlocks;
-    int64_t n_parts = table->blocks;
-    if (ZERO_RTABLE_GRID > 0 && table->blocks <= kMaxBlocks) {
+    int64_t n_parts = table->blocks * kRPartialsPerBlock;
+    if (ZERO_RTABLE_GRID > 0 && !ZERO_RTABLE_WAVE_PARTIALS && table->blocks <= kMaxBlocks) {
         n_parts = table->blocks < ZERO_RTABLE_GRID ? table->blocks : ZERO_RTABLE_GRID;
         hipLaunchKernelGGL(reduce_table_stride_kernel, dim3(static_cast<unsigned>(n_parts)), dim3(kThreads),
                            0, stream, table->table, table->index, table->ptrs, table->n_rep, table->out,
