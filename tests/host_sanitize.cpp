@@ -37,6 +37,88 @@ void fail(const std::string& what) {
 // Fake 256-byte-aligned device addresses: the checks compare addresses only.
 uint16_t* fake(uint64_t base) { return reinterpret_cast<uint16_t*>(static_cast<uintptr_t>(base)); }
 
+// Reduce-table contents for every rank: the pieces tile [0, S) in shard order,
+// the tensor pieces are exactly the rank's segments, the 16-byte flag follows
+// its rule, every workgroup's index entry names the piece its chunk lies in,
+// the replica pointers are tensor-major; a NULL tensor a segment needs, and a
+// shard_grad overlapping a replica tensor, are refused.
+void check_reduce_table(const zero_plan* p, const std::vector<int64_t>& numels, int n_ranks) {
+    const int64_t T = static_cast<int64_t>(numels.size());
+    const int64_t S = zero_plan_shard_numel(p);
+    const int32_t R = 3;
+    const int64_t chunk = 2048;
+    // replica k's tensor t at a 16-byte-aligned fake address, except replica 1's odd tensors
+    std::vector<const uint16_t*> reps(static_cast<size_t>(R * T));
+    for (int32_t k = 0; k < R; ++k)
+        for (int64_t t = 0; t < T; ++t)
+            reps[static_cast<size_t>(k * T + t)] =
+                fake((uint64_t(k + 1) << 44) + (uint64_t(t) << 36) + (k == 1 && t % 2 == 1 ? 2 : 0));
+    const uint16_t* grad = fake(uint64_t(7) << 44);
+    for (int r = 0; r < n_ranks; ++r) {
+        std::vector<zero::copy::RPieceDesc> descs;
+        std::vector<uint32_t> index;
+        std::vector<const uint16_t*> ptrs;
+        int64_t blocks = -1;
+        if (zero::copy::reduce_table_contents(p, r, reps.data(), R, grad, chunk, &descs, &index, &ptrs,
+                                              &blocks, "t") != ZERO_OK) {
+            fail("reduce table contents");
+            return;
+        }
+        for (int64_t t = 0; t < T; ++t)
+            for (int32_t k = 0; k < R; ++k)
+                if (ptrs[static_cast<size_t>(t * R + k)] != reps[static_cast<size_t>(k * T + t)])
+                    fail("replica pointers tensor-major");
+        const int32_t ns = zero_plan_num_segments(p, r);
+        std::vector<zero_segment> segs(static_cast<size_t>(ns) + 1);
+        int32_t count = 0;
+        if (zero_plan_segments(p, r, segs.data(), ns, &count) != ZERO_OK) fail("segments");
+        int64_t pos = 0, blocks_seen = 0;
+        int32_t seg_i = 0;
+        for (const auto& d : descs) {
+            if (d.dst_off != pos || d.len <= 0) { fail("reduce pieces tile the shard"); return; }
+            if (d.first_block != blocks_seen) fail("reduce piece first block");
+            blocks_seen += (d.len + chunk - 1) / chunk;
+            if (d.tensor >= 0) {
+                if (seg_i >= count) { fail("more tensor pieces than segments"); return; }
+                const zero_segment& sg = segs[static_cast<size_t>(seg_i++)];
+                if (sg.tensor != d.tensor || sg.tensor_offset != d.src_off || sg.shard_offset != d.dst_off ||
+                    sg.length != d.len)
+                    fail("tensor piece is the rank's segment");
+                const bool aligned = !(d.tensor % 2 == 1);     // replica 1's odd tensors are 2 bytes off
+                const bool want = aligned && d.src_off % 8 == 0 && d.dst_off % 8 == 0;
+                if ((d.vec != 0) != want) fail("16-byte flag");
+            } else if (d.vec != 0) {
+                fail("padding pieces take no 16-byte path");
+            }
+            pos = d.dst_off + d.len;
+        }
+        if (pos != S || seg_i != count) fail("reduce pieces cover S and every segment");
+        if (blocks != blocks_seen) fail("reduce table blocks");
+        for (int64_t b0 = 0; b0 < blocks; b0 += zero::kTableLaunchBlocks) {
+            const int64_t nb = blocks - b0 < zero::kTableLaunchBlocks ? blocks - b0 : zero::kTableLaunchBlocks;
+            const int64_t per = (nb + 7) / 8;
+            for (int64_t x = 0; x < nb; ++x) {
+                const size_t e = static_cast<size_t>(b0 + (x & 7) * per + (x >> 3));
+                if (e >= index.size() || index[e] >= descs.size()) { fail("reduce index out of range"); return; }
+                const auto& d = descs[index[e]];
+                const int64_t start = (b0 + x - d.first_block) * chunk;
+                if (start < 0 || start >= d.len) { fail("reduce workgroup outside its piece"); return; }
+            }
+        }
+        if (count > 0) {              // errors: a needed tensor missing; the output over a tensor
+            const int32_t t = segs[0].tensor;
+            std::vector<const uint16_t*> bad = reps;
+            bad[static_cast<size_t>(2 * T + t)] = nullptr;
+            if (zero::copy::reduce_table_contents(p, r, bad.data(), R, grad, chunk, &descs, &index, &ptrs,
+                                                  &blocks, "t") != ZERO_EINVAL)
+                fail("NULL needed replica tensor");
+            if (zero::copy::reduce_table_contents(p, r, reps.data(), R, reps[static_cast<size_t>(t)], chunk,
+                                                  &descs, &index, &ptrs, &blocks, "t") != ZERO_EINVAL)
+                fail("shard_grad over a replica tensor");
+        }
+    }
+}
+
 void check_plan(const zero_plan* p, const std::vector<int64_t>& numels, const std::vector<int64_t>& dim0,
                 int kind, int n_ranks, int align, bool deep) {
     const int T = static_cast<int>(numels.size());
@@ -153,6 +235,7 @@ void check_plan(const zero_plan* p, const std::vector<int64_t>& numels, const st
     }
     (void)zero::copy::fits_tensor_major(p);
     (void)zero::copy::fits_compact(p);
+    check_reduce_table(p, numels, n_ranks);
 }
 
 bool run_plan(int kind, int n_ranks, int align, const std::vector<int64_t>& numels,

@@ -53,5 +53,70 @@ zero_status copy_table_contents(const std::vector<Piece>& pieces, int64_t chunk,
     return ZERO_OK;
 }
 
+zero_status reduce_table_contents(const zero_plan* plan, int32_t rank,
+                                  const uint16_t* const* replica_tensors, int32_t n_replicas,
+                                  const uint16_t* shard_grad, int64_t chunk,
+                                  std::vector<RPieceDesc>* descs, std::vector<uint32_t>* index,
+                                  std::vector<const uint16_t*>* ptrs, int64_t* blocks_out,
+                                  const char* who) {
+    descs->clear();
+    index->clear();
+    const int64_t T = static_cast<int64_t>(plan->numels.size());
+    const std::vector<zero_segment>& segs = plan->by_rank[static_cast<size_t>(rank)];
+    ptrs->assign(static_cast<size_t>(T * n_replicas), nullptr);
+    std::vector<char> vec_ok(static_cast<size_t>(T), 1);
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t k = 0; k < n_replicas; ++k) {
+            const uint16_t* q = replica_tensors[static_cast<int64_t>(k) * T + t];
+            (*ptrs)[static_cast<size_t>(t * n_replicas + k)] = q;
+            if ((reinterpret_cast<uintptr_t>(q) & 15) != 0) vec_ok[static_cast<size_t>(t)] = 0;
+        }
+    const bool out_ok = (reinterpret_cast<uintptr_t>(shard_grad) & 15) == 0;
+    int64_t blocks = 0;
+    auto add = [&](int32_t t, int64_t src_off, int64_t dst_off, int64_t len) -> zero_status {
+        if (len <= 0) return ZERO_OK;
+        const int64_t b = len / chunk + (len % chunk != 0 ? 1 : 0);
+        if (b > 0x7FFFFFFF - blocks || descs->size() >= 0xFFFFFFFFu)
+            return fail(ZERO_ERANGE, std::string(who) + ": more than 2^31 workgroups");
+        RPieceDesc d{};
+        d.src_off = src_off;
+        d.dst_off = dst_off;
+        d.len = len;
+        d.first_block = blocks;
+        d.tensor = t;
+        d.vec = t >= 0 && out_ok && vec_ok[static_cast<size_t>(t)] && src_off % 8 == 0 && dst_off % 8 == 0;
+        index->insert(index->end(), static_cast<size_t>(b), static_cast<uint32_t>(descs->size()));
+        descs->push_back(d);
+        blocks += b;
+        return ZERO_OK;
+    };
+    const uintptr_t out_lo = reinterpret_cast<uintptr_t>(shard_grad);
+    const uintptr_t out_hi = out_lo + static_cast<uintptr_t>(plan->shard) * 2;
+    int64_t pos = 0;
+    for (const zero_segment& seg : segs) {
+        if (seg.length <= 0) continue;
+        for (int32_t k = 0; k < n_replicas; ++k) {
+            const uint16_t* q = (*ptrs)[static_cast<size_t>(seg.tensor * static_cast<int64_t>(n_replicas) + k)];
+            if (q == nullptr)
+                return fail(ZERO_EINVAL, std::string(who) + ": NULL tensor " + std::to_string(seg.tensor) +
+                                             " of replica " + std::to_string(k));
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(q);
+            const uintptr_t hi = lo + static_cast<uintptr_t>(plan->numels[static_cast<size_t>(seg.tensor)]) * 2;
+            if (lo < out_hi && out_lo < hi)
+                return fail(ZERO_EINVAL, std::string(who) + ": shard_grad overlaps tensor " +
+                                             std::to_string(seg.tensor) + " of replica " + std::to_string(k));
+        }
+        zero_status st = add(-1, 0, pos, seg.shard_offset - pos);
+        if (st == ZERO_OK) st = add(seg.tensor, seg.tensor_offset, seg.shard_offset, seg.length);
+        if (st != ZERO_OK) return st;
+        pos = seg.shard_offset + seg.length;
+    }
+    const zero_status st = add(-1, 0, pos, plan->shard - pos);
+    if (st != ZERO_OK) return st;
+    if (blocks > 0) *index = xcd_major_index(*index);
+    *blocks_out = blocks;
+    return ZERO_OK;
+}
+
 }  // namespace copy
 }  // namespace zero

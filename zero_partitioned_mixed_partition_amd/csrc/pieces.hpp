@@ -1,5 +1,6 @@
 // Host-side piece lists of the bf16 gather and flatten copies, and the
-// contents of a device copy table (host C++, no device code).
+// contents of a device copy table and of a reduce table (host C++, no device
+// code).
 //
 // "Zero Redundancy Optimizer (ZeRO) and Fully Sharded Data Parallelism (FSDP):
 // Mathematical Foundations ...", section "Execution Flow for ZeRO-1", step 4
@@ -51,6 +52,38 @@ std::vector<Piece> flatten_pieces(const zero_plan* plan, const uint16_t* const* 
 zero_status copy_table_contents(const std::vector<Piece>& pieces, int64_t chunk,
                                 std::vector<PieceDesc>* descs, std::vector<uint32_t>* index,
                                 int64_t* blocks, const char* who);
+
+// A reduce table's descriptor of one piece of the rank's shard: a segment
+// (elements [src_off, src_off + len) of tensor `tensor` in every replica, into
+// shard elements [dst_off, dst_off + len)) or a gap of padding (tensor -1,
+// written as zeros), with its first workgroup and whether 16-byte accesses
+// apply (every replica's tensor 16-byte aligned, both offsets multiples of 8,
+// the shard 16-byte aligned).
+struct alignas(64) RPieceDesc {
+    int64_t src_off;
+    int64_t dst_off;
+    int64_t len;
+    int64_t first_block;
+    int32_t tensor;
+    int32_t vec;
+    int64_t unused[2];
+};
+static_assert(sizeof(RPieceDesc) == 64, "one 64-byte descriptor per piece");
+
+// A reduce table's contents for `rank` of `plan`, at `chunk` shard elements
+// per workgroup: the rank's segments and the padding gaps around them, in
+// shard order, as descriptors; the XCD-major per-workgroup descriptor index
+// (xcd_major_index); and the R * T replica pointers tensor-major (pointer of
+// replica k's tensor t at t * R + k; replica_tensors holds it at k * T + t).
+// ZERO_EINVAL for a NULL replica tensor that a segment needs, or one that
+// overlaps shard_grad's S elements; ZERO_ERANGE past 2^31 workgroups; throws
+// std::bad_alloc.
+zero_status reduce_table_contents(const zero_plan* plan, int32_t rank,
+                                  const uint16_t* const* replica_tensors, int32_t n_replicas,
+                                  const uint16_t* shard_grad, int64_t chunk,
+                                  std::vector<RPieceDesc>* descs, std::vector<uint32_t>* index,
+                                  std::vector<const uint16_t*>* ptrs, int64_t* blocks_out,
+                                  const char* who);
 
 }  // namespace copy
 }  // namespace zero

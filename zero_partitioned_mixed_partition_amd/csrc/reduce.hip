@@ -32,6 +32,7 @@
 
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "pieces.hpp"
 
 #pragma clang fp contract(off)
 
@@ -736,16 +737,7 @@ extern "C" zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t ran
 // the squared norm. A workgroup reduces kRChunk elements of one piece, 8 per
 // lane through 16-byte accesses where every replica's tensor, the offsets and
 // the shard are 8-element aligned, element by element otherwise.
-struct alignas(64) RPieceDesc {
-    int64_t src_off;       // element offset into tensor `tensor` of every replica
-    int64_t dst_off;       // element offset into the shard gradient
-    int64_t len;
-    int64_t first_block;
-    int32_t tensor;        // -1: padding, written as zeros
-    int32_t vec;           // 16-byte accesses
-    int64_t unused[2];
-};
-static_assert(sizeof(RPieceDesc) == 64, "one 64-byte descriptor per piece");
+using zero::copy::RPieceDesc;
 
 namespace {
 
@@ -914,64 +906,15 @@ extern "C" zero_status zero_reduce_table_create(const zero_plan* plan, int32_t r
                                      std::to_string(ZERO_MAX_REPLICAS));
     if (plan->shard > 0 && shard_grad == nullptr)
         return fail(ZERO_EINVAL, "zero_reduce_table_create: NULL shard_grad");
-    const int64_t T = static_cast<int64_t>(plan->numels.size());
-    const std::vector<zero_segment>& segs = plan->by_rank[static_cast<size_t>(rank)];
     std::vector<RPieceDesc> descs;
     std::vector<uint32_t> index;
     std::vector<const uint16_t*> ptrs;
     int64_t blocks = 0;
     try {
-        ptrs.assign(static_cast<size_t>(T * n_replicas), nullptr);
-        std::vector<char> vec_ok(static_cast<size_t>(T), 1);
-        for (int64_t t = 0; t < T; ++t)
-            for (int32_t k = 0; k < n_replicas; ++k) {
-                const uint16_t* q = replica_tensors[static_cast<int64_t>(k) * T + t];
-                ptrs[static_cast<size_t>(t * n_replicas + k)] = q;
-                if ((reinterpret_cast<uintptr_t>(q) & 15) != 0) vec_ok[static_cast<size_t>(t)] = 0;
-            }
-        const bool out_ok = (reinterpret_cast<uintptr_t>(shard_grad) & 15) == 0;
-        auto add = [&](int32_t t, int64_t src_off, int64_t dst_off, int64_t len) -> zero_status {
-            if (len <= 0) return ZERO_OK;
-            const int64_t b = len / kRChunk + (len % kRChunk != 0 ? 1 : 0);
-            if (b > 0x7FFFFFFF - blocks || descs.size() >= 0xFFFFFFFFu)
-                return fail(ZERO_ERANGE, std::string(who) + ": more than 2^31 workgroups");
-            RPieceDesc dsc{};
-            dsc.src_off = src_off;
-            dsc.dst_off = dst_off;
-            dsc.len = len;
-            dsc.first_block = blocks;
-            dsc.tensor = t;
-            dsc.vec = t >= 0 && out_ok && vec_ok[static_cast<size_t>(t)] && src_off % 8 == 0 &&
-                      dst_off % 8 == 0;
-            index.insert(index.end(), static_cast<size_t>(b), static_cast<uint32_t>(descs.size()));
-            descs.push_back(dsc);
-            blocks += b;
-            return ZERO_OK;
-        };
-        const uintptr_t out_lo = reinterpret_cast<uintptr_t>(shard_grad);
-        const uintptr_t out_hi = out_lo + static_cast<uintptr_t>(plan->shard) * 2;
-        int64_t pos = 0;
-        for (const zero_segment& seg : segs) {
-            if (seg.length <= 0) continue;
-            for (int32_t k = 0; k < n_replicas; ++k) {
-                const uint16_t* q = ptrs[static_cast<size_t>(seg.tensor * static_cast<int64_t>(n_replicas) + k)];
-                if (q == nullptr)
-                    return fail(ZERO_EINVAL, std::string(who) + ": NULL tensor " +
-                                                 std::to_string(seg.tensor) + " of replica " + std::to_string(k));
-                const uintptr_t lo = reinterpret_cast<uintptr_t>(q);
-                const uintptr_t hi = lo + static_cast<uintptr_t>(plan->numels[static_cast<size_t>(seg.tensor)]) * 2;
-                if (lo < out_hi && out_lo < hi)
-                    return fail(ZERO_EINVAL, std::string(who) + ": shard_grad overlaps tensor " +
-                                                 std::to_string(seg.tensor) + " of replica " + std::to_string(k));
-            }
-            zero_status st = add(-1, 0, pos, seg.shard_offset - pos);
-            if (st == ZERO_OK) st = add(seg.tensor, seg.tensor_offset, seg.shard_offset, seg.length);
-            if (st != ZERO_OK) return st;
-            pos = seg.shard_offset + seg.length;
-        }
-        const zero_status st = add(-1, 0, pos, plan->shard - pos);
-        if (st != ZERO_OK) return st;
-        if (blocks > 0) index = zero::xcd_major_index(index);
+        const zero_status cs = zero::copy::reduce_table_contents(
+            plan, rank, replica_tensors, n_replicas, shard_grad, kRChunk, &descs, &index, &ptrs,
+            &blocks, who);
+        if (cs != ZERO_OK) return cs;
     } catch (const std::bad_alloc&) {
         return fail(ZERO_ENOMEM, std::string(who) + ": host allocation failed");
     }
