@@ -177,7 +177,9 @@ zero_status zero_plan_memory_bytes(const zero_plan* plan, int32_t stage, int32_t
  * begin,count  the global flat window the replica buffers cover (count >= 0,
  *              begin >= 0, begin + count <= P).
  * shard_grad   device [S]: element i is global element rank*S + i. Only the
- *              window's intersection with rank's shard is written:
+ *              window's intersection with rank's shard is written; that slice
+ *              must not overlap the replicas' slices the call reads, or the
+ *              workspace:
  *              out = bf16_rne( (sum over k = 0..R-1, in order, of fp32(rep_k)) / R ),
  *              the sum and the division in IEEE fp32.
  * sqnorm_out   device, nullable: receives the fp64 sum of squares of the bf16
@@ -200,7 +202,8 @@ zero_status zero_plan_memory_bytes(const zero_plan* plan, int32_t stage, int32_t
  *              differ. Without a norm the one-pass kernel needs no workspace.
  * Errors: ZERO_EINVAL (null plan/replicas/shard_grad, a null replica pointer,
  * R out of range, rank out of range, bad window, workspace not 8-byte
- * aligned); ZERO_ENOSPACE; ZERO_EHIP. */
+ * aligned, the written slice overlapping a replica's slice or the workspace,
+ * named in zero_last_error()); ZERO_ENOSPACE; ZERO_EHIP. */
 zero_status zero_grad_reduce_shard(const zero_plan* plan, int32_t rank,
                                    const uint16_t* const* replicas, int32_t n_replicas,
                                    int64_t begin, int64_t count, uint16_t* shard_grad,
@@ -288,12 +291,16 @@ zero_status zero_clip_scale(const double* partials, int32_t n_partials, double m
  *   param_out = bf16_rne(p)
  * master, exp_avg, exp_avg_sq  device [n] fp32, updated in place.
  * grad         device [n] bf16, read only.
- * param_out    device [n] bf16, written; must not overlap the fp32 arrays.
+ * param_out    device [n] bf16, written.
+ *              The four written arrays must not overlap one another or grad
+ *              (each element is read and written by one lane; arrays shifted
+ *              against each other would race).
  * step         t >= 1 (1-based bias-correction step).
  * clip_scale   device float, nullable (NULL means 1). A non-finite value skips
  *              the update: nothing is read or written.
  * Errors: ZERO_EINVAL (null pointers with n > 0, n < 0, step < 1, beta1 or
- * beta2 outside [0, 1), eps <= 0, lr < 0, non-finite scalars); ZERO_EHIP. */
+ * beta2 outside [0, 1), eps <= 0, lr < 0, non-finite scalars, overlapping
+ * arrays, named in zero_last_error()); ZERO_EHIP. */
 zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_sq,
                                   const uint16_t* grad, uint16_t* param_out, int64_t n,
                                   int64_t step, double lr, double beta1, double beta2, double eps,
@@ -312,19 +319,21 @@ zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_
  * through HBM (2R + 26 bytes per element instead of 2R + 30).
  * plan, rank, replicas, n_replicas, begin, count: as zero_grad_reduce_shard.
  * master, exp_avg, exp_avg_sq  device [S] fp32, the rank's shard state, in place.
- * param_out    device [S] bf16, the rank's parameter shard; must not overlap
- *              the fp32 arrays. Element i of these arrays is global element
- *              rank*S + i; only the window's part of the shard is read and written.
+ * param_out    device [S] bf16, the rank's parameter shard. Element i of
+ *              these arrays is global element rank*S + i; only the window's
+ *              part of the shard is read and written.
  * shard_grad   device [S] bf16, nullable: when given, also receives the
- *              averaged gradient, as zero_grad_reduce_shard writes it; must
- *              not overlap the fp32 arrays or param_out.
+ *              averaged gradient, as zero_grad_reduce_shard writes it.
+ *              Within the window, the written arrays (the three fp32 arrays,
+ *              param_out, shard_grad) must not overlap one another or the
+ *              replicas' slices the call reads.
  * step, lr, beta1, beta2, eps, weight_decay, clip_scale: as
  *              zero_shard_adamw_step; a non-finite coefficient skips the
  *              update (shard_grad, when given, is still written).
  * Errors: ZERO_EINVAL (null plan or replicas, a null replica or state array
  * for a non-empty window, R or rank out of range, bad window, bad
- * hyperparameters, param_out or shard_grad overlapping the state, shard_grad
- * overlapping param_out); ZERO_EHIP. */
+ * hyperparameters, overlapping arrays, named in zero_last_error());
+ * ZERO_EHIP. */
 zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t rank,
                                    const uint16_t* const* replicas, int32_t n_replicas,
                                    int64_t begin, int64_t count, float* master, float* exp_avg,
@@ -338,8 +347,10 @@ zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t rank,
  * optimizer step runs over a ragged list of per-parameter tensors rather than
  * one flat buffer. Tensor t has its own arrays masters[t], exp_avgs[t],
  * exp_avg_sqs[t] (device [numels[t]] fp32, in place), grads[t] (device bf16,
- * read only) and params_out[t] (device bf16, written; must not overlap tensor
- * t's fp32 arrays); the pointer arrays and numels are host arrays of
+ * read only) and params_out[t] (device bf16, written); tensor t's four
+ * written arrays must not overlap one another or grads[t], and different
+ * tensors' written arrays must not overlap (that is the caller's to keep: the
+ * call checks each tensor's arrays against each other only); the pointer arrays and numels are host arrays of
  * n_tensors entries. Every element gets zero_shard_adamw_step's arithmetic
  * (identical bits), with one step, one set of hyperparameters and one clip
  * coefficient for the whole list. Zero-sized tensors are skipped (their
@@ -541,7 +552,9 @@ zero_status zero_host_adamw_step(float* master, float* exp_avg, float* exp_avg_s
  * streams of the current device (default priority). The call returns when the
  * host update is done and the staging buffers are free again, on errors too.
  * Calls from several host threads are safe: they share the worker pool and the
- * copy streams and so run one after another.
+ * copy streams and so run one after another. The written ranges (the three
+ * host state arrays, the staging in use, d_param_out) must not overlap one
+ * another or d_grad.
  * Errors: as zero_host_adamw_step; ZERO_ENOSPACE if staging_elems < 4; ZERO_EHIP. */
 zero_status zero_offload_adamw_step(float* h_master, float* h_exp_avg, float* h_exp_avg_sq,
                                     const uint16_t* d_grad, uint16_t* d_param_out,

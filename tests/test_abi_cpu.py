@@ -160,6 +160,68 @@ def test_reduce_adamw_rejects_bad_arguments_before_touching_the_gpu(zm):
     assert "shard_grad" in zm.zero_last_error()
 
 
+def test_overlapping_arrays_are_refused_before_touching_the_gpu(zm):
+    """Each kernel reads and writes element i of its arrays from one lane, so a
+    written array shifted against another array it touches would race: the
+    entry points refuse such arguments and name the pair (checked before any
+    HIP call; the addresses are never dereferenced). Arrays that are only read
+    may overlap one another."""
+    lib = zm._binding
+    E = lib.ZERO_EINVAL
+    hp = (1e-3, 0.9, 0.999, 1e-8, 0.01)
+    master, m, v = 0x100000, 0x200000, 0x300000                # 500 floats each
+    param, grad = 0x900000, 0xA00000                           # 500 bf16 each
+
+    def adamw(mst=master, ea=m, eas=v, g=grad, p=param, n=500):
+        return lib._adamw(mst, ea, eas, g, p, n, 1, *hp, None, None)
+    assert adamw(ea=master + 4) == E
+    assert zm.zero_last_error().endswith("master overlaps exp_avg")
+    assert adamw(g=param + 2) == E
+    assert zm.zero_last_error().endswith("param_out overlaps grad")
+    assert adamw(g=v + 1996) == E                                  # the last 4 bytes of v
+    assert zm.zero_last_error().endswith("exp_avg_sq overlaps grad")
+
+    # rank 1 of a [1000] list over 2 ranks reads elements [500, 1000) of each replica
+    plan = zm.zero_partition_plan([1000], 2, 1)
+    reps = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+
+    def fused(state=(master, m, v), p=param, g=None, replicas=reps):
+        return lib._reduce_adamw(plan.handle, 1, replicas, 2, 0, 1000, *state, p, g, 1, *hp, None, None)
+    assert fused(p=0x20000 + 1000) == E
+    assert zm.zero_last_error().endswith("param_out overlaps replica 1")
+    assert fused(state=(0x10000 + 1998, m, v)) == E                # master's first 2 bytes
+    assert zm.zero_last_error().endswith("master overlaps replica 0")
+    assert fused(g=m + 100) == E
+    assert zm.zero_last_error().endswith("exp_avg overlaps shard_grad")
+
+    def reduce(g=0x900000, sq=None, ws=None, ws_bytes=0):
+        return lib._reduce(plan.handle, 1, reps, 2, 0, 1000, g, sq, ws, ws_bytes, None)
+    assert reduce(g=0x10000 + 2) == E                              # 2 bytes into replica 0's slice
+    assert zm.zero_last_error().endswith("shard_grad overlaps replica 0")
+    wsb = zm.zero_sqnorm_workspace_bytes()
+    assert reduce(sq=0xB00000, ws=0x900000 - wsb + 8, ws_bytes=wsb) == E
+    assert zm.zero_last_error().endswith("shard_grad overlaps workspace")
+    assert reduce(sq=0xB00000, ws=0x20000 + 1024, ws_bytes=wsb) == E
+    assert zm.zero_last_error().endswith("workspace overlaps replica 1")
+    assert lib._reduce_noalloc(plan.handle, 1, reps, 2, 0, 1000, 0x20000 + 1500, None, None) == E
+    assert zm.zero_last_error().endswith("shard_grad overlaps replica 1")
+
+    # the multi-tensor list and table, per tensor
+    def ptrs(*a):
+        return (ctypes.c_void_p * len(a))(*a)
+    n = (ctypes.c_int64 * 2)(500, 300)
+    ok = dict(ms=ptrs(master, 0x400000), ea=ptrs(m, 0x500000), eas=ptrs(v, 0x600000),
+              g=ptrs(grad, 0x700000), p=ptrs(param, 0x800000))
+    bad = dict(ok, g=ptrs(grad, 0x800000 + 598))                    # tensor 1's grad over its param
+    assert lib._mt_adamw(bad["ms"], bad["ea"], bad["eas"], bad["g"], bad["p"], n, 2, 1, *hp,
+                         None, None) == E
+    assert zm.zero_last_error().endswith("param overlaps grad of tensor 1")
+    out = ctypes.c_void_p()
+    assert lib._mt_create(bad["ms"], bad["ea"], bad["eas"], bad["g"], bad["p"], n, 2,
+                          ctypes.byref(out)) == E
+    assert "of tensor 1" in zm.zero_last_error() and not out.value
+
+
 def test_reduce_table_rejects_bad_arguments_before_touching_the_gpu(zm):
     """zero_reduce_table_create's argument checks, all before any HIP call (the
     addresses are never dereferenced)."""

@@ -75,6 +75,14 @@ def test_host_adamw_argument_errors(zm):
         zm.zero_host_adamw_step(x, x.copy(), x.copy(), h, h.copy(), 1, **dict(HP, beta2=1.0))
     with pytest.raises(ValueError):
         zm.zero_host_adamw_step(x, x.copy(), x.copy(), h[:2], h.copy(), 1, **HP)
+    # arrays that share memory: the pool's slices would race
+    with pytest.raises(zm.ZeroError, match="master overlaps exp_avg"):
+        zm.zero_host_adamw_step(x, x, x.copy(), h, h.copy(), 1, **HP)
+    with pytest.raises(zm.ZeroError, match="param_out overlaps grad"):
+        zm.zero_host_adamw_step(x, x.copy(), x.copy(), h, h, 1, **HP)
+    y = np.zeros(8, np.float32)
+    with pytest.raises(zm.ZeroError, match="exp_avg overlaps exp_avg_sq"):
+        zm.zero_host_adamw_step(x, y[:4], y[3:7], h, h.copy(), 1, **HP)
 
 
 def test_host_pool_repeated_and_concurrent_runs_agree(zm):

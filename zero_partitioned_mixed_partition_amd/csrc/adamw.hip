@@ -380,11 +380,6 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_kernel(FusedReplicas re
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool ranges_overlap(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    return x < y + b_bytes && y < x + a_bytes;
-}
-
 int64_t blocks_for(int64_t items) {
     const int64_t blocks = (items + kThreads - 1) / kThreads;
     return blocks < 1 ? 1 : blocks;
@@ -419,10 +414,11 @@ zero_status check_mt_list(float* const* masters, float* const* exp_avgs, float* 
         if (!masters[t] || !exp_avgs[t] || !exp_avg_sqs[t] || !grads[t] || !params_out[t])
             return fail(ZERO_EINVAL, w + ": NULL array for tensor " + std::to_string(t));
         const size_t fb = static_cast<size_t>(n) * 4, hb = static_cast<size_t>(n) * 2;
-        if (ranges_overlap(params_out[t], hb, masters[t], fb) ||
-            ranges_overlap(params_out[t], hb, exp_avgs[t], fb) ||
-            ranges_overlap(params_out[t], hb, exp_avg_sqs[t], fb))
-            return fail(ZERO_EINVAL, w + ": param overlaps the fp32 state of tensor " + std::to_string(t));
+        const zero::Span wr[] = {{masters[t], fb, "master"}, {exp_avgs[t], fb, "exp_avg"},
+                                 {exp_avg_sqs[t], fb, "exp_avg_sq"}, {params_out[t], hb, "param"}};
+        const zero::Span rd[] = {{grads[t], hb, "grad"}};
+        const std::string clash = zero::first_overlap(wr, 4, rd, 1);
+        if (!clash.empty()) return fail(ZERO_EINVAL, w + ": " + clash + " of tensor " + std::to_string(t));
         if ((n + kMtChunk - 1) / kMtChunk > 0x7FFFFFFF)
             return fail(ZERO_ERANGE, w + ": tensor " + std::to_string(t) + " too large");
     }
@@ -463,10 +459,11 @@ extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, floa
     if (!master || !exp_avg || !exp_avg_sq || !grad || !param_out)
         return fail(ZERO_EINVAL, "zero_shard_adamw_step: NULL array");
     const size_t fbytes = static_cast<size_t>(n) * 4, hbytes = static_cast<size_t>(n) * 2;
-    if (ranges_overlap(param_out, hbytes, master, fbytes) ||
-        ranges_overlap(param_out, hbytes, exp_avg, fbytes) ||
-        ranges_overlap(param_out, hbytes, exp_avg_sq, fbytes))
-        return fail(ZERO_EINVAL, "zero_shard_adamw_step: param_out overlaps the fp32 state");
+    const zero::Span wr[] = {{master, fbytes, "master"}, {exp_avg, fbytes, "exp_avg"},
+                             {exp_avg_sq, fbytes, "exp_avg_sq"}, {param_out, hbytes, "param_out"}};
+    const zero::Span rd[] = {{grad, hbytes, "grad"}};
+    const std::string clash = zero::first_overlap(wr, 4, rd, 1);
+    if (!clash.empty()) return fail(ZERO_EINVAL, "zero_shard_adamw_step: " + clash);
 
     AdamScalars c;
     st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, "zero_shard_adamw_step");
@@ -732,16 +729,19 @@ extern "C" zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t ran
     }
     const int64_t n = hi - lo, src_off = lo - begin, at = lo - shard_lo;
     const size_t fbytes = static_cast<size_t>(n) * 4, hbytes = static_cast<size_t>(n) * 2;
-    if (ranges_overlap(param_out + at, hbytes, master + at, fbytes) ||
-        ranges_overlap(param_out + at, hbytes, exp_avg + at, fbytes) ||
-        ranges_overlap(param_out + at, hbytes, exp_avg_sq + at, fbytes))
-        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: param_out overlaps the fp32 state");
-    if (shard_grad != nullptr &&
-        (ranges_overlap(shard_grad + at, hbytes, master + at, fbytes) ||
-         ranges_overlap(shard_grad + at, hbytes, exp_avg + at, fbytes) ||
-         ranges_overlap(shard_grad + at, hbytes, exp_avg_sq + at, fbytes) ||
-         ranges_overlap(shard_grad + at, hbytes, param_out + at, hbytes)))
-        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: shard_grad overlaps the state or param_out");
+    std::string clash;
+    try {
+        const zero::Span wr[] = {{master + at, fbytes, "master"}, {exp_avg + at, fbytes, "exp_avg"},
+                                 {exp_avg_sq + at, fbytes, "exp_avg_sq"}, {param_out + at, hbytes, "param_out"},
+                                 {shard_grad != nullptr ? shard_grad + at : nullptr, shard_grad ? hbytes : 0,
+                                  "shard_grad"}};
+        std::vector<zero::Span> rd(static_cast<size_t>(n_replicas));
+        for (int32_t k = 0; k < n_replicas; ++k) rd[static_cast<size_t>(k)] = {replicas[k] + src_off, hbytes, "replica", k};
+        clash = zero::first_overlap(wr, 5, rd.data(), n_replicas);
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "zero_reduce_adamw_step: host allocation failed");
+    }
+    if (!clash.empty()) return fail(ZERO_EINVAL, "zero_reduce_adamw_step: " + clash);
     AdamScalars c;
     st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
     if (st != ZERO_OK) return st;

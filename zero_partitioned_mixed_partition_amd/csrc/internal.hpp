@@ -1,6 +1,7 @@
 // Internal declarations shared by the library's translation units.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -32,6 +33,42 @@ void clear_error();
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
+
+// Host-side argument checks: whether [a, a + a_bytes) and [b, b + b_bytes)
+// share a byte.
+inline bool ranges_overlap(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return a_bytes > 0 && b_bytes > 0 && x < y + b_bytes && y < x + a_bytes;
+}
+
+// A device range an entry point reads or writes, named for the error message
+// ("replica 3" when index >= 0).
+struct Span {
+    const void* p;
+    size_t bytes;
+    const char* name;
+    int index = -1;
+};
+
+inline std::string span_name(const Span& s) {
+    return s.index < 0 ? std::string(s.name) : std::string(s.name) + " " + std::to_string(s.index);
+}
+
+// The kernels read and write element i of every array from one lane, so a
+// written range that shares bytes with another written range, or with a range
+// they read, races. Returns "<a> overlaps <b>" for the first such pair, or an
+// empty string; ranges that are only read may overlap one another.
+inline std::string first_overlap(const Span* written, int n_written, const Span* read, int n_read) {
+    for (int i = 0; i < n_written; ++i) {
+        for (int j = i + 1; j < n_written; ++j)
+            if (ranges_overlap(written[i].p, written[i].bytes, written[j].p, written[j].bytes))
+                return span_name(written[i]) + " overlaps " + span_name(written[j]);
+        for (int j = 0; j < n_read; ++j)
+            if (ranges_overlap(written[i].p, written[i].bytes, read[j].p, read[j].bytes))
+                return span_name(written[i]) + " overlaps " + span_name(read[j]);
+    }
+    return std::string();
+}
 
 // Device-resident tables (multi-tensor AdamW, gather/flatten copies) hold one
 // descriptor index per workgroup. The dispatcher deals a launch's workgroups

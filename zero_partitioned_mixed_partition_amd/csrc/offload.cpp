@@ -363,6 +363,14 @@ extern "C" zero_status zero_host_adamw_step(float* master, float* exp_avg, float
     if (n == 0) return ZERO_OK;
     if (!master || !exp_avg || !exp_avg_sq || !grad || !param_out)
         return fail(ZERO_EINVAL, "zero_host_adamw_step: NULL array");
+    {
+        const size_t fb = static_cast<size_t>(n) * 4, hb = static_cast<size_t>(n) * 2;
+        const zero::Span wr[] = {{master, fb, "master"}, {exp_avg, fb, "exp_avg"},
+                                 {exp_avg_sq, fb, "exp_avg_sq"}, {param_out, hb, "param_out"}};
+        const zero::Span rd[] = {{grad, hb, "grad"}};
+        const std::string clash = zero::first_overlap(wr, 4, rd, 1);
+        if (!clash.empty()) return fail(ZERO_EINVAL, "zero_host_adamw_step: " + clash);
+    }
     if (!std::isfinite(clip_scale)) return ZERO_OK;        // a non-finite norm skips the step
     c.clip = clip_scale;
     host_adamw_parallel(master, exp_avg, exp_avg_sq, grad, param_out, n, c,
@@ -389,6 +397,16 @@ extern "C" zero_status zero_offload_adamw_step(float* h_master, float* h_exp_avg
         return fail(ZERO_EINVAL, "zero_offload_adamw_step: NULL array");
     const int64_t chunk = staging_elems / 4;
     if (chunk < 1) return fail(ZERO_ENOSPACE, "zero_offload_adamw_step: staging holds < 4 elements");
+    {
+        const size_t fb = static_cast<size_t>(n) * 4, hb = static_cast<size_t>(n) * 2;
+        const zero::Span wr[] = {{h_master, fb, "h_master"}, {h_exp_avg, fb, "h_exp_avg"},
+                                 {h_exp_avg_sq, fb, "h_exp_avg_sq"},
+                                 {h_staging, static_cast<size_t>(chunk) * 4 * 2, "h_staging"},
+                                 {d_param_out, hb, "d_param_out"}};
+        const zero::Span rd[] = {{d_grad, hb, "d_grad"}};
+        const std::string clash = zero::first_overlap(wr, 5, rd, 1);
+        if (!clash.empty()) return fail(ZERO_EINVAL, std::string(who) + ": " + clash);
+    }
     CopyStreams cs;
     st = copy_streams(&cs);
     if (st != ZERO_OK) return st;

@@ -90,8 +90,7 @@ zero_status reduce_table_contents(const zero_plan* plan, int32_t rank,
         blocks += b;
         return ZERO_OK;
     };
-    const uintptr_t out_lo = reinterpret_cast<uintptr_t>(shard_grad);
-    const uintptr_t out_hi = out_lo + static_cast<uintptr_t>(plan->shard) * 2;
+    const size_t out_bytes = static_cast<size_t>(plan->shard) * 2;
     int64_t pos = 0;
     for (const zero_segment& seg : segs) {
         if (seg.length <= 0) continue;
@@ -100,9 +99,8 @@ zero_status reduce_table_contents(const zero_plan* plan, int32_t rank,
             if (q == nullptr)
                 return fail(ZERO_EINVAL, std::string(who) + ": NULL tensor " + std::to_string(seg.tensor) +
                                              " of replica " + std::to_string(k));
-            const uintptr_t lo = reinterpret_cast<uintptr_t>(q);
-            const uintptr_t hi = lo + static_cast<uintptr_t>(plan->numels[static_cast<size_t>(seg.tensor)]) * 2;
-            if (lo < out_hi && out_lo < hi)
+            const size_t q_bytes = static_cast<size_t>(plan->numels[static_cast<size_t>(seg.tensor)]) * 2;
+            if (ranges_overlap(shard_grad, out_bytes, q, q_bytes))
                 return fail(ZERO_EINVAL, std::string(who) + ": shard_grad overlaps tensor " +
                                              std::to_string(seg.tensor) + " of replica " + std::to_string(k));
         }

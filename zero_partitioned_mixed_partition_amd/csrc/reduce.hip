@@ -29,6 +29,7 @@
 #include <cmath>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -595,6 +596,21 @@ zero_status reduce_shard(const zero_plan* plan, int32_t rank, const uint16_t* co
     const int64_t n = hi - lo, src_off = lo - begin;
     uint16_t* out = shard_grad + (lo - shard_lo);
     const bool norm = sqnorm_out != nullptr;
+    {
+        std::string clash;
+        try {
+            const size_t bytes = static_cast<size_t>(n) * 2;
+            const zero::Span wr[] = {{out, bytes, "shard_grad"},
+                                     {partials, norm ? workspace_bytes : 0, "workspace"}};
+            std::vector<zero::Span> rd(static_cast<size_t>(n_replicas));
+            for (int32_t k = 0; k < n_replicas; ++k)
+                rd[static_cast<size_t>(k)] = {replicas[k] + src_off, bytes, "replica", k};
+            clash = zero::first_overlap(wr, 2, rd.data(), n_replicas);
+        } catch (const std::bad_alloc&) {
+            return fail(ZERO_ENOMEM, "zero_grad_reduce_shard: host allocation failed");
+        }
+        if (!clash.empty()) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: " + clash);
+    }
     // Large windows of at most one load batch of replicas: the one-pass
     // kernel, when every replica slice and the output are 4-byte aligned and
     // the workspace holds its partials. (With more replicas a lane makes one
