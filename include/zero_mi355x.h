@@ -416,7 +416,9 @@ zero_status zero_mt_table_adamw_step(const zero_mt_table* table, int64_t step, d
  * tensors      host [T] of device pointers, tensor t to numel_t bf16 values
  *              (may be NULL only for zero-sized tensors). Outputs must not
  *              overlap the shards or each other.
- * Errors: ZERO_EINVAL (null plan/arrays or a needed null pointer); ZERO_EHIP. */
+ * Errors: ZERO_EINVAL (null plan/arrays or a needed null pointer, a tensor
+ * overlapping another tensor or a shard, named in zero_last_error());
+ * ZERO_ENOMEM; ZERO_EHIP. */
 zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* shards,
                                uint16_t* const* tensors, hipStream_t stream);
 
@@ -435,7 +437,8 @@ zero_status zero_gather_params(const zero_plan* plan, const uint16_t* const* sha
  * tensors      host [T] of device pointers, tensor t to numel_t bf16 values
  *              (may be NULL only for zero-sized tensors).
  * flat         device [P] bf16, written entirely; must not overlap the tensors.
- * Errors: ZERO_EINVAL (null plan/arrays or a needed null pointer); ZERO_EHIP. */
+ * Errors: ZERO_EINVAL (null plan/arrays or a needed null pointer, flat
+ * overlapping a tensor, named in zero_last_error()); ZERO_ENOMEM; ZERO_EHIP. */
 zero_status zero_flatten_params(const zero_plan* plan, const uint16_t* const* tensors,
                                 uint16_t* flat, hipStream_t stream);
 

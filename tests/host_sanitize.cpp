@@ -196,6 +196,19 @@ void check_plan(const zero_plan* p, const std::vector<int64_t>& numels, const st
     const uint64_t tbase = 0x100000000000ull, fbase = 0x200000000000ull;
     for (int t = 0; t < T; ++t) tensors[static_cast<size_t>(t)] = fake(tbase + (static_cast<uint64_t>(t) << 36));
     for (int r = 0; r < n_ranks; ++r) shards[static_cast<size_t>(r)] = fake(fbase) + static_cast<int64_t>(r) * S;
+    // disjoint buffers pass the range checks; a tensor moved onto the last rank's shard does not
+    if (zero::copy::check_gather_ranges(p, shards.data(), tensors.data(), "t") != ZERO_OK ||
+        zero::copy::check_flatten_ranges(p, tensors.data(), fake(fbase), "t") != ZERO_OK)
+        fail("range checks refuse disjoint buffers");
+    for (int t = 0; t < T; ++t) {
+        if (p->numels[static_cast<size_t>(t)] == 0 || S == 0) continue;
+        std::vector<uint16_t*> moved = tensors;
+        moved[static_cast<size_t>(t)] = shards[static_cast<size_t>(n_ranks - 1)] + S - 1;
+        if (zero::copy::check_gather_ranges(p, shards.data(), moved.data(), "t") != ZERO_EINVAL ||
+            zero::copy::check_flatten_ranges(p, moved.data(), fake(fbase), "t") != ZERO_EINVAL)
+            fail("range checks miss a tensor over a shard");
+        break;
+    }
     const std::vector<zero::copy::Piece> g = zero::copy::gather_pieces(p, shards.data(), tensors.data());
     int64_t gathered = 0;
     for (const auto& pc : g) gathered += pc.len;
@@ -287,6 +300,53 @@ void edge_cases() {
     if (!run_plan(1, 4, 8, {0, 6, 0}, {0, 2, 0}, true)) fail("zero-sized Shard(0)");
 }
 
+// The sorted overlap check against the pairwise one on random lists of small
+// ranges (many touching, some empty or NULL): both find a clash on the same
+// lists, and a clash the sorted one names is a real one.
+void check_overlap_search() {
+    std::mt19937_64 rng(5);
+    int clashes = 0;
+    for (int it = 0; it < 20000; ++it) {
+        const int nw = static_cast<int>(rng() % 7), nr = static_cast<int>(rng() % 5);
+        std::vector<zero::Span> wr, rd;
+        auto one = [&](const char* name, int i) {
+            const uint64_t at = 0x1000 + 8 * (rng() % 40);
+            const size_t bytes = 8 * (rng() % 6);            // 0 .. 40 bytes
+            const bool null = rng() % 16 == 0;
+            return zero::Span{null ? nullptr : fake(at), bytes, name, i};
+        };
+        for (int i = 0; i < nw; ++i) wr.push_back(one("w", i));
+        for (int i = 0; i < nr; ++i) rd.push_back(one("r", i));
+        auto live = [](std::vector<zero::Span> v) {
+            for (auto& x : v)
+                if (x.p == nullptr) x.bytes = 0;
+            return v;
+        };
+        const std::vector<zero::Span> lw = live(wr), lr = live(rd);
+        const std::string brute = zero::first_overlap(lw.data(), nw, lr.data(), nr);
+        const std::string sorted = zero::copy::first_overlap_sorted(wr, rd);
+        if (brute.empty() != sorted.empty()) {
+            fail("sorted overlap search: '" + sorted + "' against '" + brute + "'");
+            return;
+        }
+        if (sorted.empty()) continue;
+        ++clashes;
+        // the named pair overlaps
+        auto find = [&](const std::string& name) -> const zero::Span* {
+            for (const auto& x : lw)
+                if (zero::span_name(x) == name) return &x;
+            for (const auto& x : lr)
+                if (zero::span_name(x) == name) return &x;
+            return nullptr;
+        };
+        const size_t cut = sorted.find(" overlaps ");
+        const zero::Span* a = find(sorted.substr(0, cut));
+        const zero::Span* b = find(sorted.substr(cut + 10));
+        if (!a || !b || !zero::ranges_overlap(a->p, a->bytes, b->p, b->bytes)) fail("named pair: " + sorted);
+    }
+    if (clashes < 1000) fail("too few overlapping lists drawn");
+}
+
 }  // namespace
 
 int main() {
@@ -305,6 +365,7 @@ int main() {
         if (!run_plan(kind, n_ranks, align, numels, dim0, phi <= 20000000)) fail("workload plan refused");
     }
     edge_cases();
+    check_overlap_search();
     std::mt19937_64 rng(11);
     for (int it = 0; it < 400; ++it) {
         const int T = static_cast<int>(rng() % 9);

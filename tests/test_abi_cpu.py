@@ -222,6 +222,37 @@ def test_overlapping_arrays_are_refused_before_touching_the_gpu(zm):
     assert "of tensor 1" in zm.zero_last_error() and not out.value
 
 
+def test_gather_and_flatten_refuse_overlapping_ranges_before_touching_the_gpu(zm):
+    """The gather writes the tensors and reads the shards; the flatten writes
+    the flat buffer and reads the tensors. A written range that meets another
+    range of the call is refused, naming the pair, in the per-call and in the
+    table forms (fake addresses, never dereferenced)."""
+    lib = zm._binding
+    E = lib.ZERO_EINVAL
+    plan = zm.zero_partition_plan([100, 28], 2, 1)            # P = 128, S = 64
+
+    def arr(*a):
+        return (ctypes.c_void_p * len(a))(*a)
+    shards = arr(0x30000, 0x30080)                              # 128 bytes each, back to back
+    out = ctypes.c_void_p()
+    # tensor 0 (200 bytes) runs into tensor 1
+    for f in (lambda s, t: lib._gather(plan.handle, s, t, None),
+              lambda s, t: lib._gt_create(plan.handle, s, t, ctypes.byref(out))):
+        assert f(shards, arr(0x10000, 0x10000 + 198)) == E
+        assert zm.zero_last_error().endswith("tensor 0 overlaps tensor 1")
+        assert f(arr(0x20000 + 20, 0x30080), arr(0x10000, 0x20000)) == E
+        assert zm.zero_last_error().endswith("tensor 1 overlaps shard 0")
+        assert f(arr(None, 0x10000 + 100), arr(0x10000, 0x20000)) == E   # a NULL shard is skipped
+        assert zm.zero_last_error().endswith("tensor 0 overlaps shard 1")
+    assert not out.value
+    # the flat buffer (256 bytes) meets tensor 1's last element
+    for f in (lambda t, fl: lib._flatten(plan.handle, t, fl, None),
+              lambda t, fl: lib._ft_create(plan.handle, t, fl, ctypes.byref(out))):
+        assert f(arr(0x10000, 0x40000 - 54), 0x40000) == E
+        assert zm.zero_last_error().endswith("flat overlaps tensor 1")
+    assert not out.value
+
+
 def test_reduce_table_rejects_bad_arguments_before_touching_the_gpu(zm):
     """zero_reduce_table_create's argument checks, all before any HIP call (the
     addresses are never dereferenced)."""

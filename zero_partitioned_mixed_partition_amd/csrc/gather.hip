@@ -390,6 +390,12 @@ extern "C" zero_status zero_gather_params(const zero_plan* plan, const uint16_t*
         return fail(ZERO_EINVAL, "zero_gather_params: NULL plan or shards");
     zero_status st = check_tensors(plan, tensors, "zero_gather_params");
     if (st != ZERO_OK) return st;
+    try {
+        st = zero::copy::check_gather_ranges(plan, shards, tensors, "zero_gather_params");
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "zero_gather_params: allocation failed");
+    }
+    if (st != ZERO_OK) return st;
     // A NULL shard skips that rank's segments (a caller gathers ranks as their
     // shards become ready, or the others while the own shard is still updated).
     bool all_present = true;
@@ -413,6 +419,12 @@ extern "C" zero_status zero_flatten_params(const zero_plan* plan, const uint16_t
     if (plan == nullptr) return fail(ZERO_EINVAL, "zero_flatten_params: NULL plan");
     if (plan->padded > 0 && flat == nullptr) return fail(ZERO_EINVAL, "zero_flatten_params: NULL flat");
     zero_status st = check_tensors(plan, tensors, "zero_flatten_params");
+    if (st != ZERO_OK) return st;
+    try {
+        st = zero::copy::check_flatten_ranges(plan, tensors, flat, "zero_flatten_params");
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "zero_flatten_params: allocation failed");
+    }
     if (st != ZERO_OK) return st;
     // Every gap between segments (and after the last) is filled with zeros;
     // Shard(0) plans copy the tensors with the tensor-major kernel, flat plans
@@ -512,6 +524,8 @@ extern "C" zero_status zero_gather_table_create(const zero_plan* plan, const uin
     if (st != ZERO_OK) return st;
     std::vector<Piece> pieces;
     try {
+        st = zero::copy::check_gather_ranges(plan, shards, tensors, "zero_gather_table_create");
+        if (st != ZERO_OK) return st;
         pieces = gather_pieces(plan, shards, tensors);
     } catch (const std::bad_alloc&) {
         return fail(ZERO_ENOMEM, "zero_gather_table_create: allocation failed");
@@ -532,6 +546,8 @@ extern "C" zero_status zero_flatten_table_create(const zero_plan* plan, const ui
     if (st != ZERO_OK) return st;
     std::vector<Piece> pieces;
     try {
+        st = zero::copy::check_flatten_ranges(plan, tensors, flat, "zero_flatten_table_create");
+        if (st != ZERO_OK) return st;
         pieces = flatten_pieces(plan, tensors, flat, true);
     } catch (const std::bad_alloc&) {
         return fail(ZERO_ENOMEM, "zero_flatten_table_create: allocation failed");

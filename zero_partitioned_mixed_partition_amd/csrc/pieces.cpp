@@ -1,6 +1,7 @@
 // Host-side piece lists and copy-table contents (see pieces.hpp).
 #include "pieces.hpp"
 
+#include <algorithm>
 #include <string>
 
 namespace zero {
@@ -114,6 +115,50 @@ zero_status reduce_table_contents(const zero_plan* plan, int32_t rank,
     if (blocks > 0) *index = xcd_major_index(*index);
     *blocks_out = blocks;
     return ZERO_OK;
+}
+
+std::string first_overlap_sorted(std::vector<Span> written, const std::vector<Span>& read) {
+    auto lo = [](const Span& x) { return reinterpret_cast<uintptr_t>(x.p); };
+    written.erase(std::remove_if(written.begin(), written.end(),
+                                 [](const Span& x) { return x.p == nullptr || x.bytes == 0; }),
+                  written.end());
+    std::sort(written.begin(), written.end(), [&](const Span& a, const Span& b) { return lo(a) < lo(b); });
+    // Sorted by start, two ranges overlap only if some neighbours do.
+    for (size_t i = 1; i < written.size(); ++i)
+        if (lo(written[i]) < lo(written[i - 1]) + written[i - 1].bytes)
+            return span_name(written[i - 1]) + " overlaps " + span_name(written[i]);
+    // Now disjoint, so their ends rise with their starts: the one written range
+    // that can meet [a, b) first is the first ending after a.
+    for (const Span& r : read) {
+        if (r.p == nullptr || r.bytes == 0) continue;
+        const auto it = std::upper_bound(written.begin(), written.end(), lo(r),
+                                         [&](uintptr_t a, const Span& w) { return a < lo(w) + w.bytes; });
+        if (it != written.end() && lo(*it) < lo(r) + r.bytes) return span_name(*it) + " overlaps " + span_name(r);
+    }
+    return std::string();
+}
+
+zero_status check_gather_ranges(const zero_plan* plan, const uint16_t* const* shards,
+                                uint16_t* const* tensors, const char* who) {
+    std::vector<Span> wr, rd;
+    wr.reserve(plan->numels.size());
+    for (size_t t = 0; t < plan->numels.size(); ++t)
+        wr.push_back({tensors[t], static_cast<size_t>(plan->numels[t]) * 2, "tensor", static_cast<int>(t)});
+    for (int32_t r = 0; r < plan->n_ranks; ++r)
+        rd.push_back({shards[r], static_cast<size_t>(plan->shard) * 2, "shard", r});
+    const std::string clash = first_overlap_sorted(std::move(wr), rd);
+    return clash.empty() ? ZERO_OK : fail(ZERO_EINVAL, std::string(who) + ": " + clash);
+}
+
+zero_status check_flatten_ranges(const zero_plan* plan, const uint16_t* const* tensors,
+                                 const uint16_t* flat, const char* who) {
+    std::vector<Span> rd;
+    rd.reserve(plan->numels.size());
+    for (size_t t = 0; t < plan->numels.size(); ++t)
+        rd.push_back({tensors[t], static_cast<size_t>(plan->numels[t]) * 2, "tensor", static_cast<int>(t)});
+    const std::string clash =
+        first_overlap_sorted({{flat, static_cast<size_t>(plan->padded) * 2, "flat"}}, rd);
+    return clash.empty() ? ZERO_OK : fail(ZERO_EINVAL, std::string(who) + ": " + clash);
 }
 
 }  // namespace copy

@@ -11,6 +11,7 @@
 #pragma once
 
 #include <cstdint>
+#include <string>
 #include <vector>
 
 #include "internal.hpp"
@@ -84,6 +85,24 @@ zero_status reduce_table_contents(const zero_plan* plan, int32_t rank,
                                   std::vector<RPieceDesc>* descs, std::vector<uint32_t>* index,
                                   std::vector<const uint16_t*>* ptrs, int64_t* blocks_out,
                                   const char* who);
+
+// first_overlap for long lists (a gather's tensors and shards): "<a> overlaps
+// <b>" for a written range that shares bytes with another written range or
+// with a read range, or an empty string. Ranges with a NULL pointer or no
+// bytes are left out. Sorts the written ranges, so O((W + R) log W). Throws
+// std::bad_alloc.
+std::string first_overlap_sorted(std::vector<Span> written, const std::vector<Span>& read);
+
+// The gather's ranges: tensor t (numel_t elements) is written, each non-NULL
+// shard (S elements) is read. ZERO_EINVAL naming the first overlap; throws
+// std::bad_alloc.
+zero_status check_gather_ranges(const zero_plan* plan, const uint16_t* const* shards,
+                                uint16_t* const* tensors, const char* who);
+
+// The flatten's ranges: the flat buffer (P elements) is written, each tensor
+// read. ZERO_EINVAL naming the first overlap; throws std::bad_alloc.
+zero_status check_flatten_ranges(const zero_plan* plan, const uint16_t* const* tensors,
+                                 const uint16_t* flat, const char* who);
 
 }  // namespace copy
 }  // namespace zero
