@@ -48,7 +48,10 @@ constexpr int kThreads = 256;
 // Below the cap each thread handles one group of 8 elements; above it threads
 // stride.
 // The grid depends on n only, so the summation order (and the fp64 result)
-// is the same on every device.
+// is the same on every device. Re-measured for the replica reduce, two rounds,
+// with its final sum: caps of 512, 1,024, 2,048 and 4,096 workgroups took
+// 4,453, 2,823-2,824, 2,522-2,523 and 2,513-2,516 us on Llama-3-8B (64
+// replicas) and 80.2-80.3, 53.3-53.4, 47.0 and 47.5 us on GPT-2 (8).
 #ifndef ZERO_REDUCE_MAX_BLOCKS
 #define ZERO_REDUCE_MAX_BLOCKS 2048
 #endif
@@ -257,6 +260,83 @@ __global__ __launch_bounds__(kThreads) void reduce_vec(ReplicaTable reps, int n_
     const int64_t tail = n - groups * kEpt;
     if (tid < tail) {
         const int64_t e = groups * kEpt + tid;
+        float acc = 0.0f;
+        for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(reps.p[k][src_off + e]);
+        const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
+        out[e] = h;
+        if (kNorm) sq += sq1(h);
+    }
+    if (kNorm) store_partial(sq, partials);
+}
+
+// Rows form of the vector path (ZERO_REDUCE_ROWS = G > 1; 1, the default,
+// keeps reduce_vec): a workgroup covers G * kThreads consecutive 8-element
+// groups per pass, lane l the groups base + l + q * kThreads (q < G). For each
+// replica in order a lane issues its G loads together, so a workgroup's loads
+// in flight all fall in one contiguous G * 4 KB run of one replica; then it
+// adds them. Lanes past the end load the last group again (every load is
+// unconditional) and drop it. Each element's sum is the same as reduce_vec's.
+// Measured on MI355X, two rounds, reduce phase with its final sum: Llama-3-8B
+// (64 replicas, six 25 M buckets) 2,526-2,527 us with reduce_vec, 2,709-2,710
+// with G = 2, 2,675 with 4, 2,571-2,578 with 8; GPT-2 (8 replicas) 47.5 us,
+// 47.3-47.4, 48.4 and 47.9-48.1 us. More loads in flight per lane cost even
+// when they all fall in one replica's run, so reduce_vec stays.
+#ifndef ZERO_REDUCE_ROWS
+#define ZERO_REDUCE_ROWS 1
+#endif
+constexpr int kRows = ZERO_REDUCE_ROWS;
+
+template <bool kNorm>
+__global__ __launch_bounds__(kThreads) void reduce_rows(ReplicaTable reps, int n_rep, int64_t src_off,
+                                                        uint16_t* __restrict__ out, int64_t n,
+                                                        double* __restrict__ partials) {
+    static_assert(kEpt == 8, "the rows form takes 16-byte groups");
+    const float r = static_cast<float>(n_rep);
+    const int64_t groups = n / 8;
+    const int64_t span = int64_t(kRows) * kThreads;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * span;
+    double sq = 0.0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * span; base < groups; base += stride) {
+        int64_t at[kRows];
+#pragma unroll
+        for (int q = 0; q < kRows; ++q) {
+            const int64_t i = base + threadIdx.x + int64_t(q) * kThreads;
+            at[q] = i < groups ? i : groups - 1;
+        }
+        float acc[kRows][8];
+#pragma unroll
+        for (int q = 0; q < kRows; ++q)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[q][j] = 0.0f;
+        for (int k = 0; k < n_rep; ++k) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(reps.p[k] + src_off);
+            u32x4 x[kRows];
+#pragma unroll
+            for (int q = 0; q < kRows; ++q) x[q] = zero::dev::ld_stream(src + at[q]);
+#pragma unroll
+            for (int q = 0; q < kRows; ++q)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[q][2 * j] = acc[q][2 * j] + zero::dev::lo_bf16(x[q][j]);
+                    acc[q][2 * j + 1] = acc[q][2 * j + 1] + zero::dev::hi_bf16(x[q][j]);
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < kRows; ++q) {
+            const int64_t i = base + threadIdx.x + int64_t(q) * kThreads;
+            if (i >= groups) break;
+            u32x4 w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = zero::dev::pack_bf16(acc[q][2 * j] / r, acc[q][2 * j + 1] / r);
+            if (kNorm) sq += sq8(w);
+            store_grad(reinterpret_cast<u32x4*>(out) + i, w);
+        }
+    }
+    // Ragged tail (< 8 elements), one per thread of the first threads.
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t tail = n - groups * 8;
+    if (tid < tail) {
+        const int64_t e = groups * 8 + tid;
         float acc = 0.0f;
         for (int k = 0; k < n_rep; ++k) acc = acc + zero::dev::bf16_to_f32(reps.p[k][src_off + e]);
         const uint16_t h = static_cast<uint16_t>(zero::dev::f32_to_bf16(acc / r));
@@ -662,10 +742,18 @@ zero_status reduce_shard(const zero_plan* plan, int32_t rank, const uint16_t* co
     }
     bool vec = aligned(out, 2 * kEpt);
     for (int32_t k = 0; k < n_replicas && vec; ++k) vec = aligned(replicas[k] + src_off, 2 * kEpt);
-    const int blocks = grid_for(vec ? n / kEpt : n, ZERO_REDUCE_MAX_BLOCKS);
+    const int blocks = grid_for(vec ? (kRows > 1 ? (n / kEpt + kRows - 1) / kRows : n / kEpt) : n,
+                                ZERO_REDUCE_MAX_BLOCKS);
     if (vec) {
         const bool two = n_replicas <= kReplicaBatch && n >= kTwoGroupsFrom;
-        if (norm && two)
+        if constexpr (kRows > 1) {
+            if (norm)
+                hipLaunchKernelGGL(reduce_rows<true>, dim3(blocks), dim3(kThreads), 0, stream, table,
+                                   n_replicas, src_off, out, n, partials);
+            else
+                hipLaunchKernelGGL(reduce_rows<false>, dim3(blocks), dim3(kThreads), 0, stream, table,
+                                   n_replicas, src_off, out, n, partials);
+        } else if (norm && two)
             hipLaunchKernelGGL((reduce_vec<true, 2>), dim3(blocks), dim3(kThreads), 0, stream, table,
                                n_replicas, src_off, out, n, partials);
         else if (norm)
