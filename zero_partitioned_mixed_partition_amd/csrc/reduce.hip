@@ -502,6 +502,44 @@ __global__ __launch_bounds__(kThreads) void sqnorm_pass(const uint16_t* __restri
     store_partial(sq, partials);
 }
 
+// Grid-stride form with rows (ZERO_SQNORM_ROWS = R > 0; 0, the default, keeps
+// sqnorm_pass for large inputs): a fixed grid of at most ZERO_SQNORM_MAX_BLOCKS
+// workgroups; per pass a workgroup reads R * kThreads consecutive groups, each
+// lane R of them kThreads apart, all R loads issued together (lanes past the
+// end reload the last group and drop it). One partial per workgroup, so one
+// final-sum kernel. Measured on MI355X, Llama-3-70B rank 7's 8.8 G-element
+// gradient in the benchmark step, two rounds: sqnorm_pass 2,601-2,656 us;
+// R = 4, 8, 16 over 4,096 workgroups 2,640-2,654, 2,659-2,707 and
+// 2,641-2,749 us; R = 8 over 2,048 workgroups 2,616-2,666 us. Off.
+#ifndef ZERO_SQNORM_ROWS
+#define ZERO_SQNORM_ROWS 0
+#endif
+constexpr int kSqRows = ZERO_SQNORM_ROWS;
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void sqnorm_rows(const uint16_t* __restrict__ g, int64_t n,
+                                                        double* __restrict__ partials) {
+    const int64_t groups = n / 8;
+    const int64_t span = int64_t(R) * kThreads;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * span;
+    const u32x4* g4 = reinterpret_cast<const u32x4*>(g);
+    double sq = 0.0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * span; base < groups; base += stride) {
+        u32x4 x[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int64_t i = base + int64_t(q) * kThreads + threadIdx.x;
+            x[q] = zero::dev::ld_stream(g4 + (i < groups ? i : groups - 1));
+        }
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+            if (base + int64_t(q) * kThreads + threadIdx.x < groups) sq += sq8(x[q]);
+    }
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (tid < n - groups * 8) sq += sq1(g[groups * 8 + tid]);
+    store_partial(sq, partials);
+}
+
 __global__ __launch_bounds__(kThreads) void sqnorm_scalar(const uint16_t* __restrict__ g, int64_t n,
                                                           double* __restrict__ partials) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
@@ -1211,6 +1249,19 @@ extern "C" zero_status zero_grad_sqnorm(const uint16_t* grad, int64_t n, double*
     const int64_t lanes = n / 8 + n % 8;
     const int64_t pblocks = (lanes + kThreads * kSqPassGroups - 1) / (kThreads * kSqPassGroups);
     const int64_t plevel1 = (pblocks + kFinishChunk - 1) / kFinishChunk;
+    if constexpr (kSqRows > 0) {
+        if (vec && n >= kOnePassFrom) {
+            const int64_t span = int64_t(kSqRows) * kThreads;
+            const int64_t want = (n / 8 + span - 1) / span;
+            const int blocks = static_cast<int>(want < ZERO_SQNORM_MAX_BLOCKS ? want : ZERO_SQNORM_MAX_BLOCKS);
+            hipLaunchKernelGGL(sqnorm_rows<kSqRows>, dim3(blocks), dim3(kThreads), 0, stream, grad, n,
+                               partials);
+            zero_status st = zero::check_hip(hipGetLastError(), "zero_grad_sqnorm launch");
+            if (st != ZERO_OK) return st;
+            hipLaunchKernelGGL(finish_sum, dim3(1), dim3(kThreads), 0, stream, partials, blocks, sqnorm_out);
+            return zero::check_hip(hipGetLastError(), "zero_grad_sqnorm finish launch");
+        }
+    }
     if (vec && n >= kOnePassFrom &&
         workspace_bytes >= static_cast<size_t>(pblocks + plevel1) * sizeof(double)) {
         constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / kThreads - 1;
