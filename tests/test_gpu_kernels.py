@@ -54,6 +54,43 @@ def test_adamw_matches_oracle(zm, n):
     assert_bits_equal(host_u16(dout), bits, "param bf16")
 
 
+# Hyperparameter corners: no momentum, betas next to 1 (bias corrections of
+# 1e-6), negative and large weight decay (a decay factor of 0), lr and eps of 1,
+# and step counts where the bias corrections round to 1.
+HP_CORNERS = {
+    "betas-zero-no-decay": (dict(HP, beta1=0.0, beta2=0.0, weight_decay=0.0), (1, 2, 3)),
+    "betas-near-one": (dict(HP, beta1=0.999999, beta2=0.999999), (1, 2)),
+    "lr-eps-one-negative-decay": (dict(HP, lr=1.0, eps=1.0, weight_decay=-0.5), (1, 2)),
+    "decay-factor-zero": (dict(HP, lr=0.01, weight_decay=100.0), (1, 2)),
+    "huge-steps": (HP, (10 ** 6, 2 ** 40)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(HP_CORNERS))
+def test_adamw_hyperparameter_corners(zm, case):
+    """The flat kernel and the one-pass reduce and update (one replica, whose
+    average is the gradient itself) against the oracle, bit for bit, where the
+    host's fp64 scalars meet their extremes."""
+    hp, steps = HP_CORNERS[case]
+    n = 4097
+    note(f"adamw corners {case}")
+    p, m, v, g = _adamw_inputs(n, 31)
+    dp, dm, dv, dg = to_dev_f32(p), to_dev_f32(m), to_dev_f32(v), to_dev_u16(g)
+    fp, fm, fv = to_dev_f32(p), to_dev_f32(m), to_dev_f32(v)
+    dout = torch.zeros(n, dtype=torch.int16, device=dev())
+    fout = torch.zeros(n, dtype=torch.int16, device=dev())
+    plan = zm.zero_partition_plan([n], 1, 1)
+    for t in steps:
+        zm.zero_shard_adamw_step(dp, dm, dv, dg, dout, t, **hp)
+        zm.zero_reduce_adamw_step(plan, 0, [dg], 0, n, fp, fm, fv, fout, t, **hp)
+        p, m, v, bits = oracle.adamw_step(p, m, v, g, t, **hp)
+    torch.cuda.synchronize()
+    for pre, outs in (("flat", (dp, dm, dv, dout)), ("one-pass", (fp, fm, fv, fout))):
+        for got, want, what in zip(outs[:3], (p, m, v), ("master", "exp_avg", "exp_avg_sq")):
+            assert_bits_equal(host_f32(got).view(np.uint32), want.view(np.uint32), f"{pre} {what}")
+        assert_bits_equal(host_u16(outs[3]), bits, f"{pre} param bf16")
+
+
 @pytest.mark.parametrize("offset", [1, 3])
 def test_adamw_unaligned_pointers_take_the_scalar_path(zm, offset):
     n = 5000
@@ -209,6 +246,32 @@ def test_reduce_matches_oracle(zm, numels, n_ranks, align, rank, R, window):
     want_sq = oracle.sqnorm(want[lo - rank * S:hi - rank * S]) if hi > lo else 0.0
     got_sq = float(d_sq.item())
     assert abs(got_sq - want_sq) <= 1e-12 * abs(want_sq), (got_sq, want_sq)
+
+
+@pytest.mark.parametrize("R,n,off", [(3, 100_003, 0), (8, 100_003, 0), (64, 30_011, 0),
+                                     (8, (1 << 24) + 5, 0), (5, 100_003, 1)])
+def test_reduce_identical_replicas_return_the_input(zm, R, n, off):
+    """A closed form, independent of the oracle: R identical bf16 replicas
+    (R <= 2^16, finite values far from overflow) sum exactly in fp32 to R*x,
+    and the division by R gives x back, so the averaged gradient is the
+    replica itself, bit for bit, and its squared norm is the input's. Covers
+    the grid-stride kernel (3, 8 and 64 replicas), the one-pass kernel (2^24 +
+    5 elements, with the workspace it needs) and the scalar path (a window
+    starting one element into the buffer)."""
+    note(f"reduce identical replicas R={R} n={n} off={off}")
+    plan = zm.zero_partition_plan([n + off], 1, 1)
+    x = synth.normal_bf16(n + off, 9, synth.KIND_REPLICA, 1, 0, sigma=1.0)
+    d = to_dev_u16(x)
+    out = torch.full((n + off,), 0x1234, dtype=torch.int16, device=dev())
+    sq = torch.zeros(1, dtype=torch.float64, device=dev())
+    ws = zm.reduce_workspace(n, dev())
+    zm.zero_grad_reduce_shard(plan, 0, [d[off:]] * R, off, n, out, sqnorm_out=sq, workspace=ws)
+    torch.cuda.synchronize()
+    got = host_u16(out)
+    assert_bits_equal(got[off:], x[off:], "averaged gradient")
+    assert got[:off].tolist() == [0x1234] * off, "element outside the window written"
+    want = oracle.sqnorm(x[off:])
+    assert abs(float(sq.item()) - want) <= 1e-12 * want
 
 
 def test_reduce_argument_errors(zm):

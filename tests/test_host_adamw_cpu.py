@@ -41,6 +41,32 @@ def test_host_adamw_matches_oracle_bit_for_bit(zm, n, threads):
     assert (out == B).all()
 
 
+@pytest.mark.parametrize("case", ["betas-zero-no-decay", "betas-near-one", "lr-eps-one-negative-decay",
+                                  "decay-factor-zero", "huge-steps"])
+def test_host_adamw_hyperparameter_corners(zm, case):
+    """The host update's own fp64 scalars at their extremes, against the oracle
+    bit for bit (no momentum, betas next to 1, negative and large weight decay,
+    lr and eps of 1, bias corrections that round to 1)."""
+    hp, steps = {
+        "betas-zero-no-decay": (dict(HP, beta1=0.0, beta2=0.0, weight_decay=0.0), (1, 2, 3)),
+        "betas-near-one": (dict(HP, beta1=0.999999, beta2=0.999999), (1, 2)),
+        "lr-eps-one-negative-decay": (dict(HP, lr=1.0, eps=1.0, weight_decay=-0.5), (1, 2)),
+        "decay-factor-zero": (dict(HP, lr=0.01, weight_decay=100.0), (1, 2)),
+        "huge-steps": (HP, (10 ** 6, 2 ** 40)),
+    }[case]
+    n = 4097
+    p, m, v, g = _inputs(n, 31)
+    out = np.zeros(n, np.uint16)
+    P, M, V = p.copy(), m.copy(), v.copy()
+    for t in steps:
+        zm.zero_host_adamw_step(p, m, v, g, out, t, n_threads=2, **hp)
+        P, M, V, B = oracle.adamw_step(P, M, V, g, t, **hp)
+    assert (p.view(np.uint32) == P.view(np.uint32)).all()
+    assert (m.view(np.uint32) == M.view(np.uint32)).all()
+    assert (v.view(np.uint32) == V.view(np.uint32)).all()
+    assert (out == B).all()
+
+
 def test_host_adamw_special_values_and_skip(zm):
     n = 64
     p = np.linspace(-3, 3, n).astype(np.float32)
