@@ -823,8 +823,8 @@ def cpu_baseline(wl, budget_s: float):
                                                              clip=clip, **hp)
         work = f"reduce of {R} replica windows, " if R else ""
         work += "AdamW" if fused else "exact norm, clip, AdamW"
-        sample = (f"the per-element work of this workload ({work}) "
-                  f"on a {n}-element slice of the shard")
+        sample = (f"passes of the per-element work of this workload ({work}) "
+                  f"over a {n}-element slice of the shard")
         per_step = n
     one(1)          # untimed: the first touch of fresh host pages is not oracle work
     t0 = time.perf_counter()

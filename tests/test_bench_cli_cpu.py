@@ -51,3 +51,26 @@ def test_traffic_record_matches_sources_and_sizes():
         got = bench.measured_traffic(e["elems"], e["kernel"])
         assert got == (e["bytes_per_launch"] if e["source_sha256"] == digest else None)
     assert bench.measured_traffic(12345) is None
+
+
+@pytest.mark.parametrize("replicas,fused", [(0, False), (8, False), (8, True)])
+def test_cpu_baseline_reports_its_sample_and_core_count(replicas, fused):
+    """The cpu_baseline leg on a small stand-in workload (the attributes it
+    reads, no device): one pass at least, a readable sample naming the count and
+    the work, one core."""
+    import types
+    sys.path.insert(0, ROOT)
+    import bench
+    import synth
+    from zero_partitioned_mixed_partition_amd.step import Hyper
+    w = synth.WORKLOADS["tiny-a"]
+    wl = types.SimpleNamespace(name="stand-in", hyper=Hyper(), S=4096, rank=1, seed=7,
+                               phi=w.numel if hasattr(w, "numel") else sum(w.numels),
+                               replicas=replicas, fused=fused)
+    r = bench.cpu_baseline(wl, 0.0)
+    assert r["kind"] == "oracle" and r["unit"] == "params/s" and r["cores"] == 1
+    assert r["value"] > 0 and r["seconds"] > 0
+    count, rest = r["sample"].split(" ", 1)
+    assert int(count) >= 1 and rest.startswith("passes of the per-element work")
+    assert ("reduce of 8 replica windows" in rest) == (replicas == 8)
+    assert ("clip" in rest) == (not fused)
