@@ -715,18 +715,13 @@ zero_status reduce_shard(const zero_plan* plan, int32_t rank, const uint16_t* co
     uint16_t* out = shard_grad + (lo - shard_lo);
     const bool norm = sqnorm_out != nullptr;
     {
-        std::string clash;
-        try {
-            const size_t bytes = static_cast<size_t>(n) * 2;
-            const zero::Span wr[] = {{out, bytes, "shard_grad"},
-                                     {partials, norm ? workspace_bytes : 0, "workspace"}};
-            std::vector<zero::Span> rd(static_cast<size_t>(n_replicas));
-            for (int32_t k = 0; k < n_replicas; ++k)
-                rd[static_cast<size_t>(k)] = {replicas[k] + src_off, bytes, "replica", k};
-            clash = zero::first_overlap(wr, 2, rd.data(), n_replicas);
-        } catch (const std::bad_alloc&) {
-            return fail(ZERO_ENOMEM, "zero_grad_reduce_shard: host allocation failed");
-        }
+        // On the stack: the no-allocation entry point comes through here too.
+        const size_t bytes = static_cast<size_t>(n) * 2;
+        const zero::Span wr[] = {{out, bytes, "shard_grad"},
+                                 {partials, norm ? workspace_bytes : 0, "workspace"}};
+        zero::Span rd[ZERO_MAX_REPLICAS];
+        for (int32_t k = 0; k < n_replicas; ++k) rd[k] = {replicas[k] + src_off, bytes, "replica", k};
+        const std::string clash = zero::first_overlap(wr, 2, rd, n_replicas);
         if (!clash.empty()) return fail(ZERO_EINVAL, "zero_grad_reduce_shard: " + clash);
     }
     // Large windows of at most one load batch of replicas: the one-pass
