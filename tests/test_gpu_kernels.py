@@ -108,6 +108,7 @@ def test_adamw_unaligned_pointers_take_the_scalar_path(zm, offset):
     assert_bits_equal(host_f32(dp)[:offset].view(np.uint32), p[:offset].view(np.uint32), "untouched")
 
 
+@pytest.mark.filterwarnings("ignore:overflow encountered:RuntimeWarning", "ignore:invalid value encountered:RuntimeWarning")
 def test_adamw_special_values(zm):
     n = 64
     p = np.linspace(-3, 3, n).astype(np.float32)
@@ -145,6 +146,7 @@ def _bf16_rounding_cases() -> np.ndarray:
     return np.concatenate([grid, nans]).view(np.float32)
 
 
+@pytest.mark.filterwarnings("ignore:overflow encountered:RuntimeWarning", "ignore:invalid value encountered:RuntimeWarning")
 @pytest.mark.parametrize("entry", ["flat", "list", "table"])
 def test_adamw_bf16_emit_every_rounding_case(zm, entry):
     """The kernels emit bf16 parameters with gfx950's packed convert. With lr = 0

@@ -67,6 +67,7 @@ def test_host_adamw_hyperparameter_corners(zm, case):
     assert (out == B).all()
 
 
+@pytest.mark.filterwarnings("ignore:overflow encountered:RuntimeWarning", "ignore:invalid value encountered:RuntimeWarning")
 def test_host_adamw_special_values_and_skip(zm):
     n = 64
     p = np.linspace(-3, 3, n).astype(np.float32)
