@@ -26,7 +26,7 @@ def zm():
     return m
 
 
-def _run(zm, n_ranks):
+def _run(zm, n_ranks, order=None):
     plan = zm.zero_partition_plan(NUMELS, n_ranks, 128)
     P, S, phi = plan.padded_numel, plan.shard_numel, plan.numel
     master = torch.empty(P, dtype=torch.float32, device=dev())
@@ -40,7 +40,7 @@ def _run(zm, n_ranks):
     for t in (1, 2):
         for k, r in enumerate(reps):
             synth.device_normal_bf16(r, 7, synth.KIND_REPLICA, t, k, 0, phi, 1e-3)
-        for rank in range(n_ranks):
+        for rank in (order if order is not None else range(n_ranks)):
             sl = slice(rank * S, (rank + 1) * S)
             zm.zero_grad_reduce_shard(plan, rank, reps, 0, P, grad[sl])
             zm.zero_shard_adamw_step(master[sl], m[sl], v[sl], grad[sl], param[sl], t,
@@ -88,3 +88,18 @@ def test_empty_window_and_empty_tensors(zm):
     zm.zero_flatten_params(empty, [torch.empty(0, dtype=torch.int16, device=dev())] * 2,
                            torch.empty(0, dtype=torch.int16, device=dev()))
     torch.cuda.synchronize()
+
+
+def test_rank_results_do_not_depend_on_update_order(zm):
+    """The emulated ranks share one device: each rank's reduce and update must
+    depend only on its own slice, not on which ranks ran before it. Eight ranks
+    updated in reverse and in a shuffled order give the bits of rank order."""
+    base = _run(zm, 8)
+    for order in (list(range(7, -1, -1)), [3, 6, 0, 5, 1, 7, 2, 4]):
+        note(f"update order {order}")
+        got = _run(zm, 8, order)
+        for name, a, b in zip(("master", "exp_avg", "exp_avg_sq", "grad"), got[:4], base[:4]):
+            assert_bits_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b, f"{order} {name}")
+        for i, (a, b) in enumerate(zip(got[4], base[4])):
+            assert_bits_equal(a, b, f"{order} tensor {i}")
