@@ -307,6 +307,59 @@ zero_status zero_shard_adamw_step(float* master, float* exp_avg, float* exp_avg_
                                   double weight_decay, const float* clip_scale,
                                   hipStream_t stream);
 
+/* Step counted on the device, for a step captured in a HIP graph. [ZF] "Execution
+ * Flow for ZeRO-1", step 3, repeated every iteration: zero_shard_adamw_step
+ * takes t from the host and computes the step's scalars there, so a captured
+ * launch would replay one step forever. A schedule holds, in device memory,
+ * the number of updates applied and the scalars of the next step, and a table
+ * of the scalars of steps 1..L (each as zero_shard_adamw_step computes them
+ * on the host, so the results are the same bits). L is the step from which
+ * both bias corrections are exactly 1 in fp64 (beta^t < 2^-56), or the length
+ * of the learning-rate list if longer: every later step has step L's scalars.
+ * For beta2 = 0.999, L = 38,797 (1.2 MB).
+ *
+ * zero_adamw_schedule_create: lr is a host array of n_lr >= 1 learning rates,
+ * step t using lr[min(t, n_lr) - 1] (one value: a constant rate); betas, eps
+ * and weight_decay as zero_shard_adamw_step; the first update applied is step
+ * first_step >= 1 (a resumed run passes its next step). Allocates on the
+ * current device. Errors: ZERO_EINVAL (bad hyperparameters, NULL lr or out,
+ * n_lr < 1, first_step < 1); ZERO_ERANGE when L would pass 2^24 (a beta within
+ * about 2.3e-6 of 1, or a longer list); ZERO_ENOMEM; ZERO_EHIP.
+ * zero_shard_adamw_step_scheduled: zero_shard_adamw_step's update and
+ * arguments, with the step's scalars read on the device from the schedule;
+ * it does not move the schedule on, so a step may update any number of
+ * arrays with it (buckets, tensors, ranks).
+ * zero_adamw_schedule_advance: once per step, after the step's updates on the
+ * same stream: counts the step as applied and loads the next step's scalars.
+ * A non-finite clip coefficient (the updates skipped) leaves the schedule as it
+ * is, so a skipped step is not counted. One lane; allocates nothing.
+ * zero_adamw_schedule_applied: the number of updates applied, read back
+ * synchronously (hipMemcpy; the caller first waits for the streams that
+ * advanced the schedule). zero_adamw_schedule_length: L (-1 for NULL).
+ * Calls that move one schedule on must be ordered by the caller (one stream).
+ * Errors of the step and advance: ZERO_EINVAL (NULL schedule, the schedule on
+ * another device, as zero_shard_adamw_step otherwise); ZERO_EHIP.
+ *
+ * zero_adamw_step_scalars: host only; the eight fp32 scalars every AdamW entry
+ * point computes for step t, in order beta1, 1-beta1, beta2, 1-beta2, eps,
+ * lr/(1-beta1^t), sqrt(1-beta2^t), 1-lr*weight_decay. Errors: as
+ * zero_shard_adamw_step's hyperparameter checks; ZERO_EINVAL for a NULL out. */
+typedef struct zero_adamw_schedule zero_adamw_schedule;
+zero_status zero_adamw_schedule_create(const double* lr, int64_t n_lr, double beta1, double beta2,
+                                       double eps, double weight_decay, int64_t first_step,
+                                       zero_adamw_schedule** out);
+void zero_adamw_schedule_free(zero_adamw_schedule* schedule);
+int64_t zero_adamw_schedule_length(const zero_adamw_schedule* schedule);
+zero_status zero_adamw_schedule_applied(const zero_adamw_schedule* schedule, int64_t* applied);
+zero_status zero_adamw_schedule_advance(zero_adamw_schedule* schedule, const float* clip_scale,
+                                        hipStream_t stream);
+zero_status zero_shard_adamw_step_scheduled(float* master, float* exp_avg, float* exp_avg_sq,
+                                            const uint16_t* grad, uint16_t* param_out, int64_t n,
+                                            const zero_adamw_schedule* schedule,
+                                            const float* clip_scale, hipStream_t stream);
+zero_status zero_adamw_step_scalars(int64_t step, double lr, double beta1, double beta2, double eps,
+                                    double weight_decay, float* out);
+
 /* Reduce and update in one pass. [ZF] "Execution Flow for ZeRO-1", steps 2-3:
  * the rank receives the averaged gradient of its slice and updates its master
  * weights and optimizer state from it. When the step needs no global norm

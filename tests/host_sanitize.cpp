@@ -25,6 +25,7 @@
 
 #include "internal.hpp"
 #include "pieces.hpp"
+#include "schedule.hpp"
 #include "tensor_major.hpp"
 
 namespace {
@@ -347,6 +348,49 @@ void check_overlap_search() {
     if (clashes < 1000) fail("too few overlapping lists drawn");
 }
 
+// A step schedule's table against the direct per-step computation: entry t - 1
+// is step t's scalars (with lr[min(t, n) - 1]), and every step past the table
+// has the last entry's scalars, bit for bit.
+void check_schedules() {
+    struct Case { std::vector<double> lr; double b1, b2, eps, wd; };
+    const Case cases[] = {{{1e-3}, 0.9, 0.999, 1e-8, 0.01},
+                          {{1e-3, 2e-3, 3e-3, 2.5e-3}, 0.9, 0.99, 1e-8, 0.1},
+                          {{0.5}, 0.0, 0.0, 1e-6, 0.0},
+                          {{1e-4}, 0.99, 0.9999, 1.0, -0.5},
+                          {std::vector<double>(50000, 7e-4), 0.5, 0.9, 1e-8, 0.01}};
+    for (const Case& c : cases) {
+        std::vector<zero::adam::StepScalars> table;
+        if (zero::adam::schedule_table(c.lr.data(), static_cast<int64_t>(c.lr.size()), c.b1, c.b2, c.eps,
+                                       c.wd, &table, "t") != ZERO_OK) {
+            fail("schedule table refused");
+            continue;
+        }
+        const int64_t L = static_cast<int64_t>(table.size()), n = static_cast<int64_t>(c.lr.size());
+        if (L < n) fail("schedule shorter than its learning rates");
+        auto same = [](const zero::adam::StepScalars& a, const zero::adam::StepScalars& b) {
+            return std::memcmp(&a, &b, sizeof(a)) == 0;
+        };
+        for (int64_t t = 1; t <= L + 2000; ++t) {
+            zero::adam::StepScalars want{};
+            if (zero::adam::step_scalars(t, c.lr[static_cast<size_t>((t < n ? t : n) - 1)], c.b1, c.b2, c.wd,
+                                         c.eps, &want, "t") != ZERO_OK) {
+                fail("step scalars refused");
+                break;
+            }
+            const auto& got = table[static_cast<size_t>((t < L ? t : L) - 1)];
+            if (!same(got, want)) { fail("schedule entry differs from the step's scalars"); break; }
+        }
+        for (const int64_t t : {int64_t(1) << 31, int64_t(1) << 40, int64_t(1) << 62}) {
+            zero::adam::StepScalars want{};
+            zero::adam::step_scalars(t, c.lr.back(), c.b1, c.b2, c.wd, c.eps, &want, "t");
+            if (!same(table.back(), want)) fail("far step differs from the schedule's last entry");
+        }
+    }
+    if (zero::adam::settled_step(0.9, 0.999, zero::adam::kMaxScheduleSteps) != 38797) fail("settled step");
+    if (zero::adam::settled_step(0.0, 0.0, 100) != 1) fail("settled step of zero betas");
+    if (zero::adam::settled_step(0.9, 1.0 - 1e-7, zero::adam::kMaxScheduleSteps) != -1) fail("settled step cap");
+}
+
 }  // namespace
 
 int main() {
@@ -366,6 +410,7 @@ int main() {
     }
     edge_cases();
     check_overlap_search();
+    check_schedules();
     std::mt19937_64 rng(11);
     for (int it = 0; it < 400; ++it) {
         const int T = static_cast<int>(rng() % 9);

@@ -1,7 +1,7 @@
 """The library's host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
-tests/host_sanitize.cpp is built with g++ together with plan.cpp, pieces.cpp and
-status.cpp, with -fsanitize=address,undefined and no recovery, and run on the
+tests/host_sanitize.cpp is built with g++ together with plan.cpp, pieces.cpp,
+schedule.cpp and status.cpp, with -fsanitize=address,undefined and no recovery, and run on the
 workload lists (flat and Shard(0), the large ones checked through the ABI's
 segment queries, the small ones element by element), 800 random lists, empty
 and zero-sized tensors, argument errors and sizes that overflow int64. Any
@@ -29,7 +29,8 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
            "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", f"-I{ROCM}/include",
            "-D__HIP_PLATFORM_AMD__", f"-I{CSRC}", f"-I{os.path.join(ROOT, 'include')}",
            os.path.join(ROOT, "tests", "host_sanitize.cpp"), os.path.join(CSRC, "plan.cpp"),
-           os.path.join(CSRC, "pieces.cpp"), os.path.join(CSRC, "status.cpp"), "-o", exe,
+           os.path.join(CSRC, "pieces.cpp"), os.path.join(CSRC, "schedule.cpp"),
+           os.path.join(CSRC, "status.cpp"), "-o", exe,
            f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib"]
     b = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert b.returncode == 0, b.stderr[-3000:]

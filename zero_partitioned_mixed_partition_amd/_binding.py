@@ -101,6 +101,16 @@ _ct_free = _fn("zero_copy_table_free", None, [c_vp])
 _rt_create = _fn("zero_reduce_table_create", c_i32,
                  [c_vp, c_i32, ctypes.POINTER(c_vp), c_i32, c_vp, ctypes.POINTER(c_vp)])
 _rt_run = _fn("zero_reduce_table_run", c_i32, [c_vp, c_vp, c_vp])
+_sched_create = _fn("zero_adamw_schedule_create", c_i32,
+                    [ctypes.POINTER(c_dbl), c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_i64, ctypes.POINTER(c_vp)])
+_sched_free = _fn("zero_adamw_schedule_free", None, [c_vp])
+_sched_length = _fn("zero_adamw_schedule_length", c_i64, [c_vp])
+_sched_applied = _fn("zero_adamw_schedule_applied", c_i32, [c_vp, ctypes.POINTER(c_i64)])
+_sched_advance = _fn("zero_adamw_schedule_advance", c_i32, [c_vp, c_vp, c_vp])
+_adamw_sched = _fn("zero_shard_adamw_step_scheduled", c_i32,
+                   [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp])
+_step_scalars = _fn("zero_adamw_step_scalars", c_i32,
+                    [c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl, ctypes.POINTER(ctypes.c_float)])
 _rt_blocks = _fn("zero_reduce_table_blocks", c_i64, [c_vp])
 _rt_free = _fn("zero_reduce_table_free", None, [c_vp])
 _status_string = _fn("zero_status_string", ctypes.c_char_p, [c_i32])
@@ -674,6 +684,92 @@ def zero_last_error() -> str:
 # The same entry points with their arguments marshalled once, for loops that
 # call them with unchanged buffers every step: each call then costs one ctypes
 # dispatch instead of rebuilding pointer tables.
+
+def zero_adamw_step_scalars(step: int, lr: float, beta1: float, beta2: float, eps: float,
+                            weight_decay: float):
+    """The eight fp32 scalars every AdamW call computes for `step` (host only): beta1,
+    1-beta1, beta2, 1-beta2, eps, lr/(1-beta1^t), sqrt(1-beta2^t), 1-lr*weight_decay."""
+    import numpy as np
+    out = (ctypes.c_float * 8)()
+    _check(_step_scalars(step, lr, beta1, beta2, eps, weight_decay, out), "zero_adamw_step_scalars")
+    return np.frombuffer(bytes(out), dtype=np.float32).copy()
+
+
+class AdamWSchedule:
+    """Owner of a zero_adamw_schedule: AdamW's step counted on the device (on the
+    current device), so that a step captured in a HIP graph replays successive
+    steps. lr: one learning rate, or a sequence (step t uses lr[min(t, len) - 1])."""
+
+    def __init__(self, lr, beta1: float, beta2: float, eps: float, weight_decay: float,
+                 first_step: int = 1):
+        rates = [float(x) for x in (lr if hasattr(lr, "__len__") else [lr])]
+        arr = (c_dbl * max(len(rates), 1))(*rates)
+        self._h = c_vp()
+        _check(_sched_create(arr, len(rates), beta1, beta2, eps, weight_decay, first_step,
+                             ctypes.byref(self._h)), "zero_adamw_schedule_create")
+        self._free = _sched_free
+        import torch
+        self._device = torch.cuda.current_device()
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        free = getattr(self, "_free", None)
+        if h is not None and h.value and free is not None:
+            free(h)
+            h.value = None
+
+    @property
+    def handle(self) -> c_vp:
+        return self._h
+
+    @property
+    def length(self) -> int:
+        return int(_sched_length(self._h))
+
+    def applied(self) -> int:
+        """Updates applied so far (a synchronous read; wait for the streams first)."""
+        out = c_i64()
+        _check(_sched_applied(self._h, ctypes.byref(out)), "zero_adamw_schedule_applied")
+        return int(out.value)
+
+    def _stream_of(self, stream) -> int:
+        if stream is not None:
+            return int(stream)
+        import torch
+        return torch.cuda.current_stream(self._device).cuda_stream
+
+    def advance(self, clip_scale=None, stream=None) -> None:
+        self.prepare_advance(clip_scale, stream)()
+
+    def prepare_advance(self, clip_scale=None, stream=None) -> "Prepared":
+        _need(clip_scale, 1, "clip_scale")
+        p = Prepared(_sched_advance, [self._h, _ptr(clip_scale, 4, "clip_scale"), self._stream_of(stream)],
+                     "zero_adamw_schedule_advance")
+        p._keep = (self, clip_scale)
+        return p
+
+
+def prepare_shard_adamw_step_scheduled(master, exp_avg, exp_avg_sq, grad, param_out,
+                                       schedule: AdamWSchedule, clip_scale=None, stream=None) -> "Prepared":
+    """zero_shard_adamw_step_scheduled with its arguments marshalled once."""
+    n = master.numel()
+    _check_adamw_args(n, (master, exp_avg, exp_avg_sq, grad, param_out), clip_scale)
+    p = Prepared(_adamw_sched, [_ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                                _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(grad, 2, "grad"),
+                                _ptr(param_out, 2, "param_out"), n, schedule.handle,
+                                _ptr(clip_scale, 4, "clip_scale"), _stream(stream, master)],
+                 "zero_shard_adamw_step_scheduled")
+    p._keep = (master, exp_avg, exp_avg_sq, grad, param_out, schedule, clip_scale)
+    return p
+
+
+def zero_shard_adamw_step_scheduled(master, exp_avg, exp_avg_sq, grad, param_out,
+                                    schedule: AdamWSchedule, clip_scale=None, stream=None) -> None:
+    """The flat AdamW update with the step's scalars read on the device from `schedule`
+    (which this call does not move on: call schedule.advance once per step)."""
+    prepare_shard_adamw_step_scheduled(master, exp_avg, exp_avg_sq, grad, param_out, schedule,
+                                       clip_scale, stream)()
+
 
 class Prepared:
     def __init__(self, fn, args, where: str, step_index: Optional[int] = None):

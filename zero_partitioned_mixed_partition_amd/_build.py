@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzero_mi355x.so")
 
-SOURCES = ["status.cpp", "plan.cpp", "pieces.cpp", "offload.cpp", "adamw.hip", "reduce.hip", "gather.hip"]
+SOURCES = ["status.cpp", "plan.cpp", "pieces.cpp", "schedule.cpp", "offload.cpp", "adamw.hip", "reduce.hip",
+           "gather.hip"]
 
 # -ffp-contract=off: the AdamW and reduction arithmetic is specified operation
 # by operation; no multiply-add fusion. Packed fp32 instructions are disabled.

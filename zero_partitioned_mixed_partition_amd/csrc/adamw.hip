@@ -29,6 +29,7 @@
 
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "schedule.hpp"
 
 #pragma clang fp contract(off)
 
@@ -50,9 +51,8 @@ constexpr int kThreads = ZERO_ADAMW_THREADS;
 constexpr int kEpt = ZERO_ADAMW_EPT;
 static_assert(kEpt == 1 || kEpt == 2 || kEpt == 4, "1, 2 or 4 elements per lane");
 
-struct AdamScalars {
-    float beta1, one_minus_beta1, beta2, one_minus_beta2, eps, step_size, sqrt_bc2, decay;
-};
+// The per-step scalars, computed on the host (schedule.hpp).
+using AdamScalars = zero::adam::StepScalars;
 
 // One element, in the documented order; every line is one IEEE fp32 operation.
 __device__ __forceinline__ void adam_elem(float& p, float& m, float& v, float g,
@@ -179,15 +179,10 @@ constexpr int kPersistPerCu = ZERO_ADAMW_PERSIST;
 // Lane groups [0, n/E) of E consecutive elements, then the n % E tail one
 // element per lane. For E > 1 the pointers are aligned to E elements.
 template <int E>
-__global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ master,
-                                                         float* __restrict__ m,
-                                                         float* __restrict__ v,
-                                                         const uint16_t* __restrict__ grad,
-                                                         uint16_t* __restrict__ param, int64_t n,
-                                                         AdamScalars c,
-                                                         const float* __restrict__ clip_scale) {
-    const float clip = read_clip(clip_scale);
-    if (!isfinite(clip)) return;
+__device__ __forceinline__ void adamw_body(float* __restrict__ master, float* __restrict__ m,
+                                           float* __restrict__ v, const uint16_t* __restrict__ grad,
+                                           uint16_t* __restrict__ param, int64_t n,
+                                           const AdamScalars& c, float clip) {
     const int64_t groups = n / E;
     // The grid is one row of workgroups, or, past the 2^32 work-items one grid
     // dimension holds, several rows; the dispatcher issues them row after row,
@@ -206,6 +201,58 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ mas
         const int64_t tail = n - groups * E;
         if (tid < tail) Lane<1>::update(master, m, v, grad, param, groups * E + tid, clip, c);
     }
+}
+
+template <int E>
+__global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ master,
+                                                         float* __restrict__ m,
+                                                         float* __restrict__ v,
+                                                         const uint16_t* __restrict__ grad,
+                                                         uint16_t* __restrict__ param, int64_t n,
+                                                         AdamScalars c,
+                                                         const float* __restrict__ clip_scale) {
+    const float clip = read_clip(clip_scale);
+    if (!isfinite(clip)) return;
+    adamw_body<E>(master, m, v, grad, param, n, c, clip);
+}
+
+// A step schedule's device state: the scalars of the next step to apply and
+// the number of updates applied so far. The scheduled AdamW reads `next`; the
+// advance kernel, once per step, moves both on.
+struct alignas(64) AdamState {
+    AdamScalars next;
+    int64_t applied;
+    int64_t unused[3];
+};
+static_assert(sizeof(AdamState) == 64, "one 64-byte state");
+
+// The flat update with the step's scalars read from the schedule's state (one
+// 32-byte load per wave, beside the clip coefficient's), so a captured graph
+// replays successive steps.
+template <int E>
+__global__ __launch_bounds__(kThreads) void adamw_sched_kernel(float* __restrict__ master,
+                                                               float* __restrict__ m,
+                                                               float* __restrict__ v,
+                                                               const uint16_t* __restrict__ grad,
+                                                               uint16_t* __restrict__ param, int64_t n,
+                                                               const AdamState* __restrict__ state,
+                                                               const float* __restrict__ clip_scale) {
+    const float clip = read_clip(clip_scale);
+    if (!isfinite(clip)) return;
+    const AdamScalars c = state->next;
+    adamw_body<E>(master, m, v, grad, param, n, c, clip);
+}
+
+// One lane: after a step's updates, counts the step as applied and loads the
+// following step's scalars, table[min(t, length) - 1] for step t. A
+// non-finite clip coefficient (the updates skipped) leaves the state as it is.
+__global__ void adamw_advance_kernel(AdamState* __restrict__ state, const AdamScalars* __restrict__ table,
+                                     int64_t length, const float* __restrict__ clip_scale) {
+    if (threadIdx.x != 0 || !isfinite(read_clip(clip_scale))) return;
+    const int64_t applied = state->applied + 1;
+    const int64_t next = applied + 1;
+    state->next = table[(next < length ? next : length) - 1];
+    state->applied = applied;
 }
 
 // Multi-tensor form: a ragged list of tensors, each with its own five arrays,
@@ -385,20 +432,6 @@ int64_t blocks_for(int64_t items) {
     return blocks < 1 ? 1 : blocks;
 }
 
-zero_status check_hyper(int64_t step, double lr, double beta1, double beta2, double eps,
-                        double weight_decay, const char* who) {
-    using zero::fail;
-    const std::string w(who);
-    if (step < 1) return fail(ZERO_EINVAL, w + ": step must be >= 1");
-    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
-        return fail(ZERO_EINVAL, w + ": betas must lie in [0, 1)");
-    if (!(eps > 0.0) || !std::isfinite(eps))
-        return fail(ZERO_EINVAL, w + ": eps must be finite and > 0");
-    if (!(lr >= 0.0) || !std::isfinite(lr) || !std::isfinite(weight_decay))
-        return fail(ZERO_EINVAL, w + ": lr and weight_decay must be finite, lr >= 0");
-    return ZERO_OK;
-}
-
 // The checks every multi-tensor call makes on its list (n_tensors > 0).
 zero_status check_mt_list(float* const* masters, float* const* exp_avgs, float* const* exp_avg_sqs,
                           const uint16_t* const* grads, uint16_t* const* params_out,
@@ -425,21 +458,46 @@ zero_status check_mt_list(float* const* masters, float* const* exp_avgs, float* 
     return ZERO_OK;
 }
 
-// Scalars in fp64, each rounded once to fp32.
-zero_status make_scalars(int64_t step, double lr, double beta1, double beta2, double weight_decay,
-                         double eps, AdamScalars* c, const char* who) {
-    const double bc1 = 1.0 - std::pow(beta1, static_cast<double>(step));
-    const double bc2 = 1.0 - std::pow(beta2, static_cast<double>(step));
-    if (!(bc1 > 0.0) || !(bc2 > 0.0))
-        return zero::fail(ZERO_EINVAL, std::string(who) + ": bias correction is zero");
-    c->beta1 = static_cast<float>(beta1);
-    c->one_minus_beta1 = static_cast<float>(1.0 - beta1);
-    c->beta2 = static_cast<float>(beta2);
-    c->one_minus_beta2 = static_cast<float>(1.0 - beta2);
-    c->eps = static_cast<float>(eps);
-    c->step_size = static_cast<float>(lr / bc1);
-    c->sqrt_bc2 = static_cast<float>(std::sqrt(bc2));
-    c->decay = static_cast<float>(1.0 - lr * weight_decay);
+}  // namespace
+
+namespace {
+
+// The flat update's argument checks (n > 0): no NULL array, no written array
+// overlapping another array of the call.
+zero_status check_flat(float* master, float* exp_avg, float* exp_avg_sq, const uint16_t* grad,
+                       uint16_t* param_out, int64_t n, const char* who) {
+    using zero::fail;
+    if (!master || !exp_avg || !exp_avg_sq || !grad || !param_out)
+        return fail(ZERO_EINVAL, std::string(who) + ": NULL array");
+    const size_t fbytes = static_cast<size_t>(n) * 4, hbytes = static_cast<size_t>(n) * 2;
+    const zero::Span wr[] = {{master, fbytes, "master"}, {exp_avg, fbytes, "exp_avg"},
+                             {exp_avg_sq, fbytes, "exp_avg_sq"}, {param_out, hbytes, "param_out"}};
+    const zero::Span rd[] = {{grad, hbytes, "grad"}};
+    const std::string clash = zero::first_overlap(wr, 4, rd, 1);
+    if (!clash.empty()) return fail(ZERO_EINVAL, std::string(who) + ": " + clash);
+    return ZERO_OK;
+}
+
+// The flat update's launch shape (n > 0): one lane group per lane, the whole
+// shard in one dispatch. A grid dimension holds fewer than 2^32 work-items, so
+// a larger shard (Llama-3-70B's rank: 8.8e9 elements) takes a grid of up to
+// kMaxRow workgroups per row and as many rows as it needs, at most rows - 1
+// workgroups past the shard's end. `vec` tells whether every pointer is
+// aligned for kEpt elements per lane.
+zero_status flat_grid(float* master, float* exp_avg, float* exp_avg_sq, const uint16_t* grad,
+                      uint16_t* param_out, int64_t n, dim3* grid, bool* vec, const char* who) {
+    constexpr int64_t kMaxRow = (int64_t(1) << 32) / kThreads - 1;
+    *vec = kEpt > 1 && aligned(master, 4 * kEpt) && aligned(exp_avg, 4 * kEpt) &&
+           aligned(exp_avg_sq, 4 * kEpt) && aligned(grad, 2 * kEpt) && aligned(param_out, 2 * kEpt);
+    const int ept = *vec ? kEpt : 1;
+    int64_t blocks = blocks_for(n / ept + (n % ept ? 1 : 0));
+    if (kPersistPerCu > 0) {
+        const int64_t cap = static_cast<int64_t>(kPersistPerCu) * zero::device_cu_count();
+        if (blocks > cap) blocks = cap;
+    }
+    const int64_t rows = (blocks + kMaxRow - 1) / kMaxRow;
+    if (rows > 0x7FFFFFFF) return zero::fail(ZERO_ERANGE, std::string(who) + ": n too large for one dispatch");
+    *grid = dim3(static_cast<unsigned>((blocks + rows - 1) / rows), static_cast<unsigned>(rows));
     return ZERO_OK;
 }
 
@@ -451,42 +509,21 @@ extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, floa
                                              double eps, double weight_decay,
                                              const float* clip_scale, hipStream_t stream) {
     using zero::fail;
+    static const char* const who = "zero_shard_adamw_step";
     zero::clear_error();
     if (n < 0) return fail(ZERO_EINVAL, "zero_shard_adamw_step: n < 0");
-    zero_status st = check_hyper(step, lr, beta1, beta2, eps, weight_decay, "zero_shard_adamw_step");
+    zero_status st = zero::adam::check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
     if (st != ZERO_OK) return st;
     if (n == 0) return ZERO_OK;
-    if (!master || !exp_avg || !exp_avg_sq || !grad || !param_out)
-        return fail(ZERO_EINVAL, "zero_shard_adamw_step: NULL array");
-    const size_t fbytes = static_cast<size_t>(n) * 4, hbytes = static_cast<size_t>(n) * 2;
-    const zero::Span wr[] = {{master, fbytes, "master"}, {exp_avg, fbytes, "exp_avg"},
-                             {exp_avg_sq, fbytes, "exp_avg_sq"}, {param_out, hbytes, "param_out"}};
-    const zero::Span rd[] = {{grad, hbytes, "grad"}};
-    const std::string clash = zero::first_overlap(wr, 4, rd, 1);
-    if (!clash.empty()) return fail(ZERO_EINVAL, "zero_shard_adamw_step: " + clash);
-
-    AdamScalars c;
-    st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, "zero_shard_adamw_step");
+    st = check_flat(master, exp_avg, exp_avg_sq, grad, param_out, n, who);
     if (st != ZERO_OK) return st;
-
-    // One lane group per lane, the whole shard in one dispatch. A grid dimension
-    // holds fewer than 2^32 work-items, so a larger shard (Llama-3-70B's rank:
-    // 8.8e9 elements) takes a grid of up to kMaxRow workgroups per row and as
-    // many rows as it needs, at most rows - 1 workgroups past the shard's end.
-    constexpr int64_t kMaxRow = (int64_t(1) << 32) / kThreads - 1;
-    const bool vec = kEpt > 1 && aligned(master, 4 * kEpt) && aligned(exp_avg, 4 * kEpt) &&
-                     aligned(exp_avg_sq, 4 * kEpt) && aligned(grad, 2 * kEpt) &&
-                     aligned(param_out, 2 * kEpt);
-    const int ept = vec ? kEpt : 1;
-    int64_t blocks = blocks_for(n / ept + (n % ept ? 1 : 0));
-    if (kPersistPerCu > 0) {
-        const int64_t cap = static_cast<int64_t>(kPersistPerCu) * zero::device_cu_count();
-        if (blocks > cap) blocks = cap;
-    }
-    const int64_t rows = (blocks + kMaxRow - 1) / kMaxRow;
-    if (rows > 0x7FFFFFFF)
-        return fail(ZERO_ERANGE, "zero_shard_adamw_step: n too large for one dispatch");
-    const dim3 grid(static_cast<unsigned>((blocks + rows - 1) / rows), static_cast<unsigned>(rows));
+    AdamScalars c;
+    st = zero::adam::step_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
+    if (st != ZERO_OK) return st;
+    dim3 grid;
+    bool vec = false;
+    st = flat_grid(master, exp_avg, exp_avg_sq, grad, param_out, n, &grid, &vec, who);
+    if (st != ZERO_OK) return st;
     if (vec)
         hipLaunchKernelGGL(adamw_kernel<kEpt>, grid, dim3(kThreads), 0, stream, master, exp_avg,
                            exp_avg_sq, grad, param_out, n, c, clip_scale);
@@ -494,6 +531,149 @@ extern "C" zero_status zero_shard_adamw_step(float* master, float* exp_avg, floa
         hipLaunchKernelGGL(adamw_kernel<1>, grid, dim3(kThreads), 0, stream, master, exp_avg,
                            exp_avg_sq, grad, param_out, n, c, clip_scale);
     return zero::check_hip(hipGetLastError(), "zero_shard_adamw_step launch");
+}
+
+// ------------------------------------------------------------ step schedule
+
+struct zero_adamw_schedule {
+    int device = -1;
+    void* mem = nullptr;               // the state, then the table
+    AdamState* state = nullptr;
+    const AdamScalars* table = nullptr;
+    int64_t length = 0;
+};
+
+extern "C" zero_status zero_adamw_step_scalars(int64_t step, double lr, double beta1, double beta2,
+                                               double eps, double weight_decay, float* out) {
+    static const char* const who = "zero_adamw_step_scalars";
+    zero::clear_error();
+    if (out == nullptr) return zero::fail(ZERO_EINVAL, "zero_adamw_step_scalars: NULL out");
+    zero_status st = zero::adam::check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
+    if (st != ZERO_OK) return st;
+    AdamScalars c;
+    st = zero::adam::step_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
+    if (st != ZERO_OK) return st;
+    const float v[8] = {c.beta1, c.one_minus_beta1, c.beta2, c.one_minus_beta2, c.eps, c.step_size,
+                        c.sqrt_bc2, c.decay};
+    for (int k = 0; k < 8; ++k) out[k] = v[k];
+    return ZERO_OK;
+}
+
+extern "C" zero_status zero_adamw_schedule_create(const double* lr, int64_t n_lr, double beta1,
+                                                  double beta2, double eps, double weight_decay,
+                                                  int64_t first_step, zero_adamw_schedule** out) {
+    using zero::fail;
+    static const char* const who = "zero_adamw_schedule_create";
+    zero::clear_error();
+    if (out == nullptr) return fail(ZERO_EINVAL, "zero_adamw_schedule_create: NULL out");
+    *out = nullptr;
+    if (first_step < 1) return fail(ZERO_EINVAL, "zero_adamw_schedule_create: first_step must be >= 1");
+    std::vector<AdamScalars> table;
+    zero_adamw_schedule* sch = nullptr;
+    try {
+        const zero_status cs = zero::adam::schedule_table(lr, n_lr, beta1, beta2, eps, weight_decay, &table, who);
+        if (cs != ZERO_OK) return cs;
+        sch = new zero_adamw_schedule;
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "zero_adamw_schedule_create: host allocation failed");
+    }
+    sch->length = static_cast<int64_t>(table.size());
+    AdamState state{};
+    state.applied = first_step - 1;
+    state.next = table[static_cast<size_t>((first_step < sch->length ? first_step : sch->length) - 1)];
+    zero_status st = zero::check_hip(hipGetDevice(&sch->device), who);
+    const size_t table_bytes = table.size() * sizeof(AdamScalars);
+    if (st == ZERO_OK) st = zero::check_hip(hipMalloc(&sch->mem, 256 + table_bytes), who);
+    if (st == ZERO_OK) {
+        sch->state = static_cast<AdamState*>(sch->mem);
+        sch->table = reinterpret_cast<const AdamScalars*>(static_cast<char*>(sch->mem) + 256);
+        st = zero::check_hip(hipMemcpy(sch->state, &state, sizeof(state), hipMemcpyHostToDevice), who);
+    }
+    if (st == ZERO_OK)
+        st = zero::check_hip(hipMemcpy(const_cast<AdamScalars*>(sch->table), table.data(), table_bytes,
+                                       hipMemcpyHostToDevice), who);
+    if (st != ZERO_OK) {
+        if (sch->mem) (void)hipFree(sch->mem);
+        delete sch;
+        return st;
+    }
+    *out = sch;
+    return ZERO_OK;
+}
+
+extern "C" void zero_adamw_schedule_free(zero_adamw_schedule* schedule) {
+    if (!schedule) return;
+    if (schedule->mem) (void)hipFree(schedule->mem);
+    delete schedule;
+}
+
+extern "C" int64_t zero_adamw_schedule_length(const zero_adamw_schedule* schedule) {
+    return schedule ? schedule->length : -1;
+}
+
+extern "C" zero_status zero_adamw_schedule_applied(const zero_adamw_schedule* schedule, int64_t* applied) {
+    zero::clear_error();
+    if (schedule == nullptr || applied == nullptr)
+        return zero::fail(ZERO_EINVAL, "zero_adamw_schedule_applied: NULL schedule or out");
+    AdamState state{};
+    const zero_status st = zero::check_hip(hipMemcpy(&state, schedule->state, sizeof(state), hipMemcpyDeviceToHost),
+                                           "zero_adamw_schedule_applied");
+    if (st == ZERO_OK) *applied = state.applied;
+    return st;
+}
+
+namespace {
+
+zero_status check_schedule_device(const zero_adamw_schedule* schedule, const char* who) {
+    int dev = -1;
+    const zero_status st = zero::check_hip(hipGetDevice(&dev), who);
+    if (st != ZERO_OK) return st;
+    if (dev != schedule->device)
+        return zero::fail(ZERO_EINVAL, std::string(who) + ": the schedule lives on device " +
+                                           std::to_string(schedule->device) + ", the current device is " +
+                                           std::to_string(dev));
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_adamw_schedule_advance(zero_adamw_schedule* schedule, const float* clip_scale,
+                                                   hipStream_t stream) {
+    static const char* const who = "zero_adamw_schedule_advance";
+    zero::clear_error();
+    if (schedule == nullptr) return zero::fail(ZERO_EINVAL, "zero_adamw_schedule_advance: NULL schedule");
+    const zero_status st = check_schedule_device(schedule, who);
+    if (st != ZERO_OK) return st;
+    hipLaunchKernelGGL(adamw_advance_kernel, dim3(1), dim3(64), 0, stream, schedule->state, schedule->table,
+                       schedule->length, clip_scale);
+    return zero::check_hip(hipGetLastError(), "zero_adamw_schedule_advance launch");
+}
+
+extern "C" zero_status zero_shard_adamw_step_scheduled(float* master, float* exp_avg, float* exp_avg_sq,
+                                                       const uint16_t* grad, uint16_t* param_out, int64_t n,
+                                                       const zero_adamw_schedule* schedule,
+                                                       const float* clip_scale, hipStream_t stream) {
+    using zero::fail;
+    static const char* const who = "zero_shard_adamw_step_scheduled";
+    zero::clear_error();
+    if (schedule == nullptr) return fail(ZERO_EINVAL, "zero_shard_adamw_step_scheduled: NULL schedule");
+    if (n < 0) return fail(ZERO_EINVAL, "zero_shard_adamw_step_scheduled: n < 0");
+    zero_status st = check_schedule_device(schedule, who);
+    if (st != ZERO_OK) return st;
+    if (n == 0) return ZERO_OK;
+    st = check_flat(master, exp_avg, exp_avg_sq, grad, param_out, n, who);
+    if (st != ZERO_OK) return st;
+    dim3 grid;
+    bool vec = false;
+    st = flat_grid(master, exp_avg, exp_avg_sq, grad, param_out, n, &grid, &vec, who);
+    if (st != ZERO_OK) return st;
+    if (vec)
+        hipLaunchKernelGGL(adamw_sched_kernel<kEpt>, grid, dim3(kThreads), 0, stream, master, exp_avg,
+                           exp_avg_sq, grad, param_out, n, schedule->state, clip_scale);
+    else
+        hipLaunchKernelGGL(adamw_sched_kernel<1>, grid, dim3(kThreads), 0, stream, master, exp_avg,
+                           exp_avg_sq, grad, param_out, n, schedule->state, clip_scale);
+    return zero::check_hip(hipGetLastError(), "zero_shard_adamw_step_scheduled launch");
 }
 
 extern "C" zero_status zero_multi_tensor_adamw_step(float* const* masters, float* const* exp_avgs,
@@ -508,13 +688,13 @@ extern "C" zero_status zero_multi_tensor_adamw_step(float* const* masters, float
     static const char* const who = "zero_multi_tensor_adamw_step";
     zero::clear_error();
     if (n_tensors < 0) return fail(ZERO_EINVAL, "zero_multi_tensor_adamw_step: n_tensors < 0");
-    zero_status st = check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
+    zero_status st = zero::adam::check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
     if (st != ZERO_OK) return st;
     if (n_tensors == 0) return ZERO_OK;
     st = check_mt_list(masters, exp_avgs, exp_avg_sqs, grads, params_out, numels, n_tensors, who);
     if (st != ZERO_OK) return st;
     AdamScalars c;
-    st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
+    st = zero::adam::step_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
     if (st != ZERO_OK) return st;
     MtBatch batch{};
     auto flush = [&]() -> zero_status {
@@ -667,7 +847,7 @@ extern "C" zero_status zero_mt_table_adamw_step(const zero_mt_table* table, int6
     static const char* const who = "zero_mt_table_adamw_step";
     zero::clear_error();
     if (!table) return fail(ZERO_EINVAL, "zero_mt_table_adamw_step: NULL table");
-    zero_status st = check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
+    zero_status st = zero::adam::check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
     if (st != ZERO_OK) return st;
     if (table->blocks == 0) return ZERO_OK;
     int dev = -1;
@@ -678,7 +858,7 @@ extern "C" zero_status zero_mt_table_adamw_step(const zero_mt_table* table, int6
                                      std::to_string(table->device) + ", the current device is " +
                                      std::to_string(dev));
     AdamScalars c;
-    st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
+    st = zero::adam::step_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
     if (st != ZERO_OK) return st;
     // A dispatch holds fewer than 2^32 work-items: longer lists take several launches.
     constexpr int64_t kMaxBlocks = zero::kTableLaunchBlocks;
@@ -713,7 +893,7 @@ extern "C" zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t ran
                                      std::to_string(ZERO_MAX_REPLICAS));
     if (begin < 0 || count < 0 || begin > plan->padded || count > plan->padded - begin)
         return fail(ZERO_EINVAL, "zero_reduce_adamw_step: window outside [0, P)");
-    zero_status st = check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
+    zero_status st = zero::adam::check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
     if (st != ZERO_OK) return st;
     const int64_t shard_lo = static_cast<int64_t>(rank) * plan->shard;
     const int64_t lo = begin > shard_lo ? begin : shard_lo;
@@ -743,7 +923,7 @@ extern "C" zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t ran
     }
     if (!clash.empty()) return fail(ZERO_EINVAL, "zero_reduce_adamw_step: " + clash);
     AdamScalars c;
-    st = make_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
+    st = zero::adam::step_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
     if (st != ZERO_OK) return st;
     constexpr int64_t kMaxRow = (int64_t(1) << 32) / kThreads - 1;
     const int64_t blocks = blocks_for(n);

@@ -73,6 +73,14 @@ class RankStep:
                  parameter shard stay coalesced buffers (the reduce's output
                  and the gather's input), and the shard's padding is never
                  updated.
+    device_step  AdamW's step counted on the device (a zero_adamw_schedule,
+                 self.schedule): the update reads the step's scalars from device
+                 memory and an advance call after it counts the step, only when
+                 the clip coefficient is finite. A skipped step is then not
+                 counted, and the whole step can be captured in a HIP graph and
+                 replayed for successive steps. Flat device state only (not
+                 with per_param or offload); the one-pass update, which takes
+                 the step from the host, is not used.
     """
 
     # Measured on MI355X, no clip: with 8 replicas per window the one pass takes
@@ -84,9 +92,11 @@ class RankStep:
     def __init__(self, plan: zb.Plan, rank: int, n_windows: int, hyper: Hyper, max_norm: float,
                  device: torch.device, gather: bool = True, offload: bool = False,
                  offload_chunk: int = 1 << 21, host_threads: int = 0, fuse: bool = True,
-                 per_param: bool = False):
+                 per_param: bool = False, device_step: bool = False):
         if per_param and offload:
             raise ValueError("per-parameter state and ZeRO-Offload are separate layouts")
+        if device_step and (per_param or offload):
+            raise ValueError("the device-counted step takes the flat device state")
         self.plan, self.rank, self.hyper, self.max_norm = plan, rank, hyper, max_norm
         self.device = device
         self.offload, self.host_threads = offload, host_threads
@@ -131,6 +141,12 @@ class RankStep:
         self.workspace = zb.reduce_workspace(s, device)
         self.n_windows = n_windows
         self.t = 0
+        self.device_step = device_step
+        self.schedule = None
+        if device_step:
+            with torch.cuda.device(device):
+                self.schedule = zb.AdamWSchedule(hyper.lr, hyper.beta1, hyper.beta2, hyper.eps,
+                                                 hyper.weight_decay)
         self._calls = {}
 
     def set_remote_partials(self, partials: Sequence[float]) -> None:
@@ -191,6 +207,12 @@ class RankStep:
         lowers self.t.)"""
         self.t += 1
         clip = self.scale if self.max_norm > 0 else None
+        if self.device_step:    # the step's scalars on the device, then the count moves on
+            self._prepared("adamw", stream, lambda st: zb.prepare_shard_adamw_step_scheduled(
+                self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
+                self.schedule, clip_scale=clip, stream=st))()
+            self._prepared("advance", stream, lambda st: self.schedule.prepare_advance(clip, st))()
+            return
         if self.per_param:
             own = self.param_shards[self.rank]
             sl = [slice(soff, soff + ln) for (_, _, soff, ln) in self.segments]
@@ -209,6 +231,11 @@ class RankStep:
             self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
             clip_scale=clip, stream=st, **self.hyper.as_kwargs()))(self.t)
 
+    def steps_applied(self) -> int:
+        """Updates applied: the device count with device_step (a synchronous read),
+        else self.t (iterations issued, skipped ones included)."""
+        return self.schedule.applied() if self.device_step else self.t
+
     def reduce_update(self, windows: Sequence[Tuple[int, int, Sequence[torch.Tensor]]],
                       stream=None):
         """reduce() then adamw() with no clip, as one pass per window
@@ -218,9 +245,9 @@ class RankStep:
         averaged gradient is not stored and no norm partial is taken."""
         if len(windows) != self.n_windows:
             raise ValueError("window count differs from the one the step was built for")
-        if self.offload or self.per_param or self.max_norm > 0:
+        if self.offload or self.per_param or self.max_norm > 0 or self.device_step:
             raise ValueError("the one-pass update runs on the device, over flat state, without "
-                             "clipping")
+                             "clipping, with the step from the host")
         spans = sorted((b, b + c) for b, c, _ in windows if c > 0)
         if any(a[1] > b[0] for a, b in zip(spans, spans[1:])):
             raise ValueError("windows overlap: the one-pass update needs disjoint windows")
@@ -244,7 +271,7 @@ class RankStep:
         disjoint = all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
         narrow = all(len(reps) <= self.FUSE_MAX_REPLICAS for _, _, reps in windows)
         if (self.fuse and self.max_norm <= 0 and not self.offload and not self.per_param
-                and disjoint and narrow):
+                and not self.device_step and disjoint and narrow):
             self.reduce_update(windows, stream)
         else:
             self.reduce(windows, stream)
