@@ -359,6 +359,13 @@ zero_status zero_shard_adamw_step_scheduled(float* master, float* exp_avg, float
                                             const float* clip_scale, hipStream_t stream);
 zero_status zero_adamw_step_scalars(int64_t step, double lr, double beta1, double beta2, double eps,
                                     double weight_decay, float* out);
+/* The scheduled forms of the multi-tensor table step and of the one-pass
+ * reduce and update (declared with their plain forms below): the same
+ * arguments and results, with the step's scalars read on the device from the
+ * schedule, which they do not move on. Errors: as their plain forms (without
+ * the hyperparameter checks); ZERO_EINVAL for a NULL schedule or one that
+ * lives on another device than the current one (or, for the table, than the
+ * table). */
 
 /* Reduce and update in one pass. [ZF] "Execution Flow for ZeRO-1", steps 2-3:
  * the rank receives the averaged gradient of its slice and updates its master
@@ -394,6 +401,12 @@ zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t rank,
                                    int64_t step, double lr, double beta1, double beta2, double eps,
                                    double weight_decay, const float* clip_scale,
                                    hipStream_t stream);
+zero_status zero_reduce_adamw_step_scheduled(const zero_plan* plan, int32_t rank,
+                                             const uint16_t* const* replicas, int32_t n_replicas,
+                                             int64_t begin, int64_t count, float* master,
+                                             float* exp_avg, float* exp_avg_sq, uint16_t* param_out,
+                                             uint16_t* shard_grad, const zero_adamw_schedule* schedule,
+                                             const float* clip_scale, hipStream_t stream);
 
 /* Multi-tensor form. [ZF] "FSDP-2: Per-Parameter Sharding via DTensor
  * (fully_shard)": each parameter keeps its own local shard, so the rank's
@@ -452,6 +465,9 @@ int64_t zero_mt_table_blocks(const zero_mt_table* table);
 zero_status zero_mt_table_adamw_step(const zero_mt_table* table, int64_t step, double lr,
                                      double beta1, double beta2, double eps, double weight_decay,
                                      const float* clip_scale, hipStream_t stream);
+zero_status zero_mt_table_adamw_step_scheduled(const zero_mt_table* table,
+                                               const zero_adamw_schedule* schedule,
+                                               const float* clip_scale, hipStream_t stream);
 
 /* ------------------------------------------------------------------ gather
  *

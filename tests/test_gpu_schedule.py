@@ -204,3 +204,118 @@ def test_captured_rank_step_with_the_step_on_the_device(zm):
         for i, (a, b) in enumerate(zip(rs.tensors, want["tensors"])):
             assert_bf16_close(host_u16(a), b, f"iteration {it} tensor {i}")
     assert applied == 4
+
+
+def test_scheduled_table_and_one_pass_match_their_plain_forms(zm):
+    """The multi-tensor table step and the one-pass reduce and update, scheduled
+    (one advance per step) against their plain forms with the host's step
+    number and against the oracle, bit for bit; the table's third step carries
+    a NaN coefficient and is neither applied nor counted."""
+    hp = HP
+    # multi-tensor table over three tensors
+    lens = [5000, 37, 20_011]
+    ins = [_inputs(n, 20 + i) for i, n in enumerate(lens)]
+    A = [[to_dev_f32(x) for x in st] for st in ins]
+    B = [[to_dev_f32(x) for x in st] for st in ins]
+    gs = [torch.zeros(n, dtype=torch.int16, device=dev()) for n in lens]
+    a_out = [torch.zeros(n, dtype=torch.int16, device=dev()) for n in lens]
+    b_out = [torch.zeros(n, dtype=torch.int16, device=dev()) for n in lens]
+    ta = zm.MultiTensorTable([a[0] for a in A], [a[1] for a in A], [a[2] for a in A], gs, a_out)
+    tb = zm.MultiTensorTable([b[0] for b in B], [b[1] for b in B], [b[2] for b in B], gs, b_out)
+    sched = zm.AdamWSchedule(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+    clip = torch.ones(1, dtype=torch.float32, device=dev())
+    want = [list(st) for st in ins]
+    bits = [np.zeros(n, np.uint16) for n in lens]
+    t = 0
+    for it, coef in enumerate([1.0, 0.5, float("nan"), 0.75]):
+        host_g = [_grad(n, 30 + i, it) for i, n in enumerate(lens)]
+        for d, h in zip(gs, host_g):
+            d.copy_(to_dev_u16(h))
+        clip.fill_(coef)
+        ta.step_scheduled(sched, clip_scale=clip)
+        sched.advance(clip_scale=clip)
+        if math.isfinite(coef):
+            t += 1
+            tb.step(t, clip_scale=clip, **hp)
+            for i in range(len(lens)):
+                p, m, v, b = oracle.adamw_step(*want[i], host_g[i], t, clip=coef, **hp)
+                want[i], bits[i] = [p, m, v], b
+        torch.cuda.synchronize()
+        assert sched.applied() == t
+        for i in range(len(lens)):
+            _check(*A[i], a_out[i], *want[i], bits[i], f"table iteration {it} tensor {i}")
+            _check(*B[i], b_out[i], *want[i], bits[i], f"plain table iteration {it} tensor {i}")
+    # one-pass reduce and update: rank 1 of a 2-rank plan, three replicas
+    numels = [30_000, 7, 12_345]
+    plan = zm.zero_partition_plan(numels, 2, 128)
+    ref = oracle.partition_plan(numels, 2, 128)
+    P, S, phi = ref.padded_numel, ref.shard_numel, ref.numel
+    master = synth.normal_f32(S, 40, synth.KIND_MASTER, 0, 0, S, phi, 0.02)
+    fa = [to_dev_f32(master), torch.zeros(S, device=dev()), torch.zeros(S, device=dev())]
+    fb = [to_dev_f32(master), torch.zeros(S, device=dev()), torch.zeros(S, device=dev())]
+    pa = torch.zeros(S, dtype=torch.int16, device=dev())
+    pb = torch.zeros(S, dtype=torch.int16, device=dev())
+    sched2 = zm.AdamWSchedule(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+    p, m, v = master.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    for t in (1, 2, 3):
+        full = [synth.normal_bf16(P, 41, synth.KIND_REPLICA, t, k, 0, phi, 0.05) for k in range(3)]
+        reps = [to_dev_u16(x) for x in full]
+        zm.zero_reduce_adamw_step_scheduled(plan, 1, reps, 0, P, *fa, pa, sched2)
+        sched2.advance()
+        zm.zero_reduce_adamw_step(plan, 1, reps, 0, P, *fb, pb, t, **hp)
+        g = np.zeros(S, np.uint16)
+        oracle.reduce_shard(ref, 1, full, 0, g)
+        p, m, v, bits1 = oracle.adamw_step(p, m, v, g, t, **hp)
+        torch.cuda.synchronize()
+        _check(*fa, pa, p, m, v, bits1, f"one-pass scheduled step {t}")
+        _check(*fb, pb, p, m, v, bits1, f"one-pass plain step {t}")
+    assert sched2.applied() == 3
+
+
+@pytest.mark.parametrize("mode", ["per-parameter", "one-pass"])
+def test_rank_step_device_step_equals_the_host_counted_step(zm, mode):
+    """RankStep(device_step=True) against RankStep with the step counted on the
+    host, on the same inputs, three steps, bit for bit: FSDP-2's per-parameter
+    state (clipped, through the multi-tensor table), or the one-pass reduce and
+    update over three bucket windows (no clipping)."""
+    from zero_partitioned_mixed_partition_amd.step import Hyper, RankStep, rank_step_plan_windows
+    numels = [1000 * 16, 37 * 16, 4096, 3 * 16, 777 * 16]
+    dim0 = [1000, 37, 4096, 3, 777]
+    n_ranks, rank, R = 4, 2, 3
+    if mode == "per-parameter":
+        plan = zm.zero_partition_plan_shard0(numels, dim0, n_ranks, 128)
+        kw, max_norm, bucket = dict(per_param=True), 1.0, 0
+    else:
+        plan = zm.zero_partition_plan(numels, n_ranks, 128)
+        kw, max_norm, bucket = dict(), 0.0, 7000
+    P, S, phi = plan.padded_numel, plan.shard_numel, plan.numel
+    wins = rank_step_plan_windows(plan, rank, bucket)
+    steps = [RankStep(plan, rank, len(wins), Hyper(), max_norm, dev(), gather=True, device_step=d, **kw)
+             for d in (True, False)]
+    master = synth.normal_f32(S, 50, synth.KIND_MASTER, 0, 0, rank * S, phi, 0.02)
+    for rs in steps:
+        if mode == "per-parameter":
+            for tt, (_, _, soff, ln) in zip(rs.master_tensors, rs.segments):
+                tt.copy_(torch.from_numpy(master[soff:soff + ln]))
+        else:
+            rs.master.copy_(torch.from_numpy(master))
+        rs.set_remote_partials([0.3, 0.1, 0.0, 0.2])
+    for t in (1, 2, 3):
+        full = [synth.normal_bf16(P, 51, synth.KIND_REPLICA, t, k, 0, phi, 0.05) for k in range(R)]
+        dfull = [to_dev_u16(x) for x in full]
+        for rs in steps:
+            rs.step([(b, c, [x[b:b + c] for x in dfull]) for b, c in wins])
+        torch.cuda.synchronize()
+        a, b = steps
+        if mode == "per-parameter":
+            pairs = list(zip(a.master_tensors + a.exp_avg_tensors + a.exp_avg_sq_tensors,
+                             b.master_tensors + b.exp_avg_tensors + b.exp_avg_sq_tensors))
+        else:
+            pairs = [(a.master, b.master), (a.exp_avg, b.exp_avg), (a.exp_avg_sq, b.exp_avg_sq)]
+        for x, y in pairs:
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), f"{mode} step {t}: fp32 state"
+        assert torch.equal(a.param_shards[rank], b.param_shards[rank]), f"{mode} step {t}: shard"
+        for x, y in zip(a.tensors, b.tensors):
+            assert torch.equal(x, y), f"{mode} step {t}: tensors"
+        assert a.steps_applied() == b.steps_applied() == t
+    assert ("reduce_update", 0) in steps[0]._calls if mode == "one-pass" else "adamw" in steps[0]._calls

@@ -91,3 +91,9 @@ def test_schedule_arguments_are_checked_before_touching_the_gpu(zm):
     assert lib._step_scalars(0, 1e-3, 0.9, 0.999, 1e-8, 0.0, f) == E     # step < 1
     assert lib._step_scalars(1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == E
     assert lib._adamw_sched(None, None, None, None, None, 1, None, None, None) == E   # NULL schedule
+    assert lib._mt_step_sched(None, None, None, None) == E                           # NULL table
+    plan = zm.zero_partition_plan([1000], 2, 1)
+    reps = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    state = [ctypes.c_void_p(0x100000 * (k + 1)) for k in range(4)]
+    assert lib._reduce_adamw_sched(plan.handle, 1, reps, 2, 0, 1000, *state, None, None, None, None) == E
+    assert "NULL schedule" in zm.zero_last_error()

@@ -122,18 +122,18 @@ def test_rank_step_chooses_the_one_pass_update_only_where_it_applies(step):
     assert [t.numel() for t in rs.master_tensors] == [ln for (_, _, _, ln) in plan.segments(2)]
     with pytest.raises(ValueError, match="separate layouts"):
         step.RankStep(plan, 2, 1, step.Hyper(), 1.0, torch.device("cpu"), offload=True, per_param=True)
-    # the device-counted step takes the flat device state, and keeps the two calls (the
-    # one-pass kernel takes the step number from the host)
-    for kw in (dict(per_param=True), dict(offload=True)):
-        with pytest.raises(ValueError, match="flat device state"):
-            step.RankStep(plan, 2, 1, step.Hyper(), 1.0, torch.device("cpu"), device_step=True, **kw)
-    rs = step.RankStep(plan, 2, 3, step.Hyper(), 0.0, torch.device("cpu"), gather=False)
-    rs.device_step = True           # (the schedule itself needs a GPU)
-    calls = []
-    rs.reduce_update = lambda w, s=None: calls.append("one-pass")
-    rs.reduce = lambda w, s=None: calls.append("reduce")
-    rs.clip = lambda s=None: calls.append("clip")
-    rs.adamw = lambda s=None: calls.append("adamw")
-    rs.gather = lambda s=None: calls.append("gather")
-    rs.step(disjoint)
-    assert calls == two_calls
+    # the device-counted step takes device state (not ZeRO-Offload's), and chooses its calls
+    # as the host-counted step does
+    with pytest.raises(ValueError, match="not ZeRO-Offload"):
+        step.RankStep(plan, 2, 1, step.Hyper(), 1.0, torch.device("cpu"), device_step=True, offload=True)
+    for max_norm, want in ((0.0, ["one-pass", "gather"]), (1.0, two_calls)):
+        rs = step.RankStep(plan, 2, 3, step.Hyper(), max_norm, torch.device("cpu"), gather=False)
+        rs.device_step = True           # (the schedule itself needs a GPU)
+        calls = []
+        rs.reduce_update = lambda w, s=None: calls.append("one-pass")
+        rs.reduce = lambda w, s=None: calls.append("reduce")
+        rs.clip = lambda s=None: calls.append("clip")
+        rs.adamw = lambda s=None: calls.append("adamw")
+        rs.gather = lambda s=None: calls.append("gather")
+        rs.step(disjoint)
+        assert calls == want

@@ -32,6 +32,7 @@ RankStep(..., offload=True) keeps the fp32 state in host memory (ZeRO-Offload).
 from ._binding import (LIB_PATH, ZERO_MAX_REPLICAS, AdamWSchedule, CopyTable,  # noqa: F401
                        MultiTensorTable, Plan, ReduceTable,
                        zero_adamw_step_scalars, zero_shard_adamw_step_scheduled,
+                       zero_reduce_adamw_step_scheduled,
                        ZeroError, reduce_workspace, zero_reduce_workspace_bytes,
                        sqnorm_workspace, zero_clip_scale, zero_flatten_params, zero_gather_params,
                        zero_grad_reduce_shard, zero_grad_reduce_shard_noalloc,

@@ -109,6 +109,10 @@ _sched_applied = _fn("zero_adamw_schedule_applied", c_i32, [c_vp, ctypes.POINTER
 _sched_advance = _fn("zero_adamw_schedule_advance", c_i32, [c_vp, c_vp, c_vp])
 _adamw_sched = _fn("zero_shard_adamw_step_scheduled", c_i32,
                    [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp])
+_mt_step_sched = _fn("zero_mt_table_adamw_step_scheduled", c_i32, [c_vp, c_vp, c_vp, c_vp])
+_reduce_adamw_sched = _fn("zero_reduce_adamw_step_scheduled", c_i32,
+                          [c_vp, c_i32, ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
+                           c_vp, c_vp, c_vp, c_vp])
 _step_scalars = _fn("zero_adamw_step_scalars", c_i32,
                     [c_i64, c_dbl, c_dbl, c_dbl, c_dbl, c_dbl, ctypes.POINTER(ctypes.c_float)])
 _rt_blocks = _fn("zero_reduce_table_blocks", c_i64, [c_vp])
@@ -411,6 +415,38 @@ def zero_reduce_adamw_step(plan: Plan, rank: int, replicas: Sequence, begin: int
                               stream)(step)
 
 
+def prepare_reduce_adamw_step_scheduled(plan: Plan, rank: int, replicas: Sequence, begin: int,
+                                        count: int, master, exp_avg, exp_avg_sq, param_out,
+                                        schedule: "AdamWSchedule", clip_scale=None, shard_grad=None,
+                                        stream=None) -> "Prepared":
+    """zero_reduce_adamw_step_scheduled with its arguments marshalled once."""
+    S = plan.shard_numel
+    for r in replicas:
+        _need(r, count, "a replica")
+    for t, what in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"),
+                    (param_out, "param_out")):
+        _need(t, S, what)
+    _need(shard_grad, S, "shard_grad")
+    _need(clip_scale, 1, "clip_scale")
+    ptrs = (c_vp * max(len(replicas), 1))(*[_ptr(r, 2, "replica") for r in replicas])
+    p = Prepared(_reduce_adamw_sched, [plan.handle, rank, ptrs, len(replicas), begin, count,
+                                       _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                                       _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"),
+                                       _ptr(shard_grad, 2, "shard_grad"), schedule.handle,
+                                       _ptr(clip_scale, 4, "clip_scale"), _stream(stream, master)],
+                 "zero_reduce_adamw_step_scheduled")
+    p._keep = (ptrs, replicas, master, exp_avg, exp_avg_sq, param_out, shard_grad, schedule, clip_scale)
+    return p
+
+
+def zero_reduce_adamw_step_scheduled(plan: Plan, rank: int, replicas: Sequence, begin: int, count: int,
+                                     master, exp_avg, exp_avg_sq, param_out, schedule: "AdamWSchedule",
+                                     clip_scale=None, shard_grad=None, stream=None) -> None:
+    """zero_reduce_adamw_step with the step's scalars read on the device from `schedule`."""
+    prepare_reduce_adamw_step_scheduled(plan, rank, replicas, begin, count, master, exp_avg, exp_avg_sq,
+                                        param_out, schedule, clip_scale, shard_grad, stream)()
+
+
 def zero_gather_params(plan: Plan, shards: Sequence, tensors: Sequence, stream=None) -> None:
     _check_gather_args(plan, shards, tensors)
     sp = (c_vp * max(len(shards), 1))(*[_ptr(s, 2, "shard") for s in shards])   # None skips a rank
@@ -523,6 +559,19 @@ class MultiTensorTable:
             _stream(None, self._keep[0][0]) if self._keep[0] else 0)
         _check(_mt_step(self._h, step, lr, beta1, beta2, eps, weight_decay,
                         _ptr(clip_scale, 4, "clip_scale"), st), "zero_mt_table_adamw_step")
+
+    def prepare_step_scheduled(self, schedule: "AdamWSchedule", clip_scale=None, stream=None) -> "Prepared":
+        """zero_mt_table_adamw_step_scheduled with its arguments marshalled once."""
+        _need(clip_scale, 1, "clip_scale")
+        st = stream if stream is not None else (
+            _stream(None, self._keep[0][0]) if self._keep[0] else 0)
+        p = Prepared(_mt_step_sched, [self._h, schedule.handle, _ptr(clip_scale, 4, "clip_scale"), st],
+                     "zero_mt_table_adamw_step_scheduled")
+        p._keep = (self, schedule, clip_scale)
+        return p
+
+    def step_scheduled(self, schedule: "AdamWSchedule", clip_scale=None, stream=None) -> None:
+        self.prepare_step_scheduled(schedule, clip_scale, stream)()
 
 
 class CopyTable:

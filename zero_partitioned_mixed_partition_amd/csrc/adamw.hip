@@ -371,6 +371,24 @@ __global__ __launch_bounds__(kThreads) void adamw_table_kernel(const MtDesc* __r
               clip_scale);
 }
 
+// The table form with the step's scalars read from a schedule's state (used
+// after the element loads are issued, as the clip coefficient is).
+__global__ __launch_bounds__(kThreads) void adamw_table_sched_kernel(const MtDesc* __restrict__ table,
+                                                                     const uint32_t* __restrict__ index,
+                                                                     int64_t blk0, int64_t per,
+                                                                     const AdamState* __restrict__ state,
+                                                                     const float* __restrict__ clip_scale) {
+    const int64_t blk = blk0 + static_cast<int64_t>(blockIdx.x);
+#if ZERO_MT_DESC_PER_WG
+    (void)index;
+    const MtDesc d = table[zero::dev::xcd_major_entry(blk0, per)];
+#else
+    const MtDesc d = table[index[zero::dev::xcd_major_entry(blk0, per)]];
+#endif
+    mt_update(d.p, d.m, d.v, d.g, d.o, d.n, (blk - d.first_block) * kMtChunk + threadIdx.x, state->next,
+              clip_scale);
+}
+
 // Reduce and update in one pass, for a step whose clip coefficient is known
 // before the update (no clipping, or a coefficient the caller has): lane e
 // averages element e of the R replicas exactly as the reduce does (an fp32 sum
@@ -391,15 +409,11 @@ struct FusedReplicas {
 #endif
 constexpr int kFusedBatch = ZERO_FUSED_BATCH;
 
-__global__ __launch_bounds__(kThreads) void reduce_adamw_kernel(FusedReplicas reps, int n_rep,
-                                                                int64_t src_off,
-                                                                float* __restrict__ master,
-                                                                float* __restrict__ m,
-                                                                float* __restrict__ v,
-                                                                uint16_t* __restrict__ param,
-                                                                uint16_t* __restrict__ grad_out,
-                                                                int64_t n, AdamScalars c,
-                                                                const float* __restrict__ clip_scale) {
+__device__ __forceinline__ void reduce_adamw_body(const FusedReplicas& reps, int n_rep, int64_t src_off,
+                                                  float* __restrict__ master, float* __restrict__ m,
+                                                  float* __restrict__ v, uint16_t* __restrict__ param,
+                                                  uint16_t* __restrict__ grad_out, int64_t n,
+                                                  const AdamScalars& c, const float* __restrict__ clip_scale) {
     const int64_t blk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
     const int64_t i = blk * kThreads + threadIdx.x;
     if (i >= n) return;
@@ -423,6 +437,32 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_kernel(FusedReplicas re
     zero::dev::st_stream(m + i, mm);
     zero::dev::st_stream(v + i, vv);
     zero::dev::st_stream(param + i, static_cast<uint16_t>(zero::dev::f32_to_bf16(p)));
+}
+
+__global__ __launch_bounds__(kThreads) void reduce_adamw_kernel(FusedReplicas reps, int n_rep,
+                                                                int64_t src_off,
+                                                                float* __restrict__ master,
+                                                                float* __restrict__ m,
+                                                                float* __restrict__ v,
+                                                                uint16_t* __restrict__ param,
+                                                                uint16_t* __restrict__ grad_out,
+                                                                int64_t n, AdamScalars c,
+                                                                const float* __restrict__ clip_scale) {
+    reduce_adamw_body(reps, n_rep, src_off, master, m, v, param, grad_out, n, c, clip_scale);
+}
+
+// The one-pass form with the step's scalars read from a schedule's state.
+__global__ __launch_bounds__(kThreads) void reduce_adamw_sched_kernel(FusedReplicas reps, int n_rep,
+                                                                      int64_t src_off,
+                                                                      float* __restrict__ master,
+                                                                      float* __restrict__ m,
+                                                                      float* __restrict__ v,
+                                                                      uint16_t* __restrict__ param,
+                                                                      uint16_t* __restrict__ grad_out,
+                                                                      int64_t n,
+                                                                      const AdamState* __restrict__ state,
+                                                                      const float* __restrict__ clip_scale) {
+    reduce_adamw_body(reps, n_rep, src_off, master, m, v, param, grad_out, n, state->next, clip_scale);
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -873,6 +913,97 @@ extern "C" zero_status zero_mt_table_adamw_step(const zero_mt_table* table, int6
     return ZERO_OK;
 }
 
+extern "C" zero_status zero_mt_table_adamw_step_scheduled(const zero_mt_table* table,
+                                                          const zero_adamw_schedule* schedule,
+                                                          const float* clip_scale, hipStream_t stream) {
+    using zero::fail;
+    static const char* const who = "zero_mt_table_adamw_step_scheduled";
+    zero::clear_error();
+    if (!table || !schedule) return fail(ZERO_EINVAL, "zero_mt_table_adamw_step_scheduled: NULL table or schedule");
+    zero_status st = check_schedule_device(schedule, who);
+    if (st != ZERO_OK) return st;
+    if (table->blocks == 0) return ZERO_OK;
+    if (table->device != schedule->device)
+        return fail(ZERO_EINVAL, "zero_mt_table_adamw_step_scheduled: the table lives on device " +
+                                     std::to_string(table->device) + ", the schedule on device " +
+                                     std::to_string(schedule->device));
+    constexpr int64_t kMaxBlocks = zero::kTableLaunchBlocks;
+    for (int64_t b0 = 0; b0 < table->blocks; b0 += kMaxBlocks) {
+        const int64_t nb = table->blocks - b0 < kMaxBlocks ? table->blocks - b0 : kMaxBlocks;
+        const int64_t per = (nb + 7) / 8;
+        hipLaunchKernelGGL(adamw_table_sched_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0,
+                           stream, table->table, table->index, b0, per, schedule->state, clip_scale);
+        st = zero::check_hip(hipGetLastError(), "zero_mt_table_adamw_step_scheduled launch");
+        if (st != ZERO_OK) return st;
+    }
+    return ZERO_OK;
+}
+
+namespace {
+
+// The one-pass reduce and update's window checks.
+zero_status fused_check_window(const zero_plan* plan, int32_t rank, const uint16_t* const* replicas,
+                               int32_t n_replicas, int64_t begin, int64_t count, const char* who) {
+    using zero::fail;
+    const std::string w(who);
+    if (plan == nullptr || replicas == nullptr) return fail(ZERO_EINVAL, w + ": NULL plan or replicas");
+    if (rank < 0 || rank >= plan->n_ranks) return fail(ZERO_EINVAL, w + ": rank out of range");
+    if (n_replicas < 1 || n_replicas > ZERO_MAX_REPLICAS)
+        return fail(ZERO_EINVAL, w + ": n_replicas must be 1.." + std::to_string(ZERO_MAX_REPLICAS));
+    if (begin < 0 || count < 0 || begin > plan->padded || count > plan->padded - begin)
+        return fail(ZERO_EINVAL, w + ": window outside [0, P)");
+    return ZERO_OK;
+}
+
+// Its launch: the window's part of the rank's shard, the replica table, the
+// grid (rows of workgroups past 2^32 work-items). `empty` when the window
+// misses the shard.
+struct FusedCall {
+    FusedReplicas table{};
+    int64_t n = 0, src_off = 0, at = 0;
+    dim3 grid;
+    bool empty = true;
+};
+
+zero_status fused_prepare(const zero_plan* plan, int32_t rank, const uint16_t* const* replicas,
+                          int32_t n_replicas, int64_t begin, int64_t count, float* master, float* exp_avg,
+                          float* exp_avg_sq, uint16_t* param_out, uint16_t* shard_grad, const char* who,
+                          FusedCall* call) {
+    using zero::fail;
+    const std::string w(who);
+    const int64_t shard_lo = static_cast<int64_t>(rank) * plan->shard;
+    const int64_t lo = begin > shard_lo ? begin : shard_lo;
+    const int64_t end = begin + count, shard_hi = shard_lo + plan->shard;
+    const int64_t hi = end < shard_hi ? end : shard_hi;
+    call->empty = lo >= hi;
+    if (call->empty) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !param_out) return fail(ZERO_EINVAL, w + ": NULL state array");
+    for (int32_t k = 0; k < n_replicas; ++k) {
+        if (replicas[k] == nullptr) return fail(ZERO_EINVAL, w + ": NULL replica");
+        call->table.p[k] = replicas[k];
+    }
+    const int64_t n = hi - lo, src_off = lo - begin, at = lo - shard_lo;
+    const size_t fbytes = static_cast<size_t>(n) * 4, hbytes = static_cast<size_t>(n) * 2;
+    const zero::Span wr[] = {{master + at, fbytes, "master"}, {exp_avg + at, fbytes, "exp_avg"},
+                             {exp_avg_sq + at, fbytes, "exp_avg_sq"}, {param_out + at, hbytes, "param_out"},
+                             {shard_grad != nullptr ? shard_grad + at : nullptr, shard_grad ? hbytes : 0,
+                              "shard_grad"}};
+    zero::Span rd[ZERO_MAX_REPLICAS];
+    for (int32_t k = 0; k < n_replicas; ++k) rd[k] = {replicas[k] + src_off, hbytes, "replica", k};
+    const std::string clash = zero::first_overlap(wr, 5, rd, n_replicas);
+    if (!clash.empty()) return fail(ZERO_EINVAL, w + ": " + clash);
+    constexpr int64_t kMaxRow = (int64_t(1) << 32) / kThreads - 1;
+    const int64_t blocks = blocks_for(n);
+    const int64_t rows = (blocks + kMaxRow - 1) / kMaxRow;
+    call->grid = dim3(static_cast<unsigned>((blocks + rows - 1) / rows), static_cast<unsigned>(rows));
+    call->n = n;
+    call->src_off = src_off;
+    call->at = at;
+    return ZERO_OK;
+}
+
+}  // namespace
+
 extern "C" zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t rank,
                                               const uint16_t* const* replicas, int32_t n_replicas,
                                               int64_t begin, int64_t count, float* master,
@@ -881,56 +1012,47 @@ extern "C" zero_status zero_reduce_adamw_step(const zero_plan* plan, int32_t ran
                                               double beta1, double beta2, double eps,
                                               double weight_decay, const float* clip_scale,
                                               hipStream_t stream) {
-    using zero::fail;
     static const char* const who = "zero_reduce_adamw_step";
     zero::clear_error();
-    if (plan == nullptr || replicas == nullptr)
-        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: NULL plan or replicas");
-    if (rank < 0 || rank >= plan->n_ranks)
-        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: rank out of range");
-    if (n_replicas < 1 || n_replicas > ZERO_MAX_REPLICAS)
-        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: n_replicas must be 1.." +
-                                     std::to_string(ZERO_MAX_REPLICAS));
-    if (begin < 0 || count < 0 || begin > plan->padded || count > plan->padded - begin)
-        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: window outside [0, P)");
-    zero_status st = zero::adam::check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
+    zero_status st = fused_check_window(plan, rank, replicas, n_replicas, begin, count, who);
     if (st != ZERO_OK) return st;
-    const int64_t shard_lo = static_cast<int64_t>(rank) * plan->shard;
-    const int64_t lo = begin > shard_lo ? begin : shard_lo;
-    const int64_t end = begin + count, shard_hi = shard_lo + plan->shard;
-    const int64_t hi = end < shard_hi ? end : shard_hi;
-    if (lo >= hi) return ZERO_OK;
-    if (!master || !exp_avg || !exp_avg_sq || !param_out)
-        return fail(ZERO_EINVAL, "zero_reduce_adamw_step: NULL state array");
-    FusedReplicas table{};
-    for (int32_t k = 0; k < n_replicas; ++k) {
-        if (replicas[k] == nullptr) return fail(ZERO_EINVAL, "zero_reduce_adamw_step: NULL replica");
-        table.p[k] = replicas[k];
-    }
-    const int64_t n = hi - lo, src_off = lo - begin, at = lo - shard_lo;
-    const size_t fbytes = static_cast<size_t>(n) * 4, hbytes = static_cast<size_t>(n) * 2;
-    std::string clash;
-    try {
-        const zero::Span wr[] = {{master + at, fbytes, "master"}, {exp_avg + at, fbytes, "exp_avg"},
-                                 {exp_avg_sq + at, fbytes, "exp_avg_sq"}, {param_out + at, hbytes, "param_out"},
-                                 {shard_grad != nullptr ? shard_grad + at : nullptr, shard_grad ? hbytes : 0,
-                                  "shard_grad"}};
-        std::vector<zero::Span> rd(static_cast<size_t>(n_replicas));
-        for (int32_t k = 0; k < n_replicas; ++k) rd[static_cast<size_t>(k)] = {replicas[k] + src_off, hbytes, "replica", k};
-        clash = zero::first_overlap(wr, 5, rd.data(), n_replicas);
-    } catch (const std::bad_alloc&) {
-        return fail(ZERO_ENOMEM, "zero_reduce_adamw_step: host allocation failed");
-    }
-    if (!clash.empty()) return fail(ZERO_EINVAL, "zero_reduce_adamw_step: " + clash);
+    st = zero::adam::check_hyper(step, lr, beta1, beta2, eps, weight_decay, who);
+    if (st != ZERO_OK) return st;
+    FusedCall call;
+    st = fused_prepare(plan, rank, replicas, n_replicas, begin, count, master, exp_avg, exp_avg_sq, param_out,
+                       shard_grad, who, &call);
+    if (st != ZERO_OK || call.empty) return st;
     AdamScalars c;
     st = zero::adam::step_scalars(step, lr, beta1, beta2, weight_decay, eps, &c, who);
     if (st != ZERO_OK) return st;
-    constexpr int64_t kMaxRow = (int64_t(1) << 32) / kThreads - 1;
-    const int64_t blocks = blocks_for(n);
-    const int64_t rows = (blocks + kMaxRow - 1) / kMaxRow;
-    const dim3 grid(static_cast<unsigned>((blocks + rows - 1) / rows), static_cast<unsigned>(rows));
-    hipLaunchKernelGGL(reduce_adamw_kernel, grid, dim3(kThreads), 0, stream, table, n_replicas,
-                       src_off, master + at, exp_avg + at, exp_avg_sq + at, param_out + at,
-                       shard_grad != nullptr ? shard_grad + at : nullptr, n, c, clip_scale);
+    const int64_t at = call.at;
+    hipLaunchKernelGGL(reduce_adamw_kernel, call.grid, dim3(kThreads), 0, stream, call.table, n_replicas,
+                       call.src_off, master + at, exp_avg + at, exp_avg_sq + at, param_out + at,
+                       shard_grad != nullptr ? shard_grad + at : nullptr, call.n, c, clip_scale);
     return zero::check_hip(hipGetLastError(), "zero_reduce_adamw_step launch");
+}
+
+extern "C" zero_status zero_reduce_adamw_step_scheduled(const zero_plan* plan, int32_t rank,
+                                                        const uint16_t* const* replicas, int32_t n_replicas,
+                                                        int64_t begin, int64_t count, float* master,
+                                                        float* exp_avg, float* exp_avg_sq,
+                                                        uint16_t* param_out, uint16_t* shard_grad,
+                                                        const zero_adamw_schedule* schedule,
+                                                        const float* clip_scale, hipStream_t stream) {
+    static const char* const who = "zero_reduce_adamw_step_scheduled";
+    zero::clear_error();
+    if (schedule == nullptr) return zero::fail(ZERO_EINVAL, "zero_reduce_adamw_step_scheduled: NULL schedule");
+    zero_status st = fused_check_window(plan, rank, replicas, n_replicas, begin, count, who);
+    if (st != ZERO_OK) return st;
+    st = check_schedule_device(schedule, who);
+    if (st != ZERO_OK) return st;
+    FusedCall call;
+    st = fused_prepare(plan, rank, replicas, n_replicas, begin, count, master, exp_avg, exp_avg_sq, param_out,
+                       shard_grad, who, &call);
+    if (st != ZERO_OK || call.empty) return st;
+    const int64_t at = call.at;
+    hipLaunchKernelGGL(reduce_adamw_sched_kernel, call.grid, dim3(kThreads), 0, stream, call.table, n_replicas,
+                       call.src_off, master + at, exp_avg + at, exp_avg_sq + at, param_out + at,
+                       shard_grad != nullptr ? shard_grad + at : nullptr, call.n, schedule->state, clip_scale);
+    return zero::check_hip(hipGetLastError(), "zero_reduce_adamw_step_scheduled launch");
 }

@@ -78,9 +78,9 @@ class RankStep:
                  memory and an advance call after it counts the step, only when
                  the clip coefficient is finite. A skipped step is then not
                  counted, and the whole step can be captured in a HIP graph and
-                 replayed for successive steps. Flat device state only (not
-                 with per_param or offload); the one-pass update, which takes
-                 the step from the host, is not used.
+                 replayed for successive steps. Flat or per-parameter device
+                 state, and the one-pass update; not with offload (the host
+                 update computes its own scalars).
     """
 
     # Measured on MI355X, no clip: with 8 replicas per window the one pass takes
@@ -95,8 +95,8 @@ class RankStep:
                  per_param: bool = False, device_step: bool = False):
         if per_param and offload:
             raise ValueError("per-parameter state and ZeRO-Offload are separate layouts")
-        if device_step and (per_param or offload):
-            raise ValueError("the device-counted step takes the flat device state")
+        if device_step and offload:
+            raise ValueError("the device-counted step takes device state, not ZeRO-Offload's")
         self.plan, self.rank, self.hyper, self.max_norm = plan, rank, hyper, max_norm
         self.device = device
         self.offload, self.host_threads = offload, host_threads
@@ -208,18 +208,18 @@ class RankStep:
         self.t += 1
         clip = self.scale if self.max_norm > 0 else None
         if self.device_step:    # the step's scalars on the device, then the count moves on
-            self._prepared("adamw", stream, lambda st: zb.prepare_shard_adamw_step_scheduled(
-                self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
-                self.schedule, clip_scale=clip, stream=st))()
+            if self.per_param:
+                self._prepared("adamw", stream, lambda st: self._mt_table().prepare_step_scheduled(
+                    self.schedule, clip_scale=clip, stream=st))()
+            else:
+                self._prepared("adamw", stream, lambda st: zb.prepare_shard_adamw_step_scheduled(
+                    self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
+                    self.schedule, clip_scale=clip, stream=st))()
             self._prepared("advance", stream, lambda st: self.schedule.prepare_advance(clip, st))()
             return
         if self.per_param:
-            own = self.param_shards[self.rank]
-            sl = [slice(soff, soff + ln) for (_, _, soff, ln) in self.segments]
-            self._prepared("adamw", stream, lambda st: zb.MultiTensorTable(
-                self.master_tensors, self.exp_avg_tensors, self.exp_avg_sq_tensors,
-                [self.grad[x] for x in sl], [own[x] for x in sl]).prepare_step(
-                    clip_scale=clip, stream=st, **self.hyper.as_kwargs()))(self.t)
+            self._prepared("adamw", stream, lambda st: self._mt_table().prepare_step(
+                clip_scale=clip, stream=st, **self.hyper.as_kwargs()))(self.t)
             return
         if self.offload:        # returns once the host update is done; `stream` orders the copies
             self._prepared("adamw", stream, lambda st: zb.prepare_offload_adamw_step(
@@ -230,6 +230,14 @@ class RankStep:
         self._prepared("adamw", stream, lambda st: zb.prepare_shard_adamw_step(
             self.master, self.exp_avg, self.exp_avg_sq, self.grad, self.param_shards[self.rank],
             clip_scale=clip, stream=st, **self.hyper.as_kwargs()))(self.t)
+
+    def _mt_table(self) -> zb.MultiTensorTable:
+        """The per-parameter state's device table (the gradient and the parameter
+        shard cut at the segments)."""
+        own = self.param_shards[self.rank]
+        sl = [slice(soff, soff + ln) for (_, _, soff, ln) in self.segments]
+        return zb.MultiTensorTable(self.master_tensors, self.exp_avg_tensors, self.exp_avg_sq_tensors,
+                                   [self.grad[x] for x in sl], [own[x] for x in sl])
 
     def steps_applied(self) -> int:
         """Updates applied: the device count with device_step (a synchronous read),
@@ -245,19 +253,26 @@ class RankStep:
         averaged gradient is not stored and no norm partial is taken."""
         if len(windows) != self.n_windows:
             raise ValueError("window count differs from the one the step was built for")
-        if self.offload or self.per_param or self.max_norm > 0 or self.device_step:
+        if self.offload or self.per_param or self.max_norm > 0:
             raise ValueError("the one-pass update runs on the device, over flat state, without "
-                             "clipping, with the step from the host")
+                             "clipping")
         spans = sorted((b, b + c) for b, c, _ in windows if c > 0)
         if any(a[1] > b[0] for a, b in zip(spans, spans[1:])):
             raise ValueError("windows overlap: the one-pass update needs disjoint windows")
         self.t += 1
         for w, (begin, count, reps) in enumerate(windows):
             sig = (begin, count, tuple(r.data_ptr() for r in reps))
-            self._prepared(("reduce_update", w), stream, lambda st: zb.prepare_reduce_adamw_step(
-                self.plan, self.rank, reps, begin, count, self.master, self.exp_avg,
-                self.exp_avg_sq, self.param_shards[self.rank], clip_scale=None, stream=st,
-                **self.hyper.as_kwargs()), sig)(self.t)
+            if self.device_step:
+                self._prepared(("reduce_update", w), stream, lambda st: zb.prepare_reduce_adamw_step_scheduled(
+                    self.plan, self.rank, reps, begin, count, self.master, self.exp_avg,
+                    self.exp_avg_sq, self.param_shards[self.rank], self.schedule, stream=st), sig)()
+            else:
+                self._prepared(("reduce_update", w), stream, lambda st: zb.prepare_reduce_adamw_step(
+                    self.plan, self.rank, reps, begin, count, self.master, self.exp_avg,
+                    self.exp_avg_sq, self.param_shards[self.rank], clip_scale=None, stream=st,
+                    **self.hyper.as_kwargs()), sig)(self.t)
+        if self.device_step:    # every window updated: the step counts once
+            self._prepared("advance", stream, lambda st: self.schedule.prepare_advance(None, st))()
 
     def gather(self, stream=None):
         # The shards and tensors are this object's fixed buffers, so the gather
@@ -271,7 +286,7 @@ class RankStep:
         disjoint = all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
         narrow = all(len(reps) <= self.FUSE_MAX_REPLICAS for _, _, reps in windows)
         if (self.fuse and self.max_norm <= 0 and not self.offload and not self.per_param
-                and not self.device_step and disjoint and narrow):
+                and disjoint and narrow):
             self.reduce_update(windows, stream)
         else:
             self.reduce(windows, stream)
