@@ -31,6 +31,9 @@
  *                           fixed buffers (no flatten of each replica first)
  *   zero_offload_adamw_step ZeRO-Offload: the update on the host CPU, with the
  *                           gradient and parameter transfers overlapped
+ *   zero_adamw_schedule_*, zero_*_scheduled  AdamW with the step number counted
+ *                           on the device, so a step captured in a HIP graph
+ *                           replays successive steps
  *
  * Conventions, for every function below:
  *   - bf16 values travel as raw uint16_t bit patterns; fp32 as float.
