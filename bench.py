@@ -75,6 +75,10 @@ def parse_args(argv=None):
                     help="rough budget for the oracle's host timing (0 disables it)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only this many steps, untimed, for a profiler (no JSON)")
+    ap.add_argument("--device-step", action="store_true",
+                    help="count AdamW's step on the device (RankStep(device_step=True)): the "
+                         "scheduled update kernels, the AdamW phase including the one-lane "
+                         "advance; a comparison run, not the benchmark's line")
     ap.add_argument("--profile-extra", action="store_true",
                     help="with --profile-steps: first run each phase timed outside the step once "
                          "(the step's dispatches stay the run's last ones)")
@@ -117,7 +121,7 @@ class RankWorkload:
         "gpt2-small-fsdp2-pertensor": ("gpt2-small", 8, 7, 8, 0, True, "shard0"),
     }
 
-    def __init__(self, name: str, device):
+    def __init__(self, name: str, device, device_step: bool = False):
         import torch
 
         import synth
@@ -145,9 +149,12 @@ class RankWorkload:
         self.offload = name.endswith("-offload")
         self.n_threads = len(os.sched_getaffinity(0))
         self.per_tensor = name.endswith("-pertensor")
+        if device_step and self.offload:
+            raise SystemExit("bench.py: --device-step takes device state; not with the offload workload")
         self.rs = RankStep(self.plan, rank, len(spans), self.hyper, self.max_norm, device,
                            gather=gather, offload=self.offload, offload_chunk=OFFLOAD_CHUNK,
-                           host_threads=self.n_threads, per_param=self.per_tensor)
+                           host_threads=self.n_threads, per_param=self.per_tensor,
+                           device_step=device_step)
         rs = self.rs
         if self.offload:         # the fp32 master lives in host memory
             rs.master.copy_(torch.from_numpy(synth.normal_f32(S, self.seed, synth.KIND_MASTER, 0, 0,
@@ -552,9 +559,15 @@ def padding_mask(plan, rank: int):
     return mask
 
 
-def make_workload(name: str, device):
-    return (AllRanksWorkload(name, device) if name.startswith("gpt-1.3b")
-            else RankWorkload(name, device))
+def make_workload(name: str, device, device_step: bool = False):
+    if name.startswith("gpt-1.3b"):
+        if device_step:
+            raise SystemExit("bench.py: --device-step applies to the one-rank workloads")
+        return AllRanksWorkload(name, device)
+    wl = RankWorkload(name, device, device_step)
+    if device_step:     # the scheduled kernels; the traffic entries are the plain kernel's
+        wl.adamw_kernel = "adamw_table_sched_kernel" if wl.per_tensor else "adamw_sched_kernel"
+    return wl
 
 
 def run_step(wl) -> None:
@@ -966,7 +979,7 @@ def main(argv=None):
     if args.separate_arrays:
         step_module._staggered_arena = _separate_arrays
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
-    wl = make_workload(args.workload, device)
+    wl = make_workload(args.workload, device, args.device_step)
     if args.profile_steps:
         if args.calibrate_copy:
             src = torch.ones(1 << 28, dtype=torch.float32, device=device)
