@@ -32,6 +32,8 @@ def test_every_workload_has_default_steps_and_a_description_path():
     import bench
     assert set(bench.DEFAULT_STEPS) == set(bench.WORKLOAD_NAMES)
     assert bench.parse_args([]).workload == "llama3-70b"
+    assert bench.parse_args([]).device_step is False           # the benchmark's line: host step
+    assert bench.parse_args(["--device-step"]).device_step is True
     for name in bench.WORKLOAD_NAMES:
         steps, warmup = bench.DEFAULT_STEPS[name]
         assert steps >= 1 and 0 <= warmup <= steps
