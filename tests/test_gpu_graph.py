@@ -2,13 +2,15 @@
 
 The caller the no-allocation reduce is for: code under graph capture, which
 cannot allocate. The captured step is zero_grad_reduce_shard_noalloc (norm
-partials in the library's device array), zero_clip_scale and
-zero_shard_adamw_step; the device buffers are allocated before capture. The
-graph is replayed four times with the program's own eager work (a second,
-uncaptured reduce into another buffer, host synchronisations) between the
-replays, and after every replay the gradient, the fp32 state and the bf16
-parameters are compared bit for bit with an eager run of the same number of
-steps through the workspace entry points, and with the oracle.
+partials in the library's device array), zero_clip_scale, and AdamW with its
+step number counted on the device (zero_shard_adamw_step_scheduled and
+zero_adamw_schedule_advance), so replay k applies step k; the device buffers
+and the schedule are allocated before capture. The graph is replayed four
+times with the program's own eager work (a second, uncaptured reduce into
+another buffer, host synchronisations) between the replays, and after every
+replay the gradient, the fp32 state and the bf16 parameters are compared bit
+for bit with an eager run of the same steps through the workspace entry points
+and the host-counted AdamW, and with the oracle.
 """
 import numpy as np
 import pytest
@@ -51,13 +53,14 @@ def test_captured_rank_step_replays_match_eager_and_oracle(zm):
                 "scale": torch.zeros(1, dtype=torch.float32, device=dev())}
 
     g_st, e_st = state(), state()
+    sched = zm.AdamWSchedule(HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"])
     ws = zm.sqnorm_workspace(dev())
     # the first call on the device, outside capture: it looks up the array's address
     zm.zero_grad_reduce_shard_noalloc(plan, rank, reps, 0, P, g_st["grad"],
                                       sqnorm_out=g_st["parts"][rank:rank + 1])
     torch.cuda.synchronize()
 
-    def step(st, noalloc):
+    def step(st, noalloc, t=None):
         if noalloc:
             zm.zero_grad_reduce_shard_noalloc(plan, rank, reps, 0, P, st["grad"],
                                               sqnorm_out=st["parts"][rank:rank + 1])
@@ -66,8 +69,13 @@ def test_captured_rank_step_replays_match_eager_and_oracle(zm):
             zm.zero_grad_reduce_shard(plan, rank, reps, 0, P, st["grad"],
                                       sqnorm_out=st["parts"][rank:rank + 1], workspace=big)
         zm.zero_clip_scale(st["parts"], max_norm, st["scale"])
-        zm.zero_shard_adamw_step(st["master"], st["m"], st["v"], st["grad"], st["param"], 1,
-                                 clip_scale=st["scale"], **HP)
+        if noalloc:             # the step number on the device
+            zm.zero_shard_adamw_step_scheduled(st["master"], st["m"], st["v"], st["grad"], st["param"],
+                                               sched, clip_scale=st["scale"])
+            sched.advance(clip_scale=st["scale"])
+        else:
+            zm.zero_shard_adamw_step(st["master"], st["m"], st["v"], st["grad"], st["param"], t,
+                                     clip_scale=st["scale"], **HP)
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):                       # recorded, not run
@@ -82,10 +90,11 @@ def test_captured_rank_step_replays_match_eager_and_oracle(zm):
     for k in range(4):
         graph.replay()
         torch.cuda.synchronize()
-        step(e_st, False)                               # eager, the workspace entry point
+        step(e_st, False, k + 1)                        # eager, the workspace entry point
         zm.zero_grad_reduce_shard(plan, (rank + 1) % n_ranks, reps, 0, P, other)   # unrelated eager work
         torch.cuda.synchronize()
-        want = oracle.rank_step(ref, rank, reps_h, 0, o_state, o_shards, remote, 1, HP, max_norm)
+        want = oracle.rank_step(ref, rank, reps_h, 0, o_state, o_shards, remote, k + 1, HP, max_norm)
+        assert sched.applied() == k + 1
         note(f"graph replay {k}: clip {g_st['scale'].item()} (eager {e_st['scale'].item()}, "
              f"oracle {want['clip']})")
         for key in ("grad", "param"):
