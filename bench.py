@@ -959,8 +959,8 @@ def main(argv=None):
     if args.write_traffic:
         return write_traffic(args)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the per-rank step is measured on one GPU's share)", file=sys.stderr)
+        print(f"bench.py: times one rank's step on one GPU; --gpus {args.gpus} is not supported "
+              "(collectives across GPUs are not implemented)", file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():
