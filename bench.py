@@ -19,9 +19,10 @@ Other workloads (`--workload`), each timed as its own configuration states:
   llama3-8b   rank 63 of 64: six 25M-element buckets of 64 replicas reduced
               into the 125,472,896-element shard, clip 1.0, AdamW
   gpt-1.3b    all 8 ranks of the 1.3B GPT list: 8 replicas reduced for every
-              rank, AdamW on every shard, gather to 292 tensors
+              rank, AdamW on every shard, gather to 292 tensors (the job does
+              not clip, so no squared norm is computed)
   gpt-1.3b-fused  the same with each rank's reduce and AdamW in one pass
-              (zero_reduce_adamw_step: no global norm or clip between them)
+              (zero_reduce_adamw_step)
   gpt2-small-fsdp2  the gpt2-small step on FSDP-2's per-parameter Shard(0) layout
               (every tensor cut along dim 0; a rank's chunks in one coalesced
               buffer); the replicas are per-tensor gradients flattened into it
@@ -462,13 +463,14 @@ class AllRanksWorkload:
             synth.device_normal_bf16(t, self.seed, synth.KIND_REPLICA, 1, k, 0, phi, synth.GRAD_SIGMA)
         self.tensors = [torch.empty(n, dtype=torch.int16, device=device)
                         for n in plan_numels(self.plan)]
-        self.partials = torch.zeros(w.n_ranks, dtype=torch.float64, device=device)
-        self.workspace = zb.reduce_workspace(S, device)
+        # this job does not clip, so the reduce computes no squared norm
+        if w.max_norm > 0:
+            raise ValueError(f"{name}: the all-ranks workload runs without clipping")
+        self.max_norm = 0.0
         st = torch.cuda.current_stream(device).cuda_stream
         sl = [slice(r * S, (r + 1) * S) for r in range(w.n_ranks)]
         self._reduce = [zb.prepare_grad_reduce_shard(self.plan, r, self.reps, 0, P,
-                                                     self.grad[sl[r]], self.partials[r:r + 1],
-                                                     self.workspace, st)
+                                                     self.grad[sl[r]], None, None, st)
                         for r in range(w.n_ranks)]
         self._adamw = [zb.prepare_shard_adamw_step(self.master[sl[r]], self.m[sl[r]],
                                                    self.v[sl[r]], self.grad[sl[r]],
@@ -532,11 +534,11 @@ class AllRanksWorkload:
                 "flatten_call": 4 * self.phi + 2 * (P - self.phi)}
 
     def describe(self):
-        update = (f"reduce of {self.replicas} bf16 replicas and AdamW in one pass per rank (no clip)"
+        update = (f"reduce of {self.replicas} bf16 replicas and AdamW in one pass per rank"
                   if self.fused else
                   f"reduce of {self.replicas} bf16 replicas per rank + AdamW per shard")
         return (f"{self.workload.name} tensor list, N_d={self.n_ranks}, all {self.n_ranks} ranks in "
-                f"turn ({self.S} elements each); step = {update} + gather of "
+                f"turn ({self.S} elements each); step = {update} (no norm or clip) + gather of "
                 f"{len(self.workload.numels)} tensors")
 
 
@@ -783,8 +785,8 @@ def write_traffic(args) -> int:
 def cpu_baseline(wl, budget_s: float):
     """The oracle on the host for the same workload, bounded in time. The default
     workload times the oracle's whole rank step; the large ones time the same
-    per-element work (the reduce where the step has one, exact norm, clip, AdamW)
-    on a 2^24-element slice."""
+    per-element work (the reduce where the step has one, the exact norm and clip
+    where it clips, AdamW) on a 2^24-element slice."""
     import numpy as np
 
     import oracle
@@ -810,7 +812,7 @@ def cpu_baseline(wl, budget_s: float):
         per_step = S
     else:
         n = min(wl.S, 1 << 24)
-        fused = getattr(wl, "fused", False)
+        clips = wl.max_norm > 0
         g0 = (wl.rank or 0) * wl.S
         R = wl.replicas
         if R:
@@ -830,12 +832,12 @@ def cpu_baseline(wl, budget_s: float):
                 oracle.reduce_shard(window, 0, reps, 0, g)
             else:                   # gradients arrive averaged: no reduce in the step
                 g = reps[0]
-            # the one-pass workload updates with no clip between reduce and AdamW
-            clip = 1.0 if fused else oracle.clip_scale([oracle.sqnorm(g)], 1.0)
+            # the all-ranks job does not clip: no norm between its reduce and AdamW
+            clip = oracle.clip_scale([oracle.sqnorm(g)], wl.max_norm) if clips else 1.0
             st["p"], st["m"], st["v"], _ = oracle.adamw_step(st["p"], st["m"], st["v"], g, t,
                                                              clip=clip, **hp)
         work = f"reduce of {R} replica windows, " if R else ""
-        work += "AdamW" if fused else "exact norm, clip, AdamW"
+        work += "exact norm, clip, AdamW" if clips else "AdamW"
         sample = (f"passes of the per-element work of this workload ({work}) "
                   f"over a {n}-element slice of the shard")
         per_step = n

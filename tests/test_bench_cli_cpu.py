@@ -55,11 +55,11 @@ def test_traffic_record_matches_sources_and_sizes():
     assert bench.measured_traffic(12345) is None
 
 
-@pytest.mark.parametrize("replicas,fused", [(0, False), (8, False), (8, True)])
-def test_cpu_baseline_reports_its_sample_and_core_count(replicas, fused):
+@pytest.mark.parametrize("replicas,max_norm", [(0, 1.0), (8, 1.0), (8, 0.0)])
+def test_cpu_baseline_reports_its_sample_and_core_count(replicas, max_norm):
     """The cpu_baseline leg on a small stand-in workload (the attributes it
     reads, no device): one pass at least, a readable sample naming the count and
-    the work, one core."""
+    the work (the norm and clip only where the workload clips), one core."""
     import types
     sys.path.insert(0, ROOT)
     import bench
@@ -68,11 +68,11 @@ def test_cpu_baseline_reports_its_sample_and_core_count(replicas, fused):
     w = synth.WORKLOADS["tiny-a"]
     wl = types.SimpleNamespace(name="stand-in", hyper=Hyper(), S=4096, rank=1, seed=7,
                                phi=w.numel if hasattr(w, "numel") else sum(w.numels),
-                               replicas=replicas, fused=fused)
+                               replicas=replicas, max_norm=max_norm)
     r = bench.cpu_baseline(wl, 0.0)
     assert r["kind"] == "oracle" and r["unit"] == "params/s" and r["cores"] == 1
     assert r["value"] > 0 and r["seconds"] > 0
     count, rest = r["sample"].split(" ", 1)
     assert int(count) >= 1 and rest.startswith("passes of the per-element work")
     assert ("reduce of 8 replica windows" in rest) == (replicas == 8)
-    assert ("clip" in rest) == (not fused)
+    assert ("clip" in rest) == (max_norm > 0)
