@@ -729,15 +729,22 @@ def _counter_means(folder: str, counter: str):
 
 def write_traffic(args) -> int:
     """profiles/adamw_traffic.json's entry for this workload, from the counter runs."""
+    import synth
     import zero_partitioned_mixed_partition_amd as zm
-    if args.workload not in RankWorkload.SPECS or args.workload.endswith("-pertensor") \
+    if args.workload == "gpt-1.3b":         # every rank's shard in turn, one launch each
+        w = synth.WORKLOADS[args.workload]
+        nd = w.n_ranks
+        plan = zm.zero_partition_plan(w.numels, nd, w.align)
+        who = f"{args.workload}, each of the {nd} ranks' shards"
+    elif args.workload not in RankWorkload.SPECS or args.workload.endswith("-pertensor") \
             or args.workload.endswith("-offload"):
         raise SystemExit("bench.py: --write-traffic covers the flat-array AdamW workloads")
-    lst, nd, rank, *_rest, layout = RankWorkload.SPECS[args.workload]
-    import synth
-    w = synth.WORKLOADS[lst]
-    plan = (zm.zero_partition_plan_shard0(w.numels, [x[0] for x in w.shapes], nd, w.align)
-            if layout == "shard0" else zm.zero_partition_plan(w.numels, nd, w.align))
+    else:
+        lst, nd, rank, *_rest, layout = RankWorkload.SPECS[args.workload]
+        w = synth.WORKLOADS[lst]
+        plan = (zm.zero_partition_plan_shard0(w.numels, [x[0] for x in w.shapes], nd, w.align)
+                if layout == "shard0" else zm.zero_partition_plan(w.numels, nd, w.align))
+        who = f"{args.workload} rank {rank} of {nd}"
     S = plan.shard_numel
     calls = args.profile_steps
     if calls < 1:
@@ -754,9 +761,13 @@ def write_traffic(args) -> int:
     if len(ad) != 1:
         raise SystemExit(f"bench.py: expected one AdamW kernel name, found {ad}")
     ad = ad[0]
-    f_bytes = sum(fetch[ad]) * 1024 * f_scale / calls
-    w_bytes = sum(write[ad]) * 1024 * w_scale / calls
-    entry = {"kernel": "adamw_kernel", "workload": f"{args.workload} rank {rank} of {nd}",
+    if len(fetch[ad]) % calls or len(write[ad]) != len(fetch[ad]):
+        raise SystemExit(f"bench.py: {len(fetch[ad])} and {len(write[ad])} AdamW dispatches "
+                         f"for {calls} steps")
+    # per launch: the mean over the profiled steps' dispatches
+    f_bytes = sum(fetch[ad]) * 1024 * f_scale / len(fetch[ad])
+    w_bytes = sum(write[ad]) * 1024 * w_scale / len(write[ad])
+    entry = {"kernel": "adamw_kernel", "workload": who,
              "elems": S, "dispatches_per_call": len(fetch[ad]) // calls,
              "fetch_bytes": f_bytes, "write_bytes": w_bytes, "bytes_per_launch": f_bytes + w_bytes,
              "algorithmic_bytes": 28 * S, "fetch_scale": f_scale, "write_scale": w_scale,
