@@ -11,6 +11,9 @@ gpt2-small       GPT-2-small tensor list, N_d = 8, rank 7 (15.6M elements),
 bench pipeline   the benchmark's own step (8 replicas reduced for rank 7, fused
                  norm, clip, AdamW, gather of 148 tensors): full arrays for 2 steps;
                  also on the Shard(0) layout and with the AdamW offloaded to the host.
+all ranks        the benchmark's own 1.3B GPT step (every rank's reduce and AdamW,
+                 as two calls or in one pass, then the gather of 292 tensors): two
+                 steps, windows at every rank's ends and across rank boundaries.
 """
 import numpy as np
 import pytest
@@ -151,6 +154,59 @@ def test_gpt2_small_rank7_hundred_steps_clip(zm):
                 assert gpu_digests[t][c][k] == want[c][t][k], \
                     f"step {t + 1}: {name} differs from the oracle in [{a}, {b})"
     note(f"gpt2-small: {steps} steps x {len(chunks)} windows x 4 arrays bit-identical")
+
+
+@pytest.mark.parametrize("name", ["gpt-1.3b", "gpt-1.3b-fused"])
+def test_bench_all_ranks_step_matches_oracle(zm, name):
+    """The benchmark's 1.3B GPT step as bench.py times it: every rank's reduce of
+    its 8 replicas (no norm: the job does not clip) and AdamW, as two calls or
+    in one pass, then the gather of all 292 tensors. After two steps, on 4,096-
+    element windows at both ends of every rank's shard, across every boundary
+    between two ranks and at one random offset per rank: the reduced gradient
+    (two calls), the fp32 master, m and v and the bf16 parameters bit for bit
+    against the oracle's reduce and two AdamW steps; and every gathered tensor
+    equals its span of the parameter buffer."""
+    import bench
+    wl = bench.make_workload(name, dev())
+    try:
+        P, S, phi, R = wl.P, wl.S, wl.phi, wl.replicas
+        hp = wl.hyper.as_kwargs()
+        note(f"bench all ranks {name}: {wl.n_ranks} ranks x {S} elements, {R} replicas, 2 steps")
+        steps = 2
+        for _ in range(steps):
+            bench.run_step(wl)
+        torch.cuda.synchronize()
+        n = 4096
+        rng = np.random.default_rng(5)
+        starts = []
+        for r in range(wl.n_ranks):
+            starts += [r * S, (r + 1) * S - n, r * S + int(rng.integers(0, S - n))]
+            if r:
+                starts.append(r * S - n // 2)
+        win = oracle.partition_plan([n], 1, 1)
+        for a in starts:
+            reps = [synth.normal_bf16(n, wl.seed, synth.KIND_REPLICA, 1, k, a, phi, synth.GRAD_SIGMA)
+                    for k in range(R)]
+            g = np.zeros(n, np.uint16)
+            oracle.reduce_shard(win, 0, reps, 0, g)
+            p = synth.normal_f32(n, wl.seed, synth.KIND_MASTER, 0, 0, a, phi, synth.MASTER_SIGMA)
+            m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+            bits = None
+            for t in range(1, steps + 1):
+                p, m, v, bits = oracle.adamw_step(p, m, v, g, t, clip=1.0, **hp)
+            sl = slice(a, a + n)
+            if not wl.fused:
+                assert_bits_equal(host_u16(wl.grad[sl]), g, f"gradient at {a}")
+            for got, want, what in ((wl.master, p, "master"), (wl.m, m, "m"), (wl.v, v, "v")):
+                assert_bits_equal(host_f32(got[sl]).view(np.uint32), want.view(np.uint32),
+                                  f"{what} at {a}")
+            assert_bits_equal(host_u16(wl.param[sl]), bits, f"parameters at {a}")
+        for t, dst in enumerate(wl.tensors):
+            off = wl.plan.tensor_offset(t)
+            assert torch.equal(dst, wl.param[off:off + dst.numel()]), f"tensor {t}"
+    finally:
+        del wl
+        torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", ["gpt2-small", "gpt2-small-fsdp2", "gpt2-small-offload",
