@@ -351,7 +351,7 @@ static_assert(sizeof(MtDesc) == 64, "one 64-byte descriptor per tensor");
 // XCD-major order), so a workgroup finds its tensor with one scalar load
 // instead of two dependent ones; 0 (default): one descriptor per tensor and a
 // per-workgroup index. Measured on MI355X, GPT-2 rank 7's 148 Shard(0) chunks,
-// three rounds: 71.6-71.8 us against 71.4-71.6 us in the step; no gain.
+// three runs: 71.6-71.8 us against 71.4-71.6 us in the step; no gain.
 #ifndef ZERO_MT_DESC_PER_WG
 #define ZERO_MT_DESC_PER_WG 0
 #endif

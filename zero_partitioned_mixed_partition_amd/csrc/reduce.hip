@@ -48,7 +48,7 @@ constexpr int kThreads = 256;
 // Below the cap each thread handles one group of 8 elements; above it threads
 // stride.
 // The grid depends on n only, so the summation order (and the fp64 result)
-// is the same on every device. Re-measured for the replica reduce, two rounds,
+// is the same on every device. Re-measured for the replica reduce, two runs,
 // with its final sum: caps of 512, 1,024, 2,048 and 4,096 workgroups took
 // 4,453, 2,823-2,824, 2,522-2,523 and 2,513-2,516 us on Llama-3-8B (64
 // replicas) and 80.2-80.3, 53.3-53.4, 47.0 and 47.5 us on GPT-2 (8).
@@ -76,7 +76,7 @@ constexpr int kReplicaBatch = ZERO_REDUCE_BATCH;   // replicas per load batch
 
 // 1: the reduce kernels store the averaged gradient with plain (cache-allocating)
 // stores, so a following AdamW can read it from cache; 0 (default): streaming
-// write-through stores. Measured on MI355X, three rounds: the reduce 7% slower
+// write-through stores. Measured on MI355X, three runs: the reduce 7% slower
 // on GPT-2 (51.2-51.8 against 47.6-47.9 us), 5% on Llama-3-8B, 4% on the 1.3B
 // GPT; AdamW after it 1.5% faster on Llama-3-8B only; steps level or slower.
 #ifndef ZERO_REDUCE_OUT_CACHED
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void reduce_vec(ReplicaTable reps, int n_
 // in flight all fall in one contiguous G * 4 KB run of one replica; then it
 // adds them. Lanes past the end load the last group again (every load is
 // unconditional) and drop it. Each element's sum is the same as reduce_vec's.
-// Measured on MI355X, two rounds, reduce phase with its final sum: Llama-3-8B
+// Measured on MI355X, two runs, reduce phase with its final sum: Llama-3-8B
 // (64 replicas, six 25 M buckets) 2,526-2,527 us with reduce_vec, 2,709-2,710
 // with G = 2, 2,675 with 4, 2,571-2,578 with 8; GPT-2 (8 replicas) 47.5 us,
 // 47.3-47.4, 48.4 and 47.9-48.1 us. More loads in flight per lane cost even
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void sqnorm_pass(const uint16_t* __restri
 // lane R of them kThreads apart, all R loads issued together (lanes past the
 // end reload the last group and drop it). One partial per workgroup, so one
 // final-sum kernel. Measured on MI355X, Llama-3-70B rank 7's 8.8 G-element
-// gradient in the benchmark step, two rounds: sqnorm_pass 2,601-2,656 us;
+// gradient in the benchmark step, two runs: sqnorm_pass 2,601-2,656 us;
 // R = 4, 8, 16 over 4,096 workgroups 2,640-2,654, 2,659-2,707 and
 // 2,641-2,749 us; R = 8 over 2,048 workgroups 2,616-2,666 us. Off.
 #ifndef ZERO_SQNORM_ROWS
@@ -880,7 +880,7 @@ namespace {
 
 // 2,048-element groups per workgroup (the descriptor lookup is paid once per
 // workgroup). Measured on MI355X, GPT-2 rank 7 from 8 per-tensor replicas, two
-// rounds, flat plan: 1 group 49.4-49.9 us, 2 groups 50.7-50.8 us, 4 groups
+// runs, flat plan: 1 group 49.4-49.9 us, 2 groups 50.7-50.8 us, 4 groups
 // 54.7-54.8 us (Shard(0): 51.8-52.0, 52.7-52.9, 57.7-58.0 us). One stays.
 #ifndef ZERO_RTABLE_GROUPS
 #define ZERO_RTABLE_GROUPS 1
@@ -889,7 +889,7 @@ constexpr int kRGroups = ZERO_RTABLE_GROUPS;
 constexpr int64_t kRChunk = int64_t(kThreads) * 8 * kRGroups;   // elements per workgroup
 // 1: the one-pass form leaves one norm partial per wave (no LDS, no barrier;
 // four times the partials); 0 (default): one per workgroup. Measured on MI355X,
-// GPT-2 rank 7 from 8 per-tensor replicas, two rounds: 50.4-50.5 us against
+// GPT-2 rank 7 from 8 per-tensor replicas, two runs: 50.4-50.5 us against
 // 49.8-50.0 us (Shard(0): 51.7 against 50.9-51.1 us).
 #ifndef ZERO_RTABLE_WAVE_PARTIALS
 #define ZERO_RTABLE_WAVE_PARTIALS 0
@@ -897,14 +897,14 @@ constexpr int64_t kRChunk = int64_t(kThreads) * 8 * kRGroups;   // elements per 
 constexpr int64_t kRPartialsPerBlock = ZERO_RTABLE_WAVE_PARTIALS ? kThreads / 64 : 1;
 // Workgroups of the grid-stride form (0, default: one workgroup per chunk, one
 // pass). Measured on MI355X, GPT-2 rank 7 from 8 per-tensor replicas, two
-// rounds: one pass 50.5-50.9 us; grids of 1,024, 2,048 and 4,096 workgroups
+// runs: one pass 50.5-50.9 us; grids of 1,024, 2,048 and 4,096 workgroups
 // 55.7-56.1, 55.8-56.1 and 51.9-52.1 us.
 #ifndef ZERO_RTABLE_GRID
 #define ZERO_RTABLE_GRID 0
 #endif
 // 1: the 16-byte path issues each batch of replica loads together
 // (zero::dev::for_replicas); 0 (default): a guarded load per replica. Measured
-// on MI355X, GPT-2 rank 7 from 8 per-tensor replicas, two rounds: 51.3-51.5 us
+// on MI355X, GPT-2 rank 7 from 8 per-tensor replicas, two runs: 51.3-51.5 us
 // against 50.6-51.1 us on the flat plan, 53.5 against 51.3-51.9 us on Shard(0).
 #ifndef ZERO_RTABLE_BATCHED_ISSUE
 #define ZERO_RTABLE_BATCHED_ISSUE 0

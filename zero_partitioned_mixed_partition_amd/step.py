@@ -296,7 +296,7 @@ class RankStep:
 
 
 # Gap between consecutive arrays of an arena (and between replica buffers).
-# Measured on MI355X over the benchmark's steps, two rounds each: 2048 bytes was
+# Measured on MI355X over the benchmark's steps, two runs each: 2048 bytes was
 # the fastest or level on every workload; against 4352 bytes it took the 1.3B
 # GPT step from 10.04 to 9.83-9.88 ms, Llama-3-8B's from 3.12 to 3.06 ms and
 # Llama-3-70B's from 40.51-40.55 to 40.10-40.11 ms (AdamW 81.5% -> 82.2% of
