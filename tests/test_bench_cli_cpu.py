@@ -76,3 +76,47 @@ def test_cpu_baseline_reports_its_sample_and_core_count(replicas, max_norm):
     assert int(count) >= 1 and rest.startswith("passes of the per-element work")
     assert ("reduce of 8 replica windows" in rest) == (replicas == 8)
     assert ("clip" in rest) == (max_norm > 0)
+
+
+def _counter_csv(folder, counter, rows):
+    """A rocprofv3-style counter_collection.csv: (dispatch, kernel, KiB) rows,
+    each dispatch split over two channel rows as the real files are."""
+    import csv
+    folder.mkdir(parents=True)
+    with open(folder / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, name, kib in rows:
+            w.writerow([d, name, counter, kib / 2])
+            w.writerow([d, name, counter, kib / 2])
+
+
+@pytest.mark.parametrize("workload,steps,launches", [("gpt-1.3b", 1, 8), ("gpt2-small", 2, 1)])
+def test_write_traffic_takes_bytes_per_launch(tmp_path, monkeypatch, workload, steps, launches):
+    """--write-traffic on synthetic counter files: reads scaled by the 1 GiB
+    copy's FETCH_SIZE (which reads it as half), writes by its WRITE_SIZE, and
+    the entry's bytes are per AdamW launch (the mean over the profiled
+    dispatches), whatever the launches per step."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import synth
+    import zero_partitioned_mixed_partition_amd as zm
+    w = synth.WORKLOADS[workload]
+    S = zm.zero_partition_plan(w.numels, w.n_ranks, w.align).shard_numel
+    kib = 28 * S / 1024 / 2          # each direction, before scaling
+    copy = "__amd_rocclr_copyBuffer"
+    n = steps * launches
+    fetch = [(0, copy, float(1 << 19))] + [(1 + i, "adamw_kernel(float*)", kib / 2) for i in range(n)]
+    write = [(0, copy, float(1 << 20))] + [(1 + i, "adamw_kernel(float*)", kib) for i in range(n)]
+    _counter_csv(tmp_path / "fetch", "FETCH_SIZE", fetch)
+    _counter_csv(tmp_path / "write", "WRITE_SIZE", write)
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    args = bench.parse_args(["--workload", workload, "--profile-steps", str(steps), "--write-traffic",
+                             str(tmp_path / "fetch"), str(tmp_path / "write")])
+    assert bench.write_traffic(args) == 0
+    (e,) = json.load(open(out))["runs"]
+    assert e["elems"] == S and e["dispatches_per_call"] == launches
+    assert e["fetch_scale"] == 2.0 and e["write_scale"] == 1.0
+    assert e["bytes_per_launch"] == pytest.approx(28 * S, rel=1e-12)
+    assert e["algorithmic_bytes"] == 28 * S
